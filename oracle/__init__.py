@@ -1,0 +1,198 @@
+"""CPU oracle for the compressed branch of NSA -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It wraps ``nsa_oracle.c`` (plain C,
+float64 on bfloat16-widened inputs) through ctypes and shares no code with
+the HIP library in ``kv_compression_block_amd``.
+
+Every function here either marshals arrays or chains the C steps in the
+order the operator pages give them:
+
+* ``compress``  -- the NSA Compress formula ("aclnnNsaCompress", Formula);
+* ``attention`` -- steps 1-7 of "mindspore.ops.nsa_compress_attention"
+  (scores, mask, softmax, output, importance remap, group sum, top-k).
+
+The compressed keys/values that feed attention are the compression results
+rounded to bfloat16 (round to nearest, ties to even), because that is the
+dtype the attention operator takes for its key and value inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nsa_oracle.c")
+_LIB = os.path.join(_HERE, "libnsa_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile nsa_oracle.c with gcc (no -ffast-math: IEEE semantics kept)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-D_DEFAULT_SOURCE", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-Werror", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.nsa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.nsa_oracle_bf16_to_double.restype = ctypes.c_double
+    lib.nsa_oracle_double_to_bf16.argtypes = [ctypes.c_double]
+    lib.nsa_oracle_double_to_bf16.restype = ctypes.c_uint16
+    lib.nsa_oracle_round_to_bf16.argtypes = [P, P, I64]
+    lib.nsa_oracle_round_to_bf16.restype = None
+    lib.nsa_oracle_threads.argtypes = []
+    lib.nsa_oracle_threads.restype = ctypes.c_int
+    lib.nsa_oracle_n_cmp.argtypes = [I64, I64, I64]
+    lib.nsa_oracle_n_cmp.restype = I64
+    lib.nsa_oracle_compress.argtypes = [P, P, P, I64, I64, I64, I64, I64, P]
+    lib.nsa_oracle_compress.restype = ctypes.c_int
+    lib.nsa_oracle_attention.argtypes = [P, P, I64, P, P, P, P, I64,
+                                         I64, I64, I64, I64, ctypes.c_double,
+                                         I64, I64, I64, I64,
+                                         P, P, P, P, I64, P]
+    lib.nsa_oracle_attention.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected bfloat16 bit patterns as uint16, got {a.dtype}")
+    return a
+
+
+def _i64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def threads() -> int:
+    return int(_load().nsa_oracle_threads())
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns."""
+    b = _u16(bits)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def to_bf16(x) -> np.ndarray:
+    """Round float64 values to bfloat16 bit patterns (nearest, ties to even)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().nsa_oracle_round_to_bf16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def n_cmp(T: int, l: int, d: int) -> int:
+    return int(_load().nsa_oracle_n_cmp(T, l, d))
+
+
+def cmp_prefix(seqlens: Sequence[int], l: int, d: int) -> np.ndarray:
+    """Prefix sums of the compressed lengths of each sequence."""
+    return np.cumsum([n_cmp(int(T), l, d) for T in seqlens]).astype(np.int64)
+
+
+def sel_prefix(seqlens: Sequence[int], lsel: int) -> np.ndarray:
+    """Prefix sums of the number of select blocks, ceil(T / l'), per sequence."""
+    return np.cumsum([-(-int(T) // lsel) for T in seqlens]).astype(np.int64)
+
+
+def compress(x_bits, w_bits, act_seq_len, l: int, d: int) -> np.ndarray:
+    """x: [T, N, D] bf16 bits, w: [l, N] bf16 bits -> [T2, N, D] float64."""
+    x = _u16(x_bits)
+    w = _u16(w_bits)
+    T, N, D = x.shape
+    if w.shape != (l, N):
+        raise ValueError(f"weight shape {w.shape} != {(l, N)}")
+    act = _i64(act_seq_len)
+    if act[-1] != T:
+        raise ValueError("prefix sums do not end at the token count")
+    starts = np.concatenate([[0], act[:-1]])
+    T2 = int(sum(n_cmp(int(e - s), l, d) for s, e in zip(starts, act)))
+    out = np.empty((T2, N, D), dtype=np.float64)
+    rc = _load().nsa_oracle_compress(_ptr(x), _ptr(w), _ptr(act), len(act), N, D, l, d, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_compress returned {rc}")
+    return out
+
+
+def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_kvlen,
+              N1: int, N2: int, scale: float, l: int, d: int, lsel: int, count: int,
+              s_stride: Optional[int] = None) -> dict:
+    """Steps 1-7 for the listed global tokens.
+
+    q_rows_bits: [n_tok, N1, D1] bf16 bits of those tokens' query rows.
+    Returns dict(out [n,N1,D2], max [n,N1], sum [n,N1],
+                 pslc [n,N2,s_stride], topk [n,N2,count] int32).
+    """
+    q = _u16(q_rows_bits)
+    kc = _u16(kc_bits)
+    vc = _u16(vc_bits)
+    tok = _i64(tokens)
+    n_tok = len(tok)
+    D1 = kc.shape[2]
+    D2 = vc.shape[2]
+    if q.shape != (n_tok, N1, D1):
+        raise ValueError(f"q rows shape {q.shape} != {(n_tok, N1, D1)}")
+    actq = _i64(act_seq_qlen)
+    actc = _i64(act_cmp_seq_kvlen)
+    starts = np.concatenate([[0], actq[:-1]])
+    s_sel_max = int(max(-(-(int(e - s)) // lsel) for s, e in zip(starts, actq)))
+    if s_stride is None:
+        s_stride = max(1, s_sel_max)
+    out = np.empty((n_tok, N1, D2), dtype=np.float64)
+    smax = np.empty((n_tok, N1), dtype=np.float64)
+    ssum = np.empty((n_tok, N1), dtype=np.float64)
+    pslc = np.empty((n_tok, N2, s_stride), dtype=np.float64)
+    topk = np.empty((n_tok, N2, count), dtype=np.int32)
+    rc = _load().nsa_oracle_attention(_ptr(q), _ptr(tok), n_tok, _ptr(kc), _ptr(vc),
+                                      _ptr(actq), _ptr(actc), len(actq),
+                                      N1, N2, D1, D2, float(scale), l, d, lsel, count,
+                                      _ptr(out), _ptr(smax), _ptr(ssum), _ptr(pslc), s_stride,
+                                      _ptr(topk))
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_attention returned {rc}")
+    return {"out": out, "max": smax, "sum": ssum, "pslc": pslc, "topk": topk}
+
+
+def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None) -> dict:
+    """The whole path for a workload: compress K and V, round them to
+    bfloat16, then steps 1-7 for ``tokens`` (all tokens when None)."""
+    actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
+    kc = compress(k_bits, w_bits, actq, wl.l, wl.d)
+    vc = compress(v_bits, w_bits, actq, wl.l, wl.d)
+    kc_b = to_bf16(kc)
+    vc_b = to_bf16(vc)
+    if tokens is None:
+        tokens = np.arange(wl.T, dtype=np.int64)
+        q_rows = q_bits
+    else:
+        tokens = np.asarray(tokens, dtype=np.int64)
+        q_rows = q_bits[tokens]
+    res = attention(q_rows, tokens, kc_b, vc_b, actq, cmp_prefix(wl.seqlens, wl.l, wl.d),
+                    wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count)
+    res.update({"kc": kc, "vc": vc, "kc_bf16": kc_b, "vc_bf16": vc_b, "tokens": tokens})
+    return res

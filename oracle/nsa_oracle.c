@@ -1,0 +1,348 @@
+/*
+ * CPU oracle for the compressed branch of Native Sparse Attention (NSA).
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  The product (the HIP library and
+ * its Python binding) never calls it, and it shares no code, header, table or
+ * helper with the product.
+ *
+ * What it computes is the plain definition, step by step, in the order the
+ * two operator pages give it:
+ *
+ *   - "aclnnNsaCompress" (CANN operator page), section "Formula": the
+ *     compressed keys of a sequence of length t are phi applied to the windows
+ *     k_{id+1 : id+l} for 0 <= i <= floor((t-l)/d).  phi is read as a
+ *     per-window-position weighted sum with a weight of shape [l, N]: a
+ *     scalar per (window position, head), broadcast over the head dim.
+ *
+ *   - "mindspore.ops.nsa_compress_attention" (MindSpore operator page),
+ *     steps 1-7: scaled QK^T, attention mask, softmax -> P_cmp,
+ *     attentionOut = P_cmp . value, the importance-score remap
+ *     P_slc[j] = sum_{m<l'/d} sum_{n<l/d} P_cmp[l'/d*j - m - n],
+ *     the sum of P_slc over the query heads of a KV-head group, the top-k
+ *     mask and the top-k indices.
+ *
+ * Arithmetic is float64 on inputs that are bfloat16 bit patterns widened
+ * exactly.  The one decision that floating point turns into integers (which
+ * blocks the top-k picks) is taken on the importance scores rounded to
+ * float32, the precision the GPU kernels take it in.
+ *
+ * Readings of points the pages leave open (each also listed in the design
+ * notes of the repository):
+ *   - a compressed block i is visible to the query at local position t iff
+ *     i*d + l - 1 <= t (the last token of its window is not in the future);
+ *     no explicit mask tensor is taken;
+ *   - select block j is a top-k candidate iff j*l' <= t; picks beyond the
+ *     number of candidates are -1;
+ *   - query head h belongs to KV head floor(h / (N1/N2));
+ *   - a remap index outside [0, number of compressed blocks) adds 0;
+ *   - l/d in the remap's upper limit is floor(l/d); l'/d is an integer
+ *     (the page requires l' % d == 0);
+ *   - the number of select blocks of a sequence of length T is ceil(T/l');
+ *   - a query with no visible block has output 0, softmax max -inf and
+ *     softmax sum 0;
+ *   - top-k order: descending score, ties to the lower block index.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- bfloat16 ------------------------------------------------------------ */
+
+/* Widen a bfloat16 bit pattern: it is the top half of a float32. */
+double nsa_oracle_bf16_to_double(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16, ties to even (one rounding step,
+ * straight from double).  bfloat16 keeps 8 significant bits and float32's
+ * exponent range; below 2^-126 its spacing is fixed at 2^-133. */
+uint16_t nsa_oracle_double_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0)
+        return sign;
+    if (isinf(ax))
+        return (uint16_t)(sign | 0x7F80);
+    int e;
+    frexp(ax, &e);                 /* ax = m * 2^e, m in [0.5, 1) */
+    int qexp = e - 8;              /* spacing of 8 significant bits */
+    if (qexp < -133)
+        qexp = -133;               /* subnormal range */
+    double r = nearbyint(ldexp(ax, -qexp));  /* default mode: nearest, ties even */
+    double y = ldexp(r, qexp);
+    const double bf16_max = 3.3895313892515355e38;  /* (2 - 2^-7) * 2^127 */
+    if (y > bf16_max)
+        return (uint16_t)(sign | 0x7F80);
+    float f = (float)y;            /* exact: y has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+void nsa_oracle_round_to_bf16(const double* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = nsa_oracle_double_to_bf16(x[i]);
+}
+
+int nsa_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---- step A: compression (aclnnNsaCompress, "Formula") -------------------- */
+
+/* Number of windows of a length-T sequence: i runs from 0 to floor((T-l)/d),
+ * and there is none when T < l. */
+int64_t nsa_oracle_n_cmp(int64_t T, int64_t l, int64_t d)
+{
+    if (T < l)
+        return 0;
+    return (T - l) / d + 1;
+}
+
+static int64_t seq_start(const int64_t* prefix, int64_t b)
+{
+    return b == 0 ? 0 : prefix[b - 1];
+}
+
+/* x: [T, N, D] bf16 (TND, sequences back to back, lengths given as prefix
+ * sums act_seq_len[B]); w: [l, N] bf16; out: [sum_b n_cmp_b, N, D] double.
+ * out[i, h, e] = sum_{p<l} w[p, h] * x[start + i*d + p, h, e]: the 1-based
+ * window k_{id+1 : id+l} is rows i*d .. i*d+l-1 counted from 0. */
+int nsa_oracle_compress(const uint16_t* x, const uint16_t* w, const int64_t* act_seq_len,
+                        int64_t B, int64_t N, int64_t D, int64_t l, int64_t d, double* out)
+{
+    if (B < 1 || N < 1 || D < 1 || l < 1 || d < 1)
+        return -1;
+    int64_t out_row = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t start = seq_start(act_seq_len, b);
+        int64_t T = act_seq_len[b] - start;
+        if (T < 0)
+            return -2;
+        int64_t n = nsa_oracle_n_cmp(T, l, d);
+        for (int64_t i = 0; i < n; ++i) {
+            for (int64_t h = 0; h < N; ++h) {
+                for (int64_t e = 0; e < D; ++e) {
+                    double acc = 0.0;
+                    for (int64_t p = 0; p < l; ++p) {
+                        double wp = nsa_oracle_bf16_to_double(w[p * N + h]);
+                        double xv = nsa_oracle_bf16_to_double(x[((start + i * d + p) * N + h) * D + e]);
+                        acc += wp * xv;
+                    }
+                    out[((out_row + i) * N + h) * D + e] = acc;
+                }
+            }
+        }
+        out_row += n;
+    }
+    return 0;
+}
+
+/* ---- steps 1-7 of nsa_compress_attention ---------------------------------- */
+
+/* Which sequence a global token belongs to, and its local position. */
+static int64_t find_seq(const int64_t* act_seq_qlen, int64_t B, int64_t tg, int64_t* t_local)
+{
+    for (int64_t b = 0; b < B; ++b) {
+        if (tg < act_seq_qlen[b]) {
+            *t_local = tg - seq_start(act_seq_qlen, b);
+            return b;
+        }
+    }
+    return -1;
+}
+
+/* Steps 1-3 for one (token, query head): scores s_i = scale * <q, k_i> over
+ * the visible compressed blocks, the softmax P_cmp and the output
+ * sum_i P_i v_i.  P receives P_cmp for every i < n_cmp (0 where masked). */
+static void attend_one_head(const uint16_t* qh, const uint16_t* kc, const uint16_t* vc,
+                            int64_t cmp0, int64_t n_cmp, int64_t t, int64_t g,
+                            int64_t N2, int64_t D1, int64_t D2, double scale,
+                            int64_t l, int64_t d,
+                            double* s, double* P, double* out_h, double* m_out, double* L_out)
+{
+    /* step 1: QK = scale * query . key^T, then the attention mask. */
+    double m = -INFINITY;
+    int any = 0;
+    for (int64_t i = 0; i < n_cmp; ++i) {
+        int visible = (i * d + l - 1 <= t);
+        if (!visible) {
+            s[i] = -INFINITY;
+            continue;
+        }
+        const uint16_t* ki = kc + ((cmp0 + i) * N2 + g) * D1;
+        double dot = 0.0;
+        for (int64_t e = 0; e < D1; ++e)
+            dot += nsa_oracle_bf16_to_double(qh[e]) * nsa_oracle_bf16_to_double(ki[e]);
+        s[i] = scale * dot;
+        if (!any || s[i] > m)
+            m = s[i];
+        any = 1;
+    }
+    /* step 2: P_cmp = Softmax(QK), natural base. */
+    double L = 0.0;
+    for (int64_t i = 0; i < n_cmp; ++i)
+        L += (s[i] == -INFINITY) ? 0.0 : exp(s[i] - m);
+    for (int64_t i = 0; i < n_cmp; ++i)
+        P[i] = (s[i] == -INFINITY) ? 0.0 : exp(s[i] - m) / L;
+    /* step 3: attentionOut = P_cmp . value. */
+    for (int64_t e = 0; e < D2; ++e) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < n_cmp; ++i) {
+            acc += P[i] * nsa_oracle_bf16_to_double(vc[((cmp0 + i) * N2 + g) * D2 + e]);
+        }
+        out_h[e] = acc;
+    }
+    *m_out = any ? m : -INFINITY;
+    *L_out = any ? L : 0.0;
+}
+
+/* Step 4 for one head: P_slc[j] = sum_{m=0}^{R-1} sum_{n=0}^{L2-1} P[R*j - m - n],
+ * R = l'/d and L2 = floor(l/d); indices outside [0, n_cmp) add nothing. */
+static void remap_one_head(const double* P, int64_t n_cmp, int64_t S_sel,
+                           int64_t R, int64_t L2, double* Pslc_h)
+{
+    for (int64_t j = 0; j < S_sel; ++j) {
+        double acc = 0.0;
+        for (int64_t m = 0; m < R; ++m) {
+            for (int64_t n = 0; n < L2; ++n) {
+                int64_t idx = R * j - m - n;
+                if (idx >= 0 && idx < n_cmp)
+                    acc += P[idx];
+            }
+        }
+        Pslc_h[j] = acc;
+    }
+}
+
+/* Steps 6-7 for one (token, KV head): candidates are the j with j*l' <= t;
+ * pick the `count` largest scores (descending, ties to the lower j) by
+ * repeated selection; slots left over hold -1. */
+static void topk_one_group(const double* Pslc_g, int64_t S_sel, int64_t t, int64_t lsel,
+                           int64_t count, unsigned char* taken, int32_t* idx_out)
+{
+    for (int64_t j = 0; j < S_sel; ++j)
+        taken[j] = !(j * lsel <= t);   /* topk_mask: not a candidate */
+    for (int64_t k = 0; k < count; ++k) {
+        int64_t best = -1;
+        float best_v = 0.0f;
+        for (int64_t j = 0; j < S_sel; ++j) {
+            if (taken[j])
+                continue;
+            float v = (float)Pslc_g[j];
+            if (best < 0 || v > best_v) {
+                best = j;
+                best_v = v;
+            }
+        }
+        if (best >= 0)
+            taken[best] = 1;
+        idx_out[k] = (int32_t)best;
+    }
+}
+
+/*
+ * Compressed attention, importance scores and top-k for the listed tokens.
+ *
+ * q_rows   : [n_tok, N1, D1] bf16, the query rows of the listed tokens
+ * tokens   : [n_tok] global token indices into the TND query tensor
+ * kc, vc   : [T2, N2, D1] and [T2, N2, D2] bf16 compressed keys / values
+ * act_seq_qlen, act_cmp_seq_kvlen : [B] prefix sums of the query and the
+ *            compressed lengths of each sequence
+ * out      : [n_tok, N1, D2]; smax, ssum: [n_tok, N1]
+ * pslc     : [n_tok, N2, s_stride] group-summed importance scores before the
+ *            top-k mask, j < ceil(T_b/l'), zero beyond
+ * topk     : [n_tok, N2, count] int32
+ * Returns 0, or a negative code for arguments it cannot evaluate.
+ */
+int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t n_tok,
+                         const uint16_t* kc, const uint16_t* vc,
+                         const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen, int64_t B,
+                         int64_t N1, int64_t N2, int64_t D1, int64_t D2, double scale,
+                         int64_t l, int64_t d, int64_t lsel, int64_t count,
+                         double* out, double* smax, double* ssum,
+                         double* pslc, int64_t s_stride, int32_t* topk)
+{
+    if (N2 < 1 || N1 % N2 != 0 || d < 1 || lsel % d != 0 || count < 1 || B < 1)
+        return -1;
+    const int64_t G = N1 / N2;
+    const int64_t R = lsel / d;
+    const int64_t L2 = l / d;
+    int64_t n_cmp_max = 0, s_sel_max = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t nc = act_cmp_seq_kvlen[b] - seq_start(act_cmp_seq_kvlen, b);
+        int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
+        int64_t ss = (T + lsel - 1) / lsel;
+        if (nc > n_cmp_max) n_cmp_max = nc;
+        if (ss > s_sel_max) s_sel_max = ss;
+    }
+    if (s_stride < s_sel_max)
+        return -2;
+    for (int64_t k = 0; k < n_tok; ++k) {
+        int64_t tl = 0;
+        if (find_seq(act_seq_qlen, B, tokens[k], &tl) < 0)
+            return -3;
+    }
+    int err = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(n_cmp_max + 1));
+        double* P = (double*)malloc(sizeof(double) * (size_t)(n_cmp_max + 1));
+        double* Ph = (double*)malloc(sizeof(double) * (size_t)(s_sel_max + 1));
+        unsigned char* taken = (unsigned char*)malloc((size_t)(s_sel_max + 1));
+        if (!s || !P || !Ph || !taken) {
+#pragma omp atomic write
+            err = -4;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t k = 0; k < n_tok; ++k) {
+                int64_t t = 0;
+                int64_t b = find_seq(act_seq_qlen, B, tokens[k], &t);
+                int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
+                int64_t cmp0 = seq_start(act_cmp_seq_kvlen, b);
+                int64_t n_cmp = act_cmp_seq_kvlen[b] - cmp0;
+                int64_t S_sel = (T + lsel - 1) / lsel;
+                double* pslc_k = pslc + k * N2 * s_stride;
+                for (int64_t x = 0; x < N2 * s_stride; ++x)
+                    pslc_k[x] = 0.0;
+                for (int64_t h = 0; h < N1; ++h) {
+                    int64_t g = h / G;
+                    attend_one_head(q_rows + (k * N1 + h) * D1, kc, vc, cmp0, n_cmp, t, g,
+                                    N2, D1, D2, scale, l, d, s, P,
+                                    out + (k * N1 + h) * D2,
+                                    smax + k * N1 + h, ssum + k * N1 + h);
+                    /* step 4, then step 5: heads of a group summed in order. */
+                    remap_one_head(P, n_cmp, S_sel, R, L2, Ph);
+                    for (int64_t j = 0; j < S_sel; ++j)
+                        pslc_k[g * s_stride + j] += Ph[j];
+                }
+                for (int64_t g = 0; g < N2; ++g)
+                    topk_one_group(pslc_k + g * s_stride, S_sel, t, lsel, count, taken,
+                                   topk + (k * N2 + g) * count);
+            }
+        }
+        free(s);
+        free(P);
+        free(Ph);
+        free(taken);
+    }
+    return err;
+}

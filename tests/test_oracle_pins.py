@@ -1,0 +1,540 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test ties one step of the oracle to a library routine, a closed form,
+an invariant, a hand-derived table or brute force, chosen so that a dropped
+term, a wrong sign or index, or a swapped operand in the oracle fails at
+least one of them.  No GPU is involved.
+
+Passages: "aclnnNsaCompress" page, Formula (compression);
+"mindspore.ops.nsa_compress_attention" page, steps 1-7 (attention,
+importance remap, group sum, top-k).
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bits(x) -> np.ndarray:
+    """bf16 bit patterns of values that must already be bf16-representable."""
+    t = torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    b = synth.bf16_bits(t)
+    assert np.array_equal(oracle.bf16_to_f64(b), np.asarray(x, dtype=np.float64)), \
+        "test input is not exactly representable in bfloat16"
+    return b
+
+
+def rand_bf16(rng, shape, std=1.0) -> np.ndarray:
+    x = torch.tensor(rng.standard_normal(shape).astype(np.float32) * std).to(torch.bfloat16)
+    return synth.bf16_bits(x)
+
+
+def starts_of(lens):
+    return np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+
+
+def n_vis_of(t, l, d, n_cmp):
+    """Number of compressed blocks i with i*d + l - 1 <= t (capped at n_cmp),
+    counted by brute force."""
+    return sum(1 for i in range(n_cmp) if i * d + l - 1 <= t)
+
+
+def run_all(q, kc, vc, lens, N1, N2, scale, l, d, lsel, count):
+    """Oracle steps 1-7 for every token of the given sequences."""
+    actq = np.cumsum(lens).astype(np.int64)
+    actc = oracle.cmp_prefix(lens, l, d)
+    tokens = np.arange(int(sum(lens)), dtype=np.int64)
+    return oracle.attention(q, tokens, kc, vc, actq, actc, N1, N2, scale, l, d, lsel, count)
+
+
+# --------------------------------------------------------------------------
+# bfloat16 rounding
+# --------------------------------------------------------------------------
+
+def test_bf16_rounding_matches_torch_on_float32_inputs():
+    """For float32 inputs, one rounding step from double equals torch's
+    float32 -> bfloat16 conversion (round to nearest, ties to even)."""
+    rng = np.random.default_rng(0)
+    mant = rng.standard_normal(200_000).astype(np.float32)
+    expo = rng.integers(-140, 128, 200_000).astype(np.float32)
+    with np.errstate(over="ignore"):
+        x = (mant * np.exp2(expo)).astype(np.float32)
+    tie_bits = (rng.integers(0, 2 ** 31, 50_000, dtype=np.uint64).astype(np.uint32) & 0xFFFF0000) | 0x8000
+    x = np.concatenate([x, tie_bits.view(np.float32)])
+    x = x[np.isfinite(x)]
+    ref = synth.bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+    got = oracle.to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("x,expect", [
+    (1.0, 0x3F80), (-1.0, 0xBF80), (0.0, 0x0000), (-0.0, 0x8000),
+    (1 + 2 ** -8, 0x3F80),            # tie -> even (down)
+    (1 + 3 * 2 ** -8, 0x3F82),        # tie -> even (up)
+    (1 + 2 ** -8 + 2 ** -40, 0x3F81), # just above a tie: up, in one step
+    (2.0 ** -133, 0x0001),            # smallest subnormal
+    (2.0 ** -134, 0x0000),            # tie between 0 and it -> 0
+    (3 * 2.0 ** -134, 0x0002),        # tie between 1 and 2 subnormal steps -> 2
+    (3.3895313892515355e38, 0x7F7F),  # largest finite
+    (3.4e38, 0x7F80),                 # rounds past it -> inf
+    (float("inf"), 0x7F80),
+])
+def test_bf16_rounding_special_values(x, expect):
+    assert int(oracle.to_bf16(np.array([x]))[0]) == expect
+
+
+# --------------------------------------------------------------------------
+# Compression ("aclnnNsaCompress", Formula)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,l,d,n", [(0, 32, 16, 0), (31, 32, 16, 0), (32, 32, 16, 1),
+                                     (47, 32, 16, 1), (48, 32, 16, 2), (512, 32, 16, 31),
+                                     (65536, 64, 32, 2047), (100, 16, 16, 6)])
+def test_number_of_windows(T, l, d, n):
+    """i runs over 0 .. floor((T-l)/d): counted by brute force over start rows."""
+    brute = sum(1 for i in range(T + 1) if i * d + l <= T)
+    assert brute == n
+    assert oracle.n_cmp(T, l, d) == n
+
+
+def test_compress_block_means_when_stride_equals_window():
+    """l = d and w = 1/l: windows do not overlap and each output is the mean
+    of its block, computed here with numpy reshape + mean."""
+    rng = np.random.default_rng(1)
+    l = d = 16
+    lens = [16 * 5, 16 * 3 + 7, 9, 16]
+    N, D = 3, 5
+    x = rand_bf16(rng, (sum(lens), N, D))
+    w = bits(np.full((l, N), 1.0 / l))
+    got = oracle.compress(x, w, np.cumsum(lens), l, d)
+    xf = oracle.bf16_to_f64(x)
+    ref = []
+    for s, T in zip(starts_of(lens), lens):
+        nb = T // l
+        ref.append(xf[s:s + nb * l].reshape(nb, l, N, D).mean(axis=1))
+    ref = np.concatenate(ref)
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("l,d", [(32, 16), (48, 16), (64, 32), (16, 16)])
+def test_compress_impulse_response(l, d):
+    """A single 1 at row r of head n, column e reaches output i exactly when
+    row r lies in window i (rows i*d .. i*d+l-1), with the weight of its
+    position in the window, and nowhere else -- not across sequences."""
+    rng = np.random.default_rng(2)
+    lens = [l + 3 * d + 5, l + d]
+    N, D = 2, 3
+    T = sum(lens)
+    w = rand_bf16(rng, (l, N))
+    wf = oracle.bf16_to_f64(w)
+    starts = starts_of(lens)
+    outs_per = [oracle.n_cmp(t, l, d) for t in lens]
+    out_starts = np.concatenate([[0], np.cumsum(outs_per)[:-1]])
+    for r in [0, 1, d, l - 1, l, lens[0] - 1, lens[0], T - 1]:
+        n, e = r % N, (r * 7) % D
+        xf = np.zeros((T, N, D))
+        xf[r, n, e] = 1.0
+        got = oracle.compress(bits(xf), w, np.cumsum(lens), l, d)
+        expect = np.zeros_like(got)
+        b = int(np.searchsorted(np.cumsum(lens), r, side="right"))
+        rl = r - starts[b]
+        for i in range(outs_per[b]):
+            p = rl - i * d
+            if 0 <= p < l:
+                expect[out_starts[b] + i, n, e] = wf[p, n]
+        assert np.array_equal(got, expect), f"impulse at row {r}"
+
+
+def test_compress_constant_rows():
+    """Rows constant along the sequence: every output is (sum_p w[p,n]) * c[n]."""
+    rng = np.random.default_rng(3)
+    l, d, N, D = 32, 16, 4, 6
+    lens = [200, 77]
+    c = np.array([1.5, -2.0, 0.25, 3.0])
+    xf = np.broadcast_to(c[None, :, None], (sum(lens), N, D))
+    w = rand_bf16(rng, (l, N))
+    got = oracle.compress(bits(xf), w, np.cumsum(lens), l, d)
+    expect = oracle.bf16_to_f64(w).sum(axis=0)[None, :, None] * c[None, :, None]
+    np.testing.assert_allclose(got, np.broadcast_to(expect, got.shape), rtol=1e-13)
+
+
+def test_compress_is_linear():
+    """compress(2x + y) = 2 compress(x) + compress(y) on small integers (exact)."""
+    rng = np.random.default_rng(4)
+    l, d, N, D = 32, 16, 2, 4
+    lens = [150]
+    xf = rng.integers(-8, 9, (150, N, D)).astype(np.float64)
+    yf = rng.integers(-8, 9, (150, N, D)).astype(np.float64)
+    w = bits(rng.integers(0, 4, (l, N)) / 4.0)
+    a = oracle.compress(bits(2 * xf + yf), w, lens, l, d)
+    b = 2 * oracle.compress(bits(xf), w, lens, l, d) + oracle.compress(bits(yf), w, lens, l, d)
+    assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------
+# Steps 1-3: scaled scores, mask, softmax, output
+# --------------------------------------------------------------------------
+
+def _attention_case(seed, lens, N1, N2, D1, D2, l, d, kv_std=1.0):
+    rng = np.random.default_rng(seed)
+    T = sum(lens)
+    T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
+    q = rand_bf16(rng, (T, N1, D1))
+    kc = rand_bf16(rng, (T2, N2, D1), kv_std)
+    vc = rand_bf16(rng, (T2, N2, D2), kv_std)
+    return q, kc, vc
+
+
+def test_attention_matches_torch_sdpa():
+    """Rows with at least one visible block equal torch's scaled dot-product
+    attention (float64, boolean mask built from the visibility rule);
+    softmax max and sum equal torch's masked max and exp(logsumexp - max)."""
+    lens = [40, 77, 130, 31]
+    N1, N2, D1, D2, l, d, lsel, count = 6, 2, 16, 8, 32, 16, 64, 2
+    scale = 0.3
+    q, kc, vc = _attention_case(5, lens, N1, N2, D1, D2, l, d)
+    res = run_all(q, kc, vc, lens, N1, N2, scale, l, d, lsel, count)
+    qf, kf, vf = (torch.from_numpy(oracle.bf16_to_f64(a)) for a in (q, kc, vc))
+    actc = oracle.cmp_prefix(lens, l, d)
+    cstarts = np.concatenate([[0], actc[:-1]])
+    G = N1 // N2
+    for b, (s, T) in enumerate(zip(starts_of(lens), lens)):
+        nc = int(actc[b] - cstarts[b])
+        if nc == 0:
+            continue
+        t = torch.arange(T)[:, None]
+        i = torch.arange(nc)[None, :]
+        mask = (i * d + l - 1) <= t                      # [T, nc]
+        has = mask.any(dim=1)
+        for h in range(N1):
+            g = h // G
+            qb = qf[s:s + T, h]
+            kb = kf[cstarts[b]:cstarts[b] + nc, g]
+            vb = vf[cstarts[b]:cstarts[b] + nc, g]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qb[None, None], kb[None, None], vb[None, None], attn_mask=mask[None, None],
+                scale=scale)[0, 0]
+            got = torch.from_numpy(res["out"][s:s + T, h])
+            torch.testing.assert_close(got[has], ref[has], rtol=1e-12, atol=1e-13)
+            sc = torch.where(mask, scale * (qb @ kb.T), torch.tensor(-float("inf"), dtype=torch.float64))
+            mx = sc.max(dim=1).values
+            lse = torch.logsumexp(sc, dim=1)
+            torch.testing.assert_close(torch.from_numpy(res["max"][s:s + T, h])[has], mx[has],
+                                       rtol=1e-13, atol=1e-13)
+            torch.testing.assert_close(torch.from_numpy(res["sum"][s:s + T, h])[has],
+                                       torch.exp(lse - mx)[has], rtol=1e-12, atol=0)
+
+
+def _identity_value_case(lens, N1, N2, D1, l, d, seed=6, scale=0.5):
+    """Values are unit vectors: output row h of token t is P_cmp itself."""
+    T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
+    actc = oracle.cmp_prefix(lens, l, d)
+    n_cmp_max = int(max(np.diff(np.concatenate([[0], actc]))))
+    D2 = max(n_cmp_max, 1)
+    rng = np.random.default_rng(seed)
+    q = rand_bf16(rng, (sum(lens), N1, D1))
+    kc = rand_bf16(rng, (T2, N2, D1))
+    vcf = np.zeros((T2, N2, D2))
+    for s, e in zip(np.concatenate([[0], actc[:-1]]), actc):
+        for i in range(int(e - s)):
+            vcf[s + i, :, i] = 1.0
+    return q, kc, bits(vcf), D2, scale
+
+
+def test_softmax_rows_sum_to_one():
+    """With unit-vector values the output is P_cmp; each row with a visible
+    block sums to 1 and equals scipy's softmax of the masked scores."""
+    from scipy.special import softmax
+    lens = [200, 95]
+    N1, N2, D1, l, d = 4, 2, 8, 32, 16
+    q, kc, vc, D2, scale = _identity_value_case(lens, N1, N2, D1, l, d)
+    res = run_all(q, kc, vc, lens, N1, N2, scale, l, d, 64, 4)
+    qf, kf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(kc)
+    actc = oracle.cmp_prefix(lens, l, d)
+    cst = np.concatenate([[0], actc[:-1]])
+    for b, (s, T) in enumerate(zip(starts_of(lens), lens)):
+        nc = int(actc[b] - cst[b])
+        for t in range(T):
+            nv = n_vis_of(t, l, d, nc)
+            for h in range(N1):
+                P = res["out"][s + t, h]
+                if nv == 0:
+                    assert np.all(P == 0)
+                    continue
+                assert abs(P.sum() - 1.0) < 1e-13
+                assert np.all(P[nv:] == 0)
+                sc = scale * (kf[cst[b]:cst[b] + nv, h // (N1 // N2)] @ qf[s + t, h])
+                np.testing.assert_allclose(P[:nv], softmax(sc), rtol=1e-12, atol=1e-15)
+
+
+def test_identical_keys_closed_form():
+    """All compressed keys equal: scores are equal, so the output is the mean
+    of the visible values, the softmax sum is n_vis and the max is
+    scale * <q, k>."""
+    rng = np.random.default_rng(7)
+    lens = [300, 64]
+    N1, N2, D1, D2, l, d = 4, 1, 8, 8, 32, 16
+    T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
+    q = rand_bf16(rng, (sum(lens), N1, D1))
+    k1 = oracle.bf16_to_f64(rand_bf16(rng, (D1,)))
+    kc = bits(np.broadcast_to(k1, (T2, N2, D1)))
+    vc = rand_bf16(rng, (T2, N2, D2))
+    scale = 0.25
+    res = run_all(q, kc, vc, lens, N1, N2, scale, l, d, 64, 4)
+    qf, vf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(vc)
+    actc = oracle.cmp_prefix(lens, l, d)
+    cst = np.concatenate([[0], actc[:-1]])
+    for b, (s, T) in enumerate(zip(starts_of(lens), lens)):
+        nc = int(actc[b] - cst[b])
+        for t in range(T):
+            nv = n_vis_of(t, l, d, nc)
+            for h in range(N1):
+                if nv == 0:
+                    assert np.all(res["out"][s + t, h] == 0)
+                    assert res["max"][s + t, h] == -np.inf and res["sum"][s + t, h] == 0
+                    continue
+                np.testing.assert_allclose(res["out"][s + t, h], vf[cst[b]:cst[b] + nv, 0].mean(axis=0),
+                                           rtol=1e-12, atol=1e-14)
+                assert abs(res["sum"][s + t, h] - nv) < 1e-12 * nv
+                assert abs(res["max"][s + t, h] - scale * float(qf[s + t, h] @ k1)) < 1e-13
+
+
+def test_single_visible_block_and_empty_rows():
+    """Tokens l-1 .. l+d-2 see only block 0: output = v_0, sum = 1,
+    max = s_0.  Tokens before l-1 see nothing: output 0, max -inf, sum 0."""
+    lens = [96]
+    N1, N2, D1, D2, l, d = 2, 1, 8, 4, 32, 16
+    q, kc, vc = _attention_case(8, lens, N1, N2, D1, D2, l, d)
+    scale = 0.7
+    res = run_all(q, kc, vc, lens, N1, N2, scale, l, d, 64, 2)
+    qf, kf, vf = (oracle.bf16_to_f64(a) for a in (q, kc, vc))
+    for t in range(l - 1):
+        assert np.all(res["out"][t] == 0)
+        assert np.all(res["max"][t] == -np.inf) and np.all(res["sum"][t] == 0)
+    for t in range(l - 1, l + d - 1):
+        for h in range(N1):
+            assert np.array_equal(res["out"][t, h], vf[0, 0])
+            assert res["sum"][t, h] == 1.0
+            assert abs(res["max"][t, h] - scale * float(qf[t, h] @ kf[0, 0])) < 1e-14
+    assert not np.array_equal(res["out"][l + d - 1, 0], vf[0, 0])
+
+
+def test_gqa_head_to_group_mapping():
+    """Query head h reads KV head floor(h / G): make KV head 1's values a
+    constant, so exactly heads G..2G-1 output that constant."""
+    rng = np.random.default_rng(9)
+    lens = [120]
+    N1, N2, D1, D2, l, d = 6, 2, 8, 4, 32, 16
+    G = N1 // N2
+    T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
+    q = rand_bf16(rng, (120, N1, D1))
+    kc = rand_bf16(rng, (T2, N2, D1))
+    vcf = oracle.bf16_to_f64(rand_bf16(rng, (T2, N2, D2)))
+    vcf[:, 1, :] = 0.625
+    res = run_all(q, kc, bits(vcf), lens, N1, N2, 0.4, l, d, 64, 2)
+    for t in range(l - 1, 120):
+        for h in range(N1):
+            is_const = np.allclose(res["out"][t, h], 0.625, rtol=1e-14, atol=0)
+            assert is_const == (h // G == 1), (t, h)
+
+
+# --------------------------------------------------------------------------
+# Steps 4-5: importance-score remap and the sum over a KV-head group
+# --------------------------------------------------------------------------
+
+def _load_coefficients():
+    rows = {}
+    with open(os.path.join(GOLDEN, "remap_coefficients.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if not line:
+                continue
+            l, d, lsel, R, L2, *c = map(int, line)
+            rows[(l, d, lsel)] = (R, L2, c)
+    return rows
+
+
+COEFFS = _load_coefficients()
+
+
+def _p_and_pslc(lens, N1, N2, l, d, lsel, seed=10):
+    """Oracle P_cmp (through unit-vector values) and its P_slc'."""
+    q, kc, vc, D2, scale = _identity_value_case(lens, N1, N2, 8, l, d, seed=seed, scale=0.9)
+    actc = oracle.cmp_prefix(lens, l, d)
+    res = run_all(q, kc, vc, lens, N1, N2, scale, l, d, lsel, 3)
+    return res, actc
+
+
+@pytest.mark.parametrize("l,d,lsel", sorted(COEFFS))
+def test_remap_scatter_form(l, d, lsel):
+    """Scatter form: every compressed block i adds P_cmp[i] to select block
+    j = (i + m + n) / R for each (m, n) that makes it an integer -- the
+    page's gather sum read the other way round; summed over the group's
+    heads."""
+    lens = [23 * d + l, 7 * d + l + 3]
+    N1, N2 = 4, 2
+    G = N1 // N2
+    R, L2 = lsel // d, l // d
+    res, actc = _p_and_pslc(lens, N1, N2, l, d, lsel)
+    cst = np.concatenate([[0], actc[:-1]])
+    for b, (s, T) in enumerate(zip(starts_of(lens), lens)):
+        nc = int(actc[b] - cst[b])
+        S = -(-T // lsel)
+        for t in range(T):
+            for g in range(N2):
+                acc = np.zeros(S + R + L2 + 2)
+                for h in range(g * G, (g + 1) * G):
+                    P = res["out"][s + t, h, :nc]
+                    for i in range(nc):
+                        for m in range(R):
+                            for n in range(L2):
+                                if (i + m + n) % R == 0:
+                                    acc[(i + m + n) // R] += P[i]
+                np.testing.assert_allclose(res["pslc"][s + t, g, :S], acc[:S], rtol=1e-13, atol=1e-15)
+                assert np.all(res["pslc"][s + t, g, S:] == 0)
+
+
+@pytest.mark.parametrize("l,d,lsel", sorted(COEFFS))
+def test_remap_hand_derived_coefficients(l, d, lsel):
+    """Stencil form with the coefficient table derived by hand (golden file):
+    P_slc'[j] = sum_r c(r) * sum_h P_cmp^h[R*j - r]."""
+    R, L2, c = COEFFS[(l, d, lsel)]
+    assert R == lsel // d and L2 == l // d
+    lens = [17 * d + l + 5]
+    N1, N2 = 2, 1
+    res, actc = _p_and_pslc(lens, N1, N2, l, d, lsel, seed=11)
+    nc = int(actc[0])
+    S = -(-lens[0] // lsel)
+    for t in range(lens[0]):
+        Psum = res["out"][t, :, :nc].sum(axis=0)
+        for j in range(S):
+            ref = sum(cr * Psum[R * j - r] for r, cr in enumerate(c) if 0 <= R * j - r < nc)
+            assert abs(res["pslc"][t, 0, j] - ref) <= 1e-13 * max(1.0, abs(ref))
+
+
+def test_remap_mass_invariant():
+    """Each compressed block is counted floor(l/d) times over all select
+    blocks, so a row whose remap stays inside the select range has
+    sum_j P_slc'[j] = G * floor(l/d) (softmax rows sum to 1)."""
+    wl = synth.small_variant(2, [700, 333])
+    inp = synth.make_inputs(wl)
+    b = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    res = oracle.run(wl, b["q"], b["k"], b["v"], b["w"])
+    R, L2 = wl.lsel // wl.d, wl.l // wl.d
+    H = R + L2 - 2
+    G = wl.N1 // wl.N2
+    actc = oracle.cmp_prefix(wl.seqlens, wl.l, wl.d)
+    cst = np.concatenate([[0], actc[:-1]])
+    checked = 0
+    for bi, (s, T) in enumerate(zip(starts_of(wl.seqlens), wl.seqlens)):
+        nc = int(actc[bi] - cst[bi])
+        S = -(-T // wl.lsel)
+        for t in range(T):
+            nv = n_vis_of(t, wl.l, wl.d, nc)
+            if nv == 0 or (nv - 1 + H) // R >= S:
+                continue
+            sums = res["pslc"][s + t].sum(axis=1)
+            np.testing.assert_allclose(sums, G * L2, rtol=1e-12)
+            checked += 1
+    assert checked > 500
+
+
+def test_remap_identical_keys_closed_form():
+    """Identical keys make P_cmp uniform, 1/n_vis on the visible blocks, so
+    P_slc'[j] = G * sum_r c(r) [0 <= R*j - r < n_vis] / n_vis."""
+    rng = np.random.default_rng(12)
+    l, d, lsel = 32, 16, 64
+    R, L2, c = COEFFS[(l, d, lsel)]
+    lens = [400]
+    N1, N2 = 8, 2
+    G = N1 // N2
+    T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
+    q = rand_bf16(rng, (400, N1, 8))
+    kc = bits(np.broadcast_to(oracle.bf16_to_f64(rand_bf16(rng, (8,))), (T2, N2, 8)))
+    vc = rand_bf16(rng, (T2, N2, 4))
+    res = run_all(q, kc, vc, lens, N1, N2, 0.3, l, d, lsel, 4)
+    S = -(-400 // lsel)
+    for t in range(400):
+        nv = n_vis_of(t, l, d, T2)
+        for j in range(S):
+            ref = 0.0 if nv == 0 else G * sum(cr for r, cr in enumerate(c) if 0 <= R * j - r < nv) / nv
+            for g in range(N2):
+                assert abs(res["pslc"][t, g, j] - ref) <= 1e-12 * max(1.0, ref)
+
+
+# --------------------------------------------------------------------------
+# Steps 6-7: top-k mask and top-k
+# --------------------------------------------------------------------------
+
+def _check_topk_brute(res, lens, lsel, count):
+    for s, T in zip(starts_of(lens), lens):
+        S = -(-T // lsel)
+        for t in range(T):
+            for g in range(res["pslc"].shape[1]):
+                valid = np.array([j for j in range(S) if j * lsel <= t])
+                keys = res["pslc"][s + t, g, valid].astype(np.float32)
+                order = valid[np.lexsort((valid, -keys))]     # score desc, index asc
+                expect = np.full(count, -1, dtype=np.int32)
+                expect[:min(count, len(order))] = order[:count]
+                assert np.array_equal(res["topk"][s + t, g], expect), (s + t, g)
+
+
+def test_topk_matches_brute_force_sort_tiny_workload():
+    """Full sort (numpy lexsort on float32 scores) of the candidates of each
+    row, on the tiny workload."""
+    wl = synth.WORKLOADS[0]
+    inp = synth.make_inputs(wl)
+    b = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    res = oracle.run(wl, b["q"], b["k"], b["v"], b["w"])
+    _check_topk_brute(res, wl.seqlens, wl.lsel, wl.count)
+
+
+def test_topk_brute_force_gqa_varlen():
+    wl = dataclasses.replace(synth.small_variant(4, [640, 300]), N1=8, D1=16, D2=16)
+    inp = synth.make_inputs(wl)
+    b = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    res = oracle.run(wl, b["q"], b["k"], b["v"], b["w"])
+    _check_topk_brute(res, wl.seqlens, wl.lsel, wl.count)
+
+
+def test_topk_forced_when_few_candidates():
+    """With at most `count` candidates every candidate is picked, whatever
+    the scores; the rest are -1."""
+    wl = synth.WORKLOADS[0]
+    inp = synth.make_inputs(wl)
+    b = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    res = oracle.run(wl, b["q"], b["k"], b["v"], b["w"])
+    for t in range(wl.count * wl.lsel):
+        nvalid = t // wl.lsel + 1
+        picks = res["topk"][t, 0]
+        assert sorted(picks[:nvalid].tolist()) == list(range(nvalid))
+        assert np.all(picks[nvalid:] == -1)
+    assert np.array_equal(res["topk"][0, 0], [0, -1, -1, -1])
+
+
+def test_topk_ties_go_to_lower_index():
+    """Identical keys make interior importance scores exactly equal; the picks
+    are the candidates sorted by (score desc, index asc) -- numpy lexsort."""
+    rng = np.random.default_rng(13)
+    l, d, lsel, count = 32, 16, 64, 4
+    lens = [640]
+    N1, N2 = 4, 1
+    T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
+    q = rand_bf16(rng, (640, N1, 8))
+    kc = bits(np.broadcast_to(oracle.bf16_to_f64(rand_bf16(rng, (8,))), (T2, N2, 8)))
+    vc = rand_bf16(rng, (T2, N2, 4))
+    res = run_all(q, kc, vc, lens, N1, N2, 0.3, l, d, lsel, count)
+    ties = 0
+    for t in range(640):
+        row = res["pslc"][t, 0, : t // lsel + 1].astype(np.float32)
+        ties += len(row) - len(np.unique(row))
+    assert ties > 100
+    _check_topk_brute(res, lens, lsel, count)

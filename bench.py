@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the compressed NSA branch on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input resident in
+HBM: compress K, compress V (nsa_compress), compressed attention
+(nsa_compress_attention_fwd: scores, mask, softmax, P.V) and the importance
+scores + top-k (nsa_compress_attention_select).  W untimed warm-up steps,
+then K timed steps bracketed by synchronisations; HIP events recorded on the
+launch stream between the four calls give each kernel's duration inside the
+same timed region.
+
+Prints one JSON line.  ``value`` is query tokens per second of the whole
+step; the roofline object is for the dominant kernel (the attention
+kernel, bound by bf16 MFMA); ``cpu_baseline`` times the CPU oracle on a
+bounded random sample of the same workload's tokens.
+
+    python bench.py [--steps K] [--warmup W] [--workload 0..4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/sec (compress+attn+topk); TFLOP/s as % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def n_visible(t: np.ndarray, l: int, d: int, n_cmp: int) -> np.ndarray:
+    n = np.where(t >= l - 1, (t - l + 1) // d + 1, 0)
+    return np.minimum(n, n_cmp)
+
+
+def workload_work(wl, T2: int) -> dict:
+    """Algorithmic work of one step (bookkeeping for the report)."""
+    vis = 0
+    for T in wl.seqlens:
+        nc = (T - wl.l) // wl.d + 1 if T >= wl.l else 0
+        vis += int(n_visible(np.arange(T), wl.l, wl.d, nc).sum())
+    attn_flops = 2.0 * (wl.D1 + wl.D2) * vis * wl.N1
+    comp_flops = 2.0 * wl.l * T2 * wl.N2 * (wl.D1 + wl.D2)
+    bytes_ck = 2.0 * (wl.T + T2) * wl.N2 * wl.D1
+    bytes_cv = 2.0 * (wl.T + T2) * wl.N2 * wl.D2
+    bytes_attn = (2.0 * wl.T * wl.N1 * (wl.D1 + wl.D2) + 2.0 * T2 * wl.N2 * (wl.D1 + wl.D2)
+                  + 2 * 32.0 * wl.T * wl.N1)
+    bytes_sel = (2.0 * wl.T * wl.N1 * wl.D1 + 2.0 * T2 * wl.N2 * wl.D1 + 8.0 * wl.T * wl.N1
+                 + 4.0 * wl.T * wl.N2 * wl.count)
+    return {"visible_pairs": vis, "attn_flops": attn_flops, "compress_flops": comp_flops,
+            "bytes_compress_k": bytes_ck, "bytes_compress_v": bytes_cv,
+            "bytes_attn": bytes_attn, "bytes_select": bytes_sel}
+
+
+def cpu_baseline(wl, inp, budget_s: float) -> dict:
+    """The oracle, as it is, on this host: full compression of K and V plus
+    attention/remap/top-k on a seeded uniform sample of tokens, scaled to the
+    whole workload's token count."""
+    import oracle
+    import synth
+    kb, vb, wb = synth.bf16_bits(inp["k"]), synth.bf16_bits(inp["v"]), synth.bf16_bits(inp["w"])
+    actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
+    t0 = time.perf_counter()
+    kc = oracle.to_bf16(oracle.compress(kb, wb, actq, wl.l, wl.d))
+    vc = oracle.to_bf16(oracle.compress(vb, wb, actq, wl.l, wl.d))
+    t_comp = time.perf_counter() - t0
+    actc = oracle.cmp_prefix(wl.seqlens, wl.l, wl.d)
+    rng = np.random.default_rng(1234)
+    import torch
+
+    def attn(tokens):
+        q_rows = synth.bf16_bits(inp["q"][torch.from_numpy(tokens).to(inp["q"].device)])
+        t = time.perf_counter()
+        oracle.attention(q_rows, tokens, kc, vc, actq, actc, wl.N1, wl.N2, wl.scale, wl.l, wl.d,
+                         wl.lsel, wl.count)
+        return time.perf_counter() - t
+
+    pilot = np.sort(rng.choice(wl.T, min(wl.T, 32), replace=False)).astype(np.int64)
+    t_pilot = attn(pilot)
+    n = int(min(wl.T, max(32, len(pilot) * max(0.0, budget_s - t_comp) / max(t_pilot, 1e-6))))
+    sample = np.sort(rng.choice(wl.T, n, replace=False)).astype(np.int64)
+    t_att = attn(sample)
+    est = t_comp + t_att * wl.T / n
+    return {"value": wl.T / est, "unit": "query tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": (f"compression of all K/V ({t_comp:.2f} s) + attention/remap/top-k for {n} of "
+                       f"{wl.T} tokens drawn uniformly ({t_att:.2f} s), scaled to all tokens"),
+            "seconds_measured": round(t_comp + t_att, 3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, choices=range(5))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the path runs on a single MI355X and this build has no "
+              f"multi-GPU leg (asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    import kv_compression_block_amd as nsa
+    from kv_compression_block_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from kv_compression_block_amd import build as _build
+        _build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(wl, device=dev, chunk_rows=16384)
+    c_pre, s_pre, pc, ps = [], [], 0, 0
+    for T in wl.seqlens:
+        pc += nsa.nsa_compress_out_len(T, wl.l, wl.d)
+        ps += -(-T // wl.lsel)
+        c_pre.append(pc)
+        s_pre.append(ps)
+    T2 = pc
+    plan = nsa.nsa_compress_attention_get_workspace(wl.act_seq_qlen, c_pre, s_pre, wl.N1, wl.N2, wl.D1,
+                                                    wl.D2, wl.scale, wl.l, wl.d, wl.lsel, wl.count)
+    kc = torch.empty((T2, wl.N2, wl.D1), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty((T2, wl.N2, wl.D2), dtype=torch.bfloat16, device=dev)
+    outs = {"attention_out": torch.empty((wl.T, wl.N1, wl.D2), dtype=torch.bfloat16, device=dev),
+            "topk_indices": torch.empty((wl.T, wl.N2, wl.count), dtype=torch.int32, device=dev),
+            "softmax_max": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev),
+            "softmax_sum": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev)}
+    ws = torch.empty((max(plan.workspace_bytes, 1),), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nsa.nsa_compress(inp["k"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=kc, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nsa.nsa_compress(inp["v"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=vc, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc, workspace=ws, outputs=outs, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        nsa.nsa_compress_attention_select(plan, inp["q"], kc, outs["softmax_max"], outs["softmax_sum"],
+                                          workspace=ws, outputs=outs, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    names = ["compress_k", "compress_v", "attention", "select_topk"]
+    per = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
+           for j, n in enumerate(names)}
+    work = workload_work(wl, T2)
+    value = wl.T / (ms_step / 1e3)
+    total_flops = work["attn_flops"] + work["compress_flops"]
+    attn_s = per["attention"] / 1e3
+    attn_tflops = work["attn_flops"] / attn_s / 1e12
+    kernels = {
+        "compress_k": {"ms": per["compress_k"], "GB/s": work["bytes_compress_k"] / (per["compress_k"] / 1e3) / 1e9},
+        "compress_v": {"ms": per["compress_v"], "GB/s": work["bytes_compress_v"] / (per["compress_v"] / 1e3) / 1e9},
+        "attention": {"ms": per["attention"], "TFLOP/s": attn_tflops, "mfma_frac": attn_tflops / PEAK_BF16_TFLOPS},
+        "select_topk": {"ms": per["select_topk"],
+                        "GB/s": work["bytes_select"] / (per["select_topk"] / 1e3) / 1e9},
+    }
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "N1": wl.N1, "N2": wl.N2, "D1": wl.D1,
+                   "D2": wl.D2, "l": wl.l, "d": wl.d, "lsel": wl.lsel, "count": wl.count,
+                   "scale": wl.scale, "parallelism": "single-gpu"},
+        "tflops_algorithmic": total_flops / (ms_step / 1e3) / 1e12,
+        "frac_of_bf16_peak": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": "k_cmp_attn_fwd", "bound": "mfma", "achieved": attn_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None,
+                     "work_per_launch": f"{work['attn_flops']:.4e} flop = 2*(D1+D2) x {work['visible_pairs']} "
+                                        f"visible (token, block) pairs x {wl.N1} heads"},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    plan.destroy()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,237 @@
+/*
+ * nsa_cmp.h -- C ABI of the MI355X (gfx950) library for the compressed branch
+ * of Native Sparse Attention (NSA): compression of K/V, compressed attention,
+ * the importance-score remap and the per-(token, KV head) top-k.
+ *
+ * The operations are the ones two operator pages define:
+ *   - "aclnnNsaCompress" (CANN operator page), section "Formula", for
+ *     nsa_compress;
+ *   - "mindspore.ops.nsa_compress_attention" (MindSpore operator page),
+ *     steps 1-7, parameters and returns, for nsa_compress_attention.
+ * The call pattern follows the CANN page's two phases: a first call that
+ * validates every argument and returns the workspace size (together with a
+ * reusable "plan", the executor of that page), and a second call that
+ * computes.  Validation failures come back as status codes.
+ *
+ * Conventions shared by every entry point
+ *   - Layout is TND: tokens of all sequences back to back, then heads, then
+ *     the head dim (contiguous).  Sequence lengths are passed as host arrays
+ *     of prefix sums (cumulative counts, one entry per sequence, the last one
+ *     equal to the total), as both pages require.
+ *   - Device pointers are caller-owned device memory; the library never
+ *     allocates, frees or retains them beyond the call.  Tensors must be
+ *     contiguous and 16-byte aligned (topk_indices 4-byte aligned).
+ *   - Host arrays are read only during the call that receives them.
+ *   - GPU work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream) and the library never synchronises: a call returns once its
+ *     launches are enqueued.  Launch errors are reported as NSA_ERR_HIP; an
+ *     error inside a kernel surfaces at the caller's next synchronisation.
+ *   - A status other than NSA_OK means nothing was enqueued.  The reason is
+ *     available from nsa_last_error() on the calling thread.
+ *   - Results are deterministic: the same inputs give bitwise identical
+ *     outputs (no floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef NSA_CMP_H
+#define NSA_CMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nsa_status {
+    NSA_OK = 0,
+    NSA_ERR_NULLPTR = 1,      /* a required pointer is NULL */
+    NSA_ERR_DTYPE = 2,        /* dtype code not recognised (Python: TypeError) */
+    NSA_ERR_SHAPE = 3,        /* sizes / prefix sums inconsistent (Python: ValueError) */
+    NSA_ERR_CONSTRAINT = 4,   /* a documented parameter constraint fails (ValueError) */
+    NSA_ERR_WORKSPACE = 5,    /* workspace missing or too small */
+    NSA_ERR_UNSUPPORTED = 6,  /* legal on the pages, not built here (never a silent fallback) */
+    NSA_ERR_HIP = 7           /* the HIP runtime refused a copy or a launch */
+} nsa_status;
+
+/* Element types of q/k/v and of the outputs that carry them.  Both pages
+ * allow float16 and bfloat16; this build computes bfloat16 and answers
+ * NSA_ERR_UNSUPPORTED for float16. */
+typedef enum nsa_dtype {
+    NSA_DTYPE_BF16 = 0,
+    NSA_DTYPE_FP16 = 1
+} nsa_dtype;
+
+/* Opaque, reusable handle produced by the first phase of the attention
+ * operator (the CANN page's "executor").  Read-only while executing, so one
+ * plan may serve several streams at once.  Free with nsa_plan_destroy. */
+typedef struct nsa_plan_s* nsa_plan;
+
+/* Number of compressed entries of a sequence of length seq_len: the window
+ * index i runs over 0 .. floor((seq_len - l) / d), so this is
+ * floor((seq_len - l) / d) + 1, or 0 when seq_len < l ("aclnnNsaCompress",
+ * Formula).  Returns -1 when l < 1, d < 1 or seq_len < 0. */
+int64_t nsa_compress_out_len(int64_t seq_len, int64_t compress_block_size,
+                             int64_t compress_stride);
+
+/*
+ * nsa_compress -- "aclnnNsaCompress", Formula: for every sequence and every
+ * window i, output[i, n, :] = sum_{p < l} weight[p, n] * input[i*d + p, n, :]
+ * (rows counted from the sequence start; the page's 1-based window
+ * k_{id+1 : id+l}), accumulated in float32 in ascending p and rounded once
+ * to the output dtype (nearest, ties to even).
+ *
+ *   input          [total_tokens, num_heads, head_dim], device
+ *   weight         [compress_block_size, num_heads], device, same dtype as
+ *                  input (one scalar per window position and head, broadcast
+ *                  over the head dim)
+ *   act_seq_len    host, batch prefix sums of the token counts; non-empty,
+ *                  non-decreasing, last entry == total_tokens
+ *   output         [output_tokens, num_heads, head_dim], device;
+ *                  output_tokens must equal sum_b nsa_compress_out_len(T_b).
+ *                  May be NULL only when output_tokens == 0.
+ *   stream         hipStream_t
+ *
+ * Constraints (CANN page, constraints list; its names are garbled in the
+ * copy these comments were written from, so the reading is stated):
+ * compress_block_size (l) a multiple of 16 in [16, 128]; compress_stride (d)
+ * a multiple of 16 with 16 <= d <= l; head_dim a multiple of 16, <= 256;
+ * num_heads >= 1.
+ * Errors: NSA_ERR_NULLPTR, NSA_ERR_DTYPE, NSA_ERR_SHAPE (prefix sums or
+ * output_tokens inconsistent), NSA_ERR_CONSTRAINT, NSA_ERR_UNSUPPORTED
+ * (float16), NSA_ERR_HIP.
+ */
+nsa_status nsa_compress(const void* input, const void* weight,
+                        const int64_t* act_seq_len, int64_t batch,
+                        int64_t total_tokens, int64_t num_heads, int64_t head_dim,
+                        int64_t compress_block_size, int64_t compress_stride,
+                        nsa_dtype dtype, void* output, int64_t output_tokens,
+                        void* stream);
+
+/*
+ * nsa_compress_attention_get_workspace -- first phase of
+ * "mindspore.ops.nsa_compress_attention".  Host only: validates, derives the
+ * per-sequence extents, plans the launches and returns the workspace size
+ * and a plan.  Touches no device state.
+ *
+ *   batch                 number of sequences B >= 1
+ *   act_seq_qlen          host [B] prefix sums of the query token counts T_b
+ *   act_cmp_seq_kvlen     host [B] prefix sums of the compressed counts;
+ *                         entry b must equal floor((T_b - l)/d) + 1 (0 if T_b < l)
+ *   act_sel_seq_kvlen     host [B] prefix sums of the select-block counts;
+ *                         entry b must equal ceil(T_b / l')
+ *   head_num, kv_head_num N1 and N2: N1 >= N2 >= 1, N1 % N2 == 0
+ *   d1, d2                q/k and v head dims: multiples of 16, d1 >= d2
+ *   scale_value           finite float multiplying q.k^T
+ *   compress_block_size   l: multiple of 16 in [16, 128]
+ *   compress_stride       d: multiple of 16 in [16, 64], d <= l
+ *   select_block_size     l': multiple of 16 in [16, 128], l' >= l, l' % d == 0
+ *   select_block_count    k: in [1, 32]
+ *   dtype                 element type of q/k/v/out
+ *   workspace_bytes       out: bytes of device workspace the second phase needs
+ *   plan_out              out: the plan (caller frees it)
+ *
+ * Errors: NSA_ERR_NULLPTR, NSA_ERR_DTYPE, NSA_ERR_SHAPE, NSA_ERR_CONSTRAINT,
+ * NSA_ERR_UNSUPPORTED (float16; head dims outside {64,128,192} x {64,128};
+ * N1/N2 > 64; more than 1024 select blocks in one sequence).  On error
+ * *plan_out is set to NULL.
+ */
+nsa_status nsa_compress_attention_get_workspace(
+    int64_t batch, const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen,
+    const int64_t* act_sel_seq_kvlen, int64_t head_num, int64_t kv_head_num,
+    int64_t d1, int64_t d2, float scale_value, int64_t compress_block_size,
+    int64_t compress_stride, int64_t select_block_size, int64_t select_block_count,
+    nsa_dtype dtype, size_t* workspace_bytes, nsa_plan* plan_out);
+
+/*
+ * nsa_compress_attention -- second phase: steps 1-7 of
+ * "mindspore.ops.nsa_compress_attention".
+ *   1. QK = scale_value * query . key^T, masked: compressed block i is
+ *      visible to the query at local position t iff i*d + l - 1 <= t;
+ *   2. P_cmp = softmax over the visible blocks (natural base);
+ *   3. attention_out = P_cmp . value;
+ *   4. P_slc[j] = sum_{m < l'/d} sum_{n < l/d} P_cmp[(l'/d) j - m - n]
+ *      (indices outside the sequence's compressed range add 0);
+ *   5. P_slc' = sum of P_slc over the N1/N2 query heads of each KV head
+ *      (query head h belongs to KV head floor(h / (N1/N2)));
+ *   6. top-k mask: select block j is a candidate iff j*l' <= t;
+ *   7. topk_indices = the select_block_count candidates with the largest
+ *      P_slc' (descending; ties to the lower j), -1 in unused slots.
+ *
+ *   query          [T1, N1, d1] device
+ *   key, value     [T2, N2, d1], [T2, N2, d2] device (T2 = last cmp prefix sum)
+ *   attention_out  [T1, N1, d2] device; rows with no visible block are 0
+ *   topk_indices   [T1, N2, select_block_count] int32 device
+ *   softmax_max    [T1, N1, 8] float32 device: max of the scaled, masked
+ *                  scores (all 8 slots equal; -inf when nothing is visible)
+ *   softmax_sum    [T1, N1, 8] float32 device: sum of exp(score - max)
+ *                  (all 8 slots equal; 0 when nothing is visible)
+ *   p_slc_debug    NULL, or [T1, N2, S] float32 device with S the largest
+ *                  select-block count of any sequence: P_slc' before the
+ *                  top-k mask, 0 beyond the sequence's own count
+ *   workspace      device, >= the size phase one returned (may be NULL if 0)
+ *   stream         hipStream_t
+ *
+ * The plan fixes every size; the pointers must describe tensors of those
+ * sizes.  Errors: NSA_ERR_NULLPTR, NSA_ERR_WORKSPACE, NSA_ERR_CONSTRAINT
+ * (misaligned pointer), NSA_ERR_HIP.
+ */
+nsa_status nsa_compress_attention(nsa_plan plan, const void* query, const void* key,
+                                  const void* value, void* attention_out,
+                                  int32_t* topk_indices, float* softmax_max,
+                                  float* softmax_sum, float* p_slc_debug,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The second phase in two stream-ordered halves; nsa_compress_attention is
+ * exactly nsa_compress_attention_fwd followed by
+ * nsa_compress_attention_select on the same stream.
+ *
+ * nsa_compress_attention_fwd -- steps 1-3: attention_out, softmax_max and
+ * softmax_sum (arguments as for nsa_compress_attention).
+ *
+ * nsa_compress_attention_select -- steps 4-7: topk_indices (and p_slc_debug)
+ * from query, key and the softmax_max / softmax_sum the first half wrote;
+ * the recomputed P_cmp = exp(score - max) / sum is the normalised softmax.
+ * It must run after nsa_compress_attention_fwd of the same inputs (same
+ * stream, or an event in between).
+ *
+ * Both take the plan and a workspace of the size phase one returned, and
+ * return the same errors as nsa_compress_attention.
+ */
+nsa_status nsa_compress_attention_fwd(nsa_plan plan, const void* query, const void* key,
+                                      const void* value, void* attention_out, float* softmax_max,
+                                      float* softmax_sum, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+nsa_status nsa_compress_attention_select(nsa_plan plan, const void* query, const void* key,
+                                         const float* softmax_max, const float* softmax_sum,
+                                         int32_t* topk_indices, float* p_slc_debug,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sizes a plan fixed, for callers that allocate outputs from a plan. */
+typedef struct nsa_plan_info {
+    int64_t batch;
+    int64_t total_q_tokens;     /* T1 */
+    int64_t total_cmp_tokens;   /* T2 */
+    int64_t total_sel_blocks;   /* sum_b ceil(T_b / l') */
+    int64_t max_sel_blocks;     /* S of p_slc_debug */
+    int64_t head_num, kv_head_num, d1, d2, select_block_count;
+    size_t workspace_bytes;
+} nsa_plan_info;
+
+nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info);
+
+/* Frees a plan; NULL is ignored. */
+void nsa_plan_destroy(nsa_plan plan);
+
+/* Static text naming a status. */
+const char* nsa_status_string(nsa_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if
+ * none).  Valid until the next call into the library on that thread. */
+const char* nsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_CMP_H */

@@ -1,0 +1,296 @@
+"""MI355X (gfx950) compressed branch of Native Sparse Attention.
+
+A thin Python binding over ``libnsa_cmp.so`` (C ABI in include/nsa_cmp.h).
+PyTorch is used only to own device memory and to name the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+The functions here only check Python-level types, marshal pointers and
+sizes, and allocate output tensors.
+
+Entry points (same names as the C ABI):
+
+* ``nsa_compress`` -- NSA compression of K or V ("aclnnNsaCompress");
+* ``nsa_compress_attention_get_workspace`` -- first phase: validation,
+  workspace size, plan;
+* ``nsa_compress_attention`` -- second phase: attention output, top-k
+  indices, softmax max/sum (and optionally the importance scores);
+* ``compress_attention`` -- both phases in one call with the argument list
+  of ``mindspore.ops.nsa_compress_attention``.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import NsaError, PlanInfo  # noqa: F401
+
+__all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_workspace",
+           "nsa_compress_attention", "nsa_compress_attention_fwd", "nsa_compress_attention_select",
+           "compress_attention", "Plan", "NsaError", "library_path"]
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return _lib.NSA_DTYPE_BF16
+    if dt == torch.float16:
+        return _lib.NSA_DTYPE_FP16
+    raise TypeError(f"q/k/v must be bfloat16 or float16 tensors, got {dt}")
+
+
+def _stream_ptr(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _prefix(arr, name: str) -> "ctypes.Array":
+    if isinstance(arr, torch.Tensor):
+        arr = arr.tolist()
+    try:
+        vals = [int(x) for x in arr]
+    except TypeError as e:
+        raise TypeError(f"{name} must be a sequence of ints") from e
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals), len(vals)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need_tensor(t, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def nsa_compress_out_len(seq_len: int, compress_block_size: int, compress_stride: int) -> int:
+    n = _lib.load().nsa_compress_out_len(int(seq_len), int(compress_block_size), int(compress_stride))
+    if n < 0:
+        raise ValueError("invalid arguments to nsa_compress_out_len")
+    return int(n)
+
+
+def nsa_compress(input: torch.Tensor, weight: torch.Tensor, act_seq_len: Sequence[int],
+                 compress_block_size: int, compress_stride: int,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Compress a TND tensor ``input [T, N, D]`` with ``weight [l, N]``.
+
+    ``act_seq_len`` holds the sequences' token counts as prefix sums.
+    Returns ``[sum_b n_cmp_b, N, D]`` in the input dtype."""
+    _need_tensor(input, "input")
+    _need_tensor(weight, "weight")
+    if input.dim() != 3:
+        raise ValueError(f"input must be [T, N, D], got shape {tuple(input.shape)}")
+    if weight.dtype != input.dtype:
+        raise TypeError("weight must have the input's dtype")
+    T, N, D = input.shape
+    l, dd = int(compress_block_size), int(compress_stride)
+    if tuple(weight.shape) != (l, N):
+        raise ValueError(f"weight must be [{l}, {N}], got {tuple(weight.shape)}")
+    pre, B = _prefix(act_seq_len, "act_seq_len")
+    prev, T2 = 0, 0
+    lib = _lib.load()
+    for x in list(pre)[:B]:
+        n = lib.nsa_compress_out_len(int(x) - prev, l, dd)
+        prev = int(x)
+        T2 += max(0, int(n))
+    if out is None:
+        out = torch.empty((T2, N, D), dtype=input.dtype, device=input.device)
+    else:
+        _need_tensor(out, "out")
+    st = _lib.load().nsa_compress(_ptr(input), _ptr(weight), pre, B, T, N, D, l, dd,
+                                  _dtype_code(input.dtype), _ptr(out), out.shape[0],
+                                  _stream_ptr(input.device, stream))
+    _lib.check(st)
+    return out
+
+
+class Plan:
+    """Owns an nsa_plan handle (first phase of the attention operator)."""
+
+    def __init__(self, handle: ctypes.c_void_p, workspace_bytes: int):
+        self._h = handle
+        self.workspace_bytes = int(workspace_bytes)
+        info = PlanInfo()
+        _lib.check(_lib.load().nsa_plan_get_info(self._h, ctypes.byref(info)))
+        self.info = {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise ValueError("plan was destroyed")
+        return self._h
+
+    def destroy(self) -> None:
+        if self._h is not None:
+            _lib.load().nsa_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def nsa_compress_attention_get_workspace(actual_seq_qlen, actual_cmp_seq_kvlen, actual_sel_seq_kvlen,
+                                         head_num: int, kv_head_num: int, d1: int, d2: int,
+                                         scale_value: float, compress_block_size: int,
+                                         compress_stride: int, select_block_size: int,
+                                         select_block_count: int,
+                                         dtype: torch.dtype = torch.bfloat16) -> Plan:
+    if not isinstance(scale_value, (int, float)):
+        raise TypeError("scale_value must be a float")
+    for name, v in (("head_num", head_num), ("kv_head_num", kv_head_num), ("d1", d1), ("d2", d2),
+                    ("compress_block_size", compress_block_size), ("compress_stride", compress_stride),
+                    ("select_block_size", select_block_size), ("select_block_count", select_block_count)):
+        if not isinstance(v, int) or isinstance(v, bool):
+            raise TypeError(f"{name} must be an int")
+    q, B = _prefix(actual_seq_qlen, "actual_seq_qlen")
+    c, Bc = _prefix(actual_cmp_seq_kvlen, "actual_cmp_seq_kvlen")
+    s, Bs = _prefix(actual_sel_seq_kvlen, "actual_sel_seq_kvlen")
+    if not (B == Bc == Bs):
+        raise ValueError("the three prefix-sum lists must have the same length")
+    ws = ctypes.c_size_t(0)
+    h = ctypes.c_void_p(0)
+    st = _lib.load().nsa_compress_attention_get_workspace(
+        B, q, c, s, head_num, kv_head_num, d1, d2, float(scale_value), compress_block_size,
+        compress_stride, select_block_size, select_block_count, _dtype_code(dtype),
+        ctypes.byref(ws), ctypes.byref(h))
+    _lib.check(st)
+    return Plan(h, ws.value)
+
+
+def _check_qkv(plan: Plan, query, key, value=None):
+    info = plan.info
+    _need_tensor(query, "query")
+    _need_tensor(key, "key")
+    T1, N1, D1, N2, T2 = (info["total_q_tokens"], info["head_num"], info["d1"], info["kv_head_num"],
+                          info["total_cmp_tokens"])
+    if tuple(query.shape) != (T1, N1, D1):
+        raise ValueError(f"query must be {(T1, N1, D1)}, got {tuple(query.shape)}")
+    if tuple(key.shape) != (T2, N2, D1):
+        raise ValueError(f"key must be {(T2, N2, D1)}, got {tuple(key.shape)}")
+    if query.dtype != key.dtype:
+        raise TypeError("query and key must share a dtype")
+    if value is not None:
+        _need_tensor(value, "value")
+        if tuple(value.shape) != (T2, N2, info["d2"]):
+            raise ValueError(f"value must be {(T2, N2, info['d2'])}, got {tuple(value.shape)}")
+        if value.dtype != query.dtype:
+            raise TypeError("query and value must share a dtype")
+
+
+def _workspace(plan: Plan, workspace, dev):
+    if workspace is None:
+        workspace = torch.empty((max(plan.workspace_bytes, 1),), dtype=torch.uint8, device=dev)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _alloc_outputs(plan: Plan, query, outputs, want_pslc: bool):
+    info = plan.info
+    T1, N1, N2, D2 = info["total_q_tokens"], info["head_num"], info["kv_head_num"], info["d2"]
+    cnt, S = info["select_block_count"], info["max_sel_blocks"]
+    dev = query.device
+    o = dict(outputs or {})
+    if o.get("attention_out") is None:
+        o["attention_out"] = torch.empty((T1, N1, D2), dtype=query.dtype, device=dev)
+    if o.get("topk_indices") is None:
+        o["topk_indices"] = torch.empty((T1, N2, cnt), dtype=torch.int32, device=dev)
+    if o.get("softmax_max") is None:
+        o["softmax_max"] = torch.empty((T1, N1, 8), dtype=torch.float32, device=dev)
+    if o.get("softmax_sum") is None:
+        o["softmax_sum"] = torch.empty((T1, N1, 8), dtype=torch.float32, device=dev)
+    if want_pslc and o.get("p_slc") is None:
+        o["p_slc"] = torch.empty((T1, N2, max(S, 1)), dtype=torch.float32, device=dev)
+    return o
+
+
+def nsa_compress_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                           workspace: Optional[torch.Tensor] = None, return_p_slc: bool = False,
+                           outputs: Optional[dict] = None, stream=None):
+    """Second phase.  Returns (attention_out, topk_indices, softmax_max,
+    softmax_sum) and, with ``return_p_slc``, the importance scores
+    [T1, N2, S] as a fifth element."""
+    _check_qkv(plan, query, key, value)
+    o = _alloc_outputs(plan, query, outputs, return_p_slc)
+    ws, ws_bytes = _workspace(plan, workspace, query.device)
+    st = _lib.load().nsa_compress_attention(
+        plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(o["attention_out"]),
+        _ptr(o["topk_indices"]), _ptr(o["softmax_max"]), _ptr(o["softmax_sum"]),
+        _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws), ws_bytes,
+        _stream_ptr(query.device, stream))
+    _lib.check(st)
+    res = (o["attention_out"], o["topk_indices"], o["softmax_max"], o["softmax_sum"])
+    return res + (o["p_slc"],) if return_p_slc else res
+
+
+def nsa_compress_attention_fwd(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                               workspace: Optional[torch.Tensor] = None, outputs: Optional[dict] = None,
+                               stream=None):
+    """Steps 1-3 only: returns (attention_out, softmax_max, softmax_sum)."""
+    _check_qkv(plan, query, key, value)
+    o = _alloc_outputs(plan, query, outputs, False)
+    ws, ws_bytes = _workspace(plan, workspace, query.device)
+    st = _lib.load().nsa_compress_attention_fwd(
+        plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(o["attention_out"]),
+        _ptr(o["softmax_max"]), _ptr(o["softmax_sum"]), _ptr(ws), ws_bytes,
+        _stream_ptr(query.device, stream))
+    _lib.check(st)
+    return o["attention_out"], o["softmax_max"], o["softmax_sum"]
+
+
+def nsa_compress_attention_select(plan: Plan, query: torch.Tensor, key: torch.Tensor,
+                                  softmax_max: torch.Tensor, softmax_sum: torch.Tensor,
+                                  workspace: Optional[torch.Tensor] = None, return_p_slc: bool = False,
+                                  outputs: Optional[dict] = None, stream=None):
+    """Steps 4-7 from the first half's softmax statistics: returns
+    topk_indices (and the importance scores with ``return_p_slc``)."""
+    _check_qkv(plan, query, key)
+    for t, name in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
+        _need_tensor(t, name)
+        if t.dtype != torch.float32 or tuple(t.shape) != (plan.info["total_q_tokens"], plan.info["head_num"], 8):
+            raise ValueError(f"{name} must be float32 [T1, N1, 8]")
+    o = _alloc_outputs(plan, query, outputs, return_p_slc)
+    ws, ws_bytes = _workspace(plan, workspace, query.device)
+    st = _lib.load().nsa_compress_attention_select(
+        plan.handle, _ptr(query), _ptr(key), _ptr(softmax_max), _ptr(softmax_sum),
+        _ptr(o["topk_indices"]), _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws), ws_bytes,
+        _stream_ptr(query.device, stream))
+    _lib.check(st)
+    return (o["topk_indices"], o["p_slc"]) if return_p_slc else o["topk_indices"]
+
+
+def compress_attention(query, key, value, scale_value, head_num, compress_block_size,
+                       compress_stride, select_block_size, select_block_count, *,
+                       actual_seq_qlen, actual_cmp_seq_kvlen, actual_sel_seq_kvlen,
+                       topk_mask=None, atten_mask=None, return_p_slc: bool = False):
+    """Both phases with the argument list of the MindSpore operator.
+    Explicit mask tensors are not built: the causal rules are generated from
+    positions (pass None)."""
+    if topk_mask is not None or atten_mask is not None:
+        raise NotImplementedError("explicit atten_mask / topk_mask tensors are not built; "
+                                  "the causal masks are generated from token positions")
+    _need_tensor(query, "query")
+    _need_tensor(key, "key")
+    if query.dim() != 3 or key.dim() != 3 or value.dim() != 3:
+        raise ValueError("query, key and value must be TND (3-D)")
+    plan = nsa_compress_attention_get_workspace(
+        actual_seq_qlen, actual_cmp_seq_kvlen, actual_sel_seq_kvlen, int(head_num),
+        int(key.shape[1]), int(query.shape[2]), int(value.shape[2]), scale_value,
+        int(compress_block_size), int(compress_stride), int(select_block_size),
+        int(select_block_count), query.dtype)
+    try:
+        return nsa_compress_attention(plan, query, key, value, return_p_slc=return_p_slc)
+    finally:
+        plan.destroy()

@@ -1,0 +1,339 @@
+// Kernel (b): compressed attention, steps 1-3 of
+// "mindspore.ops.nsa_compress_attention" -- scaled QK^T, the causal mask
+// over compressed blocks, softmax and P.V -- fused, plus the softmax max and
+// sum outputs.
+//
+// Design (gfx950, bf16 MFMA 32x32x16, fp32 accumulate):
+//   * A workgroup is 4 waves x 64 query rows of one (sequence, KV head).  A
+//     row is (token, query head of the group): the group's heads of a token
+//     are adjacent rows, so they share every K/V tile and every mask.
+//   * K and V tiles of 64 compressed entries are staged in LDS, double
+//     buffered; the next tile's global loads are in flight during the current
+//     tile's MFMAs.  K is stored row-major (entry, dim), V transposed
+//     (dim, entry) with the entries of each 16-group ordered to match the
+//     layout the score accumulator leaves P in.
+//   * Scores are computed transposed, S^T = K Q^T: a lane owns one query
+//     column and 16 keys per 32x32 block, so the row max and sum are
+//     in-lane plus one exchange with the lane 32 away.  P^T is then directly
+//     the B operand of O^T += V^T P^T: no shuffles between the two MFMAs.
+//   * Online softmax in base 2 with the scale folded into one FMA; the
+//     running reference max only moves when a tile's max exceeds it by more
+//     than 2^8, so the O rescale is rare.  The true max is tracked apart for
+//     the softmax_max output.
+#include "nsa_device.h"
+
+namespace nsa {
+
+template <int D1, int D2>
+struct AttnCfg {
+    static constexpr int KT = kKeyTile;     // compressed entries per tile
+    static constexpr int KS = D1 + 8;       // LDS row stride of K (bf16): 16 B pad
+    static constexpr int VS = KT + 8;       // LDS row stride of V^T (bf16): 16 B pad
+    static constexpr int NKS = D1 / 16;     // k-steps of QK^T
+    static constexpr int NDB = D2 / 32;     // 32-row blocks of O^T
+    static constexpr int KCH = D1 / 8;      // 16-byte chunks per K row
+    static constexpr int KLD = KT * KCH / 256;
+    static constexpr int VIT = 16 * (D2 / 8);  // (entry quad, dim octet) staging items
+    static_assert(KT * KCH % 256 == 0, "K tile staging");
+    static_assert(VIT <= 256, "V tile staging");
+};
+
+// Slot of entry quad kq (4 entries) inside the transposed V row: within each
+// group of 16 entries the quads are stored in the order 0, 2, 1, 3 so that a
+// lane of half h reads entries {4h..4h+3, 8+4h..8+4h+3} as one 16-byte chunk.
+__device__ __forceinline__ int v_slot(int kq)
+{
+    const int q = kq & 3;
+    const int perm = (q == 1) ? 2 : (q == 2 ? 1 : q);
+    return (kq >> 2) * 16 + perm * 4;
+}
+
+template <int D1, int D2>
+__global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
+{
+    using C = AttnCfg<D1, D2>;
+    constexpr int KT = C::KT;
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * C::KS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D2 * C::VS];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+
+    // ---- tile -> (sequence, KV head, row block) ---------------------------
+    const int tile = blockIdx.x;
+    const int b = find_batch<true>(p.bt, p.B, tile);
+    const BatchEnt be = p.bt[b];
+    const int idx = tile - be.tile_off_a;
+    const int g = idx % p.N2;
+    const int rb = be.n_rb_a - 1 - idx / p.N2;
+    const int G = p.G;
+    const int rows_total = be.T * G;
+    const int row_wg = rb * kAttnRowsPerWG;
+
+    int nvq[2];
+    bool vq[2];
+    int64_t grow[2];
+    bf16x8 qf[2][C::NKS];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const int r = row_wg + wave * 64 + qb * 32 + l32;
+        vq[qb] = r < rows_total;
+        const int tok = r / G;
+        const int hh = r - tok * G;
+        grow[qb] = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
+        nvq[qb] = vq[qb] ? n_visible(tok, p.l, p.d, be.n_cmp) : 0;
+        const uint16_t* qrow = p.q + grow[qb] * D1 + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (vq[qb]) {
+                v = *(const u32x4*)(qrow + ks * 16);
+                v ^= p.qsign;
+            }
+            qf[qb][ks] = as_bf16x8(v);
+        }
+    }
+    const int last_row = min(row_wg + kAttnRowsPerWG, rows_total) - 1;
+    const int nv_max = n_visible(last_row / G, p.l, p.d, be.n_cmp);
+    const int nv_min = n_visible(row_wg / G, p.l, p.d, be.n_cmp);
+    const int n_kt = (nv_max + KT - 1) / KT;
+
+    // ---- tile staging ------------------------------------------------------
+    const int64_t kv_stride1 = (int64_t)p.N2 * D1;
+    const int64_t kv_stride2 = (int64_t)p.N2 * D2;
+    const uint16_t* kbase = p.kc + ((int64_t)be.cmp_off * p.N2 + g) * D1;
+    const uint16_t* vbase = p.vc + ((int64_t)be.cmp_off * p.N2 + g) * D2;
+    const int v_o = tid >> 4;        // dim octet of this thread's V item
+    const int v_kq = tid & 15;       // entry quad of this thread's V item
+    u32x4 kreg[C::KLD];
+    u32x4 vreg[4];
+
+    auto load_tile = [&](int kt) {
+        const int key0 = kt * KT;
+#pragma unroll
+        for (int i = 0; i < C::KLD; ++i) {
+            const int cidx = tid + 256 * i;
+            const int row = cidx / C::KCH;
+            const int col = cidx % C::KCH;
+            const int key = key0 + row;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (key < be.n_cmp)
+                v = *(const u32x4*)(kbase + (int64_t)key * kv_stride1 + col * 8);
+            kreg[i] = v;
+        }
+        if (tid < C::VIT) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = key0 + 4 * v_kq + e;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (key < be.n_cmp)
+                    v = *(const u32x4*)(vbase + (int64_t)key * kv_stride2 + v_o * 8);
+                vreg[e] = v;
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < C::KLD; ++i) {
+            const int cidx = tid + 256 * i;
+            const int row = cidx / C::KCH;
+            const int col = cidx % C::KCH;
+            *(u32x4*)&Ks[buf][row * C::KS + col * 8] = kreg[i];
+        }
+        if (tid < C::VIT) {
+            const int slot = v_slot(v_kq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sh = (j & 1) * 16;
+                const uint32_t e0 = (vreg[0][j >> 1] >> sh) & 0xFFFFu;
+                const uint32_t e1 = (vreg[1][j >> 1] >> sh) & 0xFFFFu;
+                const uint32_t e2 = (vreg[2][j >> 1] >> sh) & 0xFFFFu;
+                const uint32_t e3 = (vreg[3][j >> 1] >> sh) & 0xFFFFu;
+                u32x2 w2 = {e0 | (e1 << 16), e2 | (e3 << 16)};
+                *(u32x2*)&Vt[buf][(v_o * 8 + j) * C::VS + slot] = w2;
+            }
+        }
+    };
+
+    // ---- state ---------------------------------------------------------------
+    f32x16 o[2][C::NDB];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                o[qb][db][r] = 0.f;
+    float mref[2] = {-INFINITY, -INFINITY};
+    float mtrue[2] = {-INFINITY, -INFINITY};
+    float lsum[2] = {0.f, 0.f};
+    const float c = p.c;
+
+    if (n_kt > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < n_kt)
+            load_tile(kt + 1);
+
+        // S^T = K Q^T for 64 keys x 64 queries.
+        f32x16 s[2][2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[qb][kb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 ka = as_bf16x8(*(const u32x4*)&Ks[buf][(kb * 32 + l32) * C::KS + ks * 16 + hf * 8]);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    s[qb][kb] = mfma32(ka, qf[qb][ks], s[qb][kb]);
+            }
+        }
+
+        // Mask, online softmax, P (in place of S).
+        const bool need_mask = (kt + 1) * KT > nv_min;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float v = s[qb][kb][r];
+                    if (need_mask) {
+                        const int key = kt * KT + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        v = (key < nvq[qb]) ? v : -INFINITY;
+                        s[qb][kb][r] = v;
+                    }
+                    tmax = fmaxf(tmax, v);
+                }
+            }
+            tmax = half_max(tmax);
+            mtrue[qb] = fmaxf(mtrue[qb], tmax);
+            const bool grow_ref = tmax > mref[qb] + p.thr;
+            if (__ballot(grow_ref)) {
+                float alpha = 1.f;
+                if (grow_ref) {
+                    alpha = (mref[qb] == -INFINITY) ? 0.f : fast_exp2((mref[qb] - tmax) * c);
+                    mref[qb] = tmax;
+                }
+                lsum[qb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        o[qb][db][r] *= alpha;
+            }
+            const float nb = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
+            float ps = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float sv = s[qb][kb][r];
+                    float pv = fast_exp2(fmaf(sv, c, nb));
+                    if (need_mask)
+                        pv = (sv == -INFINITY) ? 0.f : pv;
+                    s[qb][kb][r] = pv;
+                    ps += pv;
+                }
+            }
+            lsum[qb] += ps;
+        }
+
+        // O^T += V^T P^T, 16 keys per MFMA.
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int kb = kk >> 1;
+            const int r0 = (kk & 1) * 8;
+            bf16x8 pf[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                u32x4 w4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w4[j] = pack_bf16x2(s[qb][kb][r0 + 2 * j], s[qb][kb][r0 + 2 * j + 1]);
+                pf[qb] = as_bf16x8(w4);
+            }
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db) {
+                const bf16x8 va = as_bf16x8(*(const u32x4*)&Vt[buf][(db * 32 + l32) * C::VS + kk * 16 + hf * 8]);
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    o[qb][db] = mfma32(va, pf[qb], o[qb][db]);
+            }
+        }
+
+        if (kt + 1 < n_kt)
+            store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue ----------------------------------------------------------
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float lf = half_sum(lsum[qb]);
+        const bool empty = (mtrue[qb] == -INFINITY);
+        const float inv = empty ? 0.f : 1.f / lf;
+        if (!vq[qb])
+            continue;
+        uint16_t* orow = p.out + grow[qb] * D2;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int dv = db * 32 + 8 * r4 + 4 * hf;
+                u32x2 w2 = {pack_bf16x2(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv),
+                            pack_bf16x2(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv)};
+                *(u32x2*)(orow + dv) = w2;
+            }
+        }
+        const float smv = empty ? -INFINITY : mtrue[qb] * p.abs_scale;
+        const float ssv = empty ? 0.f : lf * fast_exp2((mref[qb] - mtrue[qb]) * c);
+        const float val = hf == 0 ? smv : ssv;
+        float* dst = (hf == 0 ? p.smax : p.ssum) + grow[qb] * 8;
+        f32x4 v4 = {val, val, val, val};
+        *(f32x4*)dst = v4;
+        *(f32x4*)(dst + 4) = v4;
+    }
+}
+
+template <int D1, int D2>
+static hipError_t launch_t(const AttnParams& p, int n_tiles, hipStream_t stream)
+{
+    hipLaunchKernelGGL((k_cmp_attn_fwd<D1, D2>), dim3(n_tiles), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+bool cmp_attn_supported(int d1, int d2)
+{
+    return (d1 == 64 && d2 == 64) || (d1 == 128 && (d2 == 64 || d2 == 128)) ||
+           (d1 == 192 && (d2 == 64 || d2 == 128));
+}
+
+hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream)
+{
+    if (n_tiles <= 0)
+        return hipSuccess;
+    if (d1 == 64 && d2 == 64) return launch_t<64, 64>(p, n_tiles, stream);
+    if (d1 == 128 && d2 == 64) return launch_t<128, 64>(p, n_tiles, stream);
+    if (d1 == 128 && d2 == 128) return launch_t<128, 128>(p, n_tiles, stream);
+    if (d1 == 192 && d2 == 64) return launch_t<192, 64>(p, n_tiles, stream);
+    if (d1 == 192 && d2 == 128) return launch_t<192, 128>(p, n_tiles, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace nsa

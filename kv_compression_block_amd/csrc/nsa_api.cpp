@@ -1,0 +1,537 @@
+// C ABI of the library (include/nsa_cmp.h): argument validation, extent
+// derivation, launch planning and launches.  The library allocates no device
+// memory; the attention call copies a small per-sequence table into the
+// caller's workspace and launches two kernels on the caller's stream.
+#include "nsa_cmp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <initializer_list>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "nsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+nsa_status fail(nsa_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+nsa_status ok()
+{
+    g_last_error.clear();
+    return NSA_OK;
+}
+
+bool mult16(int64_t v) { return v > 0 && v % 16 == 0; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t n_cmp_of(int64_t T, int64_t l, int64_t d) { return T < l ? 0 : (T - l) / d + 1; }
+
+// Validates host prefix sums; fills per-sequence lengths.
+nsa_status read_prefix(const int64_t* prefix, int64_t batch, const char* name,
+                       std::vector<int64_t>& lens)
+{
+    if (!prefix)
+        return fail(NSA_ERR_NULLPTR, "%s is NULL", name);
+    lens.resize((size_t)batch);
+    int64_t prev = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        if (prefix[b] < prev)
+            return fail(NSA_ERR_SHAPE, "%s must be non-decreasing prefix sums from 0 (entry %lld = %lld after %lld)",
+                        name, (long long)b, (long long)prefix[b], (long long)prev);
+        lens[(size_t)b] = prefix[b] - prev;
+        prev = prefix[b];
+    }
+    if (prev > INT32_MAX)
+        return fail(NSA_ERR_UNSUPPORTED, "%s total %lld exceeds 2^31-1", name, (long long)prev);
+    return NSA_OK;
+}
+
+nsa_status check_dtype(int dtype)
+{
+    if (dtype == NSA_DTYPE_BF16)
+        return NSA_OK;
+    if (dtype == NSA_DTYPE_FP16)
+        return fail(NSA_ERR_UNSUPPORTED, "float16 is not built; use bfloat16");
+    return fail(NSA_ERR_DTYPE, "unknown dtype code %d", dtype);
+}
+
+}  // namespace
+
+struct nsa_plan_s {
+    int64_t B, N1, N2, D1, D2, l, d, lsel, count;
+    float scale;
+    int64_t T1, T2, S_total, S_max;
+    int log2gp, topk_waves, sb;
+    size_t topk_lds;
+    int64_t tiles_a, tiles_c;
+    size_t ws_bytes;
+    std::vector<nsa::BatchEnt> table;
+};
+
+extern "C" {
+
+int64_t nsa_compress_out_len(int64_t seq_len, int64_t l, int64_t d)
+{
+    if (l < 1 || d < 1 || seq_len < 0)
+        return -1;
+    return n_cmp_of(seq_len, l, d);
+}
+
+const char* nsa_status_string(nsa_status s)
+{
+    switch (s) {
+    case NSA_OK: return "NSA_OK";
+    case NSA_ERR_NULLPTR: return "NSA_ERR_NULLPTR";
+    case NSA_ERR_DTYPE: return "NSA_ERR_DTYPE";
+    case NSA_ERR_SHAPE: return "NSA_ERR_SHAPE";
+    case NSA_ERR_CONSTRAINT: return "NSA_ERR_CONSTRAINT";
+    case NSA_ERR_WORKSPACE: return "NSA_ERR_WORKSPACE";
+    case NSA_ERR_UNSUPPORTED: return "NSA_ERR_UNSUPPORTED";
+    case NSA_ERR_HIP: return "NSA_ERR_HIP";
+    }
+    return "NSA_ERR_UNKNOWN";
+}
+
+const char* nsa_last_error(void) { return g_last_error.c_str(); }
+
+nsa_status nsa_compress(const void* input, const void* weight, const int64_t* act_seq_len,
+                        int64_t batch, int64_t total_tokens, int64_t num_heads, int64_t head_dim,
+                        int64_t l, int64_t d, nsa_dtype dtype, void* output,
+                        int64_t output_tokens, void* stream)
+{
+    if (!input || !weight || !act_seq_len)
+        return fail(NSA_ERR_NULLPTR, "input, weight and act_seq_len must not be NULL");
+    nsa_status st = check_dtype((int)dtype);
+    if (st != NSA_OK)
+        return st;
+    if (batch < 1)
+        return fail(NSA_ERR_SHAPE, "act_seq_len must not be empty (batch = %lld)", (long long)batch);
+    if (num_heads < 1)
+        return fail(NSA_ERR_SHAPE, "num_heads must be >= 1");
+    if (!mult16(head_dim) || head_dim > 256)
+        return fail(NSA_ERR_CONSTRAINT, "head_dim must be a multiple of 16 and <= 256 (got %lld)", (long long)head_dim);
+    if (!mult16(l) || l > 128)
+        return fail(NSA_ERR_CONSTRAINT, "compress_block_size must be a multiple of 16 in [16, 128] (got %lld)", (long long)l);
+    if (!mult16(d) || d > l)
+        return fail(NSA_ERR_CONSTRAINT, "compress_stride must be a multiple of 16 with 16 <= d <= compress_block_size (got %lld)", (long long)d);
+    if (l * num_heads > 128 * 64)
+        return fail(NSA_ERR_UNSUPPORTED, "compress_block_size * num_heads must be <= 8192");
+    std::vector<int64_t> lens;
+    st = read_prefix(act_seq_len, batch, "act_seq_len", lens);
+    if (st != NSA_OK)
+        return st;
+    if (act_seq_len[batch - 1] != total_tokens)
+        return fail(NSA_ERR_SHAPE, "last prefix sum %lld != total_tokens %lld",
+                    (long long)act_seq_len[batch - 1], (long long)total_tokens);
+    int64_t T2 = 0;
+    for (int64_t T : lens)
+        T2 += n_cmp_of(T, l, d);
+    if (T2 != output_tokens)
+        return fail(NSA_ERR_SHAPE, "output_tokens %lld != sum of compressed lengths %lld",
+                    (long long)output_tokens, (long long)T2);
+    if (T2 > 0 && !output)
+        return fail(NSA_ERR_NULLPTR, "output must not be NULL");
+    if (!aligned(input, 16) || (output && !aligned(output, 16)) || !aligned(weight, 2))
+        return fail(NSA_ERR_CONSTRAINT, "input/output must be 16-byte aligned");
+    if (T2 == 0)
+        return ok();
+
+    const int64_t nd8 = num_heads * head_dim / 8;
+    nsa::CompressParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x = (const uint16_t*)input;
+    p.w = (const uint16_t*)weight;
+    p.y = (uint16_t*)output;
+    p.N = (int)num_heads;
+    p.D = (int)head_dim;
+    p.l = (int)l;
+    p.d = (int)d;
+    int64_t in_off = 0, out_off = 0;
+    size_t b = 0;
+    while (b < lens.size()) {
+        p.nseg = 0;
+        int64_t max_items = 0;
+        while (b < lens.size() && p.nseg < nsa::kCompressMaxSeg) {
+            const int64_t n = n_cmp_of(lens[b], l, d);
+            if (n > 0) {
+                p.in_off[p.nseg] = (int)in_off;
+                p.out_off[p.nseg] = (int)out_off;
+                p.n_out[p.nseg] = (int)n;
+                if (n * nd8 > max_items)
+                    max_items = n * nd8;
+                ++p.nseg;
+            }
+            in_off += lens[b];
+            out_off += n;
+            ++b;
+        }
+        if (p.nseg == 0)
+            continue;
+        p.max_blocks_x = (int)((max_items + 255) / 256);
+        hipError_t e = nsa::launch_compress(p, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return fail(NSA_ERR_HIP, "compress launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+nsa_status nsa_compress_attention_get_workspace(
+    int64_t batch, const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen,
+    const int64_t* act_sel_seq_kvlen, int64_t head_num, int64_t kv_head_num, int64_t d1,
+    int64_t d2, float scale_value, int64_t l, int64_t d, int64_t lsel, int64_t count,
+    nsa_dtype dtype, size_t* workspace_bytes, nsa_plan* plan_out)
+{
+    if (plan_out)
+        *plan_out = nullptr;
+    if (!workspace_bytes || !plan_out)
+        return fail(NSA_ERR_NULLPTR, "workspace_bytes and plan_out must not be NULL");
+    nsa_status st = check_dtype((int)dtype);
+    if (st != NSA_OK)
+        return st;
+    if (batch < 1)
+        return fail(NSA_ERR_SHAPE, "the prefix-sum lists must not be empty (batch = %lld)", (long long)batch);
+    // Parameter constraints of the compressed-attention operator.
+    if (!mult16(l) || l > 128)
+        return fail(NSA_ERR_CONSTRAINT, "compress_block_size must be a multiple of 16 in [16, 128] (got %lld)", (long long)l);
+    if (!mult16(d) || d > 64)
+        return fail(NSA_ERR_CONSTRAINT, "compress_stride must be a multiple of 16 in [16, 64] (got %lld)", (long long)d);
+    if (!mult16(lsel) || lsel > 128)
+        return fail(NSA_ERR_CONSTRAINT, "select_block_size must be a multiple of 16 in [16, 128] (got %lld)", (long long)lsel);
+    if (count < 1 || count > 32)
+        return fail(NSA_ERR_CONSTRAINT, "select_block_count must be in [1, 32] (got %lld)", (long long)count);
+    if (l < d)
+        return fail(NSA_ERR_CONSTRAINT, "compress_block_size (%lld) must be >= compress_stride (%lld)", (long long)l, (long long)d);
+    if (lsel < l)
+        return fail(NSA_ERR_CONSTRAINT, "select_block_size (%lld) must be >= compress_block_size (%lld)", (long long)lsel, (long long)l);
+    if (lsel % d != 0)
+        return fail(NSA_ERR_CONSTRAINT, "select_block_size (%lld) must be a multiple of compress_stride (%lld)", (long long)lsel, (long long)d);
+    if (!mult16(d1) || !mult16(d2))
+        return fail(NSA_ERR_CONSTRAINT, "head dims must be positive multiples of 16 (D1 = %lld, D2 = %lld)", (long long)d1, (long long)d2);
+    if (d1 < d2)
+        return fail(NSA_ERR_CONSTRAINT, "D1 (%lld) must be >= D2 (%lld)", (long long)d1, (long long)d2);
+    if (kv_head_num < 1 || head_num < kv_head_num || head_num % kv_head_num != 0)
+        return fail(NSA_ERR_CONSTRAINT, "need N1 >= N2 >= 1 and N1 %% N2 == 0 (N1 = %lld, N2 = %lld)", (long long)head_num, (long long)kv_head_num);
+    if (!std::isfinite(scale_value))
+        return fail(NSA_ERR_CONSTRAINT, "scale_value must be finite");
+
+    std::vector<int64_t> qlen, clen, slen;
+    if ((st = read_prefix(act_seq_qlen, batch, "actual_seq_qlen", qlen)) != NSA_OK) return st;
+    if ((st = read_prefix(act_cmp_seq_kvlen, batch, "actual_cmp_seq_kvlen", clen)) != NSA_OK) return st;
+    if ((st = read_prefix(act_sel_seq_kvlen, batch, "actual_sel_seq_kvlen", slen)) != NSA_OK) return st;
+    int64_t S_max = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t T = qlen[(size_t)b];
+        const int64_t nc = n_cmp_of(T, l, d);
+        const int64_t ns = (T + lsel - 1) / lsel;
+        if (clen[(size_t)b] != nc)
+            return fail(NSA_ERR_SHAPE, "sequence %lld: compressed length %lld != floor((%lld - l)/d) + 1 = %lld",
+                        (long long)b, (long long)clen[(size_t)b], (long long)T, (long long)nc);
+        if (slen[(size_t)b] != ns)
+            return fail(NSA_ERR_SHAPE, "sequence %lld: select length %lld != ceil(%lld / l') = %lld",
+                        (long long)b, (long long)slen[(size_t)b], (long long)T, (long long)ns);
+        if (ns > S_max)
+            S_max = ns;
+    }
+
+    // What this build implements.
+    if (!nsa::cmp_attn_supported((int)d1, (int)d2) || !nsa::slc_topk_supported((int)d1))
+        return fail(NSA_ERR_UNSUPPORTED, "head dims (D1, D2) = (%lld, %lld) are not built; built: D1 in {64,128,192}, D2 in {64,128}, D2 <= D1",
+                    (long long)d1, (long long)d2);
+    const int64_t G = head_num / kv_head_num;
+    const int log2gp = nsa::topk_log2_gp((int)G);
+    if (log2gp < 0)
+        return fail(NSA_ERR_UNSUPPORTED, "N1/N2 = %lld > 64 query heads per KV head is not built", (long long)G);
+    if (S_max > 64 * nsa::kTopkMaxNpl)
+        return fail(NSA_ERR_UNSUPPORTED, "%lld select blocks in one sequence; at most %d are built",
+                    (long long)S_max, 64 * nsa::kTopkMaxNpl);
+    const int R = (int)(lsel / d);
+    const int H = R + (int)(l / d) - 2;
+    if (H + 1 > 16 || H >= nsa::kKeyTile)
+        return fail(NSA_ERR_UNSUPPORTED, "remap stencil of %d taps is not built", H + 1);
+    const int sb = (int)(((S_max + 63) / 64) * 64 > 0 ? ((S_max + 63) / 64) * 64 : 64);
+    int waves = 4;
+    size_t lds = nsa::topk_lds_bytes((int)d1, log2gp, waves, sb);
+    while (waves > 1 && lds > 80 * 1024) {
+        waves >>= 1;
+        lds = nsa::topk_lds_bytes((int)d1, log2gp, waves, sb);
+    }
+    if (lds > 160 * 1024)
+        return fail(NSA_ERR_UNSUPPORTED, "importance scores of %lld select blocks x %d tokens do not fit in LDS",
+                    (long long)S_max, 64 >> log2gp);
+
+    nsa_plan_s* plan = new (std::nothrow) nsa_plan_s();
+    if (!plan)
+        return fail(NSA_ERR_WORKSPACE, "out of host memory");
+    plan->B = batch;
+    plan->N1 = head_num;
+    plan->N2 = kv_head_num;
+    plan->D1 = d1;
+    plan->D2 = d2;
+    plan->l = l;
+    plan->d = d;
+    plan->lsel = lsel;
+    plan->count = count;
+    plan->scale = scale_value;
+    plan->S_max = S_max;
+    plan->log2gp = log2gp;
+    plan->topk_waves = waves;
+    plan->sb = sb;
+    plan->topk_lds = lds;
+    plan->table.resize((size_t)batch);
+    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, S_total = 0;
+    const int64_t rows_c = (int64_t)waves * 64;
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t T = qlen[(size_t)b];
+        nsa::BatchEnt& e = plan->table[(size_t)b];
+        std::memset(&e, 0, sizeof e);
+        e.q_off = (int32_t)q_off;
+        e.T = (int32_t)T;
+        e.cmp_off = (int32_t)c_off;
+        e.n_cmp = (int32_t)clen[(size_t)b];
+        e.n_rb_a = (int32_t)((T * G + nsa::kAttnRowsPerWG - 1) / nsa::kAttnRowsPerWG);
+        e.tile_off_a = (int32_t)ta;
+        e.n_rb_c = (int32_t)((T * (1 << log2gp) + rows_c - 1) / rows_c);
+        e.tile_off_c = (int32_t)tc;
+        e.S_sel = (int32_t)slen[(size_t)b];
+        ta += (int64_t)e.n_rb_a * kv_head_num;
+        tc += (int64_t)e.n_rb_c * kv_head_num;
+        q_off += T;
+        c_off += clen[(size_t)b];
+        S_total += slen[(size_t)b];
+    }
+    if (ta > INT32_MAX || tc > INT32_MAX || q_off * head_num * 8 > ((int64_t)1 << 62)) {
+        delete plan;
+        return fail(NSA_ERR_UNSUPPORTED, "problem too large for one launch");
+    }
+    plan->T1 = q_off;
+    plan->T2 = c_off;
+    plan->S_total = S_total;
+    plan->tiles_a = ta;
+    plan->tiles_c = tc;
+    plan->ws_bytes = ((size_t)batch * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
+    *workspace_bytes = plan->ws_bytes;
+    *plan_out = plan;
+    return ok();
+}
+
+nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info)
+{
+    if (!plan || !info)
+        return fail(NSA_ERR_NULLPTR, "plan and info must not be NULL");
+    info->batch = plan->B;
+    info->total_q_tokens = plan->T1;
+    info->total_cmp_tokens = plan->T2;
+    info->total_sel_blocks = plan->S_total;
+    info->max_sel_blocks = plan->S_max;
+    info->head_num = plan->N1;
+    info->kv_head_num = plan->N2;
+    info->d1 = plan->D1;
+    info->d2 = plan->D2;
+    info->select_block_count = plan->count;
+    info->workspace_bytes = plan->ws_bytes;
+    return ok();
+}
+
+void nsa_plan_destroy(nsa_plan plan) { delete plan; }
+
+}  // extern "C"
+
+namespace {
+
+nsa_status check_exec(nsa_plan plan, void* workspace, size_t workspace_bytes,
+                      std::initializer_list<const void*> a16, std::initializer_list<const void*> a4)
+{
+    if (workspace_bytes < plan->ws_bytes || (plan->ws_bytes > 0 && !workspace))
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, plan->ws_bytes);
+    for (const void* ptr : a16)
+        if (ptr && !aligned(ptr, 16))
+            return fail(NSA_ERR_CONSTRAINT, "tensors and workspace must be 16-byte aligned");
+    for (const void* ptr : a4)
+        if (ptr && !aligned(ptr, 4))
+            return fail(NSA_ERR_CONSTRAINT, "topk_indices and p_slc_debug must be 4-byte aligned");
+    return NSA_OK;
+}
+
+nsa_status upload_table(nsa_plan plan, void* workspace, hipStream_t s)
+{
+    hipError_t e = hipMemcpyAsync(workspace, plan->table.data(), plan->table.size() * sizeof(nsa::BatchEnt),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "workspace upload failed: %s", hipGetErrorString(e));
+    return NSA_OK;
+}
+
+float exp2_scale(const nsa_plan_s* plan) { return std::fabs(plan->scale) * 1.4426950408889634f; }
+uint32_t q_sign(const nsa_plan_s* plan) { return plan->scale < 0.f ? 0x80008000u : 0u; }
+
+nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const void* value,
+                      void* attention_out, float* softmax_max, float* softmax_sum, void* workspace,
+                      hipStream_t s)
+{
+    const float abs_scale = std::fabs(plan->scale);
+    const float c = exp2_scale(plan);
+    nsa::AttnParams a;
+    std::memset(&a, 0, sizeof a);
+    a.q = (const uint16_t*)query;
+    a.kc = (const uint16_t*)key;
+    a.vc = (const uint16_t*)value;
+    a.out = (uint16_t*)attention_out;
+    a.smax = softmax_max;
+    a.ssum = softmax_sum;
+    a.bt = (const nsa::BatchEnt*)workspace;
+    a.B = (int)plan->B;
+    a.N1 = (int)plan->N1;
+    a.N2 = (int)plan->N2;
+    a.G = (int)(plan->N1 / plan->N2);
+    a.l = (int)plan->l;
+    a.d = (int)plan->d;
+    a.c = c;
+    a.abs_scale = abs_scale;
+    // the running max moves only when a score beats it by more than 8 in base 2
+    a.thr = (c > 0.f) ? std::fmin(8.0f / c, 3.0e38f) : 3.0e38f;
+    a.qsign = q_sign(plan);
+    hipError_t e = nsa::launch_cmp_attn((int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, s);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+    return NSA_OK;
+}
+
+nsa_status launch_select(nsa_plan plan, const void* query, const void* key, const float* softmax_max,
+                         const float* softmax_sum, int32_t* topk_indices, float* p_slc_debug,
+                         void* workspace, hipStream_t s)
+{
+    nsa::TopkParams t;
+    std::memset(&t, 0, sizeof t);
+    t.q = (const uint16_t*)query;
+    t.kc = (const uint16_t*)key;
+    t.smax = softmax_max;
+    t.ssum = softmax_sum;
+    t.topk = topk_indices;
+    t.pslc = p_slc_debug;
+    t.bt = (const nsa::BatchEnt*)workspace;
+    t.B = (int)plan->B;
+    t.N1 = (int)plan->N1;
+    t.N2 = (int)plan->N2;
+    t.G = (int)(plan->N1 / plan->N2);
+    t.l = (int)plan->l;
+    t.d = (int)plan->d;
+    t.lsel = (int)plan->lsel;
+    t.count = (int)plan->count;
+    t.R = (int)(plan->lsel / plan->d);
+    const int L2 = (int)(plan->l / plan->d);
+    t.H = t.R + L2 - 2;
+    // P_slc[j] = sum_m sum_n P[R*j - m - n]: entry R*j - r is counted once per
+    // pair (m, n) with m + n = r, 0 <= m < R, 0 <= n < L2.
+    for (int r = 0; r <= t.H; ++r) {
+        int cnt = 0;
+        for (int m = 0; m < t.R; ++m)
+            if (r - m >= 0 && r - m < L2)
+                ++cnt;
+        t.coef[r] = (float)cnt;
+    }
+    t.c = exp2_scale(plan);
+    t.qsign = q_sign(plan);
+    t.s_stride = (int)plan->S_max;
+    t.sb = plan->sb;
+    t.npl = plan->sb / 64;
+    t.waves = plan->topk_waves;
+    hipError_t e = nsa::launch_slc_topk((int)plan->D1, plan->log2gp, t, (int)plan->tiles_c, plan->topk_lds, s);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "top-k launch failed: %s", hipGetErrorString(e));
+    return NSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nsa_status nsa_compress_attention_fwd(nsa_plan plan, const void* query, const void* key,
+                                      const void* value, void* attention_out, float* softmax_max,
+                                      float* softmax_sum, void* workspace, size_t workspace_bytes,
+                                      void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !attention_out || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query and the three outputs must not be NULL");
+    if (plan->T2 > 0 && (!key || !value))
+        return fail(NSA_ERR_NULLPTR, "key and value must not be NULL");
+    nsa_status st = check_exec(plan, workspace, workspace_bytes,
+                               {query, key, value, attention_out, softmax_max, softmax_sum, workspace}, {});
+    if (st != NSA_OK || plan->T1 == 0)
+        return st == NSA_OK ? ok() : st;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s)) != NSA_OK)
+        return st;
+    return ok();
+}
+
+nsa_status nsa_compress_attention_select(nsa_plan plan, const void* query, const void* key,
+                                         const float* softmax_max, const float* softmax_sum,
+                                         int32_t* topk_indices, float* p_slc_debug,
+                                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !topk_indices || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query, softmax_max, softmax_sum and topk_indices must not be NULL");
+    if (plan->T2 > 0 && !key)
+        return fail(NSA_ERR_NULLPTR, "key must not be NULL");
+    nsa_status st = check_exec(plan, workspace, workspace_bytes, {query, key, softmax_max, softmax_sum, workspace},
+                               {topk_indices, p_slc_debug});
+    if (st != NSA_OK || plan->T1 == 0)
+        return st == NSA_OK ? ok() : st;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s)) != NSA_OK)
+        return st;
+    return ok();
+}
+
+nsa_status nsa_compress_attention(nsa_plan plan, const void* query, const void* key,
+                                  const void* value, void* attention_out, int32_t* topk_indices,
+                                  float* softmax_max, float* softmax_sum, float* p_slc_debug,
+                                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !attention_out || !topk_indices || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query and the four outputs must not be NULL");
+    if (plan->T2 > 0 && (!key || !value))
+        return fail(NSA_ERR_NULLPTR, "key and value must not be NULL");
+    nsa_status st = check_exec(plan, workspace, workspace_bytes,
+                               {query, key, value, attention_out, softmax_max, softmax_sum, workspace},
+                               {topk_indices, p_slc_debug});
+    if (st != NSA_OK || plan->T1 == 0)
+        return st == NSA_OK ? ok() : st;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s)) != NSA_OK)
+        return st;
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s)) != NSA_OK)
+        return st;
+    return ok();
+}
+
+}  // extern "C"

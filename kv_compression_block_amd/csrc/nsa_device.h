@@ -1,0 +1,80 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16 packing,
+// MFMA wrappers and cross-lane helpers.  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nsa_internal.h"
+
+namespace nsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two floats -> two bf16 in one word (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D(32x32, f32) += A(32x16, bf16) * B(16x32, bf16).
+// Lane l holds A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32] as the
+// same k-slots; D element (row, col) sits in lane col + 32*((row/4)%2),
+// register 4*(row/8) + row%4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Combine a value with the one held by the lane 32 positions away.
+__device__ __forceinline__ float half_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float half_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Largest b with tile_off(b) <= tile: tile ranges are ascending in b.
+template <bool kAttn>
+__device__ __forceinline__ int find_batch(const BatchEnt* bt, int B, int tile)
+{
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        int off = kAttn ? bt[mid].tile_off_a : bt[mid].tile_off_c;
+        if (off <= tile)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Compressed blocks visible to local position t: i*d + l - 1 <= t.
+__device__ __forceinline__ int n_visible(int t, int l, int d, int n_cmp)
+{
+    if (t < l - 1)
+        return 0;
+    int n = (t - l + 1) / d + 1;
+    return n < n_cmp ? n : n_cmp;
+}
+
+}  // namespace nsa

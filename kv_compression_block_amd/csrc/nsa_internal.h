@@ -1,0 +1,98 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+// Nothing here is part of the public interface (include/nsa_cmp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+// Per-sequence extents and launch-tile ranges, uploaded into the workspace.
+// Tiles of one kernel are numbered sequence by sequence; inside a sequence
+// they run from the last row block (largest causal cost) to the first, and
+// the KV heads of a row block are adjacent.
+struct BatchEnt {
+    int32_t q_off;      // first query token of the sequence (global)
+    int32_t T;          // query tokens of the sequence
+    int32_t cmp_off;    // first compressed entry of the sequence (global)
+    int32_t n_cmp;      // compressed entries of the sequence
+    int32_t tile_off_a; // first tile of the attention kernel
+    int32_t n_rb_a;     // row blocks of the attention kernel (per KV head)
+    int32_t tile_off_c; // first tile of the importance/top-k kernel
+    int32_t n_rb_c;     // row blocks of the importance/top-k kernel
+    int32_t S_sel;      // select blocks of the sequence, ceil(T / l')
+    int32_t pad[3];
+};
+static_assert(sizeof(BatchEnt) == 48, "BatchEnt layout");
+
+// ---- compression kernel ---------------------------------------------------
+constexpr int kCompressMaxSeg = 128;   // sequences per launch (more -> several launches)
+
+struct CompressParams {
+    const uint16_t* x;   // [T, N, D]
+    const uint16_t* w;   // [l, N]
+    uint16_t* y;         // [T2, N, D]
+    int N, D, l, d;
+    int nseg;
+    int max_blocks_x;
+    int in_off[kCompressMaxSeg];   // first input token of each sequence
+    int out_off[kCompressMaxSeg];  // first output entry of each sequence
+    int n_out[kCompressMaxSeg];    // output entries of each sequence
+};
+
+hipError_t launch_compress(const CompressParams& p, hipStream_t stream);
+
+// ---- attention kernels ------------------------------------------------------
+struct AttnParams {
+    const uint16_t* q;    // [T1, N1, D1]
+    const uint16_t* kc;   // [T2, N2, D1]
+    const uint16_t* vc;   // [T2, N2, D2]
+    uint16_t* out;        // [T1, N1, D2]
+    float* smax;          // [T1, N1, 8]
+    float* ssum;          // [T1, N1, 8]
+    const BatchEnt* bt;   // [B], device
+    int B, N1, N2, G;
+    int l, d;
+    float c;              // |scale| * log2(e): raw score -> base-2 exponent
+    float abs_scale;      // |scale|: raw score -> natural-unit score
+    float thr;            // running-max slack before rescaling, raw-score units
+    uint32_t qsign;       // 0x80008000 when scale < 0 (q negated), else 0
+};
+
+// Rows per workgroup of the attention kernel (4 waves x 64 query rows).
+constexpr int kAttnRowsPerWG = 256;
+constexpr int kKeyTile = 64;
+
+hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream);
+bool cmp_attn_supported(int d1, int d2);
+
+struct TopkParams {
+    const uint16_t* q;    // [T1, N1, D1]
+    const uint16_t* kc;   // [T2, N2, D1]
+    const float* smax;    // [T1, N1, 8]
+    const float* ssum;    // [T1, N1, 8]
+    int32_t* topk;        // [T1, N2, count]
+    float* pslc;          // NULL or [T1, N2, s_stride]
+    const BatchEnt* bt;   // [B], device
+    int B, N1, N2, G;
+    int l, d, lsel, count;
+    int R, H;             // R = l'/d; H = largest remap offset = R + floor(l/d) - 2
+    float coef[16];       // remap coefficient of P_cmp[R*j - r], r = 0..H
+    float c;              // |scale| * log2(e)
+    uint32_t qsign;
+    int s_stride;         // row stride of pslc (max select blocks)
+    int sb;               // LDS row length of the importance scores (multiple of 64)
+    int npl;              // candidates per lane in top-k, sb / 64
+    int waves;            // waves per workgroup
+};
+
+constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)
+constexpr int kTopkMaxNpl = 16;        // at most 1024 select blocks per sequence
+
+int topk_log2_gp(int G);               // log2 of the padded group size, -1 if G > 64
+size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb);
+hipError_t launch_slc_topk(int d1, int log2gp, const TopkParams& p, int n_tiles, size_t lds,
+                           hipStream_t stream);
+bool slc_topk_supported(int d1);
+
+}  // namespace nsa

@@ -1,0 +1,450 @@
+// Kernel (c): importance scores and top-k, steps 4-7 of
+// "mindspore.ops.nsa_compress_attention".
+//
+//   P_slc'[t, g, j] = sum_{h in group g} sum_{m < R} sum_{n < L2} P_cmp^h[R*j - m - n]
+//   R = l'/d, L2 = floor(l/d); then the top-k mask (candidates j*l' <= t) and
+//   the select_block_count largest scores, ties to the lower j, -1 padded.
+//
+// P_cmp is recomputed rather than stored: S = Q K^T on MFMA (bf16 in, fp32
+// out) and P = exp2(S * c - bias) with bias = max * log2(e) + log2(sum) from
+// the attention kernel's outputs, i.e. already normalised.
+//
+// Design (gfx950):
+//   * Rows are (token, query head) with the group padded to a power of two GP
+//     (<= 64), so the GP heads of a token are adjacent rows of one wave.  S is
+//     computed un-transposed (rows = heads, columns = compressed entries):
+//     the sum over a token's heads is then an in-lane sum of accumulator
+//     registers plus, for GP >= 8, one exchange with the lane 32 away.
+//   * The group-summed P of each token goes to a 128-entry LDS ring indexed
+//     by compressed-entry number; after every 64-entry tile the select blocks
+//     whose whole stencil is available are finished as a fixed-order weighted
+//     sum of at most H+1 ring entries (the remap written as a stencil over
+//     r = m + n with coefficient c(r) = number of (m, n) pairs).  The ring
+//     keeps the H entries a later block still needs.
+//   * Top-k per (token, KV head) row is a wave-wide radix select on the
+//     float bits (scores are >= 0, so their bit patterns order like the
+//     values): 31 ballot-count rounds find the k-th largest score; the rows
+//     above it and the lowest-index ties are compacted, then sorted by
+//     (score desc, index asc) with a 32-lane bitonic network.
+//   * Deterministic: every sum has a fixed order; no atomics.
+#include "nsa_device.h"
+
+namespace nsa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D1, int LOG2GP>
+__global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
+{
+    constexpr int GP = 1 << LOG2GP;
+    constexpr int TOKW = 64 / GP;           // tokens per wave
+    constexpr int KT = kKeyTile;
+    constexpr int KS = D1 + 8;
+    constexpr int NKS = D1 / 16;
+    constexpr int KCH = D1 / 8;
+    constexpr int KLD = KT * KCH / 256;
+    constexpr int RING = kTopkRing;
+    constexpr int HSH = 4 >> LOG2GP;        // token offset of the upper half-wave (GP <= 4)
+
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int waves = p.waves;
+    uint16_t* Ks = (uint16_t*)smem;
+    float* ring = (float*)(smem + KT * KS * 2);
+    float* bins = ring + waves * TOKW * RING;
+    uint32_t* stg = (uint32_t*)(bins + waves * TOKW * p.sb);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+    const int nthreads = waves * 64;
+
+    // ---- tile -> (sequence, KV head, row block) -------------------------------
+    const int tile = blockIdx.x;
+    const int b = find_batch<false>(p.bt, p.B, tile);
+    const BatchEnt be = p.bt[b];
+    const int idx = tile - be.tile_off_c;
+    const int g = idx % p.N2;
+    const int rb = be.n_rb_c - 1 - idx / p.N2;
+    const int G = p.G;
+    const int tok_wg = rb * ((waves * 64) >> LOG2GP);
+    const int tok_w = tok_wg + wave * TOKW;
+
+    // Q rows as the A operand: lane l32 holds row rb_*32 + l32 of its wave.
+    bf16x8 qa[2][NKS];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const int pr = rr * 32 + l32;
+        const int tok = tok_w + (pr >> LOG2GP);
+        const int hh = pr & (GP - 1);
+        const bool valid = tok < be.T && hh < G;
+        const uint16_t* qrow = p.q + ((int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh) * D1 + hf * 8;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (valid) {
+                v = *(const u32x4*)(qrow + ks * 16);
+                v ^= p.qsign;
+            }
+            qa[rr][ks] = as_bf16x8(v);
+        }
+    }
+    // Per accumulator register: P = exp2(S*c - bias) is the normalised P_cmp.
+    // Rows that are padding, past the sequence, or see no block get +inf.
+    float bias[2][16];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const int tok = tok_w + (pr >> LOG2GP);
+            const int hh = pr & (GP - 1);
+            float bv = INFINITY;
+            if (tok < be.T && hh < G) {
+                const int64_t row = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
+                const float m = p.smax[row * 8];
+                const float L = p.ssum[row * 8];
+                if (L > 0.f)
+                    bv = m * kLog2e + log2f(L);
+            }
+            bias[rr][r] = bv;
+        }
+    }
+
+    const int tok_last = min(tok_wg + ((waves * 64) >> LOG2GP), be.T) - 1;
+    const int nv_max = tok_last >= tok_wg ? n_visible(tok_last, p.l, p.d, be.n_cmp) : 0;
+    const int nv_min = n_visible(tok_wg, p.l, p.d, be.n_cmp);
+    const int n_kt = (nv_max + KT - 1) / KT;
+
+    for (int x = tid; x < waves * TOKW * RING; x += nthreads)
+        ring[x] = 0.f;
+
+    const int64_t kstride = (int64_t)p.N2 * D1;
+    const uint16_t* kbase = p.kc + ((int64_t)be.cmp_off * p.N2 + g) * D1;
+    u32x4 kreg[KLD];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int cidx = tid + 256 * i;
+            const int row = cidx / KCH;
+            const int col = cidx % KCH;
+            const int key = kt * KT + row;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (key < be.n_cmp)
+                v = *(const u32x4*)(kbase + (int64_t)key * kstride + col * 8);
+            kreg[i] = v;
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int i = 0; i < KLD; ++i) {
+            const int cidx = tid + 256 * i;
+            const int row = cidx / KCH;
+            const int col = cidx % KCH;
+            *(u32x4*)&Ks[row * KS + col * 8] = kreg[i];
+        }
+    };
+    // A workgroup narrower than 256 threads stages K in several passes.
+    auto stage_tile = [&](int kt) {
+        for (int base = 0; base < 256; base += nthreads) {
+#pragma unroll
+            for (int i = 0; i < KLD; ++i) {
+                const int cidx = tid + base + 256 * i;
+                const int row = cidx / KCH;
+                const int col = cidx % KCH;
+                const int key = kt * KT + row;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (key < be.n_cmp)
+                    v = *(const u32x4*)(kbase + (int64_t)key * kstride + col * 8);
+                *(u32x4*)&Ks[row * KS + col * 8] = v;
+            }
+        }
+    };
+    const bool full_wg = (nthreads == 256);
+
+    const float c = p.c;
+    const int R = p.R;
+    const int H = p.H;
+    float* my_ring = ring + wave * TOKW * RING;
+    float* my_bins = bins + wave * TOKW * p.sb;
+
+    if (n_kt > 0) {
+        if (full_wg) {
+            load_tile(0);
+            store_tile();
+        } else {
+            stage_tile(0);
+        }
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < n_kt; ++kt) {
+        if (full_wg && kt + 1 < n_kt)
+            load_tile(kt + 1);
+
+        f32x16 s[2][2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[rr][kb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 kf = as_bf16x8(*(const u32x4*)&Ks[(kb * 32 + l32) * KS + ks * 16 + hf * 8]);
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr)
+                    s[rr][kb] = mfma32(qa[rr][ks], kf, s[rr][kb]);
+            }
+        }
+
+        // P, masked, summed over the heads of each token.
+        const bool need_mask = (kt + 1) * KT > nv_min;
+        float acc[TOKW][2];
+#pragma unroll
+        for (int tw = 0; tw < TOKW; ++tw)
+            acc[tw][0] = acc[tw][1] = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int key = kt * KT + kb * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pv = fast_exp2(fmaf(s[rr][kb][r], c, -bias[rr][r]));
+                    if (need_mask) {
+                        const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        const int tok = tok_w + (pr >> LOG2GP);
+                        // visible iff key*d + l - 1 <= tok
+                        pv = (key * p.d + p.l - 1 <= tok) ? pv : 0.f;
+                    }
+                    acc[(rr * 32 + 8 * (r >> 2) + (r & 3)) >> LOG2GP][kb] += pv;
+                }
+            }
+        }
+#pragma unroll
+        for (int tw = 0; tw < TOKW; ++tw) {
+            if constexpr (GP >= 8) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const float v = half_sum(acc[tw][kb]);
+                    if (hf == 0)
+                        my_ring[tw * RING + ((kt * KT + kb * 32 + l32) & (RING - 1))] = v;
+                }
+            } else {
+                if ((tw & HSH) == 0) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+                        my_ring[(tw + hf * HSH) * RING + ((kt * KT + kb * 32 + l32) & (RING - 1))] = acc[tw][kb];
+                }
+            }
+        }
+        __syncthreads();   // ring written; every wave is done reading Ks
+
+        if (kt + 1 < n_kt) {
+            if (full_wg)
+                store_tile();
+            else
+                stage_tile(kt + 1);
+        }
+
+        // Select blocks j whose stencil top R*j lies in this tile.
+        const int key0 = kt * KT;
+        const int jlo = (key0 + R - 1) / R;
+        const int jhi = min((key0 + KT + R - 1) / R, be.S_sel);
+        const int nj = jhi - jlo;
+        if (nj > 0) {
+            for (int x = lane; x < TOKW * nj; x += 64) {
+                const int tw = x / nj;
+                const int j = jlo + (x - tw * nj);
+                const float* rg = my_ring + tw * RING;
+                float v = 0.f;
+                for (int r = 0; r <= H; ++r)
+                    v = fmaf(p.coef[r], rg[(R * j - r) & (RING - 1)], v);
+                my_bins[tw * p.sb + j] = v;
+            }
+        }
+        __syncthreads();   // bins read the ring before the next tile overwrites it
+    }
+
+    // Select blocks past the last tile: only entries < keys_done can be non-zero.
+    {
+        const int keys_done = n_kt * KT;
+        const int jlo = (keys_done + R - 1) / R;
+        const int nj = be.S_sel - jlo;
+        if (nj > 0) {
+            for (int x = lane; x < TOKW * nj; x += 64) {
+                const int tw = x / nj;
+                const int j = jlo + (x - tw * nj);
+                const float* rg = my_ring + tw * RING;
+                float v = 0.f;
+                for (int r = 0; r <= H; ++r) {
+                    const int k = R * j - r;
+                    const float e = (k < keys_done) ? rg[k & (RING - 1)] : 0.f;
+                    v = fmaf(p.coef[r], e, v);
+                }
+                my_bins[tw * p.sb + j] = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- top-k per (token, KV head) ---------------------------------------------
+    uint32_t* my_stg = stg + wave * 64;      // [0,32): score bits, [32,64): index
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int tw = 0; tw < TOKW; ++tw) {
+        const int tok = tok_w + tw;
+        const bool active = tok < be.T;
+        const float* brow = my_bins + tw * p.sb;
+        const int64_t tg = (int64_t)be.q_off + tok;
+        int kk = 0;
+        if (active) {
+            if (p.pslc) {
+                float* dst = p.pslc + (tg * p.N2 + g) * p.s_stride;
+                for (int j = lane; j < p.s_stride; j += 64)
+                    dst[j] = (j < be.S_sel) ? brow[j] : 0.f;
+            }
+            const int nvalid = min(tok / p.lsel + 1, be.S_sel);
+            kk = min(p.count, nvalid);
+            uint32_t key[kTopkMaxNpl];
+            bool valid[kTopkMaxNpl];
+#pragma unroll
+            for (int i = 0; i < kTopkMaxNpl; ++i) {
+                const int j = lane + 64 * i;
+                valid[i] = (i < p.npl) && (j < nvalid);
+                key[i] = valid[i] ? __float_as_uint(brow[j]) : 0u;
+            }
+            // Radix select of the kk-th largest bit pattern.
+            uint32_t tau = 0;
+            if (nvalid > kk) {
+                for (int bit = 30; bit >= 0; --bit) {
+                    const uint32_t cand = tau | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int i = 0; i < kTopkMaxNpl; ++i)
+                        if (i < p.npl)
+                            cnt += __popcll(__ballot(valid[i] && key[i] >= cand));
+                    if (cnt >= kk)
+                        tau = cand;
+                }
+            }
+            int n_gt = 0;
+#pragma unroll
+            for (int i = 0; i < kTopkMaxNpl; ++i)
+                if (i < p.npl)
+                    n_gt += __popcll(__ballot(valid[i] && key[i] > tau));
+            const int need_eq = kk - n_gt;
+            int pos_gt = 0, pos_eq = 0;
+#pragma unroll
+            for (int i = 0; i < kTopkMaxNpl; ++i) {
+                if (i < p.npl) {
+                    const bool gt = valid[i] && key[i] > tau;
+                    const bool eq = valid[i] && key[i] == tau;
+                    const uint64_t bg = __ballot(gt);
+                    const uint64_t beq = __ballot(eq);
+                    const int rg = __popcll(bg & lt_mask);
+                    const int re = __popcll(beq & lt_mask);
+                    if (gt) {
+                        my_stg[pos_gt + rg] = key[i];
+                        my_stg[32 + pos_gt + rg] = (uint32_t)(lane + 64 * i);
+                    }
+                    if (eq && pos_eq + re < need_eq) {
+                        my_stg[n_gt + pos_eq + re] = key[i];
+                        my_stg[32 + n_gt + pos_eq + re] = (uint32_t)(lane + 64 * i);
+                    }
+                    pos_gt += __popcll(bg);
+                    pos_eq += __popcll(beq);
+                }
+            }
+        }
+        __syncthreads();
+        if (active) {
+            // Bitonic sort of kk <= 32 (score, index) pairs on lanes 0..31:
+            // score descending, index ascending; pads sort last.
+            const int sl = lane & 31;
+            int sk = (sl < kk) ? (int)my_stg[sl] : -1;
+            int si = (sl < kk) ? (int)my_stg[32 + sl] : 0x7FFFFFFF;
+            for (int k2 = 2; k2 <= 32; k2 <<= 1) {
+                for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
+                    const int pk = __shfl_xor(sk, jj);
+                    const int pi = __shfl_xor(si, jj);
+                    const bool p_first = (pk > sk) || (pk == sk && pi < si);
+                    const bool m_first = (sk > pk) || (sk == pk && si < pi);
+                    const bool lower = (sl & jj) == 0;
+                    const bool asc = (sl & k2) == 0;
+                    const bool want_first = (lower == asc);
+                    const bool take = want_first ? p_first : m_first;
+                    if (take) {
+                        sk = pk;
+                        si = pi;
+                    }
+                }
+            }
+            if (lane < p.count)
+                p.topk[(tg * p.N2 + g) * p.count + lane] = (lane < kk) ? si : -1;
+        }
+        __syncthreads();
+    }
+}
+
+template <int D1, int LOG2GP>
+static hipError_t launch_t(const TopkParams& p, int n_tiles, size_t lds, hipStream_t stream)
+{
+    auto kern = k_slc_topk<D1, LOG2GP>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(n_tiles), dim3(p.waves * 64), lds, stream, p);
+    return hipGetLastError();
+}
+
+template <int D1>
+static hipError_t launch_d(int log2gp, const TopkParams& p, int n_tiles, size_t lds, hipStream_t stream)
+{
+    switch (log2gp) {
+    case 0: return launch_t<D1, 0>(p, n_tiles, lds, stream);
+    case 1: return launch_t<D1, 1>(p, n_tiles, lds, stream);
+    case 2: return launch_t<D1, 2>(p, n_tiles, lds, stream);
+    case 3: return launch_t<D1, 3>(p, n_tiles, lds, stream);
+    case 4: return launch_t<D1, 4>(p, n_tiles, lds, stream);
+    case 5: return launch_t<D1, 5>(p, n_tiles, lds, stream);
+    case 6: return launch_t<D1, 6>(p, n_tiles, lds, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int topk_log2_gp(int G)
+{
+    int lg = 0;
+    while ((1 << lg) < G)
+        ++lg;
+    return lg <= 6 ? lg : -1;
+}
+
+size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb)
+{
+    const size_t tokw = (size_t)(64 >> log2gp);
+    return (size_t)kKeyTile * (d1 + 8) * 2 + (size_t)waves * tokw * kTopkRing * 4 +
+           (size_t)waves * tokw * sb * 4 + (size_t)waves * 64 * 4;
+}
+
+bool slc_topk_supported(int d1) { return d1 == 64 || d1 == 128 || d1 == 192; }
+
+hipError_t launch_slc_topk(int d1, int log2gp, const TopkParams& p, int n_tiles, size_t lds,
+                           hipStream_t stream)
+{
+    if (n_tiles <= 0)
+        return hipSuccess;
+    if (d1 == 64) return launch_d<64>(log2gp, p, n_tiles, lds, stream);
+    if (d1 == 128) return launch_d<128>(log2gp, p, n_tiles, lds, stream);
+    if (d1 == 192) return launch_d<192>(log2gp, p, n_tiles, lds, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace nsa

@@ -1,0 +1,153 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+* small workloads (all tokens), the five workloads' head/dim/parameter
+  settings with shorter, ragged sequences: compression, then attention,
+  softmax statistics, importance scores and top-k -- staged (the GPU's
+  attention consumes the oracle's compressed K/V) and end to end;
+* the five workloads at full size, in the launch configuration the
+  benchmark times: compression in full, attention on sampled tokens;
+* edge cases: empty and short sequences, negative and zero scale, groups
+  that are not powers of two, MHA, other remap stencils, count 1;
+* bitwise determinism across runs.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (assert_close_out, assert_pslc, assert_softmax_stats, assert_topk,
+                    bf16_to_f64, gpu_attention, gpu_compress, log, upload_bits)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    0: synth.WORKLOADS[0],
+    1: synth.small_variant(1, [1500, 777]),
+    2: synth.small_variant(2, [1000, 2050, 64, 17]),
+    3: synth.small_variant(3, [3000]),
+    4: synth.small_variant(4, [2000, 1500, 300]),
+}
+
+
+def _check_all(wl, g, ref, tokens, tie_rel=1e-4):
+    assert_close_out(bf16_to_f64(g["out"])[tokens] if g["out"].shape[0] != len(tokens) else bf16_to_f64(g["out"]),
+                     ref["out"], "attention_out")
+    gmax = g["max"].cpu().numpy()
+    gsum = g["sum"].cpu().numpy()
+    gp = g["pslc"].cpu().numpy()
+    gt = g["topk"].cpu().numpy()
+    if gmax.shape[0] != len(tokens):
+        gmax, gsum, gp, gt = gmax[tokens], gsum[tokens], gp[tokens], gt[tokens]
+    assert_softmax_stats(gmax, gsum, ref["max"], ref["sum"])
+    assert_pslc(gp, ref["pslc"])
+    assert_topk(wl, tokens, gt, ref["topk"], ref["pslc"], tie_rel=tie_rel)
+
+
+def _run_small(wl, end_to_end=True):
+    log(f"[case] {wl.name}: generate on GPU")
+    inp = synth.make_inputs(wl, device="cuda")
+    bits = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    log(f"[case] {wl.name}: oracle")
+    ref = oracle.run(wl, bits["q"], bits["k"], bits["v"], bits["w"])
+    log(f"[case] {wl.name}: GPU compress")
+    kc_g = gpu_compress(wl, inp["k"], inp["w"])
+    vc_g = gpu_compress(wl, inp["v"], inp["w"])
+    torch.cuda.synchronize()
+    assert_close_out(bf16_to_f64(kc_g), ref["kc"], "compressed K")
+    assert_close_out(bf16_to_f64(vc_g), ref["vc"], "compressed V")
+    log(f"[case] {wl.name}: GPU attention on the oracle's compressed K/V")
+    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bf16"]), upload_bits(ref["vc_bf16"]))
+    _check_all(wl, g, ref, ref["tokens"])
+    if end_to_end:
+        log(f"[case] {wl.name}: GPU attention on its own compressed K/V")
+        g2 = gpu_attention(wl, inp["q"], kc_g, vc_g)
+        _check_all(wl, g2, ref, ref["tokens"], tie_rel=1e-3)
+    return inp, g
+
+
+@pytest.mark.parametrize("wid", [0, 1, 2, 3, 4])
+def test_small_workloads_all_tokens(wid):
+    _run_small(SMALL[wid])
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_full_size_workloads_sampled(wid):
+    wl = synth.WORKLOADS[wid]
+    log(f"[case] full {wl.name}: generate on GPU")
+    inp = synth.make_inputs(wl, device="cuda")
+    kb, vb, wb = synth.bf16_bits(inp["k"]), synth.bf16_bits(inp["v"]), synth.bf16_bits(inp["w"])
+    actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
+    log(f"[case] full {wl.name}: oracle compress")
+    kc_ref = oracle.compress(kb, wb, actq, wl.l, wl.d)
+    vc_ref = oracle.compress(vb, wb, actq, wl.l, wl.d)
+    log(f"[case] full {wl.name}: GPU compress")
+    kc_g = gpu_compress(wl, inp["k"], inp["w"])
+    vc_g = gpu_compress(wl, inp["v"], inp["w"])
+    torch.cuda.synchronize()
+    assert_close_out(bf16_to_f64(kc_g), kc_ref, "compressed K")
+    assert_close_out(bf16_to_f64(vc_g), vc_ref, "compressed V")
+    del kc_g, vc_g
+    kc_b, vc_b = oracle.to_bf16(kc_ref), oracle.to_bf16(vc_ref)
+    tokens = synth.sample_tokens(wl, per_seq=6)
+    log(f"[case] full {wl.name}: oracle attention on {len(tokens)} tokens")
+    q_rows = synth.bf16_bits(inp["q"][torch.from_numpy(tokens).cuda()])
+    ref = oracle.attention(q_rows, tokens, kc_b, vc_b, actq, oracle.cmp_prefix(wl.seqlens, wl.l, wl.d),
+                           wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count)
+    log(f"[case] full {wl.name}: GPU attention (all tokens)")
+    g = gpu_attention(wl, inp["q"], upload_bits(kc_b), upload_bits(vc_b))
+    tok_t = torch.from_numpy(tokens).cuda()
+    gs = {"out": g["out"][tok_t], "max": g["max"][tok_t], "sum": g["sum"][tok_t],
+          "pslc": g["pslc"][tok_t], "topk": g["topk"][tok_t]}
+    _check_all(wl, gs, ref, tokens)
+    # Properties that hold for every row of the full output.
+    log(f"[case] full {wl.name}: whole-output properties")
+    assert torch.isfinite(g["out"].float()).all()
+    gsum = g["sum"][..., 0]
+    gmax = g["max"][..., 0]
+    assert bool(((gsum > 0) == torch.isfinite(gmax)).all())
+    topk = g["topk"]
+    assert int(topk.max()) < max(-(-T // wl.lsel) for T in wl.seqlens)
+    assert int(topk[:, :, 0].min()) == 0 or int(topk[:, :, 0].min()) >= 0
+
+
+BASE = synth.Workload("edge", (300,), 8, 2, 64, 64, 32, 16, 64, 4, 0.125, seed=900)
+EDGES = {
+    "short-and-empty-seqs": dataclasses.replace(BASE, seqlens=(5, 0, 31, 32, 33, 47, 48, 200, 1, 130)),
+    "negative-scale": dataclasses.replace(BASE, scale=-0.09, seqlens=(400, 77)),
+    "zero-scale": dataclasses.replace(BASE, scale=0.0, seqlens=(333,)),
+    "group-of-3": dataclasses.replace(BASE, N1=12, N2=4, D1=128, D2=64, seqlens=(520, 64)),
+    "mha-group-1": dataclasses.replace(BASE, N1=4, N2=4, seqlens=(700, 129)),
+    "group-of-32": dataclasses.replace(BASE, N1=64, N2=2, D1=128, D2=128, seqlens=(600,)),
+    "stencil-R3": dataclasses.replace(BASE, l=48, d=16, lsel=48, count=8, seqlens=(900, 250)),
+    "stencil-R8": dataclasses.replace(BASE, l=128, d=16, lsel=128, count=32, seqlens=(1500,)),
+    "stride-64": dataclasses.replace(BASE, l=64, d=64, lsel=128, count=3, seqlens=(1000, 65)),
+    "count-1": dataclasses.replace(BASE, count=1, seqlens=(500,)),
+    "d192-group-16": dataclasses.replace(BASE, N1=16, N2=1, D1=192, D2=64, seqlens=(777,)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGES))
+def test_edge_cases(name):
+    _run_small(dataclasses.replace(EDGES[name], name=name))
+
+
+def test_bitwise_deterministic():
+    wl = SMALL[2]
+    log(f"[case] determinism {wl.name}")
+    inp = synth.make_inputs(wl, device="cuda")
+    kc1 = gpu_compress(wl, inp["k"], inp["w"])
+    vc1 = gpu_compress(wl, inp["v"], inp["w"])
+    a = gpu_attention(wl, inp["q"], kc1, vc1)
+    kc2 = gpu_compress(wl, inp["k"], inp["w"])
+    vc2 = gpu_compress(wl, inp["v"], inp["w"])
+    b = gpu_attention(wl, inp["q"], kc2, vc2)
+    assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+    # the debug output does not change anything else
+    c = gpu_attention(wl, inp["q"], kc1, vc1, return_p_slc=False)
+    for k in ("out", "topk", "max", "sum"):
+        assert torch.equal(a[k], c[k]), k

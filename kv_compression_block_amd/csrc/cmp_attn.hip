@@ -20,6 +20,8 @@
 //     running reference max only moves when a tile's max exceeds it by more
 //     than 2^8, so the O rescale is rare.  The true max is tracked apart for
 //     the softmax_max output.
+#include <type_traits>
+
 #include "nsa_device.h"
 
 namespace nsa {
@@ -63,10 +65,10 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
     const int hf = lane >> 5;
 
     // ---- tile -> (sequence, KV head, row block) ---------------------------
-    const int tile = blockIdx.x;
-    const int b = find_batch<true>(p.bt, p.B, tile);
+    const int wg_tile = blockIdx.x;
+    const int b = find_batch<true>(p.bt, p.B, wg_tile);
     const BatchEnt be = p.bt[b];
-    const int idx = tile - be.tile_off_a;
+    const int idx = wg_tile - be.tile_off_a;
     const int g = idx % p.N2;
     const int rb = be.n_rb_a - 1 - idx / p.N2;
     const int G = p.G;
@@ -178,12 +180,15 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
     }
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
+    // One 64-entry tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  The
+    // masked variant only runs on the last tiles, where some rows of the
+    // workgroup stop seeing entries.
+    auto key_tile = [&](const int kt, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = kt & 1;
         if (kt + 1 < n_kt)
             load_tile(kt + 1);
 
-        // S^T = K Q^T for 64 keys x 64 queries.
         f32x16 s[2][2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
@@ -203,28 +208,29 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
             }
         }
 
-        // Mask, online softmax, P (in place of S).
-        const bool need_mask = (kt + 1) * KT > nv_min;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
+            if constexpr (MASK) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kt * KT + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        s[qb][kb][r] = (key < nvq[qb]) ? s[qb][kb][r] : -INFINITY;
+                    }
+            }
             float tmax = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float v = s[qb][kb][r];
-                    if (need_mask) {
-                        const int key = kt * KT + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        v = (key < nvq[qb]) ? v : -INFINITY;
-                        s[qb][kb][r] = v;
-                    }
-                    tmax = fmaxf(tmax, v);
-                }
-            }
+                for (int r = 0; r < 16; ++r)
+                    tmax = fmaxf(tmax, s[qb][kb][r]);
             tmax = half_max(tmax);
             mtrue[qb] = fmaxf(mtrue[qb], tmax);
             const bool grow_ref = tmax > mref[qb] + p.thr;
-            if (__ballot(grow_ref)) {
+            if (__builtin_expect(__ballot(grow_ref) != 0, 0)) {
+                // Rare: the running reference max moves; rescale O and the sum.
+                __asm__ volatile("" ::: "memory");
                 float alpha = 1.f;
                 if (grow_ref) {
                     alpha = (mref[qb] == -INFINITY) ? 0.f : fast_exp2((mref[qb] - tmax) * c);
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
                 for (int r = 0; r < 16; ++r) {
                     const float sv = s[qb][kb][r];
                     float pv = fast_exp2(fmaf(sv, c, nb));
-                    if (need_mask)
+                    if constexpr (MASK)
                         pv = (sv == -INFINITY) ? 0.f : pv;
                     s[qb][kb][r] = pv;
                     ps += pv;
@@ -254,7 +260,6 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
             lsum[qb] += ps;
         }
 
-        // O^T += V^T P^T, 16 keys per MFMA.
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int kb = kk >> 1;
@@ -280,7 +285,15 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
         if (kt + 1 < n_kt)
             store_tile(buf ^ 1);
         __syncthreads();
-    }
+    };
+
+    // Tiles every row of the workgroup sees in full need no mask.
+    const int n_full = min(nv_min / KT, n_kt);
+    int kt = 0;
+    for (; kt < n_full; ++kt)
+        key_tile(kt, std::false_type{});
+    for (; kt < n_kt; ++kt)
+        key_tile(kt, std::true_type{});
 
     // ---- epilogue ----------------------------------------------------------
 #pragma unroll

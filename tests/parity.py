@@ -12,6 +12,16 @@ Tolerances:
   the rest -1; picks are candidates and unique; every pick outside the
   oracle's set has an oracle score >= (1 - tie_rel) * the oracle's k-th
   score (tie_rel = 1e-4 when both sides see identical compressed K/V).
+
+Staged runs (the GPU's attention consumes the oracle's compressed K/V) use
+the bounds above.  End-to-end runs (the GPU consumes its own compressed K/V)
+compare against an oracle fed with the oracle's compressed K/V: the two
+compressions round the same exact sums to bfloat16 and can differ by one
+bf16 ulp (2^-8 relative) in an element, which moves a score by about
+|scale| * |q_e| * 2^-8 |k_e| per differing element (observed: 1.0e-3 on a
+softmax max near 4).  There the softmax max/sum and P_slc' bounds are
+widened to 1e-2 and the top-k tie band to 1e-2; attention_out keeps its
+2e-2 + 1e-2|ref| bound.
 """
 from __future__ import annotations
 
@@ -82,7 +92,8 @@ def assert_close_out(got: np.ndarray, ref: np.ndarray, what: str):
     assert not bad.any(), f"{what}: {int(bad.sum())} elements outside 2e-2 + 1e-2|ref|; first at {np.argwhere(bad)[0]}"
 
 
-def assert_softmax_stats(gmax: np.ndarray, gsum: np.ndarray, rmax: np.ndarray, rsum: np.ndarray):
+def assert_softmax_stats(gmax: np.ndarray, gsum: np.ndarray, rmax: np.ndarray, rsum: np.ndarray,
+                         max_atol: float = MAX_ATOL, sum_rtol: float = SUM_RTOL):
     """gmax/gsum: [n, N1, 8] float32 from the GPU; rmax/rsum: [n, N1] oracle."""
     for k in range(8):
         assert np.array_equal(gmax[..., k], gmax[..., 0]) and np.array_equal(gsum[..., k], gsum[..., 0])
@@ -95,16 +106,16 @@ def assert_softmax_stats(gmax: np.ndarray, gsum: np.ndarray, rmax: np.ndarray, r
         dm = np.abs(gm[fin] - rmax[fin])
         ds = np.abs(gs[fin] - rsum[fin]) / rsum[fin]
         log(f"  softmax max: max|err| {dm.max():.3e}; sum: max rel {ds.max():.3e}")
-        assert dm.max() <= MAX_ATOL
-        assert ds.max() <= SUM_RTOL
+        assert dm.max() <= max_atol
+        assert ds.max() <= sum_rtol
 
 
-def assert_pslc(gp: np.ndarray, rp: np.ndarray):
+def assert_pslc(gp: np.ndarray, rp: np.ndarray, rtol: float = PSLC_RTOL):
     """[n, N2, S] both; S of the GPU may exceed nothing: same stride."""
     assert gp.shape == rp.shape, (gp.shape, rp.shape)
     zero = rp == 0
     assert np.all(gp[zero] == 0), f"P_slc: {int((gp[zero] != 0).sum())} non-zeros where the oracle is 0"
-    bad = np.abs(gp - rp) > PSLC_RTOL * np.abs(rp) + PSLC_ATOL
+    bad = np.abs(gp - rp) > rtol * np.abs(rp) + PSLC_ATOL
     mabs, mrel = err_stats(gp[~zero], rp[~zero])
     log(f"  P_slc: max|err| {mabs:.3e}  max rel {mrel:.3e}")
     assert not bad.any(), f"P_slc: {int(bad.sum())} outside tolerance; first at {np.argwhere(bad)[0]}"

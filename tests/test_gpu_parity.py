@@ -32,18 +32,18 @@ SMALL = {
 }
 
 
-def _check_all(wl, g, ref, tokens, tie_rel=1e-4):
-    assert_close_out(bf16_to_f64(g["out"])[tokens] if g["out"].shape[0] != len(tokens) else bf16_to_f64(g["out"]),
-                     ref["out"], "attention_out")
-    gmax = g["max"].cpu().numpy()
-    gsum = g["sum"].cpu().numpy()
-    gp = g["pslc"].cpu().numpy()
-    gt = g["topk"].cpu().numpy()
-    if gmax.shape[0] != len(tokens):
-        gmax, gsum, gp, gt = gmax[tokens], gsum[tokens], gp[tokens], gt[tokens]
-    assert_softmax_stats(gmax, gsum, ref["max"], ref["sum"])
-    assert_pslc(gp, ref["pslc"])
-    assert_topk(wl, tokens, gt, ref["topk"], ref["pslc"], tie_rel=tie_rel)
+def _check_all(wl, g, ref, tokens, staged=True):
+    """g: GPU outputs whose rows are the given tokens, in order."""
+    assert_close_out(bf16_to_f64(g["out"]), ref["out"], "attention_out")
+    gmax, gsum = g["max"].cpu().numpy(), g["sum"].cpu().numpy()
+    if staged:
+        assert_softmax_stats(gmax, gsum, ref["max"], ref["sum"])
+        assert_pslc(g["pslc"].cpu().numpy(), ref["pslc"])
+        assert_topk(wl, tokens, g["topk"].cpu().numpy(), ref["topk"], ref["pslc"], tie_rel=1e-4)
+    else:
+        assert_softmax_stats(gmax, gsum, ref["max"], ref["sum"], max_atol=1e-2, sum_rtol=1e-2)
+        assert_pslc(g["pslc"].cpu().numpy(), ref["pslc"], rtol=1e-2)
+        assert_topk(wl, tokens, g["topk"].cpu().numpy(), ref["topk"], ref["pslc"], tie_rel=1e-2)
 
 
 def _run_small(wl, end_to_end=True):
@@ -64,7 +64,7 @@ def _run_small(wl, end_to_end=True):
     if end_to_end:
         log(f"[case] {wl.name}: GPU attention on its own compressed K/V")
         g2 = gpu_attention(wl, inp["q"], kc_g, vc_g)
-        _check_all(wl, g2, ref, ref["tokens"], tie_rel=1e-3)
+        _check_all(wl, g2, ref, ref["tokens"], staged=False)
     return inp, g
 
 

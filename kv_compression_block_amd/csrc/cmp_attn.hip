@@ -4,12 +4,16 @@
 // sum outputs.
 //
 // Design (gfx950, bf16 MFMA 32x32x16, fp32 accumulate):
-//   * A workgroup is 4 waves x 64 query rows of one (sequence, KV head).  A
-//     row is (token, query head of the group): the group's heads of a token
-//     are adjacent rows, so they share every K/V tile and every mask.
-//   * K and V tiles of 64 compressed entries are staged in LDS, double
-//     buffered; the next tile's global loads are in flight during the current
-//     tile's MFMAs.  K is stored row-major (entry, dim), V transposed
+//   * A workgroup is 4 waves; a wave owns QB blocks of 32 query rows of one
+//     (sequence, KV head).  A row is (token, query head of the group): the
+//     group's heads of a token are adjacent rows, so they share every K/V
+//     tile and every mask.  With QB = 1 a wave stays within 256 registers,
+//     so two waves share each SIMD (two workgroups per CU): one wave's
+//     softmax VALU work overlaps the other's MFMAs, and one workgroup's
+//     prologue/epilogue overlaps the other's main loop.
+//   * K and V tiles of KT compressed entries are staged in LDS, double
+//     buffered; the next tile's global loads are in flight during the
+//     current tile's MFMAs.  K is stored row-major (entry, dim), V transposed
 //     (dim, entry) with the entries of each 16-group ordered to match the
 //     layout the score accumulator leaves P in.
 //   * Scores are computed transposed, S^T = K Q^T: a lane owns one query
@@ -18,27 +22,15 @@
 //     the B operand of O^T += V^T P^T: no shuffles between the two MFMAs.
 //   * Online softmax in base 2 with the scale folded into one FMA; the
 //     running reference max only moves when a tile's max exceeds it by more
-//     than 2^8, so the O rescale is rare.  The true max is tracked apart for
-//     the softmax_max output.
+//     than 2^8, so the O rescale is rare (and is a real branch).  The true
+//     max is tracked apart for the softmax_max output.
+//   * Tiles that every row of the workgroup sees in full run a mask-free
+//     body; only the last one or two tiles of a workgroup apply the mask.
 #include <type_traits>
 
 #include "nsa_device.h"
 
 namespace nsa {
-
-template <int D1, int D2>
-struct AttnCfg {
-    static constexpr int KT = kKeyTile;     // compressed entries per tile
-    static constexpr int KS = D1 + 8;       // LDS row stride of K (bf16): 16 B pad
-    static constexpr int VS = KT + 8;       // LDS row stride of V^T (bf16): 16 B pad
-    static constexpr int NKS = D1 / 16;     // k-steps of QK^T
-    static constexpr int NDB = D2 / 32;     // 32-row blocks of O^T
-    static constexpr int KCH = D1 / 8;      // 16-byte chunks per K row
-    static constexpr int KLD = KT * KCH / 256;
-    static constexpr int VIT = 16 * (D2 / 8);  // (entry quad, dim octet) staging items
-    static_assert(KT * KCH % 256 == 0, "K tile staging");
-    static_assert(VIT <= 256, "V tile staging");
-};
 
 // Slot of entry quad kq (4 entries) inside the transposed V row: within each
 // group of 16 entries the quads are stored in the order 0, 2, 1, 3 so that a
@@ -50,11 +42,25 @@ __device__ __forceinline__ int v_slot(int kq)
     return (kq >> 2) * 16 + perm * 4;
 }
 
-template <int D1, int D2>
-__global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
+template <int D1, int D2, int QB, int KT>
+struct AttnCfg {
+    static constexpr int ROWS = 4 * 32 * QB;   // query rows per workgroup
+    static constexpr int KS = D1 + 8;          // LDS row stride of K (bf16): 16 B pad
+    static constexpr int VS = KT + 8;          // LDS row stride of V^T (bf16): 16 B pad
+    static constexpr int NKB = KT / 32;        // 32-entry blocks per tile
+    static constexpr int NKS = D1 / 16;        // k-steps of QK^T
+    static constexpr int NDB = D2 / 32;        // 32-row blocks of O^T
+    static constexpr int KCH = D1 / 8;         // 16-byte chunks per K row
+    static constexpr int KLD = KT * KCH / 256; // K chunks staged per thread
+    static constexpr int VIT = (KT / 4) * (D2 / 8);  // (entry quad, dim octet) items
+    static constexpr int VLD = (VIT + 255) / 256;    // V items per thread
+    static_assert(KT % 32 == 0 && KT * KCH % 256 == 0, "K tile staging");
+};
+
+template <int D1, int D2, int QB, int KT>
+__global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnParams p)
 {
-    using C = AttnCfg<D1, D2>;
-    constexpr int KT = C::KT;
+    using C = AttnCfg<D1, D2, QB, KT>;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * C::KS];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D2 * C::VS];
 
@@ -64,24 +70,24 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
     const int l32 = lane & 31;
     const int hf = lane >> 5;
 
-    // ---- tile -> (sequence, KV head, row block) ---------------------------
-    const int wg_tile = blockIdx.x;
-    const int b = find_batch<true>(p.bt, p.B, wg_tile);
+    // ---- workgroup -> (sequence, KV head, row block) -------------------------
+    const int wg = blockIdx.x;
+    const int b = find_batch<true>(p.bt, p.B, wg);
     const BatchEnt be = p.bt[b];
-    const int idx = wg_tile - be.tile_off_a;
+    const int idx = wg - be.tile_off_a;
     const int g = idx % p.N2;
     const int rb = be.n_rb_a - 1 - idx / p.N2;
     const int G = p.G;
     const int rows_total = be.T * G;
-    const int row_wg = rb * kAttnRowsPerWG;
+    const int row_wg = rb * C::ROWS;
 
-    int nvq[2];
-    bool vq[2];
-    int64_t grow[2];
-    bf16x8 qf[2][C::NKS];
+    int nvq[QB];
+    bool vq[QB];
+    int64_t grow[QB];
+    bf16x8 qf[QB][C::NKS];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const int r = row_wg + wave * 64 + qb * 32 + l32;
+    for (int qb = 0; qb < QB; ++qb) {
+        const int r = row_wg + (wave * QB + qb) * 32 + l32;
         vq[qb] = r < rows_total;
         const int tok = r / G;
         const int hh = r - tok * G;
@@ -98,20 +104,18 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
             qf[qb][ks] = as_bf16x8(v);
         }
     }
-    const int last_row = min(row_wg + kAttnRowsPerWG, rows_total) - 1;
+    const int last_row = min(row_wg + C::ROWS, rows_total) - 1;
     const int nv_max = n_visible(last_row / G, p.l, p.d, be.n_cmp);
     const int nv_min = n_visible(row_wg / G, p.l, p.d, be.n_cmp);
     const int n_kt = (nv_max + KT - 1) / KT;
 
-    // ---- tile staging ------------------------------------------------------
+    // ---- tile staging ----------------------------------------------------------
     const int64_t kv_stride1 = (int64_t)p.N2 * D1;
     const int64_t kv_stride2 = (int64_t)p.N2 * D2;
     const uint16_t* kbase = p.kc + ((int64_t)be.cmp_off * p.N2 + g) * D1;
     const uint16_t* vbase = p.vc + ((int64_t)be.cmp_off * p.N2 + g) * D2;
-    const int v_o = tid >> 4;        // dim octet of this thread's V item
-    const int v_kq = tid & 15;       // entry quad of this thread's V item
     u32x4 kreg[C::KLD];
-    u32x4 vreg[4];
+    u32x4 vreg[C::VLD][4];
 
     auto load_tile = [&](int kt) {
         const int key0 = kt * KT;
@@ -126,14 +130,18 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
                 v = *(const u32x4*)(kbase + (int64_t)key * kv_stride1 + col * 8);
             kreg[i] = v;
         }
-        if (tid < C::VIT) {
+#pragma unroll
+        for (int i = 0; i < C::VLD; ++i) {
+            const int item = tid + 256 * i;
+            const int v_o = item / (KT / 4);   // dim octet
+            const int v_kq = item % (KT / 4);  // entry quad
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int key = key0 + 4 * v_kq + e;
                 u32x4 v = {0u, 0u, 0u, 0u};
-                if (key < be.n_cmp)
+                if (item < C::VIT && key < be.n_cmp)
                     v = *(const u32x4*)(vbase + (int64_t)key * kv_stride2 + v_o * 8);
-                vreg[e] = v;
+                vreg[i][e] = v;
             }
         }
     };
@@ -145,33 +153,42 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
             const int col = cidx % C::KCH;
             *(u32x4*)&Ks[buf][row * C::KS + col * 8] = kreg[i];
         }
-        if (tid < C::VIT) {
-            const int slot = v_slot(v_kq);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int sh = (j & 1) * 16;
-                const uint32_t e0 = (vreg[0][j >> 1] >> sh) & 0xFFFFu;
-                const uint32_t e1 = (vreg[1][j >> 1] >> sh) & 0xFFFFu;
-                const uint32_t e2 = (vreg[2][j >> 1] >> sh) & 0xFFFFu;
-                const uint32_t e3 = (vreg[3][j >> 1] >> sh) & 0xFFFFu;
-                u32x2 w2 = {e0 | (e1 << 16), e2 | (e3 << 16)};
-                *(u32x2*)&Vt[buf][(v_o * 8 + j) * C::VS + slot] = w2;
+        for (int i = 0; i < C::VLD; ++i) {
+            const int item = tid + 256 * i;
+            if (item < C::VIT) {
+                const int v_o = item / (KT / 4);
+                const int slot = v_slot(item % (KT / 4));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int sh = (j & 1) * 16;
+                    const uint32_t e0 = (vreg[i][0][j >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t e1 = (vreg[i][1][j >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t e2 = (vreg[i][2][j >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t e3 = (vreg[i][3][j >> 1] >> sh) & 0xFFFFu;
+                    u32x2 w2 = {e0 | (e1 << 16), e2 | (e3 << 16)};
+                    *(u32x2*)&Vt[buf][(v_o * 8 + j) * C::VS + slot] = w2;
+                }
             }
         }
     };
 
-    // ---- state ---------------------------------------------------------------
-    f32x16 o[2][C::NDB];
+    // ---- state -------------------------------------------------------------------
+    f32x16 o[QB][C::NDB];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 o[qb][db][r] = 0.f;
-    float mref[2] = {-INFINITY, -INFINITY};
-    float mtrue[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.f, 0.f};
+    float mref[QB], mtrue[QB], lsum[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        mref[qb] = -INFINITY;
+        mtrue[qb] = -INFINITY;
+        lsum[qb] = 0.f;
+    }
     const float c = p.c;
 
     if (n_kt > 0) {
@@ -180,39 +197,37 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
     }
     __syncthreads();
 
-    // One 64-entry tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  The
-    // masked variant only runs on the last tiles, where some rows of the
-    // workgroup stop seeing entries.
+    // One tile of KT entries: S^T = K Q^T, online softmax, O^T += V^T P^T.
     auto key_tile = [&](const int kt, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = kt & 1;
         if (kt + 1 < n_kt)
             load_tile(kt + 1);
 
-        f32x16 s[2][2];
+        f32x16 s[QB][C::NKB];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     s[qb][kb][r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < C::NKB; ++kb) {
                 const bf16x8 ka = as_bf16x8(*(const u32x4*)&Ks[buf][(kb * 32 + l32) * C::KS + ks * 16 + hf * 8]);
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < QB; ++qb)
                     s[qb][kb] = mfma32(ka, qf[qb][ks], s[qb][kb]);
             }
         }
 
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             if constexpr (MASK) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kt * KT + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
@@ -221,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
             }
             float tmax = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     tmax = fmaxf(tmax, s[qb][kb][r]);
@@ -246,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
             const float nb = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
             float ps = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float sv = s[qb][kb][r];
@@ -261,12 +276,12 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
         }
 
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 2 * C::NKB; ++kk) {
             const int kb = kk >> 1;
             const int r0 = (kk & 1) * 8;
-            bf16x8 pf[2];
+            bf16x8 pf[QB];
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < QB; ++qb) {
                 u32x4 w4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
@@ -277,7 +292,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
             for (int db = 0; db < C::NDB; ++db) {
                 const bf16x8 va = as_bf16x8(*(const u32x4*)&Vt[buf][(db * 32 + l32) * C::VS + kk * 16 + hf * 8]);
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
+                for (int qb = 0; qb < QB; ++qb)
                     o[qb][db] = mfma32(va, pf[qb], o[qb][db]);
             }
         }
@@ -295,9 +310,9 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
     for (; kt < n_kt; ++kt)
         key_tile(kt, std::true_type{});
 
-    // ---- epilogue ----------------------------------------------------------
+    // ---- epilogue ------------------------------------------------------------------
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const float lf = half_sum(lsum[qb]);
         const bool empty = (mtrue[qb] == -INFINITY);
         const float inv = empty ? 0.f : 1.f / lf;
@@ -324,28 +339,44 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_fwd(AttnParams p)
     }
 }
 
-template <int D1, int D2>
-static hipError_t launch_t(const AttnParams& p, int n_tiles, hipStream_t stream)
-{
-    hipLaunchKernelGGL((k_cmp_attn_fwd<D1, D2>), dim3(n_tiles), dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
+// Launch shape per head-dim pair: query-row blocks per wave (QB) and key-tile
+// length (KT).  QB = 1 keeps each wave within 256 registers (two waves per
+// SIMD); KT = 32 keeps the D1 = 192 double-buffered tiles within 80 KB of LDS
+// so that two workgroups share a CU.
+#define NSA_ATTN_CONFIGS(X)      \
+    X(64, 64, 1, 64)             \
+    X(128, 64, 1, 64)            \
+    X(128, 128, 1, 64)           \
+    X(192, 64, 1, 32)            \
+    X(192, 128, 1, 32)
 
 bool cmp_attn_supported(int d1, int d2)
 {
-    return (d1 == 64 && d2 == 64) || (d1 == 128 && (d2 == 64 || d2 == 128)) ||
-           (d1 == 192 && (d2 == 64 || d2 == 128));
+#define X(a, b, q, k) if (d1 == a && d2 == b) return true;
+    NSA_ATTN_CONFIGS(X)
+#undef X
+    return false;
+}
+
+int cmp_attn_rows_per_wg(int d1, int d2)
+{
+#define X(a, b, q, k) if (d1 == a && d2 == b) return AttnCfg<a, b, q, k>::ROWS;
+    NSA_ATTN_CONFIGS(X)
+#undef X
+    return 0;
 }
 
 hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream)
 {
     if (n_tiles <= 0)
         return hipSuccess;
-    if (d1 == 64 && d2 == 64) return launch_t<64, 64>(p, n_tiles, stream);
-    if (d1 == 128 && d2 == 64) return launch_t<128, 64>(p, n_tiles, stream);
-    if (d1 == 128 && d2 == 128) return launch_t<128, 128>(p, n_tiles, stream);
-    if (d1 == 192 && d2 == 64) return launch_t<192, 64>(p, n_tiles, stream);
-    if (d1 == 192 && d2 == 128) return launch_t<192, 128>(p, n_tiles, stream);
+#define X(a, b, q, k)                                                                          \
+    if (d1 == a && d2 == b) {                                                                  \
+        hipLaunchKernelGGL((k_cmp_attn_fwd<a, b, q, k>), dim3(n_tiles), dim3(256), 0, stream, p); \
+        return hipGetLastError();                                                              \
+    }
+    NSA_ATTN_CONFIGS(X)
+#undef X
     return hipErrorInvalidValue;
 }
 

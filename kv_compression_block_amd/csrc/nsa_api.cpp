@@ -297,6 +297,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->table.resize((size_t)batch);
     int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, S_total = 0;
     const int64_t rows_c = (int64_t)waves * 64;
+    const int64_t rows_a = nsa::cmp_attn_rows_per_wg((int)d1, (int)d2);
     for (int64_t b = 0; b < batch; ++b) {
         const int64_t T = qlen[(size_t)b];
         nsa::BatchEnt& e = plan->table[(size_t)b];
@@ -305,7 +306,7 @@ nsa_status nsa_compress_attention_get_workspace(
         e.T = (int32_t)T;
         e.cmp_off = (int32_t)c_off;
         e.n_cmp = (int32_t)clen[(size_t)b];
-        e.n_rb_a = (int32_t)((T * G + nsa::kAttnRowsPerWG - 1) / nsa::kAttnRowsPerWG);
+        e.n_rb_a = (int32_t)((T * G + rows_a - 1) / rows_a);
         e.tile_off_a = (int32_t)ta;
         e.n_rb_c = (int32_t)((T * (1 << log2gp) + rows_c - 1) / rows_c);
         e.tile_off_c = (int32_t)tc;

@@ -59,12 +59,11 @@ struct AttnParams {
     uint32_t qsign;       // 0x80008000 when scale < 0 (q negated), else 0
 };
 
-// Rows per workgroup of the attention kernel (4 waves x 64 query rows).
-constexpr int kAttnRowsPerWG = 256;
-constexpr int kKeyTile = 64;
+constexpr int kKeyTile = 64;   // compressed entries per tile of the top-k kernel
 
 hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream);
 bool cmp_attn_supported(int d1, int d2);
+int cmp_attn_rows_per_wg(int d1, int d2);   // query rows per attention workgroup
 
 struct TopkParams {
     const uint16_t* q;    // [T1, N1, D1]

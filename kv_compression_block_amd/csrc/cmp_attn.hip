@@ -93,14 +93,14 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
         const int hh = r - tok * G;
         grow[qb] = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
         nvq[qb] = vq[qb] ? n_visible(tok, p.l, p.d, be.n_cmp) : 0;
-        const uint16_t* qrow = p.q + grow[qb] * D1 + hf * 8;
+        // Rows past the sequence read the workgroup's first row (always valid);
+        // they see no block and are never written.
+        const int64_t qsrc = vq[qb] ? grow[qb] : (int64_t)(be.q_off + row_wg / G) * p.N1 + (int64_t)g * G;
+        const uint16_t* qrow = p.q + qsrc * D1 + hf * 8;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (vq[qb]) {
-                v = *(const u32x4*)(qrow + ks * 16);
-                v ^= p.qsign;
-            }
+            u32x4 v = *(const u32x4*)(qrow + ks * 16);
+            v ^= p.qsign;
             qf[qb][ks] = as_bf16x8(v);
         }
     }
@@ -117,33 +117,39 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
     u32x4 kreg[C::KLD];
     u32x4 vreg[C::VLD][4];
 
+    // Per-thread byte offsets inside a tile are fixed; each tile gets a buffer
+    // resource that starts at its first entry and ends after the sequence's
+    // last one, so entries past the end load as zero (they are masked).
+    const uint32_t kst_b = (uint32_t)(kv_stride1 * 2);
+    const uint32_t vst_b = (uint32_t)(kv_stride2 * 2);
+    uint32_t koff[C::KLD], voff[C::VLD][4];
+#pragma unroll
+    for (int i = 0; i < C::KLD; ++i) {
+        const int cidx = tid + 256 * i;
+        koff[i] = (uint32_t)(cidx / C::KCH) * kst_b + (uint32_t)(cidx % C::KCH) * 16u;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VLD; ++i) {
+        const int item = min(tid + 256 * i, C::VIT - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            voff[i][e] = (uint32_t)(4 * (item % (KT / 4)) + e) * vst_b + (uint32_t)(item / (KT / 4)) * 16u;
+    }
     auto load_tile = [&](int kt) {
         const int key0 = kt * KT;
+        const int nvalid = min(KT, be.n_cmp - key0);
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * kv_stride1,
+                                                    (uint32_t)(nvalid - 1) * kst_b + D1 * 2);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)key0 * kv_stride2,
+                                                    (uint32_t)(nvalid - 1) * vst_b + D2 * 2);
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int cidx = tid + 256 * i;
-            const int row = cidx / C::KCH;
-            const int col = cidx % C::KCH;
-            const int key = key0 + row;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < be.n_cmp)
-                v = *(const u32x4*)(kbase + (int64_t)key * kv_stride1 + col * 8);
-            kreg[i] = v;
-        }
+        for (int i = 0; i < C::KLD; ++i)
+            kreg[i] = buffer_load16(kr, koff[i]);
 #pragma unroll
-        for (int i = 0; i < C::VLD; ++i) {
-            const int item = tid + 256 * i;
-            const int v_o = item / (KT / 4);   // dim octet
-            const int v_kq = item % (KT / 4);  // entry quad
+        for (int i = 0; i < C::VLD; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = key0 + 4 * v_kq + e;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (item < C::VIT && key < be.n_cmp)
-                    v = *(const u32x4*)(vbase + (int64_t)key * kv_stride2 + v_o * 8);
-                vreg[i][e] = v;
-            }
-        }
+            for (int e = 0; e < 4; ++e)
+                vreg[i][e] = buffer_load16(vr, voff[i][e]);
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -161,12 +167,10 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                 const int slot = v_slot(item % (KT / 4));
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int sh = (j & 1) * 16;
-                    const uint32_t e0 = (vreg[i][0][j >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t e1 = (vreg[i][1][j >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t e2 = (vreg[i][2][j >> 1] >> sh) & 0xFFFFu;
-                    const uint32_t e3 = (vreg[i][3][j >> 1] >> sh) & 0xFFFFu;
-                    u32x2 w2 = {e0 | (e1 << 16), e2 | (e3 << 16)};
+                    // dim j of entries e0..e3: low halves for even j, high for odd
+                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                    u32x2 w2 = {__builtin_amdgcn_perm(vreg[i][1][j >> 1], vreg[i][0][j >> 1], sel),
+                                __builtin_amdgcn_perm(vreg[i][3][j >> 1], vreg[i][2][j >> 1], sel)};
                     *(u32x2*)&Vt[buf][(v_o * 8 + j) * C::VS + slot] = w2;
                 }
             }

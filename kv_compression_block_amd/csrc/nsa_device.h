@@ -52,6 +52,19 @@ __device__ __forceinline__ float half_sum(float x)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Buffer resource over [base, base + bytes): raw (unstrided) loads at byte
+// offsets >= bytes return zero, so a tile that runs past the end of its rows
+// needs neither a clamp nor a branch per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, 0, 0);
+}
+
 // Largest b with tile_off(b) <= tile: tile ranges are ascending in b.
 template <bool kAttn>
 __device__ __forceinline__ int find_batch(const BatchEnt* bt, int B, int tile)

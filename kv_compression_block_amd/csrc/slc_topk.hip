@@ -122,42 +122,37 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
 
     const int64_t kstride = (int64_t)p.N2 * D1;
     const uint16_t* kbase = p.kc + ((int64_t)be.cmp_off * p.N2 + g) * D1;
+    const uint32_t kst_b = (uint32_t)(kstride * 2);
     u32x4 kreg[KLD];
+    // Each tile's buffer resource starts at its first entry and ends after the
+    // sequence's last one: entries past the end load as zero (they are masked).
+    auto tile_rsrc = [&](int kt) {
+        const int key0 = kt * KT;
+        const int nvalid = min(KT, be.n_cmp - key0);
+        return make_rsrc(kbase + (int64_t)key0 * kstride, (uint32_t)(nvalid - 1) * kst_b + D1 * 2);
+    };
+    auto chunk_off = [&](int cidx) { return (uint32_t)(cidx / KCH) * kst_b + (uint32_t)(cidx % KCH) * 16u; };
     auto load_tile = [&](int kt) {
+        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kt);
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int cidx = tid + 256 * i;
-            const int row = cidx / KCH;
-            const int col = cidx % KCH;
-            const int key = kt * KT + row;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (key < be.n_cmp)
-                v = *(const u32x4*)(kbase + (int64_t)key * kstride + col * 8);
-            kreg[i] = v;
-        }
+        for (int i = 0; i < KLD; ++i)
+            kreg[i] = buffer_load16(kr, chunk_off(tid + 256 * i));
     };
     auto store_tile = [&]() {
 #pragma unroll
         for (int i = 0; i < KLD; ++i) {
             const int cidx = tid + 256 * i;
-            const int row = cidx / KCH;
-            const int col = cidx % KCH;
-            *(u32x4*)&Ks[row * KS + col * 8] = kreg[i];
+            *(u32x4*)&Ks[(cidx / KCH) * KS + (cidx % KCH) * 8] = kreg[i];
         }
     };
     // A workgroup narrower than 256 threads stages K in several passes.
     auto stage_tile = [&](int kt) {
+        const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kt);
         for (int base = 0; base < 256; base += nthreads) {
 #pragma unroll
             for (int i = 0; i < KLD; ++i) {
                 const int cidx = tid + base + 256 * i;
-                const int row = cidx / KCH;
-                const int col = cidx % KCH;
-                const int key = kt * KT + row;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (key < be.n_cmp)
-                    v = *(const u32x4*)(kbase + (int64_t)key * kstride + col * 8);
-                *(u32x4*)&Ks[row * KS + col * 8] = v;
+                *(u32x4*)&Ks[(cidx / KCH) * KS + (cidx % KCH) * 8] = buffer_load16(kr, chunk_off(cidx));
             }
         }
     };

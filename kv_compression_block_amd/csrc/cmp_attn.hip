@@ -135,30 +135,34 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
         for (int e = 0; e < 4; ++e)
             voff[i][e] = (uint32_t)(4 * (item % (KT / 4)) + e) * vst_b + (uint32_t)(item / (KT / 4)) * 16u;
     }
-    auto load_tile = [&](int kt) {
-        const int key0 = kt * KT;
-        const int nvalid = min(KT, be.n_cmp - key0);
-        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)key0 * kv_stride1,
-                                                    (uint32_t)(nvalid - 1) * kst_b + D1 * 2);
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)key0 * kv_stride2,
-                                                    (uint32_t)(nvalid - 1) * vst_b + D2 * 2);
+    // A tile index at or past n_kt gets an empty range (its loads return zero
+    // and are never read); otherwise the range ends after the last entry.
+    auto tile_bytes = [&](int kt, uint32_t stride_b, int row_bytes) -> uint32_t __attribute__((always_inline)) {
+        const int nvalid = min(KT, be.n_cmp - kt * KT);
+        return nvalid > 0 ? (uint32_t)(nvalid - 1) * stride_b + (uint32_t)row_bytes : 0u;
+    };
+    auto load_k = [&](int kt) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)kt * KT * kv_stride1, tile_bytes(kt, kst_b, D1 * 2));
 #pragma unroll
         for (int i = 0; i < C::KLD; ++i)
             kreg[i] = buffer_load16(kr, koff[i]);
+    };
+    auto load_v = [&](int kt) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)kt * KT * kv_stride2, tile_bytes(kt, vst_b, D2 * 2));
 #pragma unroll
         for (int i = 0; i < C::VLD; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 vreg[i][e] = buffer_load16(vr, voff[i][e]);
     };
-    auto store_tile = [&](int buf) {
+    auto store_k = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::KLD; ++i) {
             const int cidx = tid + 256 * i;
-            const int row = cidx / C::KCH;
-            const int col = cidx % C::KCH;
-            *(u32x4*)&Ks[buf][row * C::KS + col * 8] = kreg[i];
+            *(u32x4*)&Ks[buf][(cidx / C::KCH) * C::KS + (cidx % C::KCH) * 8] = kreg[i];
         }
+    };
+    auto store_v = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::VLD; ++i) {
             const int item = tid + 256 * i;
@@ -194,21 +198,12 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
         lsum[qb] = 0.f;
     }
     const float c = p.c;
+    f32x16 scur[QB][C::NKB], snxt[QB][C::NKB];
 
-    if (n_kt > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    // One tile of KT entries: S^T = K Q^T, online softmax, O^T += V^T P^T.
-    auto key_tile = [&](const int kt, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+    // S^T = K Q^T for tile kt (K in LDS buffer kt & 1) into snxt.
+    auto qk = [&](const int kt) __attribute__((always_inline)) {
         const int buf = kt & 1;
-        if (kt + 1 < n_kt)
-            load_tile(kt + 1);
-
-        f32x16 s[QB][C::NKB];
+        auto& s = snxt;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -226,7 +221,14 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                     s[qb][kb] = mfma32(ka, qf[qb][ks], s[qb][kb]);
             }
         }
+    };
 
+    // Online softmax of tile kt, first half: mask, tile max, running max and
+    // the rare rescale of O when the reference max moves.
+    float nbias[QB];
+    auto softmax_max = [&](const int kt, auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        auto& s = scur;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             if constexpr (MASK) {
@@ -262,14 +264,22 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                     for (int r = 0; r < 16; ++r)
                         o[qb][db][r] *= alpha;
             }
-            const float nb = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
+            nbias[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
+        }
+    };
+    // Second half: P = exp2(S*c - mref*c) in place and the running sum.
+    auto softmax_exp = [&](auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        auto& s = scur;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
             float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float sv = s[qb][kb][r];
-                    float pv = fast_exp2(fmaf(sv, c, nb));
+                    float pv = fast_exp2(fmaf(sv, c, nbias[qb]));
                     if constexpr (MASK)
                         pv = (sv == -INFINITY) ? 0.f : pv;
                     s[qb][kb][r] = pv;
@@ -278,7 +288,12 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
             }
             lsum[qb] += ps;
         }
+    };
 
+    // O^T += V^T P^T for tile kt (V in LDS buffer kt & 1), 16 keys per MFMA.
+    auto pv = [&](const int kt) __attribute__((always_inline)) {
+        const int buf = kt & 1;
+        auto& s = scur;
 #pragma unroll
         for (int kk = 0; kk < 2 * C::NKB; ++kk) {
             const int kb = kk >> 1;
@@ -300,19 +315,63 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                     o[qb][db] = mfma32(va, pf[qb], o[qb][db]);
             }
         }
-
-        if (kt + 1 < n_kt)
-            store_tile(buf ^ 1);
-        __syncthreads();
     };
 
-    // Tiles every row of the workgroup sees in full need no mask.
+    // Software pipeline, one barrier per tile.  K runs one tile ahead of V:
+    // step kt issues the QK^T MFMAs of tile kt+1 next to the softmax VALU work
+    // of tile kt, then P.V of tile kt.  Step kt reads K buffer (kt+1)&1 and V
+    // buffer kt&1 and refills K buffer kt&1 (tile kt+2) and V buffer (kt+1)&1
+    // (tile kt+1): the buffers it writes were last read in step kt-1.
+    auto step = [&](const int kt, auto mask_tag, auto last_tag) __attribute__((always_inline)) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        if constexpr (!LAST) {
+            load_k(kt + 2);
+            load_v(kt + 1);
+        }
+        softmax_max(kt, mask_tag);
+        if constexpr (!LAST)
+            qk(kt + 1);   // independent of the exponentials below: they interleave
+        softmax_exp(mask_tag);
+        pv(kt);
+        if constexpr (!LAST) {
+            store_k(kt & 1);
+            store_v((kt + 1) & 1);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int kb = 0; kb < C::NKB; ++kb)
+                    scur[qb][kb] = snxt[qb][kb];
+            __syncthreads();
+        }
+    };
+    // Tiles every row of the workgroup sees in full need no mask; the last
+    // tile has no successor to prefetch.
     const int n_full = min(nv_min / KT, n_kt);
-    int kt = 0;
-    for (; kt < n_full; ++kt)
-        key_tile(kt, std::false_type{});
-    for (; kt < n_kt; ++kt)
-        key_tile(kt, std::true_type{});
+    if (n_kt > 0) {
+        load_k(0);
+        load_v(0);
+        store_k(0);
+        store_v(0);
+        load_k(1);
+        store_k(1);
+        __syncthreads();
+        qk(0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+                scur[qb][kb] = snxt[qb][kb];
+        __syncthreads();   // step 0 refills K buffer 0, which qk(0) just read
+        int kt = 0;
+        for (; kt < min(n_full, n_kt - 1); ++kt)
+            step(kt, std::false_type{}, std::false_type{});
+        for (; kt < n_kt - 1; ++kt)
+            step(kt, std::true_type{}, std::false_type{});
+        if (kt < n_full)
+            step(kt, std::false_type{}, std::true_type{});
+        else
+            step(kt, std::true_type{}, std::true_type{});
+    }
 
     // ---- epilogue ------------------------------------------------------------------
 #pragma unroll

@@ -78,7 +78,7 @@ struct nsa_plan_s {
     int64_t B, N1, N2, D1, D2, l, d, lsel, count;
     float scale;
     int64_t T1, T2, S_total, S_max;
-    int log2gp, topk_waves, sb;
+    int log2gp, topk_waves, topk_kbufs, sb;
     size_t topk_lds;
     int64_t tiles_a, tiles_c;
     size_t ws_bytes;
@@ -266,11 +266,18 @@ nsa_status nsa_compress_attention_get_workspace(
     if (H + 1 > 16 || H >= nsa::kKeyTile)
         return fail(NSA_ERR_UNSUPPORTED, "remap stencil of %d taps is not built", H + 1);
     const int sb = (int)(((S_max + 63) / 64) * 64 > 0 ? ((S_max + 63) / 64) * 64 : 64);
-    int waves = 4;
-    size_t lds = nsa::topk_lds_bytes((int)d1, log2gp, waves, sb);
-    while (waves > 1 && lds > 80 * 1024) {
-        waves >>= 1;
-        lds = nsa::topk_lds_bytes((int)d1, log2gp, waves, sb);
+    // Largest workgroup whose LDS lets two workgroups share a CU; K double
+    // buffered when that still fits.
+    int waves = 4, kbufs = 2;
+    size_t lds = nsa::topk_lds_bytes((int)d1, log2gp, waves, sb, kbufs);
+    while (lds > 80 * 1024 && (waves > 1 || kbufs > 1)) {
+        if (kbufs == 2)
+            kbufs = 1;
+        else {
+            waves >>= 1;
+            kbufs = 2;
+        }
+        lds = nsa::topk_lds_bytes((int)d1, log2gp, waves, sb, kbufs);
     }
     if (lds > 160 * 1024)
         return fail(NSA_ERR_UNSUPPORTED, "importance scores of %lld select blocks x %d tokens do not fit in LDS",
@@ -292,6 +299,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->S_max = S_max;
     plan->log2gp = log2gp;
     plan->topk_waves = waves;
+    plan->topk_kbufs = kbufs;
     plan->sb = sb;
     plan->topk_lds = lds;
     plan->table.resize((size_t)batch);
@@ -453,6 +461,7 @@ nsa_status launch_select(nsa_plan plan, const void* query, const void* key, cons
     t.sb = plan->sb;
     t.npl = plan->sb / 64;
     t.waves = plan->topk_waves;
+    t.kbufs = plan->topk_kbufs;
     hipError_t e = nsa::launch_slc_topk((int)plan->D1, plan->log2gp, t, (int)plan->tiles_c, plan->topk_lds, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "top-k launch failed: %s", hipGetErrorString(e));

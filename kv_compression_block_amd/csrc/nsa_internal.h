@@ -83,13 +83,14 @@ struct TopkParams {
     int sb;               // LDS row length of the importance scores (multiple of 64)
     int npl;              // candidates per lane in top-k, sb / 64
     int waves;            // waves per workgroup
+    int kbufs;            // K tile buffers in LDS (2 = double buffered)
 };
 
 constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)
 constexpr int kTopkMaxNpl = 16;        // at most 1024 select blocks per sequence
 
 int topk_log2_gp(int G);               // log2 of the padded group size, -1 if G > 64
-size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb);
+size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs);
 hipError_t launch_slc_topk(int d1, int log2gp, const TopkParams& p, int n_tiles, size_t lds,
                            hipStream_t stream);
 bool slc_topk_supported(int d1);

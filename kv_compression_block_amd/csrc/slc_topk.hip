@@ -15,6 +15,11 @@
 //     computed un-transposed (rows = heads, columns = compressed entries):
 //     the sum over a token's heads is then an in-lane sum of accumulator
 //     registers plus, for GP >= 8, one exchange with the lane 32 away.
+//   * K tiles of 64 entries are double buffered in LDS and loaded with
+//     range-limited buffer loads one tile ahead; one workgroup barrier per
+//     tile.  Everything else a wave touches in LDS (its tokens' rings,
+//     importance scores and top-k staging) is private to the wave and needs
+//     only wave-level ordering.
 //   * The group-summed P of each token goes to a 128-entry LDS ring indexed
 //     by compressed-entry number; after every 64-entry tile the select blocks
 //     whose whole stencil is available are finished as a fixed-order weighted
@@ -27,11 +32,22 @@
 //     above it and the lowest-index ties are compacted, then sorted by
 //     (score desc, index asc) with a 32-lane bitonic network.
 //   * Deterministic: every sum has a fixed order; no atomics.
+#include <type_traits>
+
 #include "nsa_device.h"
 
 namespace nsa {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Orders this wave's LDS accesses: a wave's LDS operations execute in order,
+// so it is enough to keep the compiler from moving them across this point.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int D1, int LOG2GP>
 __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
@@ -48,10 +64,11 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int waves = p.waves;
-    uint16_t* Ks = (uint16_t*)smem;
-    float* ring = (float*)(smem + KT * KS * 2);
-    float* bins = ring + waves * TOKW * RING;
-    uint32_t* stg = (uint32_t*)(bins + waves * TOKW * p.sb);
+    const int nbuf = p.kbufs;                              // K tile buffers: 2, or 1 if LDS is tight
+    uint16_t* Ks = (uint16_t*)smem;                        // [nbuf][KT * KS]
+    float* ring = (float*)(smem + nbuf * KT * KS * 2);     // [waves * TOKW][RING]
+    float* bins = ring + waves * TOKW * RING;              // [waves * TOKW][sb]
+    uint32_t* stg = (uint32_t*)(bins + waves * TOKW * p.sb);  // [waves][64]
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -60,18 +77,20 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
     const int hf = lane >> 5;
     const int nthreads = waves * 64;
 
-    // ---- tile -> (sequence, KV head, row block) -------------------------------
-    const int tile = blockIdx.x;
-    const int b = find_batch<false>(p.bt, p.B, tile);
+    // ---- workgroup -> (sequence, KV head, row block) ---------------------------
+    const int wg = blockIdx.x;
+    const int b = find_batch<false>(p.bt, p.B, wg);
     const BatchEnt be = p.bt[b];
-    const int idx = tile - be.tile_off_c;
+    const int idx = wg - be.tile_off_c;
     const int g = idx % p.N2;
     const int rb = be.n_rb_c - 1 - idx / p.N2;
     const int G = p.G;
     const int tok_wg = rb * ((waves * 64) >> LOG2GP);
     const int tok_w = tok_wg + wave * TOKW;
 
-    // Q rows as the A operand: lane l32 holds row rb_*32 + l32 of its wave.
+    // Q rows as the A operand: lane l32 holds row rr*32 + l32 of its wave.
+    // Padding heads and tokens past the sequence read the workgroup's first
+    // row; their bias below makes their P zero.
     bf16x8 qa[2][NKS];
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
@@ -79,51 +98,53 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
         const int tok = tok_w + (pr >> LOG2GP);
         const int hh = pr & (GP - 1);
         const bool valid = tok < be.T && hh < G;
-        const uint16_t* qrow = p.q + ((int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh) * D1 + hf * 8;
+        const int64_t row = valid ? (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh
+                                  : (int64_t)(be.q_off + tok_wg) * p.N1 + (int64_t)g * G;
+        const uint16_t* qrow = p.q + row * D1 + hf * 8;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (valid) {
-                v = *(const u32x4*)(qrow + ks * 16);
-                v ^= p.qsign;
-            }
+            u32x4 v = *(const u32x4*)(qrow + ks * 16);
+            v ^= p.qsign;
             qa[rr][ks] = as_bf16x8(v);
         }
     }
     // Per accumulator register: P = exp2(S*c - bias) is the normalised P_cmp.
     // Rows that are padding, past the sequence, or see no block get +inf.
-    float bias[2][16];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const int tok = tok_w + (pr >> LOG2GP);
-            const int hh = pr & (GP - 1);
-            float bv = INFINITY;
-            if (tok < be.T && hh < G) {
-                const int64_t row = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
-                const float m = p.smax[row * 8];
-                const float L = p.ssum[row * 8];
-                if (L > 0.f)
-                    bv = m * kLog2e + log2f(L);
-            }
-            bias[rr][r] = bv;
+    // Each lane loads the statistics of row `lane` of its wave (two loads),
+    // then every register fetches its row's bias from that lane.
+    float bias_lane = INFINITY;
+    {
+        const int tok = tok_w + (lane >> LOG2GP);
+        const int hh = lane & (GP - 1);
+        if (tok < be.T && hh < G) {
+            const int64_t row = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
+            const float m = p.smax[row * 8];
+            const float L = p.ssum[row * 8];
+            if (L > 0.f)
+                bias_lane = m * kLog2e + __builtin_amdgcn_logf(L);
         }
     }
+    float bias[2][16];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            bias[rr][r] = __shfl(bias_lane, rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3));
 
     const int tok_last = min(tok_wg + ((waves * 64) >> LOG2GP), be.T) - 1;
-    const int nv_max = tok_last >= tok_wg ? n_visible(tok_last, p.l, p.d, be.n_cmp) : 0;
+    const int nv_max = n_visible(tok_last, p.l, p.d, be.n_cmp);
     const int nv_min = n_visible(tok_wg, p.l, p.d, be.n_cmp);
     const int n_kt = (nv_max + KT - 1) / KT;
 
-    for (int x = tid; x < waves * TOKW * RING; x += nthreads)
-        ring[x] = 0.f;
+    float* my_ring = ring + wave * TOKW * RING;
+    float* my_bins = bins + wave * TOKW * p.sb;
+    for (int x = lane; x < TOKW * RING; x += 64)
+        my_ring[x] = 0.f;
 
+    // ---- K tile staging ------------------------------------------------------------
     const int64_t kstride = (int64_t)p.N2 * D1;
     const uint16_t* kbase = p.kc + ((int64_t)be.cmp_off * p.N2 + g) * D1;
     const uint32_t kst_b = (uint32_t)(kstride * 2);
-    u32x4 kreg[KLD];
     // Each tile's buffer resource starts at its first entry and ends after the
     // sequence's last one: entries past the end load as zero (they are masked).
     auto tile_rsrc = [&](int kt) {
@@ -132,49 +153,46 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
         return make_rsrc(kbase + (int64_t)key0 * kstride, (uint32_t)(nvalid - 1) * kst_b + D1 * 2);
     };
     auto chunk_off = [&](int cidx) { return (uint32_t)(cidx / KCH) * kst_b + (uint32_t)(cidx % KCH) * 16u; };
+    auto ks_at = [&](int buf, int cidx) -> u32x4* {
+        return (u32x4*)&Ks[buf * KT * KS + (cidx / KCH) * KS + (cidx % KCH) * 8];
+    };
+    const bool full_wg = (nthreads == 256);
+    u32x4 kreg[KLD];
     auto load_tile = [&](int kt) {
         const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kt);
 #pragma unroll
         for (int i = 0; i < KLD; ++i)
             kreg[i] = buffer_load16(kr, chunk_off(tid + 256 * i));
     };
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int cidx = tid + 256 * i;
-            *(u32x4*)&Ks[(cidx / KCH) * KS + (cidx % KCH) * 8] = kreg[i];
-        }
+        for (int i = 0; i < KLD; ++i)
+            *ks_at(buf, tid + 256 * i) = kreg[i];
     };
-    // A workgroup narrower than 256 threads stages K in several passes.
-    auto stage_tile = [&](int kt) {
+    // A workgroup narrower than 256 threads loads and stores in several passes.
+    auto stage_tile = [&](int kt, int buf) {
         const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kt);
-        for (int base = 0; base < 256; base += nthreads) {
-#pragma unroll
-            for (int i = 0; i < KLD; ++i) {
-                const int cidx = tid + base + 256 * i;
-                *(u32x4*)&Ks[(cidx / KCH) * KS + (cidx % KCH) * 8] = buffer_load16(kr, chunk_off(cidx));
-            }
-        }
+        for (int cidx = tid; cidx < KT * KCH; cidx += nthreads)
+            *ks_at(buf, cidx) = buffer_load16(kr, chunk_off(cidx));
     };
-    const bool full_wg = (nthreads == 256);
 
     const float c = p.c;
     const int R = p.R;
     const int H = p.H;
-    float* my_ring = ring + wave * TOKW * RING;
-    float* my_bins = bins + wave * TOKW * p.sb;
 
     if (n_kt > 0) {
         if (full_wg) {
             load_tile(0);
-            store_tile();
+            store_tile(0);
         } else {
-            stage_tile(0);
+            stage_tile(0, 0);
         }
     }
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
+    auto key_tile = [&](const int kt, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const int buf = (nbuf == 2) ? (kt & 1) : 0;
         if (full_wg && kt + 1 < n_kt)
             load_tile(kt + 1);
 
@@ -186,19 +204,19 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     s[rr][kb][r] = 0.f;
+        const uint16_t* kt_lds = Ks + buf * KT * KS;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 kf = as_bf16x8(*(const u32x4*)&Ks[(kb * 32 + l32) * KS + ks * 16 + hf * 8]);
+                const bf16x8 kf = as_bf16x8(*(const u32x4*)&kt_lds[(kb * 32 + l32) * KS + ks * 16 + hf * 8]);
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr)
                     s[rr][kb] = mfma32(qa[rr][ks], kf, s[rr][kb]);
             }
         }
 
-        // P, masked, summed over the heads of each token.
-        const bool need_mask = (kt + 1) * KT > nv_min;
+        // P, masked on the last tiles, summed over the heads of each token.
         float acc[TOKW][2];
 #pragma unroll
         for (int tw = 0; tw < TOKW; ++tw)
@@ -211,7 +229,7 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pv = fast_exp2(fmaf(s[rr][kb][r], c, -bias[rr][r]));
-                    if (need_mask) {
+                    if constexpr (MASK) {
                         const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
                         const int tok = tok_w + (pr >> LOG2GP);
                         // visible iff key*d + l - 1 <= tok
@@ -238,24 +256,15 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
                 }
             }
         }
-        __syncthreads();   // ring written; every wave is done reading Ks
+        wave_lds_sync();
 
-        if (kt + 1 < n_kt) {
-            if (full_wg)
-                store_tile();
-            else
-                stage_tile(kt + 1);
-        }
-
-        // Select blocks j whose stencil top R*j lies in this tile.
+        // Select blocks j whose stencil top R*j lies in this tile (<= 64 of them).
         const int key0 = kt * KT;
         const int jlo = (key0 + R - 1) / R;
-        const int jhi = min((key0 + KT + R - 1) / R, be.S_sel);
-        const int nj = jhi - jlo;
-        if (nj > 0) {
-            for (int x = lane; x < TOKW * nj; x += 64) {
-                const int tw = x / nj;
-                const int j = jlo + (x - tw * nj);
+        const int nj = min((key0 + KT + R - 1) / R, be.S_sel) - jlo;
+        if (lane < nj) {
+            const int j = jlo + lane;
+            for (int tw = 0; tw < TOKW; ++tw) {
                 const float* rg = my_ring + tw * RING;
                 float v = 0.f;
                 for (int r = 0; r <= H; ++r)
@@ -263,18 +272,33 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
                 my_bins[tw * p.sb + j] = v;
             }
         }
-        __syncthreads();   // bins read the ring before the next tile overwrites it
-    }
+        wave_lds_sync();
+
+        if (kt + 1 < n_kt) {
+            if (nbuf == 1)
+                __syncthreads();   // single buffer: every wave is done reading it
+            if (full_wg)
+                store_tile(nbuf == 2 ? (buf ^ 1) : 0);
+            else
+                stage_tile(kt + 1, nbuf == 2 ? (buf ^ 1) : 0);
+        }
+        __syncthreads();
+    };
+
+    // Tiles every row of the workgroup sees in full need no mask.
+    const int n_full = min(nv_min / KT, n_kt);
+    int kt = 0;
+    for (; kt < n_full; ++kt)
+        key_tile(kt, std::false_type{});
+    for (; kt < n_kt; ++kt)
+        key_tile(kt, std::true_type{});
 
     // Select blocks past the last tile: only entries < keys_done can be non-zero.
     {
         const int keys_done = n_kt * KT;
         const int jlo = (keys_done + R - 1) / R;
-        const int nj = be.S_sel - jlo;
-        if (nj > 0) {
-            for (int x = lane; x < TOKW * nj; x += 64) {
-                const int tw = x / nj;
-                const int j = jlo + (x - tw * nj);
+        for (int j = jlo + lane; j < be.S_sel; j += 64) {
+            for (int tw = 0; tw < TOKW; ++tw) {
                 const float* rg = my_ring + tw * RING;
                 float v = 0.f;
                 for (int r = 0; r <= H; ++r) {
@@ -286,103 +310,100 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
             }
         }
     }
-    __syncthreads();
+    wave_lds_sync();
 
-    // ---- top-k per (token, KV head) ---------------------------------------------
+    // ---- top-k per (token, KV head), wave-local ----------------------------------
     uint32_t* my_stg = stg + wave * 64;      // [0,32): score bits, [32,64): index
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int tw = 0; tw < TOKW; ++tw) {
         const int tok = tok_w + tw;
-        const bool active = tok < be.T;
+        if (tok >= be.T)
+            break;                           // wave-uniform
         const float* brow = my_bins + tw * p.sb;
         const int64_t tg = (int64_t)be.q_off + tok;
-        int kk = 0;
-        if (active) {
-            if (p.pslc) {
-                float* dst = p.pslc + (tg * p.N2 + g) * p.s_stride;
-                for (int j = lane; j < p.s_stride; j += 64)
-                    dst[j] = (j < be.S_sel) ? brow[j] : 0.f;
-            }
-            const int nvalid = min(tok / p.lsel + 1, be.S_sel);
-            kk = min(p.count, nvalid);
-            uint32_t key[kTopkMaxNpl];
-            bool valid[kTopkMaxNpl];
+        if (p.pslc) {
+            float* dst = p.pslc + (tg * p.N2 + g) * p.s_stride;
+            for (int j = lane; j < p.s_stride; j += 64)
+                dst[j] = (j < be.S_sel) ? brow[j] : 0.f;
+        }
+        const int nvalid = min(tok / p.lsel + 1, be.S_sel);
+        const int kk = min(p.count, nvalid);
+        // Candidates as float bits; non-candidates hold 0 and never reach a
+        // threshold >= 1 below.
+        uint32_t key[kTopkMaxNpl];
 #pragma unroll
-            for (int i = 0; i < kTopkMaxNpl; ++i) {
-                const int j = lane + 64 * i;
-                valid[i] = (i < p.npl) && (j < nvalid);
-                key[i] = valid[i] ? __float_as_uint(brow[j]) : 0u;
-            }
-            // Radix select of the kk-th largest bit pattern.
-            uint32_t tau = 0;
-            if (nvalid > kk) {
-                for (int bit = 30; bit >= 0; --bit) {
-                    const uint32_t cand = tau | (1u << bit);
-                    int cnt = 0;
+        for (int i = 0; i < kTopkMaxNpl; ++i) {
+            const int j = lane + 64 * i;
+            key[i] = (i < p.npl && j < nvalid) ? __float_as_uint(brow[j]) : 0u;
+        }
+        // Radix select of the kk-th largest bit pattern.
+        uint32_t tau = 0;
+        if (nvalid > kk) {
+            for (int bit = 30; bit >= 0; --bit) {
+                const uint32_t cand = tau | (1u << bit);
+                int cnt = 0;
 #pragma unroll
-                    for (int i = 0; i < kTopkMaxNpl; ++i)
-                        if (i < p.npl)
-                            cnt += __popcll(__ballot(valid[i] && key[i] >= cand));
-                    if (cnt >= kk)
-                        tau = cand;
+                for (int i = 0; i < kTopkMaxNpl; ++i)
+                    if (i < p.npl)
+                        cnt += __popcll(__ballot(key[i] >= cand));
+                if (cnt >= kk)
+                    tau = cand;
+            }
+        }
+        // Everything above tau, then the lowest-index candidates equal to tau.
+        int n_gt = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkMaxNpl; ++i)
+            if (i < p.npl)
+                n_gt += __popcll(__ballot(key[i] > tau));
+        const int need_eq = kk - n_gt;
+        int pos_gt = 0, pos_eq = 0;
+#pragma unroll
+        for (int i = 0; i < kTopkMaxNpl; ++i) {
+            if (i < p.npl) {
+                const bool cand_i = lane + 64 * i < nvalid;
+                const bool gt = cand_i && key[i] > tau;
+                const bool eq = cand_i && key[i] == tau;
+                const uint64_t bg = __ballot(gt);
+                const uint64_t beq = __ballot(eq);
+                const int rg = __popcll(bg & lt_mask);
+                const int re = __popcll(beq & lt_mask);
+                if (gt) {
+                    my_stg[pos_gt + rg] = key[i];
+                    my_stg[32 + pos_gt + rg] = (uint32_t)(lane + 64 * i);
                 }
+                if (eq && pos_eq + re < need_eq) {
+                    my_stg[n_gt + pos_eq + re] = key[i];
+                    my_stg[32 + n_gt + pos_eq + re] = (uint32_t)(lane + 64 * i);
+                }
+                pos_gt += __popcll(bg);
+                pos_eq += __popcll(beq);
             }
-            int n_gt = 0;
-#pragma unroll
-            for (int i = 0; i < kTopkMaxNpl; ++i)
-                if (i < p.npl)
-                    n_gt += __popcll(__ballot(valid[i] && key[i] > tau));
-            const int need_eq = kk - n_gt;
-            int pos_gt = 0, pos_eq = 0;
-#pragma unroll
-            for (int i = 0; i < kTopkMaxNpl; ++i) {
-                if (i < p.npl) {
-                    const bool gt = valid[i] && key[i] > tau;
-                    const bool eq = valid[i] && key[i] == tau;
-                    const uint64_t bg = __ballot(gt);
-                    const uint64_t beq = __ballot(eq);
-                    const int rg = __popcll(bg & lt_mask);
-                    const int re = __popcll(beq & lt_mask);
-                    if (gt) {
-                        my_stg[pos_gt + rg] = key[i];
-                        my_stg[32 + pos_gt + rg] = (uint32_t)(lane + 64 * i);
-                    }
-                    if (eq && pos_eq + re < need_eq) {
-                        my_stg[n_gt + pos_eq + re] = key[i];
-                        my_stg[32 + n_gt + pos_eq + re] = (uint32_t)(lane + 64 * i);
-                    }
-                    pos_gt += __popcll(bg);
-                    pos_eq += __popcll(beq);
+        }
+        wave_lds_sync();
+        // Bitonic sort of kk <= 32 (score, index) pairs on lanes 0..31:
+        // score descending, index ascending; pads sort last.
+        const int sl = lane & 31;
+        int sk = (sl < kk) ? (int)my_stg[sl] : -1;
+        int si = (sl < kk) ? (int)my_stg[32 + sl] : 0x7FFFFFFF;
+        wave_lds_sync();
+        for (int k2 = 2; k2 <= 32; k2 <<= 1) {
+            for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
+                const int pk = __shfl_xor(sk, jj);
+                const int pi = __shfl_xor(si, jj);
+                const bool p_first = (pk > sk) || (pk == sk && pi < si);
+                const bool m_first = (sk > pk) || (sk == pk && si < pi);
+                const bool lower = (sl & jj) == 0;
+                const bool asc = (sl & k2) == 0;
+                const bool take = (lower == asc) ? p_first : m_first;
+                if (take) {
+                    sk = pk;
+                    si = pi;
                 }
             }
         }
-        __syncthreads();
-        if (active) {
-            // Bitonic sort of kk <= 32 (score, index) pairs on lanes 0..31:
-            // score descending, index ascending; pads sort last.
-            const int sl = lane & 31;
-            int sk = (sl < kk) ? (int)my_stg[sl] : -1;
-            int si = (sl < kk) ? (int)my_stg[32 + sl] : 0x7FFFFFFF;
-            for (int k2 = 2; k2 <= 32; k2 <<= 1) {
-                for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-                    const int pk = __shfl_xor(sk, jj);
-                    const int pi = __shfl_xor(si, jj);
-                    const bool p_first = (pk > sk) || (pk == sk && pi < si);
-                    const bool m_first = (sk > pk) || (sk == pk && si < pi);
-                    const bool lower = (sl & jj) == 0;
-                    const bool asc = (sl & k2) == 0;
-                    const bool want_first = (lower == asc);
-                    const bool take = want_first ? p_first : m_first;
-                    if (take) {
-                        sk = pk;
-                        si = pi;
-                    }
-                }
-            }
-            if (lane < p.count)
-                p.topk[(tg * p.N2 + g) * p.count + lane] = (lane < kk) ? si : -1;
-        }
-        __syncthreads();
+        if (lane < p.count)
+            p.topk[(tg * p.N2 + g) * p.count + lane] = (lane < kk) ? si : -1;
     }
 }
 
@@ -422,10 +443,10 @@ int topk_log2_gp(int G)
     return lg <= 6 ? lg : -1;
 }
 
-size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb)
+size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs)
 {
     const size_t tokw = (size_t)(64 >> log2gp);
-    return (size_t)kKeyTile * (d1 + 8) * 2 + (size_t)waves * tokw * kTopkRing * 4 +
+    return (size_t)kbufs * kKeyTile * (d1 + 8) * 2 + (size_t)waves * tokw * kTopkRing * 4 +
            (size_t)waves * tokw * sb * 4 + (size_t)waves * 64 * 4;
 }
 

@@ -34,6 +34,35 @@ METRIC = "query tokens/sec (compress+attn+topk); TFLOP/s as % of MI355X bf16 MFM
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
+# HBM bytes of the attention kernel per launch, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes scaled by a plain copy of known size.  They are reported
+# only while the kernel's sources hash to what they were when counted.
+ATTN_SOURCES = ["kv_compression_block_amd/csrc/cmp_attn.hip", "kv_compression_block_amd/csrc/nsa_device.h",
+                "kv_compression_block_amd/csrc/nsa_internal.h", "kv_compression_block_amd/csrc/nsa_api.cpp"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_cmp_attn_fwd_batched-varlen-B16_hbm.json")
+
+
+def attn_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Counted HBM bytes per attention launch, or None when there is no count
+    for this workload or the kernel changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("source_sha256") != attn_source_digest():
+        return None
+    return float(rec["bytes_per_launch"])
+
 
 def n_visible(t: np.ndarray, l: int, d: int, n_cmp: int) -> np.ndarray:
     n = np.where(t >= l - 1, (t - l + 1) // d + 1, 0)
@@ -102,6 +131,9 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, choices=range(5))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (calibrates the HBM byte "
+                         "counters against a kernel of known traffic) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the path runs on a single MI355X and this build has no "
@@ -121,6 +153,20 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        print(json.dumps({"copy_bytes": args.copy_bytes, "read_bytes": args.copy_bytes,
+                          "write_bytes": args.copy_bytes, "ms": ms,
+                          "GB/s": 2 * args.copy_bytes / (ms / 1e3) / 1e9}), flush=True)
+        return 0
     wl = synth.WORKLOADS[args.workload]
     print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(wl, device=dev, chunk_rows=16384)
@@ -207,7 +253,8 @@ def main() -> int:
         "frac_of_bf16_peak": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"kernel": "k_cmp_attn_fwd", "bound": "mfma", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None,
+                     "traffic": measured_traffic(wl.name),
+                     "traffic_unit": "HBM bytes per launch",
                      "work_per_launch": f"{work['attn_flops']:.4e} flop = 2*(D1+D2) x {work['visible_pairs']} "
                                         f"visible (token, block) pairs x {wl.N1} heads"},
         "kernels": kernels,

@@ -199,6 +199,7 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
     }
     const float c = p.c;
     f32x16 scur[QB][C::NKB], snxt[QB][C::NKB];
+    u32x4 pfr[QB][2 * C::NKB];   // P of the current tile, bf16 B operands of P.V
 
     // S^T = K Q^T for tile kt (K in LDS buffer kt & 1) into snxt.
     auto qk = [&](const int kt) __attribute__((always_inline)) {
@@ -223,12 +224,14 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
         }
     };
 
-    // Online softmax of tile kt, first half: mask, tile max, running max and
-    // the rare rescale of O when the reference max moves.
-    float nbias[QB];
-    auto softmax_max = [&](const int kt, auto mask_tag) __attribute__((always_inline)) {
+    // Mask and max of tile kt (in snxt); decides whether the reference max
+    // must move.  The move itself (and the O rescale) waits for rescale(),
+    // after the P.V of the previous tile has been accumulated.
+    float tmaxq[QB], nbias[QB];
+    bool growq[QB];
+    auto tile_max = [&](const int kt, auto mask_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        auto& s = scur;
+        auto& s = snxt;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             if constexpr (MASK) {
@@ -248,14 +251,25 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                     tmax = fmaxf(tmax, s[qb][kb][r]);
             tmax = half_max(tmax);
             mtrue[qb] = fmaxf(mtrue[qb], tmax);
-            const bool grow_ref = tmax > mref[qb] + p.thr;
-            if (__builtin_expect(__ballot(grow_ref) != 0, 0)) {
-                // Rare: the running reference max moves; rescale O and the sum.
-                __asm__ volatile("" ::: "memory");
+            tmaxq[qb] = tmax;
+            growq[qb] = tmax > mref[qb] + p.thr;
+        }
+    };
+    // Rare: move the reference max where a row asked for it, rescaling O and
+    // the running sum; then the exponent bias of the next tile.
+    auto rescale = [&]() __attribute__((always_inline)) {
+        bool any = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            any |= growq[qb];
+        if (__builtin_expect(__ballot(any) != 0, 0)) {
+            __asm__ volatile("" ::: "memory");
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
                 float alpha = 1.f;
-                if (grow_ref) {
-                    alpha = (mref[qb] == -INFINITY) ? 0.f : fast_exp2((mref[qb] - tmax) * c);
-                    mref[qb] = tmax;
+                if (growq[qb]) {
+                    alpha = (mref[qb] == -INFINITY) ? 0.f : fast_exp2((mref[qb] - tmaxq[qb]) * c);
+                    mref[qb] = tmaxq[qb];
                 }
                 lsum[qb] *= alpha;
 #pragma unroll
@@ -264,10 +278,13 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                     for (int r = 0; r < 16; ++r)
                         o[qb][db][r] *= alpha;
             }
-            nbias[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
         }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            nbias[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
     };
-    // Second half: P = exp2(S*c - mref*c) in place and the running sum.
+    // P = exp2(S*c - mref*c) of the current tile, the running sum, and P
+    // packed to bf16 in the order the P.V MFMAs consume it.
     auto softmax_exp = [&](auto mask_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         auto& s = scur;
@@ -287,53 +304,52 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                 }
             }
             lsum[qb] += ps;
+#pragma unroll
+            for (int kk = 0; kk < 2 * C::NKB; ++kk) {
+                const int kb = kk >> 1;
+                const int r0 = (kk & 1) * 8;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pfr[qb][kk][j] = pack_bf16x2(s[qb][kb][r0 + 2 * j], s[qb][kb][r0 + 2 * j + 1]);
+            }
         }
     };
 
     // O^T += V^T P^T for tile kt (V in LDS buffer kt & 1), 16 keys per MFMA.
     auto pv = [&](const int kt) __attribute__((always_inline)) {
         const int buf = kt & 1;
-        auto& s = scur;
 #pragma unroll
         for (int kk = 0; kk < 2 * C::NKB; ++kk) {
-            const int kb = kk >> 1;
-            const int r0 = (kk & 1) * 8;
-            bf16x8 pf[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                u32x4 w4;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    w4[j] = pack_bf16x2(s[qb][kb][r0 + 2 * j], s[qb][kb][r0 + 2 * j + 1]);
-                pf[qb] = as_bf16x8(w4);
-            }
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
                 const bf16x8 va = as_bf16x8(*(const u32x4*)&Vt[buf][(db * 32 + l32) * C::VS + kk * 16 + hf * 8]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    o[qb][db] = mfma32(va, pf[qb], o[qb][db]);
+                    o[qb][db] = mfma32(va, as_bf16x8(pfr[qb][kk]), o[qb][db]);
             }
         }
     };
 
-    // Software pipeline, one barrier per tile.  K runs one tile ahead of V:
-    // step kt issues the QK^T MFMAs of tile kt+1 next to the softmax VALU work
-    // of tile kt, then P.V of tile kt.  Step kt reads K buffer (kt+1)&1 and V
-    // buffer kt&1 and refills K buffer kt&1 (tile kt+2) and V buffer (kt+1)&1
-    // (tile kt+1): the buffers it writes were last read in step kt-1.
-    auto step = [&](const int kt, auto mask_tag, auto last_tag) __attribute__((always_inline)) {
+    // Software pipeline, one barrier per tile.  On entry to step kt, scur
+    // holds S(kt) with its mask applied and nbias is final for it.  The
+    // step issues the QK^T MFMAs of tile kt+1 next to the exponentials of
+    // tile kt, then the P.V MFMAs of tile kt next to the max of tile kt+1,
+    // so both MFMA phases have independent vector work beside them.  K runs
+    // one tile ahead of V: step kt reads K buffer (kt+1)&1 and V buffer kt&1
+    // and refills K buffer kt&1 (tile kt+2) and V buffer (kt+1)&1 (tile
+    // kt+1), both last read in step kt-1.
+    auto step = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
         if constexpr (!LAST) {
             load_k(kt + 2);
             load_v(kt + 1);
+            qk(kt + 1);
         }
-        softmax_max(kt, mask_tag);
-        if constexpr (!LAST)
-            qk(kt + 1);   // independent of the exponentials below: they interleave
-        softmax_exp(mask_tag);
+        softmax_exp(mask_cur);
         pv(kt);
         if constexpr (!LAST) {
+            tile_max(kt + 1, mask_next);
+            rescale();
             store_k(kt & 1);
             store_v((kt + 1) & 1);
 #pragma unroll
@@ -346,6 +362,8 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
     };
     // Tiles every row of the workgroup sees in full need no mask; the last
     // tile has no successor to prefetch.
+    using F = std::false_type;
+    using T = std::true_type;
     const int n_full = min(nv_min / KT, n_kt);
     if (n_kt > 0) {
         load_k(0);
@@ -356,6 +374,11 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
         store_k(1);
         __syncthreads();
         qk(0);
+        if (n_full > 0)
+            tile_max(0, F{});
+        else
+            tile_max(0, T{});
+        rescale();
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -363,14 +386,20 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
                 scur[qb][kb] = snxt[qb][kb];
         __syncthreads();   // step 0 refills K buffer 0, which qk(0) just read
         int kt = 0;
-        for (; kt < min(n_full, n_kt - 1); ++kt)
-            step(kt, std::false_type{}, std::false_type{});
-        for (; kt < n_kt - 1; ++kt)
-            step(kt, std::true_type{}, std::false_type{});
+        // tiles kt and kt+1 both unmasked
+        for (; kt + 1 < min(n_full, n_kt); ++kt)
+            step(kt, F{}, F{}, F{});
+        // tile kt unmasked, kt+1 masked
+        if (kt < n_full && kt + 1 < n_kt) {
+            step(kt, F{}, T{}, F{});
+            ++kt;
+        }
+        for (; kt + 1 < n_kt; ++kt)
+            step(kt, T{}, T{}, F{});
         if (kt < n_full)
-            step(kt, std::false_type{}, std::true_type{});
+            step(kt, F{}, F{}, T{});
         else
-            step(kt, std::true_type{}, std::true_type{});
+            step(kt, T{}, T{}, T{});
     }
 
     // ---- epilogue ------------------------------------------------------------------

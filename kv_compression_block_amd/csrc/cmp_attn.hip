@@ -42,25 +42,26 @@ __device__ __forceinline__ int v_slot(int kq)
     return (kq >> 2) * 16 + perm * 4;
 }
 
-template <int D1, int D2, int QB, int KT>
+template <int D1, int D2, int QB, int KT, int W>
 struct AttnCfg {
-    static constexpr int ROWS = 4 * 32 * QB;   // query rows per workgroup
+    static constexpr int NT = 64 * W;          // threads per workgroup (W waves)
+    static constexpr int ROWS = W * 32 * QB;   // query rows per workgroup
     static constexpr int KS = D1 + 8;          // LDS row stride of K (bf16): 16 B pad
     static constexpr int VS = KT + 8;          // LDS row stride of V^T (bf16): 16 B pad
     static constexpr int NKB = KT / 32;        // 32-entry blocks per tile
     static constexpr int NKS = D1 / 16;        // k-steps of QK^T
     static constexpr int NDB = D2 / 32;        // 32-row blocks of O^T
     static constexpr int KCH = D1 / 8;         // 16-byte chunks per K row
-    static constexpr int KLD = KT * KCH / 256; // K chunks staged per thread
+    static constexpr int KLD = KT * KCH / NT;  // K chunks staged per thread
     static constexpr int VIT = (KT / 4) * (D2 / 8);  // (entry quad, dim octet) items
-    static constexpr int VLD = (VIT + 255) / 256;    // V items per thread
-    static_assert(KT % 32 == 0 && KT * KCH % 256 == 0, "K tile staging");
+    static constexpr int VLD = (VIT + NT - 1) / NT;  // V items per thread
+    static_assert(KT % 32 == 0 && KT * KCH % NT == 0, "K tile staging");
 };
 
-template <int D1, int D2, int QB, int KT>
-__global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnParams p)
+template <int D1, int D2, int QB, int KT, int W>
+__global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_fwd(AttnParams p)
 {
-    using C = AttnCfg<D1, D2, QB, KT>;
+    using C = AttnCfg<D1, D2, QB, KT, W>;
     __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * C::KS];
     __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D2 * C::VS];
 
@@ -125,12 +126,12 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
     uint32_t koff[C::KLD], voff[C::VLD][4];
 #pragma unroll
     for (int i = 0; i < C::KLD; ++i) {
-        const int cidx = tid + 256 * i;
+        const int cidx = tid + C::NT * i;
         koff[i] = (uint32_t)(cidx / C::KCH) * kst_b + (uint32_t)(cidx % C::KCH) * 16u;
     }
 #pragma unroll
     for (int i = 0; i < C::VLD; ++i) {
-        const int item = min(tid + 256 * i, C::VIT - 1);
+        const int item = min(tid + C::NT * i, C::VIT - 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             voff[i][e] = (uint32_t)(4 * (item % (KT / 4)) + e) * vst_b + (uint32_t)(item / (KT / 4)) * 16u;
@@ -151,21 +152,22 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)kt * KT * kv_stride2, tile_bytes(kt, vst_b, D2 * 2));
 #pragma unroll
         for (int i = 0; i < C::VLD; ++i)
+            if (C::VIT % C::NT == 0 || tid + C::NT * i < C::VIT)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                vreg[i][e] = buffer_load16(vr, voff[i][e]);
+                for (int e = 0; e < 4; ++e)
+                    vreg[i][e] = buffer_load16(vr, voff[i][e]);
     };
     auto store_k = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::KLD; ++i) {
-            const int cidx = tid + 256 * i;
+            const int cidx = tid + C::NT * i;
             *(u32x4*)&Ks[buf][(cidx / C::KCH) * C::KS + (cidx % C::KCH) * 8] = kreg[i];
         }
     };
     auto store_v = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < C::VLD; ++i) {
-            const int item = tid + 256 * i;
+            const int item = tid + C::NT * i;
             if (item < C::VIT) {
                 const int v_o = item / (KT / 4);
                 const int slot = v_slot(item % (KT / 4));
@@ -436,15 +438,15 @@ __global__ __launch_bounds__(256, (QB == 1 ? 2 : 1)) void k_cmp_attn_fwd(AttnPar
 // SIMD); KT = 32 keeps the D1 = 192 double-buffered tiles within 80 KB of LDS
 // so that two workgroups share a CU.
 #define NSA_ATTN_CONFIGS(X)      \
-    X(64, 64, 1, 64)             \
-    X(128, 64, 1, 64)            \
-    X(128, 128, 1, 64)           \
-    X(192, 64, 1, 32)            \
-    X(192, 128, 1, 32)
+    X(64, 64, 1, 64, 4)          \
+    X(128, 64, 1, 64, 4)         \
+    X(128, 128, 1, 64, 4)        \
+    X(192, 64, 1, 32, 4)         \
+    X(192, 128, 1, 32, 4)
 
 bool cmp_attn_supported(int d1, int d2)
 {
-#define X(a, b, q, k) if (d1 == a && d2 == b) return true;
+#define X(a, b, q, k, w) if (d1 == a && d2 == b) return true;
     NSA_ATTN_CONFIGS(X)
 #undef X
     return false;
@@ -452,7 +454,7 @@ bool cmp_attn_supported(int d1, int d2)
 
 int cmp_attn_rows_per_wg(int d1, int d2)
 {
-#define X(a, b, q, k) if (d1 == a && d2 == b) return AttnCfg<a, b, q, k>::ROWS;
+#define X(a, b, q, k, w) if (d1 == a && d2 == b) return AttnCfg<a, b, q, k, w>::ROWS;
     NSA_ATTN_CONFIGS(X)
 #undef X
     return 0;
@@ -462,9 +464,9 @@ hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hip
 {
     if (n_tiles <= 0)
         return hipSuccess;
-#define X(a, b, q, k)                                                                          \
+#define X(a, b, q, k, w)                                                                          \
     if (d1 == a && d2 == b) {                                                                  \
-        hipLaunchKernelGGL((k_cmp_attn_fwd<a, b, q, k>), dim3(n_tiles), dim3(256), 0, stream, p); \
+        hipLaunchKernelGGL((k_cmp_attn_fwd<a, b, q, k, w>), dim3(n_tiles), dim3(64 * w), 0, stream, p); \
         return hipGetLastError();                                                              \
     }
     NSA_ATTN_CONFIGS(X)

@@ -206,9 +206,9 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
                     s[rr][kb][r] = 0.f;
         const uint16_t* kt_lds = Ks + buf * KT * KS;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8 kf = as_bf16x8(*(const u32x4*)&kt_lds[(kb * 32 + l32) * KS + ks * 16 + hf * 8]);
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr)
@@ -222,9 +222,9 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
         for (int tw = 0; tw < TOKW; ++tw)
             acc[tw][0] = acc[tw][1] = 0.f;
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int rr = 0; rr < 2; ++rr) {
                 const int key = kt * KT + kb * 32 + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -328,15 +328,19 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
         }
         const int nvalid = min(tok / p.lsel + 1, be.S_sel);
         const int kk = min(p.count, nvalid);
+        const int nch = (nvalid + 63) >> 6;   // 64-candidate chunks of this row
         // Candidates as float bits; non-candidates hold 0 and never reach a
         // threshold >= 1 below.
         uint32_t key[kTopkMaxNpl];
 #pragma unroll
         for (int i = 0; i < kTopkMaxNpl; ++i) {
             const int j = lane + 64 * i;
-            key[i] = (i < p.npl && j < nvalid) ? __float_as_uint(brow[j]) : 0u;
+            key[i] = (i < nch && j < nvalid) ? __float_as_uint(brow[j]) : 0u;
         }
-        // Radix select of the kk-th largest bit pattern.
+        // Radix select, most significant bit first: tau grows while at least
+        // kk keys stay >= tau.  Once exactly kk keys are >= tau they are the
+        // kk largest and the search stops; otherwise tau ends as the kk-th
+        // largest bit pattern.
         uint32_t tau = 0;
         if (nvalid > kk) {
             for (int bit = 30; bit >= 0; --bit) {
@@ -344,23 +348,26 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
                 int cnt = 0;
 #pragma unroll
                 for (int i = 0; i < kTopkMaxNpl; ++i)
-                    if (i < p.npl)
+                    if (i < nch)
                         cnt += __popcll(__ballot(key[i] >= cand));
-                if (cnt >= kk)
+                if (cnt >= kk) {
                     tau = cand;
+                    if (cnt == kk)
+                        break;
+                }
             }
         }
         // Everything above tau, then the lowest-index candidates equal to tau.
         int n_gt = 0;
 #pragma unroll
         for (int i = 0; i < kTopkMaxNpl; ++i)
-            if (i < p.npl)
+            if (i < nch)
                 n_gt += __popcll(__ballot(key[i] > tau));
         const int need_eq = kk - n_gt;
         int pos_gt = 0, pos_eq = 0;
 #pragma unroll
         for (int i = 0; i < kTopkMaxNpl; ++i) {
-            if (i < p.npl) {
+            if (i < nch) {
                 const bool cand_i = lane + 64 * i < nvalid;
                 const bool gt = cand_i && key[i] > tau;
                 const bool eq = cand_i && key[i] == tau;
@@ -381,29 +388,25 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
             }
         }
         wave_lds_sync();
-        // Bitonic sort of kk <= 32 (score, index) pairs on lanes 0..31:
-        // score descending, index ascending; pads sort last.
-        const int sl = lane & 31;
-        int sk = (sl < kk) ? (int)my_stg[sl] : -1;
-        int si = (sl < kk) ? (int)my_stg[32 + sl] : 0x7FFFFFFF;
-        wave_lds_sync();
-        for (int k2 = 2; k2 <= 32; k2 <<= 1) {
-            for (int jj = k2 >> 1; jj > 0; jj >>= 1) {
-                const int pk = __shfl_xor(sk, jj);
-                const int pi = __shfl_xor(si, jj);
-                const bool p_first = (pk > sk) || (pk == sk && pi < si);
-                const bool m_first = (sk > pk) || (sk == pk && si < pi);
-                const bool lower = (sl & jj) == 0;
-                const bool asc = (sl & k2) == 0;
-                const bool take = (lower == asc) ? p_first : m_first;
-                if (take) {
-                    sk = pk;
-                    si = pi;
-                }
+        // Order: score descending, index ascending.  Each pick counts the picks
+        // that precede it and writes itself at that rank; unused slots get -1.
+        int32_t* trow = p.topk + (tg * p.N2 + g) * p.count;
+        if (lane < kk) {
+            const uint32_t mk = my_stg[lane];
+            const uint32_t mi = my_stg[32 + lane];
+            int rank = 0;
+            for (int q = 0; q < kk; q += 4) {
+                const u32x4 ok = *(const u32x4*)&my_stg[q];
+                const u32x4 oi = *(const u32x4*)&my_stg[32 + q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rank += (q + e < kk) && (ok[e] > mk || (ok[e] == mk && oi[e] < mi));
             }
+            trow[rank] = (int32_t)mi;
+        } else if (lane < p.count) {
+            trow[lane] = -1;
         }
-        if (lane < p.count)
-            p.topk[(tg * p.N2 + g) * p.count + lane] = (lane < kk) ? si : -1;
+        wave_lds_sync();   // the staging area is reused by the next token
     }
 }
 

@@ -11,11 +11,13 @@
 //     so two waves share each SIMD (two workgroups per CU): one wave's
 //     softmax VALU work overlaps the other's MFMAs, and one workgroup's
 //     prologue/epilogue overlaps the other's main loop.
-//   * K and V tiles of KT compressed entries are staged in LDS, double
-//     buffered; the next tile's global loads are in flight during the
-//     current tile's MFMAs.  K is stored row-major (entry, dim), V transposed
-//     (dim, entry) with the entries of each 16-group ordered to match the
-//     layout the score accumulator leaves P in.
+//   * K and V tiles of KT compressed entries are copied straight from
+//     global memory into LDS by the buffer unit (no register staging),
+//     double buffered: the copies of the next tiles are in flight during the
+//     current tile's MFMAs.  K rows carry 16 bytes of padding; V rows are
+//     stored as they are, with XOR-swizzled 16-byte chunks, and the P.V
+//     operand is read transposed (ds_read_b64_tr_b16) in the order the score
+//     accumulator leaves P in.
 //   * Scores are computed transposed, S^T = K Q^T: a lane owns one query
 //     column and 16 keys per 32x32 block, so the row max and sum are
 //     in-lane plus one exchange with the lane 32 away.  P^T is then directly
@@ -32,41 +34,64 @@
 
 namespace nsa {
 
-// Slot of entry quad kq (4 entries) inside the transposed V row: within each
-// group of 16 entries the quads are stored in the order 0, 2, 1, 3 so that a
-// lane of half h reads entries {4h..4h+3, 8+4h..8+4h+3} as one 16-byte chunk.
-__device__ __forceinline__ int v_slot(int kq)
-{
-    const int q = kq & 3;
-    const int perm = (q == 1) ? 2 : (q == 2 ? 1 : q);
-    return (kq >> 2) * 16 + perm * 4;
-}
-
 template <int D1, int D2, int QB, int KT, int W>
 struct AttnCfg {
     static constexpr int NT = 64 * W;          // threads per workgroup (W waves)
     static constexpr int ROWS = W * 32 * QB;   // query rows per workgroup
     static constexpr int KS = D1 + 8;          // LDS row stride of K (bf16): 16 B pad
-    static constexpr int VS = KT + 8;          // LDS row stride of V^T (bf16): 16 B pad
     static constexpr int NKB = KT / 32;        // 32-entry blocks per tile
     static constexpr int NKS = D1 / 16;        // k-steps of QK^T
     static constexpr int NDB = D2 / 32;        // 32-row blocks of O^T
     static constexpr int KCH = D1 / 8;         // 16-byte chunks per K row
-    static constexpr int KLD = KT * KCH / NT;  // K chunks staged per thread
-    static constexpr int VIT = (KT / 4) * (D2 / 8);  // (entry quad, dim octet) items
-    static constexpr int VLD = (VIT + NT - 1) / NT;  // V items per thread
-    static_assert(KT % 32 == 0 && KT * KCH % NT == 0, "K tile staging");
+    static constexpr int VCH = D2 / 8;         // 16-byte chunks per V row
+    // Tiles are copied global -> LDS by the buffer unit (16 bytes per lane,
+    // 64 consecutive 16-byte LDS slots per wave instruction).  A K row is
+    // KCH + 1 slots (the last one is padding, loaded from outside the
+    // buffer's range); a V row is VCH slots in a swizzled order.
+    static constexpr int KSLOT = KT * (KCH + 1);
+    static constexpr int KINS = (KSLOT + 63) / 64;   // wave instructions per K tile
+    static constexpr int KIPW = (KINS + W - 1) / W;  // ... per wave
+    static constexpr int KBUF = KINS * 64 * 8;       // bf16 per K buffer (with slack)
+    static constexpr int VINS = KT * VCH / 64;       // wave instructions per V tile
+    static constexpr int VIPW = VINS / W;
+    static_assert(KT % 32 == 0 && (KT * VCH) % (64 * W) == 0, "V tile copy");
+    static_assert(D2 == 64 || D2 == 128, "V swizzle");
 };
+
+// 16-byte chunk c of V row r sits at chunk v_swz(r, c) of that row.  The
+// P.V operand reads (ds_read_b64_tr_b16) touch 8 consecutive rows and 4
+// consecutive chunks per instruction; this XOR spreads them over all 64
+// banks twice, the minimum for 512 bytes.
+template <int D2>
+__device__ __forceinline__ int v_swz(int r, int c)
+{
+    if constexpr (D2 == 128)
+        return c ^ ((r & 3) << 2);
+    else
+        return c ^ (((r >> 1) & 1) << 2);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Copies 16 bytes per lane from a buffer into LDS: lane i's bytes land at
+// lds + 16 i (the LDS address must be the same in every lane).
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
 
 template <int D1, int D2, int QB, int KT, int W>
 __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_fwd(AttnParams p)
 {
     using C = AttnCfg<D1, D2, QB, KT, W>;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * C::KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D2 * C::VS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * D2];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int hf = lane >> 5;
@@ -115,73 +140,64 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     const int64_t kv_stride2 = (int64_t)p.N2 * D2;
     const uint16_t* kbase = p.kc + ((int64_t)be.cmp_off * p.N2 + g) * D1;
     const uint16_t* vbase = p.vc + ((int64_t)be.cmp_off * p.N2 + g) * D2;
-    u32x4 kreg[C::KLD];
-    u32x4 vreg[C::VLD][4];
-
-    // Per-thread byte offsets inside a tile are fixed; each tile gets a buffer
-    // resource that starts at its first entry and ends after the sequence's
-    // last one, so entries past the end load as zero (they are masked).
     const uint32_t kst_b = (uint32_t)(kv_stride1 * 2);
     const uint32_t vst_b = (uint32_t)(kv_stride2 * 2);
-    uint32_t koff[C::KLD], voff[C::VLD][4];
+    // Global byte offset (inside a tile) that each lane copies into LDS slot
+    // 64*q + lane of instruction q.  Padding slots point past any tile range
+    // and load zero.
+    uint32_t kdo[C::KIPW], vdo[C::VIPW];
 #pragma unroll
-    for (int i = 0; i < C::KLD; ++i) {
-        const int cidx = tid + C::NT * i;
-        koff[i] = (uint32_t)(cidx / C::KCH) * kst_b + (uint32_t)(cidx % C::KCH) * 16u;
+    for (int j = 0; j < C::KIPW; ++j) {
+        const int slot = (j * W + wave) * 64 + lane;
+        const int r = slot / (C::KCH + 1), ch = slot % (C::KCH + 1);
+        kdo[j] = (ch < C::KCH && r < KT) ? (uint32_t)r * kst_b + (uint32_t)ch * 16u : 0x7FFFFFF0u;
     }
 #pragma unroll
-    for (int i = 0; i < C::VLD; ++i) {
-        const int item = min(tid + C::NT * i, C::VIT - 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            voff[i][e] = (uint32_t)(4 * (item % (KT / 4)) + e) * vst_b + (uint32_t)(item / (KT / 4)) * 16u;
+    for (int j = 0; j < C::VIPW; ++j) {
+        const int slot = (j * W + wave) * 64 + lane;
+        const int r = slot / C::VCH;
+        const int ch = v_swz<D2>(r, slot % C::VCH);   // the XOR is its own inverse
+        vdo[j] = (uint32_t)r * vst_b + (uint32_t)ch * 16u;
     }
-    // A tile index at or past n_kt gets an empty range (its loads return zero
-    // and are never read); otherwise the range ends after the last entry.
+    // Each tile's buffer resource starts at its first entry and ends after
+    // the sequence's last one, so entries past the end load as zero (they are
+    // masked); a tile index at or past the last one gets an empty range.
     auto tile_bytes = [&](int kt, uint32_t stride_b, int row_bytes) -> uint32_t __attribute__((always_inline)) {
         const int nvalid = min(KT, be.n_cmp - kt * KT);
         return nvalid > 0 ? (uint32_t)(nvalid - 1) * stride_b + (uint32_t)row_bytes : 0u;
     };
-    auto load_k = [&](int kt) __attribute__((always_inline)) {
+    auto load_k = [&](int kt, uint16_t* dst) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)kt * KT * kv_stride1, tile_bytes(kt, kst_b, D1 * 2));
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i)
-            kreg[i] = buffer_load16(kr, koff[i]);
+        for (int j = 0; j < C::KIPW; ++j)
+            if (C::KINS % W == 0 || j * W + wave < C::KINS)
+                copy16_to_lds(kr, dst + (j * W + wave) * 512, kdo[j]);
     };
-    auto load_v = [&](int kt) __attribute__((always_inline)) {
+    auto load_v = [&](int kt, uint16_t* dst) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)kt * KT * kv_stride2, tile_bytes(kt, vst_b, D2 * 2));
 #pragma unroll
-        for (int i = 0; i < C::VLD; ++i)
-            if (C::VIT % C::NT == 0 || tid + C::NT * i < C::VIT)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    vreg[i][e] = buffer_load16(vr, voff[i][e]);
+        for (int j = 0; j < C::VIPW; ++j)
+            copy16_to_lds(vr, dst + (j * W + wave) * 512, vdo[j]);
     };
-    auto store_k = [&](int buf) __attribute__((always_inline)) {
+    // The copies of this wave have landed in LDS (the barrier that follows
+    // makes every wave's copies visible).
+    auto copies_done = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
+
+    // P.V operand addressing (ds_read_b64_tr_b16): in each 16-lane group,
+    // lane i supplies the 8 bytes of row key0 + i/4, dims dimbase + 4*(i%4)
+    // and receives V[key0 + 0..3][dimbase + i].  k-slots 0-3 of a lane in
+    // half hf are keys 16kk + 4hf + 0..3, k-slots 4-7 keys 16kk + 8 + 4hf +
+    // 0..3: the order the score accumulator leaves P in.
+    int voff_lane[C::NDB];
+    {
+        const int vi = lane & 15, vgrp = (lane >> 4) & 1;
+        const int r0 = 4 * hf + (vi >> 2);           // row inside a 16-key chunk
 #pragma unroll
-        for (int i = 0; i < C::KLD; ++i) {
-            const int cidx = tid + C::NT * i;
-            *(u32x4*)&Ks[buf][(cidx / C::KCH) * C::KS + (cidx % C::KCH) * 8] = kreg[i];
+        for (int db = 0; db < C::NDB; ++db) {
+            const int dim = db * 32 + 16 * vgrp + 4 * (vi & 3);
+            voff_lane[db] = r0 * D2 + v_swz<D2>(r0, dim >> 3) * 8 + (dim & 7);
         }
-    };
-    auto store_v = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < C::VLD; ++i) {
-            const int item = tid + C::NT * i;
-            if (item < C::VIT) {
-                const int v_o = item / (KT / 4);
-                const int slot = v_slot(item % (KT / 4));
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    // dim j of entries e0..e3: low halves for even j, high for odd
-                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                    u32x2 w2 = {__builtin_amdgcn_perm(vreg[i][1][j >> 1], vreg[i][0][j >> 1], sel),
-                                __builtin_amdgcn_perm(vreg[i][3][j >> 1], vreg[i][2][j >> 1], sel)};
-                    *(u32x2*)&Vt[buf][(v_o * 8 + j) * C::VS + slot] = w2;
-                }
-            }
-        }
-    };
+    }
 
     // ---- state -------------------------------------------------------------------
     f32x16 o[QB][C::NDB];
@@ -204,8 +220,7 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     u32x4 pfr[QB][2 * C::NKB];   // P of the current tile, bf16 B operands of P.V
 
     // S^T = K Q^T for tile kt (K in LDS buffer kt & 1) into snxt.
-    auto qk = [&](const int kt) __attribute__((always_inline)) {
-        const int buf = kt & 1;
+    auto qk = [&](const uint16_t* kbuf) __attribute__((always_inline)) {
         auto& s = snxt;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
@@ -218,7 +233,7 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
         for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
-                const bf16x8 ka = as_bf16x8(*(const u32x4*)&Ks[buf][(kb * 32 + l32) * C::KS + ks * 16 + hf * 8]);
+                const bf16x8 ka = as_bf16x8(*(const u32x4*)&kbuf[(kb * 32 + l32) * C::KS + ks * 16 + hf * 8]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     s[qb][kb] = mfma32(ka, qf[qb][ks], s[qb][kb]);
@@ -318,13 +333,15 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     };
 
     // O^T += V^T P^T for tile kt (V in LDS buffer kt & 1), 16 keys per MFMA.
-    auto pv = [&](const int kt) __attribute__((always_inline)) {
-        const int buf = kt & 1;
+    auto pv = [&](const uint16_t* vbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < 2 * C::NKB; ++kk) {
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db) {
-                const bf16x8 va = as_bf16x8(*(const u32x4*)&Vt[buf][(db * 32 + l32) * C::VS + kk * 16 + hf * 8]);
+                const uint16_t* vb = &vbuf[voff_lane[db] + kk * 16 * D2];
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * D2));
+                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     o[qb][db] = mfma32(va, as_bf16x8(pfr[qb][kk]), o[qb][db]);
@@ -340,20 +357,24 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     // one tile ahead of V: step kt reads K buffer (kt+1)&1 and V buffer kt&1
     // and refills K buffer kt&1 (tile kt+2) and V buffer (kt+1)&1 (tile
     // kt+1), both last read in step kt-1.
-    auto step = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag) __attribute__((always_inline)) {
+    //
+    // The two buffers a step reads and the two it refills are distinct; they
+    // are passed as restrict pointers to say so.
+    auto step_bufs = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag,
+                         uint16_t* __restrict__ k_rd, uint16_t* __restrict__ k_cp,
+                         uint16_t* __restrict__ v_rd, uint16_t* __restrict__ v_cp) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
         if constexpr (!LAST) {
-            load_k(kt + 2);
-            load_v(kt + 1);
-            qk(kt + 1);
+            load_k(kt + 2, k_cp);
+            load_v(kt + 1, v_cp);
+            qk(k_rd);
         }
         softmax_exp(mask_cur);
-        pv(kt);
+        pv(v_rd);
         if constexpr (!LAST) {
             tile_max(kt + 1, mask_next);
             rescale();
-            store_k(kt & 1);
-            store_v((kt + 1) & 1);
+            copies_done();
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -362,20 +383,22 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
             __syncthreads();
         }
     };
+    auto step = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag) __attribute__((always_inline)) {
+        const int cur = kt & 1, nxt = cur ^ 1;
+        step_bufs(kt, mask_cur, mask_next, last_tag, Ks[nxt], Ks[cur], Vs[cur], Vs[nxt]);
+    };
     // Tiles every row of the workgroup sees in full need no mask; the last
     // tile has no successor to prefetch.
     using F = std::false_type;
     using T = std::true_type;
     const int n_full = min(nv_min / KT, n_kt);
     if (n_kt > 0) {
-        load_k(0);
-        load_v(0);
-        store_k(0);
-        store_v(0);
-        load_k(1);
-        store_k(1);
+        load_k(0, Ks[0]);
+        load_v(0, Vs[0]);
+        load_k(1, Ks[1]);
+        copies_done();
         __syncthreads();
-        qk(0);
+        qk(Ks[0]);
         if (n_full > 0)
             tile_max(0, F{});
         else

@@ -252,13 +252,14 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             if constexpr (MASK) {
+                // key kt*KT + kb*32 + 8*(r/4) + 4*hf + r%4 is visible iff it is
+                // below nvq: compare the compile-time part against one bound
+                const int lim = nvq[qb] - kt * KT - 4 * hf;
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kt * KT + kb * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        s[qb][kb][r] = (key < nvq[qb]) ? s[qb][kb][r] : -INFINITY;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        s[qb][kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3) < lim) ? s[qb][kb][r] : -INFINITY;
             }
             float tmax = -INFINITY;
 #pragma unroll
@@ -301,9 +302,10 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
             nbias[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
     };
     // P = exp2(S*c - mref*c) of the current tile, the running sum, and P
-    // packed to bf16 in the order the P.V MFMAs consume it.
+    // packed to bf16 in the order the P.V MFMAs consume it.  Masked scores
+    // are -inf and c > 0, so their exponentials are exactly 0.
     auto softmax_exp = [&](auto mask_tag) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(mask_tag)::value;
+        (void)mask_tag;
         auto& s = scur;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
@@ -313,9 +315,7 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const float sv = s[qb][kb][r];
-                    float pv = fast_exp2(fmaf(sv, c, nbias[qb]));
-                    if constexpr (MASK)
-                        pv = (sv == -INFINITY) ? 0.f : pv;
+                    const float pv = fast_exp2(fmaf(sv, c, nbias[qb]));
                     s[qb][kb][r] = pv;
                     ps += pv;
                 }

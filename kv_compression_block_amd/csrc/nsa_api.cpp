@@ -411,10 +411,12 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
     a.G = (int)(plan->N1 / plan->N2);
     a.l = (int)plan->l;
     a.d = (int)plan->d;
-    a.c = c;
+    // A positive exponent scale keeps exp2(-inf * c) = 0 for masked scores
+    // (a zero scale makes every score 0: any tiny c gives the same P = 1).
+    a.c = std::fmax(c, 1e-30f);
     a.abs_scale = abs_scale;
     // the running max moves only when a score beats it by more than 8 in base 2
-    a.thr = (c > 0.f) ? std::fmin(8.0f / c, 3.0e38f) : 3.0e38f;
+    a.thr = std::fmin(8.0f / a.c, 3.0e38f);
     a.qsign = q_sign(plan);
     hipError_t e = nsa::launch_cmp_attn((int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, s);
     if (e != hipSuccess)

@@ -456,14 +456,15 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     }
 }
 
-// Launch shape per head-dim pair: query-row blocks per wave (QB) and key-tile
-// length (KT).  QB = 1 keeps each wave within 256 registers (two waves per
-// SIMD); KT = 32 keeps the D1 = 192 double-buffered tiles within 80 KB of LDS
-// so that two workgroups share a CU.
+// Launch shape per head-dim pair: query-row blocks per wave (QB), key-tile
+// length (KT) and waves per workgroup.  QB = 1 keeps each wave within 256
+// registers; KT = 32 keeps the score tiles small enough for three
+// workgroups per CU (four for D2 = 64) and the double-buffered tiles within
+// the LDS share of each.
 #define NSA_ATTN_CONFIGS(X)      \
-    X(64, 64, 1, 64, 4)          \
-    X(128, 64, 1, 64, 4)         \
-    X(128, 128, 1, 64, 4)        \
+    X(64, 64, 1, 32, 4)          \
+    X(128, 64, 1, 32, 4)         \
+    X(128, 128, 1, 32, 4)        \
     X(192, 64, 1, 32, 4)         \
     X(192, 128, 1, 32, 4)
 

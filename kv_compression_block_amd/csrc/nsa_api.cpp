@@ -263,7 +263,7 @@ nsa_status nsa_compress_attention_get_workspace(
                     (long long)S_max, 64 * nsa::kTopkMaxNpl);
     const int R = (int)(lsel / d);
     const int H = R + (int)(l / d) - 2;
-    if (H + 1 > 16 || H >= nsa::kKeyTile)
+    if (H + 1 > 16 || H >= nsa::kKeyTileMin)
         return fail(NSA_ERR_UNSUPPORTED, "remap stencil of %d taps is not built", H + 1);
     const int sb = (int)(((S_max + 63) / 64) * 64 > 0 ? ((S_max + 63) / 64) * 64 : 64);
     // Largest workgroup whose LDS lets two workgroups share a CU; K double

@@ -59,7 +59,11 @@ struct AttnParams {
     uint32_t qsign;       // 0x80008000 when scale < 0 (q negated), else 0
 };
 
-constexpr int kKeyTile = 64;   // compressed entries per tile of the top-k kernel
+// Compressed entries per key tile of the importance/top-k kernel: 32 keeps
+// its registers within three waves per SIMD up to D1 = 128; D1 = 192 stays
+// at two waves either way and prefers the longer tile.
+constexpr int topk_key_tile(int d1) { return d1 > 128 ? 64 : 32; }
+constexpr int kKeyTileMin = 32;
 
 hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream);
 bool cmp_attn_supported(int d1, int d2);

@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
 {
     constexpr int GP = 1 << LOG2GP;
     constexpr int TOKW = 64 / GP;           // tokens per wave
-    constexpr int KT = kKeyTile;
+    constexpr int KT = topk_key_tile(D1);
+    constexpr int NKB = KT / 32;            // 32-entry blocks per key tile
     constexpr int KS = D1 + 8;
     constexpr int NKS = D1 / 16;
     constexpr int KCH = D1 / 8;
@@ -196,17 +197,17 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
         if (full_wg && kt + 1 < n_kt)
             load_tile(kt + 1);
 
-        f32x16 s[2][2];
+        f32x16 s[2][NKB];
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     s[rr][kb][r] = 0.f;
         const uint16_t* kt_lds = Ks + buf * KT * KS;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
                 const bf16x8 kf = as_bf16x8(*(const u32x4*)&kt_lds[(kb * 32 + l32) * KS + ks * 16 + hf * 8]);
@@ -217,12 +218,13 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
         }
 
         // P, masked on the last tiles, summed over the heads of each token.
-        float acc[TOKW][2];
+        float acc[TOKW][NKB];
 #pragma unroll
         for (int tw = 0; tw < TOKW; ++tw)
-            acc[tw][0] = acc[tw][1] = 0.f;
+            for (int kb = 0; kb < NKB; ++kb)
+                acc[tw][kb] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
                 const int key = kt * KT + kb * 32 + l32;
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
         for (int tw = 0; tw < TOKW; ++tw) {
             if constexpr (GP >= 8) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
+                for (int kb = 0; kb < NKB; ++kb) {
                     const float v = half_sum(acc[tw][kb]);
                     if (hf == 0)
                         my_ring[tw * RING + ((kt * KT + kb * 32 + l32) & (RING - 1))] = v;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
             } else {
                 if ((tw & HSH) == 0) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    for (int kb = 0; kb < NKB; ++kb)
                         my_ring[(tw + hf * HSH) * RING + ((kt * KT + kb * 32 + l32) & (RING - 1))] = acc[tw][kb];
                 }
             }
@@ -449,7 +451,7 @@ int topk_log2_gp(int G)
 size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs)
 {
     const size_t tokw = (size_t)(64 >> log2gp);
-    return (size_t)kbufs * kKeyTile * (d1 + 8) * 2 + (size_t)waves * tokw * kTopkRing * 4 +
+    return (size_t)kbufs * topk_key_tile(d1) * (d1 + 8) * 2 + (size_t)waves * tokw * kTopkRing * 4 +
            (size_t)waves * tokw * sb * 4 + (size_t)waves * 64 * 4;
 }
 

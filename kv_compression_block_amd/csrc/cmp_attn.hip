@@ -7,17 +7,18 @@
 //   * A workgroup is 4 waves; a wave owns QB blocks of 32 query rows of one
 //     (sequence, KV head).  A row is (token, query head of the group): the
 //     group's heads of a token are adjacent rows, so they share every K/V
-//     tile and every mask.  With QB = 1 a wave stays within 256 registers,
-//     so two waves share each SIMD (two workgroups per CU): one wave's
-//     softmax VALU work overlaps the other's MFMAs, and one workgroup's
-//     prologue/epilogue overlaps the other's main loop.
+//     tile and every mask.  With QB = 1 and KT = 32 a wave of the D1 = D2 =
+//     128 kernel stays within 168 registers, so three waves share each SIMD
+//     (three workgroups per CU): one wave's softmax VALU work overlaps the
+//     others' MFMAs, and one workgroup's prologue/epilogue overlaps the
+//     others' main loops.
 //   * K and V tiles of KT compressed entries are copied straight from
 //     global memory into LDS by the buffer unit (no register staging),
-//     double buffered: the copies of the next tiles are in flight during the
-//     current tile's MFMAs.  K rows carry 16 bytes of padding; V rows are
-//     stored as they are, with XOR-swizzled 16-byte chunks, and the P.V
-//     operand is read transposed (ds_read_b64_tr_b16) in the order the score
-//     accumulator leaves P in.
+//     through three rotating slots each, so a copy has about one pipeline
+//     step to land before anything waits for it.  K rows carry 16 bytes of
+//     padding; V rows are stored as they are, with XOR-swizzled 16-byte
+//     chunks, and the P.V operand is read transposed (ds_read_b64_tr_b16)
+//     in the order the score accumulator leaves P in.
 //   * Scores are computed transposed, S^T = K Q^T: a lane owns one query
 //     column and 16 keys per 32x32 block, so the row max and sum are
 //     in-lane plus one exchange with the lane 32 away.  P^T is then directly
@@ -87,8 +88,8 @@ template <int D1, int D2, int QB, int KT, int W>
 __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_fwd(AttnParams p)
 {
     using C = AttnCfg<D1, D2, QB, KT, W>;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::KBUF];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KT * D2];
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[3][C::KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[3][KT * D2];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)kt * KT * kv_stride1, tile_bytes(kt, kst_b, D1 * 2));
 #pragma unroll
         for (int j = 0; j < C::KIPW; ++j)
-            if (C::KINS % W == 0 || j * W + wave < C::KINS)
+            if (j < C::KINS / W || j * W + wave < C::KINS)
                 copy16_to_lds(kr, dst + (j * W + wave) * 512, kdo[j]);
     };
     auto load_v = [&](int kt, uint16_t* dst) __attribute__((always_inline)) {
@@ -179,9 +180,22 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
         for (int j = 0; j < C::VIPW; ++j)
             copy16_to_lds(vr, dst + (j * W + wave) * 512, vdo[j]);
     };
-    // The copies of this wave have landed in LDS (the barrier that follows
+    // All copies of this wave have landed in LDS (the barrier that follows
     // makes every wave's copies visible).
     auto copies_done = [&]() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };
+    // End of a pipeline step: this wave's LDS reads have returned and its
+    // copies issued before the step have landed (only the step's own, at
+    // least NCP per wave, may still be in flight); then the workgroup
+    // barrier.  The empty asm statements keep the compiler from moving LDS
+    // accesses across the barrier.
+    constexpr int NCP = C::KINS / W + C::VIPW;
+    static_assert(NCP < 64, "vmcnt range");
+    auto step_barrier = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt((NCP & 15) | ((NCP >> 4) << 14) | 0x0070);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    };
 
     // P.V operand addressing (ds_read_b64_tr_b16): in each 16-lane group,
     // lane i supplies the 8 bytes of row key0 + i/4, dims dimbase + 4*(i%4)
@@ -353,39 +367,39 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     // holds S(kt) with its mask applied and nbias is final for it.  The
     // step issues the QK^T MFMAs of tile kt+1 next to the exponentials of
     // tile kt, then the P.V MFMAs of tile kt next to the max of tile kt+1,
-    // so both MFMA phases have independent vector work beside them.  K runs
-    // one tile ahead of V: step kt reads K buffer (kt+1)&1 and V buffer kt&1
-    // and refills K buffer kt&1 (tile kt+2) and V buffer (kt+1)&1 (tile
-    // kt+1), both last read in step kt-1.
+    // so both MFMA phases have independent vector work beside them.
     //
-    // The two buffers a step reads and the two it refills are distinct; they
-    // are passed as restrict pointers to say so.
-    auto step_bufs = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag,
-                         uint16_t* __restrict__ k_rd, uint16_t* __restrict__ k_cp,
-                         uint16_t* __restrict__ v_rd, uint16_t* __restrict__ v_cp) __attribute__((always_inline)) {
+    // K and V tiles rotate through three LDS slots each (tile t in slot
+    // t % 3; bs0/bs1/bs2 hold the slots of tiles kt, kt+1, kt+2).  Step kt
+    // reads K(kt+1) and V(kt); right after its last read of a kind it
+    // refills the slot read in step kt-1: K(kt+3) once the QK^T operands are
+    // in registers, V(kt+2) once the P.V operands are.  A copy therefore has
+    // the rest of its step and part of the next to land, and the barrier at
+    // the end of a step waits only for the copies issued before the step.
+    int bs0 = 0, bs1 = 1, bs2 = 2;
+    auto step = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
         if constexpr (!LAST) {
-            load_k(kt + 2, k_cp);
-            load_v(kt + 1, v_cp);
-            qk(k_rd);
+            qk(Ks[bs1]);
+            load_k(kt + 3, Ks[bs0]);
         }
         softmax_exp(mask_cur);
-        pv(v_rd);
+        pv(Vs[bs0]);
         if constexpr (!LAST) {
+            load_v(kt + 2, Vs[bs2]);
             tile_max(kt + 1, mask_next);
             rescale();
-            copies_done();
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
                     scur[qb][kb] = snxt[qb][kb];
-            __syncthreads();
+            const int t = bs0;
+            bs0 = bs1;
+            bs1 = bs2;
+            bs2 = t;
+            step_barrier();
         }
-    };
-    auto step = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag) __attribute__((always_inline)) {
-        const int cur = kt & 1, nxt = cur ^ 1;
-        step_bufs(kt, mask_cur, mask_next, last_tag, Ks[nxt], Ks[cur], Vs[cur], Vs[nxt]);
     };
     // Tiles every row of the workgroup sees in full need no mask; the last
     // tile has no successor to prefetch.
@@ -396,6 +410,8 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
         load_k(0, Ks[0]);
         load_v(0, Vs[0]);
         load_k(1, Ks[1]);
+        load_k(2, Ks[2]);
+        load_v(1, Vs[1]);
         copies_done();
         __syncthreads();
         qk(Ks[0]);
@@ -459,8 +475,8 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
 // Launch shape per head-dim pair: query-row blocks per wave (QB), key-tile
 // length (KT) and waves per workgroup.  QB = 1 keeps each wave within 256
 // registers; KT = 32 keeps the score tiles small enough for three
-// workgroups per CU (four for D2 = 64) and the double-buffered tiles within
-// the LDS share of each.
+// workgroups per CU (four for D2 = 64) and the three K and V slots within
+// the LDS share of each (52 KB for D1 = D2 = 128).
 #define NSA_ATTN_CONFIGS(X)      \
     X(64, 64, 1, 32, 4)          \
     X(128, 64, 1, 32, 4)         \

@@ -444,24 +444,50 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     }
 
     // ---- epilogue ------------------------------------------------------------------
+    // O goes out through LDS so that the global stores are whole 16-byte
+    // chunks of consecutive dims, 128 contiguous bytes per output row and
+    // pass: a lane's accumulators hold 4-dim pieces of one row.  Every wave
+    // is done with the K slots after this barrier; each wave stages its rows
+    // in a private part of them, half of D2 per pass.
+    __syncthreads();
+    constexpr int HD = D2 / 2;                 // dims per pass
+    constexpr int OPITCH = HD + 8;             // staging row pitch (bf16), 16 B pad
+    constexpr int CPR = HD / 8;                // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPR;              // staged rows per read instruction
+    static_assert(W * 32 * OPITCH <= 3 * C::KBUF, "O staging fits the K slots");
+    uint16_t* ostg = &Ks[0][0] + wave * 32 * OPITCH;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float lf = half_sum(lsum[qb]);
         const bool empty = (mtrue[qb] == -INFINITY);
         const float inv = empty ? 0.f : 1.f / lf;
-        if (!vq[qb])
-            continue;
-        uint16_t* orow = p.out + grow[qb] * D2;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int dv = db * 32 + 8 * r4 + 4 * hf;
-                u32x2 w2 = {pack_bf16x2(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv),
-                            pack_bf16x2(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv)};
-                *(u32x2*)(orow + dv) = w2;
+            for (int db = h * C::NDB / 2; db < (h + 1) * C::NDB / 2; ++db) {
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int dv = (db - h * C::NDB / 2) * 32 + 8 * r4 + 4 * hf;
+                    u32x2 w2 = {pack_bf16x2(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv),
+                                pack_bf16x2(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv)};
+                    *(u32x2*)&ostg[l32 * OPITCH + dv] = w2;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int rr = i * RPI + lane / CPR;          // staged row
+                const int ch = lane % CPR;
+                const u32x4 v = *(const u32x4*)&ostg[rr * OPITCH + ch * 8];
+                const int r = row_wg + (wave * QB + qb) * 32 + rr;
+                if (r < rows_total) {
+                    const int tok = r / G;
+                    const int64_t orow = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + (r - tok * G);
+                    *(u32x4*)(p.out + orow * D2 + h * HD + ch * 8) = v;
+                }
             }
         }
+        if (!vq[qb])
+            continue;
         const float smv = empty ? -INFINITY : mtrue[qb] * p.abs_scale;
         const float ssv = empty ? 0.f : lf * fast_exp2((mref[qb] - mtrue[qb]) * c);
         const float val = hf == 0 ? smv : ssv;

@@ -206,6 +206,10 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
                 for (int r = 0; r < 16; ++r)
                     s[rr][kb][r] = 0.f;
         const uint16_t* kt_lds = Ks + buf * KT * KS;
+        // Raised wave priority while the MFMAs issue: a wave that reaches its
+        // MFMAs gets them into the matrix pipe ahead of the other waves'
+        // vector work, which then fills the MFMA shadow.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -216,6 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
                     s[rr][kb] = mfma32(qa[rr][ks], kf, s[rr][kb]);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // P, masked on the last tiles, summed over the heads of each token.
         float acc[TOKW][NKB];

@@ -84,12 +84,20 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
 }
 
 
+// At least three waves per SIMD for D1 = D2 = 128 (168 registers, a few
+// values spilled around the main loop), which the unrolled loop would
+// otherwise exceed; two elsewhere.
 template <int D1, int D2, int QB, int KT, int W>
-__global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_fwd(AttnParams p)
+__global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cmp_attn_fwd(AttnParams p)
 {
     using C = AttnCfg<D1, D2, QB, KT, W>;
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[3][C::KBUF];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[3][KT * D2];
+    // Three K and three V slots, each its own LDS object: the compiler then
+    // knows which slot every copy and every read touches and inserts no wait
+    // for a copy into another slot.
+    __shared__ __attribute__((aligned(16))) uint16_t K0[C::KBUF], K1[C::KBUF], K2[C::KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t V0[KT * D2], V1[KT * D2], V2[KT * D2];
+    auto kslot = [&](int i) __attribute__((always_inline)) { return i == 0 ? K0 : (i == 1 ? K1 : K2); };
+    auto vslot = [&](int i) __attribute__((always_inline)) { return i == 0 ? V0 : (i == 1 ? V1 : V2); };
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -370,23 +378,23 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     // so both MFMA phases have independent vector work beside them.
     //
     // K and V tiles rotate through three LDS slots each (tile t in slot
-    // t % 3; bs0/bs1/bs2 hold the slots of tiles kt, kt+1, kt+2).  Step kt
-    // reads K(kt+1) and V(kt); right after its last read of a kind it
-    // refills the slot read in step kt-1: K(kt+3) once the QK^T operands are
-    // in registers, V(kt+2) once the P.V operands are.  A copy therefore has
-    // the rest of its step and part of the next to land, and the barrier at
-    // the end of a step waits only for the copies issued before the step.
-    int bs0 = 0, bs1 = 1, bs2 = 2;
-    auto step = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag) __attribute__((always_inline)) {
+    // t % 3).  Step kt reads K(kt+1) and V(kt), and first refills the slots
+    // read in step kt-1 with K(kt+3) and V(kt+2): the first barrier that
+    // waits for those copies is the one at the end of step kt+1, so each has
+    // more than a step to land.  The main loop runs three steps per trip with
+    // fixed slot objects, which is what lets the compiler see that the
+    // step's reads and copies touch different slots.
+    auto step_bufs = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag,
+                         uint16_t* k_rd, uint16_t* k_cp, uint16_t* v_rd, uint16_t* v_cp) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
         if constexpr (!LAST) {
-            qk(Ks[bs1]);
-            load_k(kt + 3, Ks[bs0]);
+            load_k(kt + 3, k_cp);
+            load_v(kt + 2, v_cp);
+            qk(k_rd);
         }
         softmax_exp(mask_cur);
-        pv(Vs[bs0]);
+        pv(v_rd);
         if constexpr (!LAST) {
-            load_v(kt + 2, Vs[bs2]);
             tile_max(kt + 1, mask_next);
             rescale();
 #pragma unroll
@@ -394,12 +402,14 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
                     scur[qb][kb] = snxt[qb][kb];
-            const int t = bs0;
-            bs0 = bs1;
-            bs1 = bs2;
-            bs2 = t;
             step_barrier();
         }
+    };
+    // Step with the slots picked at run time (the few steps outside the
+    // unrolled loop).
+    auto step = [&](const int kt, auto mask_cur, auto mask_next, auto last_tag) __attribute__((always_inline)) {
+        const int b0 = kt % 3, b1 = (kt + 1) % 3, b2 = (kt + 2) % 3;
+        step_bufs(kt, mask_cur, mask_next, last_tag, kslot(b1), kslot(b0), vslot(b0), vslot(b2));
     };
     // Tiles every row of the workgroup sees in full need no mask; the last
     // tile has no successor to prefetch.
@@ -407,14 +417,14 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     using T = std::true_type;
     const int n_full = min(nv_min / KT, n_kt);
     if (n_kt > 0) {
-        load_k(0, Ks[0]);
-        load_v(0, Vs[0]);
-        load_k(1, Ks[1]);
-        load_k(2, Ks[2]);
-        load_v(1, Vs[1]);
+        load_k(0, K0);
+        load_v(0, V0);
+        load_k(1, K1);
+        load_k(2, K2);
+        load_v(1, V1);
         copies_done();
         __syncthreads();
-        qk(Ks[0]);
+        qk(K0);
         if (n_full > 0)
             tile_max(0, F{});
         else
@@ -427,7 +437,15 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
                 scur[qb][kb] = snxt[qb][kb];
         __syncthreads();   // step 0 refills K buffer 0, which qk(0) just read
         int kt = 0;
-        // tiles kt and kt+1 both unmasked
+        // tiles kt and kt+1 both unmasked, three steps per trip
+        for (; kt + 3 < min(n_full, n_kt); kt += 3) {
+            step_bufs(kt, F{}, F{}, F{}, K1, K0, V0, V2);
+            __builtin_amdgcn_sched_barrier(0);
+            step_bufs(kt + 1, F{}, F{}, F{}, K2, K1, V1, V0);
+            __builtin_amdgcn_sched_barrier(0);
+            step_bufs(kt + 2, F{}, F{}, F{}, K0, K2, V2, V1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         for (; kt + 1 < min(n_full, n_kt); ++kt)
             step(kt, F{}, F{}, F{});
         // tile kt unmasked, kt+1 masked
@@ -454,8 +472,9 @@ __global__ __launch_bounds__(64 * W, (QB == 1 ? 8 / W : 4 / W)) void k_cmp_attn_
     constexpr int OPITCH = HD + 8;             // staging row pitch (bf16), 16 B pad
     constexpr int CPR = HD / 8;                // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;              // staged rows per read instruction
-    static_assert(W * 32 * OPITCH <= 3 * C::KBUF, "O staging fits the K slots");
-    uint16_t* ostg = &Ks[0][0] + wave * 32 * OPITCH;
+    constexpr int WPS = C::KBUF / (32 * OPITCH);   // waves staged per K slot
+    static_assert(WPS >= 1 && (W + WPS - 1) / WPS <= 3, "O staging fits the K slots");
+    uint16_t* ostg = kslot(wave / WPS) + (wave % WPS) * 32 * OPITCH;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const float lf = half_sum(lsum[qb]);

@@ -26,11 +26,14 @@
 //     sum of at most H+1 ring entries (the remap written as a stencil over
 //     r = m + n with coefficient c(r) = number of (m, n) pairs).  The ring
 //     keeps the H entries a later block still needs.
-//   * Top-k per (token, KV head) row is a wave-wide radix select on the
-//     float bits (scores are >= 0, so their bit patterns order like the
-//     values): 31 ballot-count rounds find the k-th largest score; the rows
-//     above it and the lowest-index ties are compacted, then sorted by
-//     (score desc, index asc) with a 32-lane bitonic network.
+//   * Top-k per (token, KV head) row, wave-local, on the float bits (scores
+//     are >= 0, so their bit patterns order like the values).  A radix
+//     select over the 64 per-lane maxima (one ballot per bit) gives a lower
+//     bound of the k-th largest score; the few candidates at or above it are
+//     staged in LDS and each finds its rank by (score desc, index asc)
+//     against the others.  When more than 64 reach the bound (heavy ties),
+//     a radix select over all candidates finds the k-th largest score and
+//     the picks above it plus the lowest-index ties are ranked the same way.
 //   * Deterministic: every sum has a fixed order; no atomics.
 #include <type_traits>
 
@@ -50,7 +53,9 @@ __device__ __forceinline__ void wave_lds_sync()
 }
 
 template <int D1, int LOG2GP>
-__global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
+// Three waves per SIMD where the registers allow it (D1 = 128 with groups
+// of 16 or more), two elsewhere.
+__global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc_topk(TopkParams p)
 {
     constexpr int GP = 1 << LOG2GP;
     constexpr int TOKW = 64 / GP;           // tokens per wave
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
     uint16_t* Ks = (uint16_t*)smem;                        // [nbuf][KT * KS]
     float* ring = (float*)(smem + nbuf * KT * KS * 2);     // [waves * TOKW][RING]
     float* bins = ring + waves * TOKW * RING;              // [waves * TOKW][sb]
-    uint32_t* stg = (uint32_t*)(bins + waves * TOKW * p.sb);  // [waves][64]
+    uint32_t* stg = (uint32_t*)(bins + waves * TOKW * p.sb);  // [waves][128]
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
     wave_lds_sync();
 
     // ---- top-k per (token, KV head), wave-local ----------------------------------
-    uint32_t* my_stg = stg + wave * 64;      // [0,32): score bits, [32,64): index
+    uint32_t* my_stg = stg + wave * 128;     // staged picks: score bits, then indices
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int tw = 0; tw < TOKW; ++tw) {
         const int tok = tok_w + tw;
@@ -344,74 +349,137 @@ __global__ __launch_bounds__(256, 2) void k_slc_topk(TopkParams p)
             const int j = lane + 64 * i;
             key[i] = (i < nch && j < nvalid) ? __float_as_uint(brow[j]) : 0u;
         }
-        // Radix select, most significant bit first: tau grows while at least
-        // kk keys stay >= tau.  Once exactly kk keys are >= tau they are the
-        // kk largest and the search stops; otherwise tau ends as the kk-th
-        // largest bit pattern.
-        uint32_t tau = 0;
+        int32_t* trow = p.topk + (tg * p.N2 + g) * p.count;
+        // Lower bound first: the kk-th largest of the per-lane maxima.  The
+        // kk lanes at or above it hold kk distinct scores >= it, so every
+        // score of the top kk is >= it too; usually only a few dozen
+        // candidates reach it.
+        uint32_t tau0 = 0;
         if (nvalid > kk) {
-            for (int bit = 30; bit >= 0; --bit) {
-                const uint32_t cand = tau | (1u << bit);
-                int cnt = 0;
+            uint32_t lmax = 0;
 #pragma unroll
-                for (int i = 0; i < kTopkMaxNpl; ++i)
-                    if (i < nch)
-                        cnt += __popcll(__ballot(key[i] >= cand));
+            for (int i = 0; i < kTopkMaxNpl; ++i)
+                if (i < nch)
+                    lmax = max(lmax, key[i]);
+            for (int bit = 30; bit >= 0; --bit) {
+                const uint32_t cand = tau0 | (1u << bit);
+                const int cnt = __popcll(__ballot(lmax >= cand));
                 if (cnt >= kk) {
-                    tau = cand;
+                    tau0 = cand;
                     if (cnt == kk)
                         break;
                 }
             }
         }
-        // Everything above tau, then the lowest-index candidates equal to tau.
-        int n_gt = 0;
+        int ncand = 0;
 #pragma unroll
         for (int i = 0; i < kTopkMaxNpl; ++i)
             if (i < nch)
-                n_gt += __popcll(__ballot(key[i] > tau));
-        const int need_eq = kk - n_gt;
-        int pos_gt = 0, pos_eq = 0;
+                ncand += __popcll(__ballot(lane + 64 * i < nvalid && key[i] >= tau0));
+        if (ncand <= 64) {
+            // Stage the candidates (score bits at [0, 64), indices at [64, 128)),
+            // then each ranks itself against all of them by (score desc,
+            // index asc); the first kk ranks are the picks.
+            int pos = 0;
 #pragma unroll
-        for (int i = 0; i < kTopkMaxNpl; ++i) {
-            if (i < nch) {
-                const bool cand_i = lane + 64 * i < nvalid;
-                const bool gt = cand_i && key[i] > tau;
-                const bool eq = cand_i && key[i] == tau;
-                const uint64_t bg = __ballot(gt);
-                const uint64_t beq = __ballot(eq);
-                const int rg = __popcll(bg & lt_mask);
-                const int re = __popcll(beq & lt_mask);
-                if (gt) {
-                    my_stg[pos_gt + rg] = key[i];
-                    my_stg[32 + pos_gt + rg] = (uint32_t)(lane + 64 * i);
+            for (int i = 0; i < kTopkMaxNpl; ++i) {
+                if (i < nch) {
+                    const bool sel = lane + 64 * i < nvalid && key[i] >= tau0;
+                    const uint64_t bs = __ballot(sel);
+                    if (sel) {
+                        const int at = pos + __popcll(bs & lt_mask);
+                        my_stg[at] = key[i];
+                        my_stg[64 + at] = (uint32_t)(lane + 64 * i);
+                    }
+                    pos += __popcll(bs);
                 }
-                if (eq && pos_eq + re < need_eq) {
-                    my_stg[n_gt + pos_eq + re] = key[i];
-                    my_stg[32 + n_gt + pos_eq + re] = (uint32_t)(lane + 64 * i);
-                }
-                pos_gt += __popcll(bg);
-                pos_eq += __popcll(beq);
             }
-        }
-        wave_lds_sync();
-        // Order: score descending, index ascending.  Each pick counts the picks
-        // that precede it and writes itself at that rank; unused slots get -1.
-        int32_t* trow = p.topk + (tg * p.N2 + g) * p.count;
-        if (lane < kk) {
-            const uint32_t mk = my_stg[lane];
-            const uint32_t mi = my_stg[32 + lane];
-            int rank = 0;
-            for (int q = 0; q < kk; q += 4) {
-                const u32x4 ok = *(const u32x4*)&my_stg[q];
-                const u32x4 oi = *(const u32x4*)&my_stg[32 + q];
+            wave_lds_sync();
+            if (lane < ncand) {
+                const uint32_t mk = my_stg[lane];
+                const uint32_t mi = my_stg[64 + lane];
+                int rank = 0;
+                for (int q = 0; q < ncand; q += 4) {
+                    const u32x4 ok = *(const u32x4*)&my_stg[q];
+                    const u32x4 oi = *(const u32x4*)&my_stg[64 + q];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rank += (q + e < kk) && (ok[e] > mk || (ok[e] == mk && oi[e] < mi));
+                    for (int e = 0; e < 4; ++e)
+                        rank += (q + e < ncand) && (ok[e] > mk || (ok[e] == mk && oi[e] < mi));
+                }
+                if (rank < kk)
+                    trow[rank] = (int32_t)mi;
             }
-            trow[rank] = (int32_t)mi;
-        } else if (lane < p.count) {
-            trow[lane] = -1;
+            if (lane >= kk && lane < p.count)
+                trow[lane] = -1;
+        } else {
+            // Radix select, most significant bit first: tau grows while at least
+            // kk keys stay >= tau.  Once exactly kk keys are >= tau they are the
+            // kk largest and the search stops; otherwise tau ends as the kk-th
+            // largest bit pattern.
+            uint32_t tau = 0;
+            if (nvalid > kk) {
+                for (int bit = 30; bit >= 0; --bit) {
+                    const uint32_t cand = tau | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int i = 0; i < kTopkMaxNpl; ++i)
+                        if (i < nch)
+                            cnt += __popcll(__ballot(key[i] >= cand));
+                    if (cnt >= kk) {
+                        tau = cand;
+                        if (cnt == kk)
+                            break;
+                    }
+                }
+            }
+            // Everything above tau, then the lowest-index candidates equal to tau.
+            int n_gt = 0;
+#pragma unroll
+            for (int i = 0; i < kTopkMaxNpl; ++i)
+                if (i < nch)
+                    n_gt += __popcll(__ballot(key[i] > tau));
+            const int need_eq = kk - n_gt;
+            int pos_gt = 0, pos_eq = 0;
+#pragma unroll
+            for (int i = 0; i < kTopkMaxNpl; ++i) {
+                if (i < nch) {
+                    const bool cand_i = lane + 64 * i < nvalid;
+                    const bool gt = cand_i && key[i] > tau;
+                    const bool eq = cand_i && key[i] == tau;
+                    const uint64_t bg = __ballot(gt);
+                    const uint64_t beq = __ballot(eq);
+                    const int rg = __popcll(bg & lt_mask);
+                    const int re = __popcll(beq & lt_mask);
+                    if (gt) {
+                        my_stg[pos_gt + rg] = key[i];
+                        my_stg[32 + pos_gt + rg] = (uint32_t)(lane + 64 * i);
+                    }
+                    if (eq && pos_eq + re < need_eq) {
+                        my_stg[n_gt + pos_eq + re] = key[i];
+                        my_stg[32 + n_gt + pos_eq + re] = (uint32_t)(lane + 64 * i);
+                    }
+                    pos_gt += __popcll(bg);
+                    pos_eq += __popcll(beq);
+                }
+            }
+            wave_lds_sync();
+            // Order: score descending, index ascending.  Each pick counts the picks
+            // that precede it and writes itself at that rank; unused slots get -1.
+            if (lane < kk) {
+                const uint32_t mk = my_stg[lane];
+                const uint32_t mi = my_stg[32 + lane];
+                int rank = 0;
+                for (int q = 0; q < kk; q += 4) {
+                    const u32x4 ok = *(const u32x4*)&my_stg[q];
+                    const u32x4 oi = *(const u32x4*)&my_stg[32 + q];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        rank += (q + e < kk) && (ok[e] > mk || (ok[e] == mk && oi[e] < mi));
+                }
+                trow[rank] = (int32_t)mi;
+            } else if (lane < p.count) {
+                trow[lane] = -1;
+            }
         }
         wave_lds_sync();   // the staging area is reused by the next token
     }
@@ -457,7 +525,7 @@ size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs)
 {
     const size_t tokw = (size_t)(64 >> log2gp);
     return (size_t)kbufs * topk_key_tile(d1) * (d1 + 8) * 2 + (size_t)waves * tokw * kTopkRing * 4 +
-           (size_t)waves * tokw * sb * 4 + (size_t)waves * 64 * 4;
+           (size_t)waves * tokw * sb * 4 + (size_t)waves * 128 * 4;
 }
 
 bool slc_topk_supported(int d1) { return d1 == 64 || d1 == 128 || d1 == 192; }

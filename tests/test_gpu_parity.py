@@ -19,7 +19,7 @@ import torch
 import oracle
 import synth
 from parity import (assert_close_out, assert_pslc, assert_softmax_stats, assert_topk,
-                    bf16_to_f64, gpu_attention, gpu_compress, log, upload_bits)
+                    bf16_to_f64, gpu_attention, gpu_compress, log, token_meta, upload_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +132,33 @@ EDGES = {
 @pytest.mark.parametrize("name", sorted(EDGES))
 def test_edge_cases(name):
     _run_small(dataclasses.replace(EDGES[name], name=name))
+
+
+def test_topk_exact_ties():
+    """q = 0: every score is 0, every visible P of a row is the same and the
+    importance scores of all interior select blocks are bitwise equal.  The
+    top-k must then pick the lowest-index interior blocks exactly (ties go to
+    the lower index), both where at most 64 candidates tie (rows of up to ~66
+    blocks) and where more do (rows past ~4200 tokens, up to 94 blocks)."""
+    wl = dataclasses.replace(BASE, name="exact-ties", count=16, seqlens=(6000,))
+    log(f"[case] {wl.name}: generate on GPU, q = 0")
+    inp = synth.make_inputs(wl, device="cuda")
+    inp["q"].zero_()
+    bits = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    log(f"[case] {wl.name}: oracle")
+    ref = oracle.run(wl, bits["q"], bits["k"], bits["v"], bits["w"])
+    log(f"[case] {wl.name}: GPU attention on the oracle's compressed K/V")
+    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bf16"]), upload_bits(ref["vc_bf16"]))
+    _check_all(wl, g, ref, ref["tokens"])
+    gi, ri = g["topk"].cpu().numpy(), ref["topk"]
+    long_rows = 0
+    for k, (t, S) in enumerate(token_meta(wl, ref["tokens"])):
+        nvalid = min(t // wl.lsel + 1, S)
+        kk = min(wl.count, nvalid)
+        long_rows += nvalid >= 70
+        for h in range(wl.N2):
+            assert sorted(gi[k, h, :kk].tolist()) == sorted(ri[k, h, :kk].tolist()), (t, h, gi[k, h], ri[k, h])
+    assert long_rows > 0
 
 
 def test_bitwise_deterministic():

@@ -185,6 +185,33 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     const float c = p.c;
     const int R = p.R;
     const int H = p.H;
+    float cf[8];                          // remap coefficients, kept in registers
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        cf[r] = p.coef[r];
+    // Importance score of select block j from a token's ring: the remap
+    // stencil sum over r = 0..H of coef(r) * P[R*j - r], ascending r, with the
+    // entries at or past `limit` taken as 0.  Up to H = 7 the ring reads are
+    // independent and go out together.
+    auto stencil = [&](const float* rg, int j, int limit) __attribute__((always_inline)) {
+        float v = 0.f;
+        if (H < 8) {
+            float e[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                e[r] = rg[(R * j - r) & (RING - 1)];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                if (r <= H)
+                    v = fmaf(cf[r], (R * j - r < limit) ? e[r] : 0.f, v);
+        } else {
+            for (int r = 0; r <= H; ++r) {
+                const int k = R * j - r;
+                v = fmaf(p.coef[r], (k < limit) ? rg[k & (RING - 1)] : 0.f, v);
+            }
+        }
+        return v;
+    };
 
     if (n_kt > 0) {
         if (full_wg) {
@@ -276,13 +303,8 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         const int nj = min((key0 + KT + R - 1) / R, be.S_sel) - jlo;
         if (lane < nj) {
             const int j = jlo + lane;
-            for (int tw = 0; tw < TOKW; ++tw) {
-                const float* rg = my_ring + tw * RING;
-                float v = 0.f;
-                for (int r = 0; r <= H; ++r)
-                    v = fmaf(p.coef[r], rg[(R * j - r) & (RING - 1)], v);
-                my_bins[tw * p.sb + j] = v;
-            }
+            for (int tw = 0; tw < TOKW; ++tw)
+                my_bins[tw * p.sb + j] = stencil(my_ring + tw * RING, j, 0x7FFFFFFF);
         }
         wave_lds_sync();
 
@@ -305,22 +327,16 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     for (; kt < n_kt; ++kt)
         key_tile(kt, std::true_type{});
 
-    // Select blocks past the last tile: only entries < keys_done can be non-zero.
+    // Select blocks past the last tile: only entries < keys_done can be
+    // non-zero.  Without the debug output only the blocks the wave's tokens
+    // may pick (j * l' <= t) are needed.
     {
         const int keys_done = n_kt * KT;
         const int jlo = (keys_done + R - 1) / R;
-        for (int j = jlo + lane; j < be.S_sel; j += 64) {
-            for (int tw = 0; tw < TOKW; ++tw) {
-                const float* rg = my_ring + tw * RING;
-                float v = 0.f;
-                for (int r = 0; r <= H; ++r) {
-                    const int k = R * j - r;
-                    const float e = (k < keys_done) ? rg[k & (RING - 1)] : 0.f;
-                    v = fmaf(p.coef[r], e, v);
-                }
-                my_bins[tw * p.sb + j] = v;
-            }
-        }
+        const int j_end = p.pslc ? be.S_sel : min(be.S_sel, (tok_w + TOKW - 1) / p.lsel + 1);
+        for (int j = jlo + lane; j < j_end; j += 64)
+            for (int tw = 0; tw < TOKW; ++tw)
+                my_bins[tw * p.sb + j] = stencil(my_ring + tw * RING, j, keys_done);
     }
     wave_lds_sync();
 

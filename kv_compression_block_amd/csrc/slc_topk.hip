@@ -15,13 +15,13 @@
 //     computed un-transposed (rows = heads, columns = compressed entries):
 //     the sum over a token's heads is then an in-lane sum of accumulator
 //     registers plus, for GP >= 8, one exchange with the lane 32 away.
-//   * K tiles of 64 entries are double buffered in LDS and loaded with
-//     range-limited buffer loads one tile ahead; one workgroup barrier per
-//     tile.  Everything else a wave touches in LDS (its tokens' rings,
+//   * K tiles (32 entries up to D1 = 128, 64 above) are double buffered in
+//     LDS and loaded with range-limited buffer loads one tile ahead; one
+//     workgroup barrier per tile.  Everything else a wave touches in LDS (its tokens' rings,
 //     importance scores and top-k staging) is private to the wave and needs
 //     only wave-level ordering.
 //   * The group-summed P of each token goes to a 128-entry LDS ring indexed
-//     by compressed-entry number; after every 64-entry tile the select blocks
+//     by compressed-entry number; after every key tile the select blocks
 //     whose whole stencil is available are finished as a fixed-order weighted
 //     sum of at most H+1 ring entries (the remap written as a stencil over
 //     r = m + n with coefficient c(r) = number of (m, n) pairs).  The ring

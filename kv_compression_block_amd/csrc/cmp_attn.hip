@@ -464,7 +464,9 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     // ---- epilogue ------------------------------------------------------------------
     // O goes out through LDS so that the global stores are whole 16-byte
     // chunks of consecutive dims, 128 contiguous bytes per output row and
-    // pass: a lane's accumulators hold 4-dim pieces of one row.  Every wave
+    // pass: a lane's accumulators hold 4-dim pieces of one row.  Outputs are
+    // stored non-temporal: nothing in this kernel reads them back, and the
+    // L2 is better kept for the K/V tiles.  Every wave
     // is done with the K slots after this barrier; each wave stages its rows
     // in a private part of them, half of D2 per pass.
     __syncthreads();
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                 if (r < rows_total) {
                     const int tok = r / G;
                     const int64_t orow = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + (r - tok * G);
-                    *(u32x4*)(p.out + orow * D2 + h * HD + ch * 8) = v;
+                    __builtin_nontemporal_store(v, (u32x4*)(p.out + orow * D2 + h * HD + ch * 8));
                 }
             }
         }
@@ -512,8 +514,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         const float val = hf == 0 ? smv : ssv;
         float* dst = (hf == 0 ? p.smax : p.ssum) + grow[qb] * 8;
         f32x4 v4 = {val, val, val, val};
-        *(f32x4*)dst = v4;
-        *(f32x4*)(dst + 4) = v4;
+        __builtin_nontemporal_store(v4, (f32x4*)dst);
+        __builtin_nontemporal_store(v4, (f32x4*)(dst + 4));
     }
 }
 

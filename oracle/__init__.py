@@ -2,7 +2,7 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It wraps ``nsa_oracle.c`` (plain C,
-float64 on bfloat16-widened inputs) through ctypes and shares no code with
+float64 on exactly widened bfloat16 or float16 inputs) through ctypes and shares no code with
 the HIP library in ``kv_compression_block_amd``.
 
 Every function here either marshals arrays or chains the C steps in the
@@ -13,8 +13,9 @@ order the operator pages give them:
   (scores, mask, softmax, output, importance remap, group sum, top-k).
 
 The compressed keys/values that feed attention are the compression results
-rounded to bfloat16 (round to nearest, ties to even), because that is the
-dtype the attention operator takes for its key and value inputs.
+rounded to the element type of the inputs (round to nearest, ties to even),
+because that is the dtype the attention operator takes for its key and value
+inputs.  ``dtype`` is "bf16" or "f16" throughout.
 """
 from __future__ import annotations
 
@@ -58,15 +59,21 @@ def _load():
     lib.nsa_oracle_double_to_bf16.restype = ctypes.c_uint16
     lib.nsa_oracle_round_to_bf16.argtypes = [P, P, I64]
     lib.nsa_oracle_round_to_bf16.restype = None
+    lib.nsa_oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+    lib.nsa_oracle_f16_to_double.restype = ctypes.c_double
+    lib.nsa_oracle_double_to_f16.argtypes = [ctypes.c_double]
+    lib.nsa_oracle_double_to_f16.restype = ctypes.c_uint16
+    lib.nsa_oracle_round_to_f16.argtypes = [P, P, I64]
+    lib.nsa_oracle_round_to_f16.restype = None
     lib.nsa_oracle_threads.argtypes = []
     lib.nsa_oracle_threads.restype = ctypes.c_int
     lib.nsa_oracle_n_cmp.argtypes = [I64, I64, I64]
     lib.nsa_oracle_n_cmp.restype = I64
-    lib.nsa_oracle_compress.argtypes = [P, P, P, I64, I64, I64, I64, I64, P]
+    lib.nsa_oracle_compress.argtypes = [P, P, P, I64, I64, I64, I64, I64, ctypes.c_int, P]
     lib.nsa_oracle_compress.restype = ctypes.c_int
     lib.nsa_oracle_attention.argtypes = [P, P, I64, P, P, P, P, I64,
                                          I64, I64, I64, I64, ctypes.c_double,
-                                         I64, I64, I64, I64,
+                                         I64, I64, I64, I64, ctypes.c_int,
                                          P, P, P, P, I64, P]
     lib.nsa_oracle_attention.restype = ctypes.c_int
     _lib = lib
@@ -80,7 +87,7 @@ def _ptr(a: np.ndarray):
 def _u16(a) -> np.ndarray:
     a = np.ascontiguousarray(a)
     if a.dtype != np.uint16:
-        raise TypeError(f"expected bfloat16 bit patterns as uint16, got {a.dtype}")
+        raise TypeError(f"expected 16-bit float bit patterns as uint16, got {a.dtype}")
     return a
 
 
@@ -106,6 +113,45 @@ def to_bf16(x) -> np.ndarray:
     return out
 
 
+def f16_to_f64(bits) -> np.ndarray:
+    """Exact widening of float16 (IEEE binary16) bit patterns, element by
+    element through the C decoder."""
+    b = _u16(bits)
+    lib = _load()
+    flat = b.reshape(-1)
+    # 65536 patterns at most: decode each distinct one once.
+    uniq, inv = np.unique(flat, return_inverse=True)
+    vals = np.array([lib.nsa_oracle_f16_to_double(int(u)) for u in uniq], dtype=np.float64)
+    return vals[inv].reshape(b.shape)
+
+
+def to_f16(x) -> np.ndarray:
+    """Round float64 values to float16 bit patterns (nearest, ties to even)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().nsa_oracle_round_to_f16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+DTYPES = {"bf16": 0, "f16": 1}
+
+
+def _code(dtype: str) -> int:
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(DTYPES)}, got {dtype!r}")
+    return DTYPES[dtype]
+
+
+def widen(bits, dtype: str = "bf16") -> np.ndarray:
+    """Exact float64 values of bit patterns of element type ``dtype``."""
+    return f16_to_f64(bits) if _code(dtype) == 1 else bf16_to_f64(bits)
+
+
+def round_to(x, dtype: str = "bf16") -> np.ndarray:
+    """Round float64 values to bit patterns of element type ``dtype``."""
+    return to_f16(x) if _code(dtype) == 1 else to_bf16(x)
+
+
 def n_cmp(T: int, l: int, d: int) -> int:
     return int(_load().nsa_oracle_n_cmp(T, l, d))
 
@@ -120,8 +166,9 @@ def sel_prefix(seqlens: Sequence[int], lsel: int) -> np.ndarray:
     return np.cumsum([-(-int(T) // lsel) for T in seqlens]).astype(np.int64)
 
 
-def compress(x_bits, w_bits, act_seq_len, l: int, d: int) -> np.ndarray:
-    """x: [T, N, D] bf16 bits, w: [l, N] bf16 bits -> [T2, N, D] float64."""
+def compress(x_bits, w_bits, act_seq_len, l: int, d: int, dtype: str = "bf16") -> np.ndarray:
+    """x: [T, N, D] bits, w: [l, N] bits, both of element type ``dtype``
+    -> [T2, N, D] float64."""
     x = _u16(x_bits)
     w = _u16(w_bits)
     T, N, D = x.shape
@@ -133,7 +180,8 @@ def compress(x_bits, w_bits, act_seq_len, l: int, d: int) -> np.ndarray:
     starts = np.concatenate([[0], act[:-1]])
     T2 = int(sum(n_cmp(int(e - s), l, d) for s, e in zip(starts, act)))
     out = np.empty((T2, N, D), dtype=np.float64)
-    rc = _load().nsa_oracle_compress(_ptr(x), _ptr(w), _ptr(act), len(act), N, D, l, d, _ptr(out))
+    rc = _load().nsa_oracle_compress(_ptr(x), _ptr(w), _ptr(act), len(act), N, D, l, d,
+                                     _code(dtype), _ptr(out))
     if rc != 0:
         raise ValueError(f"nsa_oracle_compress returned {rc}")
     return out
@@ -141,10 +189,11 @@ def compress(x_bits, w_bits, act_seq_len, l: int, d: int) -> np.ndarray:
 
 def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_kvlen,
               N1: int, N2: int, scale: float, l: int, d: int, lsel: int, count: int,
-              s_stride: Optional[int] = None) -> dict:
+              s_stride: Optional[int] = None, dtype: str = "bf16") -> dict:
     """Steps 1-7 for the listed global tokens.
 
-    q_rows_bits: [n_tok, N1, D1] bf16 bits of those tokens' query rows.
+    q_rows_bits: [n_tok, N1, D1] bits of those tokens' query rows; q, kc and
+    vc are all of element type ``dtype``.
     Returns dict(out [n,N1,D2], max [n,N1], sum [n,N1],
                  pslc [n,N2,s_stride], topk [n,N2,count] int32).
     """
@@ -171,7 +220,7 @@ def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_k
     rc = _load().nsa_oracle_attention(_ptr(q), _ptr(tok), n_tok, _ptr(kc), _ptr(vc),
                                       _ptr(actq), _ptr(actc), len(actq),
                                       N1, N2, D1, D2, float(scale), l, d, lsel, count,
-                                      _ptr(out), _ptr(smax), _ptr(ssum), _ptr(pslc), s_stride,
+                                      _code(dtype), _ptr(out), _ptr(smax), _ptr(ssum), _ptr(pslc), s_stride,
                                       _ptr(topk))
     if rc != 0:
         raise ValueError(f"nsa_oracle_attention returned {rc}")
@@ -179,13 +228,15 @@ def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_k
 
 
 def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None) -> dict:
-    """The whole path for a workload: compress K and V, round them to
-    bfloat16, then steps 1-7 for ``tokens`` (all tokens when None)."""
+    """The whole path for a workload: compress K and V, round them to the
+    workload's element type, then steps 1-7 for ``tokens`` (all tokens when
+    None).  ``kc_bits``/``vc_bits`` are the rounded compressed tensors."""
+    dt = getattr(wl, "dtype", "bf16")
     actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
-    kc = compress(k_bits, w_bits, actq, wl.l, wl.d)
-    vc = compress(v_bits, w_bits, actq, wl.l, wl.d)
-    kc_b = to_bf16(kc)
-    vc_b = to_bf16(vc)
+    kc = compress(k_bits, w_bits, actq, wl.l, wl.d, dt)
+    vc = compress(v_bits, w_bits, actq, wl.l, wl.d, dt)
+    kc_b = round_to(kc, dt)
+    vc_b = round_to(vc, dt)
     if tokens is None:
         tokens = np.arange(wl.T, dtype=np.int64)
         q_rows = q_bits
@@ -193,6 +244,6 @@ def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None) -> dict:
         tokens = np.asarray(tokens, dtype=np.int64)
         q_rows = q_bits[tokens]
     res = attention(q_rows, tokens, kc_b, vc_b, actq, cmp_prefix(wl.seqlens, wl.l, wl.d),
-                    wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count)
-    res.update({"kc": kc, "vc": vc, "kc_bf16": kc_b, "vc_bf16": vc_b, "tokens": tokens})
+                    wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count, dtype=dt)
+    res.update({"kc": kc, "vc": vc, "kc_bits": kc_b, "vc_bits": vc_b, "tokens": tokens})
     return res

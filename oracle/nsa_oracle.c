@@ -22,8 +22,9 @@
  *     the sum of P_slc over the query heads of a KV-head group, the top-k
  *     mask and the top-k indices.
  *
- * Arithmetic is float64 on inputs that are bfloat16 bit patterns widened
- * exactly.  The one decision that floating point turns into integers (which
+ * Arithmetic is float64 on inputs that are bfloat16 or float16 bit patterns
+ * (the two element types the MindSpore page allows for query, key and value)
+ * widened exactly.  The one decision that floating point turns into integers (which
  * blocks the top-k picks) is taken on the importance scores rounded to
  * float32, the precision the GPU kernels take it in.
  *
@@ -97,6 +98,67 @@ void nsa_oracle_round_to_bf16(const double* x, uint16_t* out, int64_t n)
         out[i] = nsa_oracle_double_to_bf16(x[i]);
 }
 
+/* ---- float16 (IEEE 754 binary16) ------------------------------------------ */
+
+/* Widen a binary16 bit pattern from its definition: 1 sign bit, 5 exponent
+ * bits with bias 15, 10 fraction bits.  Exponent field 0 holds zero and the
+ * subnormals f * 2^-24; field 31 holds the infinities and NaNs. */
+double nsa_oracle_f16_to_double(uint16_t h)
+{
+    double sign = (h & 0x8000) ? -1.0 : 1.0;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    if (e == 0)
+        return sign * ldexp((double)f, -24);
+    if (e == 31)
+        return f == 0 ? sign * INFINITY : NAN;
+    return sign * ldexp((double)(1024 + f), e - 25);
+}
+
+/* Round a double to the nearest binary16, ties to even (one rounding step,
+ * straight from double).  binary16 keeps 11 significant bits down to 2^-14
+ * and a fixed spacing of 2^-24 below; anything that rounds above the largest
+ * finite value 65504 becomes infinity. */
+uint16_t nsa_oracle_double_to_f16(double x)
+{
+    if (isnan(x))
+        return 0x7E00;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double ax = fabs(x);
+    if (ax == 0.0)
+        return sign;
+    if (isinf(ax))
+        return (uint16_t)(sign | 0x7C00);
+    int e;
+    frexp(ax, &e);                 /* ax = m * 2^e, m in [0.5, 1) */
+    int qexp = e - 11;             /* spacing of 11 significant bits */
+    if (qexp < -24)
+        qexp = -24;                /* subnormal range */
+    double r = nearbyint(ldexp(ax, -qexp));  /* default mode: nearest, ties even */
+    double y = ldexp(r, qexp);
+    if (y > 65504.0)
+        return (uint16_t)(sign | 0x7C00);
+    if (y < ldexp(1.0, -14))       /* subnormal (or zero): y = r * 2^-24 */
+        return (uint16_t)(sign | (uint16_t)r);
+    int ey;
+    double my = frexp(y, &ey);     /* y = my * 2^ey, my in [0.5, 1) */
+    int field = ey - 1 + 15;       /* y = 1.f * 2^(ey-1) */
+    int frac = (int)(ldexp(my, 11) - 1024.0);
+    return (uint16_t)(sign | (uint16_t)(field << 10) | (uint16_t)frac);
+}
+
+void nsa_oracle_round_to_f16(const double* x, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = nsa_oracle_double_to_f16(x[i]);
+}
+
+/* Element types of q, k, v and the weight: 0 = bfloat16, 1 = float16. */
+static double widen(int dtype, uint16_t h)
+{
+    return dtype == 1 ? nsa_oracle_f16_to_double(h) : nsa_oracle_bf16_to_double(h);
+}
+
 int nsa_oracle_threads(void)
 {
 #ifdef _OPENMP
@@ -122,14 +184,16 @@ static int64_t seq_start(const int64_t* prefix, int64_t b)
     return b == 0 ? 0 : prefix[b - 1];
 }
 
-/* x: [T, N, D] bf16 (TND, sequences back to back, lengths given as prefix
- * sums act_seq_len[B]); w: [l, N] bf16; out: [sum_b n_cmp_b, N, D] double.
+/* x: [T, N, D] (TND, sequences back to back, lengths given as prefix
+ * sums act_seq_len[B]); w: [l, N]; both of element type dtype (0 = bfloat16,
+ * 1 = float16); out: [sum_b n_cmp_b, N, D] double.
  * out[i, h, e] = sum_{p<l} w[p, h] * x[start + i*d + p, h, e]: the 1-based
  * window k_{id+1 : id+l} is rows i*d .. i*d+l-1 counted from 0. */
 int nsa_oracle_compress(const uint16_t* x, const uint16_t* w, const int64_t* act_seq_len,
-                        int64_t B, int64_t N, int64_t D, int64_t l, int64_t d, double* out)
+                        int64_t B, int64_t N, int64_t D, int64_t l, int64_t d, int dtype,
+                        double* out)
 {
-    if (B < 1 || N < 1 || D < 1 || l < 1 || d < 1)
+    if (B < 1 || N < 1 || D < 1 || l < 1 || d < 1 || dtype < 0 || dtype > 1)
         return -1;
     int64_t out_row = 0;
     for (int64_t b = 0; b < B; ++b) {
@@ -143,8 +207,8 @@ int nsa_oracle_compress(const uint16_t* x, const uint16_t* w, const int64_t* act
                 for (int64_t e = 0; e < D; ++e) {
                     double acc = 0.0;
                     for (int64_t p = 0; p < l; ++p) {
-                        double wp = nsa_oracle_bf16_to_double(w[p * N + h]);
-                        double xv = nsa_oracle_bf16_to_double(x[((start + i * d + p) * N + h) * D + e]);
+                        double wp = widen(dtype, w[p * N + h]);
+                        double xv = widen(dtype, x[((start + i * d + p) * N + h) * D + e]);
                         acc += wp * xv;
                     }
                     out[((out_row + i) * N + h) * D + e] = acc;
@@ -176,7 +240,7 @@ static int64_t find_seq(const int64_t* act_seq_qlen, int64_t B, int64_t tg, int6
 static void attend_one_head(const uint16_t* qh, const uint16_t* kc, const uint16_t* vc,
                             int64_t cmp0, int64_t n_cmp, int64_t t, int64_t g,
                             int64_t N2, int64_t D1, int64_t D2, double scale,
-                            int64_t l, int64_t d,
+                            int64_t l, int64_t d, int dtype,
                             double* s, double* P, double* out_h, double* m_out, double* L_out)
 {
     /* step 1: QK = scale * query . key^T, then the attention mask. */
@@ -191,7 +255,7 @@ static void attend_one_head(const uint16_t* qh, const uint16_t* kc, const uint16
         const uint16_t* ki = kc + ((cmp0 + i) * N2 + g) * D1;
         double dot = 0.0;
         for (int64_t e = 0; e < D1; ++e)
-            dot += nsa_oracle_bf16_to_double(qh[e]) * nsa_oracle_bf16_to_double(ki[e]);
+            dot += widen(dtype, qh[e]) * widen(dtype, ki[e]);
         s[i] = scale * dot;
         if (!any || s[i] > m)
             m = s[i];
@@ -207,7 +271,7 @@ static void attend_one_head(const uint16_t* qh, const uint16_t* kc, const uint16
     for (int64_t e = 0; e < D2; ++e) {
         double acc = 0.0;
         for (int64_t i = 0; i < n_cmp; ++i) {
-            acc += P[i] * nsa_oracle_bf16_to_double(vc[((cmp0 + i) * N2 + g) * D2 + e]);
+            acc += P[i] * widen(dtype, vc[((cmp0 + i) * N2 + g) * D2 + e]);
         }
         out_h[e] = acc;
     }
@@ -262,9 +326,10 @@ static void topk_one_group(const double* Pslc_g, int64_t S_sel, int64_t t, int64
 /*
  * Compressed attention, importance scores and top-k for the listed tokens.
  *
- * q_rows   : [n_tok, N1, D1] bf16, the query rows of the listed tokens
+ * q_rows   : [n_tok, N1, D1], the query rows of the listed tokens
  * tokens   : [n_tok] global token indices into the TND query tensor
- * kc, vc   : [T2, N2, D1] and [T2, N2, D2] bf16 compressed keys / values
+ * kc, vc   : [T2, N2, D1] and [T2, N2, D2] compressed keys / values
+ * dtype    : element type of q_rows, kc and vc: 0 = bfloat16, 1 = float16
  * act_seq_qlen, act_cmp_seq_kvlen : [B] prefix sums of the query and the
  *            compressed lengths of each sequence
  * out      : [n_tok, N1, D2]; smax, ssum: [n_tok, N1]
@@ -277,11 +342,12 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
                          const uint16_t* kc, const uint16_t* vc,
                          const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen, int64_t B,
                          int64_t N1, int64_t N2, int64_t D1, int64_t D2, double scale,
-                         int64_t l, int64_t d, int64_t lsel, int64_t count,
+                         int64_t l, int64_t d, int64_t lsel, int64_t count, int dtype,
                          double* out, double* smax, double* ssum,
                          double* pslc, int64_t s_stride, int32_t* topk)
 {
-    if (N2 < 1 || N1 % N2 != 0 || d < 1 || lsel % d != 0 || count < 1 || B < 1)
+    if (N2 < 1 || N1 % N2 != 0 || d < 1 || lsel % d != 0 || count < 1 || B < 1 ||
+        dtype < 0 || dtype > 1)
         return -1;
     const int64_t G = N1 / N2;
     const int64_t R = lsel / d;
@@ -326,7 +392,7 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
                 for (int64_t h = 0; h < N1; ++h) {
                     int64_t g = h / G;
                     attend_one_head(q_rows + (k * N1 + h) * D1, kc, vc, cmp0, n_cmp, t, g,
-                                    N2, D1, D2, scale, l, d, s, P,
+                                    N2, D1, D2, scale, l, d, dtype, s, P,
                                     out + (k * N1 + h) * D2,
                                     smax + k * N1 + h, ssum + k * N1 + h);
                     /* step 4, then step 5: heads of a group summed in order. */

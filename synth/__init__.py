@@ -8,8 +8,8 @@ consume what it produces, so it is the one piece of code they share.
 Recipe (the same for every workload):
 
 * q, k and v are drawn as float32 normals with a workload-specific standard
-  deviation, then rounded to bfloat16 with round-to-nearest-even (torch's
-  float32 -> bfloat16 conversion).
+  deviation, then rounded to the workload's element type (bfloat16 or
+  float16) with round-to-nearest-even (torch's float32 conversion).
 * the compression weight ``w[l, N2]`` is drawn as float32 U(0, w_hi) and
   rounded the same way.
 * each tensor has its own ``torch.Generator`` seeded from (workload seed,
@@ -28,6 +28,7 @@ import numpy as np
 import torch
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "w": 3}
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,6 +50,7 @@ class Workload:
     kv_std: float = 1.0
     w_hi: float = 1.0 / 16  # weight ~ U(0, w_hi)
     seed: int = 0
+    dtype: str = "bf16"     # element type of q, k, v and the weight: "bf16" or "f16"
 
     @property
     def B(self) -> int:
@@ -67,10 +69,22 @@ class Workload:
         return dataclasses.replace(self, seqlens=tuple(int(s) for s in seqlens),
                                    name=name or f"{self.name}-lens{list(seqlens)}")
 
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return TORCH_DTYPES[self.dtype]
+
+    def with_dtype(self, dtype: str) -> "Workload":
+        if dtype not in TORCH_DTYPES:
+            raise ValueError(f"dtype must be one of {sorted(TORCH_DTYPES)}, got {dtype!r}")
+        if dtype == self.dtype:
+            return self
+        return dataclasses.replace(self, dtype=dtype, name=f"{self.name}-{dtype}")
+
     def describe(self) -> dict:
         return {"workload": self.name, "B": self.B, "T": self.T, "N1": self.N1,
                 "N2": self.N2, "D1": self.D1, "D2": self.D2, "l": self.l, "d": self.d,
-                "lsel": self.lsel, "count": self.count, "scale": self.scale}
+                "lsel": self.lsel, "count": self.count, "scale": self.scale,
+                "dtype": self.dtype}
 
 
 def _batched_lens_16() -> tuple:
@@ -107,11 +121,12 @@ def _seed(wl: Workload, tensor: str) -> int:
     return (wl.seed * 1_000_003 + TENSOR_IDS[tensor] * 7919) & 0x7FFF_FFFF_FFFF
 
 
-def _draw(shape, seed: int, device, kind: str, a: float, chunk_rows: int) -> torch.Tensor:
-    """Draw ``shape`` values in row chunks, round each chunk to bfloat16."""
+def _draw(shape, seed: int, device, kind: str, a: float, chunk_rows: int,
+          dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """Draw ``shape`` values in row chunks, round each chunk to ``dtype``."""
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    out = torch.empty(shape, dtype=dtype, device=device)
     rows = shape[0]
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
@@ -123,24 +138,30 @@ def _draw(shape, seed: int, device, kind: str, a: float, chunk_rows: int) -> tor
         else:  # uniform on [0, a)
             x = torch.rand(sub, generator=gen, device=device, dtype=torch.float32)
             x.mul_(a)
-        out[r0:r1] = x.to(torch.bfloat16)
+        out[r0:r1] = x.to(dtype)
         del x
     return out
 
 
 def make_inputs(wl: Workload, device="cpu", chunk_rows: int = 8192,
                 tensors=("q", "k", "v", "w")) -> dict:
-    """bf16 tensors q [T,N1,D1], k [T,N2,D1], v [T,N2,D2] and w [l,N2]."""
+    """Tensors q [T,N1,D1], k [T,N2,D1], v [T,N2,D2] and w [l,N2] of the
+    workload's element type."""
     T = wl.T
+    dt = wl.torch_dtype
     out = {}
     if "q" in tensors:
-        out["q"] = _draw((T, wl.N1, wl.D1), _seed(wl, "q"), device, "normal", wl.q_std, chunk_rows)
+        out["q"] = _draw((T, wl.N1, wl.D1), _seed(wl, "q"), device, "normal", wl.q_std,
+                         chunk_rows, dt)
     if "k" in tensors:
-        out["k"] = _draw((T, wl.N2, wl.D1), _seed(wl, "k"), device, "normal", wl.kv_std, chunk_rows)
+        out["k"] = _draw((T, wl.N2, wl.D1), _seed(wl, "k"), device, "normal", wl.kv_std,
+                         chunk_rows, dt)
     if "v" in tensors:
-        out["v"] = _draw((T, wl.N2, wl.D2), _seed(wl, "v"), device, "normal", wl.kv_std, chunk_rows)
+        out["v"] = _draw((T, wl.N2, wl.D2), _seed(wl, "v"), device, "normal", wl.kv_std,
+                         chunk_rows, dt)
     if "w" in tensors:
-        out["w"] = _draw((wl.l, wl.N2), _seed(wl, "w"), device, "uniform", wl.w_hi, chunk_rows)
+        out["w"] = _draw((wl.l, wl.N2), _seed(wl, "w"), device, "uniform", wl.w_hi,
+                         chunk_rows, dt)
     return out
 
 
@@ -152,6 +173,18 @@ def bf16_bits(t: torch.Tensor) -> np.ndarray:
 
 def from_bf16_bits(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """The raw bit patterns of a bfloat16 or float16 tensor as uint16."""
+    assert t.dtype in (torch.bfloat16, torch.float16)
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def from_bits(a: np.ndarray, dtype: str = "bf16") -> torch.Tensor:
+    """A CPU tensor of element type ``dtype`` holding the bit patterns ``a``."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).view(
+        TORCH_DTYPES[dtype])
 
 
 def sample_tokens(wl: Workload, per_seq: int, rng_seed: int = 7) -> np.ndarray:

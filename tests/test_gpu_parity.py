@@ -59,7 +59,7 @@ def _run_small(wl, end_to_end=True):
     assert_close_out(bf16_to_f64(kc_g), ref["kc"], "compressed K")
     assert_close_out(bf16_to_f64(vc_g), ref["vc"], "compressed V")
     log(f"[case] {wl.name}: GPU attention on the oracle's compressed K/V")
-    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bf16"]), upload_bits(ref["vc_bf16"]))
+    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bits"]), upload_bits(ref["vc_bits"]))
     _check_all(wl, g, ref, ref["tokens"])
     if end_to_end:
         log(f"[case] {wl.name}: GPU attention on its own compressed K/V")
@@ -148,7 +148,7 @@ def test_topk_exact_ties():
     log(f"[case] {wl.name}: oracle")
     ref = oracle.run(wl, bits["q"], bits["k"], bits["v"], bits["w"])
     log(f"[case] {wl.name}: GPU attention on the oracle's compressed K/V")
-    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bf16"]), upload_bits(ref["vc_bf16"]))
+    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bits"]), upload_bits(ref["vc_bits"]))
     _check_all(wl, g, ref, ref["tokens"])
     gi, ri = g["topk"].cpu().numpy(), ref["topk"]
     long_rows = 0

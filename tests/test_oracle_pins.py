@@ -36,6 +36,21 @@ def rand_bf16(rng, shape, std=1.0) -> np.ndarray:
     return synth.bf16_bits(x)
 
 
+def rand_f16(rng, shape, std=1.0) -> np.ndarray:
+    """float16 bit patterns of normals, rounded by numpy."""
+    return (rng.standard_normal(shape) * std).astype(np.float16).view(np.uint16)
+
+
+def rand_bits(rng, shape, dtype, std=1.0) -> np.ndarray:
+    return rand_f16(rng, shape, std) if dtype == "f16" else rand_bf16(rng, shape, std)
+
+
+def widen_torch(b, dtype) -> torch.Tensor:
+    """float64 values of bit patterns, widened by torch (not by the oracle)."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(tdt).to(torch.float64)
+
+
 def starts_of(lens):
     return np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
 
@@ -88,6 +103,86 @@ def test_bf16_rounding_matches_torch_on_float32_inputs():
 ])
 def test_bf16_rounding_special_values(x, expect):
     assert int(oracle.to_bf16(np.array([x]))[0]) == expect
+
+
+def test_bf16_decode_all_patterns_match_torch():
+    """Every finite bfloat16 pattern widens to torch's value (C decoder)."""
+    allb = np.arange(65536, dtype=np.uint16)
+    ref = widen_torch(allb, "bf16").numpy()
+    lib = oracle._load()
+    got = np.array([lib.nsa_oracle_bf16_to_double(int(h)) for h in allb])
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+
+
+# --------------------------------------------------------------------------
+# float16 (IEEE binary16) widening and rounding
+# --------------------------------------------------------------------------
+
+def test_f16_decode_all_patterns_match_numpy():
+    """All 65536 binary16 patterns widen to numpy's float16 values, infinities
+    and signed zeros included; NaN patterns decode to NaN."""
+    allb = np.arange(65536, dtype=np.uint16)
+    ref = allb.view(np.float16).astype(np.float64)
+    got = oracle.f16_to_f64(allb)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_f16_rounding_matches_numpy_on_float64_inputs():
+    """Doubles across the whole binary16 range, its subnormals, exact ties
+    and the overflow edge round as numpy's double -> half conversion does
+    (round to nearest, ties to even, in one step)."""
+    rng = np.random.default_rng(10)
+    mant = rng.standard_normal(200_000)
+    expo = rng.integers(-28, 18, 200_000)
+    x = mant * np.exp2(expo)
+    # exact ties: halfway between neighbouring half values (normal and subnormal)
+    h = rng.integers(0, 0x7BFF, 50_000, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    ties = (lo + hi) / 2
+    x = np.concatenate([x, ties, -ties, [65504.0, 65519.99, 65520.0, 2.0 ** -25, 2.0 ** -26]])
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = oracle.to_f16(x)
+    assert np.array_equal(got, ref)
+
+
+def test_f16_rounding_matches_torch_on_float32_inputs():
+    """For float32 inputs, one rounding step from double equals torch's
+    float32 -> float16 conversion."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(100_000) * np.exp2(rng.integers(-27, 17, 100_000))).astype(np.float32)
+    ref = synth.bits(torch.from_numpy(x).to(torch.float16))
+    got = oracle.to_f16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("x,expect", [
+    (1.0, 0x3C00), (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+    (1 + 2 ** -11, 0x3C00),           # tie -> even (down)
+    (1 + 3 * 2 ** -11, 0x3C02),       # tie -> even (up)
+    (1 + 2 ** -11 + 2 ** -40, 0x3C01),  # just above a tie: up, in one step
+    (2.0 ** -24, 0x0001),             # smallest subnormal
+    (2.0 ** -25, 0x0000),             # tie between 0 and it -> 0
+    (3 * 2.0 ** -25, 0x0002),         # tie between 1 and 2 subnormal steps -> 2
+    (2.0 ** -14, 0x0400),             # smallest normal
+    (2.0 ** -14 - 2.0 ** -25, 0x0400),  # tie between the largest subnormal and it -> even
+    (65504.0, 0x7BFF),                # largest finite
+    (65519.0, 0x7BFF),                # below the halfway point: stays finite
+    (65520.0, 0x7C00),                # halfway to 2^16: ties to even -> inf
+    (float("inf"), 0x7C00), (float("-inf"), 0xFC00),
+])
+def test_f16_rounding_special_values(x, expect):
+    assert int(oracle.to_f16(np.array([x]))[0]) == expect
+
+
+def test_f16_rounding_nan():
+    assert np.isnan(oracle.f16_to_f64(oracle.to_f16(np.array([float("nan")])))[0])
 
 
 # --------------------------------------------------------------------------
@@ -166,6 +261,27 @@ def test_compress_constant_rows():
     np.testing.assert_allclose(got, np.broadcast_to(expect, got.shape), rtol=1e-13)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_compress_matches_numpy_weighted_windows(dtype):
+    """Per element type: every output row is the numpy weighted sum of its
+    window, on inputs widened by torch -- pins that the element type picks
+    the matching decoder for both x and w."""
+    rng = np.random.default_rng(12)
+    l, d, N, D = 32, 16, 2, 8
+    lens = [140, 33, 70]
+    x = rand_bits(rng, (sum(lens), N, D), dtype)
+    w = rand_bits(rng, (l, N), dtype, std=0.1)
+    got = oracle.compress(x, w, np.cumsum(lens), l, d, dtype)
+    xf, wf = widen_torch(x, dtype).numpy(), widen_torch(w, dtype).numpy()
+    ref = []
+    for s0, T in zip(starts_of(lens), lens):
+        for i in range(oracle.n_cmp(T, l, d)):
+            win = xf[s0 + i * d:s0 + i * d + l]                 # [l, N, D]
+            ref.append(np.einsum("pn,pnd->nd", wf, win))
+    ref = np.stack(ref)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
 def test_compress_is_linear():
     """compress(2x + y) = 2 compress(x) + compress(y) on small integers (exact)."""
     rng = np.random.default_rng(4)
@@ -183,26 +299,32 @@ def test_compress_is_linear():
 # Steps 1-3: scaled scores, mask, softmax, output
 # --------------------------------------------------------------------------
 
-def _attention_case(seed, lens, N1, N2, D1, D2, l, d, kv_std=1.0):
+def _attention_case(seed, lens, N1, N2, D1, D2, l, d, kv_std=1.0, dtype="bf16"):
     rng = np.random.default_rng(seed)
     T = sum(lens)
     T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
-    q = rand_bf16(rng, (T, N1, D1))
-    kc = rand_bf16(rng, (T2, N2, D1), kv_std)
-    vc = rand_bf16(rng, (T2, N2, D2), kv_std)
+    q = rand_bits(rng, (T, N1, D1), dtype)
+    kc = rand_bits(rng, (T2, N2, D1), dtype, kv_std)
+    vc = rand_bits(rng, (T2, N2, D2), dtype, kv_std)
     return q, kc, vc
 
 
-def test_attention_matches_torch_sdpa():
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_attention_matches_torch_sdpa(dtype):
     """Rows with at least one visible block equal torch's scaled dot-product
     attention (float64, boolean mask built from the visibility rule);
-    softmax max and sum equal torch's masked max and exp(logsumexp - max)."""
+    softmax max and sum equal torch's masked max and exp(logsumexp - max).
+    Inputs are widened by torch for the reference, so the element type must
+    reach every decode in the oracle."""
     lens = [40, 77, 130, 31]
     N1, N2, D1, D2, l, d, lsel, count = 6, 2, 16, 8, 32, 16, 64, 2
     scale = 0.3
-    q, kc, vc = _attention_case(5, lens, N1, N2, D1, D2, l, d)
-    res = run_all(q, kc, vc, lens, N1, N2, scale, l, d, lsel, count)
-    qf, kf, vf = (torch.from_numpy(oracle.bf16_to_f64(a)) for a in (q, kc, vc))
+    q, kc, vc = _attention_case(5, lens, N1, N2, D1, D2, l, d, dtype=dtype)
+    actq = np.cumsum(lens).astype(np.int64)
+    res = oracle.attention(q, np.arange(int(sum(lens)), dtype=np.int64), kc, vc, actq,
+                           oracle.cmp_prefix(lens, l, d), N1, N2, scale, l, d, lsel, count,
+                           dtype=dtype)
+    qf, kf, vf = (widen_torch(a, dtype) for a in (q, kc, vc))
     actc = oracle.cmp_prefix(lens, l, d)
     cstarts = np.concatenate([[0], actc[:-1]])
     G = N1 // N2

@@ -11,10 +11,11 @@ same timed region.
 
 Prints one JSON line.  ``value`` is query tokens per second of the whole
 step; the roofline object is for the dominant kernel (the attention
-kernel, bound by bf16 MFMA); ``cpu_baseline`` times the CPU oracle on a
-bounded random sample of the same workload's tokens.
+kernel, bound by MFMA of the element type); ``cpu_baseline`` times the CPU
+oracle on a bounded random sample of the same workload's tokens.
 
-    python bench.py [--steps K] [--warmup W] [--workload 0..4] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 0..4] [--dtype bf16|f16]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ if ROOT not in sys.path:
 
 METRIC = "query tokens/sec (compress+attn+topk); TFLOP/s as % of MI355X bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # dense MFMA peak per element type
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 # HBM bytes of the attention kernel per launch, from rocprofv3 FETCH_SIZE and
@@ -94,21 +96,22 @@ def cpu_baseline(wl, inp, budget_s: float) -> dict:
     whole workload's token count."""
     import oracle
     import synth
-    kb, vb, wb = synth.bf16_bits(inp["k"]), synth.bf16_bits(inp["v"]), synth.bf16_bits(inp["w"])
+    dt = wl.dtype
+    kb, vb, wb = synth.bits(inp["k"]), synth.bits(inp["v"]), synth.bits(inp["w"])
     actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
     t0 = time.perf_counter()
-    kc = oracle.to_bf16(oracle.compress(kb, wb, actq, wl.l, wl.d))
-    vc = oracle.to_bf16(oracle.compress(vb, wb, actq, wl.l, wl.d))
+    kc = oracle.round_to(oracle.compress(kb, wb, actq, wl.l, wl.d, dt), dt)
+    vc = oracle.round_to(oracle.compress(vb, wb, actq, wl.l, wl.d, dt), dt)
     t_comp = time.perf_counter() - t0
     actc = oracle.cmp_prefix(wl.seqlens, wl.l, wl.d)
     rng = np.random.default_rng(1234)
     import torch
 
     def attn(tokens):
-        q_rows = synth.bf16_bits(inp["q"][torch.from_numpy(tokens).to(inp["q"].device)])
+        q_rows = synth.bits(inp["q"][torch.from_numpy(tokens).to(inp["q"].device)])
         t = time.perf_counter()
         oracle.attention(q_rows, tokens, kc, vc, actq, actc, wl.N1, wl.N2, wl.scale, wl.l, wl.d,
-                         wl.lsel, wl.count)
+                         wl.lsel, wl.count, dtype=dt)
         return time.perf_counter() - t
 
     pilot = np.sort(rng.choice(wl.T, min(wl.T, 32), replace=False)).astype(np.int64)
@@ -129,6 +132,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=4, choices=range(5))
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="element type of q, k, v and the weight (default bf16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -167,7 +172,7 @@ def main() -> int:
                           "write_bytes": args.copy_bytes, "ms": ms,
                           "GB/s": 2 * args.copy_bytes / (ms / 1e3) / 1e9}), flush=True)
         return 0
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[args.workload].with_dtype(args.dtype)
     print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(wl, device=dev, chunk_rows=16384)
     c_pre, s_pre, pc, ps = [], [], 0, 0
@@ -178,10 +183,11 @@ def main() -> int:
         s_pre.append(ps)
     T2 = pc
     plan = nsa.nsa_compress_attention_get_workspace(wl.act_seq_qlen, c_pre, s_pre, wl.N1, wl.N2, wl.D1,
-                                                    wl.D2, wl.scale, wl.l, wl.d, wl.lsel, wl.count)
-    kc = torch.empty((T2, wl.N2, wl.D1), dtype=torch.bfloat16, device=dev)
-    vc = torch.empty((T2, wl.N2, wl.D2), dtype=torch.bfloat16, device=dev)
-    outs = {"attention_out": torch.empty((wl.T, wl.N1, wl.D2), dtype=torch.bfloat16, device=dev),
+                                                    wl.D2, wl.scale, wl.l, wl.d, wl.lsel, wl.count,
+                                                    wl.torch_dtype)
+    kc = torch.empty((T2, wl.N2, wl.D1), dtype=wl.torch_dtype, device=dev)
+    vc = torch.empty((T2, wl.N2, wl.D2), dtype=wl.torch_dtype, device=dev)
+    outs = {"attention_out": torch.empty((wl.T, wl.N1, wl.D2), dtype=wl.torch_dtype, device=dev),
             "topk_indices": torch.empty((wl.T, wl.N2, wl.count), dtype=torch.int32, device=dev),
             "softmax_max": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev),
             "softmax_sum": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev)}
@@ -226,10 +232,11 @@ def main() -> int:
     total_flops = work["attn_flops"] + work["compress_flops"]
     attn_s = per["attention"] / 1e3
     attn_tflops = work["attn_flops"] / attn_s / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
     kernels = {
         "compress_k": {"ms": per["compress_k"], "GB/s": work["bytes_compress_k"] / (per["compress_k"] / 1e3) / 1e9},
         "compress_v": {"ms": per["compress_v"], "GB/s": work["bytes_compress_v"] / (per["compress_v"] / 1e3) / 1e9},
-        "attention": {"ms": per["attention"], "TFLOP/s": attn_tflops, "mfma_frac": attn_tflops / PEAK_BF16_TFLOPS},
+        "attention": {"ms": per["attention"], "TFLOP/s": attn_tflops, "mfma_frac": attn_tflops / peak},
         "select_topk": {"ms": per["select_topk"],
                         "GB/s": work["bytes_select"] / (per["select_topk"] / 1e3) / 1e9},
     }
@@ -244,15 +251,15 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wl.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "N1": wl.N1, "N2": wl.N2, "D1": wl.D1,
                    "D2": wl.D2, "l": wl.l, "d": wl.d, "lsel": wl.lsel, "count": wl.count,
-                   "scale": wl.scale, "parallelism": "single-gpu"},
+                   "scale": wl.scale, "dtype": wl.dtype, "parallelism": "single-gpu"},
         "tflops_algorithmic": total_flops / (ms_step / 1e3) / 1e12,
         "frac_of_bf16_peak": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"kernel": "k_cmp_attn_fwd", "bound": "mfma", "achieved": attn_tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak,
                      "traffic": measured_traffic(wl.name),
                      "traffic_unit": "HBM bytes per launch",
                      "work_per_launch": f"{work['attn_flops']:.4e} flop = 2*(D1+D2) x {work['visible_pairs']} "

@@ -52,9 +52,12 @@ typedef enum nsa_status {
     NSA_ERR_HIP = 7           /* the HIP runtime refused a copy or a launch */
 } nsa_status;
 
-/* Element types of q/k/v and of the outputs that carry them.  Both pages
- * allow float16 and bfloat16; this build computes bfloat16 and answers
- * NSA_ERR_UNSUPPORTED for float16. */
+/* Element types of q/k/v, of the compression input and weight, and of the
+ * outputs that carry them (compressed K/V, attention_out).  The MindSpore
+ * page ("mindspore.ops.nsa_compress_attention", Parameters) allows float16
+ * and bfloat16 for query, key and value; both are built.  Products run on
+ * the 32x32x16 MFMA of that type with float32 accumulation; float32 results
+ * are rounded to it once, to nearest even. */
 typedef enum nsa_dtype {
     NSA_DTYPE_BF16 = 0,
     NSA_DTYPE_FP16 = 1
@@ -95,9 +98,9 @@ int64_t nsa_compress_out_len(int64_t seq_len, int64_t compress_block_size,
  * compress_block_size (l) a multiple of 16 in [16, 128]; compress_stride (d)
  * a multiple of 16 with 16 <= d <= l; head_dim a multiple of 16, <= 256;
  * num_heads >= 1.
- * Errors: NSA_ERR_NULLPTR, NSA_ERR_DTYPE, NSA_ERR_SHAPE (prefix sums or
- * output_tokens inconsistent), NSA_ERR_CONSTRAINT, NSA_ERR_UNSUPPORTED
- * (float16), NSA_ERR_HIP.
+ * Errors: NSA_ERR_NULLPTR, NSA_ERR_DTYPE (unknown dtype code), NSA_ERR_SHAPE
+ * (prefix sums or output_tokens inconsistent), NSA_ERR_CONSTRAINT,
+ * NSA_ERR_HIP.
  */
 nsa_status nsa_compress(const void* input, const void* weight,
                         const int64_t* act_seq_len, int64_t batch,
@@ -125,12 +128,13 @@ nsa_status nsa_compress(const void* input, const void* weight,
  *   compress_stride       d: multiple of 16 in [16, 64], d <= l
  *   select_block_size     l': multiple of 16 in [16, 128], l' >= l, l' % d == 0
  *   select_block_count    k: in [1, 32]
- *   dtype                 element type of q/k/v/out
+ *   dtype                 element type of q/k/v/out; the second phase must
+ *                         be given tensors of this type
  *   workspace_bytes       out: bytes of device workspace the second phase needs
  *   plan_out              out: the plan (caller frees it)
  *
- * Errors: NSA_ERR_NULLPTR, NSA_ERR_DTYPE, NSA_ERR_SHAPE, NSA_ERR_CONSTRAINT,
- * NSA_ERR_UNSUPPORTED (float16; head dims outside {64,128,192} x {64,128};
+ * Errors: NSA_ERR_NULLPTR, NSA_ERR_DTYPE (unknown dtype code), NSA_ERR_SHAPE,
+ * NSA_ERR_CONSTRAINT, NSA_ERR_UNSUPPORTED (head dims outside {64,128,192} x {64,128};
  * N1/N2 > 64; more than 1024 select blocks in one sequence).  On error
  * *plan_out is set to NULL.
  */
@@ -216,6 +220,7 @@ typedef struct nsa_plan_info {
     int64_t max_sel_blocks;     /* S of p_slc_debug */
     int64_t head_num, kv_head_num, d1, d2, select_block_count;
     size_t workspace_bytes;
+    int64_t dtype;              /* the nsa_dtype the plan was made for */
 } nsa_plan_info;
 
 nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info);

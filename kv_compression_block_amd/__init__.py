@@ -183,6 +183,9 @@ def _check_qkv(plan: Plan, query, key, value=None):
         raise ValueError(f"key must be {(T2, N2, D1)}, got {tuple(key.shape)}")
     if query.dtype != key.dtype:
         raise TypeError("query and key must share a dtype")
+    if _dtype_code(query.dtype) != info["dtype"]:
+        raise TypeError(f"the plan was made for dtype code {info['dtype']}, "
+                        f"query is {query.dtype}")
     if value is not None:
         _need_tensor(value, "value")
         if tuple(value.shape) != (T2, N2, info["d2"]):

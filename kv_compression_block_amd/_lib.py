@@ -51,6 +51,7 @@ class PlanInfo(ctypes.Structure):
         ("d2", ctypes.c_int64),
         ("select_block_count", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
+        ("dtype", ctypes.c_int64),
     ]
 
 

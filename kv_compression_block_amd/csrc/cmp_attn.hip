@@ -3,7 +3,8 @@
 // over compressed blocks, softmax and P.V -- fused, plus the softmax max and
 // sum outputs.
 //
-// Design (gfx950, bf16 MFMA 32x32x16, fp32 accumulate):
+// Design (gfx950, bf16 or f16 MFMA 32x32x16, fp32 accumulate; the element
+// type E is a template parameter and only changes the MFMA and the packing):
 //   * A workgroup is 4 waves; a wave owns QB blocks of 32 query rows of one
 //     (sequence, KV head).  A row is (token, query head of the group): the
 //     group's heads of a token are adjacent rows, so they share every K/V
@@ -39,7 +40,7 @@ template <int D1, int D2, int QB, int KT, int W>
 struct AttnCfg {
     static constexpr int NT = 64 * W;          // threads per workgroup (W waves)
     static constexpr int ROWS = W * 32 * QB;   // query rows per workgroup
-    static constexpr int KS = D1 + 8;          // LDS row stride of K (bf16): 16 B pad
+    static constexpr int KS = D1 + 8;          // LDS row stride of K (elements): 16 B pad
     static constexpr int NKB = KT / 32;        // 32-entry blocks per tile
     static constexpr int NKS = D1 / 16;        // k-steps of QK^T
     static constexpr int NDB = D2 / 32;        // 32-row blocks of O^T
@@ -52,7 +53,7 @@ struct AttnCfg {
     static constexpr int KSLOT = KT * (KCH + 1);
     static constexpr int KINS = (KSLOT + 63) / 64;   // wave instructions per K tile
     static constexpr int KIPW = (KINS + W - 1) / W;  // ... per wave
-    static constexpr int KBUF = KINS * 64 * 8;       // bf16 per K buffer (with slack)
+    static constexpr int KBUF = KINS * 64 * 8;       // elements per K buffer (with slack)
     static constexpr int VINS = KT * VCH / 64;       // wave instructions per V tile
     static constexpr int VIPW = VINS / W;
     static_assert(KT % 32 == 0 && (KT * VCH) % (64 * W) == 0, "V tile copy");
@@ -87,7 +88,7 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
 // At least three waves per SIMD for D1 = D2 = 128 (168 registers, a few
 // values spilled around the main loop), which the unrolled loop would
 // otherwise exceed; two elsewhere.
-template <int D1, int D2, int QB, int KT, int W>
+template <typename E, int D1, int D2, int QB, int KT, int W>
 __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cmp_attn_fwd(AttnParams p)
 {
     using C = AttnCfg<D1, D2, QB, KT, W>;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     int nvq[QB];
     bool vq[QB];
     int64_t grow[QB];
-    bf16x8 qf[QB][C::NKS];
+    u32x4 qf[QB][C::NKS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int r = row_wg + (wave * QB + qb) * 32 + l32;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         for (int ks = 0; ks < C::NKS; ++ks) {
             u32x4 v = *(const u32x4*)(qrow + ks * 16);
             v ^= p.qsign;
-            qf[qb][ks] = as_bf16x8(v);
+            qf[qb][ks] = v;
         }
     }
     const int last_row = min(row_wg + C::ROWS, rows_total) - 1;
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     }
     const float c = p.c;
     f32x16 scur[QB][C::NKB], snxt[QB][C::NKB];
-    u32x4 pfr[QB][2 * C::NKB];   // P of the current tile, bf16 B operands of P.V
+    u32x4 pfr[QB][2 * C::NKB];   // P of the current tile, packed B operands of P.V
 
     // S^T = K Q^T for tile kt (K in LDS buffer kt & 1) into snxt.
     auto qk = [&](const uint16_t* kbuf) __attribute__((always_inline)) {
@@ -255,10 +256,10 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         for (int ks = 0; ks < C::NKS; ++ks) {
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
-                const bf16x8 ka = as_bf16x8(*(const u32x4*)&kbuf[(kb * 32 + l32) * C::KS + ks * 16 + hf * 8]);
+                const u32x4 ka = *(const u32x4*)&kbuf[(kb * 32 + l32) * C::KS + ks * 16 + hf * 8];
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    s[qb][kb] = mfma32(ka, qf[qb][ks], s[qb][kb]);
+                    s[qb][kb] = E::mfma(ka, qf[qb][ks], s[qb][kb]);
             }
         }
     };
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
             nbias[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c;
     };
     // P = exp2(S*c - mref*c) of the current tile, the running sum, and P
-    // packed to bf16 in the order the P.V MFMAs consume it.  Masked scores
+    // packed to the element type in the order the P.V MFMAs consume it.  Masked scores
     // are -inf and c > 0, so their exponentials are exactly 0.
     auto softmax_exp = [&](auto mask_tag) __attribute__((always_inline)) {
         (void)mask_tag;
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                 const int r0 = (kk & 1) * 8;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    pfr[qb][kk][j] = pack_bf16x2(s[qb][kb][r0 + 2 * j], s[qb][kb][r0 + 2 * j + 1]);
+                    pfr[qb][kk][j] = E::pack2(s[qb][kb][r0 + 2 * j], s[qb][kb][r0 + 2 * j + 1]);
             }
         }
     };
@@ -363,10 +364,10 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                 const uint16_t* vb = &vbuf[voff_lane[db] + kk * 16 * D2];
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vb);
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vb + 8 * D2));
-                const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const u32x4 va = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    o[qb][db] = mfma32(va, as_bf16x8(pfr[qb][kk]), o[qb][db]);
+                    o[qb][db] = E::mfma(va, pfr[qb][kk], o[qb][db]);
             }
         }
     };
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     // in a private part of them, half of D2 per pass.
     __syncthreads();
     constexpr int HD = D2 / 2;                 // dims per pass
-    constexpr int OPITCH = HD + 8;             // staging row pitch (bf16), 16 B pad
+    constexpr int OPITCH = HD + 8;             // staging row pitch (elements), 16 B pad
     constexpr int CPR = HD / 8;                // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;              // staged rows per read instruction
     constexpr int WPS = C::KBUF / (32 * OPITCH);   // waves staged per K slot
@@ -489,8 +490,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int dv = (db - h * C::NDB / 2) * 32 + 8 * r4 + 4 * hf;
-                    u32x2 w2 = {pack_bf16x2(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv),
-                                pack_bf16x2(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv)};
+                    u32x2 w2 = {E::pack2(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv),
+                                E::pack2(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv)};
                     *(u32x2*)&ostg[l32 * OPITCH + dv] = w2;
                 }
             }
@@ -547,17 +548,28 @@ int cmp_attn_rows_per_wg(int d1, int d2)
     return 0;
 }
 
-hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream)
+template <typename E>
+static hipError_t launch_typed(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream)
 {
-    if (n_tiles <= 0)
-        return hipSuccess;
 #define X(a, b, q, k, w)                                                                          \
     if (d1 == a && d2 == b) {                                                                  \
-        hipLaunchKernelGGL((k_cmp_attn_fwd<a, b, q, k, w>), dim3(n_tiles), dim3(64 * w), 0, stream, p); \
+        hipLaunchKernelGGL((k_cmp_attn_fwd<E, a, b, q, k, w>), dim3(n_tiles), dim3(64 * w), 0, stream, p); \
         return hipGetLastError();                                                              \
     }
     NSA_ATTN_CONFIGS(X)
 #undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cmp_attn(int dtype, int d1, int d2, const AttnParams& p, int n_tiles,
+                           hipStream_t stream)
+{
+    if (n_tiles <= 0)
+        return hipSuccess;
+    if (dtype == ElemBf16::code)
+        return launch_typed<ElemBf16>(d1, d2, p, n_tiles, stream);
+    if (dtype == ElemF16::code)
+        return launch_typed<ElemF16>(d1, d2, p, n_tiles, stream);
     return hipErrorInvalidValue;
 }
 

@@ -1,7 +1,8 @@
 // Kernel (a): NSA compression ("aclnnNsaCompress", Formula).
 //
 // y[i, n, :] = sum_{p < l} w[p, n] * x[start + i*d + p, n, :]   per sequence,
-// accumulated in float32 in ascending p, rounded once to bf16 (nearest even).
+// accumulated in float32 in ascending p, rounded once to the element type
+// of x and w (bfloat16 or float16, nearest even).
 //
 // HBM-bound: one thread owns 8 consecutive elements (16 bytes) of one output
 // row and walks the l input rows of its window with 16-byte loads, so a wave
@@ -16,6 +17,7 @@ namespace nsa {
 constexpr int kCompressThreads = 256;
 constexpr int kCompressMaxW = 128 * 64;   // l * N floats staged in LDS (32 KB)
 
+template <typename E>
 __global__ __launch_bounds__(kCompressThreads) void k_compress(CompressParams p)
 {
     __shared__ float wl[kCompressMaxW];
@@ -28,8 +30,7 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress(CompressParams p)
 
     const int nw = p.l * p.N;
     for (int k = threadIdx.x; k < nw; k += kCompressThreads) {
-        uint16_t h = p.w[k];
-        wl[k] = __uint_as_float((uint32_t)h << 16);
+        wl[k] = E::widen(p.w[k]);
     }
     __syncthreads();
 
@@ -53,23 +54,28 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress(CompressParams p)
         const float wv = wcol[pp * p.N];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            acc[2 * j] = fmaf(wv, bf16_lo(v[j]), acc[2 * j]);
-            acc[2 * j + 1] = fmaf(wv, bf16_hi(v[j]), acc[2 * j + 1]);
+            acc[2 * j] = fmaf(wv, E::lo(v[j]), acc[2 * j]);
+            acc[2 * j + 1] = fmaf(wv, E::hi(v[j]), acc[2 * j + 1]);
         }
     }
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        o[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+        o[j] = E::pack2(acc[2 * j], acc[2 * j + 1]);
     *(u32x4*)(p.y + ((int64_t)p.out_off[seg] + i) * row_stride + c * 8) = o;
 }
 
-hipError_t launch_compress(const CompressParams& p, hipStream_t stream)
+hipError_t launch_compress(int dtype, const CompressParams& p, hipStream_t stream)
 {
     if (p.l * p.N > kCompressMaxW)
         return hipErrorInvalidValue;
     dim3 grid(p.max_blocks_x, p.nseg, 1);
-    hipLaunchKernelGGL(k_compress, grid, dim3(kCompressThreads), 0, stream, p);
+    if (dtype == ElemBf16::code)
+        hipLaunchKernelGGL(k_compress<ElemBf16>, grid, dim3(kCompressThreads), 0, stream, p);
+    else if (dtype == ElemF16::code)
+        hipLaunchKernelGGL(k_compress<ElemF16>, grid, dim3(kCompressThreads), 0, stream, p);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -65,10 +65,8 @@ nsa_status read_prefix(const int64_t* prefix, int64_t batch, const char* name,
 
 nsa_status check_dtype(int dtype)
 {
-    if (dtype == NSA_DTYPE_BF16)
+    if (dtype == NSA_DTYPE_BF16 || dtype == NSA_DTYPE_FP16)
         return NSA_OK;
-    if (dtype == NSA_DTYPE_FP16)
-        return fail(NSA_ERR_UNSUPPORTED, "float16 is not built; use bfloat16");
     return fail(NSA_ERR_DTYPE, "unknown dtype code %d", dtype);
 }
 
@@ -76,6 +74,7 @@ nsa_status check_dtype(int dtype)
 
 struct nsa_plan_s {
     int64_t B, N1, N2, D1, D2, l, d, lsel, count;
+    int dtype;   // element type of q, k, v and attention_out (nsa_dtype)
     float scale;
     int64_t T1, T2, S_total, S_max;
     int log2gp, topk_waves, topk_kbufs, sb;
@@ -185,7 +184,7 @@ nsa_status nsa_compress(const void* input, const void* weight, const int64_t* ac
         if (p.nseg == 0)
             continue;
         p.max_blocks_x = (int)((max_items + 255) / 256);
-        hipError_t e = nsa::launch_compress(p, (hipStream_t)stream);
+        hipError_t e = nsa::launch_compress((int)dtype, p, (hipStream_t)stream);
         if (e != hipSuccess)
             return fail(NSA_ERR_HIP, "compress launch failed: %s", hipGetErrorString(e));
     }
@@ -296,6 +295,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->lsel = lsel;
     plan->count = count;
     plan->scale = scale_value;
+    plan->dtype = (int)dtype;
     plan->S_max = S_max;
     plan->log2gp = log2gp;
     plan->topk_waves = waves;
@@ -355,6 +355,7 @@ nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info)
     info->d2 = plan->D2;
     info->select_block_count = plan->count;
     info->workspace_bytes = plan->ws_bytes;
+    info->dtype = plan->dtype;
     return ok();
 }
 
@@ -418,7 +419,7 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
     // the running max moves only when a score beats it by more than 8 in base 2
     a.thr = std::fmin(8.0f / a.c, 3.0e38f);
     a.qsign = q_sign(plan);
-    hipError_t e = nsa::launch_cmp_attn((int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, s);
+    hipError_t e = nsa::launch_cmp_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     return NSA_OK;
@@ -464,7 +465,7 @@ nsa_status launch_select(nsa_plan plan, const void* query, const void* key, cons
     t.npl = plan->sb / 64;
     t.waves = plan->topk_waves;
     t.kbufs = plan->topk_kbufs;
-    hipError_t e = nsa::launch_slc_topk((int)plan->D1, plan->log2gp, t, (int)plan->tiles_c, plan->topk_lds, s);
+    hipError_t e = nsa::launch_slc_topk(plan->dtype, (int)plan->D1, plan->log2gp, t, (int)plan->tiles_c, plan->topk_lds, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "top-k launch failed: %s", hipGetErrorString(e));
     return NSA_OK;

@@ -1,5 +1,6 @@
-// Device helpers shared by the gfx950 kernels: vector types, bf16 packing,
-// MFMA wrappers and cross-lane helpers.  gfx950 only.
+// Device helpers shared by the gfx950 kernels: vector types, the two element
+// types (bfloat16 and float16: widening, packing, MFMA), cross-lane helpers.
+// gfx950 only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -36,6 +37,44 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The element types of q, k, v and the compression weight.  Tensors hold
+// raw 16-bit patterns (uint16_t); a kernel templated on one of these structs
+// widens them to float32, packs float32 pairs back (round to nearest even)
+// and feeds eight-element operands to the 32x32x16 MFMA of that type (both
+// MFMAs share the lane layout described at mfma32).
+struct ElemBf16 {
+    static constexpr int code = 0;
+    __device__ static __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+    __device__ static __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+    __device__ static __forceinline__ float widen(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+    __device__ static __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+struct ElemF16 {
+    static constexpr int code = 1;
+    __device__ static __forceinline__ float widen(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+    __device__ static __forceinline__ float lo(uint32_t w) { return widen((uint16_t)(w & 0xFFFFu)); }
+    __device__ static __forceinline__ float hi(uint32_t w) { return widen((uint16_t)(w >> 16)); }
+    __device__ static __forceinline__ uint32_t pack2(float lo, float hi)
+    {
+        f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+    __device__ static __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
 
 // Combine a value with the one held by the lane 32 positions away.
 __device__ __forceinline__ float half_max(float x)

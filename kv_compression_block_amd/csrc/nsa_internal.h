@@ -40,7 +40,8 @@ struct CompressParams {
     int n_out[kCompressMaxSeg];    // output entries of each sequence
 };
 
-hipError_t launch_compress(const CompressParams& p, hipStream_t stream);
+// dtype: 0 = bfloat16, 1 = float16 (the public enum's values).
+hipError_t launch_compress(int dtype, const CompressParams& p, hipStream_t stream);
 
 // ---- attention kernels ------------------------------------------------------
 struct AttnParams {
@@ -65,7 +66,8 @@ struct AttnParams {
 constexpr int topk_key_tile(int d1) { return d1 > 128 ? 64 : 32; }
 constexpr int kKeyTileMin = 32;
 
-hipError_t launch_cmp_attn(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream);
+hipError_t launch_cmp_attn(int dtype, int d1, int d2, const AttnParams& p, int n_tiles,
+                           hipStream_t stream);
 bool cmp_attn_supported(int d1, int d2);
 int cmp_attn_rows_per_wg(int d1, int d2);   // query rows per attention workgroup
 
@@ -95,8 +97,8 @@ constexpr int kTopkMaxNpl = 16;        // at most 1024 select blocks per sequenc
 
 int topk_log2_gp(int G);               // log2 of the padded group size, -1 if G > 64
 size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs);
-hipError_t launch_slc_topk(int d1, int log2gp, const TopkParams& p, int n_tiles, size_t lds,
-                           hipStream_t stream);
+hipError_t launch_slc_topk(int dtype, int d1, int log2gp, const TopkParams& p, int n_tiles,
+                           size_t lds, hipStream_t stream);
 bool slc_topk_supported(int d1);
 
 }  // namespace nsa

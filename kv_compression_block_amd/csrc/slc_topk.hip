@@ -5,7 +5,7 @@
 //   R = l'/d, L2 = floor(l/d); then the top-k mask (candidates j*l' <= t) and
 //   the select_block_count largest scores, ties to the lower j, -1 padded.
 //
-// P_cmp is recomputed rather than stored: S = Q K^T on MFMA (bf16 in, fp32
+// P_cmp is recomputed rather than stored: S = Q K^T on MFMA (bf16 or f16 in, fp32
 // out) and P = exp2(S * c - bias) with bias = max * log2(e) + log2(sum) from
 // the attention kernel's outputs, i.e. already normalised.
 //
@@ -52,9 +52,9 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D1, int LOG2GP>
 // Three waves per SIMD where the registers allow it (D1 = 128 with groups
 // of 16 or more), two elsewhere.
+template <typename E, int D1, int LOG2GP>
 __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc_topk(TopkParams p)
 {
     constexpr int GP = 1 << LOG2GP;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     // Q rows as the A operand: lane l32 holds row rr*32 + l32 of its wave.
     // Padding heads and tokens past the sequence read the workgroup's first
     // row; their bias below makes their P zero.
-    bf16x8 qa[2][NKS];
+    u32x4 qa[2][NKS];
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const int pr = rr * 32 + l32;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         for (int ks = 0; ks < NKS; ++ks) {
             u32x4 v = *(const u32x4*)(qrow + ks * 16);
             v ^= p.qsign;
-            qa[rr][ks] = as_bf16x8(v);
+            qa[rr][ks] = v;
         }
     }
     // Per accumulator register: P = exp2(S*c - bias) is the normalised P_cmp.
@@ -246,10 +246,10 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) {
-                const bf16x8 kf = as_bf16x8(*(const u32x4*)&kt_lds[(kb * 32 + l32) * KS + ks * 16 + hf * 8]);
+                const u32x4 kf = *(const u32x4*)&kt_lds[(kb * 32 + l32) * KS + ks * 16 + hf * 8];
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr)
-                    s[rr][kb] = mfma32(qa[rr][ks], kf, s[rr][kb]);
+                    s[rr][kb] = E::mfma(qa[rr][ks], kf, s[rr][kb]);
             }
         }
         __builtin_amdgcn_s_setprio(0);
@@ -501,10 +501,10 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     }
 }
 
-template <int D1, int LOG2GP>
+template <typename E, int D1, int LOG2GP>
 static hipError_t launch_t(const TopkParams& p, int n_tiles, size_t lds, hipStream_t stream)
 {
-    auto kern = k_slc_topk<D1, LOG2GP>;
+    auto kern = k_slc_topk<E, D1, LOG2GP>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
@@ -514,19 +514,29 @@ static hipError_t launch_t(const TopkParams& p, int n_tiles, size_t lds, hipStre
     return hipGetLastError();
 }
 
-template <int D1>
+template <typename E, int D1>
 static hipError_t launch_d(int log2gp, const TopkParams& p, int n_tiles, size_t lds, hipStream_t stream)
 {
     switch (log2gp) {
-    case 0: return launch_t<D1, 0>(p, n_tiles, lds, stream);
-    case 1: return launch_t<D1, 1>(p, n_tiles, lds, stream);
-    case 2: return launch_t<D1, 2>(p, n_tiles, lds, stream);
-    case 3: return launch_t<D1, 3>(p, n_tiles, lds, stream);
-    case 4: return launch_t<D1, 4>(p, n_tiles, lds, stream);
-    case 5: return launch_t<D1, 5>(p, n_tiles, lds, stream);
-    case 6: return launch_t<D1, 6>(p, n_tiles, lds, stream);
+    case 0: return launch_t<E, D1, 0>(p, n_tiles, lds, stream);
+    case 1: return launch_t<E, D1, 1>(p, n_tiles, lds, stream);
+    case 2: return launch_t<E, D1, 2>(p, n_tiles, lds, stream);
+    case 3: return launch_t<E, D1, 3>(p, n_tiles, lds, stream);
+    case 4: return launch_t<E, D1, 4>(p, n_tiles, lds, stream);
+    case 5: return launch_t<E, D1, 5>(p, n_tiles, lds, stream);
+    case 6: return launch_t<E, D1, 6>(p, n_tiles, lds, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <typename E>
+static hipError_t launch_e(int d1, int log2gp, const TopkParams& p, int n_tiles, size_t lds,
+                           hipStream_t stream)
+{
+    if (d1 == 64) return launch_d<E, 64>(log2gp, p, n_tiles, lds, stream);
+    if (d1 == 128) return launch_d<E, 128>(log2gp, p, n_tiles, lds, stream);
+    if (d1 == 192) return launch_d<E, 192>(log2gp, p, n_tiles, lds, stream);
+    return hipErrorInvalidValue;
 }
 
 int topk_log2_gp(int G)
@@ -546,14 +556,15 @@ size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs)
 
 bool slc_topk_supported(int d1) { return d1 == 64 || d1 == 128 || d1 == 192; }
 
-hipError_t launch_slc_topk(int d1, int log2gp, const TopkParams& p, int n_tiles, size_t lds,
-                           hipStream_t stream)
+hipError_t launch_slc_topk(int dtype, int d1, int log2gp, const TopkParams& p, int n_tiles,
+                           size_t lds, hipStream_t stream)
 {
     if (n_tiles <= 0)
         return hipSuccess;
-    if (d1 == 64) return launch_d<64>(log2gp, p, n_tiles, lds, stream);
-    if (d1 == 128) return launch_d<128>(log2gp, p, n_tiles, lds, stream);
-    if (d1 == 192) return launch_d<192>(log2gp, p, n_tiles, lds, stream);
+    if (dtype == ElemBf16::code)
+        return launch_e<ElemBf16>(d1, log2gp, p, n_tiles, lds, stream);
+    if (dtype == ElemF16::code)
+        return launch_e<ElemF16>(d1, log2gp, p, n_tiles, lds, stream);
     return hipErrorInvalidValue;
 }
 

@@ -62,12 +62,14 @@ def _good(**kw):
     return base
 
 
-def test_get_workspace_ok_and_plan_info():
-    st, ws, plan = _ws(**_good())
+@pytest.mark.parametrize("dtype", [_lib.NSA_DTYPE_BF16, _lib.NSA_DTYPE_FP16])
+def test_get_workspace_ok_and_plan_info(dtype):
+    st, ws, plan = _ws(**_good(dtype=dtype))
     assert st == _lib.NSA_OK and plan.value and ws > 0
     info = _lib.PlanInfo()
     assert _lib.load().nsa_plan_get_info(plan, ctypes.byref(info)) == 0
     assert (info.total_q_tokens, info.total_cmp_tokens, info.total_sel_blocks, info.max_sel_blocks) == (300, 16, 6, 4)
+    assert info.dtype == dtype
     _lib.load().nsa_plan_destroy(plan)
 
 
@@ -106,7 +108,6 @@ def test_get_workspace_shape_errors(kw):
 def test_get_workspace_nullptr_dtype_unsupported():
     assert _ws(**_good(qlen=None))[0] == _lib.NSA_ERR_NULLPTR
     assert _ws(**_good(dtype=7))[0] == _lib.NSA_ERR_DTYPE
-    assert _ws(**_good(dtype=1))[0] == _lib.NSA_ERR_UNSUPPORTED           # float16 not built
     assert _ws(**_good(D1=256, D2=128))[0] == _lib.NSA_ERR_UNSUPPORTED     # legal, not built
     assert _ws(**_good(N1=128, N2=1))[0] == _lib.NSA_ERR_UNSUPPORTED       # group > 64
 
@@ -136,7 +137,7 @@ def test_compute_call_rejects_before_touching_the_device():
     (dict(d=48, l=32), _lib.NSA_ERR_CONSTRAINT), (dict(D=72), _lib.NSA_ERR_CONSTRAINT),
     (dict(D=272), _lib.NSA_ERR_CONSTRAINT), (dict(out_tokens=99), _lib.NSA_ERR_SHAPE),
     (dict(total=301), _lib.NSA_ERR_SHAPE), (dict(B=0), _lib.NSA_ERR_SHAPE),
-    (dict(dtype=3), _lib.NSA_ERR_DTYPE), (dict(dtype=1), _lib.NSA_ERR_UNSUPPORTED),
+    (dict(dtype=3), _lib.NSA_ERR_DTYPE), (dict(dtype=-1), _lib.NSA_ERR_DTYPE),
     (dict(inp=None), _lib.NSA_ERR_NULLPTR),
 ])
 def test_compress_validation(kw, status):

@@ -8,7 +8,10 @@
   benchmark times: compression in full, attention on sampled tokens;
 * edge cases: empty and short sequences, negative and zero scale, groups
   that are not powers of two, MHA, other remap stencils, count 1;
-* bitwise determinism across runs.
+* bitwise determinism across runs;
+* each of the above in float16 as well as bfloat16 (edge cases: those that
+  reach a different code path per element type -- the sign flip of q for a
+  negative scale, empty sequences, odd groups, D1 = 192, the widest stencil).
 """
 import dataclasses
 
@@ -19,7 +22,7 @@ import torch
 import oracle
 import synth
 from parity import (assert_close_out, assert_pslc, assert_softmax_stats, assert_topk,
-                    bf16_to_f64, gpu_attention, gpu_compress, log, token_meta, upload_bits)
+                    gpu_attention, gpu_compress, log, to_f64, token_meta, upload_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +37,7 @@ SMALL = {
 
 def _check_all(wl, g, ref, tokens, staged=True):
     """g: GPU outputs whose rows are the given tokens, in order."""
-    assert_close_out(bf16_to_f64(g["out"]), ref["out"], "attention_out")
+    assert_close_out(to_f64(g["out"]), ref["out"], "attention_out")
     gmax, gsum = g["max"].cpu().numpy(), g["sum"].cpu().numpy()
     if staged:
         assert_softmax_stats(gmax, gsum, ref["max"], ref["sum"])
@@ -49,17 +52,18 @@ def _check_all(wl, g, ref, tokens, staged=True):
 def _run_small(wl, end_to_end=True):
     log(f"[case] {wl.name}: generate on GPU")
     inp = synth.make_inputs(wl, device="cuda")
-    bits = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    bits = {k: synth.bits(v) for k, v in inp.items()}
     log(f"[case] {wl.name}: oracle")
     ref = oracle.run(wl, bits["q"], bits["k"], bits["v"], bits["w"])
     log(f"[case] {wl.name}: GPU compress")
     kc_g = gpu_compress(wl, inp["k"], inp["w"])
     vc_g = gpu_compress(wl, inp["v"], inp["w"])
     torch.cuda.synchronize()
-    assert_close_out(bf16_to_f64(kc_g), ref["kc"], "compressed K")
-    assert_close_out(bf16_to_f64(vc_g), ref["vc"], "compressed V")
+    assert_close_out(to_f64(kc_g), ref["kc"], "compressed K")
+    assert_close_out(to_f64(vc_g), ref["vc"], "compressed V")
     log(f"[case] {wl.name}: GPU attention on the oracle's compressed K/V")
-    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bits"]), upload_bits(ref["vc_bits"]))
+    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bits"], wl.dtype),
+                      upload_bits(ref["vc_bits"], wl.dtype))
     _check_all(wl, g, ref, ref["tokens"])
     if end_to_end:
         log(f"[case] {wl.name}: GPU attention on its own compressed K/V")
@@ -68,36 +72,41 @@ def _run_small(wl, end_to_end=True):
     return inp, g
 
 
+DTYPES = ["bf16", "f16"]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("wid", [0, 1, 2, 3, 4])
-def test_small_workloads_all_tokens(wid):
-    _run_small(SMALL[wid])
+def test_small_workloads_all_tokens(wid, dtype):
+    _run_small(SMALL[wid].with_dtype(dtype))
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
-def test_full_size_workloads_sampled(wid):
-    wl = synth.WORKLOADS[wid]
+def test_full_size_workloads_sampled(wid, dtype):
+    wl = synth.WORKLOADS[wid].with_dtype(dtype)
     log(f"[case] full {wl.name}: generate on GPU")
     inp = synth.make_inputs(wl, device="cuda")
-    kb, vb, wb = synth.bf16_bits(inp["k"]), synth.bf16_bits(inp["v"]), synth.bf16_bits(inp["w"])
+    kb, vb, wb = synth.bits(inp["k"]), synth.bits(inp["v"]), synth.bits(inp["w"])
     actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
     log(f"[case] full {wl.name}: oracle compress")
-    kc_ref = oracle.compress(kb, wb, actq, wl.l, wl.d)
-    vc_ref = oracle.compress(vb, wb, actq, wl.l, wl.d)
+    kc_ref = oracle.compress(kb, wb, actq, wl.l, wl.d, dtype)
+    vc_ref = oracle.compress(vb, wb, actq, wl.l, wl.d, dtype)
     log(f"[case] full {wl.name}: GPU compress")
     kc_g = gpu_compress(wl, inp["k"], inp["w"])
     vc_g = gpu_compress(wl, inp["v"], inp["w"])
     torch.cuda.synchronize()
-    assert_close_out(bf16_to_f64(kc_g), kc_ref, "compressed K")
-    assert_close_out(bf16_to_f64(vc_g), vc_ref, "compressed V")
+    assert_close_out(to_f64(kc_g), kc_ref, "compressed K")
+    assert_close_out(to_f64(vc_g), vc_ref, "compressed V")
     del kc_g, vc_g
-    kc_b, vc_b = oracle.to_bf16(kc_ref), oracle.to_bf16(vc_ref)
+    kc_b, vc_b = oracle.round_to(kc_ref, dtype), oracle.round_to(vc_ref, dtype)
     tokens = synth.sample_tokens(wl, per_seq=6)
     log(f"[case] full {wl.name}: oracle attention on {len(tokens)} tokens")
-    q_rows = synth.bf16_bits(inp["q"][torch.from_numpy(tokens).cuda()])
+    q_rows = synth.bits(inp["q"][torch.from_numpy(tokens).cuda()])
     ref = oracle.attention(q_rows, tokens, kc_b, vc_b, actq, oracle.cmp_prefix(wl.seqlens, wl.l, wl.d),
-                           wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count)
+                           wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count, dtype=dtype)
     log(f"[case] full {wl.name}: GPU attention (all tokens)")
-    g = gpu_attention(wl, inp["q"], upload_bits(kc_b), upload_bits(vc_b))
+    g = gpu_attention(wl, inp["q"], upload_bits(kc_b, dtype), upload_bits(vc_b, dtype))
     tok_t = torch.from_numpy(tokens).cuda()
     gs = {"out": g["out"][tok_t], "max": g["max"][tok_t], "sum": g["sum"][tok_t],
           "pslc": g["pslc"][tok_t], "topk": g["topk"][tok_t]}
@@ -129,9 +138,13 @@ EDGES = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(EDGES))
-def test_edge_cases(name):
-    _run_small(dataclasses.replace(EDGES[name], name=name))
+F16_EDGES = ["short-and-empty-seqs", "negative-scale", "group-of-3", "d192-group-16", "stencil-R8"]
+
+
+@pytest.mark.parametrize("name,dtype", [(n, "bf16") for n in sorted(EDGES)] +
+                         [(n, "f16") for n in F16_EDGES])
+def test_edge_cases(name, dtype):
+    _run_small(dataclasses.replace(EDGES[name], name=name).with_dtype(dtype))
 
 
 def test_topk_exact_ties():
@@ -144,11 +157,12 @@ def test_topk_exact_ties():
     log(f"[case] {wl.name}: generate on GPU, q = 0")
     inp = synth.make_inputs(wl, device="cuda")
     inp["q"].zero_()
-    bits = {k: synth.bf16_bits(v) for k, v in inp.items()}
+    bits = {k: synth.bits(v) for k, v in inp.items()}
     log(f"[case] {wl.name}: oracle")
     ref = oracle.run(wl, bits["q"], bits["k"], bits["v"], bits["w"])
     log(f"[case] {wl.name}: GPU attention on the oracle's compressed K/V")
-    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bits"]), upload_bits(ref["vc_bits"]))
+    g = gpu_attention(wl, inp["q"], upload_bits(ref["kc_bits"], wl.dtype),
+                      upload_bits(ref["vc_bits"], wl.dtype))
     _check_all(wl, g, ref, ref["tokens"])
     gi, ri = g["topk"].cpu().numpy(), ref["topk"]
     long_rows = 0

@@ -76,6 +76,12 @@ def _load():
                                          I64, I64, I64, I64, ctypes.c_int,
                                          P, P, P, P, I64, P]
     lib.nsa_oracle_attention.restype = ctypes.c_int
+    lib.nsa_oracle_attention_masked.argtypes = [P, P, I64, P, P, P, P, I64,
+                                                I64, I64, I64, I64, ctypes.c_double,
+                                                I64, I64, I64, I64, ctypes.c_int,
+                                                P, I64, I64, P, I64, I64,
+                                                P, P, P, P, I64, P]
+    lib.nsa_oracle_attention_masked.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -189,11 +195,15 @@ def compress(x_bits, w_bits, act_seq_len, l: int, d: int, dtype: str = "bf16") -
 
 def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_kvlen,
               N1: int, N2: int, scale: float, l: int, d: int, lsel: int, count: int,
-              s_stride: Optional[int] = None, dtype: str = "bf16") -> dict:
+              s_stride: Optional[int] = None, dtype: str = "bf16",
+              atten_mask=None, topk_mask=None) -> dict:
     """Steps 1-7 for the listed global tokens.
 
     q_rows_bits: [n_tok, N1, D1] bits of those tokens' query rows; q, kc and
-    vc are all of element type ``dtype``.
+    vc are all of element type ``dtype``.  ``atten_mask`` / ``topk_mask``:
+    None (the positional rules) or 2-D boolean arrays indexed by (local
+    query position, compressed entry / select block), True = masked out,
+    shared by all sequences.
     Returns dict(out [n,N1,D2], max [n,N1], sum [n,N1],
                  pslc [n,N2,s_stride], topk [n,N2,count] int32).
     """
@@ -217,17 +227,31 @@ def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_k
     ssum = np.empty((n_tok, N1), dtype=np.float64)
     pslc = np.empty((n_tok, N2, s_stride), dtype=np.float64)
     topk = np.empty((n_tok, N2, count), dtype=np.int32)
-    rc = _load().nsa_oracle_attention(_ptr(q), _ptr(tok), n_tok, _ptr(kc), _ptr(vc),
-                                      _ptr(actq), _ptr(actc), len(actq),
-                                      N1, N2, D1, D2, float(scale), l, d, lsel, count,
-                                      _code(dtype), _ptr(out), _ptr(smax), _ptr(ssum), _ptr(pslc), s_stride,
-                                      _ptr(topk))
+
+    def mask_arg(m):
+        if m is None:
+            return None, ctypes.c_void_p(0), 0, 0
+        m = np.ascontiguousarray(np.asarray(m, dtype=bool)).view(np.uint8)
+        if m.ndim != 2:
+            raise ValueError("masks are 2-D (query position, column)")
+        return m, _ptr(m), m.shape[0], m.shape[1]
+
+    am, amp, amr, amc = mask_arg(atten_mask)
+    tm, tmp, tmr, tmc = mask_arg(topk_mask)
+    rc = _load().nsa_oracle_attention_masked(_ptr(q), _ptr(tok), n_tok, _ptr(kc), _ptr(vc),
+                                             _ptr(actq), _ptr(actc), len(actq),
+                                             N1, N2, D1, D2, float(scale), l, d, lsel, count,
+                                             _code(dtype), amp, amr, amc, tmp, tmr, tmc,
+                                             _ptr(out), _ptr(smax), _ptr(ssum), _ptr(pslc),
+                                             s_stride, _ptr(topk))
+    del am, tm
     if rc != 0:
         raise ValueError(f"nsa_oracle_attention returned {rc}")
     return {"out": out, "max": smax, "sum": ssum, "pslc": pslc, "topk": topk}
 
 
-def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None) -> dict:
+def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None, atten_mask=None,
+        topk_mask=None) -> dict:
     """The whole path for a workload: compress K and V, round them to the
     workload's element type, then steps 1-7 for ``tokens`` (all tokens when
     None).  ``kc_bits``/``vc_bits`` are the rounded compressed tensors."""
@@ -244,6 +268,7 @@ def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None) -> dict:
         tokens = np.asarray(tokens, dtype=np.int64)
         q_rows = q_bits[tokens]
     res = attention(q_rows, tokens, kc_b, vc_b, actq, cmp_prefix(wl.seqlens, wl.l, wl.d),
-                    wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count, dtype=dt)
+                    wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count, dtype=dt,
+                    atten_mask=atten_mask, topk_mask=topk_mask)
     res.update({"kc": kc, "vc": vc, "kc_bits": kc_b, "vc_bits": vc_b, "tokens": tokens})
     return res

@@ -31,10 +31,15 @@
  * Readings of points the pages leave open (each also listed in the design
  * notes of the repository):
  *   - a compressed block i is visible to the query at local position t iff
- *     i*d + l - 1 <= t (the last token of its window is not in the future);
- *     no explicit mask tensor is taken;
- *   - select block j is a top-k candidate iff j*l' <= t; picks beyond the
- *     number of candidates are -1;
+ *     i*d + l - 1 <= t (the last token of its window is not in the future),
+ *     unless an explicit atten_mask is given;
+ *   - select block j is a top-k candidate iff j*l' <= t, unless an explicit
+ *     topk_mask is given; picks beyond the number of candidates are -1;
+ *   - explicit masks (the MindSpore page's optional bool atten_mask and
+ *     topk_mask of shape (S1, S2); polarity unstated): one matrix shared by
+ *     all sequences, indexed by (local query position t, local compressed
+ *     entry i or select block j); a true element masks its pair out, and
+ *     the mask given replaces that step's positional rule;
  *   - query head h belongs to KV head floor(h / (N1/N2));
  *   - a remap index outside [0, number of compressed blocks) adds 0;
  *   - l/d in the remap's upper limit is floor(l/d); l'/d is an integer
@@ -240,14 +245,15 @@ static int64_t find_seq(const int64_t* act_seq_qlen, int64_t B, int64_t tg, int6
 static void attend_one_head(const uint16_t* qh, const uint16_t* kc, const uint16_t* vc,
                             int64_t cmp0, int64_t n_cmp, int64_t t, int64_t g,
                             int64_t N2, int64_t D1, int64_t D2, double scale,
-                            int64_t l, int64_t d, int dtype,
+                            int64_t l, int64_t d, int dtype, const uint8_t* amask_row,
                             double* s, double* P, double* out_h, double* m_out, double* L_out)
 {
-    /* step 1: QK = scale * query . key^T, then the attention mask. */
+    /* step 1: QK = scale * query . key^T, then the attention mask (the row
+     * of an explicit mask when one is given, else the positional rule). */
     double m = -INFINITY;
     int any = 0;
     for (int64_t i = 0; i < n_cmp; ++i) {
-        int visible = (i * d + l - 1 <= t);
+        int visible = amask_row ? (amask_row[i] == 0) : (i * d + l - 1 <= t);
         if (!visible) {
             s[i] = -INFINITY;
             continue;
@@ -301,10 +307,11 @@ static void remap_one_head(const double* P, int64_t n_cmp, int64_t S_sel,
  * pick the `count` largest scores (descending, ties to the lower j) by
  * repeated selection; slots left over hold -1. */
 static void topk_one_group(const double* Pslc_g, int64_t S_sel, int64_t t, int64_t lsel,
-                           int64_t count, unsigned char* taken, int32_t* idx_out)
+                           int64_t count, const uint8_t* tmask_row, unsigned char* taken,
+                           int32_t* idx_out)
 {
-    for (int64_t j = 0; j < S_sel; ++j)
-        taken[j] = !(j * lsel <= t);   /* topk_mask: not a candidate */
+    for (int64_t j = 0; j < S_sel; ++j)   /* topk_mask: not a candidate */
+        taken[j] = tmask_row ? (tmask_row[j] != 0) : !(j * lsel <= t);
     for (int64_t k = 0; k < count; ++k) {
         int64_t best = -1;
         float best_v = 0.0f;
@@ -336,15 +343,22 @@ static void topk_one_group(const double* Pslc_g, int64_t S_sel, int64_t t, int64
  * pslc     : [n_tok, N2, s_stride] group-summed importance scores before the
  *            top-k mask, j < ceil(T_b/l'), zero beyond
  * topk     : [n_tok, N2, count] int32
+ * atten_mask, am_rows, am_cols : NULL, or a [am_rows, am_cols] byte matrix
+ *            (non-zero = masked out) indexed by (local t, compressed entry i);
+ *            it needs a row for every local position and a column for every
+ *            compressed entry of each sequence
+ * topk_mask, tm_rows, tm_cols : NULL, or the same for (local t, select block j)
  * Returns 0, or a negative code for arguments it cannot evaluate.
  */
-int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t n_tok,
-                         const uint16_t* kc, const uint16_t* vc,
-                         const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen, int64_t B,
-                         int64_t N1, int64_t N2, int64_t D1, int64_t D2, double scale,
-                         int64_t l, int64_t d, int64_t lsel, int64_t count, int dtype,
-                         double* out, double* smax, double* ssum,
-                         double* pslc, int64_t s_stride, int32_t* topk)
+int nsa_oracle_attention_masked(const uint16_t* q_rows, const int64_t* tokens, int64_t n_tok,
+                                const uint16_t* kc, const uint16_t* vc,
+                                const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen,
+                                int64_t B, int64_t N1, int64_t N2, int64_t D1, int64_t D2,
+                                double scale, int64_t l, int64_t d, int64_t lsel, int64_t count,
+                                int dtype, const uint8_t* atten_mask, int64_t am_rows,
+                                int64_t am_cols, const uint8_t* topk_mask, int64_t tm_rows,
+                                int64_t tm_cols, double* out, double* smax, double* ssum,
+                                double* pslc, int64_t s_stride, int32_t* topk)
 {
     if (N2 < 1 || N1 % N2 != 0 || d < 1 || lsel % d != 0 || count < 1 || B < 1 ||
         dtype < 0 || dtype > 1)
@@ -362,6 +376,14 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
     }
     if (s_stride < s_sel_max)
         return -2;
+    int64_t T_max = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
+        if (T > T_max) T_max = T;
+    }
+    if ((atten_mask && (am_rows < T_max || am_cols < n_cmp_max)) ||
+        (topk_mask && (tm_rows < T_max || tm_cols < s_sel_max)))
+        return -5;
     for (int64_t k = 0; k < n_tok; ++k) {
         int64_t tl = 0;
         if (find_seq(act_seq_qlen, B, tokens[k], &tl) < 0)
@@ -392,7 +414,8 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
                 for (int64_t h = 0; h < N1; ++h) {
                     int64_t g = h / G;
                     attend_one_head(q_rows + (k * N1 + h) * D1, kc, vc, cmp0, n_cmp, t, g,
-                                    N2, D1, D2, scale, l, d, dtype, s, P,
+                                    N2, D1, D2, scale, l, d, dtype,
+                                    atten_mask ? atten_mask + t * am_cols : NULL, s, P,
                                     out + (k * N1 + h) * D2,
                                     smax + k * N1 + h, ssum + k * N1 + h);
                     /* step 4, then step 5: heads of a group summed in order. */
@@ -401,7 +424,8 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
                         pslc_k[g * s_stride + j] += Ph[j];
                 }
                 for (int64_t g = 0; g < N2; ++g)
-                    topk_one_group(pslc_k + g * s_stride, S_sel, t, lsel, count, taken,
+                    topk_one_group(pslc_k + g * s_stride, S_sel, t, lsel, count,
+                                   topk_mask ? topk_mask + t * tm_cols : NULL, taken,
                                    topk + (k * N2 + g) * count);
             }
         }
@@ -411,4 +435,19 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
         free(taken);
     }
     return err;
+}
+
+/* The same without explicit masks: the positional rules throughout. */
+int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t n_tok,
+                         const uint16_t* kc, const uint16_t* vc,
+                         const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen, int64_t B,
+                         int64_t N1, int64_t N2, int64_t D1, int64_t D2, double scale,
+                         int64_t l, int64_t d, int64_t lsel, int64_t count, int dtype,
+                         double* out, double* smax, double* ssum,
+                         double* pslc, int64_t s_stride, int32_t* topk)
+{
+    return nsa_oracle_attention_masked(q_rows, tokens, n_tok, kc, vc, act_seq_qlen,
+                                       act_cmp_seq_kvlen, B, N1, N2, D1, D2, scale, l, d, lsel,
+                                       count, dtype, NULL, 0, 0, NULL, 0, 0, out, smax, ssum,
+                                       pslc, s_stride, topk);
 }

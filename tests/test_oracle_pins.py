@@ -660,3 +660,131 @@ def test_topk_ties_go_to_lower_index():
         ties += len(row) - len(np.unique(row))
     assert ties > 100
     _check_topk_brute(res, lens, lsel, count)
+
+
+# --------------------------------------------------------------------------
+# Explicit atten_mask / topk_mask (MindSpore page, Parameters: optional bool
+# tensors of shape (S1, S2)).  Reading: one matrix shared by all sequences,
+# indexed by (local query position, compressed entry or select block); a
+# true element masks its pair out and replaces that step's positional rule.
+# --------------------------------------------------------------------------
+
+def _mask_case(seed, lens, N1, N2, D1, D2, l, d, lsel, extra_rows=3, extra_cols=5,
+               p_masked=0.4):
+    rng = np.random.default_rng(seed)
+    q, kc, vc = _attention_case(seed, lens, N1, N2, D1, D2, l, d)
+    actc = oracle.cmp_prefix(lens, l, d)
+    nc_max = int(np.diff(np.concatenate([[0], actc])).max())
+    s_max = max(-(-T // lsel) for T in lens)
+    rows = max(lens) + extra_rows
+    am = rng.random((rows, nc_max + extra_cols)) < p_masked
+    tm = rng.random((rows, s_max + extra_cols)) < p_masked
+    am[5, :] = True             # a row with every block masked
+    am[7, :] = False            # a row that sees blocks the causal rule hides
+    tm[6, :] = True             # a row with no top-k candidate
+    return q, kc, vc, am, tm
+
+
+def test_atten_mask_matches_torch_sdpa_and_literal_remap():
+    """An explicit atten_mask: rows with a visible block equal torch's SDPA
+    with the complementary boolean mask (torch's True = takes part); fully
+    masked rows give 0 / -inf / 0; P_slc' is the literal remap formula over
+    the masked softmax, summed over the group, computed here in numpy."""
+    lens = [90, 41, 130]
+    N1, N2, D1, D2, l, d, lsel, count = 4, 2, 16, 8, 32, 16, 64, 3
+    scale = 0.4
+    q, kc, vc, am, _ = _mask_case(21, lens, N1, N2, D1, D2, l, d, lsel)
+    actq = np.cumsum(lens).astype(np.int64)
+    actc = oracle.cmp_prefix(lens, l, d)
+    res = oracle.attention(q, np.arange(sum(lens), dtype=np.int64), kc, vc, actq, actc, N1, N2,
+                           scale, l, d, lsel, count, atten_mask=am)
+    qf, kf, vf = (widen_torch(a, "bf16") for a in (q, kc, vc))
+    cst = np.concatenate([[0], actc[:-1]])
+    G, R, L2 = N1 // N2, lsel // d, l // d
+    n_full_rows = n_empty = 0
+    for b, (s, T) in enumerate(zip(starts_of(lens), lens)):
+        nc = int(actc[b] - cst[b])
+        S = -(-T // lsel)
+        if nc == 0:
+            continue
+        vis = torch.from_numpy(~am[:T, :nc])
+        has = vis.any(dim=1)
+        pg = np.zeros((T, N2, nc))
+        for h in range(N1):
+            g = h // G
+            qb = qf[s:s + T, h]
+            kb = kf[cst[b]:cst[b] + nc, g]
+            vb = vf[cst[b]:cst[b] + nc, g]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qb[None, None], kb[None, None], vb[None, None], attn_mask=vis[None, None],
+                scale=scale)[0, 0]
+            got = torch.from_numpy(res["out"][s:s + T, h])
+            torch.testing.assert_close(got[has], ref[has], rtol=1e-12, atol=1e-13)
+            assert torch.all(got[~has] == 0)
+            assert np.all(np.isneginf(res["max"][s:s + T, h][~has.numpy()]))
+            assert np.all(res["sum"][s:s + T, h][~has.numpy()] == 0)
+            sc = torch.where(vis, scale * (qb @ kb.T), torch.tensor(-float("inf"), dtype=torch.float64))
+            P = torch.softmax(sc, dim=1)
+            P = torch.where(has[:, None], P, torch.zeros_like(P)).numpy()
+            pg[:, g] += P
+        n_full_rows += int(has.sum())
+        n_empty += int((~has).sum())
+        for t in range(T):
+            for g in range(N2):
+                for j in range(S):
+                    ref = sum(pg[t, g, R * j - m - n] for m in range(R) for n in range(L2)
+                              if 0 <= R * j - m - n < nc)
+                    assert abs(res["pslc"][s + t, g, j] - ref) <= 1e-12 * max(1.0, ref)
+    assert n_full_rows > 100 and n_empty >= 3
+
+
+def test_topk_mask_matches_brute_force():
+    """An explicit topk_mask: the candidates of row t are the j < ceil(T/l')
+    with topk_mask[t, j] false; the picks are a full numpy sort of their
+    float32 scores (descending, ties to the lower j), -1 padded."""
+    lens = [200, 70]
+    N1, N2, D1, D2, l, d, lsel, count = 4, 2, 16, 8, 32, 16, 16, 4
+    q, kc, vc, _, tm = _mask_case(22, lens, N1, N2, D1, D2, l, d, lsel)
+    actq = np.cumsum(lens).astype(np.int64)
+    res = oracle.attention(q, np.arange(sum(lens), dtype=np.int64), kc, vc, actq,
+                           oracle.cmp_prefix(lens, l, d), N1, N2, 0.3, l, d, lsel, count,
+                           topk_mask=tm)
+    short = 0
+    for s, T in zip(starts_of(lens), lens):
+        S = -(-T // lsel)
+        for t in range(T):
+            cand = np.array([j for j in range(S) if not tm[t, j]], dtype=np.int64)
+            short += len(cand) < count
+            for g in range(N2):
+                keys = res["pslc"][s + t, g, cand].astype(np.float32)
+                order = cand[np.lexsort((cand, -keys))]
+                expect = np.full(count, -1, dtype=np.int32)
+                expect[:min(count, len(order))] = order[:count]
+                assert np.array_equal(res["topk"][s + t, g], expect), (s + t, g)
+    assert short > 0
+
+
+def test_masks_that_spell_the_positional_rules_change_nothing():
+    """Masks built from the positional rules (block i masked iff
+    i*d + l - 1 > t, select block j iff j*l' > t), with extra rows and
+    columns, reproduce the mask-free results exactly: the mask is indexed
+    (query position, column) and true means masked out."""
+    lens = [150, 33, 260]
+    N1, N2, D1, D2, l, d, lsel, count = 4, 1, 16, 8, 32, 16, 64, 3
+    q, kc, vc = _attention_case(23, lens, N1, N2, D1, D2, l, d)
+    actq = np.cumsum(lens).astype(np.int64)
+    actc = oracle.cmp_prefix(lens, l, d)
+    rows, cols = max(lens) + 4, int(actc[-1]) + 3
+    t = np.arange(rows)[:, None]
+    am = np.arange(cols)[None, :] * d + l - 1 > t
+    tm = np.arange(cols)[None, :] * lsel > t
+    tok = np.arange(sum(lens), dtype=np.int64)
+    a = oracle.attention(q, tok, kc, vc, actq, actc, N1, N2, 0.3, l, d, lsel, count)
+    b = oracle.attention(q, tok, kc, vc, actq, actc, N1, N2, 0.3, l, d, lsel, count,
+                         atten_mask=am, topk_mask=tm)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+    # a mask without a column for every compressed entry is refused
+    with pytest.raises(ValueError):
+        oracle.attention(q, tok, kc, vc, actq, actc, N1, N2, 0.3, l, d, lsel, count,
+                         atten_mask=am[:, :2])

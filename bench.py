@@ -15,7 +15,11 @@ kernel, bound by MFMA of the element type); ``cpu_baseline`` times the CPU
 oracle on a bounded random sample of the same workload's tokens.
 
     python bench.py [--steps K] [--warmup W] [--workload 0..4] [--dtype bf16|f16]
-                    [--no-cpu-baseline]
+                    [--masks] [--no-cpu-baseline]
+
+``--masks`` passes the workload's causal rules as explicit atten_mask /
+topk_mask tensors (the masked entry points: mask packing plus the
+every-tile masked kernels) instead of letting the kernels generate them.
 """
 from __future__ import annotations
 
@@ -134,6 +138,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, choices=range(5))
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="element type of q, k, v and the weight (default bf16)")
+    ap.add_argument("--masks", action="store_true",
+                    help="give the causal rules as explicit atten_mask / topk_mask tensors")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -191,7 +197,18 @@ def main() -> int:
             "topk_indices": torch.empty((wl.T, wl.N2, wl.count), dtype=torch.int32, device=dev),
             "softmax_max": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev),
             "softmax_sum": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev)}
-    ws = torch.empty((max(plan.workspace_bytes, 1),), dtype=torch.uint8, device=dev)
+    masks = {}
+    if args.masks:
+        # The positional rules spelled out as masks (True = masked out), one
+        # matrix for all sequences: rows = local query positions.
+        t_max = max(wl.seqlens)
+        t = torch.arange(t_max, device=dev)[:, None]
+        masks["atten_mask"] = (torch.arange(max(nsa.nsa_compress_out_len(T, wl.l, wl.d) for T in wl.seqlens),
+                                            device=dev)[None, :] * wl.d + wl.l - 1) > t
+        masks["topk_mask"] = (torch.arange(max(-(-T // wl.lsel) for T in wl.seqlens),
+                                           device=dev)[None, :] * wl.lsel) > t
+    ws_bytes = plan.info["masked_workspace_bytes"] if args.masks else plan.workspace_bytes
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
@@ -203,11 +220,14 @@ def main() -> int:
         nsa.nsa_compress(inp["v"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=vc, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc, workspace=ws, outputs=outs, stream=stream)
+        nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc, workspace=ws, outputs=outs, stream=stream,
+                                       atten_mask=masks.get("atten_mask"))
         if ev is not None:
             ev[3].record(stream)
         nsa.nsa_compress_attention_select(plan, inp["q"], kc, outs["softmax_max"], outs["softmax_sum"],
-                                          workspace=ws, outputs=outs, stream=stream)
+                                          workspace=ws, outputs=outs, stream=stream,
+                                          atten_mask=masks.get("atten_mask"),
+                                          topk_mask=masks.get("topk_mask"))
         if ev is not None:
             ev[4].record(stream)
 
@@ -255,17 +275,22 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "N1": wl.N1, "N2": wl.N2, "D1": wl.D1,
                    "D2": wl.D2, "l": wl.l, "d": wl.d, "lsel": wl.lsel, "count": wl.count,
-                   "scale": wl.scale, "dtype": wl.dtype, "parallelism": "single-gpu"},
+                   "scale": wl.scale, "dtype": wl.dtype,
+                   "masks": "explicit tensors (the causal rules spelled out)" if args.masks else "positional rules",
+                   "parallelism": "single-gpu"},
         "tflops_algorithmic": total_flops / (ms_step / 1e3) / 1e12,
         "frac_of_bf16_peak": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"kernel": "k_cmp_attn_fwd", "bound": "mfma", "achieved": attn_tflops,
                      "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak,
-                     "traffic": measured_traffic(wl.name),
+                     "traffic": None if args.masks else measured_traffic(wl.name),
                      "traffic_unit": "HBM bytes per launch",
                      "work_per_launch": f"{work['attn_flops']:.4e} flop = 2*(D1+D2) x {work['visible_pairs']} "
                                         f"visible (token, block) pairs x {wl.N1} heads"},
         "kernels": kernels,
     }
+    if args.masks:
+        res["kernels_note"] = ("with --masks, 'attention' includes packing atten_mask and 'select_topk' "
+                               "includes packing both masks (each call packs what it reads)")
     if not args.no_cpu_baseline:
         print(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

@@ -211,6 +211,60 @@ nsa_status nsa_compress_attention_select(nsa_plan plan, const void* query, const
                                          int32_t* topk_indices, float* p_slc_debug,
                                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Explicit masks -- "mindspore.ops.nsa_compress_attention", Parameters: the
+ * optional bool atten_mask (rows = query positions, columns = compressed
+ * entries) and topk_mask (columns = select blocks), each of shape (S1, S2).
+ * The page states no polarity and no varlen layout; the reading taken here:
+ *   - one row-major byte matrix shared by every sequence of the batch, row t
+ *     for the query at local position t, column i for the sequence's i-th
+ *     compressed entry (atten_mask) or select block (topk_mask);
+ *   - a non-zero byte masks its pair out (the score becomes -inf before the
+ *     softmax, or the block is not a top-k candidate);
+ *   - a given mask replaces that step's positional rule (i*d + l - 1 <= t,
+ *     resp. j*l' <= t); a NULL mask keeps the rule.
+ * The matrices must have at least as many rows as the longest sequence has
+ * tokens and at least as many columns as the largest per-sequence count
+ * (compressed entries, resp. select blocks); extra rows and columns are not
+ * read.  They are device memory owned by the caller, read during the call's
+ * stream work only.
+ */
+typedef struct nsa_masks {
+    const void* atten_mask;     /* NULL, or [atten_rows, atten_cols] bytes, device */
+    int64_t atten_rows, atten_cols;
+    const void* topk_mask;      /* NULL, or [topk_rows, topk_cols] bytes, device */
+    int64_t topk_rows, topk_cols;
+} nsa_masks;
+
+/*
+ * The three second-phase calls with masks (masks may be NULL, and either
+ * mask in it may be NULL).  The masks are packed to bits inside the
+ * workspace first, so the workspace must hold masked_workspace_bytes (plan
+ * info) whenever a mask is given.  nsa_compress_attention_select_masked
+ * needs the same atten_mask as the fwd call whose statistics it reads.
+ * Errors: those of the unmasked calls, plus NSA_ERR_SHAPE (a mask smaller
+ * than stated above) and NSA_ERR_WORKSPACE (workspace below
+ * masked_workspace_bytes).
+ */
+nsa_status nsa_compress_attention_masked(nsa_plan plan, const void* query, const void* key,
+                                         const void* value, const nsa_masks* masks,
+                                         void* attention_out, int32_t* topk_indices,
+                                         float* softmax_max, float* softmax_sum,
+                                         float* p_slc_debug, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+nsa_status nsa_compress_attention_fwd_masked(nsa_plan plan, const void* query, const void* key,
+                                             const void* value, const nsa_masks* masks,
+                                             void* attention_out, float* softmax_max,
+                                             float* softmax_sum, void* workspace,
+                                             size_t workspace_bytes, void* stream);
+
+nsa_status nsa_compress_attention_select_masked(nsa_plan plan, const void* query, const void* key,
+                                                const nsa_masks* masks, const float* softmax_max,
+                                                const float* softmax_sum, int32_t* topk_indices,
+                                                float* p_slc_debug, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+
 /* Sizes a plan fixed, for callers that allocate outputs from a plan. */
 typedef struct nsa_plan_info {
     int64_t batch;
@@ -221,6 +275,7 @@ typedef struct nsa_plan_info {
     int64_t head_num, kv_head_num, d1, d2, select_block_count;
     size_t workspace_bytes;
     int64_t dtype;              /* the nsa_dtype the plan was made for */
+    size_t masked_workspace_bytes;  /* workspace of the calls given a mask */
 } nsa_plan_info;
 
 nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info);

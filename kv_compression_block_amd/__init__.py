@@ -15,6 +15,11 @@ Entry points (same names as the C ABI):
   indices, softmax max/sum (and optionally the importance scores);
 * ``compress_attention`` -- both phases in one call with the argument list
   of ``mindspore.ops.nsa_compress_attention``.
+
+The second-phase calls take optional ``atten_mask`` / ``topk_mask``: 2-D
+bool (or uint8) GPU tensors indexed by (local query position, compressed
+entry / select block), shared by all sequences; True masks the pair out and
+a given mask replaces that step's positional rule.
 """
 from __future__ import annotations
 
@@ -24,7 +29,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import NsaError, PlanInfo  # noqa: F401
+from ._lib import Masks, NsaError, PlanInfo  # noqa: F401
 
 __all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_workspace",
            "nsa_compress_attention", "nsa_compress_attention_fwd", "nsa_compress_attention_select",
@@ -194,10 +199,33 @@ def _check_qkv(plan: Plan, query, key, value=None):
             raise TypeError("query and value must share a dtype")
 
 
-def _workspace(plan: Plan, workspace, dev):
+def _workspace(plan: Plan, workspace, dev, masked: bool = False):
+    need = plan.info["masked_workspace_bytes"] if masked else plan.workspace_bytes
     if workspace is None:
-        workspace = torch.empty((max(plan.workspace_bytes, 1),), dtype=torch.uint8, device=dev)
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def _masks(atten_mask, topk_mask):
+    """An nsa_masks struct (and the tensors it points at), or None."""
+    if atten_mask is None and topk_mask is None:
+        return None, ()
+    m = Masks()
+    keep = []
+    for name, t in (("atten_mask", atten_mask), ("topk_mask", topk_mask)):
+        if t is None:
+            continue
+        _need_tensor(t, name)
+        if t.dim() != 2:
+            raise ValueError(f"{name} must be 2-D (query position, column), got shape {tuple(t.shape)}")
+        if t.dtype not in (torch.bool, torch.uint8):
+            raise TypeError(f"{name} must be a bool or uint8 tensor, got {t.dtype}")
+        keep.append(t)
+        pre = name.split("_")[0]
+        setattr(m, name, t.data_ptr())
+        setattr(m, f"{pre}_rows", t.shape[0])
+        setattr(m, f"{pre}_cols", t.shape[1])
+    return m, tuple(keep)
 
 
 def _alloc_outputs(plan: Plan, query, outputs, want_pslc: bool):
@@ -221,18 +249,24 @@ def _alloc_outputs(plan: Plan, query, outputs, want_pslc: bool):
 
 def nsa_compress_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                            workspace: Optional[torch.Tensor] = None, return_p_slc: bool = False,
-                           outputs: Optional[dict] = None, stream=None):
+                           outputs: Optional[dict] = None, stream=None, atten_mask=None,
+                           topk_mask=None):
     """Second phase.  Returns (attention_out, topk_indices, softmax_max,
     softmax_sum) and, with ``return_p_slc``, the importance scores
     [T1, N2, S] as a fifth element."""
     _check_qkv(plan, query, key, value)
     o = _alloc_outputs(plan, query, outputs, return_p_slc)
-    ws, ws_bytes = _workspace(plan, workspace, query.device)
-    st = _lib.load().nsa_compress_attention(
-        plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(o["attention_out"]),
-        _ptr(o["topk_indices"]), _ptr(o["softmax_max"]), _ptr(o["softmax_sum"]),
-        _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws), ws_bytes,
-        _stream_ptr(query.device, stream))
+    m, _keep = _masks(atten_mask, topk_mask)
+    ws, ws_bytes = _workspace(plan, workspace, query.device, m is not None)
+    lib = _lib.load()
+    args = (_ptr(o["attention_out"]), _ptr(o["topk_indices"]), _ptr(o["softmax_max"]),
+            _ptr(o["softmax_sum"]), _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws),
+            ws_bytes, _stream_ptr(query.device, stream))
+    if m is None:
+        st = lib.nsa_compress_attention(plan.handle, _ptr(query), _ptr(key), _ptr(value), *args)
+    else:
+        st = lib.nsa_compress_attention_masked(plan.handle, _ptr(query), _ptr(key), _ptr(value),
+                                               ctypes.byref(m), *args)
     _lib.check(st)
     res = (o["attention_out"], o["topk_indices"], o["softmax_max"], o["softmax_sum"])
     return res + (o["p_slc"],) if return_p_slc else res
@@ -240,15 +274,20 @@ def nsa_compress_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, v
 
 def nsa_compress_attention_fwd(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                                workspace: Optional[torch.Tensor] = None, outputs: Optional[dict] = None,
-                               stream=None):
+                               stream=None, atten_mask=None):
     """Steps 1-3 only: returns (attention_out, softmax_max, softmax_sum)."""
     _check_qkv(plan, query, key, value)
     o = _alloc_outputs(plan, query, outputs, False)
-    ws, ws_bytes = _workspace(plan, workspace, query.device)
-    st = _lib.load().nsa_compress_attention_fwd(
-        plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(o["attention_out"]),
-        _ptr(o["softmax_max"]), _ptr(o["softmax_sum"]), _ptr(ws), ws_bytes,
-        _stream_ptr(query.device, stream))
+    m, _keep = _masks(atten_mask, None)
+    ws, ws_bytes = _workspace(plan, workspace, query.device, m is not None)
+    lib = _lib.load()
+    args = (_ptr(o["attention_out"]), _ptr(o["softmax_max"]), _ptr(o["softmax_sum"]), _ptr(ws),
+            ws_bytes, _stream_ptr(query.device, stream))
+    if m is None:
+        st = lib.nsa_compress_attention_fwd(plan.handle, _ptr(query), _ptr(key), _ptr(value), *args)
+    else:
+        st = lib.nsa_compress_attention_fwd_masked(plan.handle, _ptr(query), _ptr(key), _ptr(value),
+                                                   ctypes.byref(m), *args)
     _lib.check(st)
     return o["attention_out"], o["softmax_max"], o["softmax_sum"]
 
@@ -256,20 +295,28 @@ def nsa_compress_attention_fwd(plan: Plan, query: torch.Tensor, key: torch.Tenso
 def nsa_compress_attention_select(plan: Plan, query: torch.Tensor, key: torch.Tensor,
                                   softmax_max: torch.Tensor, softmax_sum: torch.Tensor,
                                   workspace: Optional[torch.Tensor] = None, return_p_slc: bool = False,
-                                  outputs: Optional[dict] = None, stream=None):
+                                  outputs: Optional[dict] = None, stream=None, atten_mask=None,
+                                  topk_mask=None):
     """Steps 4-7 from the first half's softmax statistics: returns
-    topk_indices (and the importance scores with ``return_p_slc``)."""
+    topk_indices (and the importance scores with ``return_p_slc``).  The
+    atten_mask must be the one the first half was given."""
     _check_qkv(plan, query, key)
     for t, name in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
         _need_tensor(t, name)
         if t.dtype != torch.float32 or tuple(t.shape) != (plan.info["total_q_tokens"], plan.info["head_num"], 8):
             raise ValueError(f"{name} must be float32 [T1, N1, 8]")
     o = _alloc_outputs(plan, query, outputs, return_p_slc)
-    ws, ws_bytes = _workspace(plan, workspace, query.device)
-    st = _lib.load().nsa_compress_attention_select(
-        plan.handle, _ptr(query), _ptr(key), _ptr(softmax_max), _ptr(softmax_sum),
-        _ptr(o["topk_indices"]), _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws), ws_bytes,
-        _stream_ptr(query.device, stream))
+    m, _keep = _masks(atten_mask, topk_mask)
+    ws, ws_bytes = _workspace(plan, workspace, query.device, m is not None)
+    lib = _lib.load()
+    args = (_ptr(softmax_max), _ptr(softmax_sum), _ptr(o["topk_indices"]),
+            _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws), ws_bytes,
+            _stream_ptr(query.device, stream))
+    if m is None:
+        st = lib.nsa_compress_attention_select(plan.handle, _ptr(query), _ptr(key), *args)
+    else:
+        st = lib.nsa_compress_attention_select_masked(plan.handle, _ptr(query), _ptr(key),
+                                                      ctypes.byref(m), *args)
     _lib.check(st)
     return (o["topk_indices"], o["p_slc"]) if return_p_slc else o["topk_indices"]
 
@@ -278,12 +325,8 @@ def compress_attention(query, key, value, scale_value, head_num, compress_block_
                        compress_stride, select_block_size, select_block_count, *,
                        actual_seq_qlen, actual_cmp_seq_kvlen, actual_sel_seq_kvlen,
                        topk_mask=None, atten_mask=None, return_p_slc: bool = False):
-    """Both phases with the argument list of the MindSpore operator.
-    Explicit mask tensors are not built: the causal rules are generated from
-    positions (pass None)."""
-    if topk_mask is not None or atten_mask is not None:
-        raise NotImplementedError("explicit atten_mask / topk_mask tensors are not built; "
-                                  "the causal masks are generated from token positions")
+    """Both phases with the argument list of the MindSpore operator.  With
+    no mask tensors the causal rules are generated from positions."""
     _need_tensor(query, "query")
     _need_tensor(key, "key")
     if query.dim() != 3 or key.dim() != 3 or value.dim() != 3:
@@ -294,6 +337,7 @@ def compress_attention(query, key, value, scale_value, head_num, compress_block_
         int(compress_block_size), int(compress_stride), int(select_block_size),
         int(select_block_count), query.dtype)
     try:
-        return nsa_compress_attention(plan, query, key, value, return_p_slc=return_p_slc)
+        return nsa_compress_attention(plan, query, key, value, return_p_slc=return_p_slc,
+                                      atten_mask=atten_mask, topk_mask=topk_mask)
     finally:
         plan.destroy()

@@ -31,6 +31,9 @@ EXPORTS = (
     "nsa_compress_attention",
     "nsa_compress_attention_fwd",
     "nsa_compress_attention_select",
+    "nsa_compress_attention_masked",
+    "nsa_compress_attention_fwd_masked",
+    "nsa_compress_attention_select_masked",
     "nsa_plan_get_info",
     "nsa_plan_destroy",
     "nsa_status_string",
@@ -52,6 +55,19 @@ class PlanInfo(ctypes.Structure):
         ("select_block_count", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
         ("dtype", ctypes.c_int64),
+        ("masked_workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class Masks(ctypes.Structure):
+    """nsa_masks: device byte matrices (NULL = the positional rule)."""
+    _fields_ = [
+        ("atten_mask", ctypes.c_void_p),
+        ("atten_rows", ctypes.c_int64),
+        ("atten_cols", ctypes.c_int64),
+        ("topk_mask", ctypes.c_void_p),
+        ("topk_rows", ctypes.c_int64),
+        ("topk_cols", ctypes.c_int64),
     ]
 
 
@@ -84,6 +100,13 @@ def load() -> ctypes.CDLL:
     lib.nsa_compress_attention_fwd.restype = I32
     lib.nsa_compress_attention_select.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_compress_attention_select.restype = I32
+    MP = ctypes.POINTER(Masks)
+    lib.nsa_compress_attention_masked.argtypes = [P, P, P, P, MP, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.nsa_compress_attention_masked.restype = I32
+    lib.nsa_compress_attention_fwd_masked.argtypes = [P, P, P, P, MP, P, P, P, P, ctypes.c_size_t, P]
+    lib.nsa_compress_attention_fwd_masked.restype = I32
+    lib.nsa_compress_attention_select_masked.argtypes = [P, P, P, MP, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.nsa_compress_attention_select_masked.restype = I32
     lib.nsa_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.nsa_plan_get_info.restype = I32
     lib.nsa_plan_destroy.argtypes = [P]

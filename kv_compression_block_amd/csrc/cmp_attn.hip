@@ -30,6 +30,10 @@
 //     max is tracked apart for the softmax_max output.
 //   * Tiles that every row of the workgroup sees in full run a mask-free
 //     body; only the last one or two tiles of a workgroup apply the mask.
+//   * With an explicit atten_mask (XM) every tile of the sequence runs the
+//     masked body, which keeps a score iff its entry exists and its bit is
+//     set in the packed mask row of the lane's token; the row's 32-bit word
+//     for the next tile is loaded at the start of each step.
 #include <type_traits>
 
 #include "nsa_device.h"
@@ -88,10 +92,11 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
 // At least three waves per SIMD for D1 = D2 = 128 (168 registers, a few
 // values spilled around the main loop), which the unrolled loop would
 // otherwise exceed; two elsewhere.
-template <typename E, int D1, int D2, int QB, int KT, int W>
+template <typename E, bool XM, int D1, int D2, int QB, int KT, int W>
 __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cmp_attn_fwd(AttnParams p)
 {
     using C = AttnCfg<D1, D2, QB, KT, W>;
+    static_assert(!XM || KT == 32, "one mask word per key tile");
     // Three K and three V slots, each its own LDS object: the compiler then
     // knows which slot every copy and every read touches and inserts no wait
     // for a copy into another slot.
@@ -118,6 +123,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     const int row_wg = rb * C::ROWS;
 
     int nvq[QB];
+    int mrow[QB];    // packed atten_mask row of the lane's token (XM)
     bool vq[QB];
     int64_t grow[QB];
     u32x4 qf[QB][C::NKS];
@@ -129,6 +135,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         const int hh = r - tok * G;
         grow[qb] = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
         nvq[qb] = vq[qb] ? n_visible(tok, p.l, p.d, be.n_cmp) : 0;
+        mrow[qb] = vq[qb] ? tok : 0;
         // Rows past the sequence read the workgroup's first row (always valid);
         // they see no block and are never written.
         const int64_t qsrc = vq[qb] ? grow[qb] : (int64_t)(be.q_off + row_wg / G) * p.N1 + (int64_t)g * G;
@@ -141,8 +148,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         }
     }
     const int last_row = min(row_wg + C::ROWS, rows_total) - 1;
-    const int nv_max = n_visible(last_row / G, p.l, p.d, be.n_cmp);
-    const int nv_min = n_visible(row_wg / G, p.l, p.d, be.n_cmp);
+    const int nv_max = XM ? be.n_cmp : n_visible(last_row / G, p.l, p.d, be.n_cmp);
+    const int nv_min = XM ? 0 : n_visible(row_wg / G, p.l, p.d, be.n_cmp);
     const int n_kt = (nv_max + KT - 1) / KT;
 
     // ---- tile staging ----------------------------------------------------------
@@ -269,12 +276,27 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     // after the P.V of the previous tile has been accumulated.
     float tmaxq[QB], nbias[QB];
     bool growq[QB];
+    uint32_t mword[QB];   // XM: packed mask word of the next tile to mask
+    auto load_mword = [&](const int kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            mword[qb] = p.vis[(int64_t)mrow[qb] * p.vis_words + kt];
+    };
     auto tile_max = [&](const int kt, auto mask_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         auto& s = snxt;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            if constexpr (MASK) {
+            if constexpr (MASK && XM) {
+                // key kt*KT + 8*(r/4) + 4*hf + r%4 is kept iff it exists and
+                // its bit is set
+                const int lim = be.n_cmp - kt * KT - 4 * hf;
+                const uint32_t w = mword[qb] >> (4 * hf);
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    s[qb][0][r] = (8 * (r >> 2) + (r & 3) < lim && ((w >> (8 * (r >> 2) + (r & 3))) & 1u))
+                                      ? s[qb][0][r] : -INFINITY;
+            } else if constexpr (MASK) {
                 // key kt*KT + kb*32 + 8*(r/4) + 4*hf + r%4 is visible iff it is
                 // below nvq: compare the compile-time part against one bound
                 const int lim = nvq[qb] - kt * KT - 4 * hf;
@@ -389,6 +411,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                          uint16_t* k_rd, uint16_t* k_cp, uint16_t* v_rd, uint16_t* v_cp) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
         if constexpr (!LAST) {
+            if constexpr (XM)
+                load_mword(kt + 1);   // before the copies: waited for without them
             load_k(kt + 3, k_cp);
             load_v(kt + 2, v_cp);
             qk(k_rd);
@@ -425,6 +449,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         load_v(1, V1);
         copies_done();
         __syncthreads();
+        if constexpr (XM)
+            load_mword(0);
         qk(K0);
         if (n_full > 0)
             tile_max(0, F{});
@@ -548,12 +574,12 @@ int cmp_attn_rows_per_wg(int d1, int d2)
     return 0;
 }
 
-template <typename E>
+template <typename E, bool XM>
 static hipError_t launch_typed(int d1, int d2, const AttnParams& p, int n_tiles, hipStream_t stream)
 {
 #define X(a, b, q, k, w)                                                                          \
     if (d1 == a && d2 == b) {                                                                  \
-        hipLaunchKernelGGL((k_cmp_attn_fwd<E, a, b, q, k, w>), dim3(n_tiles), dim3(64 * w), 0, stream, p); \
+        hipLaunchKernelGGL((k_cmp_attn_fwd<E, XM, a, b, q, k, w>), dim3(n_tiles), dim3(64 * w), 0, stream, p); \
         return hipGetLastError();                                                              \
     }
     NSA_ATTN_CONFIGS(X)
@@ -566,10 +592,13 @@ hipError_t launch_cmp_attn(int dtype, int d1, int d2, const AttnParams& p, int n
 {
     if (n_tiles <= 0)
         return hipSuccess;
+    const bool xm = p.vis != nullptr;
     if (dtype == ElemBf16::code)
-        return launch_typed<ElemBf16>(d1, d2, p, n_tiles, stream);
+        return xm ? launch_typed<ElemBf16, true>(d1, d2, p, n_tiles, stream)
+                  : launch_typed<ElemBf16, false>(d1, d2, p, n_tiles, stream);
     if (dtype == ElemF16::code)
-        return launch_typed<ElemF16>(d1, d2, p, n_tiles, stream);
+        return xm ? launch_typed<ElemF16, true>(d1, d2, p, n_tiles, stream)
+                  : launch_typed<ElemF16, false>(d1, d2, p, n_tiles, stream);
     return hipErrorInvalidValue;
 }
 

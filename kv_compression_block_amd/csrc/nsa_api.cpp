@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -77,6 +78,9 @@ struct nsa_plan_s {
     int dtype;   // element type of q, k, v and attention_out (nsa_dtype)
     float scale;
     int64_t T1, T2, S_total, S_max;
+    int64_t T_max, ncmp_max;          // longest sequence, most compressed entries
+    int64_t vis_words, cand_words;    // packed mask row lengths (32-bit words)
+    size_t ws_masked_bytes;           // workspace of the calls that take masks
     int log2gp, topk_waves, topk_kbufs, sb;
     size_t topk_lds;
     int64_t tiles_a, tiles_c;
@@ -303,7 +307,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->sb = sb;
     plan->topk_lds = lds;
     plan->table.resize((size_t)batch);
-    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, S_total = 0;
+    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, S_total = 0, T_max = 0, ncmp_max = 0;
     const int64_t rows_c = (int64_t)waves * 64;
     const int64_t rows_a = nsa::cmp_attn_rows_per_wg((int)d1, (int)d2);
     for (int64_t b = 0; b < batch; ++b) {
@@ -324,6 +328,8 @@ nsa_status nsa_compress_attention_get_workspace(
         q_off += T;
         c_off += clen[(size_t)b];
         S_total += slen[(size_t)b];
+        T_max = std::max(T_max, T);
+        ncmp_max = std::max(ncmp_max, clen[(size_t)b]);
     }
     if (ta > INT32_MAX || tc > INT32_MAX || q_off * head_num * 8 > ((int64_t)1 << 62)) {
         delete plan;
@@ -335,6 +341,13 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->tiles_a = ta;
     plan->tiles_c = tc;
     plan->ws_bytes = ((size_t)batch * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
+    plan->T_max = T_max;
+    plan->ncmp_max = ncmp_max;
+    plan->vis_words = std::max<int64_t>(1, (ncmp_max + 31) / 32);
+    plan->cand_words = std::max<int64_t>(1, (S_max + 31) / 32);
+    const size_t vis_bytes = ((size_t)T_max * (size_t)plan->vis_words * 4 + 255) / 256 * 256;
+    const size_t cand_bytes = ((size_t)T_max * (size_t)plan->cand_words * 4 + 255) / 256 * 256;
+    plan->ws_masked_bytes = plan->ws_bytes + vis_bytes + cand_bytes;
     *workspace_bytes = plan->ws_bytes;
     *plan_out = plan;
     return ok();
@@ -356,6 +369,7 @@ nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info)
     info->select_block_count = plan->count;
     info->workspace_bytes = plan->ws_bytes;
     info->dtype = plan->dtype;
+    info->masked_workspace_bytes = plan->ws_masked_bytes;
     return ok();
 }
 
@@ -393,7 +407,7 @@ uint32_t q_sign(const nsa_plan_s* plan) { return plan->scale < 0.f ? 0x80008000u
 
 nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const void* value,
                       void* attention_out, float* softmax_max, float* softmax_sum, void* workspace,
-                      hipStream_t s)
+                      hipStream_t s, const uint32_t* vis = nullptr)
 {
     const float abs_scale = std::fabs(plan->scale);
     const float c = exp2_scale(plan);
@@ -419,6 +433,8 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
     // the running max moves only when a score beats it by more than 8 in base 2
     a.thr = std::fmin(8.0f / a.c, 3.0e38f);
     a.qsign = q_sign(plan);
+    a.vis = vis;
+    a.vis_words = (int)plan->vis_words;
     hipError_t e = nsa::launch_cmp_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
@@ -427,7 +443,8 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
 
 nsa_status launch_select(nsa_plan plan, const void* query, const void* key, const float* softmax_max,
                          const float* softmax_sum, int32_t* topk_indices, float* p_slc_debug,
-                         void* workspace, hipStream_t s)
+                         void* workspace, hipStream_t s, const uint32_t* vis = nullptr,
+                         const uint32_t* cand = nullptr)
 {
     nsa::TopkParams t;
     std::memset(&t, 0, sizeof t);
@@ -465,9 +482,60 @@ nsa_status launch_select(nsa_plan plan, const void* query, const void* key, cons
     t.npl = plan->sb / 64;
     t.waves = plan->topk_waves;
     t.kbufs = plan->topk_kbufs;
+    t.vis = vis;
+    t.vis_words = (int)plan->vis_words;
+    t.cand = cand;
+    t.cand_words = (int)plan->cand_words;
     hipError_t e = nsa::launch_slc_topk(plan->dtype, (int)plan->D1, plan->log2gp, t, (int)plan->tiles_c, plan->topk_lds, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "top-k launch failed: %s", hipGetErrorString(e));
+    return NSA_OK;
+}
+
+// Validates the masks a call uses and packs them into the workspace after
+// the sequence table: *vis / *cand point at the packed rows, or stay NULL
+// where the positional rule applies.
+nsa_status prepare_masks(nsa_plan plan, const nsa_masks* masks, bool use_atten, bool use_topk,
+                         void* workspace, size_t workspace_bytes, hipStream_t s,
+                         const uint32_t** vis, const uint32_t** cand)
+{
+    *vis = nullptr;
+    *cand = nullptr;
+    if (!masks)
+        return NSA_OK;
+    const bool a = use_atten && masks->atten_mask;
+    const bool t = use_topk && masks->topk_mask;
+    if (a && (masks->atten_rows < plan->T_max || masks->atten_cols < plan->ncmp_max))
+        return fail(NSA_ERR_SHAPE, "atten_mask is [%lld, %lld]; it needs at least [%lld, %lld] "
+                    "(longest sequence, most compressed entries)", (long long)masks->atten_rows,
+                    (long long)masks->atten_cols, (long long)plan->T_max, (long long)plan->ncmp_max);
+    if (t && (masks->topk_rows < plan->T_max || masks->topk_cols < plan->S_max))
+        return fail(NSA_ERR_SHAPE, "topk_mask is [%lld, %lld]; it needs at least [%lld, %lld] "
+                    "(longest sequence, most select blocks)", (long long)masks->topk_rows,
+                    (long long)masks->topk_cols, (long long)plan->T_max, (long long)plan->S_max);
+    if (!a && !t)
+        return NSA_OK;
+    if (workspace_bytes < plan->ws_masked_bytes)
+        return fail(NSA_ERR_WORKSPACE, "calls with masks need %zu workspace bytes, %zu given",
+                    plan->ws_masked_bytes, workspace_bytes);
+    uint32_t* vis_ws = (uint32_t*)((char*)workspace + plan->ws_bytes);
+    uint32_t* cand_ws = vis_ws + ((size_t)plan->T_max * (size_t)plan->vis_words * 4 + 255) / 256 * 64;
+    if (a) {
+        nsa::MaskPackParams mp{(const uint8_t*)masks->atten_mask, masks->atten_cols, vis_ws,
+                               (int)plan->T_max, (int)plan->vis_words};
+        hipError_t e = nsa::launch_pack_mask(mp, s);
+        if (e != hipSuccess)
+            return fail(NSA_ERR_HIP, "mask packing failed: %s", hipGetErrorString(e));
+        *vis = vis_ws;
+    }
+    if (t) {
+        nsa::MaskPackParams mp{(const uint8_t*)masks->topk_mask, masks->topk_cols, cand_ws,
+                               (int)plan->T_max, (int)plan->cand_words};
+        hipError_t e = nsa::launch_pack_mask(mp, s);
+        if (e != hipSuccess)
+            return fail(NSA_ERR_HIP, "mask packing failed: %s", hipGetErrorString(e));
+        *cand = cand_ws;
+    }
     return NSA_OK;
 }
 
@@ -543,6 +611,94 @@ nsa_status nsa_compress_attention(nsa_plan plan, const void* query, const void* 
     if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s)) != NSA_OK)
         return st;
     if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s)) != NSA_OK)
+        return st;
+    return ok();
+}
+
+nsa_status nsa_compress_attention_fwd_masked(nsa_plan plan, const void* query, const void* key,
+                                             const void* value, const nsa_masks* masks,
+                                             void* attention_out, float* softmax_max,
+                                             float* softmax_sum, void* workspace,
+                                             size_t workspace_bytes, void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !attention_out || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query and the three outputs must not be NULL");
+    if (plan->T2 > 0 && (!key || !value))
+        return fail(NSA_ERR_NULLPTR, "key and value must not be NULL");
+    nsa_status st = check_exec(plan, workspace, workspace_bytes,
+                               {query, key, value, attention_out, softmax_max, softmax_sum, workspace}, {});
+    if (st != NSA_OK || plan->T1 == 0)
+        return st == NSA_OK ? ok() : st;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t *vis = nullptr, *cand = nullptr;
+    if ((st = prepare_masks(plan, masks, true, false, workspace, workspace_bytes, s, &vis, &cand)) != NSA_OK)
+        return st;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s,
+                         vis)) != NSA_OK)
+        return st;
+    return ok();
+}
+
+nsa_status nsa_compress_attention_select_masked(nsa_plan plan, const void* query, const void* key,
+                                                const nsa_masks* masks, const float* softmax_max,
+                                                const float* softmax_sum, int32_t* topk_indices,
+                                                float* p_slc_debug, void* workspace,
+                                                size_t workspace_bytes, void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !topk_indices || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query, softmax_max, softmax_sum and topk_indices must not be NULL");
+    if (plan->T2 > 0 && !key)
+        return fail(NSA_ERR_NULLPTR, "key must not be NULL");
+    nsa_status st = check_exec(plan, workspace, workspace_bytes, {query, key, softmax_max, softmax_sum, workspace},
+                               {topk_indices, p_slc_debug});
+    if (st != NSA_OK || plan->T1 == 0)
+        return st == NSA_OK ? ok() : st;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t *vis = nullptr, *cand = nullptr;
+    if ((st = prepare_masks(plan, masks, true, true, workspace, workspace_bytes, s, &vis, &cand)) != NSA_OK)
+        return st;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s,
+                            vis, cand)) != NSA_OK)
+        return st;
+    return ok();
+}
+
+nsa_status nsa_compress_attention_masked(nsa_plan plan, const void* query, const void* key,
+                                         const void* value, const nsa_masks* masks,
+                                         void* attention_out, int32_t* topk_indices,
+                                         float* softmax_max, float* softmax_sum, float* p_slc_debug,
+                                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !attention_out || !topk_indices || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query and the four outputs must not be NULL");
+    if (plan->T2 > 0 && (!key || !value))
+        return fail(NSA_ERR_NULLPTR, "key and value must not be NULL");
+    nsa_status st = check_exec(plan, workspace, workspace_bytes,
+                               {query, key, value, attention_out, softmax_max, softmax_sum, workspace},
+                               {topk_indices, p_slc_debug});
+    if (st != NSA_OK || plan->T1 == 0)
+        return st == NSA_OK ? ok() : st;
+    hipStream_t s = (hipStream_t)stream;
+    const uint32_t *vis = nullptr, *cand = nullptr;
+    if ((st = prepare_masks(plan, masks, true, true, workspace, workspace_bytes, s, &vis, &cand)) != NSA_OK)
+        return st;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s,
+                         vis)) != NSA_OK)
+        return st;
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s,
+                            vis, cand)) != NSA_OK)
         return st;
     return ok();
 }

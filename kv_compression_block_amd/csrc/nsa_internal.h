@@ -43,6 +43,18 @@ struct CompressParams {
 // dtype: 0 = bfloat16, 1 = float16 (the public enum's values).
 hipError_t launch_compress(int dtype, const CompressParams& p, hipStream_t stream);
 
+// ---- explicit masks ---------------------------------------------------------
+// A [rows, cols] byte matrix (non-zero = masked out) becomes a bit matrix of
+// kept pairs: word w of row t holds columns 32w .. 32w+31, bit k set iff
+// column 32w + k < cols and its byte is zero.
+struct MaskPackParams {
+    const uint8_t* src;   // [src_rows, src_cols] bytes
+    int64_t src_cols;
+    uint32_t* dst;        // [rows, words]
+    int rows, words;
+};
+hipError_t launch_pack_mask(const MaskPackParams& p, hipStream_t stream);
+
 // ---- attention kernels ------------------------------------------------------
 struct AttnParams {
     const uint16_t* q;    // [T1, N1, D1]
@@ -58,6 +70,8 @@ struct AttnParams {
     float abs_scale;      // |scale|: raw score -> natural-unit score
     float thr;            // running-max slack before rescaling, raw-score units
     uint32_t qsign;       // 0x80008000 when scale < 0 (q negated), else 0
+    const uint32_t* vis;  // NULL (positional rule) or packed atten_mask [T_max, vis_words]
+    int vis_words;
 };
 
 // Compressed entries per key tile of the importance/top-k kernel: 32 keeps
@@ -90,6 +104,10 @@ struct TopkParams {
     int npl;              // candidates per lane in top-k, sb / 64
     int waves;            // waves per workgroup
     int kbufs;            // K tile buffers in LDS (2 = double buffered)
+    const uint32_t* vis;  // NULL (positional rule) or packed atten_mask [T_max, vis_words]
+    int vis_words;
+    const uint32_t* cand; // NULL (positional rule) or packed topk_mask [T_max, cand_words]
+    int cand_words;
 };
 
 constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)

@@ -34,6 +34,11 @@
 //     against the others.  When more than 64 reach the bound (heavy ties),
 //     a radix select over all candidates finds the k-th largest score and
 //     the picks above it plus the lowest-index ties are ranked the same way.
+//   * Explicit masks: with an atten_mask (XM) every key tile of the sequence
+//     runs the masked body, where P is kept iff its entry exists and its bit
+//     is set in the packed mask row of its token (the wave's mask words of a
+//     tile are loaded before the tile's MFMAs and passed through LDS); a
+//     topk_mask replaces the candidate rule j*l' <= t by the packed bits.
 //   * Deterministic: every sum has a fixed order; no atomics.
 #include <type_traits>
 
@@ -54,7 +59,7 @@ __device__ __forceinline__ void wave_lds_sync()
 
 // Three waves per SIMD where the registers allow it (D1 = 128 with groups
 // of 16 or more), two elsewhere.
-template <typename E, int D1, int LOG2GP>
+template <typename E, bool XM, int D1, int LOG2GP>
 __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc_topk(TopkParams p)
 {
     constexpr int GP = 1 << LOG2GP;
@@ -138,12 +143,13 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
             bias[rr][r] = __shfl(bias_lane, rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3));
 
     const int tok_last = min(tok_wg + ((waves * 64) >> LOG2GP), be.T) - 1;
-    const int nv_max = n_visible(tok_last, p.l, p.d, be.n_cmp);
-    const int nv_min = n_visible(tok_wg, p.l, p.d, be.n_cmp);
+    const int nv_max = XM ? be.n_cmp : n_visible(tok_last, p.l, p.d, be.n_cmp);
+    const int nv_min = XM ? 0 : n_visible(tok_wg, p.l, p.d, be.n_cmp);
     const int n_kt = (nv_max + KT - 1) / KT;
 
     float* my_ring = ring + wave * TOKW * RING;
     float* my_bins = bins + wave * TOKW * p.sb;
+    uint32_t* my_stg = stg + wave * 128;     // XM mask words in the key loop; top-k staging after it
     for (int x = lane; x < TOKW * RING; x += 64)
         my_ring[x] = 0.f;
 
@@ -226,6 +232,23 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     auto key_tile = [&](const int kt, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int buf = (nbuf == 2) ? (kt & 1) : 0;
+        // XM: lane i < TOKW * NKB fetches the mask word of token i / NKB for
+        // 32-entry block i % NKB of this tile (issued before the K loads, so
+        // waiting for it does not wait for them).
+        constexpr int MWPL = (TOKW * NKB + 63) / 64;   // mask words per lane
+        uint32_t mw_lane[MWPL];
+        if constexpr (XM) {
+#pragma unroll
+            for (int m = 0; m < MWPL; ++m) {
+                const int i = lane + 64 * m;
+                const int word = kt * NKB + i % NKB;   // past the row: entries >= n_cmp
+                mw_lane[m] = 0;
+                if (i < TOKW * NKB && word < p.vis_words) {
+                    const int tok = min(tok_w + i / NKB, be.T - 1);
+                    mw_lane[m] = p.vis[(int64_t)tok * p.vis_words + word];
+                }
+            }
+        }
         if (full_wg && kt + 1 < n_kt)
             load_tile(kt + 1);
 
@@ -253,6 +276,13 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
             }
         }
         __builtin_amdgcn_s_setprio(0);
+        if constexpr (XM) {
+#pragma unroll
+            for (int m = 0; m < MWPL; ++m)
+                if (lane + 64 * m < TOKW * NKB)
+                    my_stg[lane + 64 * m] = mw_lane[m];
+            wave_lds_sync();
+        }
 
         // P, masked on the last tiles, summed over the heads of each token.
         float acc[TOKW][NKB];
@@ -268,7 +298,12 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pv = fast_exp2(fmaf(s[rr][kb][r], c, -bias[rr][r]));
-                    if constexpr (MASK) {
+                    if constexpr (MASK && XM) {
+                        const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                        const uint32_t w = my_stg[(pr >> LOG2GP) * NKB + kb];
+                        // kept iff the entry exists and its mask bit is set
+                        pv = (key < be.n_cmp && ((w >> l32) & 1u)) ? pv : 0.f;
+                    } else if constexpr (MASK) {
                         const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
                         const int tok = tok_w + (pr >> LOG2GP);
                         // visible iff key*d + l - 1 <= tok
@@ -333,7 +368,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     {
         const int keys_done = n_kt * KT;
         const int jlo = (keys_done + R - 1) / R;
-        const int j_end = p.pslc ? be.S_sel : min(be.S_sel, (tok_w + TOKW - 1) / p.lsel + 1);
+        const int j_end = (p.pslc || p.cand) ? be.S_sel : min(be.S_sel, (tok_w + TOKW - 1) / p.lsel + 1);
         for (int j = jlo + lane; j < j_end; j += 64)
             for (int tw = 0; tw < TOKW; ++tw)
                 my_bins[tw * p.sb + j] = stencil(my_ring + tw * RING, j, keys_done);
@@ -341,7 +376,6 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     wave_lds_sync();
 
     // ---- top-k per (token, KV head), wave-local ----------------------------------
-    uint32_t* my_stg = stg + wave * 128;     // staged picks: score bits, then indices
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int tw = 0; tw < TOKW; ++tw) {
         const int tok = tok_w + tw;
@@ -354,16 +388,38 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
             for (int j = lane; j < p.s_stride; j += 64)
                 dst[j] = (j < be.S_sel) ? brow[j] : 0.f;
         }
-        const int nvalid = min(tok / p.lsel + 1, be.S_sel);
+        // Candidates: j with j*l' <= t (a prefix of the select blocks), or
+        // the set bits of the token's packed topk_mask row.  Bit i of cm:
+        // block lane + 64 i is a candidate.
+        const int range = p.cand ? be.S_sel : min(tok / p.lsel + 1, be.S_sel);
+        const int nch = (range + 63) >> 6;    // 64-block chunks of this row
+        uint32_t cm = 0;
+        int nvalid = 0;                       // number of candidates
+        if (p.cand) {
+            const uint32_t* crow = p.cand + (int64_t)tok * p.cand_words;
+#pragma unroll
+            for (int i = 0; i < kTopkMaxNpl; ++i) {
+                if (i < nch) {
+                    const int j = lane + 64 * i;
+                    const bool c_i = j < range && ((crow[j >> 5] >> (j & 31)) & 1u);
+                    cm |= (uint32_t)c_i << i;
+                    nvalid += __popcll(__ballot(c_i));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kTopkMaxNpl; ++i)
+                cm |= (uint32_t)(lane + 64 * i < range) << i;
+            nvalid = range;
+        }
         const int kk = min(p.count, nvalid);
-        const int nch = (nvalid + 63) >> 6;   // 64-candidate chunks of this row
         // Candidates as float bits; non-candidates hold 0 and never reach a
         // threshold >= 1 below.
         uint32_t key[kTopkMaxNpl];
 #pragma unroll
         for (int i = 0; i < kTopkMaxNpl; ++i) {
             const int j = lane + 64 * i;
-            key[i] = (i < nch && j < nvalid) ? __float_as_uint(brow[j]) : 0u;
+            key[i] = (i < nch && ((cm >> i) & 1u)) ? __float_as_uint(brow[j]) : 0u;
         }
         int32_t* trow = p.topk + (tg * p.N2 + g) * p.count;
         // Lower bound first: the kk-th largest of the per-lane maxima.  The
@@ -391,7 +447,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
 #pragma unroll
         for (int i = 0; i < kTopkMaxNpl; ++i)
             if (i < nch)
-                ncand += __popcll(__ballot(lane + 64 * i < nvalid && key[i] >= tau0));
+                ncand += __popcll(__ballot(((cm >> i) & 1u) && key[i] >= tau0));
         if (ncand <= 64) {
             // Stage the candidates (score bits at [0, 64), indices at [64, 128)),
             // then each ranks itself against all of them by (score desc,
@@ -400,7 +456,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
 #pragma unroll
             for (int i = 0; i < kTopkMaxNpl; ++i) {
                 if (i < nch) {
-                    const bool sel = lane + 64 * i < nvalid && key[i] >= tau0;
+                    const bool sel = ((cm >> i) & 1u) && key[i] >= tau0;
                     const uint64_t bs = __ballot(sel);
                     if (sel) {
                         const int at = pos + __popcll(bs & lt_mask);
@@ -459,7 +515,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
 #pragma unroll
             for (int i = 0; i < kTopkMaxNpl; ++i) {
                 if (i < nch) {
-                    const bool cand_i = lane + 64 * i < nvalid;
+                    const bool cand_i = (cm >> i) & 1u;
                     const bool gt = cand_i && key[i] > tau;
                     const bool eq = cand_i && key[i] == tau;
                     const uint64_t bg = __ballot(gt);
@@ -501,10 +557,10 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     }
 }
 
-template <typename E, int D1, int LOG2GP>
+template <typename E, bool XM, int D1, int LOG2GP>
 static hipError_t launch_t(const TopkParams& p, int n_tiles, size_t lds, hipStream_t stream)
 {
-    auto kern = k_slc_topk<E, D1, LOG2GP>;
+    auto kern = k_slc_topk<E, XM, D1, LOG2GP>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess)
@@ -514,28 +570,28 @@ static hipError_t launch_t(const TopkParams& p, int n_tiles, size_t lds, hipStre
     return hipGetLastError();
 }
 
-template <typename E, int D1>
+template <typename E, bool XM, int D1>
 static hipError_t launch_d(int log2gp, const TopkParams& p, int n_tiles, size_t lds, hipStream_t stream)
 {
     switch (log2gp) {
-    case 0: return launch_t<E, D1, 0>(p, n_tiles, lds, stream);
-    case 1: return launch_t<E, D1, 1>(p, n_tiles, lds, stream);
-    case 2: return launch_t<E, D1, 2>(p, n_tiles, lds, stream);
-    case 3: return launch_t<E, D1, 3>(p, n_tiles, lds, stream);
-    case 4: return launch_t<E, D1, 4>(p, n_tiles, lds, stream);
-    case 5: return launch_t<E, D1, 5>(p, n_tiles, lds, stream);
-    case 6: return launch_t<E, D1, 6>(p, n_tiles, lds, stream);
+    case 0: return launch_t<E, XM, D1, 0>(p, n_tiles, lds, stream);
+    case 1: return launch_t<E, XM, D1, 1>(p, n_tiles, lds, stream);
+    case 2: return launch_t<E, XM, D1, 2>(p, n_tiles, lds, stream);
+    case 3: return launch_t<E, XM, D1, 3>(p, n_tiles, lds, stream);
+    case 4: return launch_t<E, XM, D1, 4>(p, n_tiles, lds, stream);
+    case 5: return launch_t<E, XM, D1, 5>(p, n_tiles, lds, stream);
+    case 6: return launch_t<E, XM, D1, 6>(p, n_tiles, lds, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename E>
+template <typename E, bool XM>
 static hipError_t launch_e(int d1, int log2gp, const TopkParams& p, int n_tiles, size_t lds,
                            hipStream_t stream)
 {
-    if (d1 == 64) return launch_d<E, 64>(log2gp, p, n_tiles, lds, stream);
-    if (d1 == 128) return launch_d<E, 128>(log2gp, p, n_tiles, lds, stream);
-    if (d1 == 192) return launch_d<E, 192>(log2gp, p, n_tiles, lds, stream);
+    if (d1 == 64) return launch_d<E, XM, 64>(log2gp, p, n_tiles, lds, stream);
+    if (d1 == 128) return launch_d<E, XM, 128>(log2gp, p, n_tiles, lds, stream);
+    if (d1 == 192) return launch_d<E, XM, 192>(log2gp, p, n_tiles, lds, stream);
     return hipErrorInvalidValue;
 }
 
@@ -561,10 +617,13 @@ hipError_t launch_slc_topk(int dtype, int d1, int log2gp, const TopkParams& p, i
 {
     if (n_tiles <= 0)
         return hipSuccess;
+    const bool xm = p.vis != nullptr;
     if (dtype == ElemBf16::code)
-        return launch_e<ElemBf16>(d1, log2gp, p, n_tiles, lds, stream);
+        return xm ? launch_e<ElemBf16, true>(d1, log2gp, p, n_tiles, lds, stream)
+                  : launch_e<ElemBf16, false>(d1, log2gp, p, n_tiles, lds, stream);
     if (dtype == ElemF16::code)
-        return launch_e<ElemF16>(d1, log2gp, p, n_tiles, lds, stream);
+        return xm ? launch_e<ElemF16, true>(d1, log2gp, p, n_tiles, lds, stream)
+                  : launch_e<ElemF16, false>(d1, log2gp, p, n_tiles, lds, stream);
     return hipErrorInvalidValue;
 }
 

@@ -145,20 +145,28 @@ def token_meta(wl, tokens):
     return out
 
 
-def assert_topk(wl, tokens, g_idx: np.ndarray, r_idx: np.ndarray, r_pslc: np.ndarray, tie_rel: float = 1e-4):
-    """g_idx/r_idx: [n, N2, count]; r_pslc: oracle scores [n, N2, S]."""
+def assert_topk(wl, tokens, g_idx: np.ndarray, r_idx: np.ndarray, r_pslc: np.ndarray, tie_rel: float = 1e-4,
+                topk_mask=None):
+    """g_idx/r_idx: [n, N2, count]; r_pslc: oracle scores [n, N2, S].
+    Candidates: j*l' <= t, or the unmasked j < S of row t of ``topk_mask``."""
     meta = token_meta(wl, tokens)
     n_diff = 0
     for k, (t, S) in enumerate(meta):
-        nvalid = min(t // wl.lsel + 1, S)
+        if topk_mask is None:
+            cands = set(range(min(t // wl.lsel + 1, S)))
+        else:
+            cands = set(int(j) for j in np.flatnonzero(~np.asarray(topk_mask[t, :S], dtype=bool)))
+        nvalid = len(cands)
         kk = min(wl.count, nvalid)
         for g in range(wl.N2):
             gi = g_idx[k, g]
             ri = r_idx[k, g]
             assert np.all(gi[kk:] == -1), (tokens[k], g, gi)
             picks = gi[:kk]
-            assert np.all((picks >= 0) & (picks < nvalid)), (tokens[k], g, gi)
+            assert all(int(x) in cands for x in picks), (tokens[k], g, gi)
             assert len(set(picks.tolist())) == kk, (tokens[k], g, gi)
+            if kk == 0:
+                continue
             ref_set = set(ri[:kk].tolist())
             scores = r_pslc[k, g].astype(np.float32).astype(np.float64)
             kth = min(scores[j] for j in ref_set)

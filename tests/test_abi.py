@@ -169,3 +169,39 @@ def test_status_strings_and_python_exception_mapping():
                                                     32, 16, 64, 16)
     assert plan.info["total_q_tokens"] == 300 and plan.workspace_bytes > 0
     plan.destroy()
+
+
+def test_masked_calls_reject_before_touching_the_device():
+    """Masks smaller than the plan's longest sequence / largest counts give
+    NSA_ERR_SHAPE, a workspace below masked_workspace_bytes gives
+    NSA_ERR_WORKSPACE; both before any launch."""
+    st, ws, plan = _ws(**_good())          # sequences of 100 and 200 tokens
+    lib = _lib.load()
+    info = _lib.PlanInfo()
+    assert lib.nsa_plan_get_info(plan, ctypes.byref(info)) == 0
+    assert info.masked_workspace_bytes > info.workspace_bytes
+    fake = ctypes.c_void_p(0x1000)
+    big = info.masked_workspace_bytes
+
+    def call(m, wsb, fn="nsa_compress_attention_masked"):
+        if fn == "nsa_compress_attention_masked":
+            return lib.nsa_compress_attention_masked(plan, fake, fake, fake, ctypes.byref(m), fake, fake,
+                                                     fake, fake, None, fake, wsb, None)
+        if fn == "nsa_compress_attention_fwd_masked":
+            return lib.nsa_compress_attention_fwd_masked(plan, fake, fake, fake, ctypes.byref(m), fake,
+                                                         fake, fake, fake, wsb, None)
+        return lib.nsa_compress_attention_select_masked(plan, fake, fake, ctypes.byref(m), fake, fake,
+                                                        fake, None, fake, wsb, None)
+
+    short_rows = _lib.Masks(0x2000, 199, 11, None, 0, 0)     # needs 200 rows, 11 columns
+    short_cols = _lib.Masks(0x2000, 200, 10, None, 0, 0)
+    topk_short = _lib.Masks(None, 0, 0, 0x3000, 200, 3)       # needs 4 select blocks
+    good = _lib.Masks(0x2000, 200, 11, 0x3000, 200, 4)
+    for fn in ("nsa_compress_attention_masked", "nsa_compress_attention_fwd_masked",
+               "nsa_compress_attention_select_masked"):
+        assert call(short_rows, big, fn) == _lib.NSA_ERR_SHAPE, lib.nsa_last_error()
+        assert call(short_cols, big, fn) == _lib.NSA_ERR_SHAPE
+        assert call(good, big - 1, fn) == _lib.NSA_ERR_WORKSPACE
+    assert call(topk_short, big) == _lib.NSA_ERR_SHAPE
+    assert call(topk_short, big, "nsa_compress_attention_select_masked") == _lib.NSA_ERR_SHAPE
+    lib.nsa_plan_destroy(plan)

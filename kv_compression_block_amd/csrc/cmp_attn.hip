@@ -30,7 +30,9 @@
 //     max is tracked apart for the softmax_max output.
 //   * Tiles that every row of the workgroup sees in full run a mask-free
 //     body; only the last one or two tiles of a workgroup apply the mask.
-//   * With an explicit atten_mask (XM) every tile of the sequence runs the
+//   * With an explicit atten_mask (XM) the workgroup visits the key tiles
+//     between the first and the last mask word that keeps anything for one
+//     of its tokens (per-row spans from the packing pass), all through the
 //     masked body, which keeps a score iff its entry exists and its bit is
 //     set in the packed mask row of the lane's token; the row's 32-bit word
 //     for the next tile is loaded at the start of each step.
@@ -150,7 +152,26 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     const int last_row = min(row_wg + C::ROWS, rows_total) - 1;
     const int nv_max = XM ? be.n_cmp : n_visible(last_row / G, p.l, p.d, be.n_cmp);
     const int nv_min = XM ? 0 : n_visible(row_wg / G, p.l, p.d, be.n_cmp);
-    const int n_kt = (nv_max + KT - 1) / KT;
+    // XM: tiles [kt0, kt0 + n_kt) hold every kept entry of the workgroup's
+    // tokens (wave-uniform: every wave reduces over all of them).  Below,
+    // kt counts tiles from kt0.
+    int kt0 = 0, n_kt = (nv_max + KT - 1) / KT;
+    if constexpr (XM) {
+        int lo = 0x7FFFFFFF, hi = 0;
+        for (int tt = row_wg / G + lane; tt <= last_row / G; tt += 64) {
+            const int2 sp = p.vis_span[tt];
+            lo = min(lo, sp.x);
+            hi = max(hi, sp.y);
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            lo = min(lo, __shfl_xor(lo, m));
+            hi = max(hi, __shfl_xor(hi, m));
+        }
+        hi = min(hi, n_kt);
+        kt0 = __builtin_amdgcn_readfirstlane(lo < hi ? lo : 0);
+        n_kt = __builtin_amdgcn_readfirstlane(lo < hi ? hi - lo : 0);
+    }
 
     // ---- tile staging ----------------------------------------------------------
     const int64_t kv_stride1 = (int64_t)p.N2 * D1;
@@ -184,6 +205,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         return nvalid > 0 ? (uint32_t)(nvalid - 1) * stride_b + (uint32_t)row_bytes : 0u;
     };
     auto load_k = [&](int kt, uint16_t* dst) __attribute__((always_inline)) {
+        kt += kt0;
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)kt * KT * kv_stride1, tile_bytes(kt, kst_b, D1 * 2));
 #pragma unroll
         for (int j = 0; j < C::KIPW; ++j)
@@ -191,6 +213,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                 copy16_to_lds(kr, dst + (j * W + wave) * 512, kdo[j]);
     };
     auto load_v = [&](int kt, uint16_t* dst) __attribute__((always_inline)) {
+        kt += kt0;
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)kt * KT * kv_stride2, tile_bytes(kt, vst_b, D2 * 2));
 #pragma unroll
         for (int j = 0; j < C::VIPW; ++j)
@@ -280,7 +303,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     auto load_mword = [&](const int kt) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-            mword[qb] = p.vis[(int64_t)mrow[qb] * p.vis_words + kt];
+            mword[qb] = p.vis[(int64_t)mrow[qb] * p.vis_words + kt0 + kt];
     };
     auto tile_max = [&](const int kt, auto mask_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
@@ -289,13 +312,17 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         for (int qb = 0; qb < QB; ++qb) {
             if constexpr (MASK && XM) {
                 // key kt*KT + 8*(r/4) + 4*hf + r%4 is kept iff it exists and
-                // its bit is set
-                const int lim = be.n_cmp - kt * KT - 4 * hf;
-                const uint32_t w = mword[qb] >> (4 * hf);
+                // its bit is set; a wave whose rows keep the whole tile skips
+                // the selects
+                const int lim = be.n_cmp - (kt0 + kt) * KT - 4 * hf;
+                const bool part = mword[qb] != 0xFFFFFFFFu || (kt0 + kt + 1) * KT > be.n_cmp;
+                if (__ballot(part) != 0) {
+                    const uint32_t w = mword[qb] >> (4 * hf);
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    s[qb][0][r] = (8 * (r >> 2) + (r & 3) < lim && ((w >> (8 * (r >> 2) + (r & 3))) & 1u))
-                                      ? s[qb][0][r] : -INFINITY;
+                    for (int r = 0; r < 16; ++r)
+                        s[qb][0][r] = (8 * (r >> 2) + (r & 3) < lim && ((w >> (8 * (r >> 2) + (r & 3))) & 1u))
+                                          ? s[qb][0][r] : -INFINITY;
+                }
             } else if constexpr (MASK) {
                 // key kt*KT + kb*32 + 8*(r/4) + 4*hf + r%4 is visible iff it is
                 // below nvq: compare the compile-time part against one bound

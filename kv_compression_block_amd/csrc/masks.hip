@@ -5,6 +5,8 @@
 // One wave covers 64 consecutive columns of one row: each lane loads one
 // byte (64 contiguous bytes per wave), and one ballot gives the two 32-bit
 // words of kept pairs (bit set iff the byte is zero and the column exists).
+// A second pass records per row the span of words that keep anything, from
+// which the kernels bound the key tiles a workgroup has to visit.
 #include "nsa_device.h"
 
 namespace nsa {
@@ -31,6 +33,23 @@ __global__ __launch_bounds__(kPackThreads) void k_pack_mask(MaskPackParams p)
         p.dst[(int64_t)t * p.words + w] = (uint32_t)(lane ? bits >> 32 : bits);
 }
 
+// One thread per row: the first and one past the last non-zero word.
+__global__ __launch_bounds__(kPackThreads) void k_mask_span(MaskPackParams p)
+{
+    const int t = blockIdx.x * kPackThreads + threadIdx.x;
+    if (t >= p.rows)
+        return;
+    const uint32_t* row = p.dst + (int64_t)t * p.words;
+    int lo = p.words, hi = 0;
+    for (int w = 0; w < p.words; ++w) {
+        if (row[w] != 0u) {
+            lo = min(lo, w);
+            hi = w + 1;
+        }
+    }
+    p.span[t] = make_int2(lo, hi);
+}
+
 hipError_t launch_pack_mask(const MaskPackParams& p, hipStream_t stream)
 {
     if (p.rows <= 0 || p.words <= 0)
@@ -40,6 +59,13 @@ hipError_t launch_pack_mask(const MaskPackParams& p, hipStream_t stream)
     if (blocks > INT32_MAX)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_pack_mask, dim3((unsigned)blocks), dim3(kPackThreads), 0, stream, p);
+    if (p.span) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(k_mask_span, dim3((unsigned)((p.rows + kPackThreads - 1) / kPackThreads)),
+                           dim3(kPackThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

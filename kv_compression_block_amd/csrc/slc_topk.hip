@@ -34,9 +34,11 @@
 //     against the others.  When more than 64 reach the bound (heavy ties),
 //     a radix select over all candidates finds the k-th largest score and
 //     the picks above it plus the lowest-index ties are ranked the same way.
-//   * Explicit masks: with an atten_mask (XM) every key tile of the sequence
-//     runs the masked body, where P is kept iff its entry exists and its bit
-//     is set in the packed mask row of its token (the wave's mask words of a
+//   * Explicit masks: with an atten_mask (XM) the workgroup visits the key
+//     tiles between the first and the last mask word that keeps anything
+//     for one of its tokens, all through the masked body, where P is kept
+//     iff its entry exists and its bit is set in the packed mask row of its
+//     token (the wave's mask words of a
 //     tile are loaded before the tile's MFMAs and passed through LDS); a
 //     topk_mask replaces the candidate rule j*l' <= t by the packed bits.
 //   * Deterministic: every sum has a fixed order; no atomics.
@@ -146,6 +148,27 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     const int nv_max = XM ? be.n_cmp : n_visible(tok_last, p.l, p.d, be.n_cmp);
     const int nv_min = XM ? 0 : n_visible(tok_wg, p.l, p.d, be.n_cmp);
     const int n_kt = (nv_max + KT - 1) / KT;
+    // Key tiles [kt_begin, kt_end).  XM: the tiles that hold a kept entry of
+    // one of the workgroup's tokens (wave-uniform: every wave reduces over
+    // all of them); entries before kt_begin are zero for every token.
+    int kt_begin = 0, kt_end = n_kt;
+    if constexpr (XM) {
+        int lo = 0x7FFFFFFF, hi = 0;
+        for (int tt = tok_wg + lane; tt <= tok_last; tt += 64) {
+            const int2 sp = p.vis_span[tt];
+            lo = min(lo, sp.x);
+            hi = max(hi, sp.y);
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            lo = min(lo, __shfl_xor(lo, m));
+            hi = max(hi, __shfl_xor(hi, m));
+        }
+        const int tlo = lo / NKB;
+        const int thi = min((hi + NKB - 1) / NKB, n_kt);
+        kt_begin = __builtin_amdgcn_readfirstlane(tlo < thi ? tlo : 0);
+        kt_end = __builtin_amdgcn_readfirstlane(tlo < thi ? thi : 0);
+    }
 
     float* my_ring = ring + wave * TOKW * RING;
     float* my_bins = bins + wave * TOKW * p.sb;
@@ -219,19 +242,26 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         return v;
     };
 
-    if (n_kt > 0) {
+    if (kt_end > kt_begin) {
         if (full_wg) {
-            load_tile(0);
+            load_tile(kt_begin);
             store_tile(0);
         } else {
-            stage_tile(0, 0);
+            stage_tile(kt_begin, 0);
         }
+    }
+    // Select blocks whose stencil lies wholly before kt_begin score 0.
+    {
+        const int jz = min((kt_begin * KT + R - 1) / R, be.S_sel);
+        for (int j = lane; j < jz; j += 64)
+            for (int tw = 0; tw < TOKW; ++tw)
+                my_bins[tw * p.sb + j] = 0.f;
     }
     __syncthreads();
 
     auto key_tile = [&](const int kt, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
-        const int buf = (nbuf == 2) ? (kt & 1) : 0;
+        const int buf = (nbuf == 2) ? ((kt - kt_begin) & 1) : 0;
         // XM: lane i < TOKW * NKB fetches the mask word of token i / NKB for
         // 32-entry block i % NKB of this tile (issued before the K loads, so
         // waiting for it does not wait for them).
@@ -249,7 +279,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
                 }
             }
         }
-        if (full_wg && kt + 1 < n_kt)
+        if (full_wg && kt + 1 < kt_end)
             load_tile(kt + 1);
 
         f32x16 s[2][NKB];
@@ -298,18 +328,29 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pv = fast_exp2(fmaf(s[rr][kb][r], c, -bias[rr][r]));
-                    if constexpr (MASK && XM) {
-                        const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                        const uint32_t w = my_stg[(pr >> LOG2GP) * NKB + kb];
-                        // kept iff the entry exists and its mask bit is set
-                        pv = (key < be.n_cmp && ((w >> l32) & 1u)) ? pv : 0.f;
-                    } else if constexpr (MASK) {
+                    if constexpr (MASK && !XM) {
                         const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
                         const int tok = tok_w + (pr >> LOG2GP);
                         // visible iff key*d + l - 1 <= tok
                         pv = (key * p.d + p.l - 1 <= tok) ? pv : 0.f;
                     }
                     acc[(rr * 32 + 8 * (r >> 2) + (r & 3)) >> LOG2GP][kb] += pv;
+                }
+            }
+        }
+        if constexpr (MASK && XM) {
+            // The heads summed in acc[tw][kb] share one token (tw, plus
+            // hf * HSH for groups below 8) and one key, so the mask applies
+            // to the sum: kept iff the entry exists and its bit is set.
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bool in = kt * KT + kb * 32 + l32 < be.n_cmp;
+#pragma unroll
+                for (int tw = 0; tw < TOKW; ++tw) {
+                    if ((tw & HSH) == 0) {
+                        const uint32_t w = my_stg[(tw + hf * HSH) * NKB + kb];
+                        acc[tw][kb] = (in && ((w >> l32) & 1u)) ? acc[tw][kb] : 0.f;
+                    }
                 }
             }
         }
@@ -343,7 +384,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         }
         wave_lds_sync();
 
-        if (kt + 1 < n_kt) {
+        if (kt + 1 < kt_end) {
             if (nbuf == 1)
                 __syncthreads();   // single buffer: every wave is done reading it
             if (full_wg)
@@ -355,18 +396,18 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     };
 
     // Tiles every row of the workgroup sees in full need no mask.
-    const int n_full = min(nv_min / KT, n_kt);
-    int kt = 0;
+    const int n_full = min(nv_min / KT, n_kt);   // 0 under XM
+    int kt = kt_begin;
     for (; kt < n_full; ++kt)
         key_tile(kt, std::false_type{});
-    for (; kt < n_kt; ++kt)
+    for (; kt < kt_end; ++kt)
         key_tile(kt, std::true_type{});
 
     // Select blocks past the last tile: only entries < keys_done can be
     // non-zero.  Without the debug output only the blocks the wave's tokens
     // may pick (j * l' <= t) are needed.
     {
-        const int keys_done = n_kt * KT;
+        const int keys_done = kt_end * KT;
         const int jlo = (keys_done + R - 1) / R;
         const int j_end = (p.pslc || p.cand) ? be.S_sel : min(be.S_sel, (tok_w + TOKW - 1) / p.lsel + 1);
         for (int j = jlo + lane; j < j_end; j += 64)

@@ -10,6 +10,8 @@ masks the pair out and replaces that step's positional rule.
   rule hides, and rows without top-k candidates) against the oracle given
   the same masks, on the five workloads' shapes (short ragged sequences),
   in bf16 and one case in fp16;
+* banded masks (a sliding window over the compressed blocks), so that row
+  blocks start their key loop past the first tile;
 * one mask at a time, and the fwd/select halves against the full call;
 * a full-size workload with causal masks spelled out, against the
   mask-free path.
@@ -133,6 +135,32 @@ def test_random_masks_against_oracle(name, wl, dtype):
     log(f"[case] {wl.name}: random masks")
     inp, bits, kc, vc = _inputs(wl)
     am, tm = _random_masks(wl, seed=zlib.crc32(name.encode()))
+    ref = _oracle(wl, bits, kc, vc, am, tm)
+    g = _gpu(wl, inp["q"], upload_bits(kc, wl.dtype), upload_bits(vc, wl.dtype), am, tm)
+    _check(wl, g, ref, am, tm)
+
+
+def _band_masks(wl, width, extra=(1, 3)):
+    """Each row keeps only the last ``width`` blocks it may see causally
+    (a sliding window over compressed blocks) and the select blocks in the
+    same range of positions: later row blocks start their key loop well
+    past tile 0, at odd and even tiles."""
+    T_max, nc_max, s_max = _sizes(wl)
+    t = np.arange(T_max + extra[0])[:, None]
+    i = np.arange(nc_max + extra[1])[None, :]
+    nv = np.where(t >= wl.l - 1, (t - wl.l + 1) // wl.d + 1, 0)
+    am = ~((i < nv) & (i >= nv - width))
+    j = np.arange(s_max + extra[1])[None, :]
+    tm = ~((j * wl.lsel <= t) & (j * wl.lsel >= t - width * wl.d))
+    return am, tm
+
+
+@pytest.mark.parametrize("wid,width", [(2, 40), (3, 70), (4, 33), ("mha", 50), (1, 100)])
+def test_banded_masks_against_oracle(wid, width):
+    wl = MHA if wid == "mha" else SMALL[wid]
+    log(f"[case] {wl.name}: banded masks, width {width}")
+    inp, bits, kc, vc = _inputs(wl)
+    am, tm = _band_masks(wl, width)
     ref = _oracle(wl, bits, kc, vc, am, tm)
     g = _gpu(wl, inp["q"], upload_bits(kc, wl.dtype), upload_bits(vc, wl.dtype), am, tm)
     _check(wl, g, ref, am, tm)

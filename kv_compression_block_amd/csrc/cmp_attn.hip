@@ -153,24 +153,28 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     const int nv_max = XM ? be.n_cmp : n_visible(last_row / G, p.l, p.d, be.n_cmp);
     const int nv_min = XM ? 0 : n_visible(row_wg / G, p.l, p.d, be.n_cmp);
     // XM: tiles [kt0, kt0 + n_kt) hold every kept entry of the workgroup's
-    // tokens (wave-uniform: every wave reduces over all of them).  Below,
-    // kt counts tiles from kt0.
-    int kt0 = 0, n_kt = (nv_max + KT - 1) / KT;
+    // tokens, and the first n_full of them (only when kt0 = 0) are kept
+    // whole by every token (wave-uniform: every wave reduces over all of
+    // them).  Below, kt counts tiles from kt0.
+    int kt0 = 0, n_kt = (nv_max + KT - 1) / KT, n_full = min(nv_min / KT, n_kt);
     if constexpr (XM) {
-        int lo = 0x7FFFFFFF, hi = 0;
+        int lo = 0x7FFFFFFF, hi = 0, full = 0x7FFFFFFF;
         for (int tt = row_wg / G + lane; tt <= last_row / G; tt += 64) {
-            const int2 sp = p.vis_span[tt];
+            const int4 sp = p.vis_span[tt];
             lo = min(lo, sp.x);
             hi = max(hi, sp.y);
+            full = min(full, sp.z);
         }
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) {
             lo = min(lo, __shfl_xor(lo, m));
             hi = max(hi, __shfl_xor(hi, m));
+            full = min(full, __shfl_xor(full, m));
         }
         hi = min(hi, n_kt);
         kt0 = __builtin_amdgcn_readfirstlane(lo < hi ? lo : 0);
         n_kt = __builtin_amdgcn_readfirstlane(lo < hi ? hi - lo : 0);
+        n_full = __builtin_amdgcn_readfirstlane(lo == 0 ? min(min(full, be.n_cmp / KT), n_kt) : 0);
     }
 
     // ---- tile staging ----------------------------------------------------------
@@ -438,7 +442,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                          uint16_t* k_rd, uint16_t* k_cp, uint16_t* v_rd, uint16_t* v_cp) __attribute__((always_inline)) {
         constexpr bool LAST = decltype(last_tag)::value;
         if constexpr (!LAST) {
-            if constexpr (XM)
+            if constexpr (XM && decltype(mask_next)::value)
                 load_mword(kt + 1);   // before the copies: waited for without them
             load_k(kt + 3, k_cp);
             load_v(kt + 2, v_cp);
@@ -467,7 +471,6 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     // tile has no successor to prefetch.
     using F = std::false_type;
     using T = std::true_type;
-    const int n_full = min(nv_min / KT, n_kt);
     if (n_kt > 0) {
         load_k(0, K0);
         load_v(0, V0);
@@ -477,7 +480,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         copies_done();
         __syncthreads();
         if constexpr (XM)
-            load_mword(0);
+            if (n_full == 0)
+                load_mword(0);
         qk(K0);
         if (n_full > 0)
             tile_max(0, F{});

@@ -5,8 +5,10 @@
 // One wave covers 64 consecutive columns of one row: each lane loads one
 // byte (64 contiguous bytes per wave), and one ballot gives the two 32-bit
 // words of kept pairs (bit set iff the byte is zero and the column exists).
-// A second pass records per row the span of words that keep anything, from
-// which the kernels bound the key tiles a workgroup has to visit.
+// A second pass records per row the span of words that keep anything and
+// the number of leading words that keep everything, from which the kernels
+// bound the key tiles a workgroup has to visit and find the leading tiles
+// that need no mask.
 #include "nsa_device.h"
 
 namespace nsa {
@@ -33,21 +35,26 @@ __global__ __launch_bounds__(kPackThreads) void k_pack_mask(MaskPackParams p)
         p.dst[(int64_t)t * p.words + w] = (uint32_t)(lane ? bits >> 32 : bits);
 }
 
-// One thread per row: the first and one past the last non-zero word.
+// One thread per row: the first and one past the last non-zero word, and
+// the number of leading all-ones words.
 __global__ __launch_bounds__(kPackThreads) void k_mask_span(MaskPackParams p)
 {
     const int t = blockIdx.x * kPackThreads + threadIdx.x;
     if (t >= p.rows)
         return;
     const uint32_t* row = p.dst + (int64_t)t * p.words;
-    int lo = p.words, hi = 0;
+    int lo = p.words, hi = 0, full = 0;
+    bool lead = true;
     for (int w = 0; w < p.words; ++w) {
-        if (row[w] != 0u) {
+        const uint32_t v = row[w];
+        if (v != 0u) {
             lo = min(lo, w);
             hi = w + 1;
         }
+        lead = lead && v == 0xFFFFFFFFu;
+        full += lead;
     }
-    p.span[t] = make_int2(lo, hi);
+    p.span[t] = make_int4(lo, hi, full, 0);
 }
 
 hipError_t launch_pack_mask(const MaskPackParams& p, hipStream_t stream)

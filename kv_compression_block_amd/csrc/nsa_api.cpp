@@ -347,7 +347,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->cand_words = std::max<int64_t>(1, (S_max + 31) / 32);
     const size_t vis_bytes = ((size_t)T_max * (size_t)plan->vis_words * 4 + 255) / 256 * 256;
     const size_t cand_bytes = ((size_t)T_max * (size_t)plan->cand_words * 4 + 255) / 256 * 256;
-    const size_t span_bytes = ((size_t)T_max * 8 + 255) / 256 * 256;
+    const size_t span_bytes = ((size_t)T_max * 16 + 255) / 256 * 256;
     plan->ws_masked_bytes = plan->ws_bytes + vis_bytes + cand_bytes + span_bytes;
     *workspace_bytes = plan->ws_bytes;
     *plan_out = plan;
@@ -408,7 +408,7 @@ uint32_t q_sign(const nsa_plan_s* plan) { return plan->scale < 0.f ? 0x80008000u
 
 nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const void* value,
                       void* attention_out, float* softmax_max, float* softmax_sum, void* workspace,
-                      hipStream_t s, const uint32_t* vis = nullptr, const int2* vis_span = nullptr)
+                      hipStream_t s, const uint32_t* vis = nullptr, const int4* vis_span = nullptr)
 {
     const float abs_scale = std::fabs(plan->scale);
     const float c = exp2_scale(plan);
@@ -446,7 +446,7 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
 nsa_status launch_select(nsa_plan plan, const void* query, const void* key, const float* softmax_max,
                          const float* softmax_sum, int32_t* topk_indices, float* p_slc_debug,
                          void* workspace, hipStream_t s, const uint32_t* vis = nullptr,
-                         const int2* vis_span = nullptr, const uint32_t* cand = nullptr)
+                         const int4* vis_span = nullptr, const uint32_t* cand = nullptr)
 {
     nsa::TopkParams t;
     std::memset(&t, 0, sizeof t);
@@ -500,7 +500,7 @@ nsa_status launch_select(nsa_plan plan, const void* query, const void* key, cons
 // where the positional rule applies.
 nsa_status prepare_masks(nsa_plan plan, const nsa_masks* masks, bool use_atten, bool use_topk,
                          void* workspace, size_t workspace_bytes, hipStream_t s,
-                         const uint32_t** vis, const int2** vis_span, const uint32_t** cand)
+                         const uint32_t** vis, const int4** vis_span, const uint32_t** cand)
 {
     *vis = nullptr;
     *vis_span = nullptr;
@@ -524,7 +524,7 @@ nsa_status prepare_masks(nsa_plan plan, const nsa_masks* masks, bool use_atten, 
                     plan->ws_masked_bytes, workspace_bytes);
     uint32_t* vis_ws = (uint32_t*)((char*)workspace + plan->ws_bytes);
     uint32_t* cand_ws = vis_ws + ((size_t)plan->T_max * (size_t)plan->vis_words * 4 + 255) / 256 * 64;
-    int2* span_ws = (int2*)(cand_ws + ((size_t)plan->T_max * (size_t)plan->cand_words * 4 + 255) / 256 * 64);
+    int4* span_ws = (int4*)(cand_ws + ((size_t)plan->T_max * (size_t)plan->cand_words * 4 + 255) / 256 * 64);
     if (a) {
         nsa::MaskPackParams mp{(const uint8_t*)masks->atten_mask, masks->atten_cols, vis_ws,
                                (int)plan->T_max, (int)plan->vis_words, span_ws};
@@ -639,7 +639,7 @@ nsa_status nsa_compress_attention_fwd_masked(nsa_plan plan, const void* query, c
         return st == NSA_OK ? ok() : st;
     hipStream_t s = (hipStream_t)stream;
     const uint32_t *vis = nullptr, *cand = nullptr;
-    const int2* span = nullptr;
+    const int4* span = nullptr;
     if ((st = prepare_masks(plan, masks, true, false, workspace, workspace_bytes, s, &vis, &span, &cand)) != NSA_OK)
         return st;
     if ((st = upload_table(plan, workspace, s)) != NSA_OK)
@@ -668,7 +668,7 @@ nsa_status nsa_compress_attention_select_masked(nsa_plan plan, const void* query
         return st == NSA_OK ? ok() : st;
     hipStream_t s = (hipStream_t)stream;
     const uint32_t *vis = nullptr, *cand = nullptr;
-    const int2* span = nullptr;
+    const int4* span = nullptr;
     if ((st = prepare_masks(plan, masks, true, true, workspace, workspace_bytes, s, &vis, &span, &cand)) != NSA_OK)
         return st;
     if ((st = upload_table(plan, workspace, s)) != NSA_OK)
@@ -698,7 +698,7 @@ nsa_status nsa_compress_attention_masked(nsa_plan plan, const void* query, const
         return st == NSA_OK ? ok() : st;
     hipStream_t s = (hipStream_t)stream;
     const uint32_t *vis = nullptr, *cand = nullptr;
-    const int2* span = nullptr;
+    const int4* span = nullptr;
     if ((st = prepare_masks(plan, masks, true, true, workspace, workspace_bytes, s, &vis, &span, &cand)) != NSA_OK)
         return st;
     if ((st = upload_table(plan, workspace, s)) != NSA_OK)

@@ -52,8 +52,9 @@ struct MaskPackParams {
     int64_t src_cols;
     uint32_t* dst;        // [rows, words]
     int rows, words;
-    int2* span;           // NULL, or [rows]: (first word with a kept pair, last such word + 1),
-                          // (words, 0) for a row that keeps nothing
+    int4* span;           // NULL, or [rows]: (first word with a kept pair, last such word + 1,
+                          // number of leading words that keep all 32 pairs, 0);
+                          // (words, 0, 0, 0) for a row that keeps nothing
 };
 hipError_t launch_pack_mask(const MaskPackParams& p, hipStream_t stream);
 
@@ -73,7 +74,7 @@ struct AttnParams {
     float thr;            // running-max slack before rescaling, raw-score units
     uint32_t qsign;       // 0x80008000 when scale < 0 (q negated), else 0
     const uint32_t* vis;  // NULL (positional rule) or packed atten_mask [T_max, vis_words]
-    const int2* vis_span; // per row of vis: span of words with a kept pair
+    const int4* vis_span; // per row of vis: span of words with a kept pair, leading full words
     int vis_words;
 };
 
@@ -108,7 +109,7 @@ struct TopkParams {
     int waves;            // waves per workgroup
     int kbufs;            // K tile buffers in LDS (2 = double buffered)
     const uint32_t* vis;  // NULL (positional rule) or packed atten_mask [T_max, vis_words]
-    const int2* vis_span; // per row of vis: span of words with a kept pair
+    const int4* vis_span; // per row of vis: span of words with a kept pair, leading full words
     int vis_words;
     const uint32_t* cand; // NULL (positional rule) or packed topk_mask [T_max, cand_words]
     int cand_words;

@@ -151,23 +151,29 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     // Key tiles [kt_begin, kt_end).  XM: the tiles that hold a kept entry of
     // one of the workgroup's tokens (wave-uniform: every wave reduces over
     // all of them); entries before kt_begin are zero for every token.
-    int kt_begin = 0, kt_end = n_kt;
+    // The first n_full tiles are seen whole by every token (XM: kept whole
+    // by every token's mask row, only when kt_begin = 0) and need no mask.
+    int kt_begin = 0, kt_end = n_kt, n_full = min(nv_min / KT, n_kt);
     if constexpr (XM) {
-        int lo = 0x7FFFFFFF, hi = 0;
+        int lo = 0x7FFFFFFF, hi = 0, full = 0x7FFFFFFF;
         for (int tt = tok_wg + lane; tt <= tok_last; tt += 64) {
-            const int2 sp = p.vis_span[tt];
+            const int4 sp = p.vis_span[tt];
             lo = min(lo, sp.x);
             hi = max(hi, sp.y);
+            full = min(full, sp.z);
         }
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) {
             lo = min(lo, __shfl_xor(lo, m));
             hi = max(hi, __shfl_xor(hi, m));
+            full = min(full, __shfl_xor(full, m));
         }
         const int tlo = lo / NKB;
         const int thi = min((hi + NKB - 1) / NKB, n_kt);
         kt_begin = __builtin_amdgcn_readfirstlane(tlo < thi ? tlo : 0);
         kt_end = __builtin_amdgcn_readfirstlane(tlo < thi ? thi : 0);
+        n_full = __builtin_amdgcn_readfirstlane(
+            (tlo < thi && tlo == 0) ? min(min(full / NKB, be.n_cmp / KT), kt_end) : 0);
     }
 
     float* my_ring = ring + wave * TOKW * RING;
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         // waiting for it does not wait for them).
         constexpr int MWPL = (TOKW * NKB + 63) / 64;   // mask words per lane
         uint32_t mw_lane[MWPL];
-        if constexpr (XM) {
+        if constexpr (XM && MASK) {
 #pragma unroll
             for (int m = 0; m < MWPL; ++m) {
                 const int i = lane + 64 * m;
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        if constexpr (XM) {
+        if constexpr (XM && MASK) {
 #pragma unroll
             for (int m = 0; m < MWPL; ++m)
                 if (lane + 64 * m < TOKW * NKB)
@@ -396,7 +402,6 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     };
 
     // Tiles every row of the workgroup sees in full need no mask.
-    const int n_full = min(nv_min / KT, n_kt);   // 0 under XM
     int kt = kt_begin;
     for (; kt < n_full; ++kt)
         key_tile(kt, std::false_type{});

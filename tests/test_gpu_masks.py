@@ -11,7 +11,9 @@ masks the pair out and replaces that step's positional rule.
   the same masks, on the five workloads' shapes (short ragged sequences),
   in bf16 and one case in fp16;
 * banded masks (a sliding window over the compressed blocks), so that row
-  blocks start their key loop past the first tile;
+  blocks start their key loop past the first tile, and causal masks with
+  random holes past the first blocks (leading tiles kept whole by every
+  token run without the mask);
 * one mask at a time, and the fwd/select halves against the full call;
 * a full-size workload with causal masks spelled out, against the
   mask-free path.
@@ -161,6 +163,25 @@ def test_banded_masks_against_oracle(wid, width):
     log(f"[case] {wl.name}: banded masks, width {width}")
     inp, bits, kc, vc = _inputs(wl)
     am, tm = _band_masks(wl, width)
+    ref = _oracle(wl, bits, kc, vc, am, tm)
+    g = _gpu(wl, inp["q"], upload_bits(kc, wl.dtype), upload_bits(vc, wl.dtype), am, tm)
+    _check(wl, g, ref, am, tm)
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_causal_masks_with_holes_against_oracle(wid):
+    """The causal rule plus random holes past the first 96 blocks: leading
+    key tiles that every token keeps whole take the mask-free body, the
+    rest the masked one."""
+    wl = SMALL[wid]
+    log(f"[case] {wl.name}: causal masks with holes")
+    inp, bits, kc, vc = _inputs(wl)
+    am, tm = _causal_masks(wl)
+    rng = np.random.default_rng(31 + wid)
+    holes = rng.random(am.shape) < 0.2
+    holes[:, :96] = False
+    am = am | holes
+    tm = tm | (rng.random(tm.shape) < 0.2)
     ref = _oracle(wl, bits, kc, vc, am, tm)
     g = _gpu(wl, inp["q"], upload_bits(kc, wl.dtype), upload_bits(vc, wl.dtype), am, tm)
     _check(wl, g, ref, am, tm)

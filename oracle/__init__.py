@@ -10,7 +10,10 @@ order the operator pages give them:
 
 * ``compress``  -- the NSA Compress formula ("aclnnNsaCompress", Formula);
 * ``attention`` -- steps 1-7 of "mindspore.ops.nsa_compress_attention"
-  (scores, mask, softmax, output, importance remap, group sum, top-k).
+  (scores, mask, softmax, output, importance remap, group sum, top-k);
+* ``select_attention`` -- attention over the raw keys of the selected
+  blocks, the consumer of the top-k indices (interface of
+  "lite_boost.ops.rain_fusion_attention").
 
 The compressed keys/values that feed attention are the compression results
 rounded to the element type of the inputs (round to nearest, ties to even),
@@ -82,6 +85,9 @@ def _load():
                                                 P, I64, I64, P, I64, I64,
                                                 P, P, P, P, I64, P]
     lib.nsa_oracle_attention_masked.restype = ctypes.c_int
+    lib.nsa_oracle_select_attention.argtypes = [P, P, P, P, P, I64, P, I64, I64, I64, I64, I64,
+                                                ctypes.c_double, I64, I64, ctypes.c_int, P, P]
+    lib.nsa_oracle_select_attention.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -272,3 +278,31 @@ def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None, atten_mask=None,
                     atten_mask=atten_mask, topk_mask=topk_mask)
     res.update({"kc": kc, "vc": vc, "kc_bits": kc_b, "vc_bits": vc_b, "tokens": tokens})
     return res
+
+
+def select_attention(q_bits, k_bits, v_bits, topk, act_seq_qlen, N1: int, N2: int, scale: float,
+                     lsel: int, tokens=None, dtype: str = "bf16") -> dict:
+    """Selected-block attention for the listed global tokens (all when None).
+
+    q: [T, N1, D1], k: [T, N2, D1], v: [T, N2, D2] bits of element type
+    ``dtype``; topk: [T, N2, count] int32 block indices (-1 unused).
+    Returns dict(out [n, N1, D2], lse [n, N1]) in float64."""
+    q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
+    topk = np.ascontiguousarray(topk, dtype=np.int32)
+    T = q.shape[0]
+    D1, D2 = q.shape[2], v.shape[2]
+    if k.shape != (T, N2, D1) or v.shape[:2] != (T, N2) or q.shape[1] != N1:
+        raise ValueError("shapes of q, k, v do not match")
+    if topk.ndim != 3 or topk.shape[:2] != (T, N2):
+        raise ValueError(f"topk must be [{T}, {N2}, count], got {topk.shape}")
+    count = topk.shape[2]
+    actq = _i64(act_seq_qlen)
+    tok = _i64(np.arange(T) if tokens is None else tokens)
+    out = np.empty((len(tok), N1, D2), dtype=np.float64)
+    lse = np.empty((len(tok), N1), dtype=np.float64)
+    rc = _load().nsa_oracle_select_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(topk), _ptr(tok), len(tok),
+                                             _ptr(actq), len(actq), N1, N2, D1, D2, float(scale), lsel,
+                                             count, _code(dtype), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_select_attention returned {rc}")
+    return {"out": out, "lse": lse}

@@ -22,6 +22,10 @@
  *     the sum of P_slc over the query heads of a KV-head group, the top-k
  *     mask and the top-k indices.
  *
+ *   - the selected-block attention that consumes the top-k indices, whose
+ *     interface only is given ("lite_boost.ops.rain_fusion_attention"); its
+ *     reading is stated at nsa_oracle_select_attention below.
+ *
  * Arithmetic is float64 on inputs that are bfloat16 or float16 bit patterns
  * (the two element types the MindSpore page allows for query, key and value)
  * widened exactly.  The one decision that floating point turns into integers (which
@@ -450,4 +454,113 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
                                        act_cmp_seq_kvlen, B, N1, N2, D1, D2, scale, l, d, lsel,
                                        count, dtype, NULL, 0, 0, NULL, 0, 0, out, smax, ssum,
                                        pslc, s_stride, topk);
+}
+
+/* ---- selected-block attention (the consumer of topk_indices) --------------
+ *
+ * The pages define this step only through an interface ("lite_boost.ops.
+ * rain_fusion_attention": per query, a -1 padded list of KV block indices
+ * to attend to, returning the output and the softmax log-sum-exp).  Reading
+ * taken, the plainest one the rest supports: query token t (local position
+ * in its sequence), query head h of KV group g = floor(h / (N1/N2)), attends
+ * to the raw keys s of its own sequence with s <= t whose select block
+ * floor(s / l') is listed in topk[t, g, 0..count) (entries outside
+ * [0, ceil(T/l')) and repeats add nothing); softmax of scale * q.k over
+ * those keys, applied to v.  A query with no such key has output 0 and
+ * log-sum-exp -inf.
+ *
+ * q [T, N1, D1], k [T, N2, D1], v [T, N2, D2] (element type dtype), TND with
+ * prefix sums act_seq_qlen[B]; topk [T, N2, count] int32.  Outputs: out
+ * [T, N1, D2] and lse [T, N1] (natural log of sum_s exp(score_s)), double.
+ * Only the listed tokens (global indices) are evaluated: out and lse have
+ * n_tok rows.
+ */
+int nsa_oracle_select_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* topk, const int64_t* tokens, int64_t n_tok,
+                                const int64_t* act_seq_qlen, int64_t B, int64_t N1, int64_t N2,
+                                int64_t D1, int64_t D2, double scale, int64_t lsel, int64_t count,
+                                int dtype, double* out, double* lse)
+{
+    if (N2 < 1 || N1 % N2 != 0 || lsel < 1 || count < 1 || B < 1 || dtype < 0 || dtype > 1)
+        return -1;
+    const int64_t G = N1 / N2;
+    int64_t T_max = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
+        if (T > T_max) T_max = T;
+    }
+    for (int64_t i = 0; i < n_tok; ++i) {
+        int64_t tl = 0;
+        if (find_seq(act_seq_qlen, B, tokens[i], &tl) < 0)
+            return -3;
+    }
+    const int64_t S_max = (T_max + lsel - 1) / lsel;
+    int err = 0;
+#pragma omp parallel
+    {
+        unsigned char* sel = (unsigned char*)malloc((size_t)(S_max + 1));
+        double* s = (double*)malloc(sizeof(double) * (size_t)(T_max + 1));
+        if (!sel || !s) {
+#pragma omp atomic write
+            err = -4;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = 0; i < n_tok; ++i) {
+                int64_t t = 0;
+                const int64_t b = find_seq(act_seq_qlen, B, tokens[i], &t);
+                const int64_t s0 = seq_start(act_seq_qlen, b);
+                const int64_t T = act_seq_qlen[b] - s0;
+                const int64_t S = (T + lsel - 1) / lsel;
+                for (int64_t g = 0; g < N2; ++g) {
+                    /* the listed blocks of (t, g), as a set */
+                    for (int64_t j = 0; j < S; ++j)
+                        sel[j] = 0;
+                    const int32_t* row = topk + (tokens[i] * N2 + g) * count;
+                    for (int64_t c = 0; c < count; ++c)
+                        if (row[c] >= 0 && row[c] < S)
+                            sel[row[c]] = 1;
+                    for (int64_t hh = 0; hh < G; ++hh) {
+                        const int64_t h = g * G + hh;
+                        const uint16_t* qh = q + (tokens[i] * N1 + h) * D1;
+                        double m = -INFINITY;
+                        for (int64_t x = 0; x <= t; ++x) {
+                            s[x] = -INFINITY;
+                            if (!sel[x / lsel])
+                                continue;
+                            const uint16_t* kx = k + ((s0 + x) * N2 + g) * D1;
+                            double dot = 0.0;
+                            for (int64_t e = 0; e < D1; ++e)
+                                dot += widen(dtype, qh[e]) * widen(dtype, kx[e]);
+                            s[x] = scale * dot;
+                            if (s[x] > m)
+                                m = s[x];
+                        }
+                        double* o = out + (i * N1 + h) * D2;
+                        for (int64_t e = 0; e < D2; ++e)
+                            o[e] = 0.0;
+                        if (m == -INFINITY) {
+                            lse[i * N1 + h] = -INFINITY;
+                            continue;
+                        }
+                        double L = 0.0;
+                        for (int64_t x = 0; x <= t; ++x)
+                            if (s[x] != -INFINITY)
+                                L += exp(s[x] - m);
+                        for (int64_t x = 0; x <= t; ++x) {
+                            if (s[x] == -INFINITY)
+                                continue;
+                            const double p = exp(s[x] - m) / L;
+                            const uint16_t* vx = v + ((s0 + x) * N2 + g) * D2;
+                            for (int64_t e = 0; e < D2; ++e)
+                                o[e] += p * widen(dtype, vx[e]);
+                        }
+                        lse[i * N1 + h] = m + log(L);
+                    }
+                }
+            }
+        }
+        free(sel);
+        free(s);
+    }
+    return err;
 }

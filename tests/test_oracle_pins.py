@@ -788,3 +788,132 @@ def test_masks_that_spell_the_positional_rules_change_nothing():
     with pytest.raises(ValueError):
         oracle.attention(q, tok, kc, vc, actq, actc, N1, N2, 0.3, l, d, lsel, count,
                          atten_mask=am[:, :2])
+
+
+# --------------------------------------------------------------------------
+# Selected-block attention (consumer of the top-k indices; interface of
+# "lite_boost.ops.rain_fusion_attention").  Reading: token t, head h of
+# group g attends to the raw keys s <= t of its sequence whose block
+# floor(s / l') is listed in topk[t, g]; -1, out-of-range entries and
+# repeats add nothing; no key -> output 0, lse -inf.
+# --------------------------------------------------------------------------
+
+def _sel_case(seed, lens, N1, N2, D1, D2, lsel, count, p_empty=0.05):
+    rng = np.random.default_rng(seed)
+    T = sum(lens)
+    q = rand_bf16(rng, (T, N1, D1))
+    k = rand_bf16(rng, (T, N2, D1))
+    v = rand_bf16(rng, (T, N2, D2))
+    topk = np.full((T, N2, count), -1, dtype=np.int32)
+    for s0, Tb in zip(starts_of(lens), lens):
+        S = -(-Tb // lsel)
+        for t in range(Tb):
+            for g in range(N2):
+                if rng.random() < p_empty:
+                    continue
+                n = int(rng.integers(1, count + 1))
+                topk[s0 + t, g, :n] = rng.integers(0, S, n)   # repeats allowed, any order
+    return q, k, v, topk
+
+
+def test_select_attention_matches_torch_sdpa():
+    """Rows against torch SDPA (float64) with the boolean mask 'key s <= t and
+    block(s) listed'; lse against torch.logsumexp of the masked scores;
+    rows with no key give 0 and -inf."""
+    lens = [130, 77, 200]
+    N1, N2, D1, D2, lsel, count = 4, 2, 16, 8, 32, 4
+    scale = 0.35
+    q, k, v, topk = _sel_case(40, lens, N1, N2, D1, D2, lsel, count)
+    res = oracle.select_attention(q, k, v, topk, np.cumsum(lens), N1, N2, scale, lsel)
+    qf, kf, vf = (widen_torch(a, "bf16") for a in (q, k, v))
+    G = N1 // N2
+    n_rows = n_empty = 0
+    for s0, Tb in zip(starts_of(lens), lens):
+        S = -(-Tb // lsel)
+        t = np.arange(Tb)[:, None]
+        s = np.arange(Tb)[None, :]
+        for g in range(N2):
+            sel = np.zeros((Tb, S), dtype=bool)
+            for tt in range(Tb):
+                for j in topk[s0 + tt, g]:
+                    if 0 <= j < S:
+                        sel[tt, j] = True
+            mask = torch.from_numpy((s <= t) & sel[np.arange(Tb)[:, None], s // lsel])
+            has = mask.any(dim=1)
+            for hh in range(G):
+                h = g * G + hh
+                qb, kb, vb = qf[s0:s0 + Tb, h], kf[s0:s0 + Tb, g], vf[s0:s0 + Tb, g]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qb[None, None], kb[None, None], vb[None, None], attn_mask=mask[None, None],
+                    scale=scale)[0, 0]
+                got = torch.from_numpy(res["out"][s0:s0 + Tb, h])
+                torch.testing.assert_close(got[has], ref[has], rtol=1e-12, atol=1e-13)
+                assert torch.all(got[~has] == 0)
+                sc = torch.where(mask, scale * (qb @ kb.T), torch.tensor(-float("inf"), dtype=torch.float64))
+                lse = torch.logsumexp(sc, dim=1)
+                gl = torch.from_numpy(res["lse"][s0:s0 + Tb, h])
+                torch.testing.assert_close(gl[has], lse[has], rtol=1e-13, atol=1e-13)
+                assert torch.all(torch.isneginf(gl[~has]))
+            n_rows += int(has.sum())
+            n_empty += int((~has).sum())
+    assert n_rows > 500 and n_empty > 5
+
+
+def test_select_attention_all_blocks_is_causal_attention():
+    """Listing every block reduces to plain causal attention over the raw
+    keys (torch SDPA with is_causal=True)."""
+    lens = [150, 64]
+    N1, N2, D1, D2, lsel = 4, 1, 16, 16, 32
+    rng = np.random.default_rng(41)
+    T = sum(lens)
+    q, k, v = rand_bf16(rng, (T, N1, D1)), rand_bf16(rng, (T, N2, D1)), rand_bf16(rng, (T, N2, D2))
+    S_max = max(-(-Tb // lsel) for Tb in lens)
+    topk = np.tile(np.arange(S_max, dtype=np.int32)[::-1], (T, N2, 1))   # any order, every block
+    res = oracle.select_attention(q, k, v, topk, np.cumsum(lens), N1, N2, 0.25, lsel)
+    qf, kf, vf = (widen_torch(a, "bf16") for a in (q, k, v))
+    for s0, Tb in zip(starts_of(lens), lens):
+        for h in range(N1):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qf[s0:s0 + Tb, h][None, None], kf[s0:s0 + Tb, 0][None, None],
+                vf[s0:s0 + Tb, 0][None, None], is_causal=True, scale=0.25)[0, 0]
+            torch.testing.assert_close(torch.from_numpy(res["out"][s0:s0 + Tb, h]), ref,
+                                       rtol=1e-12, atol=1e-13)
+
+
+def test_select_attention_identical_keys_closed_form():
+    """Identical keys: uniform weights over the selected visible keys, so the
+    output is their mean value and lse = scale*<q,k> + log(count of keys)."""
+    lens = [300]
+    N1, N2, D1, D2, lsel, count = 2, 1, 8, 4, 64, 2
+    rng = np.random.default_rng(42)
+    q = rand_bf16(rng, (300, N1, D1))
+    k1 = oracle.bf16_to_f64(rand_bf16(rng, (D1,)))
+    k = bits(np.broadcast_to(k1, (300, N2, D1)))
+    v = rand_bf16(rng, (300, N2, D2))
+    topk = np.full((300, N2, count), -1, dtype=np.int32)
+    topk[:, 0, 0] = np.arange(300) // lsel          # own block
+    topk[:, 0, 1] = 0                               # and the first
+    res = oracle.select_attention(q, k, v, topk, lens, N1, N2, 0.5, lsel)
+    qf, vf = oracle.bf16_to_f64(q), oracle.bf16_to_f64(v)
+    for t in range(300):
+        keys = [s for s in range(t + 1) if s // lsel in (t // lsel, 0)]
+        for h in range(N1):
+            np.testing.assert_allclose(res["out"][t, h], vf[keys, 0].mean(axis=0), rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(res["lse"][t, h], 0.5 * qf[t, h] @ k1 + np.log(len(keys)),
+                                       rtol=1e-12)
+
+
+def test_select_attention_ignores_repeats_padding_and_out_of_range():
+    """-1, repeats and indices past the sequence's last block change nothing."""
+    lens = [200]
+    N1, N2, D1, D2, lsel, count = 4, 2, 16, 8, 32, 6
+    q, k, v, topk = _sel_case(43, lens, N1, N2, D1, D2, lsel, 3, p_empty=0.0)
+    clean = np.full((200, N2, count), -1, dtype=np.int32)
+    clean[:, :, :3] = topk
+    noisy = clean.copy()
+    noisy[:, :, 3] = topk[:, :, 0]                     # a repeat
+    noisy[:, :, 4] = 7 + 100                           # past the last block (7)
+    noisy[:, :, 5] = -5                                # negative
+    a = oracle.select_attention(q, k, v, clean, lens, N1, N2, 0.3, lsel)
+    b = oracle.select_attention(q, k, v, noisy, lens, N1, N2, 0.3, lsel)
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])

@@ -265,6 +265,41 @@ nsa_status nsa_compress_attention_select_masked(nsa_plan plan, const void* query
                                                 float* p_slc_debug, void* workspace,
                                                 size_t workspace_bytes, void* stream);
 
+/*
+ * nsa_select_attention -- the step of Native Sparse Attention that consumes
+ * topk_indices.  The pages give it only as an interface
+ * ("lite_boost.ops.rain_fusion_attention": per query a -1 padded list of KV
+ * blocks to attend to, returning the output and the softmax log-sum-exp);
+ * the reading implemented: query token t (local position in its sequence),
+ * query head h of KV head g = floor(h / (N1/N2)) attends to the raw keys
+ * s <= t of its own sequence whose select block floor(s / l') is listed in
+ * topk_indices[t, g, :]; -1, repeated entries and entries at or past the
+ * sequence's ceil(T/l') blocks add nothing.
+ *
+ *   plan           from nsa_compress_attention_get_workspace (sequence
+ *                  lengths, heads, dims, scale_value, l' = select_block_size,
+ *                  select_block_count, dtype); l' must be a multiple of 32
+ *   query          [T1, N1, d1] device
+ *   key, value     [T1, N2, d1] and [T1, N2, d2] device: the raw (not
+ *                  compressed) keys and values, same TND layout and
+ *                  sequences as query
+ *   topk_indices   [T1, N2, select_block_count] int32 device (for instance
+ *                  the output of nsa_compress_attention)
+ *   attention_out  [T1, N1, d2] device; 0 for a query with no key
+ *   softmax_lse    [T1, N1] float32 device: natural log of
+ *                  sum_s exp(scale * q.k_s) over the attended keys; -inf for
+ *                  a query with no key
+ *   workspace      device, >= the plan's workspace_bytes
+ *
+ * Errors: NSA_ERR_NULLPTR, NSA_ERR_WORKSPACE, NSA_ERR_CONSTRAINT (misaligned
+ * pointer), NSA_ERR_UNSUPPORTED (l' not a multiple of 32; head dims outside
+ * {64,128,192} x {64,128}), NSA_ERR_HIP.
+ */
+nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* key,
+                                const void* value, const int32_t* topk_indices,
+                                void* attention_out, float* softmax_lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Sizes a plan fixed, for callers that allocate outputs from a plan. */
 typedef struct nsa_plan_info {
     int64_t batch;

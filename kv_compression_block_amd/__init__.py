@@ -14,7 +14,9 @@ Entry points (same names as the C ABI):
 * ``nsa_compress_attention`` -- second phase: attention output, top-k
   indices, softmax max/sum (and optionally the importance scores);
 * ``compress_attention`` -- both phases in one call with the argument list
-  of ``mindspore.ops.nsa_compress_attention``.
+  of ``mindspore.ops.nsa_compress_attention``;
+* ``nsa_select_attention`` -- attention over the raw keys of the blocks
+  that ``topk_indices`` lists (the consumer of the top-k).
 
 The second-phase calls take optional ``atten_mask`` / ``topk_mask``: 2-D
 bool (or uint8) GPU tensors indexed by (local query position, compressed
@@ -33,7 +35,7 @@ from ._lib import Masks, NsaError, PlanInfo  # noqa: F401
 
 __all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_workspace",
            "nsa_compress_attention", "nsa_compress_attention_fwd", "nsa_compress_attention_select",
-           "compress_attention", "Plan", "NsaError", "library_path"]
+           "nsa_select_attention", "compress_attention", "Plan", "NsaError", "library_path"]
 
 
 def library_path() -> str:
@@ -341,3 +343,39 @@ def compress_attention(query, key, value, scale_value, head_num, compress_block_
                                       atten_mask=atten_mask, topk_mask=topk_mask)
     finally:
         plan.destroy()
+
+
+def nsa_select_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                         topk_indices: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                         outputs: Optional[dict] = None, stream=None):
+    """Selected-block attention over the raw ``key [T1, N2, D1]`` /
+    ``value [T1, N2, D2]`` (same sequences as ``query``) for the blocks that
+    ``topk_indices [T1, N2, count]`` lists.  Returns (attention_out
+    [T1, N1, D2], softmax_lse [T1, N1] float32)."""
+    info = plan.info
+    T1, N1, N2, D1, D2 = (info["total_q_tokens"], info["head_num"], info["kv_head_num"], info["d1"],
+                          info["d2"])
+    for t, name in ((query, "query"), (key, "key"), (value, "value"), (topk_indices, "topk_indices")):
+        _need_tensor(t, name)
+    if tuple(query.shape) != (T1, N1, D1):
+        raise ValueError(f"query must be {(T1, N1, D1)}, got {tuple(query.shape)}")
+    if tuple(key.shape) != (T1, N2, D1) or tuple(value.shape) != (T1, N2, D2):
+        raise ValueError(f"key/value must be {(T1, N2, D1)} / {(T1, N2, D2)}, got "
+                         f"{tuple(key.shape)} / {tuple(value.shape)}")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise TypeError("query, key and value must share a dtype")
+    if _dtype_code(query.dtype) != info["dtype"]:
+        raise TypeError(f"the plan was made for dtype code {info['dtype']}, query is {query.dtype}")
+    if topk_indices.dtype != torch.int32 or tuple(topk_indices.shape) != (T1, N2, info["select_block_count"]):
+        raise ValueError(f"topk_indices must be int32 {(T1, N2, info['select_block_count'])}")
+    o = dict(outputs or {})
+    if o.get("attention_out") is None:
+        o["attention_out"] = torch.empty((T1, N1, D2), dtype=query.dtype, device=query.device)
+    if o.get("softmax_lse") is None:
+        o["softmax_lse"] = torch.empty((T1, N1), dtype=torch.float32, device=query.device)
+    ws, ws_bytes = _workspace(plan, workspace, query.device)
+    st = _lib.load().nsa_select_attention(plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(topk_indices),
+                                          _ptr(o["attention_out"]), _ptr(o["softmax_lse"]), _ptr(ws), ws_bytes,
+                                          _stream_ptr(query.device, stream))
+    _lib.check(st)
+    return o["attention_out"], o["softmax_lse"]

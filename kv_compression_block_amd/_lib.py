@@ -34,6 +34,7 @@ EXPORTS = (
     "nsa_compress_attention_masked",
     "nsa_compress_attention_fwd_masked",
     "nsa_compress_attention_select_masked",
+    "nsa_select_attention",
     "nsa_plan_get_info",
     "nsa_plan_destroy",
     "nsa_status_string",
@@ -107,6 +108,8 @@ def load() -> ctypes.CDLL:
     lib.nsa_compress_attention_fwd_masked.restype = I32
     lib.nsa_compress_attention_select_masked.argtypes = [P, P, P, MP, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_compress_attention_select_masked.restype = I32
+    lib.nsa_select_attention.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.nsa_select_attention.restype = I32
     lib.nsa_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.nsa_plan_get_info.restype = I32
     lib.nsa_plan_destroy.argtypes = [P]

@@ -66,30 +66,6 @@ struct AttnCfg {
     static_assert(D2 == 64 || D2 == 128, "V swizzle");
 };
 
-// 16-byte chunk c of V row r sits at chunk v_swz(r, c) of that row.  The
-// P.V operand reads (ds_read_b64_tr_b16) touch 8 consecutive rows and 4
-// consecutive chunks per instruction; this XOR spreads them over all 64
-// banks twice, the minimum for 512 bytes.
-template <int D2>
-__device__ __forceinline__ int v_swz(int r, int c)
-{
-    if constexpr (D2 == 128)
-        return c ^ ((r & 3) << 2);
-    else
-        return c ^ (((r >> 1) & 1) << 2);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Copies 16 bytes per lane from a buffer into LDS: lane i's bytes land at
-// lds + 16 i (the LDS address must be the same in every lane).
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
-}
-
 
 // At least three waves per SIMD for D1 = D2 = 128 (168 registers, a few
 // values spilled around the main loop), which the unrolled loop would

@@ -712,4 +712,53 @@ nsa_status nsa_compress_attention_masked(nsa_plan plan, const void* query, const
     return ok();
 }
 
+nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* key, const void* value,
+                                const int32_t* topk_indices, void* attention_out, float* softmax_lse,
+                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !key || !value || !topk_indices || !attention_out || !softmax_lse))
+        return fail(NSA_ERR_NULLPTR, "query, key, value, topk_indices and the outputs must not be NULL");
+    if (plan->lsel % 32 != 0)
+        return fail(NSA_ERR_UNSUPPORTED, "selected-block attention needs select_block_size %% 32 == 0 (got %lld)",
+                    (long long)plan->lsel);
+    if (!nsa::sel_attn_supported((int)plan->D1, (int)plan->D2))
+        return fail(NSA_ERR_UNSUPPORTED, "head dims (%lld, %lld) are not built for selected-block attention",
+                    (long long)plan->D1, (long long)plan->D2);
+    nsa_status st = check_exec(plan, workspace, workspace_bytes, {query, key, value, attention_out, workspace},
+                               {topk_indices, softmax_lse});
+    if (st != NSA_OK || plan->T1 == 0)
+        return st == NSA_OK ? ok() : st;
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    nsa::SelParams a;
+    std::memset(&a, 0, sizeof a);
+    a.q = (const uint16_t*)query;
+    a.k = (const uint16_t*)key;
+    a.v = (const uint16_t*)value;
+    a.topk = topk_indices;
+    a.out = (uint16_t*)attention_out;
+    a.lse = softmax_lse;
+    a.bt = (const nsa::BatchEnt*)workspace;
+    a.B = (int)plan->B;
+    a.N1 = (int)plan->N1;
+    a.N2 = (int)plan->N2;
+    a.G = (int)(plan->N1 / plan->N2);
+    a.lsel = (int)plan->lsel;
+    a.count = (int)plan->count;
+    a.c = std::fmax(exp2_scale(plan), 1e-30f);
+    a.abs_scale = std::fabs(plan->scale);
+    a.thr = std::fmin(8.0f / a.c, 3.0e38f);
+    a.qsign = q_sign(plan);
+    a.sw = (int)std::max<int64_t>(1, (plan->S_max + 31) / 32);
+    a.tpw = 31 / a.G + 2;
+    const size_t lds = nsa::sel_attn_lds_bytes(a.tpw, a.sw);
+    hipError_t e = nsa::launch_sel_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, lds, s);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "selected-block attention launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

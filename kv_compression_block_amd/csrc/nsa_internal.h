@@ -115,6 +115,30 @@ struct TopkParams {
     int cand_words;
 };
 
+// ---- selected-block attention ------------------------------------------------
+struct SelParams {
+    const uint16_t* q;      // [T1, N1, D1]
+    const uint16_t* k;      // [T1, N2, D1] raw keys
+    const uint16_t* v;      // [T1, N2, D2] raw values
+    const int32_t* topk;    // [T1, N2, count]
+    uint16_t* out;          // [T1, N1, D2]
+    float* lse;             // [T1, N1]
+    const BatchEnt* bt;     // [B], device (tile_off_a / n_rb_a: 128 rows per workgroup)
+    int B, N1, N2, G;
+    int lsel, count;
+    float c;                // |scale| * log2(e)
+    float abs_scale;
+    float thr;              // running-max slack before rescaling, raw-score units
+    uint32_t qsign;
+    int sw;                 // 32-bit words per block set, ceil(max select blocks / 32)
+    int tpw;                // block sets per wave (tokens 32 rows can span)
+};
+
+bool sel_attn_supported(int d1, int d2);
+size_t sel_attn_lds_bytes(int tpw, int sw);   // dynamic LDS per workgroup
+hipError_t launch_sel_attn(int dtype, int d1, int d2, const SelParams& p, int n_tiles, size_t lds,
+                           hipStream_t stream);
+
 constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)
 constexpr int kTopkMaxNpl = 16;        // at most 1024 select blocks per sequence
 

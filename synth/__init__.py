@@ -202,3 +202,26 @@ def sample_tokens(wl: Workload, per_seq: int, rng_seed: int = 7) -> np.ndarray:
             if 0 <= t < T:
                 picks.append(int(s0 + t))
     return np.unique(np.array(picks, dtype=np.int64))
+
+
+def random_block_lists(wl: Workload, seed: int = 11, p_pad: float = 0.15, p_repeat: float = 0.05,
+                       p_bad: float = 0.03) -> np.ndarray:
+    """[T, N2, count] int32 lists of select-block indices drawn uniformly
+    from [0, ceil(T_b / l')) of each token's sequence, with seeded -1 padding,
+    repeats, and entries outside that range (past it, or negative other
+    than -1) -- inputs for the attention over selected blocks."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((wl.T, wl.N2, wl.count), dtype=np.int64)
+    s0 = 0
+    for T in wl.seqlens:
+        S = max(1, -(-T // wl.lsel))
+        blk = rng.integers(0, S, (T, wl.N2, wl.count))
+        u = rng.random((T, wl.N2, wl.count))
+        rep = np.roll(blk, 1, axis=2)
+        blk = np.where(u < p_repeat, rep, blk)
+        blk = np.where((u >= p_repeat) & (u < p_repeat + p_bad),
+                       np.where(rng.random(blk.shape) < 0.5, S + rng.integers(0, 3, blk.shape), -7), blk)
+        blk = np.where(rng.random(blk.shape) < p_pad, -1, blk)
+        out[s0:s0 + T] = blk
+        s0 += T
+    return out.astype(np.int32)

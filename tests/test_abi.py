@@ -205,3 +205,19 @@ def test_masked_calls_reject_before_touching_the_device():
     assert call(topk_short, big) == _lib.NSA_ERR_SHAPE
     assert call(topk_short, big, "nsa_compress_attention_select_masked") == _lib.NSA_ERR_SHAPE
     lib.nsa_plan_destroy(plan)
+
+
+def test_select_attention_rejects_before_touching_the_device():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    st, ws, plan = _ws(**_good())
+    assert lib.nsa_select_attention(plan, fake, fake, fake, None, fake, fake, fake, ws, None) \
+        == _lib.NSA_ERR_NULLPTR
+    assert lib.nsa_select_attention(plan, fake, fake, fake, fake, fake, fake, fake, ws - 1, None) \
+        == _lib.NSA_ERR_WORKSPACE
+    lib.nsa_plan_destroy(plan)
+    st, ws, plan = _ws(**_good(lsel=48, slen=[3, 8]))   # l' = 48: legal, not a multiple of 32
+    assert st == _lib.NSA_OK, lib.nsa_last_error()
+    assert lib.nsa_select_attention(plan, fake, fake, fake, fake, fake, fake, fake, ws, None) \
+        == _lib.NSA_ERR_UNSUPPORTED
+    lib.nsa_plan_destroy(plan)

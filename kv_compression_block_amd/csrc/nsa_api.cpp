@@ -83,7 +83,7 @@ struct nsa_plan_s {
     size_t ws_masked_bytes;           // workspace of the calls that take masks
     int log2gp, topk_waves, topk_kbufs, sb;
     size_t topk_lds;
-    int64_t tiles_a, tiles_c;
+    int64_t tiles_a, tiles_c, tiles_s;
     size_t ws_bytes;
     std::vector<nsa::BatchEnt> table;
 };
@@ -307,7 +307,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->sb = sb;
     plan->topk_lds = lds;
     plan->table.resize((size_t)batch);
-    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, S_total = 0, T_max = 0, ncmp_max = 0;
+    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, ts = 0, S_total = 0, T_max = 0, ncmp_max = 0;
     const int64_t rows_c = (int64_t)waves * 64;
     const int64_t rows_a = nsa::cmp_attn_rows_per_wg((int)d1, (int)d2);
     for (int64_t b = 0; b < batch; ++b) {
@@ -323,6 +323,9 @@ nsa_status nsa_compress_attention_get_workspace(
         e.n_rb_c = (int32_t)((T * (1 << log2gp) + rows_c - 1) / rows_c);
         e.tile_off_c = (int32_t)tc;
         e.S_sel = (int32_t)slen[(size_t)b];
+        e.n_rb_s = (int32_t)((T * G + nsa::kSelRows - 1) / nsa::kSelRows);
+        e.tile_off_s = (int32_t)ts;
+        ts += (int64_t)e.n_rb_s * kv_head_num;
         ta += (int64_t)e.n_rb_a * kv_head_num;
         tc += (int64_t)e.n_rb_c * kv_head_num;
         q_off += T;
@@ -331,7 +334,7 @@ nsa_status nsa_compress_attention_get_workspace(
         T_max = std::max(T_max, T);
         ncmp_max = std::max(ncmp_max, clen[(size_t)b]);
     }
-    if (ta > INT32_MAX || tc > INT32_MAX || q_off * head_num * 8 > ((int64_t)1 << 62)) {
+    if (ta > INT32_MAX || tc > INT32_MAX || ts > INT32_MAX || q_off * head_num * 8 > ((int64_t)1 << 62)) {
         delete plan;
         return fail(NSA_ERR_UNSUPPORTED, "problem too large for one launch");
     }
@@ -340,6 +343,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->S_total = S_total;
     plan->tiles_a = ta;
     plan->tiles_c = tc;
+    plan->tiles_s = ts;
     plan->ws_bytes = ((size_t)batch * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
     plan->T_max = T_max;
     plan->ncmp_max = ncmp_max;
@@ -753,9 +757,9 @@ nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* ke
     a.thr = std::fmin(8.0f / a.c, 3.0e38f);
     a.qsign = q_sign(plan);
     a.sw = (int)std::max<int64_t>(1, (plan->S_max + 31) / 32);
-    a.tpw = 31 / a.G + 2;
+    a.tpw = (nsa::kSelRows - 1) / a.G + 2;
     const size_t lds = nsa::sel_attn_lds_bytes(a.tpw, a.sw);
-    hipError_t e = nsa::launch_sel_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, lds, s);
+    hipError_t e = nsa::launch_sel_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_s, lds, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "selected-block attention launch failed: %s", hipGetErrorString(e));
     return ok();

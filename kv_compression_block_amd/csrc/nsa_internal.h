@@ -21,7 +21,9 @@ struct BatchEnt {
     int32_t tile_off_c; // first tile of the importance/top-k kernel
     int32_t n_rb_c;     // row blocks of the importance/top-k kernel
     int32_t S_sel;      // select blocks of the sequence, ceil(T / l')
-    int32_t pad[3];
+    int32_t tile_off_s; // first workgroup of the selected-block attention kernel
+    int32_t n_rb_s;     // row blocks of the selected-block attention kernel (per KV head)
+    int32_t pad;
 };
 static_assert(sizeof(BatchEnt) == 48, "BatchEnt layout");
 
@@ -131,9 +133,10 @@ struct SelParams {
     float thr;              // running-max slack before rescaling, raw-score units
     uint32_t qsign;
     int sw;                 // 32-bit words per block set, ceil(max select blocks / 32)
-    int tpw;                // block sets per wave (tokens 32 rows can span)
+    int tpw;                // block sets per workgroup (tokens its rows can span)
 };
 
+constexpr int kSelRows = 64;                  // (token, head) rows per workgroup
 bool sel_attn_supported(int d1, int d2);
 size_t sel_attn_lds_bytes(int tpw, int sw);   // dynamic LDS per workgroup
 hipError_t launch_sel_attn(int dtype, int d1, int d2, const SelParams& p, int n_tiles, size_t lds,

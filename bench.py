@@ -20,6 +20,11 @@ oracle on a bounded random sample of the same workload's tokens.
 ``--masks`` passes the workload's causal rules as explicit atten_mask /
 topk_mask tensors (the masked entry points: mask packing plus the
 every-tile masked kernels) instead of letting the kernels generate them.
+
+``--select-attention`` times instead the step that consumes the top-k: the
+attention of every query over the raw keys of its selected blocks
+(nsa_select_attention), fed with the top-k the compressed branch computes
+on the same inputs (computed once, untimed).
 """
 from __future__ import annotations
 
@@ -48,24 +53,29 @@ ATTN_SOURCES = ["kv_compression_block_amd/csrc/cmp_attn.hip", "kv_compression_bl
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_cmp_attn_fwd_batched-varlen-B16_hbm.json")
 
 
-def attn_source_digest() -> str:
+SEL_SOURCES = ["kv_compression_block_amd/csrc/sel_attn.hip", "kv_compression_block_amd/csrc/nsa_device.h",
+               "kv_compression_block_amd/csrc/nsa_internal.h", "kv_compression_block_amd/csrc/nsa_api.cpp"]
+SEL_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_sel_attn_fwd_batched-varlen-B16_hbm.json")
+
+
+def attn_source_digest(sources=None) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in ATTN_SOURCES:
+    for rel in (ATTN_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """Counted HBM bytes per attention launch, or None when there is no count
-    for this workload or the kernel changed since it was taken."""
+def measured_traffic(workload: str, record: str = TRAFFIC_RECORD, sources=None):
+    """Counted HBM bytes per launch of a kernel, or None when there is no
+    count for this workload or the kernel changed since it was taken."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(record) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("source_sha256") != attn_source_digest():
+    if rec.get("workload") != workload or rec.get("source_sha256") != attn_source_digest(sources):
         return None
     return float(rec["bytes_per_launch"])
 
@@ -130,6 +140,99 @@ def cpu_baseline(wl, inp, budget_s: float) -> dict:
             "seconds_measured": round(t_comp + t_att, 3)}
 
 
+def selected_pairs(wl, topk) -> int:
+    """Attended (token, key) pairs per KV head, summed: for each token and
+    KV head, the keys s <= t of the listed blocks (each block once)."""
+    import torch
+    total = 0
+    s0 = 0
+    for T in wl.seqlens:
+        S = -(-T // wl.lsel)
+        idx = topk[s0:s0 + T].long()                              # [T, N2, count]
+        idx, _ = torch.sort(idx, dim=2)
+        first = torch.ones_like(idx, dtype=torch.bool)
+        first[:, :, 1:] = idx[:, :, 1:] != idx[:, :, :-1]
+        valid = first & (idx >= 0) & (idx < S)
+        t = torch.arange(T, device=idx.device)[:, None, None]
+        keys = torch.clamp(t - idx * wl.lsel + 1, min=0, max=wl.lsel)
+        total += int(torch.where(valid, keys, torch.zeros_like(keys)).sum())
+        s0 += T
+    return total
+
+
+def select_attention_bench(args, wl, plan, inp, topk, ws, stream) -> dict:
+    """Times nsa_select_attention on the workload with the given top-k."""
+    import torch
+    import kv_compression_block_amd as nsa
+    dev = inp["q"].device
+    outs = {"attention_out": torch.empty((wl.T, wl.N1, wl.D2), dtype=wl.torch_dtype, device=dev),
+            "softmax_lse": torch.empty((wl.T, wl.N1), dtype=torch.float32, device=dev)}
+
+    def run():
+        nsa.nsa_select_attention(plan, inp["q"], inp["k"], inp["v"], topk, workspace=ws, outputs=outs,
+                                 stream=stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        run()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_kernel = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    pairs = selected_pairs(wl, topk)
+    flops = 2.0 * (wl.D1 + wl.D2) * pairs * (wl.N1 // wl.N2)
+    tflops = flops / (ms_kernel / 1e3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    return {
+        "metric": "query tokens/sec (selected-block attention over the top-k blocks)",
+        "value": wl.T / (ms_step / 1e3), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "N1": wl.N1, "N2": wl.N2, "D1": wl.D1,
+                   "D2": wl.D2, "lsel": wl.lsel, "count": wl.count, "scale": wl.scale, "dtype": wl.dtype,
+                   "block_lists": "the compressed branch's top-k on the same inputs",
+                   "parallelism": "single-gpu"},
+        "roofline": {"kernel": "k_sel_attn_fwd", "bound": "mfma", "achieved": tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": tflops / peak,
+                     "traffic": measured_traffic(wl.name, SEL_TRAFFIC_RECORD, SEL_SOURCES),
+                     "traffic_unit": "HBM bytes per launch",
+                     "work_per_launch": f"{flops:.4e} flop = 2*(D1+D2) x {pairs} attended (token, key) "
+                                        f"pairs per KV head x {wl.N1 // wl.N2} heads per group"},
+        "kernels": {"select_attention": {"ms": ms_kernel, "TFLOP/s": tflops}},
+        "cpu_baseline": None if args.no_cpu_baseline else select_cpu_baseline(wl, inp, topk, args.cpu_seconds),
+    }
+
+
+def select_cpu_baseline(wl, inp, topk, budget_s: float) -> dict:
+    """The oracle's selected-block attention on a bounded uniform sample of
+    tokens, scaled to all tokens."""
+    import oracle
+    import synth
+    b = {k: synth.bits(inp[k]) for k in ("q", "k", "v")}
+    tk = topk.cpu().numpy()
+    rng = np.random.default_rng(4321)
+
+    def run(tokens):
+        t = time.perf_counter()
+        oracle.select_attention(b["q"], b["k"], b["v"], tk, wl.act_seq_qlen, wl.N1, wl.N2, wl.scale,
+                                wl.lsel, tokens=tokens, dtype=wl.dtype)
+        return time.perf_counter() - t
+
+    pilot = np.sort(rng.choice(wl.T, 64, replace=False)).astype(np.int64)
+    tp = run(pilot)
+    n = int(min(wl.T, max(64, 64 * budget_s / max(tp, 1e-6))))
+    sample = np.sort(rng.choice(wl.T, n, replace=False)).astype(np.int64)
+    ts = run(sample)
+    return {"value": n / ts, "unit": "query tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"selected-block attention for {n} of {wl.T} tokens drawn uniformly ({ts:.2f} s)",
+            "seconds_measured": round(tp + ts, 3)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +243,8 @@ def main() -> int:
                     help="element type of q, k, v and the weight (default bf16)")
     ap.add_argument("--masks", action="store_true",
                     help="give the causal rules as explicit atten_mask / topk_mask tensors")
+    ap.add_argument("--select-attention", action="store_true",
+                    help="time the selected-block attention over the compressed branch's top-k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -230,6 +335,14 @@ def main() -> int:
                                           topk_mask=masks.get("topk_mask"))
         if ev is not None:
             ev[4].record(stream)
+
+    if args.select_attention:
+        step()
+        torch.cuda.synchronize()
+        res = select_attention_bench(args, wl, plan, inp, outs["topk_indices"], ws, stream)
+        plan.destroy()
+        print(json.dumps(res), flush=True)
+        return 0
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

@@ -13,7 +13,9 @@ order the operator pages give them:
   (scores, mask, softmax, output, importance remap, group sum, top-k);
 * ``select_attention`` -- attention over the raw keys of the selected
   blocks, the consumer of the top-k indices (interface of
-  "lite_boost.ops.rain_fusion_attention").
+  "lite_boost.ops.rain_fusion_attention");
+* ``attention_backward`` / ``compress_backward`` -- the derivatives of the
+  compressed attention output and of the compression, for training.
 
 The compressed keys/values that feed attention are the compression results
 rounded to the element type of the inputs (round to nearest, ties to even),
@@ -88,6 +90,11 @@ def _load():
     lib.nsa_oracle_select_attention.argtypes = [P, P, P, P, P, I64, P, I64, I64, I64, I64, I64,
                                                 ctypes.c_double, I64, I64, ctypes.c_int, P, P]
     lib.nsa_oracle_select_attention.restype = ctypes.c_int
+    lib.nsa_oracle_attention_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64,
+                                                  ctypes.c_double, I64, I64, ctypes.c_int, P, P, P]
+    lib.nsa_oracle_attention_backward.restype = ctypes.c_int
+    lib.nsa_oracle_compress_backward.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_int, P, P]
+    lib.nsa_oracle_compress_backward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -306,3 +313,42 @@ def select_attention(q_bits, k_bits, v_bits, topk, act_seq_qlen, N1: int, N2: in
     if rc != 0:
         raise ValueError(f"nsa_oracle_select_attention returned {rc}")
     return {"out": out, "lse": lse}
+
+
+def attention_backward(q_bits, kc_bits, vc_bits, dout_bits, act_seq_qlen, act_cmp_seq_kvlen,
+                       N1: int, N2: int, scale: float, l: int, d: int, dtype: str = "bf16") -> dict:
+    """Gradients of steps 1-3 with respect to q, kc and vc for the gradient
+    dout [T1, N1, D2] of attention_out (all of element type ``dtype``).
+    Returns dict(dq [T1,N1,D1], dkc [T2,N2,D1], dvc [T2,N2,D2]) in float64."""
+    q, kc, vc, do = _u16(q_bits), _u16(kc_bits), _u16(vc_bits), _u16(dout_bits)
+    T1, D1 = q.shape[0], q.shape[2]
+    T2, D2 = kc.shape[0], vc.shape[2]
+    if q.shape[1] != N1 or kc.shape[1:] != (N2, D1) or vc.shape[:2] != (T2, N2) or do.shape != (T1, N1, D2):
+        raise ValueError("shapes of q, kc, vc, dout do not match")
+    actq, actc = _i64(act_seq_qlen), _i64(act_cmp_seq_kvlen)
+    dq = np.empty((T1, N1, D1)); dkc = np.empty((T2, N2, D1)); dvc = np.empty((T2, N2, D2))
+    rc = _load().nsa_oracle_attention_backward(_ptr(q), _ptr(kc), _ptr(vc), _ptr(do), _ptr(actq), _ptr(actc),
+                                               len(actq), N1, N2, D1, D2, float(scale), l, d, _code(dtype),
+                                               _ptr(dq), _ptr(dkc), _ptr(dvc))
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_attention_backward returned {rc}")
+    return {"dq": dq, "dkc": dkc, "dvc": dvc}
+
+
+def compress_backward(x_bits, w_bits, dy, act_seq_len, l: int, d: int, dtype: str = "bf16") -> dict:
+    """Gradients of the compression for the output gradient dy [T2, N, D]
+    (float64): dict(dx [T, N, D], dw [l, N]) in float64."""
+    x, w = _u16(x_bits), _u16(w_bits)
+    T, N, D = x.shape
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    act = _i64(act_seq_len)
+    starts = np.concatenate([[0], act[:-1]])
+    T2 = int(sum(n_cmp(int(e - s0), l, d) for s0, e in zip(starts, act)))
+    if dy.shape != (T2, N, D) or w.shape != (l, N):
+        raise ValueError(f"dy must be {(T2, N, D)} and w {(l, N)}")
+    dx = np.empty((T, N, D)); dw = np.empty((l, N))
+    rc = _load().nsa_oracle_compress_backward(_ptr(x), _ptr(w), _ptr(dy), _ptr(act), len(act), N, D, l, d,
+                                              _code(dtype), _ptr(dx), _ptr(dw))
+    if rc != 0:
+        raise ValueError(f"nsa_oracle_compress_backward returned {rc}")
+    return {"dx": dx, "dw": dw}

@@ -564,3 +564,151 @@ int nsa_oracle_select_attention(const uint16_t* q, const uint16_t* k, const uint
     }
     return err;
 }
+
+/* ---- backward of compression and compressed attention ---------------------
+ *
+ * The pages state the training use of the operator (the softmax max and sum
+ * outputs are kept for it) but give no backward formulas; these are the
+ * derivatives of the forward definitions above, taken with respect to the
+ * loss's gradient dout of attention_out only (softmax_max / softmax_sum are
+ * statistics, the top-k indices carry no gradient).  Per query row (t, h)
+ * with visible blocks i, P_i the softmax, O = sum_i P_i vc_i:
+ *   dvc_i += P_i * dout,   dP_i = dout . vc_i,   Dlt = sum_i P_i dP_i,
+ *   dS_i = P_i (dP_i - Dlt),   dq = scale sum_i dS_i kc_i,
+ *   dkc_i += scale dS_i q.
+ * The forward is recomputed from its definition in float64.
+ */
+int nsa_oracle_attention_backward(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                                  const uint16_t* dout, const int64_t* act_seq_qlen,
+                                  const int64_t* act_cmp_seq_kvlen, int64_t B, int64_t N1,
+                                  int64_t N2, int64_t D1, int64_t D2, double scale, int64_t l,
+                                  int64_t d, int dtype, double* dq, double* dkc, double* dvc)
+{
+    if (N2 < 1 || N1 % N2 != 0 || d < 1 || l < 1 || B < 1 || dtype < 0 || dtype > 1)
+        return -1;
+    const int64_t G = N1 / N2;
+    const int64_t T1 = act_seq_qlen[B - 1], T2 = act_cmp_seq_kvlen[B - 1];
+    for (int64_t x = 0; x < T1 * N1 * D1; ++x)
+        dq[x] = 0.0;
+    for (int64_t x = 0; x < T2 * N2 * D1; ++x)
+        dkc[x] = 0.0;
+    for (int64_t x = 0; x < T2 * N2 * D2; ++x)
+        dvc[x] = 0.0;
+    int64_t n_cmp_max = 1;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t nc = act_cmp_seq_kvlen[b] - seq_start(act_cmp_seq_kvlen, b);
+        if (nc > n_cmp_max) n_cmp_max = nc;
+    }
+    int err = 0;
+    /* one (sequence, KV head) per iteration: its dkc / dvc rows and its
+     * queries' dq rows are written by it alone */
+#pragma omp parallel
+    {
+        double* P = (double*)malloc(sizeof(double) * (size_t)n_cmp_max);
+        double* dP = (double*)malloc(sizeof(double) * (size_t)n_cmp_max);
+        if (!P || !dP) {
+#pragma omp atomic write
+            err = -4;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bg = 0; bg < B * N2; ++bg) {
+                const int64_t b = bg / N2, g = bg % N2;
+                const int64_t q0 = seq_start(act_seq_qlen, b), T = act_seq_qlen[b] - q0;
+                const int64_t c0 = seq_start(act_cmp_seq_kvlen, b);
+                const int64_t nc = act_cmp_seq_kvlen[b] - c0;
+                for (int64_t t = 0; t < T; ++t) {
+                    int64_t nv = 0;
+                    while (nv < nc && nv * d + l - 1 <= t)
+                        ++nv;
+                    if (nv == 0)
+                        continue;
+                    for (int64_t hh = 0; hh < G; ++hh) {
+                        const int64_t h = g * G + hh;
+                        const uint16_t* qh = q + ((q0 + t) * N1 + h) * D1;
+                        const uint16_t* doh = dout + ((q0 + t) * N1 + h) * D2;
+                        double m = -INFINITY;
+                        for (int64_t i = 0; i < nv; ++i) {
+                            const uint16_t* ki = kc + ((c0 + i) * N2 + g) * D1;
+                            double dot = 0.0;
+                            for (int64_t e = 0; e < D1; ++e)
+                                dot += widen(dtype, qh[e]) * widen(dtype, ki[e]);
+                            P[i] = scale * dot;
+                            if (P[i] > m)
+                                m = P[i];
+                        }
+                        double L = 0.0;
+                        for (int64_t i = 0; i < nv; ++i) {
+                            P[i] = exp(P[i] - m);
+                            L += P[i];
+                        }
+                        double Dlt = 0.0;
+                        for (int64_t i = 0; i < nv; ++i) {
+                            P[i] /= L;
+                            const uint16_t* vi = vc + ((c0 + i) * N2 + g) * D2;
+                            double acc = 0.0;
+                            for (int64_t e = 0; e < D2; ++e)
+                                acc += widen(dtype, doh[e]) * widen(dtype, vi[e]);
+                            dP[i] = acc;
+                            Dlt += P[i] * acc;
+                        }
+                        double* dqh = dq + ((q0 + t) * N1 + h) * D1;
+                        for (int64_t i = 0; i < nv; ++i) {
+                            const double dS = P[i] * (dP[i] - Dlt);
+                            const uint16_t* ki = kc + ((c0 + i) * N2 + g) * D1;
+                            double* dki = dkc + ((c0 + i) * N2 + g) * D1;
+                            double* dvi = dvc + ((c0 + i) * N2 + g) * D2;
+                            for (int64_t e = 0; e < D1; ++e) {
+                                dqh[e] += scale * dS * widen(dtype, ki[e]);
+                                dki[e] += scale * dS * widen(dtype, qh[e]);
+                            }
+                            for (int64_t e = 0; e < D2; ++e)
+                                dvi[e] += P[i] * widen(dtype, doh[e]);
+                        }
+                    }
+                }
+            }
+        }
+        free(P);
+        free(dP);
+    }
+    return err;
+}
+
+/* Backward of the compression: y[i, n, :] = sum_p w[p, n] x[start + i*d + p, n, :]
+ * gives dx[start + i*d + p, n, :] += w[p, n] dy[i, n, :] and
+ * dw[p, n] = sum over sequences, windows i and dims e of
+ * dy[i, n, e] * x[start + i*d + p, n, e].  Rows in no window get 0. */
+int nsa_oracle_compress_backward(const uint16_t* x, const uint16_t* w, const double* dy,
+                                 const int64_t* act_seq_len, int64_t B, int64_t N, int64_t D,
+                                 int64_t l, int64_t d, int dtype, double* dx, double* dw)
+{
+    if (B < 1 || N < 1 || D < 1 || l < 1 || d < 1 || dtype < 0 || dtype > 1)
+        return -1;
+    const int64_t T = act_seq_len[B - 1];
+    for (int64_t k = 0; k < T * N * D; ++k)
+        dx[k] = 0.0;
+    for (int64_t k = 0; k < l * N; ++k)
+        dw[k] = 0.0;
+    int64_t out_row = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t start = seq_start(act_seq_len, b);
+        const int64_t n = nsa_oracle_n_cmp(act_seq_len[b] - start, l, d);
+        for (int64_t i = 0; i < n; ++i) {
+            for (int64_t h = 0; h < N; ++h) {
+                const double* dyi = dy + ((out_row + i) * N + h) * D;
+                for (int64_t p = 0; p < l; ++p) {
+                    const int64_t row = start + i * d + p;
+                    const double wp = widen(dtype, w[p * N + h]);
+                    double acc = 0.0;
+                    for (int64_t e = 0; e < D; ++e) {
+                        dx[(row * N + h) * D + e] += wp * dyi[e];
+                        acc += dyi[e] * widen(dtype, x[(row * N + h) * D + e]);
+                    }
+                    dw[p * N + h] += acc;
+                }
+            }
+        }
+        out_row += n;
+    }
+    return 0;
+}

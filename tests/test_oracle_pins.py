@@ -917,3 +917,102 @@ def test_select_attention_ignores_repeats_padding_and_out_of_range():
     a = oracle.select_attention(q, k, v, clean, lens, N1, N2, 0.3, lsel)
     b = oracle.select_attention(q, k, v, noisy, lens, N1, N2, 0.3, lsel)
     assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["lse"], b["lse"])
+
+
+# --------------------------------------------------------------------------
+# Backward (training use; the pages give no formulas): gradients of the
+# compressed attention output and of the compression, against torch
+# autograd of the forward written out in float64.
+# --------------------------------------------------------------------------
+
+def test_attention_backward_matches_torch_autograd():
+    lens = [90, 41, 130]
+    N1, N2, D1, D2, l, d = 6, 2, 16, 8, 32, 16
+    scale = -0.3                                   # a negative scale too
+    rng = np.random.default_rng(50)
+    q, kc, vc = _attention_case(50, lens, N1, N2, D1, D2, l, d)
+    do = rand_bf16(rng, (sum(lens), N1, D2))
+    actq, actc = np.cumsum(lens), oracle.cmp_prefix(lens, l, d)
+    res = oracle.attention_backward(q, kc, vc, do, actq, actc, N1, N2, scale, l, d)
+    qf, kf, vf, dof = (widen_torch(a, "bf16").clone().requires_grad_(True) for a in (q, kc, vc, do))
+    cst = np.concatenate([[0], actc[:-1]])
+    G = N1 // N2
+    loss = torch.zeros((), dtype=torch.float64)
+    for b, (s0, T) in enumerate(zip(starts_of(lens), lens)):
+        nc = int(actc[b] - cst[b])
+        if nc == 0:
+            continue
+        t = torch.arange(T)[:, None]
+        i = torch.arange(nc)[None, :]
+        mask = (i * d + l - 1) <= t
+        has = mask.any(dim=1)
+        for h in range(N1):
+            g = h // G
+            sc = scale * (qf[s0:s0 + T, h] @ kf[cst[b]:cst[b] + nc, g].T)
+            sc = torch.where(mask, sc, torch.tensor(-float("inf"), dtype=torch.float64))
+            p = torch.softmax(sc[has], dim=1)
+            out = p @ vf[cst[b]:cst[b] + nc, g]
+            loss = loss + (out * dof.detach()[s0:s0 + T, h][has]).sum()
+    loss.backward()
+    np.testing.assert_allclose(res["dq"], qf.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(res["dkc"], kf.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(res["dvc"], vf.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.abs(res["dkc"]).max() > 0.1 and np.abs(res["dq"]).max() > 0.1
+
+
+def test_compress_backward_matches_torch_autograd():
+    rng = np.random.default_rng(51)
+    l, d, N, D = 32, 16, 2, 8
+    lens = [140, 33, 70]
+    x = rand_bf16(rng, (sum(lens), N, D))
+    w = rand_bf16(rng, (l, N), std=0.1)
+    T2 = int(oracle.cmp_prefix(lens, l, d)[-1])
+    dy = rng.standard_normal((T2, N, D))
+    res = oracle.compress_backward(x, w, dy, np.cumsum(lens), l, d)
+    xf = widen_torch(x, "bf16").clone().requires_grad_(True)
+    wf = widen_torch(w, "bf16").clone().requires_grad_(True)
+    ys = []
+    for s0, T in zip(starts_of(lens), lens):
+        for i in range(oracle.n_cmp(T, l, d)):
+            ys.append(torch.einsum("pn,pnd->nd", wf, xf[s0 + i * d:s0 + i * d + l]))
+    y = torch.stack(ys)
+    (y * torch.from_numpy(dy)).sum().backward()
+    np.testing.assert_allclose(res["dx"], xf.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(res["dw"], wf.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_backward_finite_differences():
+    """Central differences of <attention_out, dout> in float64 along a few
+    random directions of q, kc and vc match the oracle's gradients."""
+    lens = [70]
+    N1, N2, D1, D2, l, d, lsel = 2, 1, 8, 4, 32, 16, 64
+    rng = np.random.default_rng(52)
+    q, kc, vc = _attention_case(52, lens, N1, N2, D1, D2, l, d)
+    do = rand_bf16(rng, (70, N1, D2))
+    actq, actc = np.array([70]), oracle.cmp_prefix(lens, l, d)
+    g = oracle.attention_backward(q, kc, vc, do, actq, actc, N1, N2, 0.5, l, d)
+    dof = oracle.bf16_to_f64(do)
+    base = [oracle.bf16_to_f64(a) for a in (q, kc, vc)]
+
+    def f(qv, kv, vv):
+        # the forward in float64 from float64 inputs: softmax over visible blocks
+        tot = 0.0
+        for t in range(70):
+            nv = n_vis_of(t, l, d, kv.shape[0])
+            for h in range(N1):
+                if nv == 0:
+                    continue
+                sc = 0.5 * kv[:nv, 0] @ qv[t, h]
+                pr = np.exp(sc - sc.max())
+                pr /= pr.sum()
+                tot += (pr @ vv[:nv, 0]) @ dof[t, h]
+        return tot
+
+    eps = 1e-5
+    for which, key in enumerate(["dq", "dkc", "dvc"]):
+        direction = rng.standard_normal(base[which].shape)
+        plus = list(base); minus = list(base)
+        plus[which] = base[which] + eps * direction
+        minus[which] = base[which] - eps * direction
+        fd = (f(*plus) - f(*minus)) / (2 * eps)
+        assert abs(fd - float((g[key] * direction).sum())) <= 1e-6 * max(1.0, abs(fd)), key

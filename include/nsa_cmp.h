@@ -300,6 +300,41 @@ nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* ke
                                 void* attention_out, float* softmax_lse, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * nsa_compress_attention_backward -- gradients of steps 1-3 of
+ * "mindspore.ops.nsa_compress_attention" for training (the pages keep the
+ * softmax max and sum for this use but give no formulas).  With the
+ * forward's P = exp(scale * q.k_i - softmax_max) / softmax_sum over the
+ * visible blocks and d_attention_out = dout:
+ *   d_value[i]  = sum over the rows that see i of P_i * dout
+ *   dP_i = dout . value[i],  Delta = dout . attention_out,
+ *   dS_i = P_i * (dP_i - Delta)
+ *   d_query     = scale * sum_i dS_i * key[i]
+ *   d_key[i]    = scale * sum over the rows that see i of dS_i * query
+ * (GQA: the heads of a KV group add into its key / value rows).  The top-k
+ * indices carry no gradient; softmax_max / softmax_sum are treated as
+ * statistics, not outputs with a gradient.
+ *
+ *   query, key, value   the forward's inputs ([T1,N1,d1], [T2,N2,d1], [T2,N2,d2])
+ *   attention_out       the forward's output [T1, N1, d2]
+ *   d_attention_out     [T1, N1, d2], the element type of the plan
+ *   softmax_max/sum     the forward's [T1, N1, 8] float32 outputs
+ *   d_query             [T1, N1, d1] float32, written
+ *   d_key, d_value      [T2, N2, d1] / [T2, N2, d2] float32, written (the
+ *                       gradients of the compressed key / value; pass them to
+ *                       nsa_compress_backward for the raw ones)
+ *   workspace           >= backward_workspace_bytes (plan info)
+ * Results are bitwise repeatable (fixed summation orders, no atomics).
+ * Errors: NSA_ERR_NULLPTR, NSA_ERR_WORKSPACE, NSA_ERR_CONSTRAINT (misaligned
+ * pointer), NSA_ERR_UNSUPPORTED (head dims not built), NSA_ERR_HIP.
+ */
+nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, const void* key,
+                                          const void* value, const void* attention_out,
+                                          const void* d_attention_out, const float* softmax_max,
+                                          const float* softmax_sum, float* d_query, float* d_key,
+                                          float* d_value, void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
 /* Sizes a plan fixed, for callers that allocate outputs from a plan. */
 typedef struct nsa_plan_info {
     int64_t batch;
@@ -311,6 +346,7 @@ typedef struct nsa_plan_info {
     size_t workspace_bytes;
     int64_t dtype;              /* the nsa_dtype the plan was made for */
     size_t masked_workspace_bytes;  /* workspace of the calls given a mask */
+    size_t backward_workspace_bytes;  /* workspace of nsa_compress_attention_backward */
 } nsa_plan_info;
 
 nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info);

@@ -35,7 +35,8 @@ from ._lib import Masks, NsaError, PlanInfo  # noqa: F401
 
 __all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_workspace",
            "nsa_compress_attention", "nsa_compress_attention_fwd", "nsa_compress_attention_select",
-           "nsa_select_attention", "compress_attention", "Plan", "NsaError", "library_path"]
+           "nsa_select_attention", "nsa_compress_attention_backward", "compress_attention", "Plan",
+           "NsaError", "library_path"]
 
 
 def library_path() -> str:
@@ -379,3 +380,36 @@ def nsa_select_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, val
                                           _stream_ptr(query.device, stream))
     _lib.check(st)
     return o["attention_out"], o["softmax_lse"]
+
+
+def nsa_compress_attention_backward(plan: Plan, query, key, value, attention_out, d_attention_out,
+                                    softmax_max, softmax_sum, workspace: Optional[torch.Tensor] = None,
+                                    stream=None):
+    """Gradients of the compressed attention output with respect to query,
+    key and value (the compressed ones), float32: (d_query [T1, N1, D1],
+    d_key [T2, N2, D1], d_value [T2, N2, D2])."""
+    _check_qkv(plan, query, key, value)
+    info = plan.info
+    T1, N1, N2, D1, D2, T2 = (info["total_q_tokens"], info["head_num"], info["kv_head_num"], info["d1"],
+                              info["d2"], info["total_cmp_tokens"])
+    for t, name in ((attention_out, "attention_out"), (d_attention_out, "d_attention_out")):
+        _need_tensor(t, name)
+        if tuple(t.shape) != (T1, N1, D2) or t.dtype != query.dtype:
+            raise ValueError(f"{name} must be {(T1, N1, D2)} of the query's dtype")
+    for t, name in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
+        _need_tensor(t, name)
+        if t.dtype != torch.float32 or tuple(t.shape) != (T1, N1, 8):
+            raise ValueError(f"{name} must be float32 [T1, N1, 8]")
+    dev = query.device
+    dq = torch.empty((T1, N1, D1), dtype=torch.float32, device=dev)
+    dk = torch.empty((T2, N2, D1), dtype=torch.float32, device=dev)
+    dv = torch.empty((T2, N2, D2), dtype=torch.float32, device=dev)
+    need = info["backward_workspace_bytes"]
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    st = _lib.load().nsa_compress_attention_backward(
+        plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(attention_out), _ptr(d_attention_out),
+        _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream_ptr(dev, stream))
+    _lib.check(st)
+    return dq, dk, dv

@@ -35,6 +35,7 @@ EXPORTS = (
     "nsa_compress_attention_fwd_masked",
     "nsa_compress_attention_select_masked",
     "nsa_select_attention",
+    "nsa_compress_attention_backward",
     "nsa_plan_get_info",
     "nsa_plan_destroy",
     "nsa_status_string",
@@ -57,6 +58,7 @@ class PlanInfo(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("dtype", ctypes.c_int64),
         ("masked_workspace_bytes", ctypes.c_size_t),
+        ("backward_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -110,6 +112,8 @@ def load() -> ctypes.CDLL:
     lib.nsa_compress_attention_select_masked.restype = I32
     lib.nsa_select_attention.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_select_attention.restype = I32
+    lib.nsa_compress_attention_backward.argtypes = [P] * 12 + [ctypes.c_size_t, P]
+    lib.nsa_compress_attention_backward.restype = I32
     lib.nsa_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.nsa_plan_get_info.restype = I32
     lib.nsa_plan_destroy.argtypes = [P]

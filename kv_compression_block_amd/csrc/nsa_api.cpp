@@ -81,6 +81,8 @@ struct nsa_plan_s {
     int64_t T_max, ncmp_max;          // longest sequence, most compressed entries
     int64_t vis_words, cand_words;    // packed mask row lengths (32-bit words)
     size_t ws_masked_bytes;           // workspace of the calls that take masks
+    size_t ws_bwd_bytes;              // workspace of the backward call
+    int64_t tiles_k;                  // workgroups of the key-side backward kernel
     int log2gp, topk_waves, topk_kbufs, sb;
     size_t topk_lds;
     int64_t tiles_a, tiles_c, tiles_s;
@@ -307,7 +309,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->sb = sb;
     plan->topk_lds = lds;
     plan->table.resize((size_t)batch);
-    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, ts = 0, S_total = 0, T_max = 0, ncmp_max = 0;
+    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, ts = 0, tk = 0, S_total = 0, T_max = 0, ncmp_max = 0;
     const int64_t rows_c = (int64_t)waves * 64;
     const int64_t rows_a = nsa::cmp_attn_rows_per_wg((int)d1, (int)d2);
     for (int64_t b = 0; b < batch; ++b) {
@@ -326,6 +328,8 @@ nsa_status nsa_compress_attention_get_workspace(
         e.n_rb_s = (int32_t)((T * G + nsa::kSelRows - 1) / nsa::kSelRows);
         e.tile_off_s = (int32_t)ts;
         ts += (int64_t)e.n_rb_s * kv_head_num;
+        e.tile_off_k = (int32_t)tk;
+        tk += (clen[(size_t)b] + 31) / 32 * kv_head_num;
         ta += (int64_t)e.n_rb_a * kv_head_num;
         tc += (int64_t)e.n_rb_c * kv_head_num;
         q_off += T;
@@ -344,6 +348,7 @@ nsa_status nsa_compress_attention_get_workspace(
     plan->tiles_a = ta;
     plan->tiles_c = tc;
     plan->tiles_s = ts;
+    plan->tiles_k = tk;
     plan->ws_bytes = ((size_t)batch * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
     plan->T_max = T_max;
     plan->ncmp_max = ncmp_max;
@@ -353,6 +358,7 @@ nsa_status nsa_compress_attention_get_workspace(
     const size_t cand_bytes = ((size_t)T_max * (size_t)plan->cand_words * 4 + 255) / 256 * 256;
     const size_t span_bytes = ((size_t)T_max * 16 + 255) / 256 * 256;
     plan->ws_masked_bytes = plan->ws_bytes + vis_bytes + cand_bytes + span_bytes;
+    plan->ws_bwd_bytes = plan->ws_bytes + ((size_t)q_off * (size_t)head_num * 8 + 255) / 256 * 256;
     *workspace_bytes = plan->ws_bytes;
     *plan_out = plan;
     return ok();
@@ -375,6 +381,7 @@ nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info)
     info->workspace_bytes = plan->ws_bytes;
     info->dtype = plan->dtype;
     info->masked_workspace_bytes = plan->ws_masked_bytes;
+    info->backward_workspace_bytes = plan->ws_bwd_bytes;
     return ok();
 }
 
@@ -762,6 +769,65 @@ nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* ke
     hipError_t e = nsa::launch_sel_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_s, lds, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "selected-block attention launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, const void* key,
+                                          const void* value, const void* attention_out,
+                                          const void* d_attention_out, const float* softmax_max,
+                                          const float* softmax_sum, float* d_query, float* d_key,
+                                          float* d_value, void* workspace, size_t workspace_bytes,
+                                          void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->T1 > 0 && (!query || !attention_out || !d_attention_out || !softmax_max || !softmax_sum || !d_query))
+        return fail(NSA_ERR_NULLPTR, "query, attention_out, its gradient, the softmax statistics and d_query must not be NULL");
+    if (plan->T2 > 0 && (!key || !value || !d_key || !d_value))
+        return fail(NSA_ERR_NULLPTR, "key, value, d_key and d_value must not be NULL");
+    if (!nsa::attn_bwd_supported((int)plan->D1, (int)plan->D2))
+        return fail(NSA_ERR_UNSUPPORTED, "head dims (%lld, %lld) are not built for the backward",
+                    (long long)plan->D1, (long long)plan->D2);
+    if (workspace_bytes < plan->ws_bwd_bytes || !workspace)
+        return fail(NSA_ERR_WORKSPACE, "the backward needs %zu workspace bytes, %zu given", plan->ws_bwd_bytes,
+                    workspace_bytes);
+    nsa_status st = check_exec(plan, workspace, workspace_bytes,
+                               {query, key, value, attention_out, d_attention_out, softmax_max, softmax_sum,
+                                d_query, d_key, d_value, workspace}, {});
+    if (st != NSA_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (plan->T1 == 0)
+        return ok();
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    nsa::BwdParams a;
+    std::memset(&a, 0, sizeof a);
+    a.q = (const uint16_t*)query;
+    a.kc = (const uint16_t*)key;
+    a.vc = (const uint16_t*)value;
+    a.out = (const uint16_t*)attention_out;
+    a.dout = (const uint16_t*)d_attention_out;
+    a.smax = softmax_max;
+    a.ssum = softmax_sum;
+    a.dq = d_query;
+    a.dkc = d_key;
+    a.dvc = d_value;
+    a.rowstat = (float*)((char*)workspace + plan->ws_bytes);
+    a.bt = (const nsa::BatchEnt*)workspace;
+    a.B = (int)plan->B;
+    a.N1 = (int)plan->N1;
+    a.N2 = (int)plan->N2;
+    a.G = (int)(plan->N1 / plan->N2);
+    a.l = (int)plan->l;
+    a.d = (int)plan->d;
+    a.c = std::fmax(exp2_scale(plan), 1e-30f);
+    a.scale = plan->scale;
+    a.qsign = q_sign(plan);
+    hipError_t e = nsa::launch_attn_bwd(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a,
+                                        (int)plan->tiles_k, s);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -23,7 +23,7 @@ struct BatchEnt {
     int32_t S_sel;      // select blocks of the sequence, ceil(T / l')
     int32_t tile_off_s; // first workgroup of the selected-block attention kernel
     int32_t n_rb_s;     // row blocks of the selected-block attention kernel (per KV head)
-    int32_t pad;
+    int32_t tile_off_k; // first workgroup of the key-side backward kernel (32 entries each, per KV head)
 };
 static_assert(sizeof(BatchEnt) == 48, "BatchEnt layout");
 
@@ -140,6 +140,31 @@ constexpr int kSelRows = 64;                  // (token, head) rows per workgrou
 bool sel_attn_supported(int d1, int d2);
 size_t sel_attn_lds_bytes(int tpw, int sw);   // dynamic LDS per workgroup
 hipError_t launch_sel_attn(int dtype, int d1, int d2, const SelParams& p, int n_tiles, size_t lds,
+                           hipStream_t stream);
+
+// ---- backward of the compressed attention -------------------------------------
+struct BwdParams {
+    const uint16_t* q;     // [T1, N1, D1]
+    const uint16_t* kc;    // [T2, N2, D1]
+    const uint16_t* vc;    // [T2, N2, D2]
+    const uint16_t* out;   // [T1, N1, D2] forward attention_out
+    const uint16_t* dout;  // [T1, N1, D2] gradient of attention_out
+    const float* smax;     // [T1, N1, 8] forward softmax_max
+    const float* ssum;     // [T1, N1, 8] forward softmax_sum
+    float* dq;             // [T1, N1, D1]
+    float* dkc;            // [T2, N2, D1]
+    float* dvc;            // [T2, N2, D2]
+    float* rowstat;        // workspace [T1 * N1][2]: exponent bias and Delta = dout . out per row
+    const BatchEnt* bt;    // [B], device
+    int B, N1, N2, G;
+    int l, d;
+    float c;               // |scale| * log2(e)
+    float scale;           // signed scale
+    uint32_t qsign;        // 0x80008000 when scale < 0 (q negated), else 0
+};
+
+bool attn_bwd_supported(int d1, int d2);
+hipError_t launch_attn_bwd(int dtype, int d1, int d2, const BwdParams& p, int tiles_q, int tiles_k,
                            hipStream_t stream);
 
 constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)

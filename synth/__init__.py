@@ -225,3 +225,10 @@ def random_block_lists(wl: Workload, seed: int = 11, p_pad: float = 0.15, p_repe
         out[s0:s0 + T] = blk
         s0 += T
     return out.astype(np.int32)
+
+
+def make_output_grad(wl: Workload, device="cpu", seed: int = 77, chunk_rows: int = 8192) -> torch.Tensor:
+    """A seeded N(0, 1) gradient for attention_out [T, N1, D2] in the
+    workload's element type (for the backward)."""
+    return _draw((wl.T, wl.N1, wl.D2), (wl.seed * 1_000_003 + seed * 7919) & 0x7FFF_FFFF_FFFF, device,
+                 "normal", 1.0, chunk_rows, wl.torch_dtype)

@@ -1,0 +1,78 @@
+"""GPU parity of the backward of the compressed attention against the
+oracle (the derivatives of the forward definition; the pages give no
+backward formulas).  The GPU backward runs on the GPU forward's own
+outputs (attention_out, softmax max and sum) over the oracle's compressed
+K/V; the oracle recomputes the forward in float64.
+
+Tolerance (gradients are sums of products of bf16-rounded factors; dS is
+rounded to the element type before its MFMA, Delta uses the rounded
+attention_out): per tensor, max |gpu - oracle| <= 2e-2 * max |oracle| and
+||gpu - oracle||_2 <= 1e-2 * ||oracle||_2.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import gpu_prefix, log, to_f64, upload_bits
+
+import kv_compression_block_amd as nsa
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    0: synth.WORKLOADS[0],
+    1: synth.small_variant(1, [900, 333]),
+    2: synth.small_variant(2, [700, 1030, 64, 17]),
+    3: synth.small_variant(3, [1500]),
+    4: synth.small_variant(4, [1000, 600, 130]),
+}
+NEG = dataclasses.replace(synth.WORKLOADS[0], name="negative-scale-bwd", N1=8, N2=2, scale=-0.09,
+                          seqlens=(400, 77))
+
+
+def assert_grad_close(got: np.ndarray, ref: np.ndarray, what: str):
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    scale = float(np.abs(ref).max(initial=0.0))
+    dmax = float(np.abs(got - ref).max(initial=0.0))
+    rel2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+    log(f"  {what}: max|err| {dmax:.3e} of max|ref| {scale:.3e}; rel L2 {rel2:.3e}")
+    assert dmax <= 2e-2 * scale + 1e-30, what
+    assert rel2 <= 1e-2, what
+
+
+def _run(wl, keys=("dq",)):
+    log(f"[case] {wl.name}: backward")
+    inp = synth.make_inputs(wl, device="cuda")
+    bits = {k: synth.bits(v) for k, v in inp.items()}
+    actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
+    kc = oracle.round_to(oracle.compress(bits["k"], bits["w"], actq, wl.l, wl.d, wl.dtype), wl.dtype)
+    vc = oracle.round_to(oracle.compress(bits["v"], bits["w"], actq, wl.l, wl.d, wl.dtype), wl.dtype)
+    dout = synth.make_output_grad(wl, device="cuda")
+    ref = oracle.attention_backward(bits["q"], kc, vc, synth.bits(dout), actq,
+                                    oracle.cmp_prefix(wl.seqlens, wl.l, wl.d), wl.N1, wl.N2, wl.scale,
+                                    wl.l, wl.d, wl.dtype)
+    c, s = gpu_prefix(wl)
+    plan = nsa.nsa_compress_attention_get_workspace(
+        wl.act_seq_qlen, c, s, wl.N1, wl.N2, wl.D1, wl.D2, wl.scale, wl.l, wl.d, wl.lsel, wl.count,
+        wl.torch_dtype)
+    try:
+        kc_g, vc_g = upload_bits(kc, wl.dtype), upload_bits(vc, wl.dtype)
+        out, mx, sm = nsa.nsa_compress_attention_fwd(plan, inp["q"], kc_g, vc_g)
+        dq, dk, dv = nsa.nsa_compress_attention_backward(plan, inp["q"], kc_g, vc_g, out, dout, mx, sm)
+        torch.cuda.synchronize()
+    finally:
+        plan.destroy()
+    got = {"dq": dq, "dkc": dk, "dvc": dv}
+    for k in keys:
+        assert_grad_close(got[k].double().cpu().numpy(), ref[k], k)
+    return got
+
+
+@pytest.mark.parametrize("name,wl,dtype", [(f"w{i}", SMALL[i], "bf16") for i in SMALL] +
+                         [("neg", NEG, "bf16"), ("w2-f16", SMALL[2], "f16")])
+def test_backward_dq_against_oracle(name, wl, dtype):
+    _run(wl.with_dtype(dtype), keys=("dq",))

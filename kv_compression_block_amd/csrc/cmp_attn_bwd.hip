@@ -16,6 +16,8 @@
 // through LDS by buffer-unit copies of whole rows (16 bytes of padding per
 // row) and transposed reads (ds_read_b64_tr_b16) where an operand needs
 // the other orientation.
+#include <type_traits>
+
 #include "nsa_device.h"
 
 namespace nsa {
@@ -248,6 +250,231 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     }
 }
 
+// ---- key side: dkc, dvc ---------------------------------------------------------
+// One workgroup per (sequence, KV head, 32-entry key tile).  Keys and values
+// of the tile are B operands held in registers (lane l32 = entry); the query
+// rows that see the tile's first entry are split over the four waves in
+// 32-row tiles, each copied with its dout rows into the wave's own LDS
+// slots.  Per query tile: S = Q K^T and dP = dO V^T (rows = queries in
+// registers, lane = key), P and dS from the rows' bias and Delta, then
+// dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+template <typename E, int D1, int D2>
+__global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
+{
+    constexpr int W = 4;
+    using QR = PadRows<D1>;
+    using OR = PadRows<D2>;
+    constexpr int NKS = D1 / 16, NDS = D2 / 16, NDB1 = D1 / 32, NDB2 = D2 / 32;
+    constexpr int QSZ = QR::BUF, OSZ = OR::BUF;
+    // per wave: a query-row tile, a dout-row tile; reused at the end for the
+    // cross-wave sum (3 waves x 64 lanes x max(NDB1, NDB2) x 16 floats)
+    constexpr int SMEL = W * (QSZ + OSZ);
+    static_assert(SMEL * 2 >= 3 * 64 * (NDB1 > NDB2 ? NDB1 : NDB2) * 16 * 4, "reduction space");
+    __shared__ __attribute__((aligned(16))) uint16_t SM[SMEL];
+    __shared__ __attribute__((aligned(16))) float ST[W * 64];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int hf = lane >> 5;
+
+    const int wg = blockIdx.x;
+    int b = 0;
+    {
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.bt[mid].tile_off_k <= wg)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        b = lo;
+    }
+    const BatchEnt be = p.bt[b];
+    const int idx = wg - be.tile_off_k;
+    const int g = idx % p.N2;
+    const int i0 = (idx / p.N2) * 32;                  // first entry of the tile (local)
+    const int G = p.G;
+    const int key = i0 + l32;
+    const bool kvalid = key < be.n_cmp;
+
+    // keys and values as B operands: lane l32 = entry, k-slots 8hf..8hf+7
+    u32x4 kf[NKS], vf[NDS];
+    {
+        const int64_t krow = ((int64_t)(be.cmp_off + (kvalid ? key : i0)) * p.N2 + g);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            kf[ks] = *(const u32x4*)(p.kc + krow * D1 + ks * 16 + hf * 8);
+#pragma unroll
+        for (int ks = 0; ks < NDS; ++ks)
+            vf[ks] = *(const u32x4*)(p.vc + krow * D2 + ks * 16 + hf * 8);
+    }
+    const int key_first_tok = key * p.d + p.l - 1;    // first token that sees this lane's entry
+
+    // query rows r = t*G + hh seeing the tile's first entry: t >= i0*d + l - 1
+    const int rows_total = be.T * G;
+    const int r_first = min(i0 * p.d + p.l - 1, be.T) * G;
+    const int n_qt = (rows_total - r_first + 31) / 32;
+
+    uint16_t* qs = SM + wave * QSZ;
+    uint16_t* os = SM + W * QSZ + wave * OSZ;
+    float* st = ST + wave * 64;
+    // byte offsets inside the sequence's query rows: row r -> ((t*N1 + g*G + hh) * D) * 2
+    const uint16_t* qseq = p.q + (int64_t)be.q_off * p.N1 * D1;
+    const uint16_t* oseq = p.dout + (int64_t)be.q_off * p.N1 * D2;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qseq, (uint32_t)((int64_t)be.T * p.N1 * D1 * 2));
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(oseq, (uint32_t)((int64_t)be.T * p.N1 * D2 * 2));
+    auto row_elem = [&](int rr) -> int64_t {            // element offset of row rr in the sequence
+        const int t = rr / G;
+        return (int64_t)t * p.N1 + (int64_t)g * G + (rr - t * G);
+    };
+
+    f32x16 dka[NDB1], dva[NDB2];
+#pragma unroll
+    for (int db = 0; db < NDB1; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+            dka[db][x] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB2; ++db)
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+            dva[db][x] = 0.f;
+    int qtr[NDB1], otr[NDB2];
+#pragma unroll
+    for (int db = 0; db < NDB1; ++db)
+        qtr[db] = tr_off<QR::S>(lane, db * 32);
+#pragma unroll
+    for (int db = 0; db < NDB2; ++db)
+        otr[db] = tr_off<OR::S>(lane, db * 32);
+    const float c = p.c;
+
+    for (int qt = wave; qt < n_qt; qt += W) {
+        const int r0 = r_first + qt * 32;
+        // copy 32 query rows and their dout rows (rows past the sequence load 0)
+#pragma unroll
+        for (int q = 0; q < QR::INS; ++q) {
+            const int slot = q * 64 + lane;
+            const int rr = slot / (QR::CH + 1), ch = slot % (QR::CH + 1);
+            const bool ok = ch < QR::CH && rr < 32 && r0 + rr < rows_total;
+            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D1 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+            copy16_to_lds(qrs, qs + q * 512, off);
+        }
+#pragma unroll
+        for (int q = 0; q < OR::INS; ++q) {
+            const int slot = q * 64 + lane;
+            const int rr = slot / (OR::CH + 1), ch = slot % (OR::CH + 1);
+            const bool ok = ch < OR::CH && rr < 32 && r0 + rr < rows_total;
+            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D2 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+            copy16_to_lds(ors, os + q * 512, off);
+        }
+        if (lane < 32) {
+            const bool ok = r0 + lane < rows_total;
+            const int64_t grow = ok ? (int64_t)be.q_off * p.N1 + row_elem(r0 + lane) : 0;
+            st[lane] = ok ? p.rowstat[grow * 2] : INFINITY;
+            st[32 + lane] = ok ? p.rowstat[grow * 2 + 1] : 0.f;
+        }
+        __builtin_amdgcn_s_waitcnt(0x0070);         // this wave's copies and stores are done
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // S = Q K^T, dP = dO V^T: rows = queries 8*(x/4) + 4*hf + x%4, lane = entry
+        f32x16 s, dp;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            s[x] = 0.f;
+            dp[x] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            s = E::mfma(*(const u32x4*)&qs[l32 * QR::S + ks * 16 + hf * 8] ^ p.qsign, kf[ks], s);
+#pragma unroll
+        for (int ks = 0; ks < NDS; ++ks)
+            dp = E::mfma(*(const u32x4*)&os[l32 * OR::S + ks * 16 + hf * 8], vf[ks], dp);
+        u32x4 pf[2], dsf[2];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int qr0 = 8 * r4 + 4 * hf;             // first of 4 consecutive rows
+            const f32x4 bias4 = *(const f32x4*)&st[qr0];
+            const f32x4 del4 = *(const f32x4*)&st[32 + qr0];
+            float pv[4], dv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = 4 * r4 + e;
+                const int t = (r0 + qr0 + e) / G;
+                const bool vis = kvalid && key_first_tok <= t;
+                const float pr = vis ? fast_exp2(fmaf(s[x], c, -bias4[e])) : 0.f;
+                pv[e] = pr;
+                dv[e] = pr * (dp[x] - del4[e]);
+            }
+            const int kk = r4 >> 1, q2 = (r4 & 1) * 2;
+            pf[kk][q2] = E::pack2(pv[0], pv[1]);
+            pf[kk][q2 + 1] = E::pack2(pv[2], pv[3]);
+            dsf[kk][q2] = E::pack2(dv[0], dv[1]);
+            dsf[kk][q2 + 1] = E::pack2(dv[2], dv[3]);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the row tiles)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int db = 0; db < NDB2; ++db)
+                dva[db] = E::mfma(tr_read(&os[otr[db] + kk * 16 * OR::S], OR::S), pf[kk], dva[db]);
+#pragma unroll
+            for (int db = 0; db < NDB1; ++db)   // the true q: dkc = scale * sum dS q
+                dka[db] = E::mfma(tr_read(&qs[qtr[db] + kk * 16 * QR::S], QR::S), dsf[kk], dka[db]);
+        }
+        __asm__ volatile("" ::: "memory");          // the next copies stay after these reads
+    }
+
+    // Fixed-order sum of the four waves' partial sums: waves 1-3 park theirs
+    // in LDS, wave 0 adds them in wave order and stores (lane = entry, 4
+    // consecutive dims per register quad).
+    float* red = (float*)SM;                         // [3][64 lanes][NDB * 16]
+    auto reduce_store = [&](auto& acc, auto nb_tag, float* dst_base, int dcols, float mul) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nb_tag)::value;
+        __syncthreads();
+        if (wave > 0) {
+#pragma unroll
+            for (int db = 0; db < NB; ++db)
+#pragma unroll
+                for (int x = 0; x < 16; x += 4)
+                    *(f32x4*)&red[(((wave - 1) * 64 + lane) * NB + db) * 16 + x] =
+                        f32x4{acc[db][x], acc[db][x + 1], acc[db][x + 2], acc[db][x + 3]};
+        }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int w = 0; w < W - 1; ++w)
+#pragma unroll
+                for (int db = 0; db < NB; ++db)
+#pragma unroll
+                    for (int x = 0; x < 16; x += 4) {
+                        const f32x4 v = *(const f32x4*)&red[((w * 64 + lane) * NB + db) * 16 + x];
+                        acc[db][x] += v[0];
+                        acc[db][x + 1] += v[1];
+                        acc[db][x + 2] += v[2];
+                        acc[db][x + 3] += v[3];
+                    }
+            if (kvalid) {
+                float* dst = dst_base + ((int64_t)(be.cmp_off + key) * p.N2 + g) * dcols;
+#pragma unroll
+                for (int db = 0; db < NB; ++db)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        *(f32x4*)(dst + db * 32 + 8 * r4 + 4 * hf) =
+                            f32x4{acc[db][4 * r4] * mul, acc[db][4 * r4 + 1] * mul,
+                                  acc[db][4 * r4 + 2] * mul, acc[db][4 * r4 + 3] * mul};
+            }
+        }
+    };
+    reduce_store(dka, std::integral_constant<int, NDB1>{}, p.dkc, D1, p.scale);
+    reduce_store(dva, std::integral_constant<int, NDB2>{}, p.dvc, D2, 1.f);
+}
+
 #define NSA_BWD_CONFIGS(X) X(64, 64) X(128, 64) X(128, 128) X(192, 64) X(192, 128)
 
 bool attn_bwd_supported(int d1, int d2)
@@ -262,11 +489,12 @@ template <typename E>
 static hipError_t launch_bwd_typed(int d1, int d2, const BwdParams& p, int tiles_q, int tiles_k,
                                    hipStream_t stream)
 {
-    (void)tiles_k;
 #define X(a, b_)                                                                                    \
     if (d1 == a && d2 == b_) {                                                                      \
         if (tiles_q > 0)                                                                            \
             hipLaunchKernelGGL((k_cmp_attn_bwd_dq<E, a, b_>), dim3(tiles_q), dim3(256), 0, stream, p); \
+        if (tiles_k > 0)                                                                            \
+            hipLaunchKernelGGL((k_cmp_attn_bwd_dkv<E, a, b_>), dim3(tiles_k), dim3(256), 0, stream, p); \
         return hipGetLastError();                                                                   \
     }
     NSA_BWD_CONFIGS(X)

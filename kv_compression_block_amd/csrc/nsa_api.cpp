@@ -788,6 +788,10 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
     if (!nsa::attn_bwd_supported((int)plan->D1, (int)plan->D2))
         return fail(NSA_ERR_UNSUPPORTED, "head dims (%lld, %lld) are not built for the backward",
                     (long long)plan->D1, (long long)plan->D2);
+    for (const nsa::BatchEnt& e : plan->table)
+        if ((int64_t)e.T * plan->N1 * std::max(plan->D1, plan->D2) * 2 >= ((int64_t)1 << 32) - 64)
+            return fail(NSA_ERR_UNSUPPORTED, "a sequence's query rows exceed 4 GiB; the backward addresses "
+                        "them with 32-bit offsets");
     if (workspace_bytes < plan->ws_bwd_bytes || !workspace)
         return fail(NSA_ERR_WORKSPACE, "the backward needs %zu workspace bytes, %zu given", plan->ws_bwd_bytes,
                     workspace_bytes);

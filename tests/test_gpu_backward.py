@@ -74,5 +74,5 @@ def _run(wl, keys=("dq",)):
 
 @pytest.mark.parametrize("name,wl,dtype", [(f"w{i}", SMALL[i], "bf16") for i in SMALL] +
                          [("neg", NEG, "bf16"), ("w2-f16", SMALL[2], "f16")])
-def test_backward_dq_against_oracle(name, wl, dtype):
-    _run(wl.with_dtype(dtype), keys=("dq",))
+def test_backward_against_oracle(name, wl, dtype):
+    _run(wl.with_dtype(dtype), keys=("dq", "dkc", "dvc"))

@@ -110,6 +110,28 @@ nsa_status nsa_compress(const void* input, const void* weight,
                         void* stream);
 
 /*
+ * nsa_compress_backward -- gradients of nsa_compress (training use; the
+ * derivative of the "aclnnNsaCompress" Formula):
+ *   d_input[i*d + p, n, :] += weight[p, n] * d_output[i, n, :]
+ *   d_weight[p, n] = sum over sequences, windows i and dims e of
+ *                    d_output[i, n, e] * input[i*d + p, n, e]
+ * (rows counted from each sequence's start; rows in no window get 0).
+ *
+ *   input, weight     as given to nsa_compress (element type dtype)
+ *   d_output          [output_tokens, num_heads, head_dim] float32, device
+ *   d_input           [total_tokens, num_heads, head_dim] float32, device, written
+ *   d_weight          [compress_block_size, num_heads] float32, device, written
+ * When the same weight compresses K and V, add the two calls' d_weight.
+ * Results are bitwise repeatable.  Errors: as nsa_compress.
+ */
+nsa_status nsa_compress_backward(const void* input, const void* weight, const float* d_output,
+                                 const int64_t* act_seq_len, int64_t batch,
+                                 int64_t total_tokens, int64_t num_heads, int64_t head_dim,
+                                 int64_t compress_block_size, int64_t compress_stride,
+                                 nsa_dtype dtype, int64_t output_tokens, float* d_input,
+                                 float* d_weight, void* stream);
+
+/*
  * nsa_compress_attention_get_workspace -- first phase of
  * "mindspore.ops.nsa_compress_attention".  Host only: validates, derives the
  * per-sequence extents, plans the launches and returns the workspace size

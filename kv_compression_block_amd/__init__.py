@@ -35,7 +35,7 @@ from ._lib import Masks, NsaError, PlanInfo  # noqa: F401
 
 __all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_workspace",
            "nsa_compress_attention", "nsa_compress_attention_fwd", "nsa_compress_attention_select",
-           "nsa_select_attention", "nsa_compress_attention_backward", "compress_attention", "Plan",
+           "nsa_select_attention", "nsa_compress_attention_backward", "nsa_compress_backward", "compress_attention", "Plan",
            "NsaError", "library_path"]
 
 
@@ -413,3 +413,27 @@ def nsa_compress_attention_backward(plan: Plan, query, key, value, attention_out
         workspace.numel() * workspace.element_size(), _stream_ptr(dev, stream))
     _lib.check(st)
     return dq, dk, dv
+
+
+def nsa_compress_backward(input: torch.Tensor, weight: torch.Tensor, d_output: torch.Tensor,
+                          act_seq_len: Sequence[int], compress_block_size: int, compress_stride: int,
+                          stream=None):
+    """Gradients of nsa_compress: (d_input [T, N, D], d_weight [l, N]), float32,
+    for the float32 gradient ``d_output [T2, N, D]`` of its output."""
+    _need_tensor(input, "input")
+    _need_tensor(weight, "weight")
+    _need_tensor(d_output, "d_output")
+    if input.dim() != 3 or weight.dtype != input.dtype:
+        raise ValueError("input must be [T, N, D] and weight of the input's dtype")
+    if d_output.dtype != torch.float32:
+        raise TypeError("d_output must be float32")
+    T, N, D = input.shape
+    l, dd = int(compress_block_size), int(compress_stride)
+    pre, B = _prefix(act_seq_len, "act_seq_len")
+    dx = torch.empty((T, N, D), dtype=torch.float32, device=input.device)
+    dw = torch.empty((l, N), dtype=torch.float32, device=input.device)
+    st = _lib.load().nsa_compress_backward(_ptr(input), _ptr(weight), _ptr(d_output), pre, B, T, N, D, l, dd,
+                                           _dtype_code(input.dtype), d_output.shape[0], _ptr(dx), _ptr(dw),
+                                           _stream_ptr(input.device, stream))
+    _lib.check(st)
+    return dx, dw

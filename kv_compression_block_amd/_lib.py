@@ -36,6 +36,7 @@ EXPORTS = (
     "nsa_compress_attention_select_masked",
     "nsa_select_attention",
     "nsa_compress_attention_backward",
+    "nsa_compress_backward",
     "nsa_plan_get_info",
     "nsa_plan_destroy",
     "nsa_status_string",
@@ -114,6 +115,8 @@ def load() -> ctypes.CDLL:
     lib.nsa_select_attention.restype = I32
     lib.nsa_compress_attention_backward.argtypes = [P] * 12 + [ctypes.c_size_t, P]
     lib.nsa_compress_attention_backward.restype = I32
+    lib.nsa_compress_backward.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I64, I32, I64, P, P, P]
+    lib.nsa_compress_backward.restype = I32
     lib.nsa_plan_get_info.argtypes = [P, ctypes.POINTER(PlanInfo)]
     lib.nsa_plan_get_info.restype = I32
     lib.nsa_plan_destroy.argtypes = [P]

@@ -65,6 +65,84 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress(CompressParams p)
     *(u32x4*)(p.y + ((int64_t)p.out_off[seg] + i) * row_stride + c * 8) = o;
 }
 
+// Backward (for training; the derivative of the formula above):
+//   dx[start + i*d + p, n, :] += w[p, n] * dy[i, n, :]
+//   dw[p, n] += sum_i sum_e dy[i, n, e] * x[start + i*d + p, n, e]
+// dx: one thread per 4 consecutive floats of an input row, summing the at
+// most ceil(l/d) windows that contain the row in ascending window order
+// (rows in no window get 0).  dw: one workgroup per (p, n), each thread a
+// fixed strided share of the (window, dim) pairs, then a fixed-shape tree
+// in LDS: no atomics, bitwise repeatable.
+template <typename E>
+__global__ __launch_bounds__(kCompressThreads) void k_compress_bwd_dx(CompressBwdParams p)
+{
+    const int seg = blockIdx.y;
+    const int T = p.n_in[seg], n_out = p.n_out[seg];
+    const int nd4 = (p.N * p.D) >> 2;
+    const int64_t item = (int64_t)blockIdx.x * kCompressThreads + threadIdx.x;
+    if (item >= (int64_t)T * nd4)
+        return;
+    const int r = (int)(item / nd4);
+    const int c = (int)(item - (int64_t)r * nd4);
+    const int n = (c * 4) / p.D;
+    const int i_lo = r - p.l + 1 <= 0 ? 0 : (r - p.l + p.d) / p.d;
+    const int i_hi = min(n_out - 1, r / p.d);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int i = i_lo; i <= i_hi; ++i) {
+        const float wv = E::widen(p.w[(r - i * p.d) * p.N + n]);
+        const f32x4 g = *(const f32x4*)(p.dy + ((int64_t)p.out_off[seg] + i) * p.N * p.D + c * 4);
+        acc[0] = fmaf(wv, g[0], acc[0]);
+        acc[1] = fmaf(wv, g[1], acc[1]);
+        acc[2] = fmaf(wv, g[2], acc[2]);
+        acc[3] = fmaf(wv, g[3], acc[3]);
+    }
+    *(f32x4*)(p.dx + ((int64_t)p.in_off[seg] + r) * p.N * p.D + c * 4) = acc;
+}
+
+template <typename E>
+__global__ __launch_bounds__(kCompressThreads) void k_compress_bwd_dw(CompressBwdParams p)
+{
+    __shared__ float red[kCompressThreads];
+    const int pn = blockIdx.x;                       // p * N + n
+    const int pp = pn / p.N, n = pn - pp * p.N;
+    float acc = 0.f;
+    for (int s = 0; s < p.nseg; ++s) {
+        const int64_t pairs = (int64_t)p.n_out[s] * p.D;
+        for (int64_t k = threadIdx.x; k < pairs; k += kCompressThreads) {
+            const int i = (int)(k / p.D), e = (int)(k - (int64_t)i * p.D);
+            const float g = p.dy[(((int64_t)p.out_off[s] + i) * p.N + n) * p.D + e];
+            const float xv = E::widen(p.x[(((int64_t)p.in_off[s] + (int64_t)i * p.d + pp) * p.N + n) * p.D + e]);
+            acc = fmaf(g, xv, acc);
+        }
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = kCompressThreads / 2; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h)
+            red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        p.dw[pn] = p.accumulate ? p.dw[pn] + red[0] : red[0];
+}
+
+hipError_t launch_compress_bwd(int dtype, const CompressBwdParams& p, hipStream_t stream)
+{
+    dim3 gx(p.max_blocks_x, p.nseg, 1);
+    if (dtype == ElemBf16::code) {
+        if (p.max_blocks_x > 0)
+            hipLaunchKernelGGL(k_compress_bwd_dx<ElemBf16>, gx, dim3(kCompressThreads), 0, stream, p);
+        hipLaunchKernelGGL(k_compress_bwd_dw<ElemBf16>, dim3(p.l * p.N), dim3(kCompressThreads), 0, stream, p);
+    } else if (dtype == ElemF16::code) {
+        if (p.max_blocks_x > 0)
+            hipLaunchKernelGGL(k_compress_bwd_dx<ElemF16>, gx, dim3(kCompressThreads), 0, stream, p);
+        hipLaunchKernelGGL(k_compress_bwd_dw<ElemF16>, dim3(p.l * p.N), dim3(kCompressThreads), 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_compress(int dtype, const CompressParams& p, hipStream_t stream)
 {
     if (p.l * p.N > kCompressMaxW)

@@ -835,4 +835,94 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
     return ok();
 }
 
+nsa_status nsa_compress_backward(const void* input, const void* weight, const float* d_output,
+                                 const int64_t* act_seq_len, int64_t batch, int64_t total_tokens,
+                                 int64_t num_heads, int64_t head_dim, int64_t l, int64_t d,
+                                 nsa_dtype dtype, int64_t output_tokens, float* d_input,
+                                 float* d_weight, void* stream)
+{
+    if (!input || !weight || !act_seq_len || !d_input || !d_weight)
+        return fail(NSA_ERR_NULLPTR, "input, weight, act_seq_len, d_input and d_weight must not be NULL");
+    nsa_status st = check_dtype((int)dtype);
+    if (st != NSA_OK)
+        return st;
+    if (batch < 1)
+        return fail(NSA_ERR_SHAPE, "act_seq_len must not be empty (batch = %lld)", (long long)batch);
+    if (num_heads < 1)
+        return fail(NSA_ERR_SHAPE, "num_heads must be >= 1");
+    if (!mult16(head_dim) || head_dim > 256)
+        return fail(NSA_ERR_CONSTRAINT, "head_dim must be a multiple of 16 and <= 256 (got %lld)", (long long)head_dim);
+    if (!mult16(l) || l > 128)
+        return fail(NSA_ERR_CONSTRAINT, "compress_block_size must be a multiple of 16 in [16, 128] (got %lld)", (long long)l);
+    if (!mult16(d) || d > l)
+        return fail(NSA_ERR_CONSTRAINT, "compress_stride must be a multiple of 16 with 16 <= d <= compress_block_size (got %lld)", (long long)d);
+    std::vector<int64_t> lens;
+    if ((st = read_prefix(act_seq_len, batch, "act_seq_len", lens)) != NSA_OK)
+        return st;
+    if (act_seq_len[batch - 1] != total_tokens)
+        return fail(NSA_ERR_SHAPE, "last prefix sum %lld != total_tokens %lld",
+                    (long long)act_seq_len[batch - 1], (long long)total_tokens);
+    int64_t T2 = 0;
+    for (int64_t T : lens)
+        T2 += n_cmp_of(T, l, d);
+    if (T2 != output_tokens)
+        return fail(NSA_ERR_SHAPE, "output_tokens %lld != sum of compressed lengths %lld",
+                    (long long)output_tokens, (long long)T2);
+    if (T2 > 0 && !d_output)
+        return fail(NSA_ERR_NULLPTR, "d_output must not be NULL");
+    if (!aligned(input, 16) || !aligned(d_input, 16) || (d_output && !aligned(d_output, 16)) ||
+        !aligned(weight, 2) || !aligned(d_weight, 4))
+        return fail(NSA_ERR_CONSTRAINT, "input, d_output and d_input must be 16-byte aligned");
+    nsa::CompressBwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.x = (const uint16_t*)input;
+    p.w = (const uint16_t*)weight;
+    p.dy = d_output;
+    p.dx = d_input;
+    p.dw = d_weight;
+    p.N = (int)num_heads;
+    p.D = (int)head_dim;
+    p.l = (int)l;
+    p.d = (int)d;
+    const int64_t nd4 = num_heads * head_dim / 4;
+    int64_t in_off = 0, out_off = 0;
+    size_t b = 0;
+    bool first = true;
+    while (b < lens.size()) {
+        p.nseg = 0;
+        int64_t max_items = 0;
+        while (b < lens.size() && p.nseg < nsa::kCompressMaxSeg) {
+            const int64_t n = n_cmp_of(lens[b], l, d);
+            if (lens[b] > 0) {
+                p.in_off[p.nseg] = (int)in_off;
+                p.out_off[p.nseg] = (int)out_off;
+                p.n_in[p.nseg] = (int)lens[b];
+                p.n_out[p.nseg] = (int)n;
+                max_items = std::max(max_items, lens[b] * nd4);
+                ++p.nseg;
+            }
+            in_off += lens[b];
+            out_off += n;
+            ++b;
+        }
+        if (p.nseg == 0)
+            continue;
+        p.max_blocks_x = (int)((max_items + 255) / 256);
+        p.accumulate = first ? 0 : 1;
+        first = false;
+        hipError_t e = nsa::launch_compress_bwd((int)dtype, p, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return fail(NSA_ERR_HIP, "compress backward launch failed: %s", hipGetErrorString(e));
+    }
+    if (first) {   // no token at all: d_weight is still defined
+        p.nseg = 0;
+        p.max_blocks_x = 0;
+        p.accumulate = 0;
+        hipError_t e = nsa::launch_compress_bwd((int)dtype, p, (hipStream_t)stream);
+        if (e != hipSuccess)
+            return fail(NSA_ERR_HIP, "compress backward launch failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
 }  // extern "C"

@@ -45,6 +45,24 @@ struct CompressParams {
 // dtype: 0 = bfloat16, 1 = float16 (the public enum's values).
 hipError_t launch_compress(int dtype, const CompressParams& p, hipStream_t stream);
 
+// Backward of the compression for up to kCompressMaxSeg sequences per launch.
+struct CompressBwdParams {
+    const uint16_t* x;    // [T, N, D]
+    const uint16_t* w;    // [l, N]
+    const float* dy;      // [T2, N, D]
+    float* dx;            // [T, N, D]
+    float* dw;            // [l, N]
+    int N, D, l, d;
+    int nseg;
+    int max_blocks_x;     // dx kernel: blocks of 256 threads covering the longest sequence
+    int accumulate;       // dw kernel: add to dw (a later launch of one call) instead of writing
+    int in_off[kCompressMaxSeg];
+    int out_off[kCompressMaxSeg];
+    int n_in[kCompressMaxSeg];     // tokens of each sequence
+    int n_out[kCompressMaxSeg];    // windows of each sequence
+};
+hipError_t launch_compress_bwd(int dtype, const CompressBwdParams& p, hipStream_t stream);
+
 // ---- explicit masks ---------------------------------------------------------
 // A [rows, cols] byte matrix (non-zero = masked out) becomes a bit matrix of
 // kept pairs: word w of row t holds columns 32w .. 32w+31, bit k set iff

@@ -76,3 +76,27 @@ def _run(wl, keys=("dq",)):
                          [("neg", NEG, "bf16"), ("w2-f16", SMALL[2], "f16")])
 def test_backward_against_oracle(name, wl, dtype):
     _run(wl.with_dtype(dtype), keys=("dq", "dkc", "dvc"))
+
+
+@pytest.mark.parametrize("name,wl,dtype", [("w2", SMALL[2], "bf16"), ("w3", SMALL[3], "bf16"),
+                                           ("w4", SMALL[4], "bf16"), ("w2-f16", SMALL[2], "f16"),
+                                           ("short", dataclasses.replace(SMALL[0], name="short-seqs",
+                                                                         seqlens=(5, 0, 31, 32, 47, 200)), "bf16")])
+def test_compress_backward_against_oracle(name, wl, dtype):
+    """Gradients of the compression (d_input, d_weight) for a seeded float32
+    output gradient, against the oracle."""
+    wl = wl.with_dtype(dtype)
+    log(f"[case] {wl.name}: compress backward")
+    inp = synth.make_inputs(wl, device="cuda", tensors=("k", "w"))
+    T2 = int(oracle.cmp_prefix(wl.seqlens, wl.l, wl.d)[-1])
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(1234)
+    dy = torch.randn((T2, wl.N2, wl.D1), generator=gen, dtype=torch.float32)
+    ref = oracle.compress_backward(synth.bits(inp["k"]), synth.bits(inp["w"]), dy.double().numpy(),
+                                   wl.act_seq_qlen, wl.l, wl.d, wl.dtype)
+    dx, dw = nsa.nsa_compress_backward(inp["k"], inp["w"], dy.cuda(), wl.act_seq_qlen, wl.l, wl.d)
+    torch.cuda.synchronize()
+    assert_grad_close(dx.double().cpu().numpy(), ref["dx"], "d_input")
+    assert_grad_close(dw.double().cpu().numpy(), ref["dw"], "d_weight")
+    dx2, dw2 = nsa.nsa_compress_backward(inp["k"], inp["w"], dy.cuda(), wl.act_seq_qlen, wl.l, wl.d)
+    assert torch.equal(dx, dx2) and torch.equal(dw, dw2)

@@ -21,6 +21,11 @@ oracle on a bounded random sample of the same workload's tokens.
 topk_mask tensors (the masked entry points: mask packing plus the
 every-tile masked kernels) instead of letting the kernels generate them.
 
+``--backward`` times instead the training backward of the compressed branch
+on the same workload: the gradients of attention_out (nsa_compress_attention_
+backward: query-side and key-side kernels) and of both compressions
+(nsa_compress_backward), after one untimed forward.
+
 ``--select-attention`` times instead the step that consumes the top-k: the
 attention of every query over the raw keys of its selected blocks
 (nsa_select_attention), fed with the top-k the compressed branch computes
@@ -208,6 +213,66 @@ def select_attention_bench(args, wl, plan, inp, topk, ws, stream) -> dict:
     }
 
 
+def backward_bench(args, wl, plan, inp, kc, vc, outs, stream, T2) -> dict:
+    """Times the backward: attention (dq; dkc, dvc) then both compressions."""
+    import torch
+    import synth
+    import kv_compression_block_amd as nsa
+    dev = inp["q"].device
+    dout = synth.make_output_grad(wl, device=dev, chunk_rows=16384)
+    ws = torch.empty(plan.info["backward_workspace_bytes"], dtype=torch.uint8, device=dev)
+    grads = {}
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dq, dk, dv = nsa.nsa_compress_attention_backward(plan, inp["q"], kc, vc, outs["attention_out"], dout,
+                                                         outs["softmax_max"], outs["softmax_sum"], workspace=ws,
+                                                         stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dxk, dwk = nsa.nsa_compress_backward(inp["k"], inp["w"], dk, wl.act_seq_qlen, wl.l, wl.d, stream=stream)
+        dxv, dwv = nsa.nsa_compress_backward(inp["v"], inp["w"], dv, wl.act_seq_qlen, wl.l, wl.d, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        grads.update(dq=dq, dk=dxk, dv=dxv, dw=dwk + dwv)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in evs:
+        run(ev)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_attn = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_comp = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    work = workload_work(wl, T2)
+    pairs_heads = work["attn_flops"] / (2.0 * (wl.D1 + wl.D2))
+    # algorithmic: dV, dP, dq, dK (no recompute of the scores)
+    flops = 2.0 * (2 * wl.D1 + 2 * wl.D2) * pairs_heads
+    tflops = flops / (ms_attn / 1e3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+    return {
+        "metric": "query tokens/sec (backward of compress+attn)",
+        "value": wl.T / (ms_step / 1e3), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "N1": wl.N1, "N2": wl.N2, "D1": wl.D1,
+                   "D2": wl.D2, "l": wl.l, "d": wl.d, "dtype": wl.dtype,
+                   "gradient": "seeded N(0,1) d_attention_out", "parallelism": "single-gpu"},
+        "roofline": {"kernel": "k_cmp_attn_bwd_dq + k_cmp_attn_bwd_dkv", "bound": "mfma", "achieved": tflops,
+                     "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak, "traffic": None,
+                     "work_per_launch": f"{flops:.4e} flop = 2*(2*D1+2*D2) x {pairs_heads:.4e} visible "
+                                        f"(token, block) pairs x heads (dV, dP, dq, dK; the recomputed "
+                                        f"scores are not counted)"},
+        "kernels": {"attention_backward": {"ms": ms_attn, "TFLOP/s": tflops},
+                    "compress_backward_k_and_v": {"ms": ms_comp}},
+        "cpu_baseline": None,
+    }
+
+
 def select_cpu_baseline(wl, inp, topk, budget_s: float) -> dict:
     """The oracle's selected-block attention on a bounded uniform sample of
     tokens, scaled to all tokens."""
@@ -245,6 +310,8 @@ def main() -> int:
                     help="give the causal rules as explicit atten_mask / topk_mask tensors")
     ap.add_argument("--select-attention", action="store_true",
                     help="time the selected-block attention over the compressed branch's top-k")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the compressed attention and of the compression")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -335,6 +402,14 @@ def main() -> int:
                                           topk_mask=masks.get("topk_mask"))
         if ev is not None:
             ev[4].record(stream)
+
+    if args.backward:
+        step()
+        torch.cuda.synchronize()
+        res = backward_bench(args, wl, plan, inp, kc, vc, outs, stream, T2)
+        plan.destroy()
+        print(json.dumps(res), flush=True)
+        return 0
 
     if args.select_attention:
         step()

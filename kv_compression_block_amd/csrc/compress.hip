@@ -70,9 +70,10 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress(CompressParams p)
 //   dw[p, n] += sum_i sum_e dy[i, n, e] * x[start + i*d + p, n, e]
 // dx: one thread per 4 consecutive floats of an input row, summing the at
 // most ceil(l/d) windows that contain the row in ascending window order
-// (rows in no window get 0).  dw: one workgroup per (p, n), each thread a
-// fixed strided share of the (window, dim) pairs, then a fixed-shape tree
-// in LDS: no atomics, bitwise repeatable.
+// (rows in no window get 0).  dw: workgroups per (p, n) and chunk of the
+// windows, each thread a fixed strided share of the (window, dim) pairs and
+// a fixed-shape tree in LDS, then the chunks added in order: no atomics,
+// bitwise repeatable.  The chunk sums live in d_input before it is written.
 template <typename E>
 __global__ __launch_bounds__(kCompressThreads) void k_compress_bwd_dx(CompressBwdParams p)
 {
@@ -99,19 +100,33 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_bwd_dx(CompressBw
     *(f32x4*)(p.dx + ((int64_t)p.in_off[seg] + r) * p.N * p.D + c * 4) = acc;
 }
 
+// dw, first pass: workgroup (p*N + n, chunk) sums its chunk of the launch's
+// windows (flattened over the sequences, ascending) into part[pn * C + chunk];
+// with one chunk it writes (or adds to) dw directly.
 template <typename E>
 __global__ __launch_bounds__(kCompressThreads) void k_compress_bwd_dw(CompressBwdParams p)
 {
     __shared__ float red[kCompressThreads];
     const int pn = blockIdx.x;                       // p * N + n
+    const int chunk = blockIdx.y, C = gridDim.y;
     const int pp = pn / p.N, n = pn - pp * p.N;
+    int64_t wtot = 0;
+    for (int s = 0; s < p.nseg; ++s)
+        wtot += p.n_out[s];
+    const int64_t w_lo = wtot * chunk / C, w_hi = wtot * (chunk + 1) / C;
     float acc = 0.f;
+    int64_t wbase = 0;
     for (int s = 0; s < p.nseg; ++s) {
-        const int64_t pairs = (int64_t)p.n_out[s] * p.D;
+        const int64_t lo = max(w_lo - wbase, (int64_t)0), hi = min(w_hi - wbase, (int64_t)p.n_out[s]);
+        wbase += p.n_out[s];
+        if (lo >= hi)
+            continue;
+        const int64_t pairs = (hi - lo) * p.D;
         for (int64_t k = threadIdx.x; k < pairs; k += kCompressThreads) {
-            const int i = (int)(k / p.D), e = (int)(k - (int64_t)i * p.D);
+            const int64_t i = lo + k / p.D;
+            const int e = (int)(k % p.D);
             const float g = p.dy[(((int64_t)p.out_off[s] + i) * p.N + n) * p.D + e];
-            const float xv = E::widen(p.x[(((int64_t)p.in_off[s] + (int64_t)i * p.d + pp) * p.N + n) * p.D + e]);
+            const float xv = E::widen(p.x[(((int64_t)p.in_off[s] + i * p.d + pp) * p.N + n) * p.D + e]);
             acc = fmaf(g, xv, acc);
         }
     }
@@ -122,24 +137,52 @@ __global__ __launch_bounds__(kCompressThreads) void k_compress_bwd_dw(CompressBw
             red[threadIdx.x] += red[threadIdx.x + h];
         __syncthreads();
     }
-    if (threadIdx.x == 0)
-        p.dw[pn] = p.accumulate ? p.dw[pn] + red[0] : red[0];
+    if (threadIdx.x == 0) {
+        if (C > 1)
+            p.part[(int64_t)pn * C + chunk] = red[0];
+        else
+            p.dw[pn] = p.accumulate ? p.dw[pn] + red[0] : red[0];
+    }
 }
 
-hipError_t launch_compress_bwd(int dtype, const CompressBwdParams& p, hipStream_t stream)
+// dw, second pass: the chunks' sums in chunk order.
+__global__ __launch_bounds__(64) void k_compress_bwd_dw_sum(CompressBwdParams p, int C)
 {
-    dim3 gx(p.max_blocks_x, p.nseg, 1);
-    if (dtype == ElemBf16::code) {
-        if (p.max_blocks_x > 0)
-            hipLaunchKernelGGL(k_compress_bwd_dx<ElemBf16>, gx, dim3(kCompressThreads), 0, stream, p);
-        hipLaunchKernelGGL(k_compress_bwd_dw<ElemBf16>, dim3(p.l * p.N), dim3(kCompressThreads), 0, stream, p);
-    } else if (dtype == ElemF16::code) {
-        if (p.max_blocks_x > 0)
-            hipLaunchKernelGGL(k_compress_bwd_dx<ElemF16>, gx, dim3(kCompressThreads), 0, stream, p);
-        hipLaunchKernelGGL(k_compress_bwd_dw<ElemF16>, dim3(p.l * p.N), dim3(kCompressThreads), 0, stream, p);
-    } else {
+    const int pn = blockIdx.x * 64 + threadIdx.x;
+    if (pn >= p.l * p.N)
+        return;
+    float acc = 0.f;
+    for (int c = 0; c < C; ++c)
+        acc += p.part[(int64_t)pn * C + c];
+    p.dw[pn] = p.accumulate ? p.dw[pn] + acc : acc;
+}
+
+hipError_t launch_compress_bwd_dw(int dtype, const CompressBwdParams& p, int chunks, hipStream_t stream)
+{
+    const int C = chunks < 1 ? 1 : chunks;
+    dim3 g(p.l * p.N, C, 1);
+    if (dtype == ElemBf16::code)
+        hipLaunchKernelGGL(k_compress_bwd_dw<ElemBf16>, g, dim3(kCompressThreads), 0, stream, p);
+    else if (dtype == ElemF16::code)
+        hipLaunchKernelGGL(k_compress_bwd_dw<ElemF16>, g, dim3(kCompressThreads), 0, stream, p);
+    else
         return hipErrorInvalidValue;
-    }
+    if (C > 1)
+        hipLaunchKernelGGL(k_compress_bwd_dw_sum, dim3((p.l * p.N + 63) / 64), dim3(64), 0, stream, p, C);
+    return hipGetLastError();
+}
+
+hipError_t launch_compress_bwd_dx(int dtype, const CompressBwdParams& p, hipStream_t stream)
+{
+    if (p.max_blocks_x <= 0 || p.nseg <= 0)
+        return hipSuccess;
+    dim3 gx(p.max_blocks_x, p.nseg, 1);
+    if (dtype == ElemBf16::code)
+        hipLaunchKernelGGL(k_compress_bwd_dx<ElemBf16>, gx, dim3(kCompressThreads), 0, stream, p);
+    else if (dtype == ElemF16::code)
+        hipLaunchKernelGGL(k_compress_bwd_dx<ElemF16>, gx, dim3(kCompressThreads), 0, stream, p);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

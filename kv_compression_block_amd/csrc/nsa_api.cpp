@@ -885,42 +885,43 @@ nsa_status nsa_compress_backward(const void* input, const void* weight, const fl
     p.l = (int)l;
     p.d = (int)d;
     const int64_t nd4 = num_heads * head_dim / 4;
-    int64_t in_off = 0, out_off = 0;
-    size_t b = 0;
-    bool first = true;
-    while (b < lens.size()) {
-        p.nseg = 0;
-        int64_t max_items = 0;
-        while (b < lens.size() && p.nseg < nsa::kCompressMaxSeg) {
-            const int64_t n = n_cmp_of(lens[b], l, d);
-            if (lens[b] > 0) {
-                p.in_off[p.nseg] = (int)in_off;
-                p.out_off[p.nseg] = (int)out_off;
-                p.n_in[p.nseg] = (int)lens[b];
-                p.n_out[p.nseg] = (int)n;
-                max_items = std::max(max_items, lens[b] * nd4);
-                ++p.nseg;
+    // Weight gradient first (all launches), its chunk sums parked in d_input;
+    // then d_input itself.  Chunks: enough workgroups to fill the chip, as
+    // many as d_input can hold.
+    const int64_t room = total_tokens * head_dim / l;          // chunk sums per (p, n) d_input holds
+    const int chunks = (int)std::max<int64_t>(1, std::min<int64_t>({64, room, (1024 + l * num_heads - 1) / (l * num_heads)}));
+    for (int pass = 0; pass < 2; ++pass) {
+        int64_t in_off = 0, out_off = 0;
+        size_t b = 0;
+        bool first = true;
+        while (b < lens.size() || first) {
+            p.nseg = 0;
+            int64_t max_items = 0;
+            while (b < lens.size() && p.nseg < nsa::kCompressMaxSeg) {
+                const int64_t n = n_cmp_of(lens[b], l, d);
+                if (lens[b] > 0) {
+                    p.in_off[p.nseg] = (int)in_off;
+                    p.out_off[p.nseg] = (int)out_off;
+                    p.n_in[p.nseg] = (int)lens[b];
+                    p.n_out[p.nseg] = (int)n;
+                    max_items = std::max(max_items, lens[b] * nd4);
+                    ++p.nseg;
+                }
+                in_off += lens[b];
+                out_off += n;
+                ++b;
             }
-            in_off += lens[b];
-            out_off += n;
-            ++b;
+            if (p.nseg == 0 && !first)
+                continue;
+            p.max_blocks_x = (int)((max_items + 255) / 256);
+            p.accumulate = first ? 0 : 1;
+            p.part = d_input;
+            first = false;
+            hipError_t e = pass == 0 ? nsa::launch_compress_bwd_dw((int)dtype, p, chunks, (hipStream_t)stream)
+                                     : nsa::launch_compress_bwd_dx((int)dtype, p, (hipStream_t)stream);
+            if (e != hipSuccess)
+                return fail(NSA_ERR_HIP, "compress backward launch failed: %s", hipGetErrorString(e));
         }
-        if (p.nseg == 0)
-            continue;
-        p.max_blocks_x = (int)((max_items + 255) / 256);
-        p.accumulate = first ? 0 : 1;
-        first = false;
-        hipError_t e = nsa::launch_compress_bwd((int)dtype, p, (hipStream_t)stream);
-        if (e != hipSuccess)
-            return fail(NSA_ERR_HIP, "compress backward launch failed: %s", hipGetErrorString(e));
-    }
-    if (first) {   // no token at all: d_weight is still defined
-        p.nseg = 0;
-        p.max_blocks_x = 0;
-        p.accumulate = 0;
-        hipError_t e = nsa::launch_compress_bwd((int)dtype, p, (hipStream_t)stream);
-        if (e != hipSuccess)
-            return fail(NSA_ERR_HIP, "compress backward launch failed: %s", hipGetErrorString(e));
     }
     return ok();
 }

@@ -56,12 +56,14 @@ struct CompressBwdParams {
     int nseg;
     int max_blocks_x;     // dx kernel: blocks of 256 threads covering the longest sequence
     int accumulate;       // dw kernel: add to dw (a later launch of one call) instead of writing
+    float* part;          // dw chunk sums (scratch: the start of dx, before dx is written)
     int in_off[kCompressMaxSeg];
     int out_off[kCompressMaxSeg];
     int n_in[kCompressMaxSeg];     // tokens of each sequence
     int n_out[kCompressMaxSeg];    // windows of each sequence
 };
-hipError_t launch_compress_bwd(int dtype, const CompressBwdParams& p, hipStream_t stream);
+hipError_t launch_compress_bwd_dw(int dtype, const CompressBwdParams& p, int chunks, hipStream_t stream);
+hipError_t launch_compress_bwd_dx(int dtype, const CompressBwdParams& p, hipStream_t stream);
 
 // ---- explicit masks ---------------------------------------------------------
 // A [rows, cols] byte matrix (non-zero = masked out) becomes a bit matrix of

@@ -311,7 +311,8 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         for (int ks = 0; ks < NDS; ++ks)
             vf[ks] = *(const u32x4*)(p.vc + krow * D2 + ks * 16 + hf * 8);
     }
-    const int key_first_tok = key * p.d + p.l - 1;    // first token that sees this lane's entry
+    // first row (t*G + hh) that sees this lane's entry: t >= key*d + l - 1
+    const int key_first_row = (key * p.d + p.l - 1) * G;
 
     // query rows r = t*G + hh seeing the tile's first entry: t >= i0*d + l - 1
     const int rows_total = be.T * G;
@@ -326,8 +327,10 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     const uint16_t* oseq = p.dout + (int64_t)be.q_off * p.N1 * D2;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qseq, (uint32_t)((int64_t)be.T * p.N1 * D1 * 2));
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(oseq, (uint32_t)((int64_t)be.T * p.N1 * D2 * 2));
-    auto row_elem = [&](int rr) -> int64_t {            // element offset of row rr in the sequence
-        const int t = rr / G;
+    // element row of sequence row rr = t*G + hh: t*N1 + g*G + hh (t = rr / G
+    // by a multiply-high with the host's magic number for G)
+    auto row_elem = [&](int rr) -> int64_t {
+        const int t = (int)(((uint64_t)__umulhi((uint32_t)rr, p.gdiv_m) + (uint32_t)rr) >> p.gdiv_s);
         return (int64_t)t * p.N1 + (int64_t)g * G + (rr - t * G);
     };
 
@@ -405,8 +408,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int x = 4 * r4 + e;
-                const int t = (r0 + qr0 + e) / G;
-                const bool vis = kvalid && key_first_tok <= t;
+                const bool vis = kvalid && key_first_row <= r0 + qr0 + e;
                 const float pr = vis ? fast_exp2(fmaf(s[x], c, -bias4[e])) : 0.f;
                 pv[e] = pr;
                 dv[e] = pr * (dp[x] - del4[e]);

@@ -828,6 +828,15 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
     a.c = std::fmax(exp2_scale(plan), 1e-30f);
     a.scale = plan->scale;
     a.qsign = q_sign(plan);
+    {
+        // magic numbers for division by G (round-up method): s = ceil(log2 G),
+        // m = floor(2^32 (2^s - G) / G) + 1
+        uint32_t sh = 0;
+        while (((uint64_t)1 << sh) < (uint64_t)a.G)
+            ++sh;
+        a.gdiv_s = sh;
+        a.gdiv_m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << sh) - (uint64_t)a.G)) / (uint64_t)a.G + 1);
+    }
     hipError_t e = nsa::launch_attn_bwd(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a,
                                         (int)plan->tiles_k, s);
     if (e != hipSuccess)

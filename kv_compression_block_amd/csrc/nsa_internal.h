@@ -181,6 +181,7 @@ struct BwdParams {
     float c;               // |scale| * log2(e)
     float scale;           // signed scale
     uint32_t qsign;        // 0x80008000 when scale < 0 (q negated), else 0
+    uint32_t gdiv_m, gdiv_s;   // n / G = (umulhi(n, m) + n) >> s for 0 <= n < 2^31
 };
 
 bool attn_bwd_supported(int d1, int d2);

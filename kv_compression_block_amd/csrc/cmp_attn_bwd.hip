@@ -268,7 +268,10 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     constexpr int QSZ = QR::BUF, OSZ = OR::BUF;
     // per wave: a query-row tile, a dout-row tile; reused at the end for the
     // cross-wave sum (3 waves x 64 lanes x max(NDB1, NDB2) x 16 floats)
-    constexpr int SMEL = W * (QSZ + OSZ);
+    // Two slots per wave where the LDS allows it (the next tile's copies then
+    // overlap this tile's work), else one.
+    constexpr int NBUF = (2 * W * (QSZ + OSZ) * 2 <= 150 * 1024) ? 2 : 1;
+    constexpr int SMEL = NBUF * W * (QSZ + OSZ);
     static_assert(SMEL * 2 >= 3 * 64 * (NDB1 > NDB2 ? NDB1 : NDB2) * 16 * 4, "reduction space");
     __shared__ __attribute__((aligned(16))) uint16_t SM[SMEL];
     __shared__ __attribute__((aligned(16))) float ST[W * 64];
@@ -319,8 +322,8 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     const int r_first = min(i0 * p.d + p.l - 1, be.T) * G;
     const int n_qt = (rows_total - r_first + 31) / 32;
 
-    uint16_t* qs = SM + wave * QSZ;
-    uint16_t* os = SM + W * QSZ + wave * OSZ;
+    auto qs_at = [&](int slot) { return SM + (slot * W + wave) * QSZ; };
+    auto os_at = [&](int slot) { return SM + NBUF * W * QSZ + (slot * W + wave) * OSZ; };
     float* st = ST + wave * 64;
     // byte offsets inside the sequence's query rows: row r -> ((t*N1 + g*G + hh) * D) * 2
     const uint16_t* qseq = p.q + (int64_t)be.q_off * p.N1 * D1;
@@ -354,36 +357,57 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         otr[db] = tr_off<OR::S>(lane, db * 32);
     const float c = p.c;
 
-    for (int qt = wave; qt < n_qt; qt += W) {
+    // Tile qt's copies: the rows' bias and Delta into registers (lanes < 32),
+    // then the query and dout rows (rows past the sequence load 0).
+    float stb = INFINITY, stq = 0.f;
+    auto issue = [&](int qt, int slot) __attribute__((always_inline)) {
         const int r0 = r_first + qt * 32;
-        // copy 32 query rows and their dout rows (rows past the sequence load 0)
-#pragma unroll
-        for (int q = 0; q < QR::INS; ++q) {
-            const int slot = q * 64 + lane;
-            const int rr = slot / (QR::CH + 1), ch = slot % (QR::CH + 1);
-            const bool ok = ch < QR::CH && rr < 32 && r0 + rr < rows_total;
-            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D1 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
-            copy16_to_lds(qrs, qs + q * 512, off);
-        }
-#pragma unroll
-        for (int q = 0; q < OR::INS; ++q) {
-            const int slot = q * 64 + lane;
-            const int rr = slot / (OR::CH + 1), ch = slot % (OR::CH + 1);
-            const bool ok = ch < OR::CH && rr < 32 && r0 + rr < rows_total;
-            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D2 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
-            copy16_to_lds(ors, os + q * 512, off);
-        }
         if (lane < 32) {
             const bool ok = r0 + lane < rows_total;
             const int64_t grow = ok ? (int64_t)be.q_off * p.N1 + row_elem(r0 + lane) : 0;
-            st[lane] = ok ? p.rowstat[grow * 2] : INFINITY;
-            st[32 + lane] = ok ? p.rowstat[grow * 2 + 1] : 0.f;
+            stb = ok ? p.rowstat[grow * 2] : INFINITY;
+            stq = ok ? p.rowstat[grow * 2 + 1] : 0.f;
         }
-        __builtin_amdgcn_s_waitcnt(0x0070);         // this wave's copies and stores are done
+        uint16_t* qd = qs_at(slot);
+        uint16_t* od = os_at(slot);
+#pragma unroll
+        for (int q = 0; q < QR::INS; ++q) {
+            const int sl = q * 64 + lane;
+            const int rr = sl / (QR::CH + 1), ch = sl % (QR::CH + 1);
+            const bool ok = ch < QR::CH && rr < 32 && r0 + rr < rows_total;
+            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D1 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+            copy16_to_lds(qrs, qd + q * 512, off);
+        }
+#pragma unroll
+        for (int q = 0; q < OR::INS; ++q) {
+            const int sl = q * 64 + lane;
+            const int rr = sl / (OR::CH + 1), ch = sl % (OR::CH + 1);
+            const bool ok = ch < OR::CH && rr < 32 && r0 + rr < rows_total;
+            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D2 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
+            copy16_to_lds(ors, od + q * 512, off);
+        }
+    };
+
+    int slot = 0;
+    if (wave < n_qt)
+        issue(wave, 0);
+    for (int qt = wave; qt < n_qt; qt += W) {
+        const int r0 = r_first + qt * 32;
+        __builtin_amdgcn_s_waitcnt(0x0070);         // tile qt's copies and loads are done
         __asm__ volatile("" ::: "memory");
+        if (lane < 32) {
+            st[lane] = stb;
+            st[32 + lane] = stq;
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint16_t* qs = qs_at(slot);
+        const uint16_t* os = os_at(slot);
+        if constexpr (NBUF == 2) {
+            if (qt + W < n_qt)
+                issue(qt + W, slot ^ 1);            // the other slot's tile is done
+        }
 
         // S = Q K^T, dP = dO V^T: rows = queries 8*(x/4) + 4*hf + x%4, lane = entry
         f32x16 s, dp;
@@ -429,7 +453,13 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
             for (int db = 0; db < NDB1; ++db)   // the true q: dkc = scale * sum dS q
                 dka[db] = E::mfma(tr_read(&qs[qtr[db] + kk * 16 * QR::S], QR::S), dsf[kk], dka[db]);
         }
-        __asm__ volatile("" ::: "memory");          // the next copies stay after these reads
+        __asm__ volatile("" ::: "memory");          // later copies stay after these reads
+        if constexpr (NBUF == 1) {
+            if (qt + W < n_qt)
+                issue(qt + W, 0);
+        } else {
+            slot ^= 1;
+        }
     }
 
     // Fixed-order sum of the four waves' partial sums: waves 1-3 park theirs

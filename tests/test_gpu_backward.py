@@ -100,3 +100,59 @@ def test_compress_backward_against_oracle(name, wl, dtype):
     assert_grad_close(dw.double().cpu().numpy(), ref["dw"], "d_weight")
     dx2, dw2 = nsa.nsa_compress_backward(inp["k"], inp["w"], dy.cuda(), wl.act_seq_qlen, wl.l, wl.d)
     assert torch.equal(dx, dx2) and torch.equal(dw, dw2)
+
+
+def test_backward_full_size_properties():
+    """The batched varlen workload at its full size, in the launch
+    configuration the benchmark times (GPU compression, forward, backward).
+    No oracle at this size; instead properties of the derivatives that hold
+    exactly at any size:
+      * sum over a KV head's compressed entries of d_value equals the sum of
+        d_attention_out over its query rows that see at least one block
+        (each such row's probabilities sum to 1);
+      * sum over the entries of d_key is zero (per row, sum_i dS_i =
+        sum_i P_i dP_i - Delta = 0): the residual must sit far below the
+        random-walk size of the terms (1/sqrt(#entries) of their summed
+        magnitude), so only the rounding of P, dS and out is left;
+      * d_query of rows that see no block is exactly zero, all gradients are
+        finite, and a second call reproduces every bit."""
+    wl = synth.WORKLOADS[4]
+    log(f"[case] {wl.name}: full-size backward properties")
+    inp = synth.make_inputs(wl, device="cuda")
+    kc = nsa.nsa_compress(inp["k"], inp["w"], wl.act_seq_qlen, wl.l, wl.d)
+    vc = nsa.nsa_compress(inp["v"], inp["w"], wl.act_seq_qlen, wl.l, wl.d)
+    dout = synth.make_output_grad(wl, device="cuda", chunk_rows=16384)
+    c, s = gpu_prefix(wl)
+    plan = nsa.nsa_compress_attention_get_workspace(
+        wl.act_seq_qlen, c, s, wl.N1, wl.N2, wl.D1, wl.D2, wl.scale, wl.l, wl.d, wl.lsel, wl.count,
+        wl.torch_dtype)
+    try:
+        out, mx, sm = nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc)
+        dq, dk, dv = nsa.nsa_compress_attention_backward(plan, inp["q"], kc, vc, out, dout, mx, sm)
+        dq2, dk2, dv2 = nsa.nsa_compress_attention_backward(plan, inp["q"], kc, vc, out, dout, mx, sm)
+        torch.cuda.synchronize()
+    finally:
+        plan.destroy()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    # rows that see a block: local token t >= l - 1
+    seen = torch.zeros(wl.T, dtype=torch.bool, device="cuda")
+    start = 0
+    for T in wl.seqlens:
+        seen[start + wl.l - 1:start + T] = True
+        start += T
+    assert bool((dq[~seen] == 0).all())
+    G = wl.N1 // wl.N2
+    for g in range(wl.N2):
+        want = dout[seen, g * G:(g + 1) * G, :].double().sum((0, 1))
+        got = dv[:, g, :].double().sum(0)
+        rel = float(torch.linalg.norm(got - want) / torch.linalg.norm(want))
+        log(f"  head {g}: |sum dV - sum dout| / |sum dout| = {rel:.3e}")
+        assert rel <= 2e-3   # rounding of P to the element type: ~1e-4 seen
+        zs = dk[:, g, :].double().sum(0)
+        mag = dk[:, g, :].double().abs().sum(0)
+        ratio = float(torch.linalg.norm(zs) / torch.linalg.norm(mag))
+        walk = 1.0 / np.sqrt(dk.shape[0])
+        log(f"  head {g}: |sum dK| / |sum |dK|| = {ratio:.3e} (random walk {walk:.3e})")
+        assert ratio <= 0.1 * walk

@@ -312,6 +312,8 @@ def main() -> int:
                     help="time the selected-block attention over the compressed branch's top-k")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the compressed attention and of the compression")
+    ap.add_argument("--split-tiles", type=int, default=0,
+                    help="run the attention as the split launch, pieces of at most this many key tiles")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -380,6 +382,10 @@ def main() -> int:
         masks["topk_mask"] = (torch.arange(max(-(-T // wl.lsel) for T in wl.seqlens),
                                            device=dev)[None, :] * wl.lsel) > t
     ws_bytes = plan.info["masked_workspace_bytes"] if args.masks else plan.workspace_bytes
+    if args.split_tiles:
+        if args.masks:
+            raise SystemExit("--split-tiles applies to the positional rule only")
+        ws_bytes = max(ws_bytes, nsa.nsa_compress_attention_split_workspace(plan, args.split_tiles))
     ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -392,8 +398,12 @@ def main() -> int:
         nsa.nsa_compress(inp["v"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=vc, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc, workspace=ws, outputs=outs, stream=stream,
-                                       atten_mask=masks.get("atten_mask"))
+        if args.split_tiles:
+            nsa.nsa_compress_attention_fwd_split(plan, inp["q"], kc, vc, args.split_tiles, workspace=ws,
+                                                 outputs=outs, stream=stream)
+        else:
+            nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc, workspace=ws, outputs=outs, stream=stream,
+                                           atten_mask=masks.get("atten_mask"))
         if ev is not None:
             ev[3].record(stream)
         nsa.nsa_compress_attention_select(plan, inp["q"], kc, outs["softmax_max"], outs["softmax_sum"],
@@ -465,6 +475,8 @@ def main() -> int:
                    "D2": wl.D2, "l": wl.l, "d": wl.d, "lsel": wl.lsel, "count": wl.count,
                    "scale": wl.scale, "dtype": wl.dtype,
                    "masks": "explicit tensors (the causal rules spelled out)" if args.masks else "positional rules",
+                   "attention_launch": (f"split key ranges, at most {args.split_tiles} tiles of 32 blocks per piece"
+                                        if args.split_tiles else "single pass"),
                    "parallelism": "single-gpu"},
         "tflops_algorithmic": total_flops / (ms_step / 1e3) / 1e12,
         "frac_of_bf16_peak": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,

@@ -259,6 +259,37 @@ typedef struct nsa_masks {
 } nsa_masks;
 
 /*
+ * Split key ranges for nsa_compress_attention_fwd (same outputs, same
+ * reading of the MindSpore page's formula steps 1-7 up to P.V; positional
+ * causal rule only).  The attention kernel gives each workgroup a block of
+ * query rows and walks all the compressed blocks those rows see; when a few
+ * row blocks see far more blocks than the rest (short batches, one long
+ * sequence), their walk is the critical path of the launch.  Here a row block
+ * whose walk is longer than key_tiles_per_piece tiles of 32 compressed
+ * blocks is cut into pieces of at most that many tiles; each piece leaves
+ * unnormalised partial sums in the workspace, and a second kernel merges the
+ * pieces of every row (rescaled to their largest running max and added in
+ * piece order, so results are bitwise repeatable) and writes the outputs.
+ * The results equal the unsplit call's up to floating-point rounding.
+ *
+ * nsa_compress_attention_split_workspace -- host only: the workspace the split
+ *   call needs for this plan and key_tiles_per_piece (>= workspace_bytes of
+ *   the plan; the plan keeps the work list of the last value asked for).
+ * nsa_compress_attention_fwd_split -- as nsa_compress_attention_fwd, with
+ *   key_tiles_per_piece in [1, 2^20].
+ * Errors: those of nsa_compress_attention_fwd, plus NSA_ERR_CONSTRAINT
+ * (key_tiles_per_piece out of range) and NSA_ERR_WORKSPACE (workspace below
+ * the size returned above).
+ */
+nsa_status nsa_compress_attention_split_workspace(nsa_plan plan, int64_t key_tiles_per_piece,
+                                                  size_t* workspace_bytes);
+
+nsa_status nsa_compress_attention_fwd_split(nsa_plan plan, const void* query, const void* key,
+                                            const void* value, void* attention_out, float* softmax_max,
+                                            float* softmax_sum, int64_t key_tiles_per_piece,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The three second-phase calls with masks (masks may be NULL, and either
  * mask in it may be NULL).  The masks are packed to bits inside the
  * workspace first, so the workspace must hold masked_workspace_bytes (plan

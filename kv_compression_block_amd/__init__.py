@@ -35,6 +35,7 @@ from ._lib import Masks, NsaError, PlanInfo  # noqa: F401
 
 __all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_workspace",
            "nsa_compress_attention", "nsa_compress_attention_fwd", "nsa_compress_attention_select",
+           "nsa_compress_attention_split_workspace", "nsa_compress_attention_fwd_split",
            "nsa_select_attention", "nsa_compress_attention_backward", "nsa_compress_backward", "compress_attention", "Plan",
            "NsaError", "library_path"]
 
@@ -291,6 +292,34 @@ def nsa_compress_attention_fwd(plan: Plan, query: torch.Tensor, key: torch.Tenso
     else:
         st = lib.nsa_compress_attention_fwd_masked(plan.handle, _ptr(query), _ptr(key), _ptr(value),
                                                    ctypes.byref(m), *args)
+    _lib.check(st)
+    return o["attention_out"], o["softmax_max"], o["softmax_sum"]
+
+
+def nsa_compress_attention_split_workspace(plan: Plan, key_tiles_per_piece: int) -> int:
+    """Workspace bytes of ``nsa_compress_attention_fwd_split`` for this plan."""
+    n = ctypes.c_size_t(0)
+    _lib.check(_lib.load().nsa_compress_attention_split_workspace(plan.handle, int(key_tiles_per_piece),
+                                                                   ctypes.byref(n)))
+    return n.value
+
+
+def nsa_compress_attention_fwd_split(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                                     key_tiles_per_piece: int, workspace: Optional[torch.Tensor] = None,
+                                     outputs: Optional[dict] = None, stream=None):
+    """Steps 1-3 with the key range of long row blocks split into pieces of
+    at most ``key_tiles_per_piece`` tiles of 32 compressed blocks, merged by
+    a second kernel: returns (attention_out, softmax_max, softmax_sum)."""
+    _check_qkv(plan, query, key, value)
+    o = _alloc_outputs(plan, query, outputs, False)
+    need = nsa_compress_attention_split_workspace(plan, key_tiles_per_piece)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=query.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.load().nsa_compress_attention_fwd_split(
+        plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(o["attention_out"]), _ptr(o["softmax_max"]),
+        _ptr(o["softmax_sum"]), int(key_tiles_per_piece), _ptr(workspace), ws_bytes,
+        _stream_ptr(query.device, stream))
     _lib.check(st)
     return o["attention_out"], o["softmax_max"], o["softmax_sum"]
 

@@ -30,6 +30,8 @@ EXPORTS = (
     "nsa_compress_attention_get_workspace",
     "nsa_compress_attention",
     "nsa_compress_attention_fwd",
+    "nsa_compress_attention_split_workspace",
+    "nsa_compress_attention_fwd_split",
     "nsa_compress_attention_select",
     "nsa_compress_attention_masked",
     "nsa_compress_attention_fwd_masked",
@@ -102,6 +104,10 @@ def load() -> ctypes.CDLL:
     lib.nsa_compress_attention.restype = I32
     lib.nsa_compress_attention_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_compress_attention_fwd.restype = I32
+    lib.nsa_compress_attention_split_workspace.argtypes = [P, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.nsa_compress_attention_split_workspace.restype = I32
+    lib.nsa_compress_attention_fwd_split.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, P, ctypes.c_size_t, P]
+    lib.nsa_compress_attention_fwd_split.restype = I32
     lib.nsa_compress_attention_select.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_compress_attention_select.restype = I32
     MP = ctypes.POINTER(Masks)

@@ -91,11 +91,24 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
 
     // ---- workgroup -> (sequence, KV head, row block) -------------------------
     const int wg = blockIdx.x;
-    const int b = find_batch<true>(p.bt, p.B, wg);
+    int b, g, rb;
+    int split_kt0 = 0, split_nkt = 0, split_slot = -1;   // split launches only
+    const bool split = !XM && p.split != nullptr;
+    if (split) {
+        const SplitItem it = p.split[wg];
+        b = it.b;
+        g = it.g;
+        rb = it.rb;
+        split_kt0 = it.kt0;
+        split_nkt = it.n_kt;
+        split_slot = it.slot;
+    } else {
+        b = find_batch<true>(p.bt, p.B, wg);
+        const int idx = wg - p.bt[b].tile_off_a;
+        g = idx % p.N2;
+        rb = p.bt[b].n_rb_a - 1 - idx / p.N2;
+    }
     const BatchEnt be = p.bt[b];
-    const int idx = wg - be.tile_off_a;
-    const int g = idx % p.N2;
-    const int rb = be.n_rb_a - 1 - idx / p.N2;
     const int G = p.G;
     const int rows_total = be.T * G;
     const int row_wg = rb * C::ROWS;
@@ -151,6 +164,13 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         kt0 = __builtin_amdgcn_readfirstlane(lo < hi ? lo : 0);
         n_kt = __builtin_amdgcn_readfirstlane(lo < hi ? hi - lo : 0);
         n_full = __builtin_amdgcn_readfirstlane(lo == 0 ? min(min(full, be.n_cmp / KT), n_kt) : 0);
+    } else {
+        if (split) {
+            // this piece's tiles; those every row sees in full stay unmasked
+            n_full = max(0, min(n_full - split_kt0, split_nkt));
+            kt0 = split_kt0;
+            n_kt = split_nkt;
+        }
     }
 
     // ---- tile staging ----------------------------------------------------------
@@ -306,7 +326,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
             } else if constexpr (MASK) {
                 // key kt*KT + kb*32 + 8*(r/4) + 4*hf + r%4 is visible iff it is
                 // below nvq: compare the compile-time part against one bound
-                const int lim = nvq[qb] - kt * KT - 4 * hf;
+                const int lim = nvq[qb] - (kt0 + kt) * KT - 4 * hf;
 #pragma unroll
                 for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -503,6 +523,27 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     // L2 is better kept for the K/V tiles.  Every wave
     // is done with the K slots after this barrier; each wave stages its rows
     // in a private part of them, half of D2 per pass.
+    if (split && split_slot >= 0) {
+        // a piece of a split row block: unnormalised O with the running sum,
+        // reference max and true max of each row, for the combine kernel
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            if (!vq[qb])
+                continue;
+            const int rr = (wave * QB + qb) * 32 + l32;
+            float* dst = p.part + ((int64_t)split_slot * C::ROWS + rr) * (D2 + 4);
+            const float lf = half_sum(lsum[qb]);
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *(f32x4*)(dst + db * 32 + 8 * r4 + 4 * hf) =
+                        f32x4{o[qb][db][4 * r4], o[qb][db][4 * r4 + 1], o[qb][db][4 * r4 + 2], o[qb][db][4 * r4 + 3]};
+            if (hf == 0)
+                *(f32x4*)(dst + D2) = f32x4{lf, mref[qb], mtrue[qb], 0.f};
+        }
+        return;
+    }
     __syncthreads();
     constexpr int HD = D2 / 2;                 // dims per pass
     constexpr int OPITCH = HD + 8;             // staging row pitch (elements), 16 B pad
@@ -553,6 +594,65 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     }
 }
 
+// Combine of a split row block: per row, the pieces' partial sums are
+// brought to the largest reference max and added in piece order (bitwise
+// repeatable); then the outputs as the single-pass epilogue writes them.
+// Thread = (row, 4 consecutive dims); 256 threads stride over the block.
+template <typename E, int D2, int ROWS>
+__global__ __launch_bounds__(256) void k_cmp_attn_combine(AttnParams p, const CombineItem* items)
+{
+    const CombineItem it = items[blockIdx.x];
+    const BatchEnt be = p.bt[it.b];
+    const int G = p.G;
+    const int rows_total = be.T * G;
+    const float c = p.c;
+    for (int u = threadIdx.x; u < ROWS * (D2 / 4); u += 256) {
+        const int rr = u / (D2 / 4), d4 = (u % (D2 / 4)) * 4;
+        const int r = it.rb * ROWS + rr;
+        if (r >= rows_total)
+            continue;
+        const float* base = p.part + ((int64_t)it.slot0 * ROWS + rr) * (D2 + 4);
+        const int64_t piece = (int64_t)ROWS * (D2 + 4);
+        float R = -INFINITY, M = -INFINITY;
+        for (int s = 0; s < it.n; ++s) {
+            const f32x4 st = *(const f32x4*)(base + s * piece + D2);
+            R = fmaxf(R, st[1]);
+            M = fmaxf(M, st[2]);
+        }
+        float L = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (R != -INFINITY) {
+            for (int s = 0; s < it.n; ++s) {
+                const f32x4 st = *(const f32x4*)(base + s * piece + D2);
+                if (st[1] == -INFINITY)
+                    continue;
+                const float w = exp2f((st[1] - R) * c);
+                L += st[0] * w;
+                const f32x4 ov = *(const f32x4*)(base + s * piece + d4);
+                acc[0] += ov[0] * w;
+                acc[1] += ov[1] * w;
+                acc[2] += ov[2] * w;
+                acc[3] += ov[3] * w;
+            }
+        }
+        const bool empty = (M == -INFINITY);
+        const float inv = empty ? 0.f : 1.f / L;
+        const int tok = r / G;
+        const int64_t orow = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)it.g * G + (r - tok * G);
+        *(u32x2*)(p.out + orow * D2 + d4) = u32x2{E::pack2(acc[0] * inv, acc[1] * inv),
+                                                  E::pack2(acc[2] * inv, acc[3] * inv)};
+        if (d4 == 0) {
+            const float smv = empty ? -INFINITY : M * p.abs_scale;
+            const float ssv = empty ? 0.f : L * exp2f((R - M) * c);
+            const f32x4 a = {smv, smv, smv, smv}, bb = {ssv, ssv, ssv, ssv};
+            *(f32x4*)(p.smax + orow * 8) = a;
+            *(f32x4*)(p.smax + orow * 8 + 4) = a;
+            *(f32x4*)(p.ssum + orow * 8) = bb;
+            *(f32x4*)(p.ssum + orow * 8 + 4) = bb;
+        }
+    }
+}
+
 // Launch shape per head-dim pair: query-row blocks per wave (QB), key-tile
 // length (KT) and waves per workgroup.  QB = 1 keeps each wave within 256
 // registers; KT = 32 keeps the score tiles small enough for three
@@ -591,6 +691,33 @@ static hipError_t launch_typed(int d1, int d2, const AttnParams& p, int n_tiles,
     }
     NSA_ATTN_CONFIGS(X)
 #undef X
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+static hipError_t launch_combine_typed(int d1, int d2, const AttnParams& p, const CombineItem* items,
+                                       int n_items, hipStream_t stream)
+{
+#define X(a, b, q, k, w)                                                                          \
+    if (d1 == a && d2 == b) {                                                                  \
+        hipLaunchKernelGGL((k_cmp_attn_combine<E, b, AttnCfg<a, b, q, k, w>::ROWS>), dim3(n_items), dim3(256), 0, \
+                           stream, p, items);                                                  \
+        return hipGetLastError();                                                              \
+    }
+    NSA_ATTN_CONFIGS(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_combine(int dtype, int d1, int d2, const AttnParams& p, const CombineItem* items,
+                               int n_items, hipStream_t stream)
+{
+    if (n_items <= 0)
+        return hipSuccess;
+    if (dtype == ElemBf16::code)
+        return launch_combine_typed<ElemBf16>(d1, d2, p, items, n_items, stream);
+    if (dtype == ElemF16::code)
+        return launch_combine_typed<ElemF16>(d1, d2, p, items, n_items, stream);
     return hipErrorInvalidValue;
 }
 

@@ -88,6 +88,11 @@ struct nsa_plan_s {
     int64_t tiles_a, tiles_c, tiles_s;
     size_t ws_bytes;
     std::vector<nsa::BatchEnt> table;
+    // split attention launch for the last key_tiles_per_piece asked for
+    int64_t split_C = 0;
+    std::vector<nsa::SplitItem> split_items;
+    std::vector<nsa::CombineItem> comb_items;
+    size_t split_items_off = 0, comb_items_off = 0, split_part_off = 0, ws_split_bytes = 0;
 };
 
 extern "C" {
@@ -417,9 +422,8 @@ nsa_status upload_table(nsa_plan plan, void* workspace, hipStream_t s)
 float exp2_scale(const nsa_plan_s* plan) { return std::fabs(plan->scale) * 1.4426950408889634f; }
 uint32_t q_sign(const nsa_plan_s* plan) { return plan->scale < 0.f ? 0x80008000u : 0u; }
 
-nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const void* value,
-                      void* attention_out, float* softmax_max, float* softmax_sum, void* workspace,
-                      hipStream_t s, const uint32_t* vis = nullptr, const int4* vis_span = nullptr)
+nsa::AttnParams fwd_params(nsa_plan plan, const void* query, const void* key, const void* value,
+                           void* attention_out, float* softmax_max, float* softmax_sum, void* workspace)
 {
     const float abs_scale = std::fabs(plan->scale);
     const float c = exp2_scale(plan);
@@ -445,13 +449,65 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
     // the running max moves only when a score beats it by more than 8 in base 2
     a.thr = std::fmin(8.0f / a.c, 3.0e38f);
     a.qsign = q_sign(plan);
+    a.vis_words = (int)plan->vis_words;
+    return a;
+}
+
+nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const void* value,
+                      void* attention_out, float* softmax_max, float* softmax_sum, void* workspace,
+                      hipStream_t s, const uint32_t* vis = nullptr, const int4* vis_span = nullptr)
+{
+    nsa::AttnParams a = fwd_params(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace);
     a.vis = vis;
     a.vis_span = vis_span;
-    a.vis_words = (int)plan->vis_words;
     hipError_t e = nsa::launch_cmp_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     return NSA_OK;
+}
+
+// Work list of a split attention launch: the attention kernel's row blocks
+// in its own order (per sequence and KV head, costliest first); a row block
+// with more than C key tiles becomes ceil(n / C) pieces of at most C tiles,
+// each with a partial slot, and one combine item.
+void build_split(nsa_plan plan, int64_t C)
+{
+    if (plan->split_C == C)
+        return;
+    constexpr int KT = nsa::kKeyTileMin;   // key tile of the attention kernel
+    const int64_t rows_a = nsa::cmp_attn_rows_per_wg((int)plan->D1, (int)plan->D2);
+    const int64_t G = plan->N1 / plan->N2;
+    plan->split_C = 0;
+    plan->split_items.clear();
+    plan->comb_items.clear();
+    int32_t slot = 0;
+    for (size_t b = 0; b < plan->table.size(); ++b) {
+        const nsa::BatchEnt& e = plan->table[b];
+        for (int64_t idx = 0; idx < (int64_t)e.n_rb_a * plan->N2; ++idx) {
+            const int32_t g = (int32_t)(idx % plan->N2);
+            const int32_t rb = (int32_t)(e.n_rb_a - 1 - idx / plan->N2);
+            const int64_t last_row = std::min<int64_t>((int64_t)(rb + 1) * rows_a, (int64_t)e.T * G) - 1;
+            const int64_t t = last_row / G;
+            const int64_t nv = t < plan->l - 1 ? 0 : std::min<int64_t>((t - plan->l + 1) / plan->d + 1, e.n_cmp);
+            const int32_t n_kt = (int32_t)((nv + KT - 1) / KT);
+            if (n_kt <= C) {
+                plan->split_items.push_back({(int32_t)b, g, rb, 0, n_kt, -1, 0, 0});
+                continue;
+            }
+            const int32_t pieces = (int32_t)((n_kt + C - 1) / C);
+            for (int32_t p = 0; p < pieces; ++p)
+                plan->split_items.push_back({(int32_t)b, g, rb, (int32_t)(p * C),
+                                             (int32_t)std::min<int64_t>(C, n_kt - p * C), slot + p, 0, 0});
+            plan->comb_items.push_back({(int32_t)b, g, rb, slot, pieces, 0, 0, 0});
+            slot += pieces;
+        }
+    }
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    plan->split_items_off = plan->ws_bytes;
+    plan->comb_items_off = plan->split_items_off + up(plan->split_items.size() * sizeof(nsa::SplitItem));
+    plan->split_part_off = plan->comb_items_off + up(plan->comb_items.size() * sizeof(nsa::CombineItem));
+    plan->ws_split_bytes = plan->split_part_off + (size_t)slot * (size_t)rows_a * (size_t)(plan->D2 + 4) * 4;
+    plan->split_C = C;
 }
 
 nsa_status launch_select(nsa_plan plan, const void* query, const void* key, const float* softmax_max,
@@ -580,6 +636,70 @@ nsa_status nsa_compress_attention_fwd(nsa_plan plan, const void* query, const vo
         return st;
     if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s)) != NSA_OK)
         return st;
+    return ok();
+}
+
+nsa_status nsa_compress_attention_split_workspace(nsa_plan plan, int64_t key_tiles_per_piece,
+                                                  size_t* workspace_bytes)
+{
+    if (!plan || !workspace_bytes)
+        return fail(NSA_ERR_NULLPTR, "plan and workspace_bytes must not be NULL");
+    if (key_tiles_per_piece < 1 || key_tiles_per_piece > (1 << 20))
+        return fail(NSA_ERR_CONSTRAINT, "key_tiles_per_piece must be in [1, 2^20], got %lld",
+                    (long long)key_tiles_per_piece);
+    try {
+        build_split(plan, key_tiles_per_piece);
+    } catch (const std::bad_alloc&) {
+        plan->split_C = 0;
+        return fail(NSA_ERR_UNSUPPORTED, "out of host memory for the split work list");
+    }
+    if (plan->split_items.size() > (size_t)INT32_MAX)
+        return fail(NSA_ERR_UNSUPPORTED, "problem too large for one launch");
+    *workspace_bytes = plan->ws_split_bytes;
+    return ok();
+}
+
+nsa_status nsa_compress_attention_fwd_split(nsa_plan plan, const void* query, const void* key,
+                                            const void* value, void* attention_out, float* softmax_max,
+                                            float* softmax_sum, int64_t key_tiles_per_piece,
+                                            void* workspace, size_t workspace_bytes, void* stream)
+{
+    size_t need = 0;
+    nsa_status st = nsa_compress_attention_split_workspace(plan, key_tiles_per_piece, &need);
+    if (st != NSA_OK)
+        return st;
+    if (plan->T1 > 0 && (!query || !attention_out || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query and the three outputs must not be NULL");
+    if (plan->T2 > 0 && (!key || !value))
+        return fail(NSA_ERR_NULLPTR, "key and value must not be NULL");
+    if (workspace_bytes < need || !workspace)
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    if ((st = check_exec(plan, workspace, workspace_bytes,
+                         {query, key, value, attention_out, softmax_max, softmax_sum, workspace}, {})) != NSA_OK)
+        return st;
+    if (plan->T1 == 0)
+        return ok();
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = upload_table(plan, workspace, s)) != NSA_OK)
+        return st;
+    char* ws = (char*)workspace;
+    hipError_t e = hipMemcpyAsync(ws + plan->split_items_off, plan->split_items.data(),
+                                  plan->split_items.size() * sizeof(nsa::SplitItem), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && !plan->comb_items.empty())
+        e = hipMemcpyAsync(ws + plan->comb_items_off, plan->comb_items.data(),
+                           plan->comb_items.size() * sizeof(nsa::CombineItem), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "workspace upload failed: %s", hipGetErrorString(e));
+    nsa::AttnParams a = fwd_params(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace);
+    a.split = (const nsa::SplitItem*)(ws + plan->split_items_off);
+    a.part = (float*)(ws + plan->split_part_off);
+    e = nsa::launch_cmp_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->split_items.size(), s);
+    if (e == hipSuccess)
+        e = nsa::launch_attn_combine(plan->dtype, (int)plan->D1, (int)plan->D2, a,
+                                     (const nsa::CombineItem*)(ws + plan->comb_items_off),
+                                     (int)plan->comb_items.size(), s);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "split attention launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -81,6 +81,13 @@ struct MaskPackParams {
 hipError_t launch_pack_mask(const MaskPackParams& p, hipStream_t stream);
 
 // ---- attention kernels ------------------------------------------------------
+// One workgroup of a split attention launch: row block rb of (sequence b,
+// KV head g), key tiles [kt0, kt0 + n_kt).  slot < 0: the row block is not
+// split and the workgroup writes the outputs; else its partial slot.
+struct SplitItem {
+    int32_t b, g, rb, kt0, n_kt, slot, pad0, pad1;
+};
+
 struct AttnParams {
     const uint16_t* q;    // [T1, N1, D1]
     const uint16_t* kc;   // [T2, N2, D1]
@@ -98,7 +105,18 @@ struct AttnParams {
     const uint32_t* vis;  // NULL (positional rule) or packed atten_mask [T_max, vis_words]
     const int4* vis_span; // per row of vis: span of words with a kept pair, leading full words
     int vis_words;
+    // Split key ranges (positional rule only): NULL, or one item per
+    // workgroup; pieces with slot >= 0 leave partial sums in `part`.
+    const SplitItem* split;
+    float* part;          // [slots][rows per workgroup][D2 + 4]: O, then (L, R, M)
 };
+
+// One row block whose pieces occupy partial slots [slot0, slot0 + n).
+struct CombineItem {
+    int32_t b, g, rb, slot0, n, pad0, pad1, pad2;
+};
+hipError_t launch_attn_combine(int dtype, int d1, int d2, const AttnParams& p, const CombineItem* items,
+                               int n_items, hipStream_t stream);
 
 // Compressed entries per key tile of the importance/top-k kernel: 32 keeps
 // its registers within three waves per SIMD up to D1 = 128; D1 = 192 stays

@@ -221,3 +221,29 @@ def test_select_attention_rejects_before_touching_the_device():
     assert lib.nsa_select_attention(plan, fake, fake, fake, fake, fake, fake, fake, ws, None) \
         == _lib.NSA_ERR_UNSUPPORTED
     lib.nsa_plan_destroy(plan)
+
+
+def test_split_workspace_host_checks():
+    """The split attention's workspace query is host only: piece lengths
+    outside [1, 2^20] are refused, and shorter pieces need at least as much
+    workspace (more partial slots)."""
+    import synth
+    wl = synth.WORKLOADS[1]
+    c, s, pc, ps = [], [], 0, 0
+    for T in wl.seqlens:
+        pc += nsa.nsa_compress_out_len(T, wl.l, wl.d)
+        ps += -(-T // wl.lsel)
+        c.append(pc)
+        s.append(ps)
+    plan = nsa.nsa_compress_attention_get_workspace(wl.act_seq_qlen, c, s, wl.N1, wl.N2, wl.D1, wl.D2, wl.scale,
+                                                    wl.l, wl.d, wl.lsel, wl.count, wl.torch_dtype)
+    try:
+        for bad in (0, -3, (1 << 20) + 1):
+            with pytest.raises(ValueError):
+                nsa.nsa_compress_attention_split_workspace(plan, bad)
+        sizes = [nsa.nsa_compress_attention_split_workspace(plan, t) for t in (64, 8, 4, 1)]
+        assert sizes[0] >= plan.workspace_bytes
+        assert sizes == sorted(sizes)
+        assert sizes[-1] > sizes[0]
+    finally:
+        plan.destroy()

@@ -259,6 +259,29 @@ typedef struct nsa_masks {
 } nsa_masks;
 
 /*
+ * nsa_compress_attention_get_workspace_kv -- as
+ * nsa_compress_attention_get_workspace, for chunked prefill: sequence b has
+ * Tkv_b = act_seq_kvlen[b] - act_seq_kvlen[b-1] key/value tokens (prefix
+ * sums, host) and its Tq_b <= Tkv_b queries are the LAST Tq_b of them (the
+ * causal rules of the MindSpore page's steps 3 and 6 aligned to the
+ * bottom-right: query i has position Tkv_b - Tq_b + i).  Compressed and
+ * select lengths follow the key/value tokens: act_cmp_seq_kvlen must hold
+ * floor((Tkv_b - l)/d) + 1 and act_sel_seq_kvlen ceil(Tkv_b / l'); key and
+ * value passed to the calls are the compressed key/value tokens.  With
+ * Tkv_b = Tq_b for every b the plan equals the plain one.  A plan with some
+ * Tkv_b > Tq_b serves nsa_compress_attention, _fwd and _select (and the
+ * masked calls without masks); explicit masks, selected-block attention,
+ * the backward and the split launch return NSA_ERR_UNSUPPORTED for it.
+ * Errors: those of nsa_compress_attention_get_workspace, plus NSA_ERR_SHAPE
+ * when Tkv_b < Tq_b.
+ */
+nsa_status nsa_compress_attention_get_workspace_kv(
+    int64_t batch, const int64_t* act_seq_qlen, const int64_t* act_seq_kvlen,
+    const int64_t* act_cmp_seq_kvlen, const int64_t* act_sel_seq_kvlen, int64_t head_num,
+    int64_t kv_head_num, int64_t d1, int64_t d2, float scale_value, int64_t l, int64_t d,
+    int64_t lsel, int64_t count, nsa_dtype dtype, size_t* workspace_bytes, nsa_plan* plan_out);
+
+/*
  * Split key ranges for nsa_compress_attention_fwd (same outputs, same
  * reading of the MindSpore page's formula steps 1-7 up to P.V; positional
  * causal rule only).  The attention kernel gives each workgroup a block of

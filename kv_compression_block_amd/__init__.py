@@ -157,7 +157,11 @@ def nsa_compress_attention_get_workspace(actual_seq_qlen, actual_cmp_seq_kvlen, 
                                          scale_value: float, compress_block_size: int,
                                          compress_stride: int, select_block_size: int,
                                          select_block_count: int,
-                                         dtype: torch.dtype = torch.bfloat16) -> Plan:
+                                         dtype: torch.dtype = torch.bfloat16, actual_seq_kvlen=None) -> Plan:
+    """Validates and plans steps 2-7.  ``actual_seq_kvlen`` (prefix sums of
+    key/value tokens, optional): each sequence's queries are then its last
+    tokens (chunked prefill), and the compressed/select lengths follow the
+    key/value tokens."""
     if not isinstance(scale_value, (int, float)):
         raise TypeError("scale_value must be a float")
     for name, v in (("head_num", head_num), ("kv_head_num", kv_head_num), ("d1", d1), ("d2", d2),
@@ -172,10 +176,15 @@ def nsa_compress_attention_get_workspace(actual_seq_qlen, actual_cmp_seq_kvlen, 
         raise ValueError("the three prefix-sum lists must have the same length")
     ws = ctypes.c_size_t(0)
     h = ctypes.c_void_p(0)
-    st = _lib.load().nsa_compress_attention_get_workspace(
-        B, q, c, s, head_num, kv_head_num, d1, d2, float(scale_value), compress_block_size,
-        compress_stride, select_block_size, select_block_count, _dtype_code(dtype),
-        ctypes.byref(ws), ctypes.byref(h))
+    rest = (head_num, kv_head_num, d1, d2, float(scale_value), compress_block_size, compress_stride,
+            select_block_size, select_block_count, _dtype_code(dtype), ctypes.byref(ws), ctypes.byref(h))
+    if actual_seq_kvlen is None:
+        st = _lib.load().nsa_compress_attention_get_workspace(B, q, c, s, *rest)
+    else:
+        kv, Bk = _prefix(actual_seq_kvlen, "actual_seq_kvlen")
+        if Bk != B:
+            raise ValueError("actual_seq_kvlen must have the length of actual_seq_qlen")
+        st = _lib.load().nsa_compress_attention_get_workspace_kv(B, q, kv, c, s, *rest)
     _lib.check(st)
     return Plan(h, ws.value)
 

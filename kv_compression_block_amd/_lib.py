@@ -28,6 +28,7 @@ EXPORTS = (
     "nsa_compress_out_len",
     "nsa_compress",
     "nsa_compress_attention_get_workspace",
+    "nsa_compress_attention_get_workspace_kv",
     "nsa_compress_attention",
     "nsa_compress_attention_fwd",
     "nsa_compress_attention_split_workspace",
@@ -100,6 +101,9 @@ def load() -> ctypes.CDLL:
         I64, P, P, P, I64, I64, I64, I64, ctypes.c_float, I64, I64, I64, I64, I32,
         ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_void_p)]
     lib.nsa_compress_attention_get_workspace.restype = I32
+    lib.nsa_compress_attention_get_workspace_kv.argtypes = [
+        ctypes.c_int64, P, P, P, P] + lib.nsa_compress_attention_get_workspace.argtypes[4:]
+    lib.nsa_compress_attention_get_workspace_kv.restype = I32
     lib.nsa_compress_attention.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_compress_attention.restype = I32
     lib.nsa_compress_attention_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         const int tok = r / G;
         const int hh = r - tok * G;
         grow[qb] = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
-        nvq[qb] = vq[qb] ? n_visible(tok, p.l, p.d, be.n_cmp) : 0;
+        nvq[qb] = vq[qb] ? n_visible(tok + be.pos_off, p.l, p.d, be.n_cmp) : 0;
         mrow[qb] = vq[qb] ? tok : 0;
         // Rows past the sequence read the workgroup's first row (always valid);
         // they see no block and are never written.
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         }
     }
     const int last_row = min(row_wg + C::ROWS, rows_total) - 1;
-    const int nv_max = XM ? be.n_cmp : n_visible(last_row / G, p.l, p.d, be.n_cmp);
-    const int nv_min = XM ? 0 : n_visible(row_wg / G, p.l, p.d, be.n_cmp);
+    const int nv_max = XM ? be.n_cmp : n_visible(last_row / G + be.pos_off, p.l, p.d, be.n_cmp);
+    const int nv_min = XM ? 0 : n_visible(row_wg / G + be.pos_off, p.l, p.d, be.n_cmp);
     // XM: tiles [kt0, kt0 + n_kt) hold every kept entry of the workgroup's
     // tokens, and the first n_full of them (only when kt0 = 0) are kept
     // whole by every token (wave-uniform: every wave reduces over all of

@@ -88,6 +88,7 @@ struct nsa_plan_s {
     int64_t tiles_a, tiles_c, tiles_s;
     size_t ws_bytes;
     std::vector<nsa::BatchEnt> table;
+    bool chunked = false;   // some sequence has key/value tokens before its first query
     // split attention launch for the last key_tiles_per_piece asked for
     int64_t split_C = 0;
     std::vector<nsa::SplitItem> split_items;
@@ -202,8 +203,8 @@ nsa_status nsa_compress(const void* input, const void* weight, const int64_t* ac
     return ok();
 }
 
-nsa_status nsa_compress_attention_get_workspace(
-    int64_t batch, const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen,
+static nsa_status make_plan(
+    int64_t batch, const int64_t* act_seq_qlen, const int64_t* act_seq_kvlen, const int64_t* act_cmp_seq_kvlen,
     const int64_t* act_sel_seq_kvlen, int64_t head_num, int64_t kv_head_num, int64_t d1,
     int64_t d2, float scale_value, int64_t l, int64_t d, int64_t lsel, int64_t count,
     nsa_dtype dtype, size_t* workspace_bytes, nsa_plan* plan_out)
@@ -241,13 +242,21 @@ nsa_status nsa_compress_attention_get_workspace(
     if (!std::isfinite(scale_value))
         return fail(NSA_ERR_CONSTRAINT, "scale_value must be finite");
 
-    std::vector<int64_t> qlen, clen, slen;
+    std::vector<int64_t> qlen, kvlen, clen, slen;
     if ((st = read_prefix(act_seq_qlen, batch, "actual_seq_qlen", qlen)) != NSA_OK) return st;
+    if (act_seq_kvlen) {
+        if ((st = read_prefix(act_seq_kvlen, batch, "actual_seq_kvlen", kvlen)) != NSA_OK) return st;
+    } else {
+        kvlen = qlen;
+    }
     if ((st = read_prefix(act_cmp_seq_kvlen, batch, "actual_cmp_seq_kvlen", clen)) != NSA_OK) return st;
     if ((st = read_prefix(act_sel_seq_kvlen, batch, "actual_sel_seq_kvlen", slen)) != NSA_OK) return st;
     int64_t S_max = 0;
     for (int64_t b = 0; b < batch; ++b) {
-        const int64_t T = qlen[(size_t)b];
+        const int64_t T = kvlen[(size_t)b];
+        if (T < qlen[(size_t)b])
+            return fail(NSA_ERR_SHAPE, "sequence %lld: %lld query tokens but only %lld key/value tokens",
+                        (long long)b, (long long)qlen[(size_t)b], (long long)T);
         const int64_t nc = n_cmp_of(T, l, d);
         const int64_t ns = (T + lsel - 1) / lsel;
         if (clen[(size_t)b] != nc)
@@ -323,6 +332,9 @@ nsa_status nsa_compress_attention_get_workspace(
         std::memset(&e, 0, sizeof e);
         e.q_off = (int32_t)q_off;
         e.T = (int32_t)T;
+        e.pos_off = (int32_t)(kvlen[(size_t)b] - T);
+        if (e.pos_off > 0)
+            plan->chunked = true;
         e.cmp_off = (int32_t)c_off;
         e.n_cmp = (int32_t)clen[(size_t)b];
         e.n_rb_a = (int32_t)((T * G + rows_a - 1) / rows_a);
@@ -367,6 +379,31 @@ nsa_status nsa_compress_attention_get_workspace(
     *workspace_bytes = plan->ws_bytes;
     *plan_out = plan;
     return ok();
+}
+
+nsa_status nsa_compress_attention_get_workspace(
+    int64_t batch, const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen,
+    const int64_t* act_sel_seq_kvlen, int64_t head_num, int64_t kv_head_num, int64_t d1,
+    int64_t d2, float scale_value, int64_t l, int64_t d, int64_t lsel, int64_t count,
+    nsa_dtype dtype, size_t* workspace_bytes, nsa_plan* plan_out)
+{
+    return make_plan(batch, act_seq_qlen, nullptr, act_cmp_seq_kvlen, act_sel_seq_kvlen, head_num, kv_head_num,
+                     d1, d2, scale_value, l, d, lsel, count, dtype, workspace_bytes, plan_out);
+}
+
+nsa_status nsa_compress_attention_get_workspace_kv(
+    int64_t batch, const int64_t* act_seq_qlen, const int64_t* act_seq_kvlen,
+    const int64_t* act_cmp_seq_kvlen, const int64_t* act_sel_seq_kvlen, int64_t head_num,
+    int64_t kv_head_num, int64_t d1, int64_t d2, float scale_value, int64_t l, int64_t d,
+    int64_t lsel, int64_t count, nsa_dtype dtype, size_t* workspace_bytes, nsa_plan* plan_out)
+{
+    if (!act_seq_kvlen) {
+        if (plan_out)
+            *plan_out = nullptr;
+        return fail(NSA_ERR_NULLPTR, "actual_seq_kvlen must not be NULL");
+    }
+    return make_plan(batch, act_seq_qlen, act_seq_kvlen, act_cmp_seq_kvlen, act_sel_seq_kvlen, head_num,
+                     kv_head_num, d1, d2, scale_value, l, d, lsel, count, dtype, workspace_bytes, plan_out);
 }
 
 nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info)
@@ -576,6 +613,8 @@ nsa_status prepare_masks(nsa_plan plan, const nsa_masks* masks, bool use_atten, 
         return NSA_OK;
     const bool a = use_atten && masks->atten_mask;
     const bool t = use_topk && masks->topk_mask;
+    if ((a || t) && plan->chunked)
+        return fail(NSA_ERR_UNSUPPORTED, "explicit masks with query tokens after key/value tokens are not built");
     if (a && (masks->atten_rows < plan->T_max || masks->atten_cols < plan->ncmp_max))
         return fail(NSA_ERR_SHAPE, "atten_mask is [%lld, %lld]; it needs at least [%lld, %lld] "
                     "(longest sequence, most compressed entries)", (long long)masks->atten_rows,
@@ -644,6 +683,8 @@ nsa_status nsa_compress_attention_split_workspace(nsa_plan plan, int64_t key_til
 {
     if (!plan || !workspace_bytes)
         return fail(NSA_ERR_NULLPTR, "plan and workspace_bytes must not be NULL");
+    if (plan->chunked)
+        return fail(NSA_ERR_UNSUPPORTED, "split launches with query tokens after key/value tokens are not built");
     if (key_tiles_per_piece < 1 || key_tiles_per_piece > (1 << 20))
         return fail(NSA_ERR_CONSTRAINT, "key_tiles_per_piece must be in [1, 2^20], got %lld",
                     (long long)key_tiles_per_piece);
@@ -849,6 +890,8 @@ nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* ke
 {
     if (!plan)
         return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->chunked)
+        return fail(NSA_ERR_UNSUPPORTED, "selected-block attention with query tokens after key/value tokens is not built");
     if (plan->T1 > 0 && (!query || !key || !value || !topk_indices || !attention_out || !softmax_lse))
         return fail(NSA_ERR_NULLPTR, "query, key, value, topk_indices and the outputs must not be NULL");
     if (plan->lsel % 32 != 0)
@@ -901,6 +944,8 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
 {
     if (!plan)
         return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->chunked)
+        return fail(NSA_ERR_UNSUPPORTED, "the backward with query tokens after key/value tokens is not built");
     if (plan->T1 > 0 && (!query || !attention_out || !d_attention_out || !softmax_max || !softmax_sum || !d_query))
         return fail(NSA_ERR_NULLPTR, "query, attention_out, its gradient, the softmax statistics and d_query must not be NULL");
     if (plan->T2 > 0 && (!key || !value || !d_key || !d_value))

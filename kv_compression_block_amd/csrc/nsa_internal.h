@@ -24,8 +24,10 @@ struct BatchEnt {
     int32_t tile_off_s; // first workgroup of the selected-block attention kernel
     int32_t n_rb_s;     // row blocks of the selected-block attention kernel (per KV head)
     int32_t tile_off_k; // first workgroup of the key-side backward kernel (32 entries each, per KV head)
+    int32_t pos_off;    // KV tokens before the first query token (chunked prefill; 0 otherwise)
+    int32_t pad0, pad1, pad2;
 };
-static_assert(sizeof(BatchEnt) == 48, "BatchEnt layout");
+static_assert(sizeof(BatchEnt) == 64, "BatchEnt layout");
 
 // ---- compression kernel ---------------------------------------------------
 constexpr int kCompressMaxSeg = 128;   // sequences per launch (more -> several launches)

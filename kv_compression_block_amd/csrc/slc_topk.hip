@@ -145,8 +145,8 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
             bias[rr][r] = __shfl(bias_lane, rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3));
 
     const int tok_last = min(tok_wg + ((waves * 64) >> LOG2GP), be.T) - 1;
-    const int nv_max = XM ? be.n_cmp : n_visible(tok_last, p.l, p.d, be.n_cmp);
-    const int nv_min = XM ? 0 : n_visible(tok_wg, p.l, p.d, be.n_cmp);
+    const int nv_max = XM ? be.n_cmp : n_visible(tok_last + be.pos_off, p.l, p.d, be.n_cmp);
+    const int nv_min = XM ? 0 : n_visible(tok_wg + be.pos_off, p.l, p.d, be.n_cmp);
     const int n_kt = (nv_max + KT - 1) / KT;
     // Key tiles [kt_begin, kt_end).  XM: the tiles that hold a kept entry of
     // one of the workgroup's tokens (wave-uniform: every wave reduces over
@@ -337,8 +337,8 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
                     if constexpr (MASK && !XM) {
                         const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
                         const int tok = tok_w + (pr >> LOG2GP);
-                        // visible iff key*d + l - 1 <= tok
-                        pv = (key * p.d + p.l - 1 <= tok) ? pv : 0.f;
+                        // visible iff key*d + l - 1 <= the token's position
+                        pv = (key * p.d + p.l - 1 <= tok + be.pos_off) ? pv : 0.f;
                     }
                     acc[(rr * 32 + 8 * (r >> 2) + (r & 3)) >> LOG2GP][kb] += pv;
                 }
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     {
         const int keys_done = kt_end * KT;
         const int jlo = (keys_done + R - 1) / R;
-        const int j_end = (p.pslc || p.cand) ? be.S_sel : min(be.S_sel, (tok_w + TOKW - 1) / p.lsel + 1);
+        const int j_end = (p.pslc || p.cand) ? be.S_sel : min(be.S_sel, (tok_w + TOKW - 1 + be.pos_off) / p.lsel + 1);
         for (int j = jlo + lane; j < j_end; j += 64)
             for (int tw = 0; tw < TOKW; ++tw)
                 my_bins[tw * p.sb + j] = stencil(my_ring + tw * RING, j, keys_done);
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         // Candidates: j with j*l' <= t (a prefix of the select blocks), or
         // the set bits of the token's packed topk_mask row.  Bit i of cm:
         // block lane + 64 i is a candidate.
-        const int range = p.cand ? be.S_sel : min(tok / p.lsel + 1, be.S_sel);
+        const int range = p.cand ? be.S_sel : min((tok + be.pos_off) / p.lsel + 1, be.S_sel);
         const int nch = (range + 63) >> 6;    // 64-block chunks of this row
         uint32_t cm = 0;
         int nvalid = 0;                       // number of candidates

@@ -81,7 +81,7 @@ def _load():
                                          I64, I64, I64, I64, ctypes.c_int,
                                          P, P, P, P, I64, P]
     lib.nsa_oracle_attention.restype = ctypes.c_int
-    lib.nsa_oracle_attention_masked.argtypes = [P, P, I64, P, P, P, P, I64,
+    lib.nsa_oracle_attention_masked.argtypes = [P, P, I64, P, P, P, P, P, I64,
                                                 I64, I64, I64, I64, ctypes.c_double,
                                                 I64, I64, I64, I64, ctypes.c_int,
                                                 P, I64, I64, P, I64, I64,
@@ -209,8 +209,13 @@ def compress(x_bits, w_bits, act_seq_len, l: int, d: int, dtype: str = "bf16") -
 def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_kvlen,
               N1: int, N2: int, scale: float, l: int, d: int, lsel: int, count: int,
               s_stride: Optional[int] = None, dtype: str = "bf16",
-              atten_mask=None, topk_mask=None) -> dict:
+              atten_mask=None, topk_mask=None, act_seq_kvlen=None) -> dict:
     """Steps 1-7 for the listed global tokens.
+
+    ``act_seq_kvlen`` (prefix sums, optional): chunked prefill -- each
+    sequence's queries are the last of its key/value tokens, so query t has
+    position Tkv - Tq + t in both causal rules, and the select blocks follow
+    the key/value tokens (``tokens`` still index the query rows).
 
     q_rows_bits: [n_tok, N1, D1] bits of those tokens' query rows; q, kc and
     vc are all of element type ``dtype``.  ``atten_mask`` / ``topk_mask``:
@@ -231,8 +236,9 @@ def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_k
         raise ValueError(f"q rows shape {q.shape} != {(n_tok, N1, D1)}")
     actq = _i64(act_seq_qlen)
     actc = _i64(act_cmp_seq_kvlen)
-    starts = np.concatenate([[0], actq[:-1]])
-    s_sel_max = int(max(-(-(int(e - s)) // lsel) for s, e in zip(starts, actq)))
+    actkv = actq if act_seq_kvlen is None else _i64(act_seq_kvlen)
+    starts = np.concatenate([[0], actkv[:-1]])
+    s_sel_max = int(max(-(-(int(e - s)) // lsel) for s, e in zip(starts, actkv)))
     if s_stride is None:
         s_stride = max(1, s_sel_max)
     out = np.empty((n_tok, N1, D2), dtype=np.float64)
@@ -252,7 +258,8 @@ def attention(q_rows_bits, tokens, kc_bits, vc_bits, act_seq_qlen, act_cmp_seq_k
     am, amp, amr, amc = mask_arg(atten_mask)
     tm, tmp, tmr, tmc = mask_arg(topk_mask)
     rc = _load().nsa_oracle_attention_masked(_ptr(q), _ptr(tok), n_tok, _ptr(kc), _ptr(vc),
-                                             _ptr(actq), _ptr(actc), len(actq),
+                                             _ptr(actq), None if act_seq_kvlen is None else _ptr(actkv),
+                                             _ptr(actc), len(actq),
                                              N1, N2, D1, D2, float(scale), l, d, lsel, count,
                                              _code(dtype), amp, amr, amc, tmp, tmr, tmc,
                                              _ptr(out), _ptr(smax), _ptr(ssum), _ptr(pslc),

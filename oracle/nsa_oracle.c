@@ -356,7 +356,8 @@ static void topk_one_group(const double* Pslc_g, int64_t S_sel, int64_t t, int64
  */
 int nsa_oracle_attention_masked(const uint16_t* q_rows, const int64_t* tokens, int64_t n_tok,
                                 const uint16_t* kc, const uint16_t* vc,
-                                const int64_t* act_seq_qlen, const int64_t* act_cmp_seq_kvlen,
+                                const int64_t* act_seq_qlen, const int64_t* act_seq_kvlen,
+                                const int64_t* act_cmp_seq_kvlen,
                                 int64_t B, int64_t N1, int64_t N2, int64_t D1, int64_t D2,
                                 double scale, int64_t l, int64_t d, int64_t lsel, int64_t count,
                                 int dtype, const uint8_t* atten_mask, int64_t am_rows,
@@ -373,7 +374,8 @@ int nsa_oracle_attention_masked(const uint16_t* q_rows, const int64_t* tokens, i
     int64_t n_cmp_max = 0, s_sel_max = 0;
     for (int64_t b = 0; b < B; ++b) {
         int64_t nc = act_cmp_seq_kvlen[b] - seq_start(act_cmp_seq_kvlen, b);
-        int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
+        int64_t T = act_seq_kvlen ? act_seq_kvlen[b] - seq_start(act_seq_kvlen, b)
+                                  : act_seq_qlen[b] - seq_start(act_seq_qlen, b);
         int64_t ss = (T + lsel - 1) / lsel;
         if (nc > n_cmp_max) n_cmp_max = nc;
         if (ss > s_sel_max) s_sel_max = ss;
@@ -409,15 +411,21 @@ int nsa_oracle_attention_masked(const uint16_t* q_rows, const int64_t* tokens, i
                 int64_t t = 0;
                 int64_t b = find_seq(act_seq_qlen, B, tokens[k], &t);
                 int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
+                /* chunked prefill: the queries are the last T of the sequence's
+                 * Tkv key/value tokens, so local query t sits at position
+                 * pos = Tkv - T + t for both causal rules (bottom-right
+                 * alignment); select blocks follow the key/value tokens */
+                int64_t Tkv = act_seq_kvlen ? act_seq_kvlen[b] - seq_start(act_seq_kvlen, b) : T;
+                int64_t pos = Tkv - T + t;
                 int64_t cmp0 = seq_start(act_cmp_seq_kvlen, b);
                 int64_t n_cmp = act_cmp_seq_kvlen[b] - cmp0;
-                int64_t S_sel = (T + lsel - 1) / lsel;
+                int64_t S_sel = (Tkv + lsel - 1) / lsel;
                 double* pslc_k = pslc + k * N2 * s_stride;
                 for (int64_t x = 0; x < N2 * s_stride; ++x)
                     pslc_k[x] = 0.0;
                 for (int64_t h = 0; h < N1; ++h) {
                     int64_t g = h / G;
-                    attend_one_head(q_rows + (k * N1 + h) * D1, kc, vc, cmp0, n_cmp, t, g,
+                    attend_one_head(q_rows + (k * N1 + h) * D1, kc, vc, cmp0, n_cmp, pos, g,
                                     N2, D1, D2, scale, l, d, dtype,
                                     atten_mask ? atten_mask + t * am_cols : NULL, s, P,
                                     out + (k * N1 + h) * D2,
@@ -428,7 +436,7 @@ int nsa_oracle_attention_masked(const uint16_t* q_rows, const int64_t* tokens, i
                         pslc_k[g * s_stride + j] += Ph[j];
                 }
                 for (int64_t g = 0; g < N2; ++g)
-                    topk_one_group(pslc_k + g * s_stride, S_sel, t, lsel, count,
+                    topk_one_group(pslc_k + g * s_stride, S_sel, pos, lsel, count,
                                    topk_mask ? topk_mask + t * tm_cols : NULL, taken,
                                    topk + (k * N2 + g) * count);
             }
@@ -450,7 +458,7 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
                          double* out, double* smax, double* ssum,
                          double* pslc, int64_t s_stride, int32_t* topk)
 {
-    return nsa_oracle_attention_masked(q_rows, tokens, n_tok, kc, vc, act_seq_qlen,
+    return nsa_oracle_attention_masked(q_rows, tokens, n_tok, kc, vc, act_seq_qlen, NULL,
                                        act_cmp_seq_kvlen, B, N1, N2, D1, D2, scale, l, d, lsel,
                                        count, dtype, NULL, 0, 0, NULL, 0, 0, out, smax, ssum,
                                        pslc, s_stride, topk);

@@ -247,3 +247,21 @@ def test_split_workspace_host_checks():
         assert sizes[-1] > sizes[0]
     finally:
         plan.destroy()
+
+
+def test_chunked_plan_host_checks():
+    """Chunked-prefill plans: fewer key/value than query tokens is a shape
+    error; the paths not built for them refuse before any launch."""
+    kw = dict(head_num=4, kv_head_num=1, d1=64, d2=64, scale_value=0.125, compress_block_size=32,
+              compress_stride=16, select_block_size=64, select_block_count=4)
+    c = [nsa.nsa_compress_out_len(300, 32, 16)]
+    s = [-(-300 // 64)]
+    with pytest.raises(ValueError):
+        nsa.nsa_compress_attention_get_workspace([301], c, s, actual_seq_kvlen=[300], **kw)
+    plan = nsa.nsa_compress_attention_get_workspace([100], c, s, actual_seq_kvlen=[300], **kw)
+    try:
+        assert plan.info["total_q_tokens"] == 100 and plan.info["total_cmp_tokens"] == c[0]
+        with pytest.raises(NotImplementedError):
+            nsa.nsa_compress_attention_split_workspace(plan, 4)
+    finally:
+        plan.destroy()

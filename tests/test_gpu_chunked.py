@@ -1,0 +1,96 @@
+"""Chunked prefill on the GPU (nsa_compress_attention_get_workspace_kv):
+each sequence's queries are the last Tq of its Tkv key/value tokens and
+both causal rules are aligned bottom-right.  Parity against the oracle's
+chunked mode (outputs, P_slc', top-k), on the oracle's compressed K/V, and
+against the GPU's own full-prefill rows (bit for bit: a row's work does not
+depend on which other rows share its workgroup)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (assert_close_out, assert_pslc, assert_softmax_stats, log, to_f64, upload_bits)
+
+import kv_compression_block_amd as nsa
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # N1, N2, D1, D2, l, d, lsel, count, scale, kv_lens, q_lens
+    "gqa-d64": (8, 2, 64, 64, 32, 16, 64, 4, 0.125, [700, 333, 64, 45], [150, 333, 10, 45]),
+    "group64-d128": (64, 1, 128, 128, 32, 16, 64, 16, 128 ** -0.5, [1500, 900], [300, 1]),
+    "long-stride": (16, 1, 192, 128, 64, 32, 128, 8, 192 ** -0.5, [2100], [700]),
+}
+
+
+def _bits(rng, shape, std=1.0):
+    return torch.from_numpy((rng.standard_normal(shape) * std).astype(np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def _plan(N1, N2, D1, D2, l, d, lsel, count, scale, kv_lens, q_lens):
+    c = np.cumsum([nsa.nsa_compress_out_len(T, l, d) for T in kv_lens]).tolist()
+    s = np.cumsum([-(-T // lsel) for T in kv_lens]).tolist()
+    kv = np.cumsum(kv_lens).tolist() if kv_lens is not None else None
+    return nsa.nsa_compress_attention_get_workspace(np.cumsum(q_lens).tolist(), c, s, N1, N2, D1, D2, scale,
+                                                    l, d, lsel, count, torch.bfloat16, actual_seq_kvlen=kv)
+
+
+def _topk_check(g_idx, r_idx, r_pslc, tie_rel=1e-4):
+    for k in range(g_idx.shape[0]):
+        for g in range(g_idx.shape[1]):
+            gi, ri = g_idx[k, g], r_idx[k, g]
+            kk = int((ri >= 0).sum())
+            assert np.all(gi[kk:] == -1) and np.all(gi[:kk] >= 0), (k, g, gi, ri)
+            assert len(set(gi[:kk].tolist())) == kk
+            if kk == 0:
+                continue
+            ref = set(ri[:kk].tolist())
+            sc = r_pslc[k, g].astype(np.float32).astype(np.float64)
+            kth = min(sc[j] for j in ref)
+            for pk in gi[:kk]:
+                assert pk in ref or sc[pk] >= kth * (1 - tie_rel), (k, g, pk)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_chunked_prefill(name):
+    N1, N2, D1, D2, l, d, lsel, count, scale, kv_lens, q_lens = CASES[name]
+    log(f"[case] chunked {name}: kv {kv_lens} q {q_lens}")
+    rng = np.random.default_rng(abs(hash(name)) % (2 ** 32))
+    k = _bits(rng, (sum(kv_lens), N2, D1))
+    v = _bits(rng, (sum(kv_lens), N2, D2))
+    w = _bits(rng, (l, N2), std=1.0 / l)
+    q_full = _bits(rng, (sum(kv_lens), N1, D1))
+    actkv = np.cumsum(kv_lens).astype(np.int64)
+    kc = oracle.round_to(oracle.compress(k, w, actkv, l, d))
+    vc = oracle.round_to(oracle.compress(v, w, actkv, l, d))
+    starts = np.concatenate([[0], actkv[:-1]])
+    rows = np.concatenate([s + np.arange(T - Tq, T) for s, T, Tq in zip(starts, kv_lens, q_lens)]).astype(np.int64)
+    q_chunk = np.ascontiguousarray(q_full[rows])
+    actc = oracle.cmp_prefix(kv_lens, l, d)
+    ref = oracle.attention(q_chunk, np.arange(sum(q_lens), dtype=np.int64), kc, vc, np.cumsum(q_lens), actc,
+                           N1, N2, scale, l, d, lsel, count, act_seq_kvlen=actkv)
+    kc_g, vc_g = upload_bits(kc), upload_bits(vc)
+    plan = _plan(N1, N2, D1, D2, l, d, lsel, count, scale, kv_lens, q_lens)
+    try:
+        out, topk, mx, sm, pslc = nsa.nsa_compress_attention(plan, upload_bits(q_chunk), kc_g, vc_g,
+                                                             return_p_slc=True)
+        torch.cuda.synchronize()
+    finally:
+        plan.destroy()
+    assert_close_out(to_f64(out), ref["out"], "attention_out")
+    assert_softmax_stats(mx.cpu().numpy(), sm.cpu().numpy(), ref["max"], ref["sum"])
+    assert_pslc(pslc.cpu().numpy(), ref["pslc"])
+    _topk_check(topk.cpu().numpy(), ref["topk"], ref["pslc"])
+    # the same rows of the full prefill, computed by the GPU
+    plan = _plan(N1, N2, D1, D2, l, d, lsel, count, scale, kv_lens, kv_lens)
+    try:
+        f_out, f_topk, f_mx, f_sm, f_pslc = nsa.nsa_compress_attention(plan, upload_bits(q_full), kc_g, vc_g,
+                                                                       return_p_slc=True)
+        torch.cuda.synchronize()
+    finally:
+        plan.destroy()
+    r = torch.from_numpy(rows).cuda()
+    assert torch.equal(out, f_out[r]) and torch.equal(mx, f_mx[r]) and torch.equal(sm, f_sm[r])
+    assert torch.equal(topk, f_topk[r])
+    assert torch.equal(pslc, f_pslc[r][..., :pslc.shape[-1]])

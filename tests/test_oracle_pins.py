@@ -1016,3 +1016,43 @@ def test_attention_backward_finite_differences():
         minus[which] = base[which] - eps * direction
         fd = (f(*plus) - f(*minus)) / (2 * eps)
         assert abs(fd - float((g[key] * direction).sum())) <= 1e-6 * max(1.0, abs(fd)), key
+
+
+def test_chunked_prefill_rows_equal_full_prefill_rows():
+    """Chunked prefill (queries = the last Tq of Tkv key/value tokens, both
+    causal rules aligned bottom-right) is the full prefill restricted to
+    those rows: every output of a chunked query equals, bit for bit, the
+    full-sequence output of the token at the same position.  And Tkv = Tq
+    is the plain call."""
+    rng = np.random.default_rng(2024)
+    N1, N2, D1, D2, l, d, lsel, count, scale = 4, 2, 32, 32, 32, 16, 64, 4, 0.2
+    kv_lens = [300, 181]
+    q_lens = [77, 181]          # a chunk at the end of the first sequence, all of the second
+    kc_all, vc_all, q_full = [], [], []
+    for T in kv_lens:
+        k = rand_bf16(rng, (T, N2, D1))
+        v = rand_bf16(rng, (T, N2, D2))
+        w = rand_bf16(rng, (l, N2), std=0.05)
+        kc_all.append(oracle.round_to(oracle.compress(k, w, np.array([T]), l, d)))
+        vc_all.append(oracle.round_to(oracle.compress(v, w, np.array([T]), l, d)))
+        q_full.append(rand_bf16(rng, (T, N1, D1)))
+    kc = np.concatenate(kc_all)
+    vc = np.concatenate(vc_all)
+    actc = oracle.cmp_prefix(kv_lens, l, d)
+    full = oracle.attention(np.concatenate(q_full), np.arange(sum(kv_lens), dtype=np.int64), kc, vc,
+                            np.cumsum(kv_lens), actc, N1, N2, scale, l, d, lsel, count)
+    q_chunk = np.concatenate([qf[T - Tq:] for qf, T, Tq in zip(q_full, kv_lens, q_lens)])
+    chunk = oracle.attention(q_chunk, np.arange(sum(q_lens), dtype=np.int64), kc, vc, np.cumsum(q_lens),
+                             actc, N1, N2, scale, l, d, lsel, count, act_seq_kvlen=np.cumsum(kv_lens))
+    rows = np.concatenate([s + np.arange(T - Tq, T) for s, T, Tq in zip(starts_of(kv_lens), kv_lens, q_lens)])
+    for key in ("out", "max", "sum", "pslc", "topk"):
+        assert np.array_equal(chunk[key], full[key][rows], equal_nan=True), key
+    # the first chunk row of sequence 0 (position 223) sees blocks that a
+    # top-left alignment (position 0) would not: the alignment matters
+    assert np.isfinite(chunk["max"][0]).all()
+    same = oracle.attention(q_chunk, np.arange(sum(q_lens), dtype=np.int64), kc, vc, np.cumsum(q_lens),
+                            actc, N1, N2, scale, l, d, lsel, count, act_seq_kvlen=np.cumsum(q_lens))
+    plain = oracle.attention(q_chunk, np.arange(sum(q_lens), dtype=np.int64), kc, vc, np.cumsum(q_lens),
+                             actc, N1, N2, scale, l, d, lsel, count)
+    for key in ("out", "max", "sum", "pslc", "topk"):
+        assert np.array_equal(same[key], plain[key], equal_nan=True), key

@@ -3,9 +3,19 @@
 * small workloads (all tokens), the five workloads' head/dim/parameter
   settings with shorter, ragged sequences: compression, then attention,
   softmax statistics, importance scores and top-k -- staged (the GPU's
-  attention consumes the oracle's compressed K/V) and end to end;
+  attention consumes the oracle's compressed K/V) and end to end (the GPU's
+  attention consumes its own compression, and the oracle is fed those same
+  bits), both at the stated bounds;
+* all tokens of shapes whose long sequences enter the attention kernel's
+  unrolled three-slot loop (a workgroup whose first token sees at least
+  four whole key tiles of 32 compressed entries: token >= 2063 for
+  l = 32, d = 16 and >= 4127 for l = 64, d = 32): the MQA workload at full
+  size, and the GQA-16, long-stride and group-64 settings with a sequence
+  past that point;
 * the five workloads at full size, in the launch configuration the
-  benchmark times: compression in full, attention on sampled tokens;
+  benchmark times: compression in full, attention on whole workgroups (the
+  first, a middle and the last 64-token run of every sequence) and on
+  sampled tokens;
 * edge cases: empty and short sequences, negative and zero scale, groups
   that are not powers of two, MHA, other remap stencils, count 1;
 * bitwise determinism across runs;
@@ -22,7 +32,7 @@ import torch
 import oracle
 import synth
 from parity import (assert_close_out, assert_pslc, assert_softmax_stats, assert_topk,
-                    gpu_attention, gpu_compress, log, to_f64, token_meta, upload_bits)
+                    gpu_attention, gpu_compress, log, to_f64, token_meta, upload_bits, workgroup_runs)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,19 +44,32 @@ SMALL = {
     4: synth.small_variant(4, [2000, 1500, 300]),
 }
 
+# Shapes whose longest sequence enters the unrolled loop of the attention
+# kernel, compared on every token.
+LOOP = {
+    "mqa-full": synth.WORKLOADS[1],
+    "gqa16-d128": synth.small_variant(2, [4500, 700]),
+    "long-l64-d32": synth.small_variant(3, [5200]),
+    "group64-d128": synth.small_variant(4, [4200, 300]),
+}
 
-def _check_all(wl, g, ref, tokens, staged=True):
-    """g: GPU outputs whose rows are the given tokens, in order."""
+
+def _check_all(wl, g, ref, tokens):
+    """g: GPU outputs whose rows are the given tokens, in order; ref: the
+    oracle on the compressed K/V the GPU consumed."""
     assert_close_out(to_f64(g["out"]), ref["out"], "attention_out")
-    gmax, gsum = g["max"].cpu().numpy(), g["sum"].cpu().numpy()
-    if staged:
-        assert_softmax_stats(gmax, gsum, ref["max"], ref["sum"])
-        assert_pslc(g["pslc"].cpu().numpy(), ref["pslc"])
-        assert_topk(wl, tokens, g["topk"].cpu().numpy(), ref["topk"], ref["pslc"], tie_rel=1e-4)
-    else:
-        assert_softmax_stats(gmax, gsum, ref["max"], ref["sum"], max_atol=1e-2, sum_rtol=1e-2)
-        assert_pslc(g["pslc"].cpu().numpy(), ref["pslc"], rtol=1e-2)
-        assert_topk(wl, tokens, g["topk"].cpu().numpy(), ref["topk"], ref["pslc"], tie_rel=1e-2)
+    assert_softmax_stats(g["max"].cpu().numpy(), g["sum"].cpu().numpy(), ref["max"], ref["sum"])
+    assert_pslc(g["pslc"].cpu().numpy(), ref["pslc"])
+    assert_topk(wl, tokens, g["topk"].cpu().numpy(), ref["topk"], ref["pslc"])
+
+
+def _oracle_attention(wl, q_bits, kc_bits, vc_bits, tokens=None):
+    """Steps 1-7 of the oracle on the given compressed K/V bit patterns."""
+    if tokens is None:
+        tokens = np.arange(wl.T, dtype=np.int64)
+    return oracle.attention(q_bits, tokens, kc_bits, vc_bits, np.asarray(wl.act_seq_qlen, dtype=np.int64),
+                            oracle.cmp_prefix(wl.seqlens, wl.l, wl.d), wl.N1, wl.N2, wl.scale, wl.l, wl.d,
+                            wl.lsel, wl.count, dtype=wl.dtype)
 
 
 def _run_small(wl, end_to_end=True):
@@ -66,9 +89,10 @@ def _run_small(wl, end_to_end=True):
                       upload_bits(ref["vc_bits"], wl.dtype))
     _check_all(wl, g, ref, ref["tokens"])
     if end_to_end:
-        log(f"[case] {wl.name}: GPU attention on its own compressed K/V")
+        log(f"[case] {wl.name}: GPU attention on its own compressed K/V, oracle on the same bits")
+        ref2 = _oracle_attention(wl, bits["q"], synth.bits(kc_g), synth.bits(vc_g))
         g2 = gpu_attention(wl, inp["q"], kc_g, vc_g)
-        _check_all(wl, g2, ref, ref["tokens"], staged=False)
+        _check_all(wl, g2, ref2, ref["tokens"])
     return inp, g
 
 
@@ -79,6 +103,15 @@ DTYPES = ["bf16", "f16"]
 @pytest.mark.parametrize("wid", [0, 1, 2, 3, 4])
 def test_small_workloads_all_tokens(wid, dtype):
     _run_small(SMALL[wid].with_dtype(dtype))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("name", sorted(LOOP))
+def test_loop_shapes_all_tokens(name, dtype):
+    wl = LOOP[name].with_dtype(dtype)
+    first = {32: 2063, 64: 4127}[wl.l]
+    assert max(wl.seqlens) > first + 64, "the case must reach the unrolled loop"
+    _run_small(wl)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -98,19 +131,22 @@ def test_full_size_workloads_sampled(wid, dtype):
     torch.cuda.synchronize()
     assert_close_out(to_f64(kc_g), kc_ref, "compressed K")
     assert_close_out(to_f64(vc_g), vc_ref, "compressed V")
-    del kc_g, vc_g
+    kc_gb, vc_gb = synth.bits(kc_g), synth.bits(vc_g)
     kc_b, vc_b = oracle.round_to(kc_ref, dtype), oracle.round_to(vc_ref, dtype)
-    tokens = synth.sample_tokens(wl, per_seq=6)
-    log(f"[case] full {wl.name}: oracle attention on {len(tokens)} tokens")
-    q_rows = synth.bits(inp["q"][torch.from_numpy(tokens).cuda()])
-    ref = oracle.attention(q_rows, tokens, kc_b, vc_b, actq, oracle.cmp_prefix(wl.seqlens, wl.l, wl.d),
-                           wl.N1, wl.N2, wl.scale, wl.l, wl.d, wl.lsel, wl.count, dtype=dtype)
-    log(f"[case] full {wl.name}: GPU attention (all tokens)")
-    g = gpu_attention(wl, inp["q"], upload_bits(kc_b, dtype), upload_bits(vc_b, dtype))
+    tokens = np.union1d(workgroup_runs(wl), synth.sample_tokens(wl, per_seq=6))
     tok_t = torch.from_numpy(tokens).cuda()
-    gs = {"out": g["out"][tok_t], "max": g["max"][tok_t], "sum": g["sum"][tok_t],
-          "pslc": g["pslc"][tok_t], "topk": g["topk"][tok_t]}
-    _check_all(wl, gs, ref, tokens)
+    q_rows = synth.bits(inp["q"][tok_t])
+    for leg, kcb, vcb, kcd, vcd in (("oracle's", kc_b, vc_b, None, None), ("GPU's own", kc_gb, vc_gb, kc_g, vc_g)):
+        log(f"[case] full {wl.name}: oracle attention on {len(tokens)} tokens, {leg} compressed K/V")
+        ref = _oracle_attention(wl, q_rows, kcb, vcb, tokens)
+        log(f"[case] full {wl.name}: GPU attention (all tokens) on the {leg} compressed K/V")
+        if kcd is None:
+            kcd, vcd = upload_bits(kcb, dtype), upload_bits(vcb, dtype)
+        g = gpu_attention(wl, inp["q"], kcd, vcd)
+        gs = {"out": g["out"][tok_t], "max": g["max"][tok_t], "sum": g["sum"][tok_t],
+              "pslc": g["pslc"][tok_t], "topk": g["topk"][tok_t]}
+        _check_all(wl, gs, ref, tokens)
+    del kc_g, vc_g
     # Properties that hold for every row of the full output.
     log(f"[case] full {wl.name}: whole-output properties")
     assert torch.isfinite(g["out"].float()).all()

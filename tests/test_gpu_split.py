@@ -88,3 +88,39 @@ def test_split_full_size_sampled(wid, tiles):
     _check((out[tok_t], mx[tok_t], sm[tok_t]), ref)
     assert torch.isfinite(out.float()).all()
     assert bool(((sm[..., 0] > 0) == torch.isfinite(mx[..., 0])).all())
+
+
+def test_single_pass_matches_split_on_every_token():
+    """The batched workload's longest and shortest sequences at full size:
+    the single-pass launch (whose unrolled three-slot loop does most of the
+    work there) against the split launch with 3 key tiles per piece (which
+    never enters that loop), on every row.  Both consume the same compressed
+    K/V and compute every score with the same MFMA sequence, so the softmax
+    max agrees bit for bit; the sums and outputs differ only in summation
+    order."""
+    base = synth.WORKLOADS[4]
+    lens = (max(base.seqlens), min(base.seqlens))
+    wl = base.with_seqlens(lens, name=f"{base.name}@lens{list(lens)}")
+    log(f"[case] {wl.name}: single pass against split (3 tiles per piece), all tokens")
+    inp = synth.make_inputs(wl, device="cuda")
+    kc = nsa.nsa_compress(inp["k"], inp["w"], wl.act_seq_qlen, wl.l, wl.d)
+    vc = nsa.nsa_compress(inp["v"], inp["w"], wl.act_seq_qlen, wl.l, wl.d)
+    plan = _plan(wl)
+    try:
+        out1, mx1, sm1 = nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc)
+        torch.cuda.synchronize()
+    finally:
+        plan.destroy()
+    out2, mx2, sm2 = _split(wl, inp["q"], kc, vc, 3)
+    assert torch.equal(mx1, mx2), "softmax_max differs between the launches"
+    fin = sm1 > 0
+    assert torch.equal(fin, sm2 > 0)
+    rel = ((sm1 - sm2).abs() / sm1.clamp_min(1e-30))[fin]
+    log(f"  softmax sum: max rel diff {float(rel.max()):.3e}")
+    assert float(rel.max()) <= 1e-5
+    a, b = out1.double(), out2.double()
+    d = (a - b).abs()
+    log(f"  attention_out: max |diff| {float(d.max()):.3e}")
+    assert bool((d <= 2e-2 + 1e-2 * b.abs()).all())
+    # both round the same fp32 sums to bfloat16: at most a few ulps apart
+    assert bool((d <= 4.0 * 2.0 ** -8 * b.abs() + 1e-5).all())

@@ -58,6 +58,17 @@ def _stream_ptr(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _empty(shape, dtype: torch.dtype, device: torch.device, stream) -> torch.Tensor:
+    """A tensor the binding allocates for a call on ``stream``.  The caching
+    allocator ties a block to the stream current at allocation; when the
+    kernels run on another stream the block is recorded on it too, so it is
+    not handed out again while they may still use it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+    return t
+
+
 def _prefix(arr, name: str) -> "ctypes.Array":
     if isinstance(arr, torch.Tensor):
         arr = arr.tolist()
@@ -114,7 +125,7 @@ def nsa_compress(input: torch.Tensor, weight: torch.Tensor, act_seq_len: Sequenc
         prev = int(x)
         T2 += max(0, int(n))
     if out is None:
-        out = torch.empty((T2, N, D), dtype=input.dtype, device=input.device)
+        out = _empty((T2, N, D), input.dtype, input.device, stream)
     else:
         _need_tensor(out, "out")
     st = _lib.load().nsa_compress(_ptr(input), _ptr(weight), pre, B, T, N, D, l, dd,
@@ -212,10 +223,10 @@ def _check_qkv(plan: Plan, query, key, value=None):
             raise TypeError("query and value must share a dtype")
 
 
-def _workspace(plan: Plan, workspace, dev, masked: bool = False):
+def _workspace(plan: Plan, workspace, dev, stream, masked: bool = False):
     need = plan.info["masked_workspace_bytes"] if masked else plan.workspace_bytes
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        workspace = _empty((max(need, 1),), torch.uint8, dev, stream)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -241,22 +252,22 @@ def _masks(atten_mask, topk_mask):
     return m, tuple(keep)
 
 
-def _alloc_outputs(plan: Plan, query, outputs, want_pslc: bool):
+def _alloc_outputs(plan: Plan, query, outputs, want_pslc: bool, stream=None):
     info = plan.info
     T1, N1, N2, D2 = info["total_q_tokens"], info["head_num"], info["kv_head_num"], info["d2"]
     cnt, S = info["select_block_count"], info["max_sel_blocks"]
     dev = query.device
     o = dict(outputs or {})
     if o.get("attention_out") is None:
-        o["attention_out"] = torch.empty((T1, N1, D2), dtype=query.dtype, device=dev)
+        o["attention_out"] = _empty((T1, N1, D2), query.dtype, dev, stream)
     if o.get("topk_indices") is None:
-        o["topk_indices"] = torch.empty((T1, N2, cnt), dtype=torch.int32, device=dev)
+        o["topk_indices"] = _empty((T1, N2, cnt), torch.int32, dev, stream)
     if o.get("softmax_max") is None:
-        o["softmax_max"] = torch.empty((T1, N1, 8), dtype=torch.float32, device=dev)
+        o["softmax_max"] = _empty((T1, N1, 8), torch.float32, dev, stream)
     if o.get("softmax_sum") is None:
-        o["softmax_sum"] = torch.empty((T1, N1, 8), dtype=torch.float32, device=dev)
+        o["softmax_sum"] = _empty((T1, N1, 8), torch.float32, dev, stream)
     if want_pslc and o.get("p_slc") is None:
-        o["p_slc"] = torch.empty((T1, N2, max(S, 1)), dtype=torch.float32, device=dev)
+        o["p_slc"] = _empty((T1, N2, max(S, 1)), torch.float32, dev, stream)
     return o
 
 
@@ -268,9 +279,9 @@ def nsa_compress_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, v
     softmax_sum) and, with ``return_p_slc``, the importance scores
     [T1, N2, S] as a fifth element."""
     _check_qkv(plan, query, key, value)
-    o = _alloc_outputs(plan, query, outputs, return_p_slc)
+    o = _alloc_outputs(plan, query, outputs, return_p_slc, stream)
     m, _keep = _masks(atten_mask, topk_mask)
-    ws, ws_bytes = _workspace(plan, workspace, query.device, m is not None)
+    ws, ws_bytes = _workspace(plan, workspace, query.device, stream, m is not None)
     lib = _lib.load()
     args = (_ptr(o["attention_out"]), _ptr(o["topk_indices"]), _ptr(o["softmax_max"]),
             _ptr(o["softmax_sum"]), _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws),
@@ -290,9 +301,9 @@ def nsa_compress_attention_fwd(plan: Plan, query: torch.Tensor, key: torch.Tenso
                                stream=None, atten_mask=None):
     """Steps 1-3 only: returns (attention_out, softmax_max, softmax_sum)."""
     _check_qkv(plan, query, key, value)
-    o = _alloc_outputs(plan, query, outputs, False)
+    o = _alloc_outputs(plan, query, outputs, False, stream)
     m, _keep = _masks(atten_mask, None)
-    ws, ws_bytes = _workspace(plan, workspace, query.device, m is not None)
+    ws, ws_bytes = _workspace(plan, workspace, query.device, stream, m is not None)
     lib = _lib.load()
     args = (_ptr(o["attention_out"]), _ptr(o["softmax_max"]), _ptr(o["softmax_sum"]), _ptr(ws),
             ws_bytes, _stream_ptr(query.device, stream))
@@ -320,10 +331,10 @@ def nsa_compress_attention_fwd_split(plan: Plan, query: torch.Tensor, key: torch
     at most ``key_tiles_per_piece`` tiles of 32 compressed blocks, merged by
     a second kernel: returns (attention_out, softmax_max, softmax_sum)."""
     _check_qkv(plan, query, key, value)
-    o = _alloc_outputs(plan, query, outputs, False)
+    o = _alloc_outputs(plan, query, outputs, False, stream)
     need = nsa_compress_attention_split_workspace(plan, key_tiles_per_piece)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=query.device)
+        workspace = _empty((max(need, 1),), torch.uint8, query.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = _lib.load().nsa_compress_attention_fwd_split(
         plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(o["attention_out"]), _ptr(o["softmax_max"]),
@@ -346,9 +357,9 @@ def nsa_compress_attention_select(plan: Plan, query: torch.Tensor, key: torch.Te
         _need_tensor(t, name)
         if t.dtype != torch.float32 or tuple(t.shape) != (plan.info["total_q_tokens"], plan.info["head_num"], 8):
             raise ValueError(f"{name} must be float32 [T1, N1, 8]")
-    o = _alloc_outputs(plan, query, outputs, return_p_slc)
+    o = _alloc_outputs(plan, query, outputs, return_p_slc, stream)
     m, _keep = _masks(atten_mask, topk_mask)
-    ws, ws_bytes = _workspace(plan, workspace, query.device, m is not None)
+    ws, ws_bytes = _workspace(plan, workspace, query.device, stream, m is not None)
     lib = _lib.load()
     args = (_ptr(softmax_max), _ptr(softmax_sum), _ptr(o["topk_indices"]),
             _ptr(o.get("p_slc") if return_p_slc else None), _ptr(ws), ws_bytes,
@@ -409,10 +420,10 @@ def nsa_select_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, val
         raise ValueError(f"topk_indices must be int32 {(T1, N2, info['select_block_count'])}")
     o = dict(outputs or {})
     if o.get("attention_out") is None:
-        o["attention_out"] = torch.empty((T1, N1, D2), dtype=query.dtype, device=query.device)
+        o["attention_out"] = _empty((T1, N1, D2), query.dtype, query.device, stream)
     if o.get("softmax_lse") is None:
-        o["softmax_lse"] = torch.empty((T1, N1), dtype=torch.float32, device=query.device)
-    ws, ws_bytes = _workspace(plan, workspace, query.device)
+        o["softmax_lse"] = _empty((T1, N1), torch.float32, query.device, stream)
+    ws, ws_bytes = _workspace(plan, workspace, query.device, stream)
     st = _lib.load().nsa_select_attention(plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(topk_indices),
                                           _ptr(o["attention_out"]), _ptr(o["softmax_lse"]), _ptr(ws), ws_bytes,
                                           _stream_ptr(query.device, stream))
@@ -439,12 +450,12 @@ def nsa_compress_attention_backward(plan: Plan, query, key, value, attention_out
         if t.dtype != torch.float32 or tuple(t.shape) != (T1, N1, 8):
             raise ValueError(f"{name} must be float32 [T1, N1, 8]")
     dev = query.device
-    dq = torch.empty((T1, N1, D1), dtype=torch.float32, device=dev)
-    dk = torch.empty((T2, N2, D1), dtype=torch.float32, device=dev)
-    dv = torch.empty((T2, N2, D2), dtype=torch.float32, device=dev)
+    dq = _empty((T1, N1, D1), torch.float32, dev, stream)
+    dk = _empty((T2, N2, D1), torch.float32, dev, stream)
+    dv = _empty((T2, N2, D2), torch.float32, dev, stream)
     need = info["backward_workspace_bytes"]
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+        workspace = _empty((max(need, 1),), torch.uint8, dev, stream)
     st = _lib.load().nsa_compress_attention_backward(
         plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(attention_out), _ptr(d_attention_out),
         _ptr(softmax_max), _ptr(softmax_sum), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
@@ -468,8 +479,8 @@ def nsa_compress_backward(input: torch.Tensor, weight: torch.Tensor, d_output: t
     T, N, D = input.shape
     l, dd = int(compress_block_size), int(compress_stride)
     pre, B = _prefix(act_seq_len, "act_seq_len")
-    dx = torch.empty((T, N, D), dtype=torch.float32, device=input.device)
-    dw = torch.empty((l, N), dtype=torch.float32, device=input.device)
+    dx = _empty((T, N, D), torch.float32, input.device, stream)
+    dw = _empty((l, N), torch.float32, input.device, stream)
     st = _lib.load().nsa_compress_backward(_ptr(input), _ptr(weight), _ptr(d_output), pre, B, T, N, D, l, dd,
                                            _dtype_code(input.dtype), d_output.shape[0], _ptr(dx), _ptr(dw),
                                            _stream_ptr(input.device, stream))

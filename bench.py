@@ -10,9 +10,14 @@ launch stream between the four calls give each kernel's duration inside the
 same timed region.
 
 Prints one JSON line.  ``value`` is query tokens per second of the whole
-step; the roofline object is for the dominant kernel (the attention
-kernel, bound by MFMA of the element type); ``cpu_baseline`` times the CPU
-oracle on a bounded random sample of the same workload's tokens.
+step on the batched workload (16 sequences of 8k-32k tokens, 64 query heads
+on one KV head); the roofline object is for the dominant kernel (the
+attention kernel, bound by MFMA of the element type); ``cpu_baseline`` times
+the CPU oracle on the same workload (a seeded sample of its tokens).  Without
+``--workload`` the line also carries ``configs``: the same measurement for
+every workload (tiny, MQA, GQA varlen, long context, batched), each with its
+kernels' fractions of the MFMA and HBM peaks and the oracle timed beside it
+(in full where that takes at most --cpu-full-seconds, else sampled).
 
     python bench.py [--steps K] [--warmup W] [--workload 0..4] [--dtype bf16|f16]
                     [--masks] [--no-cpu-baseline]
@@ -109,22 +114,35 @@ def workload_work(wl, T2: int) -> dict:
             "bytes_attn": bytes_attn, "bytes_select": bytes_sel}
 
 
-def cpu_baseline(wl, inp, budget_s: float) -> dict:
-    """The oracle, as it is, on this host: full compression of K and V plus
-    attention/remap/top-k on a seeded uniform sample of tokens, scaled to the
-    whole workload's token count."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inp, budget_s: float, full_limit_s: float = 60.0) -> dict:
+    """The oracle, as it is, on this host's cores: compression of all of K
+    and V, then attention/remap/top-k for every token when a pilot run says
+    that takes at most ``full_limit_s``, else for a seeded uniform sample of
+    tokens sized to ``budget_s`` and scaled to the whole workload."""
     import oracle
     import synth
+    import torch
     dt = wl.dtype
     kb, vb, wb = synth.bits(inp["k"]), synth.bits(inp["v"]), synth.bits(inp["w"])
     actq = np.asarray(wl.act_seq_qlen, dtype=np.int64)
+    oracle.stage_reset()
     t0 = time.perf_counter()
     kc = oracle.round_to(oracle.compress(kb, wb, actq, wl.l, wl.d, dt), dt)
     vc = oracle.round_to(oracle.compress(vb, wb, actq, wl.l, wl.d, dt), dt)
     t_comp = time.perf_counter() - t0
     actc = oracle.cmp_prefix(wl.seqlens, wl.l, wl.d)
     rng = np.random.default_rng(1234)
-    import torch
 
     def attn(tokens):
         q_rows = synth.bits(inp["q"][torch.from_numpy(tokens).to(inp["q"].device)])
@@ -135,14 +153,33 @@ def cpu_baseline(wl, inp, budget_s: float) -> dict:
 
     pilot = np.sort(rng.choice(wl.T, min(wl.T, 32), replace=False)).astype(np.int64)
     t_pilot = attn(pilot)
-    n = int(min(wl.T, max(32, len(pilot) * max(0.0, budget_s - t_comp) / max(t_pilot, 1e-6))))
-    sample = np.sort(rng.choice(wl.T, n, replace=False)).astype(np.int64)
+    est_full = t_pilot * wl.T / len(pilot)
+    oracle.stage_reset()
+    if est_full <= full_limit_s:
+        n = wl.T
+        sample = np.arange(wl.T, dtype=np.int64)
+    else:
+        n = int(min(wl.T, max(32, len(pilot) * max(1.0, budget_s - t_comp) / max(t_pilot, 1e-6))))
+        sample = np.sort(rng.choice(wl.T, n, replace=False)).astype(np.int64)
     t_att = attn(sample)
+    stages = oracle.stage_seconds()
     est = t_comp + t_att * wl.T / n
+    if n == wl.T:
+        what = (f"full run: compression of all K/V ({t_comp:.2f} s) + attention/remap/top-k for all "
+                f"{wl.T} tokens ({t_att:.2f} s)")
+    else:
+        what = (f"compression of all K/V ({t_comp:.2f} s) + attention/remap/top-k for {n} of {wl.T} "
+                f"tokens drawn uniformly ({t_att:.2f} s), scaled to all tokens (a full run would take "
+                f"about {t_att * wl.T / n:.0f} s)")
+    scale_att = wl.T / n
     return {"value": wl.T / est, "unit": "query tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": (f"compression of all K/V ({t_comp:.2f} s) + attention/remap/top-k for {n} of "
-                       f"{wl.T} tokens drawn uniformly ({t_att:.2f} s), scaled to all tokens"),
-            "seconds_measured": round(t_comp + t_att, 3)}
+            "sample": what, "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "seconds_measured": round(t_comp + t_att, 3),
+            "stage_seconds_whole_workload": {
+                "compress (wall)": round(t_comp, 3),
+                **{k + " (thread-s / threads)": round(v * scale_att / max(1, oracle.threads()), 3)
+                   for k, v in stages.items() if k != "compress"}},
+            "precision": "float64 on the exactly widened element-type inputs"}
 
 
 def selected_pairs(wl, topk) -> int:
@@ -298,12 +335,136 @@ def select_cpu_baseline(wl, inp, topk, budget_s: float) -> dict:
             "seconds_measured": round(tp + ts, 3)}
 
 
+class Path:
+    """Inputs, plan, outputs and workspace of one workload, resident on the GPU."""
+
+    def __init__(self, args, wl, dev, masks_on: bool = False, split_tiles: int = 0):
+        import torch
+        import synth
+        import kv_compression_block_amd as nsa
+        self.wl, self.dev, self.split_tiles = wl, dev, split_tiles
+        print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+        self.inp = synth.make_inputs(wl, device=dev, chunk_rows=16384)
+        c_pre, s_pre, pc, ps = [], [], 0, 0
+        for T in wl.seqlens:
+            pc += nsa.nsa_compress_out_len(T, wl.l, wl.d)
+            ps += -(-T // wl.lsel)
+            c_pre.append(pc)
+            s_pre.append(ps)
+        self.T2 = pc
+        self.plan = nsa.nsa_compress_attention_get_workspace(wl.act_seq_qlen, c_pre, s_pre, wl.N1, wl.N2,
+                                                             wl.D1, wl.D2, wl.scale, wl.l, wl.d, wl.lsel,
+                                                             wl.count, wl.torch_dtype)
+        self.kc = torch.empty((pc, wl.N2, wl.D1), dtype=wl.torch_dtype, device=dev)
+        self.vc = torch.empty((pc, wl.N2, wl.D2), dtype=wl.torch_dtype, device=dev)
+        self.outs = {"attention_out": torch.empty((wl.T, wl.N1, wl.D2), dtype=wl.torch_dtype, device=dev),
+                     "topk_indices": torch.empty((wl.T, wl.N2, wl.count), dtype=torch.int32, device=dev),
+                     "softmax_max": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev),
+                     "softmax_sum": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev)}
+        self.masks = {}
+        if masks_on:
+            # The positional rules spelled out as masks (True = masked out), one
+            # matrix for all sequences: rows = local query positions.
+            t_max = max(wl.seqlens)
+            t = torch.arange(t_max, device=dev)[:, None]
+            ncm = max(nsa.nsa_compress_out_len(T, wl.l, wl.d) for T in wl.seqlens)
+            self.masks["atten_mask"] = (torch.arange(ncm, device=dev)[None, :] * wl.d + wl.l - 1) > t
+            self.masks["topk_mask"] = (torch.arange(max(-(-T // wl.lsel) for T in wl.seqlens),
+                                                    device=dev)[None, :] * wl.lsel) > t
+        ws_bytes = self.plan.info["masked_workspace_bytes"] if masks_on else self.plan.workspace_bytes
+        if split_tiles:
+            ws_bytes = max(ws_bytes, nsa.nsa_compress_attention_split_workspace(self.plan, split_tiles))
+        self.ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def step(self, ev=None):
+        """One pass of the hot path; events (if given) bracket each call."""
+        import kv_compression_block_amd as nsa
+        wl, inp, stream, outs = self.wl, self.inp, self.stream, self.outs
+        if ev is not None:
+            ev[0].record(stream)
+        nsa.nsa_compress(inp["k"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=self.kc, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        nsa.nsa_compress(inp["v"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=self.vc, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        if self.split_tiles:
+            nsa.nsa_compress_attention_fwd_split(self.plan, inp["q"], self.kc, self.vc, self.split_tiles,
+                                                 workspace=self.ws, outputs=outs, stream=stream)
+        else:
+            nsa.nsa_compress_attention_fwd(self.plan, inp["q"], self.kc, self.vc, workspace=self.ws, outputs=outs,
+                                           stream=stream, atten_mask=self.masks.get("atten_mask"))
+        if ev is not None:
+            ev[3].record(stream)
+        nsa.nsa_compress_attention_select(self.plan, inp["q"], self.kc, outs["softmax_max"], outs["softmax_sum"],
+                                          workspace=self.ws, outputs=outs, stream=stream,
+                                          atten_mask=self.masks.get("atten_mask"),
+                                          topk_mask=self.masks.get("topk_mask"))
+        if ev is not None:
+            ev[4].record(stream)
+
+    def time_steps(self, steps: int, warmup: int) -> dict:
+        """W untimed steps, then K timed steps between synchronisations; HIP
+        events on the launch stream give each call's duration."""
+        import torch
+        wl = self.wl
+        print(f"[bench] {wl.name}: warmup {warmup} steps", file=sys.stderr, flush=True)
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        print(f"[bench] {wl.name}: timing {steps} steps", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(events[i])
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / steps
+        names = ["compress_k", "compress_v", "attention", "select_topk"]
+        per = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)]))
+               for j, n in enumerate(names)}
+        work = workload_work(wl, self.T2)
+        peak = PEAK_MFMA_TFLOPS[wl.dtype]
+        attn_tflops = work["attn_flops"] / (per["attention"] / 1e3) / 1e12
+        # attainable attention rate on the roofline: min(MFMA peak, intensity x HBM peak)
+        ai = work["attn_flops"] / work["bytes_attn"]
+        attainable = min(peak, ai * PEAK_HBM_GBS / 1e3)
+        recompute = 2.0 * wl.D1 * work["visible_pairs"] * wl.N1
+
+        def gbs(b, ms):
+            return b / (ms / 1e3) / 1e9
+
+        kernels = {
+            "compress_k": {"ms": per["compress_k"], "GB/s": gbs(work["bytes_compress_k"], per["compress_k"]),
+                           "frac_of_hbm_peak": gbs(work["bytes_compress_k"], per["compress_k"]) / PEAK_HBM_GBS},
+            "compress_v": {"ms": per["compress_v"], "GB/s": gbs(work["bytes_compress_v"], per["compress_v"]),
+                           "frac_of_hbm_peak": gbs(work["bytes_compress_v"], per["compress_v"]) / PEAK_HBM_GBS},
+            "attention": {"ms": per["attention"], "TFLOP/s": attn_tflops, "mfma_frac": attn_tflops / peak,
+                          "flop_per_byte": ai, "attainable_TFLOP/s": attainable,
+                          "frac_of_attainable": attn_tflops / attainable},
+            "select_topk": {"ms": per["select_topk"], "GB/s": gbs(work["bytes_select"], per["select_topk"]),
+                            "frac_of_hbm_peak": gbs(work["bytes_select"], per["select_topk"]) / PEAK_HBM_GBS,
+                            "recompute_TFLOP/s": recompute / (per["select_topk"] / 1e3) / 1e12},
+        }
+        total_flops = work["attn_flops"] + work["compress_flops"]
+        return {"ms_per_step": ms_step, "query_tokens_per_s": wl.T / (ms_step / 1e3),
+                "tflops_algorithmic": total_flops / (ms_step / 1e3) / 1e12,
+                "frac_of_bf16_peak": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                "kernels": kernels, "work": work}
+
+    def close(self):
+        self.plan.destroy()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=4, choices=range(5))
+    ap.add_argument("--workload", type=int, default=None, choices=range(5),
+                    help="measure only this workload (default: the batched workload as the headline, "
+                         "then every other workload)")
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="element type of q, k, v and the weight (default bf16)")
     ap.add_argument("--masks", action="store_true",
@@ -315,7 +476,10 @@ def main() -> int:
     ap.add_argument("--split-tiles", type=int, default=0,
                     help="run the attention as the split launch, pieces of at most this many key tiles")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of a sampled oracle run (workloads whose full run takes longer than "
+                         "--cpu-full-seconds)")
+    ap.add_argument("--cpu-full-seconds", type=float, default=60.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (calibrates the HBM byte "
                          "counters against a kernel of known traffic) and exit")
@@ -327,7 +491,6 @@ def main() -> int:
 
     import torch
     import synth
-    import kv_compression_block_amd as nsa
     from kv_compression_block_amd import _lib
 
     if not os.path.exists(_lib.LIB_PATH):
@@ -352,120 +515,36 @@ def main() -> int:
                           "write_bytes": args.copy_bytes, "ms": ms,
                           "GB/s": 2 * args.copy_bytes / (ms / 1e3) / 1e9}), flush=True)
         return 0
-    wl = synth.WORKLOADS[args.workload].with_dtype(args.dtype)
-    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
-    inp = synth.make_inputs(wl, device=dev, chunk_rows=16384)
-    c_pre, s_pre, pc, ps = [], [], 0, 0
-    for T in wl.seqlens:
-        pc += nsa.nsa_compress_out_len(T, wl.l, wl.d)
-        ps += -(-T // wl.lsel)
-        c_pre.append(pc)
-        s_pre.append(ps)
-    T2 = pc
-    plan = nsa.nsa_compress_attention_get_workspace(wl.act_seq_qlen, c_pre, s_pre, wl.N1, wl.N2, wl.D1,
-                                                    wl.D2, wl.scale, wl.l, wl.d, wl.lsel, wl.count,
-                                                    wl.torch_dtype)
-    kc = torch.empty((T2, wl.N2, wl.D1), dtype=wl.torch_dtype, device=dev)
-    vc = torch.empty((T2, wl.N2, wl.D2), dtype=wl.torch_dtype, device=dev)
-    outs = {"attention_out": torch.empty((wl.T, wl.N1, wl.D2), dtype=wl.torch_dtype, device=dev),
-            "topk_indices": torch.empty((wl.T, wl.N2, wl.count), dtype=torch.int32, device=dev),
-            "softmax_max": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev),
-            "softmax_sum": torch.empty((wl.T, wl.N1, 8), dtype=torch.float32, device=dev)}
-    masks = {}
-    if args.masks:
-        # The positional rules spelled out as masks (True = masked out), one
-        # matrix for all sequences: rows = local query positions.
-        t_max = max(wl.seqlens)
-        t = torch.arange(t_max, device=dev)[:, None]
-        masks["atten_mask"] = (torch.arange(max(nsa.nsa_compress_out_len(T, wl.l, wl.d) for T in wl.seqlens),
-                                            device=dev)[None, :] * wl.d + wl.l - 1) > t
-        masks["topk_mask"] = (torch.arange(max(-(-T // wl.lsel) for T in wl.seqlens),
-                                           device=dev)[None, :] * wl.lsel) > t
-    ws_bytes = plan.info["masked_workspace_bytes"] if args.masks else plan.workspace_bytes
-    if args.split_tiles:
-        if args.masks:
-            raise SystemExit("--split-tiles applies to the positional rule only")
-        ws_bytes = max(ws_bytes, nsa.nsa_compress_attention_split_workspace(plan, args.split_tiles))
-    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
+    head_id = 4 if args.workload is None else args.workload
+    wl = synth.WORKLOADS[head_id].with_dtype(args.dtype)
+    if args.split_tiles and args.masks:
+        raise SystemExit("--split-tiles applies to the positional rule only")
+    path = Path(args, wl, dev, masks_on=args.masks, split_tiles=args.split_tiles)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        nsa.nsa_compress(inp["k"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=kc, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        nsa.nsa_compress(inp["v"], inp["w"], wl.act_seq_qlen, wl.l, wl.d, out=vc, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
-        if args.split_tiles:
-            nsa.nsa_compress_attention_fwd_split(plan, inp["q"], kc, vc, args.split_tiles, workspace=ws,
-                                                 outputs=outs, stream=stream)
+    if args.backward or args.select_attention:
+        path.step()
+        torch.cuda.synchronize()
+        if args.backward:
+            res = backward_bench(args, wl, path.plan, path.inp, path.kc, path.vc, path.outs, path.stream, path.T2)
         else:
-            nsa.nsa_compress_attention_fwd(plan, inp["q"], kc, vc, workspace=ws, outputs=outs, stream=stream,
-                                           atten_mask=masks.get("atten_mask"))
-        if ev is not None:
-            ev[3].record(stream)
-        nsa.nsa_compress_attention_select(plan, inp["q"], kc, outs["softmax_max"], outs["softmax_sum"],
-                                          workspace=ws, outputs=outs, stream=stream,
-                                          atten_mask=masks.get("atten_mask"),
-                                          topk_mask=masks.get("topk_mask"))
-        if ev is not None:
-            ev[4].record(stream)
-
-    if args.backward:
-        step()
-        torch.cuda.synchronize()
-        res = backward_bench(args, wl, plan, inp, kc, vc, outs, stream, T2)
-        plan.destroy()
+            res = select_attention_bench(args, wl, path.plan, path.inp, path.outs["topk_indices"], path.ws,
+                                         path.stream)
+        path.close()
         print(json.dumps(res), flush=True)
         return 0
 
-    if args.select_attention:
-        step()
-        torch.cuda.synchronize()
-        res = select_attention_bench(args, wl, plan, inp, outs["topk_indices"], ws, stream)
-        plan.destroy()
-        print(json.dumps(res), flush=True)
-        return 0
-
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    names = ["compress_k", "compress_v", "attention", "select_topk"]
-    per = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)]))
-           for j, n in enumerate(names)}
-    work = workload_work(wl, T2)
-    value = wl.T / (ms_step / 1e3)
-    total_flops = work["attn_flops"] + work["compress_flops"]
-    attn_s = per["attention"] / 1e3
-    attn_tflops = work["attn_flops"] / attn_s / 1e12
+    m = path.time_steps(args.steps, args.warmup)
+    work, kernels = m.pop("work"), m["kernels"]
     peak = PEAK_MFMA_TFLOPS[wl.dtype]
-    kernels = {
-        "compress_k": {"ms": per["compress_k"], "GB/s": work["bytes_compress_k"] / (per["compress_k"] / 1e3) / 1e9},
-        "compress_v": {"ms": per["compress_v"], "GB/s": work["bytes_compress_v"] / (per["compress_v"] / 1e3) / 1e9},
-        "attention": {"ms": per["attention"], "TFLOP/s": attn_tflops, "mfma_frac": attn_tflops / peak},
-        "select_topk": {"ms": per["select_topk"],
-                        "GB/s": work["bytes_select"] / (per["select_topk"] / 1e3) / 1e9},
-    }
+    attn_tflops = kernels["attention"]["TFLOP/s"]
     res = {
         "metric": METRIC,
-        "value": value,
+        "value": m["query_tokens_per_s"],
         "unit": "query tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -478,11 +557,11 @@ def main() -> int:
                    "attention_launch": (f"split key ranges, at most {args.split_tiles} tiles of 32 blocks per piece"
                                         if args.split_tiles else "single pass"),
                    "parallelism": "single-gpu"},
-        "tflops_algorithmic": total_flops / (ms_step / 1e3) / 1e12,
-        "frac_of_bf16_peak": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+        "tflops_algorithmic": m["tflops_algorithmic"],
+        "frac_of_bf16_peak": m["frac_of_bf16_peak"],
         "roofline": {"kernel": "k_cmp_attn_fwd", "bound": "mfma", "achieved": attn_tflops,
                      "peak": peak, "unit": "TFLOP/s", "frac": attn_tflops / peak,
-                     "traffic": None if args.masks else measured_traffic(wl.name),
+                     "traffic": None if (args.masks or args.split_tiles) else measured_traffic(wl.name),
                      "traffic_unit": "HBM bytes per launch",
                      "work_per_launch": f"{work['attn_flops']:.4e} flop = 2*(D1+D2) x {work['visible_pairs']} "
                                         f"visible (token, block) pairs x {wl.N1} heads"},
@@ -492,11 +571,33 @@ def main() -> int:
         res["kernels_note"] = ("with --masks, 'attention' includes packing atten_mask and 'select_topk' "
                                "includes packing both masks (each call packs what it reads)")
     if not args.no_cpu_baseline:
-        print(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        print(f"[bench] {wl.name}: CPU oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl, path.inp, args.cpu_seconds, args.cpu_full_seconds)
     else:
         res["cpu_baseline"] = None
-    plan.destroy()
+    path.close()
+    del path
+    torch.cuda.empty_cache()
+
+    if args.workload is None:
+        # Every other workload, measured the same way (same step, same timing);
+        # the headline above is the batched workload.
+        configs = {wl.name: {"ms_per_step": m["ms_per_step"], "query_tokens_per_s": m["query_tokens_per_s"],
+                             "tflops_algorithmic": m["tflops_algorithmic"], "kernels": kernels,
+                             "cpu_baseline": res["cpu_baseline"]}}
+        for wid in (0, 1, 2, 3):
+            w = synth.WORKLOADS[wid].with_dtype(args.dtype)
+            p = Path(args, w, dev, masks_on=args.masks, split_tiles=args.split_tiles)
+            mw = p.time_steps(max(args.steps, 200) if wid == 0 else args.steps, args.warmup)
+            mw.pop("work")
+            if not args.no_cpu_baseline:
+                print(f"[bench] {w.name}: CPU oracle baseline", file=sys.stderr, flush=True)
+                mw["cpu_baseline"] = cpu_baseline(w, p.inp, args.cpu_seconds, args.cpu_full_seconds)
+            p.close()
+            del p
+            torch.cuda.empty_cache()
+            configs[w.name] = mw
+        res["configs"] = configs
     print(json.dumps(res), flush=True)
     return 0
 

@@ -70,6 +70,10 @@ def _load():
     lib.nsa_oracle_double_to_f16.restype = ctypes.c_uint16
     lib.nsa_oracle_round_to_f16.argtypes = [P, P, I64]
     lib.nsa_oracle_round_to_f16.restype = None
+    lib.nsa_oracle_stage_reset.argtypes = []
+    lib.nsa_oracle_stage_reset.restype = None
+    lib.nsa_oracle_stage_seconds.argtypes = [P]
+    lib.nsa_oracle_stage_seconds.restype = None
     lib.nsa_oracle_threads.argtypes = []
     lib.nsa_oracle_threads.restype = ctypes.c_int
     lib.nsa_oracle_n_cmp.argtypes = [I64, I64, I64]
@@ -116,6 +120,22 @@ def _i64(a) -> np.ndarray:
 
 def threads() -> int:
     return int(_load().nsa_oracle_threads())
+
+
+STAGES = ("compress", "attention (steps 1-3)", "remap + group sum (steps 4-5)", "top-k (steps 6-7)")
+
+
+def stage_reset() -> None:
+    """Zero the per-stage timers (instrumentation only)."""
+    _load().nsa_oracle_stage_reset()
+
+
+def stage_seconds() -> dict:
+    """Thread-seconds spent per stage since the last reset: compression, then
+    steps 1-3, 4-5 and 6-7 of the attention call (summed over threads)."""
+    out = np.zeros(4, dtype=np.float64)
+    _load().nsa_oracle_stage_seconds(_ptr(out))
+    return dict(zip(STAGES, (float(x) for x in out)))
 
 
 def bf16_to_f64(bits) -> np.ndarray:

@@ -59,7 +59,38 @@
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
+#else
+#include <time.h>
 #endif
+
+/* ---- stage timers (instrumentation for the CPU baseline; no arithmetic) ---
+ * Thread-seconds spent in each stage since the last reset: 0 = compression,
+ * 1 = scores, mask, softmax and output (steps 1-3), 2 = remap and group sum
+ * (steps 4-5), 3 = top-k mask and selection (steps 6-7). */
+static double g_stage_s[4];
+
+static double now_s(void)
+{
+#ifdef _OPENMP
+    return omp_get_wtime();
+#else
+    struct timespec ts;
+    clock_gettime(CLOCK_MONOTONIC, &ts);
+    return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
+#endif
+}
+
+void nsa_oracle_stage_reset(void)
+{
+    for (int i = 0; i < 4; ++i)
+        g_stage_s[i] = 0.0;
+}
+
+void nsa_oracle_stage_seconds(double* out4)
+{
+    for (int i = 0; i < 4; ++i)
+        out4[i] = g_stage_s[i];
+}
 
 /* ---- bfloat16 ------------------------------------------------------------ */
 
@@ -204,6 +235,7 @@ int nsa_oracle_compress(const uint16_t* x, const uint16_t* w, const int64_t* act
 {
     if (B < 1 || N < 1 || D < 1 || l < 1 || d < 1 || dtype < 0 || dtype > 1)
         return -1;
+    const double t_start = now_s();
     int64_t out_row = 0;
     for (int64_t b = 0; b < B; ++b) {
         int64_t start = seq_start(act_seq_len, b);
@@ -226,6 +258,7 @@ int nsa_oracle_compress(const uint16_t* x, const uint16_t* w, const int64_t* act
         }
         out_row += n;
     }
+    g_stage_s[0] += now_s() - t_start;
     return 0;
 }
 
@@ -402,6 +435,7 @@ int nsa_oracle_attention_masked(const uint16_t* q_rows, const int64_t* tokens, i
         double* P = (double*)malloc(sizeof(double) * (size_t)(n_cmp_max + 1));
         double* Ph = (double*)malloc(sizeof(double) * (size_t)(s_sel_max + 1));
         unsigned char* taken = (unsigned char*)malloc((size_t)(s_sel_max + 1));
+        double st_attn = 0.0, st_remap = 0.0, st_topk = 0.0;   /* this thread's stage times */
         if (!s || !P || !Ph || !taken) {
 #pragma omp atomic write
             err = -4;
@@ -425,21 +459,33 @@ int nsa_oracle_attention_masked(const uint16_t* q_rows, const int64_t* tokens, i
                     pslc_k[x] = 0.0;
                 for (int64_t h = 0; h < N1; ++h) {
                     int64_t g = h / G;
+                    const double t0 = now_s();
                     attend_one_head(q_rows + (k * N1 + h) * D1, kc, vc, cmp0, n_cmp, pos, g,
                                     N2, D1, D2, scale, l, d, dtype,
                                     atten_mask ? atten_mask + t * am_cols : NULL, s, P,
                                     out + (k * N1 + h) * D2,
                                     smax + k * N1 + h, ssum + k * N1 + h);
+                    const double t1 = now_s();
                     /* step 4, then step 5: heads of a group summed in order. */
                     remap_one_head(P, n_cmp, S_sel, R, L2, Ph);
                     for (int64_t j = 0; j < S_sel; ++j)
                         pslc_k[g * s_stride + j] += Ph[j];
+                    st_attn += t1 - t0;
+                    st_remap += now_s() - t1;
                 }
+                const double t2 = now_s();
                 for (int64_t g = 0; g < N2; ++g)
                     topk_one_group(pslc_k + g * s_stride, S_sel, pos, lsel, count,
                                    topk_mask ? topk_mask + t * tm_cols : NULL, taken,
                                    topk + (k * N2 + g) * count);
+                st_topk += now_s() - t2;
             }
+        }
+#pragma omp critical(nsa_oracle_stage)
+        {
+            g_stage_s[1] += st_attn;
+            g_stage_s[2] += st_remap;
+            g_stage_s[3] += st_topk;
         }
         free(s);
         free(P);

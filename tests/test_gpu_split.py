@@ -96,8 +96,8 @@ def test_single_pass_matches_split_on_every_token():
     work there) against the split launch with 3 key tiles per piece (which
     never enters that loop), on every row.  Both consume the same compressed
     K/V and compute every score with the same MFMA sequence, so the softmax
-    max agrees bit for bit; the sums and outputs differ only in summation
-    order."""
+    max agrees bit for bit; the sums differ only in summation order, the
+    outputs also in where P is rounded."""
     base = synth.WORKLOADS[4]
     lens = (max(base.seqlens), min(base.seqlens))
     wl = base.with_seqlens(lens, name=f"{base.name}@lens{list(lens)}")
@@ -122,5 +122,8 @@ def test_single_pass_matches_split_on_every_token():
     d = (a - b).abs()
     log(f"  attention_out: max |diff| {float(d.max()):.3e}")
     assert bool((d <= 2e-2 + 1e-2 * b.abs()).all())
-    # both round the same fp32 sums to bfloat16: at most a few ulps apart
-    assert bool((d <= 4.0 * 2.0 ** -8 * b.abs() + 1e-5).all())
+    # Each launch rounds every P to bfloat16 before P.V, relative to its own
+    # running maximum (a piece starts a new one), so each output carries up
+    # to 2^-9 * max|V| of rounding, plus its own rounding to bfloat16.
+    vmax = float(vc.double().abs().max())
+    assert bool((d <= 2.0 ** -8 * vmax + 2.0 ** -7 * b.abs()).all())

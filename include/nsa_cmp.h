@@ -207,6 +207,28 @@ nsa_status nsa_compress_attention(nsa_plan plan, const void* query, const void* 
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nsa_compress_attention_noalloc -- nsa_compress_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same computation,
+ * the same kernels and bitwise the same outputs, with no workspace
+ * argument.  Its only scratch, the per-sequence table (64 bytes per
+ * sequence), lives in a static device array inside the library that holds
+ * at most 1024 sequences (64 KiB per GPU, kept until the process ends).
+ * The call allocates and frees nothing; it copies the plan's table into
+ * that array on `stream` (which must belong to the current device) and
+ * launches the two kernels.  Every call on one GPU shares that GPU's array
+ * and overwrites it: calls that overlap on one GPU (several streams or
+ * threads at once) race and must be serialised by the caller.
+ *
+ * Arguments and errors as nsa_compress_attention, plus NSA_ERR_UNSUPPORTED
+ * when the plan has more than 1024 sequences.
+ */
+nsa_status nsa_compress_attention_noalloc(nsa_plan plan, const void* query, const void* key,
+                                          const void* value, void* attention_out,
+                                          int32_t* topk_indices, float* softmax_max,
+                                          float* softmax_sum, float* p_slc_debug, void* stream);
+
+/*
  * The second phase in two stream-ordered halves; nsa_compress_attention is
  * exactly nsa_compress_attention_fwd followed by
  * nsa_compress_attention_select on the same stream.

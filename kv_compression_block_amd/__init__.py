@@ -34,7 +34,8 @@ from . import _lib
 from ._lib import Masks, NsaError, PlanInfo  # noqa: F401
 
 __all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_workspace",
-           "nsa_compress_attention", "nsa_compress_attention_fwd", "nsa_compress_attention_select",
+           "nsa_compress_attention", "nsa_compress_attention_noalloc", "nsa_compress_attention_fwd",
+           "nsa_compress_attention_select",
            "nsa_compress_attention_split_workspace", "nsa_compress_attention_fwd_split",
            "nsa_select_attention", "nsa_compress_attention_backward", "nsa_compress_backward", "compress_attention", "Plan",
            "NsaError", "library_path"]
@@ -294,6 +295,40 @@ def nsa_compress_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, v
     _lib.check(st)
     res = (o["attention_out"], o["topk_indices"], o["softmax_max"], o["softmax_sum"])
     return res + (o["p_slc"],) if return_p_slc else res
+
+
+def nsa_compress_attention_noalloc(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                                   outputs: dict, p_slc: Optional[torch.Tensor] = None, stream=None):
+    """``nsa_compress_attention`` for callers that cannot allocate: nothing
+    is allocated here or in the library (its scratch is a static per-GPU
+    table of at most 1024 sequences, shared by every call on that GPU, so
+    calls that overlap on one GPU race).  ``outputs`` must hold
+    attention_out, topk_indices, softmax_max and softmax_sum of the plan's
+    shapes; ``p_slc`` optionally receives the importance scores.  Returns
+    (attention_out, topk_indices, softmax_max, softmax_sum)."""
+    _check_qkv(plan, query, key, value)
+    info = plan.info
+    T1, N1, N2, D2 = info["total_q_tokens"], info["head_num"], info["kv_head_num"], info["d2"]
+    want = {"attention_out": ((T1, N1, D2), query.dtype), "topk_indices": ((T1, N2, info["select_block_count"]),
+                                                                          torch.int32),
+            "softmax_max": ((T1, N1, 8), torch.float32), "softmax_sum": ((T1, N1, 8), torch.float32)}
+    for name, (shape, dt) in want.items():
+        t = outputs.get(name) if outputs else None
+        if t is None:
+            raise ValueError(f"outputs[{name!r}] must be given: this entry point allocates nothing")
+        _need_tensor(t, name)
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise ValueError(f"outputs[{name!r}] must be {dt} {shape}")
+    if p_slc is not None:
+        _need_tensor(p_slc, "p_slc")
+        if tuple(p_slc.shape) != (T1, N2, max(info["max_sel_blocks"], 1)) or p_slc.dtype != torch.float32:
+            raise ValueError("p_slc must be float32 [T1, N2, max select blocks]")
+    st = _lib.load().nsa_compress_attention_noalloc(
+        plan.handle, _ptr(query), _ptr(key), _ptr(value), _ptr(outputs["attention_out"]),
+        _ptr(outputs["topk_indices"]), _ptr(outputs["softmax_max"]), _ptr(outputs["softmax_sum"]), _ptr(p_slc),
+        _stream_ptr(query.device, stream))
+    _lib.check(st)
+    return outputs["attention_out"], outputs["topk_indices"], outputs["softmax_max"], outputs["softmax_sum"]
 
 
 def nsa_compress_attention_fwd(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,

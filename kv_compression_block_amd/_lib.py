@@ -30,6 +30,7 @@ EXPORTS = (
     "nsa_compress_attention_get_workspace",
     "nsa_compress_attention_get_workspace_kv",
     "nsa_compress_attention",
+    "nsa_compress_attention_noalloc",
     "nsa_compress_attention_fwd",
     "nsa_compress_attention_split_workspace",
     "nsa_compress_attention_fwd_split",
@@ -106,6 +107,8 @@ def load() -> ctypes.CDLL:
     lib.nsa_compress_attention_get_workspace_kv.restype = I32
     lib.nsa_compress_attention.argtypes = [P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_compress_attention.restype = I32
+    lib.nsa_compress_attention_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P]
+    lib.nsa_compress_attention_noalloc.restype = I32
     lib.nsa_compress_attention_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.nsa_compress_attention_fwd.restype = I32
     lib.nsa_compress_attention_split_workspace.argtypes = [P, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]

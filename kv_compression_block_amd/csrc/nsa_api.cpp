@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -789,6 +790,85 @@ nsa_status nsa_compress_attention(nsa_plan plan, const void* query, const void* 
     if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s)) != NSA_OK)
         return st;
     if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s)) != NSA_OK)
+        return st;
+    return ok();
+}
+
+}  // extern "C"
+
+// ---- the entry point that allocates nothing -----------------------------------
+// Its scratch (the per-sequence table, the only device memory beyond inputs
+// and outputs that the two kernels of nsa_compress_attention read) is a
+// file-scope device array.  Host code never passes the array's name to a
+// kernel or a copy: each device's own address comes from
+// hipGetSymbolAddress, resolved once per device with that device current.
+namespace {
+
+constexpr int kNoAllocMaxBatch = 1024;   // sequences the scratch table holds (64 KiB)
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) nsa::BatchEnt scratch[kNoAllocMaxBatch];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the current device (NULL with the detail set on failure).
+nsa_status scratch_on_current_device(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(NSA_ERR_UNSUPPORTED, "device %d: at most %d devices are supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(NSA_ERR_HIP, "hipGetSymbolAddress of the scratch table failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return NSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nsa_status nsa_compress_attention_noalloc(nsa_plan plan, const void* query, const void* key,
+                                          const void* value, void* attention_out, int32_t* topk_indices,
+                                          float* softmax_max, float* softmax_sum, float* p_slc_debug,
+                                          void* stream)
+{
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->B > kNoAllocMaxBatch)
+        return fail(NSA_ERR_UNSUPPORTED, "the no-allocation entry point holds at most %d sequences in its static "
+                    "scratch (plan has %lld); use nsa_compress_attention with a workspace", kNoAllocMaxBatch,
+                    (long long)plan->B);
+    if (plan->T1 > 0 && (!query || !attention_out || !topk_indices || !softmax_max || !softmax_sum))
+        return fail(NSA_ERR_NULLPTR, "query and the four outputs must not be NULL");
+    if (plan->T2 > 0 && (!key || !value))
+        return fail(NSA_ERR_NULLPTR, "key and value must not be NULL");
+    void* ws = nullptr;
+    nsa_status st = scratch_on_current_device(&ws);
+    if (st != NSA_OK)
+        return st;
+    const size_t ws_bytes = sizeof(nsa::BatchEnt) * kNoAllocMaxBatch;
+    if ((st = check_exec(plan, ws, ws_bytes, {query, key, value, attention_out, softmax_max, softmax_sum},
+                         {topk_indices, p_slc_debug})) != NSA_OK)
+        return st;
+    if (plan->T1 == 0)
+        return ok();
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = upload_table(plan, ws, s)) != NSA_OK)
+        return st;
+    if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, ws, s)) != NSA_OK)
+        return st;
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, ws, s)) != NSA_OK)
         return st;
     return ok();
 }

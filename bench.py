@@ -151,9 +151,13 @@ def cpu_baseline(wl, inp, budget_s: float, full_limit_s: float = 60.0) -> dict:
                          wl.lsel, wl.count, dtype=dt)
         return time.perf_counter() - t
 
-    pilot = np.sort(rng.choice(wl.T, min(wl.T, 32), replace=False)).astype(np.int64)
+    # A token's oracle cost grows with the compressed blocks it sees; the
+    # pilot's time is scaled by that work, not by its token count.
+    cost = np.concatenate([n_visible(np.arange(T), wl.l, wl.d,
+                                     (T - wl.l) // wl.d + 1 if T >= wl.l else 0) + 8.0 for T in wl.seqlens])
+    pilot = np.sort(rng.choice(wl.T, min(wl.T, 64), replace=False)).astype(np.int64)
     t_pilot = attn(pilot)
-    est_full = t_pilot * wl.T / len(pilot)
+    est_full = t_pilot * float(cost.sum()) / float(cost[pilot].sum())
     oracle.stage_reset()
     if est_full <= full_limit_s:
         n = wl.T

@@ -64,8 +64,9 @@ typedef enum nsa_dtype {
 } nsa_dtype;
 
 /* Opaque, reusable handle produced by the first phase of the attention
- * operator (the CANN page's "executor").  Read-only while executing, so one
- * plan may serve several streams at once.  Free with nsa_plan_destroy. */
+ * operator (the CANN page's "executor").  Never written after it is made,
+ * so one plan may serve several streams and threads at once (each with its
+ * own workspace).  Free with nsa_plan_destroy. */
 typedef struct nsa_plan_s* nsa_plan;
 
 /* Number of compressed entries of a sequence of length seq_len: the window
@@ -221,7 +222,8 @@ nsa_status nsa_compress_attention(nsa_plan plan, const void* query, const void* 
  * threads at once) race and must be serialised by the caller.
  *
  * Arguments and errors as nsa_compress_attention, plus NSA_ERR_UNSUPPORTED
- * when the plan has more than 1024 sequences.
+ * when the plan has more than 1024 sequences and NSA_ERR_CONSTRAINT for a
+ * device-planned plan.
  */
 nsa_status nsa_compress_attention_noalloc(nsa_plan plan, const void* query, const void* key,
                                           const void* value, void* attention_out,
@@ -290,10 +292,13 @@ typedef struct nsa_masks {
  * select lengths follow the key/value tokens: act_cmp_seq_kvlen must hold
  * floor((Tkv_b - l)/d) + 1 and act_sel_seq_kvlen ceil(Tkv_b / l'); key and
  * value passed to the calls are the compressed key/value tokens.  With
- * Tkv_b = Tq_b for every b the plan equals the plain one.  A plan with some
- * Tkv_b > Tq_b serves nsa_compress_attention, _fwd and _select (and the
- * masked calls without masks); explicit masks, selected-block attention,
- * the backward and the split launch return NSA_ERR_UNSUPPORTED for it.
+ * Tkv_b = Tq_b for every b the plan equals the plain one.  Every second-phase
+ * call takes such a plan: explicit masks keep one row per query (row t for
+ * the sequence's t-th query, whatever its position); selected-block
+ * attention takes the raw key/value tensors of all Tkv tokens
+ * ([sum_b Tkv_b, N2, D]), query t attending to keys at positions
+ * <= Tkv_b - Tq_b + t; the backward and the split launch apply the same
+ * positions.
  * Errors: those of nsa_compress_attention_get_workspace, plus NSA_ERR_SHAPE
  * when Tkv_b < Tq_b.
  */
@@ -319,12 +324,15 @@ nsa_status nsa_compress_attention_get_workspace_kv(
  *
  * nsa_compress_attention_split_workspace -- host only: the workspace the split
  *   call needs for this plan and key_tiles_per_piece (>= workspace_bytes of
- *   the plan; the plan keeps the work list of the last value asked for).
+ *   the plan).  The work list is built on the device, inside the workspace,
+ *   by the split call itself; the plan is not written.
  * nsa_compress_attention_fwd_split -- as nsa_compress_attention_fwd, with
  *   key_tiles_per_piece in [1, 2^20].
  * Errors: those of nsa_compress_attention_fwd, plus NSA_ERR_CONSTRAINT
  * (key_tiles_per_piece out of range) and NSA_ERR_WORKSPACE (workspace below
- * the size returned above).
+ * the size returned above).  With a device-planned plan the device checks
+ * its work list against the counts of the plan's own lengths and sets the
+ * status word (below) when they differ.
  */
 nsa_status nsa_compress_attention_split_workspace(nsa_plan plan, int64_t key_tiles_per_piece,
                                                   size_t* workspace_bytes);
@@ -374,13 +382,16 @@ nsa_status nsa_compress_attention_select_masked(nsa_plan plan, const void* query
  * topk_indices[t, g, :]; -1, repeated entries and entries at or past the
  * sequence's ceil(T/l') blocks add nothing.
  *
- *   plan           from nsa_compress_attention_get_workspace (sequence
+ *   plan           from nsa_compress_attention_get_workspace(_kv) (sequence
  *                  lengths, heads, dims, scale_value, l' = select_block_size,
- *                  select_block_count, dtype); l' must be a multiple of 32
+ *                  select_block_count, dtype); l' must be a multiple of 32.
+ *                  With a chunked plan query t of a sequence has position
+ *                  Tkv - Tq + t and attends to keys s <= that position.
  *   query          [T1, N1, d1] device
- *   key, value     [T1, N2, d1] and [T1, N2, d2] device: the raw (not
- *                  compressed) keys and values, same TND layout and
- *                  sequences as query
+ *   key, value     [Tkv, N2, d1] and [Tkv, N2, d2] device (Tkv = the plan's
+ *                  total_kv_tokens, T1 unless chunked): the raw (not
+ *                  compressed) keys and values, TND, sequence b at its
+ *                  key/value prefix-sum offset
  *   topk_indices   [T1, N2, select_block_count] int32 device (for instance
  *                  the output of nsa_compress_attention)
  *   attention_out  [T1, N1, d2] device; 0 for a query with no key
@@ -445,12 +456,58 @@ typedef struct nsa_plan_info {
     int64_t dtype;              /* the nsa_dtype the plan was made for */
     size_t masked_workspace_bytes;  /* workspace of the calls given a mask */
     size_t backward_workspace_bytes;  /* workspace of nsa_compress_attention_backward */
+    int64_t total_kv_tokens;    /* sum_b Tkv_b (== total_q_tokens unless chunked) */
+    int64_t device_metadata;    /* 1 for a plan from nsa_compress_attention_device_plan */
+    int64_t status_offset;      /* byte offset of the int32 status word in the workspace */
 } nsa_plan_info;
 
 nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info);
 
 /* Frees a plan; NULL is ignored. */
 void nsa_plan_destroy(nsa_plan plan);
+
+/*
+ * Planning on the device -- "QuantLightningIndexerMetadata" (README, 功能说明):
+ * a pre-pass on the device derives, from sequence lengths that stay in
+ * device memory, each batch's blocks and load, the totals, and each core's
+ * start and end points, and hands the main operator that metadata.  Here:
+ *
+ * nsa_compress_attention_device_plan -- a copy of `plan` whose execute calls
+ *   (every second-phase call, the split launch, selected-block attention,
+ *   the backward) copy nothing from the host: they read the per-sequence
+ *   table that nsa_compress_attention_metadata wrote into their workspace.
+ *   Host only.  Free it with nsa_plan_destroy.  Errors: NSA_ERR_NULLPTR.
+ *
+ * nsa_compress_attention_metadata -- writes that table into `workspace` on
+ *   `stream`, derived by one workgroup from the device prefix sums
+ *   act_seq_qlen, act_seq_kvlen (NULL: equal to act_seq_qlen),
+ *   act_cmp_seq_kvlen and act_sel_seq_kvlen (device int64 [B] each, B the
+ *   plan's batch, 8-byte aligned), and an int32 status word at byte
+ *   status_offset (nsa_plan_info) of the workspace: 0 when the lengths pass
+ *   every check the first phase makes (non-decreasing prefix sums,
+ *   Tq_b <= Tkv_b, compressed length floor((Tkv_b - l)/d) + 1, select length
+ *   ceil(Tkv_b / l')) and fit the plan: no sequence longer, with more
+ *   compressed entries or select blocks than the plan's largest, and the
+ *   same totals and launch sizes.  Otherwise the word holds a non-zero code
+ *   (bits: 1 prefix sums, 2 fewer key/value tokens than queries, 4
+ *   compressed length, 8 select length, 16 exceeds the plan's largest
+ *   sequence, 32 totals or launch sizes differ, 64 split work list differs)
+ *   and every later call on that workspace returns from its kernels without
+ *   touching its outputs.  Lengths may differ per sequence from the ones the
+ *   plan was made from as long as they pass.  The word is read by the
+ *   kernels only; a caller that wants it copies it back after the stream.
+ *   The workspace must hold the plan's workspace_bytes; the masked, split
+ *   and backward calls need their larger sizes as usual, with the table at
+ *   its start.
+ *   Errors: NSA_ERR_NULLPTR, NSA_ERR_CONSTRAINT (not a device-planned plan;
+ *   misaligned pointers), NSA_ERR_WORKSPACE, NSA_ERR_HIP.
+ */
+nsa_status nsa_compress_attention_device_plan(nsa_plan plan, nsa_plan* device_plan);
+
+nsa_status nsa_compress_attention_metadata(nsa_plan device_plan, const int64_t* act_seq_qlen,
+                                           const int64_t* act_seq_kvlen, const int64_t* act_cmp_seq_kvlen,
+                                           const int64_t* act_sel_seq_kvlen, void* workspace,
+                                           size_t workspace_bytes, void* stream);
 
 /* Static text naming a status. */
 const char* nsa_status_string(nsa_status status);

@@ -38,7 +38,7 @@ __all__ = ["nsa_compress_out_len", "nsa_compress", "nsa_compress_attention_get_w
            "nsa_compress_attention_select",
            "nsa_compress_attention_split_workspace", "nsa_compress_attention_fwd_split",
            "nsa_select_attention", "nsa_compress_attention_backward", "nsa_compress_backward", "compress_attention", "Plan",
-           "NsaError", "library_path"]
+           "nsa_compress_attention_device_plan", "nsa_compress_attention_metadata", "NsaError", "library_path"]
 
 
 def library_path() -> str:
@@ -201,6 +201,42 @@ def nsa_compress_attention_get_workspace(actual_seq_qlen, actual_cmp_seq_kvlen, 
     return Plan(h, ws.value)
 
 
+def nsa_compress_attention_device_plan(plan: Plan) -> Plan:
+    """A copy of ``plan`` whose execute calls read their per-sequence table
+    from the workspace, where ``nsa_compress_attention_metadata`` writes it
+    from device prefix sums (no host-to-device copy per call)."""
+    h = ctypes.c_void_p(0)
+    _lib.check(_lib.load().nsa_compress_attention_device_plan(plan.handle, ctypes.byref(h)))
+    return Plan(h, plan.workspace_bytes)
+
+
+def _device_prefix(t, name: str, B: int):
+    _need_tensor(t, name)
+    if t.dtype != torch.int64 or t.dim() != 1 or t.numel() != B:
+        raise ValueError(f"{name} must be a 1-D int64 GPU tensor of {B} prefix sums")
+    return _ptr(t)
+
+
+def nsa_compress_attention_metadata(plan: Plan, actual_seq_qlen: torch.Tensor, actual_cmp_seq_kvlen: torch.Tensor,
+                                    actual_sel_seq_kvlen: torch.Tensor, workspace: torch.Tensor,
+                                    actual_seq_kvlen: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Writes the per-sequence table of a device-planned ``plan`` into
+    ``workspace`` from int64 GPU prefix sums, with a status word at byte
+    ``plan.info["status_offset"]`` (0 when the lengths pass the plan's
+    checks; otherwise every later call on this workspace leaves its outputs
+    untouched)."""
+    B = plan.info["batch"]
+    _need_tensor(workspace, "workspace")
+    args = [_device_prefix(actual_seq_qlen, "actual_seq_qlen", B),
+            None if actual_seq_kvlen is None else _device_prefix(actual_seq_kvlen, "actual_seq_kvlen", B),
+            _device_prefix(actual_cmp_seq_kvlen, "actual_cmp_seq_kvlen", B),
+            _device_prefix(actual_sel_seq_kvlen, "actual_sel_seq_kvlen", B)]
+    st = _lib.load().nsa_compress_attention_metadata(plan.handle, *args, _ptr(workspace),
+                                                     workspace.numel() * workspace.element_size(),
+                                                     _stream_ptr(workspace.device, stream))
+    _lib.check(st)
+
+
 def _check_qkv(plan: Plan, query, key, value=None):
     info = plan.info
     _need_tensor(query, "query")
@@ -226,6 +262,8 @@ def _check_qkv(plan: Plan, query, key, value=None):
 
 def _workspace(plan: Plan, workspace, dev, stream, masked: bool = False):
     need = plan.info["masked_workspace_bytes"] if masked else plan.workspace_bytes
+    if workspace is None and plan.info["device_metadata"]:
+        raise ValueError("a device-planned plan needs the workspace nsa_compress_attention_metadata wrote")
     if workspace is None:
         workspace = _empty((max(need, 1),), torch.uint8, dev, stream)
     return workspace, workspace.numel() * workspace.element_size()
@@ -368,6 +406,8 @@ def nsa_compress_attention_fwd_split(plan: Plan, query: torch.Tensor, key: torch
     _check_qkv(plan, query, key, value)
     o = _alloc_outputs(plan, query, outputs, False, stream)
     need = nsa_compress_attention_split_workspace(plan, key_tiles_per_piece)
+    if workspace is None and plan.info["device_metadata"]:
+        raise ValueError("a device-planned plan needs the workspace nsa_compress_attention_metadata wrote")
     if workspace is None:
         workspace = _empty((max(need, 1),), torch.uint8, query.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
@@ -433,19 +473,20 @@ def compress_attention(query, key, value, scale_value, head_num, compress_block_
 def nsa_select_attention(plan: Plan, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                          topk_indices: torch.Tensor, workspace: Optional[torch.Tensor] = None,
                          outputs: Optional[dict] = None, stream=None):
-    """Selected-block attention over the raw ``key [T1, N2, D1]`` /
-    ``value [T1, N2, D2]`` (same sequences as ``query``) for the blocks that
-    ``topk_indices [T1, N2, count]`` lists.  Returns (attention_out
-    [T1, N1, D2], softmax_lse [T1, N1] float32)."""
+    """Selected-block attention over the raw ``key [Tkv, N2, D1]`` /
+    ``value [Tkv, N2, D2]`` (the plan's key/value tokens: Tkv = T1 unless the
+    plan is chunked) for the blocks that ``topk_indices [T1, N2, count]``
+    lists.  Returns (attention_out [T1, N1, D2], softmax_lse [T1, N1] float32)."""
     info = plan.info
     T1, N1, N2, D1, D2 = (info["total_q_tokens"], info["head_num"], info["kv_head_num"], info["d1"],
                           info["d2"])
+    Tkv = info["total_kv_tokens"]
     for t, name in ((query, "query"), (key, "key"), (value, "value"), (topk_indices, "topk_indices")):
         _need_tensor(t, name)
     if tuple(query.shape) != (T1, N1, D1):
         raise ValueError(f"query must be {(T1, N1, D1)}, got {tuple(query.shape)}")
-    if tuple(key.shape) != (T1, N2, D1) or tuple(value.shape) != (T1, N2, D2):
-        raise ValueError(f"key/value must be {(T1, N2, D1)} / {(T1, N2, D2)}, got "
+    if tuple(key.shape) != (Tkv, N2, D1) or tuple(value.shape) != (Tkv, N2, D2):
+        raise ValueError(f"key/value must be {(Tkv, N2, D1)} / {(Tkv, N2, D2)}, got "
                          f"{tuple(key.shape)} / {tuple(value.shape)}")
     if key.dtype != query.dtype or value.dtype != query.dtype:
         raise TypeError("query, key and value must share a dtype")
@@ -489,6 +530,8 @@ def nsa_compress_attention_backward(plan: Plan, query, key, value, attention_out
     dk = _empty((T2, N2, D1), torch.float32, dev, stream)
     dv = _empty((T2, N2, D2), torch.float32, dev, stream)
     need = info["backward_workspace_bytes"]
+    if workspace is None and info["device_metadata"]:
+        raise ValueError("a device-planned plan needs the workspace nsa_compress_attention_metadata wrote")
     if workspace is None:
         workspace = _empty((max(need, 1),), torch.uint8, dev, stream)
     st = _lib.load().nsa_compress_attention_backward(

@@ -43,6 +43,8 @@ EXPORTS = (
     "nsa_compress_backward",
     "nsa_plan_get_info",
     "nsa_plan_destroy",
+    "nsa_compress_attention_device_plan",
+    "nsa_compress_attention_metadata",
     "nsa_status_string",
     "nsa_last_error",
 )
@@ -64,6 +66,9 @@ class PlanInfo(ctypes.Structure):
         ("dtype", ctypes.c_int64),
         ("masked_workspace_bytes", ctypes.c_size_t),
         ("backward_workspace_bytes", ctypes.c_size_t),
+        ("total_kv_tokens", ctypes.c_int64),
+        ("device_metadata", ctypes.c_int64),
+        ("status_offset", ctypes.c_int64),
     ]
 
 
@@ -134,6 +139,10 @@ def load() -> ctypes.CDLL:
     lib.nsa_plan_get_info.restype = I32
     lib.nsa_plan_destroy.argtypes = [P]
     lib.nsa_plan_destroy.restype = None
+    lib.nsa_compress_attention_device_plan.argtypes = [P, ctypes.POINTER(ctypes.c_void_p)]
+    lib.nsa_compress_attention_device_plan.restype = I32
+    lib.nsa_compress_attention_metadata.argtypes = [P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.nsa_compress_attention_metadata.restype = I32
     lib.nsa_status_string.argtypes = [I32]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_last_error.argtypes = []

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnsa_cmp.so")
 
-SOURCES = ["compress.hip", "cmp_attn.hip", "slc_topk.hip", "masks.hip", "sel_attn.hip", "cmp_attn_bwd.hip", "nsa_api.cpp"]
+SOURCES = ["compress.hip", "cmp_attn.hip", "slc_topk.hip", "masks.hip", "sel_attn.hip", "cmp_attn_bwd.hip", "planner.hip",
+           "nsa_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -83,6 +83,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     auto kslot = [&](int i) __attribute__((always_inline)) { return i == 0 ? K0 : (i == 1 ? K1 : K2); };
     auto vslot = [&](int i) __attribute__((always_inline)) { return i == 0 ? V0 : (i == 1 ? V1 : V2); };
 
+    if (*p.status != 0)
+        return;   // the table failed the planner's checks
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lane = tid & 63;
@@ -601,6 +603,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
 template <typename E, int D2, int ROWS>
 __global__ __launch_bounds__(256) void k_cmp_attn_combine(AttnParams p, const CombineItem* items)
 {
+    if (*p.status != 0)
+        return;
     const CombineItem it = items[blockIdx.x];
     const BatchEnt be = p.bt[it.b];
     const int G = p.G;

@@ -67,6 +67,8 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     constexpr int KIPW = (KR::INS + W - 1) / W, VIPW = (VR::INS + W - 1) / W;
     __shared__ __attribute__((aligned(16))) uint16_t K0[KR::BUF], K1[KR::BUF];
     __shared__ __attribute__((aligned(16))) uint16_t V0[VR::BUF], V1[VR::BUF];
+    if (*p.status != 0)
+        return;   // the table failed the planner's checks
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     const bool vq = r < rows_total;
     const int tok = r / G;
     const int64_t grow = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + (r - tok * G);
-    const int nvq = vq ? n_visible(tok, p.l, p.d, be.n_cmp) : 0;
+    const int nvq = vq ? n_visible(tok + be.pos_off, p.l, p.d, be.n_cmp) : 0;
     const int64_t rsrc = vq ? grow : (int64_t)(be.q_off + row_wg / G) * p.N1 + (int64_t)g * G;
 
     // q, dout and out rows as B operands (lane l32 = row, k-slots 8hf..8hf+7)
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     }
 
     const int last_row = min(row_wg + 32 * W, rows_total) - 1;
-    const int n_kt = (n_visible(last_row / G, p.l, p.d, be.n_cmp) + KT - 1) / KT;
+    const int n_kt = (n_visible(last_row / G + be.pos_off, p.l, p.d, be.n_cmp) + KT - 1) / KT;
 
     // ---- tile copies ---------------------------------------------------------------
     const int64_t kstride = (int64_t)p.N2 * D1, vstride = (int64_t)p.N2 * D2;
@@ -275,6 +277,8 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     static_assert(SMEL * 2 >= 3 * 64 * (NDB1 > NDB2 ? NDB1 : NDB2) * 16 * 4, "reduction space");
     __shared__ __attribute__((aligned(16))) uint16_t SM[SMEL];
     __shared__ __attribute__((aligned(16))) float ST[W * 64];
+    if (*p.status != 0)
+        return;   // the table failed the planner's checks
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -314,12 +318,13 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         for (int ks = 0; ks < NDS; ++ks)
             vf[ks] = *(const u32x4*)(p.vc + krow * D2 + ks * 16 + hf * 8);
     }
-    // first row (t*G + hh) that sees this lane's entry: t >= key*d + l - 1
-    const int key_first_row = (key * p.d + p.l - 1) * G;
+    // first row (t*G + hh) that sees this lane's entry: the query's
+    // position pos_off + t >= key*d + l - 1
+    const int key_first_row = (key * p.d + p.l - 1 - be.pos_off) * G;
 
-    // query rows r = t*G + hh seeing the tile's first entry: t >= i0*d + l - 1
+    // query rows r = t*G + hh seeing the tile's first entry
     const int rows_total = be.T * G;
-    const int r_first = min(i0 * p.d + p.l - 1, be.T) * G;
+    const int r_first = min(max(i0 * p.d + p.l - 1 - be.pos_off, 0), be.T) * G;
     const int n_qt = (rows_total - r_first + 31) / 32;
 
     auto qs_at = [&](int slot) { return SM + (slot * W + wave) * QSZ; };

@@ -1,7 +1,9 @@
 // C ABI of the library (include/nsa_cmp.h): argument validation, extent
 // derivation, launch planning and launches.  The library allocates no device
-// memory; the attention call copies a small per-sequence table into the
-// caller's workspace and launches two kernels on the caller's stream.
+// memory; an attention call copies a small per-sequence table into the
+// caller's workspace (or, with a device-planned plan, finds it there, written
+// by nsa_compress_attention_metadata) and launches its kernels on the
+// caller's stream.  Plans are never written after they are made.
 #include "nsa_cmp.h"
 
 #include <hip/hip_runtime.h>
@@ -88,13 +90,13 @@ struct nsa_plan_s {
     size_t topk_lds;
     int64_t tiles_a, tiles_c, tiles_s;
     size_t ws_bytes;
+    // B entries, then one zero entry whose first word is the status word
+    // (kernels exit at once when it is not 0; the upload keeps it 0)
     std::vector<nsa::BatchEnt> table;
-    bool chunked = false;   // some sequence has key/value tokens before its first query
-    // split attention launch for the last key_tiles_per_piece asked for
-    int64_t split_C = 0;
-    std::vector<nsa::SplitItem> split_items;
-    std::vector<nsa::CombineItem> comb_items;
-    size_t split_items_off = 0, comb_items_off = 0, split_part_off = 0, ws_split_bytes = 0;
+    int64_t T_kv;             // key/value tokens of all sequences (== T1 unless chunked)
+    bool chunked = false;     // some sequence has key/value tokens before its first query
+    bool device_meta = false; // execute calls read the table the device planner wrote
+    int rows_c = 0;           // rows per workgroup of the top-k kernel
 };
 
 extern "C" {
@@ -323,8 +325,8 @@ static nsa_status make_plan(
     plan->topk_kbufs = kbufs;
     plan->sb = sb;
     plan->topk_lds = lds;
-    plan->table.resize((size_t)batch);
-    int64_t q_off = 0, c_off = 0, ta = 0, tc = 0, ts = 0, tk = 0, S_total = 0, T_max = 0, ncmp_max = 0;
+    plan->table.assign((size_t)batch + 1, nsa::BatchEnt{});
+    int64_t q_off = 0, kv_off = 0, c_off = 0, ta = 0, tc = 0, ts = 0, tk = 0, S_total = 0, T_max = 0, ncmp_max = 0;
     const int64_t rows_c = (int64_t)waves * 64;
     const int64_t rows_a = nsa::cmp_attn_rows_per_wg((int)d1, (int)d2);
     for (int64_t b = 0; b < batch; ++b) {
@@ -334,6 +336,8 @@ static nsa_status make_plan(
         e.q_off = (int32_t)q_off;
         e.T = (int32_t)T;
         e.pos_off = (int32_t)(kvlen[(size_t)b] - T);
+        e.kv_off = (int32_t)kv_off;
+        kv_off += kvlen[(size_t)b];
         if (e.pos_off > 0)
             plan->chunked = true;
         e.cmp_off = (int32_t)c_off;
@@ -356,18 +360,21 @@ static nsa_status make_plan(
         T_max = std::max(T_max, T);
         ncmp_max = std::max(ncmp_max, clen[(size_t)b]);
     }
-    if (ta > INT32_MAX || tc > INT32_MAX || ts > INT32_MAX || q_off * head_num * 8 > ((int64_t)1 << 62)) {
+    if (ta > INT32_MAX || tc > INT32_MAX || ts > INT32_MAX || tk > INT32_MAX || kv_off > INT32_MAX ||
+        q_off * head_num * 8 > ((int64_t)1 << 62)) {
         delete plan;
         return fail(NSA_ERR_UNSUPPORTED, "problem too large for one launch");
     }
     plan->T1 = q_off;
+    plan->T_kv = kv_off;
+    plan->rows_c = (int)rows_c;
     plan->T2 = c_off;
     plan->S_total = S_total;
     plan->tiles_a = ta;
     plan->tiles_c = tc;
     plan->tiles_s = ts;
     plan->tiles_k = tk;
-    plan->ws_bytes = ((size_t)batch * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
+    plan->ws_bytes = ((size_t)(batch + 1) * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
     plan->T_max = T_max;
     plan->ncmp_max = ncmp_max;
     plan->vis_words = std::max<int64_t>(1, (ncmp_max + 31) / 32);
@@ -425,10 +432,80 @@ nsa_status nsa_plan_get_info(nsa_plan plan, nsa_plan_info* info)
     info->dtype = plan->dtype;
     info->masked_workspace_bytes = plan->ws_masked_bytes;
     info->backward_workspace_bytes = plan->ws_bwd_bytes;
+    info->total_kv_tokens = plan->T_kv;
+    info->device_metadata = plan->device_meta ? 1 : 0;
+    info->status_offset = plan->B * (int64_t)sizeof(nsa::BatchEnt);
     return ok();
 }
 
 void nsa_plan_destroy(nsa_plan plan) { delete plan; }
+
+nsa_status nsa_compress_attention_device_plan(nsa_plan plan, nsa_plan* device_plan)
+{
+    if (device_plan)
+        *device_plan = nullptr;
+    if (!plan || !device_plan)
+        return fail(NSA_ERR_NULLPTR, "plan and device_plan must not be NULL");
+    nsa_plan_s* p = new (std::nothrow) nsa_plan_s(*plan);
+    if (!p)
+        return fail(NSA_ERR_WORKSPACE, "out of host memory");
+    p->device_meta = true;
+    *device_plan = p;
+    return ok();
+}
+
+nsa_status nsa_compress_attention_metadata(nsa_plan device_plan, const int64_t* act_seq_qlen,
+                                           const int64_t* act_seq_kvlen, const int64_t* act_cmp_seq_kvlen,
+                                           const int64_t* act_sel_seq_kvlen, void* workspace,
+                                           size_t workspace_bytes, void* stream)
+{
+    nsa_plan plan = device_plan;
+    if (!plan)
+        return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (!plan->device_meta)
+        return fail(NSA_ERR_CONSTRAINT, "the plan does not read its metadata from the workspace; derive one "
+                    "with nsa_compress_attention_device_plan");
+    if (!act_seq_qlen || !act_cmp_seq_kvlen || !act_sel_seq_kvlen)
+        return fail(NSA_ERR_NULLPTR, "the device prefix sums of query, compressed and select lengths must not be NULL");
+    if (!workspace || workspace_bytes < plan->ws_bytes)
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, plan->ws_bytes);
+    if (!aligned(workspace, 16) || !aligned(act_seq_qlen, 8) || !aligned(act_cmp_seq_kvlen, 8) ||
+        !aligned(act_sel_seq_kvlen, 8) || (act_seq_kvlen && !aligned(act_seq_kvlen, 8)))
+        return fail(NSA_ERR_CONSTRAINT, "workspace must be 16-byte and the prefix sums 8-byte aligned");
+    nsa::MetaParams m;
+    std::memset(&m, 0, sizeof m);
+    m.qlen = act_seq_qlen;
+    m.kvlen = act_seq_kvlen;
+    m.cmplen = act_cmp_seq_kvlen;
+    m.sellen = act_sel_seq_kvlen;
+    m.table = (nsa::BatchEnt*)workspace;
+    m.status = (int*)((char*)workspace + plan->B * (int64_t)sizeof(nsa::BatchEnt));
+    m.B = (int)plan->B;
+    m.l = (int)plan->l;
+    m.d = (int)plan->d;
+    m.lsel = (int)plan->lsel;
+    m.N2 = (int)plan->N2;
+    m.G = (int)(plan->N1 / plan->N2);
+    m.GP = 1 << plan->log2gp;
+    m.rows_a = nsa::cmp_attn_rows_per_wg((int)plan->D1, (int)plan->D2);
+    m.rows_c = plan->rows_c;
+    m.rows_s = nsa::kSelRows;
+    m.T_max = plan->T_max;
+    m.ncmp_max = plan->ncmp_max;
+    m.S_max = plan->S_max;
+    m.T1 = plan->T1;
+    m.T2 = plan->T2;
+    m.Tkv_total = plan->T_kv;
+    m.S_total = plan->S_total;
+    m.tiles_a = plan->tiles_a;
+    m.tiles_c = plan->tiles_c;
+    m.tiles_s = plan->tiles_s;
+    m.tiles_k = plan->tiles_k;
+    hipError_t e = nsa::launch_meta_table(m, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(NSA_ERR_HIP, "metadata launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
 
 }  // extern "C"
 
@@ -448,13 +525,22 @@ nsa_status check_exec(nsa_plan plan, void* workspace, size_t workspace_bytes,
     return NSA_OK;
 }
 
+// The table (and its zero status word) into the workspace, unless the plan
+// is device-planned: then nsa_compress_attention_metadata wrote both there.
 nsa_status upload_table(nsa_plan plan, void* workspace, hipStream_t s)
 {
+    if (plan->device_meta)
+        return NSA_OK;
     hipError_t e = hipMemcpyAsync(workspace, plan->table.data(), plan->table.size() * sizeof(nsa::BatchEnt),
                                   hipMemcpyHostToDevice, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "workspace upload failed: %s", hipGetErrorString(e));
     return NSA_OK;
+}
+
+const int* status_word(nsa_plan plan, const void* workspace)
+{
+    return (const int*)((const char*)workspace + plan->B * (int64_t)sizeof(nsa::BatchEnt));
 }
 
 float exp2_scale(const nsa_plan_s* plan) { return std::fabs(plan->scale) * 1.4426950408889634f; }
@@ -474,6 +560,7 @@ nsa::AttnParams fwd_params(nsa_plan plan, const void* query, const void* key, co
     a.smax = softmax_max;
     a.ssum = softmax_sum;
     a.bt = (const nsa::BatchEnt*)workspace;
+    a.status = status_word(plan, workspace);
     a.B = (int)plan->B;
     a.N1 = (int)plan->N1;
     a.N2 = (int)plan->N2;
@@ -504,48 +591,46 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
     return NSA_OK;
 }
 
-// Work list of a split attention launch: the attention kernel's row blocks
-// in its own order (per sequence and KV head, costliest first); a row block
-// with more than C key tiles becomes ceil(n / C) pieces of at most C tiles,
-// each with a partial slot, and one combine item.
-void build_split(nsa_plan plan, int64_t C)
+// Counts of a split attention launch with pieces of at most C key tiles:
+// the attention kernel's row blocks in its own order (per sequence and KV
+// head, costliest first); a row block with n > C key tiles becomes
+// ceil(n / C) pieces, each with a partial slot, plus one combine item.  The
+// list itself is built on the device from the table (k_split_count /
+// k_split_fill); these host counts size the workspace and the launches, and
+// the device checks its list against them.
+struct SplitCounts {
+    int64_t items = 0, combs = 0, slots = 0;
+    size_t chunk_off = 0, items_off = 0, combs_off = 0, part_off = 0, bytes = 0;
+};
+
+SplitCounts split_counts(const nsa_plan_s* plan, int64_t C)
 {
-    if (plan->split_C == C)
-        return;
     constexpr int KT = nsa::kKeyTileMin;   // key tile of the attention kernel
     const int64_t rows_a = nsa::cmp_attn_rows_per_wg((int)plan->D1, (int)plan->D2);
     const int64_t G = plan->N1 / plan->N2;
-    plan->split_C = 0;
-    plan->split_items.clear();
-    plan->comb_items.clear();
-    int32_t slot = 0;
-    for (size_t b = 0; b < plan->table.size(); ++b) {
-        const nsa::BatchEnt& e = plan->table[b];
-        for (int64_t idx = 0; idx < (int64_t)e.n_rb_a * plan->N2; ++idx) {
-            const int32_t g = (int32_t)(idx % plan->N2);
-            const int32_t rb = (int32_t)(e.n_rb_a - 1 - idx / plan->N2);
-            const int64_t last_row = std::min<int64_t>((int64_t)(rb + 1) * rows_a, (int64_t)e.T * G) - 1;
-            const int64_t t = last_row / G;
+    SplitCounts k;
+    for (int64_t b = 0; b < plan->B; ++b) {
+        const nsa::BatchEnt& e = plan->table[(size_t)b];
+        for (int64_t rb = 0; rb < e.n_rb_a; ++rb) {
+            const int64_t last_row = std::min<int64_t>((rb + 1) * rows_a, (int64_t)e.T * G) - 1;
+            const int64_t t = last_row / G + e.pos_off;
             const int64_t nv = t < plan->l - 1 ? 0 : std::min<int64_t>((t - plan->l + 1) / plan->d + 1, e.n_cmp);
-            const int32_t n_kt = (int32_t)((nv + KT - 1) / KT);
-            if (n_kt <= C) {
-                plan->split_items.push_back({(int32_t)b, g, rb, 0, n_kt, -1, 0, 0});
-                continue;
+            const int64_t n_kt = (nv + KT - 1) / KT;
+            const int64_t pieces = n_kt > C ? (n_kt + C - 1) / C : 1;
+            k.items += pieces * plan->N2;
+            if (n_kt > C) {
+                k.combs += plan->N2;
+                k.slots += pieces * plan->N2;
             }
-            const int32_t pieces = (int32_t)((n_kt + C - 1) / C);
-            for (int32_t p = 0; p < pieces; ++p)
-                plan->split_items.push_back({(int32_t)b, g, rb, (int32_t)(p * C),
-                                             (int32_t)std::min<int64_t>(C, n_kt - p * C), slot + p, 0, 0});
-            plan->comb_items.push_back({(int32_t)b, g, rb, slot, pieces, 0, 0, 0});
-            slot += pieces;
         }
     }
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    plan->split_items_off = plan->ws_bytes;
-    plan->comb_items_off = plan->split_items_off + up(plan->split_items.size() * sizeof(nsa::SplitItem));
-    plan->split_part_off = plan->comb_items_off + up(plan->comb_items.size() * sizeof(nsa::CombineItem));
-    plan->ws_split_bytes = plan->split_part_off + (size_t)slot * (size_t)rows_a * (size_t)(plan->D2 + 4) * 4;
-    plan->split_C = C;
+    k.chunk_off = plan->ws_bytes;
+    k.items_off = k.chunk_off + up((size_t)nsa::split_plan_chunks((int)plan->tiles_a) * sizeof(int4));
+    k.combs_off = k.items_off + up((size_t)k.items * sizeof(nsa::SplitItem));
+    k.part_off = k.combs_off + up((size_t)k.combs * sizeof(nsa::CombineItem));
+    k.bytes = k.part_off + (size_t)k.slots * (size_t)rows_a * (size_t)(plan->D2 + 4) * 4;
+    return k;
 }
 
 nsa_status launch_select(nsa_plan plan, const void* query, const void* key, const float* softmax_max,
@@ -562,6 +647,7 @@ nsa_status launch_select(nsa_plan plan, const void* query, const void* key, cons
     t.topk = topk_indices;
     t.pslc = p_slc_debug;
     t.bt = (const nsa::BatchEnt*)workspace;
+    t.status = status_word(plan, workspace);
     t.B = (int)plan->B;
     t.N1 = (int)plan->N1;
     t.N2 = (int)plan->N2;
@@ -614,8 +700,6 @@ nsa_status prepare_masks(nsa_plan plan, const nsa_masks* masks, bool use_atten, 
         return NSA_OK;
     const bool a = use_atten && masks->atten_mask;
     const bool t = use_topk && masks->topk_mask;
-    if ((a || t) && plan->chunked)
-        return fail(NSA_ERR_UNSUPPORTED, "explicit masks with query tokens after key/value tokens are not built");
     if (a && (masks->atten_rows < plan->T_max || masks->atten_cols < plan->ncmp_max))
         return fail(NSA_ERR_SHAPE, "atten_mask is [%lld, %lld]; it needs at least [%lld, %lld] "
                     "(longest sequence, most compressed entries)", (long long)masks->atten_rows,
@@ -684,20 +768,13 @@ nsa_status nsa_compress_attention_split_workspace(nsa_plan plan, int64_t key_til
 {
     if (!plan || !workspace_bytes)
         return fail(NSA_ERR_NULLPTR, "plan and workspace_bytes must not be NULL");
-    if (plan->chunked)
-        return fail(NSA_ERR_UNSUPPORTED, "split launches with query tokens after key/value tokens are not built");
     if (key_tiles_per_piece < 1 || key_tiles_per_piece > (1 << 20))
         return fail(NSA_ERR_CONSTRAINT, "key_tiles_per_piece must be in [1, 2^20], got %lld",
                     (long long)key_tiles_per_piece);
-    try {
-        build_split(plan, key_tiles_per_piece);
-    } catch (const std::bad_alloc&) {
-        plan->split_C = 0;
-        return fail(NSA_ERR_UNSUPPORTED, "out of host memory for the split work list");
-    }
-    if (plan->split_items.size() > (size_t)INT32_MAX)
+    const SplitCounts k = split_counts(plan, key_tiles_per_piece);
+    if (k.items > INT32_MAX || k.slots > INT32_MAX)
         return fail(NSA_ERR_UNSUPPORTED, "problem too large for one launch");
-    *workspace_bytes = plan->ws_split_bytes;
+    *workspace_bytes = k.bytes;
     return ok();
 }
 
@@ -721,25 +798,38 @@ nsa_status nsa_compress_attention_fwd_split(nsa_plan plan, const void* query, co
         return st;
     if (plan->T1 == 0)
         return ok();
+    const SplitCounts k = split_counts(plan, key_tiles_per_piece);
     hipStream_t s = (hipStream_t)stream;
     if ((st = upload_table(plan, workspace, s)) != NSA_OK)
         return st;
     char* ws = (char*)workspace;
-    hipError_t e = hipMemcpyAsync(ws + plan->split_items_off, plan->split_items.data(),
-                                  plan->split_items.size() * sizeof(nsa::SplitItem), hipMemcpyHostToDevice, s);
-    if (e == hipSuccess && !plan->comb_items.empty())
-        e = hipMemcpyAsync(ws + plan->comb_items_off, plan->comb_items.data(),
-                           plan->comb_items.size() * sizeof(nsa::CombineItem), hipMemcpyHostToDevice, s);
+    nsa::SplitPlanParams sp;
+    std::memset(&sp, 0, sizeof sp);
+    sp.table = (const nsa::BatchEnt*)workspace;
+    sp.status = (int*)status_word(plan, workspace);
+    sp.chunk_tot = (int4*)(ws + k.chunk_off);
+    sp.items = (nsa::SplitItem*)(ws + k.items_off);
+    sp.combs = (nsa::CombineItem*)(ws + k.combs_off);
+    sp.B = (int)plan->B;
+    sp.N2 = (int)plan->N2;
+    sp.G = (int)(plan->N1 / plan->N2);
+    sp.l = (int)plan->l;
+    sp.d = (int)plan->d;
+    sp.rows_a = nsa::cmp_attn_rows_per_wg((int)plan->D1, (int)plan->D2);
+    sp.C = (int)key_tiles_per_piece;
+    sp.tiles_a = (int)plan->tiles_a;
+    sp.n_items = k.items;
+    sp.n_combs = k.combs;
+    sp.n_slots = k.slots;
+    hipError_t e = nsa::launch_split_plan(sp, s);
     if (e != hipSuccess)
-        return fail(NSA_ERR_HIP, "workspace upload failed: %s", hipGetErrorString(e));
+        return fail(NSA_ERR_HIP, "split work list launch failed: %s", hipGetErrorString(e));
     nsa::AttnParams a = fwd_params(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace);
-    a.split = (const nsa::SplitItem*)(ws + plan->split_items_off);
-    a.part = (float*)(ws + plan->split_part_off);
-    e = nsa::launch_cmp_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->split_items.size(), s);
+    a.split = sp.items;
+    a.part = (float*)(ws + k.part_off);
+    e = nsa::launch_cmp_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)k.items, s);
     if (e == hipSuccess)
-        e = nsa::launch_attn_combine(plan->dtype, (int)plan->D1, (int)plan->D2, a,
-                                     (const nsa::CombineItem*)(ws + plan->comb_items_off),
-                                     (int)plan->comb_items.size(), s);
+        e = nsa::launch_attn_combine(plan->dtype, (int)plan->D1, (int)plan->D2, a, sp.combs, (int)k.combs, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "split attention launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -807,7 +897,9 @@ namespace {
 constexpr int kNoAllocMaxBatch = 1024;   // sequences the scratch table holds (64 KiB)
 constexpr int kMaxDevices = 64;
 
-__device__ __align__(256) nsa::BatchEnt scratch[kNoAllocMaxBatch];
+// The table of up to 1024 sequences, then the entry that carries its status
+// word, rounded up to 256 bytes (the size a plan's table occupies).
+__device__ __align__(256) nsa::BatchEnt scratch[kNoAllocMaxBatch + 4];
 
 std::mutex g_scratch_mutex;
 void* g_scratch_ptr[kMaxDevices];
@@ -845,6 +937,9 @@ nsa_status nsa_compress_attention_noalloc(nsa_plan plan, const void* query, cons
 {
     if (!plan)
         return fail(NSA_ERR_NULLPTR, "plan is NULL");
+    if (plan->device_meta)
+        return fail(NSA_ERR_CONSTRAINT, "a device-planned plan reads its table from a workspace; the "
+                    "no-allocation entry point takes a plan from nsa_compress_attention_get_workspace(_kv)");
     if (plan->B > kNoAllocMaxBatch)
         return fail(NSA_ERR_UNSUPPORTED, "the no-allocation entry point holds at most %d sequences in its static "
                     "scratch (plan has %lld); use nsa_compress_attention with a workspace", kNoAllocMaxBatch,
@@ -857,7 +952,7 @@ nsa_status nsa_compress_attention_noalloc(nsa_plan plan, const void* query, cons
     nsa_status st = scratch_on_current_device(&ws);
     if (st != NSA_OK)
         return st;
-    const size_t ws_bytes = sizeof(nsa::BatchEnt) * kNoAllocMaxBatch;
+    const size_t ws_bytes = sizeof(nsa::BatchEnt) * (kNoAllocMaxBatch + 4);
     if ((st = check_exec(plan, ws, ws_bytes, {query, key, value, attention_out, softmax_max, softmax_sum},
                          {topk_indices, p_slc_debug})) != NSA_OK)
         return st;
@@ -970,8 +1065,6 @@ nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* ke
 {
     if (!plan)
         return fail(NSA_ERR_NULLPTR, "plan is NULL");
-    if (plan->chunked)
-        return fail(NSA_ERR_UNSUPPORTED, "selected-block attention with query tokens after key/value tokens is not built");
     if (plan->T1 > 0 && (!query || !key || !value || !topk_indices || !attention_out || !softmax_lse))
         return fail(NSA_ERR_NULLPTR, "query, key, value, topk_indices and the outputs must not be NULL");
     if (plan->lsel % 32 != 0)
@@ -996,6 +1089,7 @@ nsa_status nsa_select_attention(nsa_plan plan, const void* query, const void* ke
     a.out = (uint16_t*)attention_out;
     a.lse = softmax_lse;
     a.bt = (const nsa::BatchEnt*)workspace;
+    a.status = status_word(plan, workspace);
     a.B = (int)plan->B;
     a.N1 = (int)plan->N1;
     a.N2 = (int)plan->N2;
@@ -1024,8 +1118,6 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
 {
     if (!plan)
         return fail(NSA_ERR_NULLPTR, "plan is NULL");
-    if (plan->chunked)
-        return fail(NSA_ERR_UNSUPPORTED, "the backward with query tokens after key/value tokens is not built");
     if (plan->T1 > 0 && (!query || !attention_out || !d_attention_out || !softmax_max || !softmax_sum || !d_query))
         return fail(NSA_ERR_NULLPTR, "query, attention_out, its gradient, the softmax statistics and d_query must not be NULL");
     if (plan->T2 > 0 && (!key || !value || !d_key || !d_value))
@@ -1033,8 +1125,8 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
     if (!nsa::attn_bwd_supported((int)plan->D1, (int)plan->D2))
         return fail(NSA_ERR_UNSUPPORTED, "head dims (%lld, %lld) are not built for the backward",
                     (long long)plan->D1, (long long)plan->D2);
-    for (const nsa::BatchEnt& e : plan->table)
-        if ((int64_t)e.T * plan->N1 * std::max(plan->D1, plan->D2) * 2 >= ((int64_t)1 << 32) - 64)
+    for (int64_t b = 0; b < plan->B; ++b)
+        if ((int64_t)plan->table[(size_t)b].T * plan->N1 * std::max(plan->D1, plan->D2) * 2 >= ((int64_t)1 << 32) - 64)
             return fail(NSA_ERR_UNSUPPORTED, "a sequence's query rows exceed 4 GiB; the backward addresses "
                         "them with 32-bit offsets");
     if (workspace_bytes < plan->ws_bwd_bytes || !workspace)
@@ -1064,6 +1156,7 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
     a.dvc = d_value;
     a.rowstat = (float*)((char*)workspace + plan->ws_bytes);
     a.bt = (const nsa::BatchEnt*)workspace;
+    a.status = status_word(plan, workspace);
     a.B = (int)plan->B;
     a.N1 = (int)plan->N1;
     a.N2 = (int)plan->N2;

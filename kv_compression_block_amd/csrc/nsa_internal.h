@@ -25,9 +25,38 @@ struct BatchEnt {
     int32_t n_rb_s;     // row blocks of the selected-block attention kernel (per KV head)
     int32_t tile_off_k; // first workgroup of the key-side backward kernel (32 entries each, per KV head)
     int32_t pos_off;    // KV tokens before the first query token (chunked prefill; 0 otherwise)
-    int32_t pad0, pad1, pad2;
+    int32_t kv_off;     // first raw key/value token of the sequence (global; == q_off unless chunked)
+    int32_t pad1, pad2;
 };
 static_assert(sizeof(BatchEnt) == 64, "BatchEnt layout");
+
+// The table of B sequences is followed in the workspace by one more entry
+// whose first word is the status: 0 when the table is valid.  The host
+// planner uploads it as 0; the device planner writes the outcome of its
+// checks (kMetaErr* bits).  Kernels reading the table return at once, before
+// any other memory access, when it is not 0.
+constexpr int kMetaErrPrefix = 1;     // a prefix sum decreases (or is negative)
+constexpr int kMetaErrKvShort = 2;    // fewer key/value tokens than queries in a sequence
+constexpr int kMetaErrCmpLen = 4;     // compressed length != floor((Tkv - l)/d) + 1
+constexpr int kMetaErrSelLen = 8;     // select length != ceil(Tkv / l')
+constexpr int kMetaErrCapacity = 16;  // a sequence exceeds the plan's longest / largest counts
+constexpr int kMetaErrTotals = 32;    // totals or launch sizes differ from the plan's
+constexpr int kMetaErrSplit = 64;     // the split work list differs from the host's counts
+
+// ---- planning on the device ----------------------------------------------------
+struct MetaParams {
+    const int64_t* qlen;     // [B] prefix sums of query tokens, device
+    const int64_t* kvlen;    // NULL or [B] prefix sums of key/value tokens
+    const int64_t* cmplen;   // [B] prefix sums of compressed entries
+    const int64_t* sellen;   // [B] prefix sums of select blocks
+    struct BatchEnt* table;  // [B] out
+    int* status;             // out: 0 or kMetaErr* bits
+    int B, l, d, lsel, N2, G, GP;
+    int rows_a, rows_c, rows_s;        // rows per workgroup: attention, top-k (padded group), selected-block attention
+    int64_t T_max, ncmp_max, S_max;    // the plan's largest sequence, compressed and select counts
+    int64_t T1, T2, Tkv_total, S_total, tiles_a, tiles_c, tiles_s, tiles_k;   // the plan's totals
+};
+hipError_t launch_meta_table(const MetaParams& p, hipStream_t stream);
 
 // ---- compression kernel ---------------------------------------------------
 constexpr int kCompressMaxSeg = 128;   // sequences per launch (more -> several launches)
@@ -98,6 +127,7 @@ struct AttnParams {
     float* smax;          // [T1, N1, 8]
     float* ssum;          // [T1, N1, 8]
     const BatchEnt* bt;   // [B], device
+    const int* status;    // the table's status word (a kernel returns at once when it is not 0)
     int B, N1, N2, G;
     int l, d;
     float c;              // |scale| * log2(e): raw score -> base-2 exponent
@@ -117,6 +147,19 @@ struct AttnParams {
 struct CombineItem {
     int32_t b, g, rb, slot0, n, pad0, pad1, pad2;
 };
+
+// Work list of a split launch, built on the device from the table.
+struct SplitPlanParams {
+    const BatchEnt* table;   // [B]
+    int* status;             // the table's status word (set on a count mismatch)
+    int4* chunk_tot;         // [chunks]: items, combine items, slots of each 256 row blocks
+    SplitItem* items;        // [n_items]
+    CombineItem* combs;      // [n_combs]
+    int B, N2, G, l, d, rows_a, C, tiles_a;
+    int64_t n_items, n_combs, n_slots;   // the host's counts for this plan and C
+};
+int split_plan_chunks(int tiles_a);
+hipError_t launch_split_plan(const SplitPlanParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(int dtype, int d1, int d2, const AttnParams& p, const CombineItem* items,
                                int n_items, hipStream_t stream);
 
@@ -139,6 +182,7 @@ struct TopkParams {
     int32_t* topk;        // [T1, N2, count]
     float* pslc;          // NULL or [T1, N2, s_stride]
     const BatchEnt* bt;   // [B], device
+    const int* status;    // the table's status word
     int B, N1, N2, G;
     int l, d, lsel, count;
     int R, H;             // R = l'/d; H = largest remap offset = R + floor(l/d) - 2
@@ -165,7 +209,8 @@ struct SelParams {
     const int32_t* topk;    // [T1, N2, count]
     uint16_t* out;          // [T1, N1, D2]
     float* lse;             // [T1, N1]
-    const BatchEnt* bt;     // [B], device (tile_off_a / n_rb_a: 128 rows per workgroup)
+    const BatchEnt* bt;     // [B], device (tile_off_s / n_rb_s: kSelRows rows per workgroup)
+    const int* status;      // the table's status word
     int B, N1, N2, G;
     int lsel, count;
     float c;                // |scale| * log2(e)
@@ -196,6 +241,7 @@ struct BwdParams {
     float* dvc;            // [T2, N2, D2]
     float* rowstat;        // workspace [T1 * N1][2]: exponent bias and Delta = dout . out per row
     const BatchEnt* bt;    // [B], device
+    const int* status;     // the table's status word
     int B, N1, N2, G;
     int l, d;
     float c;               // |scale| * log2(e)

@@ -57,6 +57,8 @@ __global__ __launch_bounds__(kSelRows * 2, 2) void k_sel_attn_fwd(SelParams p)
     __shared__ __attribute__((aligned(16))) uint16_t K0[C::KBUF], K1[C::KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t V0[KT * D2], V1[KT * D2];
     extern __shared__ __attribute__((aligned(16))) uint32_t sel_bits[];
+    if (*p.status != 0)
+        return;   // the table failed the planner's checks
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -110,7 +112,10 @@ __global__ __launch_bounds__(kSelRows * 2, 2) void k_sel_attn_fwd(SelParams p)
     for (int x = tid; x < p.tpw * sw + sw; x += 64 * W)
         sel_bits[x] = 0u;
     __syncthreads();
-    const int jmax = min(t_hi / p.lsel, be.S_sel - 1);     // later blocks hold only future keys
+    // Chunked prefill: query t sits at position pos_off + t among the
+    // sequence's Tkv = T + pos_off key/value tokens (bottom-right alignment).
+    const int pos_hi = t_hi + be.pos_off;
+    const int jmax = min(pos_hi / p.lsel, be.S_sel - 1);   // later blocks hold only future keys
     for (int e = tid; e < ntok * p.count; e += 64 * W) {
         const int tt = e / p.count;
         const int j = p.topk[((int64_t)(be.q_off + t_lo + tt) * p.N2 + g) * p.count + (e - tt * p.count)];
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(kSelRows * 2, 2) void k_sel_attn_fwd(SelParams p)
         if (key0 < 0)
             return -1;
         const int j = key0 / p.lsel, u = (key0 - j * p.lsel) / KT;
-        if (u + 1 < nsub && key0 + KT <= t_hi)
+        if (u + 1 < nsub && key0 + KT <= pos_hi)
             return key0 + KT;
         const int jn = first_block(j + 1);
         return jn < 0 ? -1 : jn * p.lsel;
@@ -155,12 +160,13 @@ __global__ __launch_bounds__(kSelRows * 2, 2) void k_sel_attn_fwd(SelParams p)
     // ---- tile copies into LDS ----------------------------------------------------
     const int64_t kstride = (int64_t)p.N2 * D1;
     const int64_t vstride = (int64_t)p.N2 * D2;
-    const uint16_t* kbase = p.k + ((int64_t)be.q_off * p.N2 + g) * D1;
-    const uint16_t* vbase = p.v + ((int64_t)be.q_off * p.N2 + g) * D2;
+    const uint16_t* kbase = p.k + ((int64_t)be.kv_off * p.N2 + g) * D1;
+    const uint16_t* vbase = p.v + ((int64_t)be.kv_off * p.N2 + g) * D2;
+    const int Tkv = be.T + be.pos_off;
     const uint32_t kst_b = (uint32_t)(kstride * 2), vst_b = (uint32_t)(vstride * 2);
     // keys key0 .. key0+31 of the sequence; rows past its end load as zero
     auto tile_bytes = [&](int key0, uint32_t stride_b, int row_bytes) -> uint32_t {
-        const int nvalid = min(KT, be.T - key0);
+        const int nvalid = min(KT, Tkv - key0);
         return nvalid > 0 ? (uint32_t)(nvalid - 1) * stride_b + (uint32_t)row_bytes : 0u;
     };
     // Global byte offset (inside a tile) each lane copies into LDS slot
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(kSelRows * 2, 2) void k_sel_attn_fwd(SelParams p)
     auto mask_max = [&](int key0, f32x16& sc) __attribute__((always_inline)) {
         const int j = key0 / p.lsel;
         const bool listed = (my_bits[j >> 5] >> (j & 31)) & 1u;
-        const int lim = listed ? tok - key0 - 4 * hf + 1 : 0;
+        const int lim = listed ? tok + be.pos_off - key0 - 4 * hf + 1 : 0;
         if (__ballot(lim < 32) != 0) {
 #pragma unroll
             for (int x = 0; x < 16; ++x)

@@ -76,6 +76,8 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     constexpr int HSH = 4 >> LOG2GP;        // token offset of the upper half-wave (GP <= 4)
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    if (*p.status != 0)
+        return;   // the table failed the planner's checks
     const int waves = p.waves;
     const int nbuf = p.kbufs;                              // K tile buffers: 2, or 1 if LDS is tight
     uint16_t* Ks = (uint16_t*)smem;                        // [nbuf][KT * KS]

@@ -94,9 +94,15 @@ def _load():
     lib.nsa_oracle_select_attention.argtypes = [P, P, P, P, P, I64, P, I64, I64, I64, I64, I64,
                                                 ctypes.c_double, I64, I64, ctypes.c_int, P, P]
     lib.nsa_oracle_select_attention.restype = ctypes.c_int
+    lib.nsa_oracle_select_attention_kv.argtypes = [P, P, P, P, P, I64, P, P, I64, I64, I64, I64, I64,
+                                                   ctypes.c_double, I64, I64, ctypes.c_int, P, P]
+    lib.nsa_oracle_select_attention_kv.restype = ctypes.c_int
     lib.nsa_oracle_attention_backward.argtypes = [P, P, P, P, P, P, I64, I64, I64, I64, I64,
                                                   ctypes.c_double, I64, I64, ctypes.c_int, P, P, P]
     lib.nsa_oracle_attention_backward.restype = ctypes.c_int
+    lib.nsa_oracle_attention_backward_kv.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I64, I64,
+                                                     ctypes.c_double, I64, I64, ctypes.c_int, P, P, P]
+    lib.nsa_oracle_attention_backward_kv.restype = ctypes.c_int
     lib.nsa_oracle_compress_backward.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, ctypes.c_int, P, P]
     lib.nsa_oracle_compress_backward.restype = ctypes.c_int
     _lib = lib
@@ -315,17 +321,20 @@ def run(wl, q_bits, k_bits, v_bits, w_bits, tokens=None, atten_mask=None,
 
 
 def select_attention(q_bits, k_bits, v_bits, topk, act_seq_qlen, N1: int, N2: int, scale: float,
-                     lsel: int, tokens=None, dtype: str = "bf16") -> dict:
+                     lsel: int, tokens=None, dtype: str = "bf16", act_seq_kvlen=None) -> dict:
     """Selected-block attention for the listed global tokens (all when None).
 
-    q: [T, N1, D1], k: [T, N2, D1], v: [T, N2, D2] bits of element type
-    ``dtype``; topk: [T, N2, count] int32 block indices (-1 unused).
+    q: [T, N1, D1], k: [Tkv, N2, D1], v: [Tkv, N2, D2] bits of element type
+    ``dtype`` (Tkv = T unless ``act_seq_kvlen`` gives chunked prefill: each
+    sequence's queries are then the last of its key/value tokens); topk:
+    [T, N2, count] int32 block indices (-1 unused).
     Returns dict(out [n, N1, D2], lse [n, N1]) in float64."""
     q, k, v = _u16(q_bits), _u16(k_bits), _u16(v_bits)
     topk = np.ascontiguousarray(topk, dtype=np.int32)
     T = q.shape[0]
+    Tkv = T if act_seq_kvlen is None else int(np.asarray(act_seq_kvlen)[-1])
     D1, D2 = q.shape[2], v.shape[2]
-    if k.shape != (T, N2, D1) or v.shape[:2] != (T, N2) or q.shape[1] != N1:
+    if k.shape != (Tkv, N2, D1) or v.shape[:2] != (Tkv, N2) or q.shape[1] != N1:
         raise ValueError("shapes of q, k, v do not match")
     if topk.ndim != 3 or topk.shape[:2] != (T, N2):
         raise ValueError(f"topk must be [{T}, {N2}, count], got {topk.shape}")
@@ -334,18 +343,23 @@ def select_attention(q_bits, k_bits, v_bits, topk, act_seq_qlen, N1: int, N2: in
     tok = _i64(np.arange(T) if tokens is None else tokens)
     out = np.empty((len(tok), N1, D2), dtype=np.float64)
     lse = np.empty((len(tok), N1), dtype=np.float64)
-    rc = _load().nsa_oracle_select_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(topk), _ptr(tok), len(tok),
-                                             _ptr(actq), len(actq), N1, N2, D1, D2, float(scale), lsel,
-                                             count, _code(dtype), _ptr(out), _ptr(lse))
+    actkv = None if act_seq_kvlen is None else _i64(act_seq_kvlen)
+    rc = _load().nsa_oracle_select_attention_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(topk), _ptr(tok), len(tok),
+                                                _ptr(actq), None if actkv is None else _ptr(actkv), len(actq),
+                                                N1, N2, D1, D2, float(scale), lsel, count, _code(dtype),
+                                                _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"nsa_oracle_select_attention returned {rc}")
     return {"out": out, "lse": lse}
 
 
 def attention_backward(q_bits, kc_bits, vc_bits, dout_bits, act_seq_qlen, act_cmp_seq_kvlen,
-                       N1: int, N2: int, scale: float, l: int, d: int, dtype: str = "bf16") -> dict:
+                       N1: int, N2: int, scale: float, l: int, d: int, dtype: str = "bf16",
+                       act_seq_kvlen=None) -> dict:
     """Gradients of steps 1-3 with respect to q, kc and vc for the gradient
-    dout [T1, N1, D2] of attention_out (all of element type ``dtype``).
+    dout [T1, N1, D2] of attention_out (all of element type ``dtype``);
+    ``act_seq_kvlen`` (optional prefix sums) puts each sequence's queries at
+    the end of its key/value tokens (chunked prefill).
     Returns dict(dq [T1,N1,D1], dkc [T2,N2,D1], dvc [T2,N2,D2]) in float64."""
     q, kc, vc, do = _u16(q_bits), _u16(kc_bits), _u16(vc_bits), _u16(dout_bits)
     T1, D1 = q.shape[0], q.shape[2]
@@ -354,9 +368,11 @@ def attention_backward(q_bits, kc_bits, vc_bits, dout_bits, act_seq_qlen, act_cm
         raise ValueError("shapes of q, kc, vc, dout do not match")
     actq, actc = _i64(act_seq_qlen), _i64(act_cmp_seq_kvlen)
     dq = np.empty((T1, N1, D1)); dkc = np.empty((T2, N2, D1)); dvc = np.empty((T2, N2, D2))
-    rc = _load().nsa_oracle_attention_backward(_ptr(q), _ptr(kc), _ptr(vc), _ptr(do), _ptr(actq), _ptr(actc),
-                                               len(actq), N1, N2, D1, D2, float(scale), l, d, _code(dtype),
-                                               _ptr(dq), _ptr(dkc), _ptr(dvc))
+    actkv = None if act_seq_kvlen is None else _i64(act_seq_kvlen)
+    rc = _load().nsa_oracle_attention_backward_kv(_ptr(q), _ptr(kc), _ptr(vc), _ptr(do), _ptr(actq),
+                                                  None if actkv is None else _ptr(actkv), _ptr(actc), len(actq),
+                                                  N1, N2, D1, D2, float(scale), l, d, _code(dtype),
+                                                  _ptr(dq), _ptr(dkc), _ptr(dvc))
     if rc != 0:
         raise ValueError(f"nsa_oracle_attention_backward returned {rc}")
     return {"dq": dq, "dkc": dkc, "dvc": dvc}

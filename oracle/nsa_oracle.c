@@ -529,19 +529,22 @@ int nsa_oracle_attention(const uint16_t* q_rows, const int64_t* tokens, int64_t 
  * Only the listed tokens (global indices) are evaluated: out and lse have
  * n_tok rows.
  */
-int nsa_oracle_select_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                const int32_t* topk, const int64_t* tokens, int64_t n_tok,
-                                const int64_t* act_seq_qlen, int64_t B, int64_t N1, int64_t N2,
-                                int64_t D1, int64_t D2, double scale, int64_t lsel, int64_t count,
-                                int dtype, double* out, double* lse)
+int nsa_oracle_select_attention_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* topk, const int64_t* tokens, int64_t n_tok,
+                                   const int64_t* act_seq_qlen, const int64_t* act_seq_kvlen, int64_t B,
+                                   int64_t N1, int64_t N2, int64_t D1, int64_t D2, double scale,
+                                   int64_t lsel, int64_t count, int dtype, double* out, double* lse)
 {
     if (N2 < 1 || N1 % N2 != 0 || lsel < 1 || count < 1 || B < 1 || dtype < 0 || dtype > 1)
         return -1;
     const int64_t G = N1 / N2;
-    int64_t T_max = 0;
+    int64_t T_max = 0;   /* longest key/value sequence */
     for (int64_t b = 0; b < B; ++b) {
         int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
-        if (T > T_max) T_max = T;
+        int64_t Tkv = act_seq_kvlen ? act_seq_kvlen[b] - seq_start(act_seq_kvlen, b) : T;
+        if (Tkv < T)
+            return -2;
+        if (Tkv > T_max) T_max = Tkv;
     }
     for (int64_t i = 0; i < n_tok; ++i) {
         int64_t tl = 0;
@@ -560,11 +563,15 @@ int nsa_oracle_select_attention(const uint16_t* q, const uint16_t* k, const uint
         } else {
 #pragma omp for schedule(dynamic, 1)
             for (int64_t i = 0; i < n_tok; ++i) {
-                int64_t t = 0;
-                const int64_t b = find_seq(act_seq_qlen, B, tokens[i], &t);
-                const int64_t s0 = seq_start(act_seq_qlen, b);
-                const int64_t T = act_seq_qlen[b] - s0;
-                const int64_t S = (T + lsel - 1) / lsel;
+                int64_t tq = 0;
+                const int64_t b = find_seq(act_seq_qlen, B, tokens[i], &tq);
+                const int64_t T = act_seq_qlen[b] - seq_start(act_seq_qlen, b);
+                /* keys and values of the sequence start at s0 and number Tkv;
+                 * chunked prefill puts query tq at position t = Tkv - T + tq */
+                const int64_t s0 = act_seq_kvlen ? seq_start(act_seq_kvlen, b) : seq_start(act_seq_qlen, b);
+                const int64_t Tkv = act_seq_kvlen ? act_seq_kvlen[b] - s0 : T;
+                const int64_t t = Tkv - T + tq;
+                const int64_t S = (Tkv + lsel - 1) / lsel;
                 for (int64_t g = 0; g < N2; ++g) {
                     /* the listed blocks of (t, g), as a set */
                     for (int64_t j = 0; j < S; ++j)
@@ -619,6 +626,16 @@ int nsa_oracle_select_attention(const uint16_t* q, const uint16_t* k, const uint
     return err;
 }
 
+int nsa_oracle_select_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                const int32_t* topk, const int64_t* tokens, int64_t n_tok,
+                                const int64_t* act_seq_qlen, int64_t B, int64_t N1, int64_t N2,
+                                int64_t D1, int64_t D2, double scale, int64_t lsel, int64_t count,
+                                int dtype, double* out, double* lse)
+{
+    return nsa_oracle_select_attention_kv(q, k, v, topk, tokens, n_tok, act_seq_qlen, NULL, B, N1, N2, D1, D2,
+                                          scale, lsel, count, dtype, out, lse);
+}
+
 /* ---- backward of compression and compressed attention ---------------------
  *
  * The pages state the training use of the operator (the softmax max and sum
@@ -632,11 +649,12 @@ int nsa_oracle_select_attention(const uint16_t* q, const uint16_t* k, const uint
  *   dkc_i += scale dS_i q.
  * The forward is recomputed from its definition in float64.
  */
-int nsa_oracle_attention_backward(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
-                                  const uint16_t* dout, const int64_t* act_seq_qlen,
-                                  const int64_t* act_cmp_seq_kvlen, int64_t B, int64_t N1,
-                                  int64_t N2, int64_t D1, int64_t D2, double scale, int64_t l,
-                                  int64_t d, int dtype, double* dq, double* dkc, double* dvc)
+int nsa_oracle_attention_backward_kv(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                                     const uint16_t* dout, const int64_t* act_seq_qlen,
+                                     const int64_t* act_seq_kvlen, const int64_t* act_cmp_seq_kvlen,
+                                     int64_t B, int64_t N1, int64_t N2, int64_t D1, int64_t D2,
+                                     double scale, int64_t l, int64_t d, int dtype, double* dq,
+                                     double* dkc, double* dvc)
 {
     if (N2 < 1 || N1 % N2 != 0 || d < 1 || l < 1 || B < 1 || dtype < 0 || dtype > 1)
         return -1;
@@ -670,9 +688,12 @@ int nsa_oracle_attention_backward(const uint16_t* q, const uint16_t* kc, const u
                 const int64_t q0 = seq_start(act_seq_qlen, b), T = act_seq_qlen[b] - q0;
                 const int64_t c0 = seq_start(act_cmp_seq_kvlen, b);
                 const int64_t nc = act_cmp_seq_kvlen[b] - c0;
+                /* chunked prefill: query t sits at position Tkv - T + t */
+                const int64_t Tkv = act_seq_kvlen ? act_seq_kvlen[b] - seq_start(act_seq_kvlen, b) : T;
                 for (int64_t t = 0; t < T; ++t) {
+                    const int64_t pos = Tkv - T + t;
                     int64_t nv = 0;
-                    while (nv < nc && nv * d + l - 1 <= t)
+                    while (nv < nc && nv * d + l - 1 <= pos)
                         ++nv;
                     if (nv == 0)
                         continue;
@@ -726,6 +747,16 @@ int nsa_oracle_attention_backward(const uint16_t* q, const uint16_t* kc, const u
         free(dP);
     }
     return err;
+}
+
+int nsa_oracle_attention_backward(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                                  const uint16_t* dout, const int64_t* act_seq_qlen,
+                                  const int64_t* act_cmp_seq_kvlen, int64_t B, int64_t N1,
+                                  int64_t N2, int64_t D1, int64_t D2, double scale, int64_t l,
+                                  int64_t d, int dtype, double* dq, double* dkc, double* dvc)
+{
+    return nsa_oracle_attention_backward_kv(q, kc, vc, dout, act_seq_qlen, NULL, act_cmp_seq_kvlen, B, N1, N2, D1,
+                                            D2, scale, l, d, dtype, dq, dkc, dvc);
 }
 
 /* Backward of the compression: y[i, n, :] = sum_p w[p, n] x[start + i*d + p, n, :]

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import kv_compression_block_amd as nsa
@@ -251,7 +252,8 @@ def test_split_workspace_host_checks():
 
 def test_chunked_plan_host_checks():
     """Chunked-prefill plans: fewer key/value than query tokens is a shape
-    error; the paths not built for them refuse before any launch."""
+    error; the plan records the key/value total, and the split launch sizes
+    its workspace for it like for any plan."""
     kw = dict(head_num=4, kv_head_num=1, d1=64, d2=64, scale_value=0.125, compress_block_size=32,
               compress_stride=16, select_block_size=64, select_block_count=4)
     c = [nsa.nsa_compress_out_len(300, 32, 16)]
@@ -261,7 +263,37 @@ def test_chunked_plan_host_checks():
     plan = nsa.nsa_compress_attention_get_workspace([100], c, s, actual_seq_kvlen=[300], **kw)
     try:
         assert plan.info["total_q_tokens"] == 100 and plan.info["total_cmp_tokens"] == c[0]
-        with pytest.raises(NotImplementedError):
-            nsa.nsa_compress_attention_split_workspace(plan, 4)
+        assert plan.info["total_kv_tokens"] == 300
+        assert nsa.nsa_compress_attention_split_workspace(plan, 4) > plan.workspace_bytes
     finally:
+        plan.destroy()
+
+
+def test_device_plan_host_checks():
+    """A device-planned plan reports itself and the status word's place (the
+    entry after the table); the metadata call refuses a plain plan, and the
+    no-allocation call refuses a device-planned one, before any launch."""
+    kw = dict(head_num=8, kv_head_num=2, d1=64, d2=64, scale_value=0.125, compress_block_size=32,
+              compress_stride=16, select_block_size=64, select_block_count=4)
+    lens = [300, 45, 1000]
+    c = list(np.cumsum([nsa.nsa_compress_out_len(T, 32, 16) for T in lens]))
+    s = list(np.cumsum([-(-T // 64) for T in lens]))
+    plan = nsa.nsa_compress_attention_get_workspace(list(np.cumsum(lens)), c, s, **kw)
+    dplan = nsa.nsa_compress_attention_device_plan(plan)
+    try:
+        assert plan.info["device_metadata"] == 0 and dplan.info["device_metadata"] == 1
+        assert plan.info["status_offset"] == dplan.info["status_offset"] == 64 * len(lens)
+        assert plan.workspace_bytes == dplan.workspace_bytes >= 64 * (len(lens) + 1)
+        lib = _lib.load()
+        fake = ctypes.c_void_p(4096)
+        st = lib.nsa_compress_attention_metadata(plan.handle, fake, None, fake, fake, fake, 1 << 20, None)
+        assert st == _lib.NSA_ERR_CONSTRAINT
+        st = lib.nsa_compress_attention_metadata(dplan.handle, None, None, fake, fake, fake, 1 << 20, None)
+        assert st == _lib.NSA_ERR_NULLPTR
+        st = lib.nsa_compress_attention_metadata(dplan.handle, fake, None, fake, fake, fake, 16, None)
+        assert st == _lib.NSA_ERR_WORKSPACE
+        st = lib.nsa_compress_attention_noalloc(dplan.handle, *([fake] * 8), None)
+        assert st == _lib.NSA_ERR_CONSTRAINT
+    finally:
+        dplan.destroy()
         plan.destroy()

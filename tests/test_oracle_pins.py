@@ -1056,3 +1056,59 @@ def test_chunked_prefill_rows_equal_full_prefill_rows():
                              actc, N1, N2, scale, l, d, lsel, count)
     for key in ("out", "max", "sum", "pslc", "topk"):
         assert np.array_equal(same[key], plain[key], equal_nan=True), key
+
+
+def test_chunked_select_attention_rows_equal_full_prefill_rows():
+    """Selected-block attention with chunked prefill (queries = the last Tq
+    of Tkv key/value tokens, key s visible to query t iff s <= Tkv - Tq + t)
+    is the full-sequence computation restricted to those rows, bit for bit,
+    given the same block lists."""
+    rng = np.random.default_rng(77)
+    N1, N2, D1, D2, lsel, count, scale = 4, 2, 32, 32, 32, 3, 0.2
+    kv_lens, q_lens = [250, 96], [70, 96]
+    T = sum(kv_lens)
+    k = rand_bf16(rng, (T, N2, D1))
+    v = rand_bf16(rng, (T, N2, D2))
+    q_full = rand_bf16(rng, (T, N1, D1))
+    lists = np.empty((T, N2, count), dtype=np.int32)
+    for s0, Tb in zip(starts_of(kv_lens), kv_lens):
+        S = -(-Tb // lsel)
+        lists[s0:s0 + Tb] = rng.integers(-1, S + 1, (Tb, N2, count))
+    full = oracle.select_attention(q_full, k, v, lists, np.cumsum(kv_lens), N1, N2, scale, lsel)
+    rows = np.concatenate([s + np.arange(Tb - Tq, Tb) for s, Tb, Tq in zip(starts_of(kv_lens), kv_lens, q_lens)])
+    chunk = oracle.select_attention(np.ascontiguousarray(q_full[rows]), k, v, np.ascontiguousarray(lists[rows]),
+                                    np.cumsum(q_lens), N1, N2, scale, lsel, act_seq_kvlen=np.cumsum(kv_lens))
+    for key in ("out", "lse"):
+        assert np.array_equal(chunk[key], full[key][rows], equal_nan=True), key
+    # the rows sit at the end of a 250-token sequence: a top-left alignment
+    # (query t at position t) would see far fewer keys and differ
+    assert not np.array_equal(chunk["lse"][:5], full["lse"][:5])
+
+
+def test_chunked_backward_equals_full_prefill_with_zero_gradient_elsewhere():
+    """The backward with chunked prefill equals the full-sequence backward
+    whose output gradient is zero on every row outside the chunk: such rows
+    add exact zeros to d_key and d_value (dP = 0 and Delta = 0 there), so
+    d_key, d_value and the chunk's d_query agree bit for bit."""
+    rng = np.random.default_rng(78)
+    N1, N2, D1, D2, l, d, scale = 4, 2, 32, 32, 32, 16, 0.3
+    kv_lens, q_lens = [260, 130], [90, 1]
+    T = sum(kv_lens)
+    kc_all, vc_all = [], []
+    for Tb in kv_lens:
+        n = oracle.n_cmp(Tb, l, d)
+        kc_all.append(rand_bf16(rng, (n, N2, D1)))
+        vc_all.append(rand_bf16(rng, (n, N2, D2)))
+    kc, vc = np.concatenate(kc_all), np.concatenate(vc_all)
+    actc = oracle.cmp_prefix(kv_lens, l, d)
+    q_full = rand_bf16(rng, (T, N1, D1))
+    rows = np.concatenate([s + np.arange(Tb - Tq, Tb) for s, Tb, Tq in zip(starts_of(kv_lens), kv_lens, q_lens)])
+    dout_full = np.zeros((T, N1, D2), dtype=np.uint16)       # bf16 +0
+    dout_full[rows] = rand_bf16(rng, (len(rows), N1, D2))
+    full = oracle.attention_backward(q_full, kc, vc, dout_full, np.cumsum(kv_lens), actc, N1, N2, scale, l, d)
+    chunk = oracle.attention_backward(np.ascontiguousarray(q_full[rows]), kc, vc,
+                                      np.ascontiguousarray(dout_full[rows]), np.cumsum(q_lens), actc, N1, N2,
+                                      scale, l, d, act_seq_kvlen=np.cumsum(kv_lens))
+    assert np.array_equal(chunk["dq"], full["dq"][rows])
+    assert np.array_equal(chunk["dkc"], full["dkc"]) and np.array_equal(chunk["dvc"], full["dvc"])
+    assert np.abs(chunk["dkc"]).sum() > 0 and np.abs(chunk["dvc"]).sum() > 0

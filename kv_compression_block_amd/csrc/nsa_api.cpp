@@ -672,6 +672,7 @@ nsa_status launch_select(nsa_plan plan, const void* query, const void* key, cons
     t.qsign = q_sign(plan);
     t.s_stride = (int)plan->S_max;
     t.sb = plan->sb;
+    t.nj_slots = (nsa::topk_key_tile((int)plan->D1) + t.R - 1) / t.R;
     t.npl = plan->sb / 64;
     t.waves = plan->topk_waves;
     t.kbufs = plan->topk_kbufs;

@@ -191,6 +191,7 @@ struct TopkParams {
     uint32_t qsign;
     int s_stride;         // row stride of pslc (max select blocks)
     int sb;               // LDS row length of the importance scores (multiple of 64)
+    int nj_slots;         // ceil(key tile / R): select blocks a key tile can finish per token
     int npl;              // candidates per lane in top-k, sb / 64
     int waves;            // waves per workgroup
     int kbufs;            // K tile buffers in LDS (2 = double buffered)
@@ -255,6 +256,7 @@ hipError_t launch_attn_bwd(int dtype, int d1, int d2, const BwdParams& p, int ti
                            hipStream_t stream);
 
 constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)
+constexpr int kTopkRingDup = 4;        // ring slots repeated past its end (stencils of <= 5 taps)
 constexpr int kTopkMaxNpl = 16;        // at most 1024 select blocks per sequence
 
 int topk_log2_gp(int G);               // log2 of the padded group size, -1 if G > 64

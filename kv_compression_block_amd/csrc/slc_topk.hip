@@ -25,7 +25,11 @@
 //     whose whole stencil is available are finished as a fixed-order weighted
 //     sum of at most H+1 ring entries (the remap written as a stencil over
 //     r = m + n with coefficient c(r) = number of (m, n) pairs).  The ring
-//     keeps the H entries a later block still needs.
+//     keeps the H entries a later block still needs.  Its first four slots
+//     are repeated past its end, so a stencil of up to five taps (every
+//     workload's: H = R + floor(l/d) - 2 = 4) reads five consecutive slots
+//     from one address with immediate offsets.  The (token, block) pairs of
+//     a tile are spread over the wave's lanes.
 //   * Top-k per (token, KV head) row, wave-local, on the float bits (scores
 //     are >= 0, so their bit patterns order like the values).  A radix
 //     select over the 64 per-lane maxima (one ballot per bit) gives a lower
@@ -73,6 +77,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     constexpr int KCH = D1 / 8;
     constexpr int KLD = KT * KCH / 256;
     constexpr int RING = kTopkRing;
+    constexpr int RINGP = kTopkRing + kTopkRingDup;   // ring row: the ring, then its first slots again
     constexpr int HSH = 4 >> LOG2GP;        // token offset of the upper half-wave (GP <= 4)
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -81,8 +86,8 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     const int waves = p.waves;
     const int nbuf = p.kbufs;                              // K tile buffers: 2, or 1 if LDS is tight
     uint16_t* Ks = (uint16_t*)smem;                        // [nbuf][KT * KS]
-    float* ring = (float*)(smem + nbuf * KT * KS * 2);     // [waves * TOKW][RING]
-    float* bins = ring + waves * TOKW * RING;              // [waves * TOKW][sb]
+    float* ring = (float*)(smem + nbuf * KT * KS * 2);     // [waves * TOKW][RINGP]
+    float* bins = ring + waves * TOKW * RINGP;             // [waves * TOKW][sb]
     uint32_t* stg = (uint32_t*)(bins + waves * TOKW * p.sb);  // [waves][128]
 
     const int tid = threadIdx.x;
@@ -178,11 +183,16 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
             (tlo < thi && tlo == 0) ? min(min(full / NKB, be.n_cmp / KT), kt_end) : 0);
     }
 
-    float* my_ring = ring + wave * TOKW * RING;
+    float* my_ring = ring + wave * TOKW * RINGP;
     float* my_bins = bins + wave * TOKW * p.sb;
     uint32_t* my_stg = stg + wave * 128;     // XM mask words in the key loop; top-k staging after it
-    for (int x = lane; x < TOKW * RING; x += 64)
+    for (int x = lane; x < TOKW * RINGP; x += 64)
         my_ring[x] = 0.f;
+    // Stencil lanes: lane -> (token tw_l, block slot jj_l) with nj_slots =
+    // ceil(KT / R) slots per token, tpp tokens per pass over the wave.
+    const int tw_l = lane / p.nj_slots;
+    const int jj_l = lane - tw_l * p.nj_slots;
+    const int tpp = 64 / p.nj_slots;
 
     // ---- K tile staging ------------------------------------------------------------
     const int64_t kstride = (int64_t)p.N2 * D1;
@@ -230,6 +240,29 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     // stencil sum over r = 0..H of coef(r) * P[R*j - r], ascending r, with the
     // entries at or past `limit` taken as 0.  Up to H = 7 the ring reads are
     // independent and go out together.
+    // Up to five taps (H <= 4): slots w[4 - r] hold P[R*j - r]; the read
+    // never passes the ring row's end (its first slots are repeated there).
+    // Taps past H have coefficient 0 and add nothing, so the sum equals the
+    // general one below bit for bit.
+    auto stencil5 = [&](const float* rg, int j) __attribute__((always_inline)) {
+        const float* w = rg + ((R * j - kTopkRingDup) & (RING - 1));
+        float v = 0.f;
+        v = fmaf(cf[0], w[4], v);
+        v = fmaf(cf[1], w[3], v);
+        v = fmaf(cf[2], w[2], v);
+        v = fmaf(cf[3], w[1], v);
+        v = fmaf(cf[4], w[0], v);
+        return v;
+    };
+    const bool short_stencil = H < kTopkRingDup + 1;
+    // Longer stencils inside the key loop (rare): a plain loop, so that
+    // nothing of it is computed ahead of the branch that skips it.
+    auto stencil_long = [&](const float* rg, int j) __attribute__((always_inline)) {
+        float v = 0.f;
+        for (int r = 0; r <= H; ++r)
+            v = fmaf(p.coef[r], rg[(R * j - r) & (RING - 1)], v);
+        return v;
+    };
     auto stencil = [&](const float* rg, int j, int limit) __attribute__((always_inline)) {
         float v = 0.f;
         if (H < 8) {
@@ -368,27 +401,40 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
                     const float v = half_sum(acc[tw][kb]);
-                    if (hf == 0)
-                        my_ring[tw * RING + ((kt * KT + kb * 32 + l32) & (RING - 1))] = v;
+                    const int ri = (kt * KT + kb * 32 + l32) & (RING - 1);
+                    if (hf == 0) {
+                        my_ring[tw * RINGP + ri] = v;
+                        if (ri < kTopkRingDup)
+                            my_ring[tw * RINGP + RING + ri] = v;
+                    }
                 }
             } else {
                 if ((tw & HSH) == 0) {
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb)
-                        my_ring[(tw + hf * HSH) * RING + ((kt * KT + kb * 32 + l32) & (RING - 1))] = acc[tw][kb];
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        const int ri = (kt * KT + kb * 32 + l32) & (RING - 1);
+                        float* rg = my_ring + (tw + hf * HSH) * RINGP;
+                        rg[ri] = acc[tw][kb];
+                        if (ri < kTopkRingDup)
+                            rg[RING + ri] = acc[tw][kb];
+                    }
                 }
             }
         }
         wave_lds_sync();
 
-        // Select blocks j whose stencil top R*j lies in this tile (<= 64 of them).
+        // Select blocks j whose stencil top R*j lies in this tile (at most
+        // nj_slots of them per token), one (token, block) pair per lane.
         const int key0 = kt * KT;
         const int jlo = (key0 + R - 1) / R;
         const int nj = min((key0 + KT + R - 1) / R, be.S_sel) - jlo;
-        if (lane < nj) {
-            const int j = jlo + lane;
-            for (int tw = 0; tw < TOKW; ++tw)
-                my_bins[tw * p.sb + j] = stencil(my_ring + tw * RING, j, 0x7FFFFFFF);
+        for (int tw0 = 0; tw0 < TOKW; tw0 += tpp) {
+            const int tw = tw0 + tw_l;
+            if (tw_l < tpp && tw < TOKW && jj_l < nj) {
+                const int j = jlo + jj_l;
+                const float* rg = my_ring + tw * RINGP;
+                my_bins[tw * p.sb + j] = __builtin_expect(short_stencil, 1) ? stencil5(rg, j) : stencil_long(rg, j);
+            }
         }
         wave_lds_sync();
 
@@ -419,7 +465,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         const int j_end = (p.pslc || p.cand) ? be.S_sel : min(be.S_sel, (tok_w + TOKW - 1 + be.pos_off) / p.lsel + 1);
         for (int j = jlo + lane; j < j_end; j += 64)
             for (int tw = 0; tw < TOKW; ++tw)
-                my_bins[tw * p.sb + j] = stencil(my_ring + tw * RING, j, keys_done);
+                my_bins[tw * p.sb + j] = stencil(my_ring + tw * RINGP, j, keys_done);
     }
     wave_lds_sync();
 
@@ -654,7 +700,7 @@ int topk_log2_gp(int G)
 size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs)
 {
     const size_t tokw = (size_t)(64 >> log2gp);
-    return (size_t)kbufs * topk_key_tile(d1) * (d1 + 8) * 2 + (size_t)waves * tokw * kTopkRing * 4 +
+    return (size_t)kbufs * topk_key_tile(d1) * (d1 + 8) * 2 + (size_t)waves * tokw * (kTopkRing + kTopkRingDup) * 4 +
            (size_t)waves * tokw * sb * 4 + (size_t)waves * 128 * 4;
 }
 

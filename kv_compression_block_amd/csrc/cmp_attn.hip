@@ -118,7 +118,6 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     int nvq[QB];
     int mrow[QB];    // packed atten_mask row of the lane's token (XM)
     bool vq[QB];
-    int64_t grow[QB];
     u32x4 qf[QB][C::NKS];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -126,12 +125,12 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         vq[qb] = r < rows_total;
         const int tok = r / G;
         const int hh = r - tok * G;
-        grow[qb] = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
         nvq[qb] = vq[qb] ? n_visible(tok + be.pos_off, p.l, p.d, be.n_cmp) : 0;
         mrow[qb] = vq[qb] ? tok : 0;
         // Rows past the sequence read the workgroup's first row (always valid);
         // they see no block and are never written.
-        const int64_t qsrc = vq[qb] ? grow[qb] : (int64_t)(be.q_off + row_wg / G) * p.N1 + (int64_t)g * G;
+        const int64_t qsrc = vq[qb] ? (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh
+                                    : (int64_t)(be.q_off + row_wg / G) * p.N1 + (int64_t)g * G;
         const uint16_t* qrow = p.q + qsrc * D1 + hf * 8;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
@@ -525,23 +524,27 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
     // L2 is better kept for the K/V tiles.  Every wave
     // is done with the K slots after this barrier; each wave stages its rows
     // in a private part of them, half of D2 per pass.
+    // The lane and each row's output index are recomputed here rather than
+    // kept live across the key loop (which would cost registers it needs).
+    const int lane_e = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int l32_e = lane_e & 31, hf_e = lane_e >> 5;
     if (split && split_slot >= 0) {
         // a piece of a split row block: unnormalised O with the running sum,
         // reference max and true max of each row, for the combine kernel
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            if (!vq[qb])
+            const int rr = (wave * QB + qb) * 32 + l32_e;
+            if (row_wg + rr >= rows_total)
                 continue;
-            const int rr = (wave * QB + qb) * 32 + l32;
             float* dst = p.part + ((int64_t)split_slot * C::ROWS + rr) * (D2 + 4);
             const float lf = half_sum(lsum[qb]);
 #pragma unroll
             for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
-                    *(f32x4*)(dst + db * 32 + 8 * r4 + 4 * hf) =
+                    *(f32x4*)(dst + db * 32 + 8 * r4 + 4 * hf_e) =
                         f32x4{o[qb][db][4 * r4], o[qb][db][4 * r4 + 1], o[qb][db][4 * r4 + 2], o[qb][db][4 * r4 + 3]};
-            if (hf == 0)
+            if (hf_e == 0)
                 *(f32x4*)(dst + D2) = f32x4{lf, mref[qb], mtrue[qb], 0.f};
         }
         return;
@@ -565,16 +568,16 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
             for (int db = h * C::NDB / 2; db < (h + 1) * C::NDB / 2; ++db) {
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
-                    const int dv = (db - h * C::NDB / 2) * 32 + 8 * r4 + 4 * hf;
+                    const int dv = (db - h * C::NDB / 2) * 32 + 8 * r4 + 4 * hf_e;
                     u32x2 w2 = {E::pack2(o[qb][db][4 * r4 + 0] * inv, o[qb][db][4 * r4 + 1] * inv),
                                 E::pack2(o[qb][db][4 * r4 + 2] * inv, o[qb][db][4 * r4 + 3] * inv)};
-                    *(u32x2*)&ostg[l32 * OPITCH + dv] = w2;
+                    *(u32x2*)&ostg[l32_e * OPITCH + dv] = w2;
                 }
             }
 #pragma unroll
             for (int i = 0; i < 32 / RPI; ++i) {
-                const int rr = i * RPI + lane / CPR;          // staged row
-                const int ch = lane % CPR;
+                const int rr = i * RPI + lane_e / CPR;          // staged row
+                const int ch = lane_e % CPR;
                 const u32x4 v = *(const u32x4*)&ostg[rr * OPITCH + ch * 8];
                 const int r = row_wg + (wave * QB + qb) * 32 + rr;
                 if (r < rows_total) {
@@ -584,12 +587,15 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                 }
             }
         }
-        if (!vq[qb])
+        const int r = row_wg + (wave * QB + qb) * 32 + l32_e;
+        if (r >= rows_total)
             continue;
+        const int tok = r / G;
+        const int64_t grow = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + (r - tok * G);
         const float smv = empty ? -INFINITY : mtrue[qb] * p.abs_scale;
         const float ssv = empty ? 0.f : lf * fast_exp2((mref[qb] - mtrue[qb]) * c);
-        const float val = hf == 0 ? smv : ssv;
-        float* dst = (hf == 0 ? p.smax : p.ssum) + grow[qb] * 8;
+        const float val = hf_e == 0 ? smv : ssv;
+        float* dst = (hf_e == 0 ? p.smax : p.ssum) + grow * 8;
         f32x4 v4 = {val, val, val, val};
         __builtin_nontemporal_store(v4, (f32x4*)dst);
         __builtin_nontemporal_store(v4, (f32x4*)(dst + 4));

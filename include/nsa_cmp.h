@@ -491,7 +491,8 @@ void nsa_plan_destroy(nsa_plan plan);
  *   same totals and launch sizes.  Otherwise the word holds a non-zero code
  *   (bits: 1 prefix sums, 2 fewer key/value tokens than queries, 4
  *   compressed length, 8 select length, 16 exceeds the plan's largest
- *   sequence, 32 totals or launch sizes differ, 64 split work list differs)
+ *   sequence, 32 totals or launch sizes differ, 64 a work list -- split
+ *   attention or key-side backward -- differs from the host's counts)
  *   and every later call on that workspace returns from its kernels without
  *   touching its outputs.  Lengths may differ per sequence from the ones the
  *   plan was made from as long as they pass.  The word is read by the

@@ -9,13 +9,16 @@
 //   * query side (rows = (token, head), as the forward): recomputes P and dS
 //     tile by tile and accumulates dq; also leaves each row's exponent bias
 //     and Delta in the workspace for the key side;
-//   * key side (one 32-entry key tile of one KV head per workgroup): four
-//     waves split the query rows that see the tile, each accumulates dkc and
-//     dvc for it, and the four partial sums are added in a fixed order.
+//   * key side (a block of 128 compressed entries of one KV head and a
+//     range of the query tiles that see it per workgroup, each wave owning
+//     32 entries; the query tiles stream through LDS slots shared by the
+//     waves): blocks seen by more tiles than an item holds leave partial
+//     sums, added in piece order by a combine kernel.
 // Both use bf16 or f16 MFMA 32x32x16 with fp32 accumulation; tiles go
 // through LDS by buffer-unit copies of whole rows (16 bytes of padding per
 // row) and transposed reads (ds_read_b64_tr_b16) where an operand needs
 // the other orientation.
+#include <climits>
 #include <type_traits>
 
 #include "nsa_device.h"
@@ -252,31 +255,52 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     }
 }
 
-// ---- key side: dkc, dvc ---------------------------------------------------------
-// One workgroup per (sequence, KV head, 32-entry key tile).  Keys and values
-// of the tile are B operands held in registers (lane l32 = entry); the query
-// rows that see the tile's first entry are split over the four waves in
-// 32-row tiles, each copied with its dout rows into the wave's own LDS
-// slots.  Per query tile: S = Q K^T and dP = dO V^T (rows = queries in
-// registers, lane = key), P and dS from the rows' bias and Delta, then
-// dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read transposed.
+// ---- key side: dkc, dvc -----------------------------------------------------------
+// One work item per workgroup: a block of kBwdKeyBlock = 128 compressed
+// entries (keys) of one KV head and a range of the 32-row query tiles that
+// see the block.  Each of the four waves owns 32 keys: K and V are its MFMA
+// B operands in registers, dK^T and dV^T its accumulators.  The query tiles
+// (rows of q and dout, then each row's exponent bias and Delta) stream
+// through NS LDS slots shared by the four waves, copied by the buffer unit
+// NS - 1 tiles ahead of their use, so a tile is fetched once for 128 keys
+// and its copy latency is covered by NS - 1 steps of work.  Per tile and
+// wave: S = Q K^T and dP = dO V^T (rows = queries, lane = key), P and
+// dS = P (dP - Delta), then dV^T += dO^T P and dK^T += Q^T dS with the row
+// tiles read transposed.  A block seen by more query tiles than an item
+// holds is cut into pieces; a piece leaves unscaled dK and dV in its
+// partial slot and k_cmp_attn_bwd_combine adds the pieces in order.
+template <int D1, int D2>
+struct DkvCfg {
+    static constexpr int W = 4;
+    static constexpr int KB = 32 * W;
+    static_assert(KB == kBwdKeyBlock, "key block");
+    using QR = PadRows<D1>;
+    using OR = PadRows<D2>;
+    static constexpr int QIW = (QR::INS + W - 1) / W;       // Q copy instructions per wave and tile
+    static constexpr int OIW = (OR::INS + W - 1) / W;       // dout copy instructions per wave and tile
+    static constexpr int QSZ = QIW * W * 512;               // elements of a slot's Q tile (with slack)
+    static constexpr int OSZ = OIW * W * 512;
+    static constexpr int SLOT_B = (QSZ + OSZ) * 2 + 64 * 4;  // + 32 rows x (bias, Delta)
+    static constexpr int NS = 5;                            // slots: a tile is copied 4 steps ahead
+    static_assert(NS * SLOT_B <= 150 * 1024, "slots do not fit in LDS");
+    static constexpr int CPW = QIW + OIW + 1;               // copy instructions per wave and tile
+    static constexpr int NW = (NS - 2) * CPW;               // copies still in flight when a tile is read
+    static_assert(NW < 64, "wait count");
+};
+
 template <typename E, int D1, int D2>
 __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
 {
-    constexpr int W = 4;
-    using QR = PadRows<D1>;
-    using OR = PadRows<D2>;
+    using C = DkvCfg<D1, D2>;
+    using QR = typename C::QR;
+    using OR = typename C::OR;
+    constexpr int W = C::W;
     constexpr int NKS = D1 / 16, NDS = D2 / 16, NDB1 = D1 / 32, NDB2 = D2 / 32;
-    constexpr int QSZ = QR::BUF, OSZ = OR::BUF;
-    // per wave: a query-row tile, a dout-row tile; reused at the end for the
-    // cross-wave sum (3 waves x 64 lanes x max(NDB1, NDB2) x 16 floats)
-    // Two slots per wave where the LDS allows it (the next tile's copies then
-    // overlap this tile's work), else one.
-    constexpr int NBUF = (2 * W * (QSZ + OSZ) * 2 <= 150 * 1024) ? 2 : 1;
-    constexpr int SMEL = NBUF * W * (QSZ + OSZ);
-    static_assert(SMEL * 2 >= 3 * 64 * (NDB1 > NDB2 ? NDB1 : NDB2) * 16 * 4, "reduction space");
-    __shared__ __attribute__((aligned(16))) uint16_t SM[SMEL];
-    __shared__ __attribute__((aligned(16))) float ST[W * 64];
+    // Five slot objects: the main loop walks them in a fixed order, so the
+    // compiler sees that a step's LDS reads and the copies it issues touch
+    // different objects and adds no wait of its own for the copies.
+    __shared__ __attribute__((aligned(16))) unsigned char SL0[C::SLOT_B], SL1[C::SLOT_B], SL2[C::SLOT_B],
+        SL3[C::SLOT_B], SL4[C::SLOT_B];
     if (*p.status != 0)
         return;   // the table failed the planner's checks
 
@@ -286,60 +310,92 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     const int l32 = lane & 31;
     const int hf = lane >> 5;
 
-    const int wg = blockIdx.x;
-    int b = 0;
-    {
-        int lo = 0, hi = p.B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.bt[mid].tile_off_k <= wg)
-                lo = mid;
-            else
-                hi = mid - 1;
-        }
-        b = lo;
-    }
-    const BatchEnt be = p.bt[b];
-    const int idx = wg - be.tile_off_k;
-    const int g = idx % p.N2;
-    const int i0 = (idx / p.N2) * 32;                  // first entry of the tile (local)
+    const BwdItem it = p.items[blockIdx.x];
+    const BatchEnt be = p.bt[it.b];
+    const int g = it.g;
     const int G = p.G;
-    const int key = i0 + l32;
+    const int key0 = it.kb * C::KB + wave * 32;     // the wave's first key (local)
+    const int key = key0 + l32;
     const bool kvalid = key < be.n_cmp;
+    const bool wave_has_keys = key0 < be.n_cmp;
 
     // keys and values as B operands: lane l32 = entry, k-slots 8hf..8hf+7
     u32x4 kf[NKS], vf[NDS];
     {
-        const int64_t krow = ((int64_t)(be.cmp_off + (kvalid ? key : i0)) * p.N2 + g);
+        const int64_t krow = ((int64_t)(be.cmp_off + (kvalid ? key : it.kb * C::KB)) * p.N2 + g);
+        // S = (-q) k = q (-k): a negative scale negates the keys here and
+        // leaves the query tiles as they are (dK needs the true q)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            kf[ks] = *(const u32x4*)(p.kc + krow * D1 + ks * 16 + hf * 8);
+            kf[ks] = *(const u32x4*)(p.kc + krow * D1 + ks * 16 + hf * 8) ^ p.qsign;
 #pragma unroll
         for (int ks = 0; ks < NDS; ++ks)
             vf[ks] = *(const u32x4*)(p.vc + krow * D2 + ks * 16 + hf * 8);
     }
-    // first row (t*G + hh) that sees this lane's entry: the query's
-    // position pos_off + t >= key*d + l - 1
+    // query rows r = t*G + hh (local token t at position pos_off + t): the
+    // first row that sees this lane's key, the first that sees the wave's
+    // first key, the first that sees all 32 of them, and the first that
+    // sees the block's first key
     const int key_first_row = (key * p.d + p.l - 1 - be.pos_off) * G;
-
-    // query rows r = t*G + hh seeing the tile's first entry
+    const int wave_first_row = (key0 * p.d + p.l - 1 - be.pos_off) * G;
+    const int wave_full_row = key0 + 32 <= be.n_cmp ? ((key0 + 31) * p.d + p.l - 1 - be.pos_off) * G : INT_MAX;
     const int rows_total = be.T * G;
-    const int r_first = min(max(i0 * p.d + p.l - 1 - be.pos_off, 0), be.T) * G;
-    const int n_qt = (rows_total - r_first + 31) / 32;
+    const int r_first = min(max(it.kb * C::KB * p.d + p.l - 1 - be.pos_off, 0), be.T) * G;
 
-    auto qs_at = [&](int slot) { return SM + (slot * W + wave) * QSZ; };
-    auto os_at = [&](int slot) { return SM + NBUF * W * QSZ + (slot * W + wave) * OSZ; };
-    float* st = ST + wave * 64;
-    // byte offsets inside the sequence's query rows: row r -> ((t*N1 + g*G + hh) * D) * 2
     const uint16_t* qseq = p.q + (int64_t)be.q_off * p.N1 * D1;
     const uint16_t* oseq = p.dout + (int64_t)be.q_off * p.N1 * D2;
+    const float* sseq = p.rowstat + (int64_t)be.q_off * p.N1 * 2;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(qseq, (uint32_t)((int64_t)be.T * p.N1 * D1 * 2));
     const __amdgpu_buffer_rsrc_t ors = make_rsrc(oseq, (uint32_t)((int64_t)be.T * p.N1 * D2 * 2));
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(sseq, (uint32_t)((int64_t)be.T * p.N1 * 2 * 4));
     // element row of sequence row rr = t*G + hh: t*N1 + g*G + hh (t = rr / G
-    // by a multiply-high with the host's magic number for G)
-    auto row_elem = [&](int rr) -> int64_t {
-        const int t = (int)(((uint64_t)__umulhi((uint32_t)rr, p.gdiv_m) + (uint32_t)rr) >> p.gdiv_s);
-        return (int64_t)t * p.N1 + (int64_t)g * G + (rr - t * G);
+    // by a multiply-high with the host's magic number for G); the sequence's
+    // rows span less than 4 GiB, so 32-bit byte offsets hold
+    const uint32_t gG = (uint32_t)(g * G);
+    auto row_elem = [&](int rr) -> uint32_t {
+        const uint32_t t = (uint32_t)(((uint64_t)__umulhi((uint32_t)rr, p.gdiv_m) + (uint32_t)rr) >> p.gdiv_s);
+        return t * (uint32_t)p.N1 + gG + ((uint32_t)rr - t * (uint32_t)G);
+    };
+
+    // Copies of tile tt (of the item) into a slot: every wave issues the same
+    // number of copy instructions (slack ones point past the buffers and land
+    // zeros in the slot's slack), so one immediate wait count fits all; tiles
+    // past the item's end are copied as zeros for the same reason.
+    auto issue = [&](int tt, unsigned char* slot) __attribute__((always_inline)) {
+        const int r0 = r_first + 32 * (it.qt0 + tt);
+        const bool live = tt < it.n_qt;
+        uint16_t* qd = (uint16_t*)slot;
+        uint16_t* od = (uint16_t*)slot + C::QSZ;
+        float* sd = (float*)(slot + (C::QSZ + C::OSZ) * 2);
+#pragma unroll
+        for (int q = 0; q < C::QIW; ++q) {
+            const int ins = q * W + wave;
+            const int sl = ins * 64 + lane;
+            const int rr = sl / (QR::CH + 1), ch = sl % (QR::CH + 1);
+            const bool ok = live && ins < QR::INS && ch < QR::CH && rr < 32 && r0 + rr < rows_total;
+            const uint32_t off = row_elem(r0 + min(rr, 31)) * (uint32_t)(D1 * 2) + (uint32_t)ch * 16u;
+            copy16_to_lds(qrs, qd + ins * 512, ok ? off : 0xFFFFFFF0u);
+        }
+#pragma unroll
+        for (int q = 0; q < C::OIW; ++q) {
+            const int ins = q * W + wave;
+            const int sl = ins * 64 + lane;
+            const int rr = sl / (OR::CH + 1), ch = sl % (OR::CH + 1);
+            const bool ok = live && ins < OR::INS && ch < OR::CH && rr < 32 && r0 + rr < rows_total;
+            const uint32_t off = row_elem(r0 + min(rr, 31)) * (uint32_t)(D2 * 2) + (uint32_t)ch * 16u;
+            copy16_to_lds(ors, od + ins * 512, ok ? off : 0xFFFFFFF0u);
+        }
+        // rows 8*wave .. 8*wave+7: lane i < 16 copies float i%2 (bias, Delta)
+        // of row 8*wave + i/2 to sd[16*wave + i]; the other lanes stay
+        // inactive (a lane whose load falls outside the buffer still writes
+        // its zero, and lanes 16.. would land on the other waves' rows)
+        if (lane < 16) {
+            const int rr = 8 * wave + (lane >> 1);
+            const bool ok = live && r0 + rr < rows_total;
+            const uint32_t off = (row_elem(r0 + rr) * 2u + (uint32_t)(lane & 1)) * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)(sd + 16 * wave), 4, ok ? off : 0xFFFFFFF0u,
+                                                     0, 0, 0);
+        }
     };
 
     f32x16 dka[NDB1], dva[NDB2];
@@ -362,58 +418,23 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         otr[db] = tr_off<OR::S>(lane, db * 32);
     const float c = p.c;
 
-    // Tile qt's copies: the rows' bias and Delta into registers (lanes < 32),
-    // then the query and dout rows (rows past the sequence load 0).
-    float stb = INFINITY, stq = 0.f;
-    auto issue = [&](int qt, int slot) __attribute__((always_inline)) {
-        const int r0 = r_first + qt * 32;
-        if (lane < 32) {
-            const bool ok = r0 + lane < rows_total;
-            const int64_t grow = ok ? (int64_t)be.q_off * p.N1 + row_elem(r0 + lane) : 0;
-            stb = ok ? p.rowstat[grow * 2] : INFINITY;
-            stq = ok ? p.rowstat[grow * 2 + 1] : 0.f;
-        }
-        uint16_t* qd = qs_at(slot);
-        uint16_t* od = os_at(slot);
-#pragma unroll
-        for (int q = 0; q < QR::INS; ++q) {
-            const int sl = q * 64 + lane;
-            const int rr = sl / (QR::CH + 1), ch = sl % (QR::CH + 1);
-            const bool ok = ch < QR::CH && rr < 32 && r0 + rr < rows_total;
-            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D1 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
-            copy16_to_lds(qrs, qd + q * 512, off);
-        }
-#pragma unroll
-        for (int q = 0; q < OR::INS; ++q) {
-            const int sl = q * 64 + lane;
-            const int rr = sl / (OR::CH + 1), ch = sl % (OR::CH + 1);
-            const bool ok = ch < OR::CH && rr < 32 && r0 + rr < rows_total;
-            const uint32_t off = ok ? (uint32_t)(row_elem(r0 + rr) * D2 * 2) + (uint32_t)ch * 16u : 0xFFFFFFF0u;
-            copy16_to_lds(ors, od + q * 512, off);
-        }
-    };
-
-    int slot = 0;
-    if (wave < n_qt)
-        issue(wave, 0);
-    for (int qt = wave; qt < n_qt; qt += W) {
-        const int r0 = r_first + qt * 32;
-        __builtin_amdgcn_s_waitcnt(0x0070);         // tile qt's copies and loads are done
+    // Step tt: wait until tile tt's copies have landed (the NS - 2 later
+    // tiles may still be in flight) and this wave's LDS reads of the previous
+    // tile are done; after the barrier every wave's copies are visible and
+    // every wave is done with the slot the next copy overwrites.
+    auto step = [&](int tt, const unsigned char* rd, unsigned char* cp) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt((C::NW & 15) | ((C::NW >> 4) << 14) | 0x0070);
         __asm__ volatile("" ::: "memory");
-        if (lane < 32) {
-            st[lane] = stb;
-            st[32 + lane] = stq;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const uint16_t* qs = qs_at(slot);
-        const uint16_t* os = os_at(slot);
-        if constexpr (NBUF == 2) {
-            if (qt + W < n_qt)
-                issue(qt + W, slot ^ 1);            // the other slot's tile is done
-        }
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        issue(tt + C::NS - 1, cp);
 
+        const int r0 = r_first + 32 * (it.qt0 + tt);
+        if (!wave_has_keys || r0 + 31 < wave_first_row)
+            return;                                  // no row of the tile sees a key of this wave
+        const uint16_t* qs = (const uint16_t*)rd;
+        const uint16_t* os = (const uint16_t*)rd + C::QSZ;
+        const float* st = (const float*)(rd + (C::QSZ + C::OSZ) * 2);
         // S = Q K^T, dP = dO V^T: rows = queries 8*(x/4) + 4*hf + x%4, lane = entry
         f32x16 s, dp;
 #pragma unroll
@@ -423,31 +444,45 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            s = E::mfma(*(const u32x4*)&qs[l32 * QR::S + ks * 16 + hf * 8] ^ p.qsign, kf[ks], s);
+            s = E::mfma(*(const u32x4*)&qs[l32 * QR::S + ks * 16 + hf * 8], kf[ks], s);
 #pragma unroll
         for (int ks = 0; ks < NDS; ++ks)
             dp = E::mfma(*(const u32x4*)&os[l32 * OR::S + ks * 16 + hf * 8], vf[ks], dp);
+        // P and dS; the visibility test only where a row of the tile misses
+        // a key of the wave or lies past the sequence
         u32x4 pf[2], dsf[2];
+        auto p_ds = [&](auto mask_tag) __attribute__((always_inline)) {
+            constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int qr0 = 8 * r4 + 4 * hf;             // first of 4 consecutive rows
-            const f32x4 bias4 = *(const f32x4*)&st[qr0];
-            const f32x4 del4 = *(const f32x4*)&st[32 + qr0];
-            float pv[4], dv[4];
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int qr0 = 8 * r4 + 4 * hf;             // first of 4 consecutive rows
+                const f32x4 sa = *(const f32x4*)&st[2 * qr0];        // bias, Delta of rows qr0, qr0 + 1
+                const f32x4 sb = *(const f32x4*)&st[2 * qr0 + 4];    // ... of rows qr0 + 2, qr0 + 3
+                const float bias4[4] = {sa[0], sa[2], sb[0], sb[2]};
+                const float del4[4] = {sa[1], sa[3], sb[1], sb[3]};
+                float pv[4], dv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int x = 4 * r4 + e;
-                const bool vis = kvalid && key_first_row <= r0 + qr0 + e;
-                const float pr = vis ? fast_exp2(fmaf(s[x], c, -bias4[e])) : 0.f;
-                pv[e] = pr;
-                dv[e] = pr * (dp[x] - del4[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int x = 4 * r4 + e;
+                    float pr = fast_exp2(fmaf(s[x], c, -bias4[e]));
+                    if constexpr (MASK) {
+                        const int row = r0 + qr0 + e;
+                        pr = (kvalid && key_first_row <= row && row < rows_total) ? pr : 0.f;
+                    }
+                    pv[e] = pr;
+                    dv[e] = pr * (dp[x] - del4[e]);
+                }
+                const int kk = r4 >> 1, q2 = (r4 & 1) * 2;
+                pf[kk][q2] = E::pack2(pv[0], pv[1]);
+                pf[kk][q2 + 1] = E::pack2(pv[2], pv[3]);
+                dsf[kk][q2] = E::pack2(dv[0], dv[1]);
+                dsf[kk][q2 + 1] = E::pack2(dv[2], dv[3]);
             }
-            const int kk = r4 >> 1, q2 = (r4 & 1) * 2;
-            pf[kk][q2] = E::pack2(pv[0], pv[1]);
-            pf[kk][q2 + 1] = E::pack2(pv[2], pv[3]);
-            dsf[kk][q2] = E::pack2(dv[0], dv[1]);
-            dsf[kk][q2 + 1] = E::pack2(dv[2], dv[3]);
-        }
+        };
+        if (r0 >= wave_full_row && r0 + 32 <= rows_total)
+            p_ds(std::false_type{});
+        else
+            p_ds(std::true_type{});
         // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the row tiles)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -458,58 +493,89 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
             for (int db = 0; db < NDB1; ++db)   // the true q: dkc = scale * sum dS q
                 dka[db] = E::mfma(tr_read(&qs[qtr[db] + kk * 16 * QR::S], QR::S), dsf[kk], dka[db]);
         }
-        __asm__ volatile("" ::: "memory");          // later copies stay after these reads
-        if constexpr (NBUF == 1) {
-            if (qt + W < n_qt)
-                issue(qt + W, 0);
-        } else {
-            slot ^= 1;
-        }
-    }
-
-    // Fixed-order sum of the four waves' partial sums: waves 1-3 park theirs
-    // in LDS, wave 0 adds them in wave order and stores (lane = entry, 4
-    // consecutive dims per register quad).
-    float* red = (float*)SM;                         // [3][64 lanes][NDB * 16]
-    auto reduce_store = [&](auto& acc, auto nb_tag, float* dst_base, int dcols, float mul) __attribute__((always_inline)) {
-        constexpr int NB = decltype(nb_tag)::value;
-        __syncthreads();
-        if (wave > 0) {
-#pragma unroll
-            for (int db = 0; db < NB; ++db)
-#pragma unroll
-                for (int x = 0; x < 16; x += 4)
-                    *(f32x4*)&red[(((wave - 1) * 64 + lane) * NB + db) * 16 + x] =
-                        f32x4{acc[db][x], acc[db][x + 1], acc[db][x + 2], acc[db][x + 3]};
-        }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int w = 0; w < W - 1; ++w)
-#pragma unroll
-                for (int db = 0; db < NB; ++db)
-#pragma unroll
-                    for (int x = 0; x < 16; x += 4) {
-                        const f32x4 v = *(const f32x4*)&red[((w * 64 + lane) * NB + db) * 16 + x];
-                        acc[db][x] += v[0];
-                        acc[db][x + 1] += v[1];
-                        acc[db][x + 2] += v[2];
-                        acc[db][x + 3] += v[3];
-                    }
-            if (kvalid) {
-                float* dst = dst_base + ((int64_t)(be.cmp_off + key) * p.N2 + g) * dcols;
-#pragma unroll
-                for (int db = 0; db < NB; ++db)
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4)
-                        *(f32x4*)(dst + db * 32 + 8 * r4 + 4 * hf) =
-                            f32x4{acc[db][4 * r4] * mul, acc[db][4 * r4 + 1] * mul,
-                                  acc[db][4 * r4 + 2] * mul, acc[db][4 * r4 + 3] * mul};
-            }
-        }
     };
-    reduce_store(dka, std::integral_constant<int, NDB1>{}, p.dkc, D1, p.scale);
-    reduce_store(dva, std::integral_constant<int, NDB2>{}, p.dvc, D2, 1.f);
+
+    // tile tt lives in slot tt % 5; step tt refills the slot step tt - 1 read
+    issue(0, SL0);
+    issue(1, SL1);
+    issue(2, SL2);
+    issue(3, SL3);
+    for (int tt = 0; tt < it.n_qt; tt += 5) {
+        step(tt, SL0, SL4);
+        if (tt + 1 >= it.n_qt)
+            break;
+        step(tt + 1, SL1, SL0);
+        if (tt + 2 >= it.n_qt)
+            break;
+        step(tt + 2, SL2, SL1);
+        if (tt + 3 >= it.n_qt)
+            break;
+        step(tt + 3, SL3, SL2);
+        if (tt + 4 >= it.n_qt)
+            break;
+        step(tt + 4, SL4, SL3);
+    }
+    // the copies of the tiles past the end (zeros) land before the
+    // workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0070);
+
+    // lane = key, 4 consecutive dims per register quad
+    auto store = [&](auto& acc, auto nb_tag, float* dst, float mul) __attribute__((always_inline)) {
+        constexpr int NB = decltype(nb_tag)::value;
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4)
+                *(f32x4*)(dst + db * 32 + 8 * r4 + 4 * hf) =
+                    f32x4{acc[db][4 * r4] * mul, acc[db][4 * r4 + 1] * mul, acc[db][4 * r4 + 2] * mul,
+                          acc[db][4 * r4 + 3] * mul};
+    };
+    if (it.slot < 0) {
+        if (kvalid) {
+            const int64_t krow = (int64_t)(be.cmp_off + key) * p.N2 + g;
+            store(dka, std::integral_constant<int, NDB1>{}, p.dkc + krow * D1, p.scale);
+            store(dva, std::integral_constant<int, NDB2>{}, p.dvc + krow * D2, 1.f);
+        }
+    } else {
+        float* dst = p.part + ((int64_t)it.slot * C::KB + wave * 32 + l32) * (D1 + D2);
+        store(dka, std::integral_constant<int, NDB1>{}, dst, 1.f);
+        store(dva, std::integral_constant<int, NDB2>{}, dst + D1, 1.f);
+    }
+}
+
+// Key blocks cut into pieces: per entry and dim, the pieces' partial sums
+// added in piece order (bitwise repeatable), dK scaled, then stored.
+template <int D1, int D2>
+__global__ __launch_bounds__(256) void k_cmp_attn_bwd_combine(BwdParams p)
+{
+    if (*p.status != 0)
+        return;
+    const CombineItem it = p.combs[blockIdx.x];
+    const BatchEnt be = p.bt[it.b];
+    constexpr int DC = D1 + D2;
+    constexpr int Q4 = DC / 4;
+    const int64_t piece = (int64_t)kBwdKeyBlock * DC;
+    for (int u = threadIdx.x; u < kBwdKeyBlock * Q4; u += 256) {
+        const int kl = u / Q4, e = (u - kl * Q4) * 4;
+        const int key = it.rb * kBwdKeyBlock + kl;
+        if (key >= be.n_cmp)
+            continue;
+        const float* src = p.part + ((int64_t)it.slot0 * kBwdKeyBlock + kl) * DC + e;
+        f32x4 acc = *(const f32x4*)src;
+        for (int s = 1; s < it.n; ++s) {
+            const f32x4 v = *(const f32x4*)(src + s * piece);
+            acc[0] += v[0];
+            acc[1] += v[1];
+            acc[2] += v[2];
+            acc[3] += v[3];
+        }
+        const int64_t krow = (int64_t)(be.cmp_off + key) * p.N2 + it.g;
+        if (e < D1)
+            *(f32x4*)(p.dkc + krow * D1 + e) = f32x4{acc[0] * p.scale, acc[1] * p.scale, acc[2] * p.scale,
+                                                     acc[3] * p.scale};
+        else
+            *(f32x4*)(p.dvc + krow * D2 + (e - D1)) = acc;
+    }
 }
 
 #define NSA_BWD_CONFIGS(X) X(64, 64) X(128, 64) X(128, 128) X(192, 64) X(192, 128)
@@ -523,29 +589,31 @@ bool attn_bwd_supported(int d1, int d2)
 }
 
 template <typename E>
-static hipError_t launch_bwd_typed(int d1, int d2, const BwdParams& p, int tiles_q, int tiles_k,
+static hipError_t launch_bwd_typed(int d1, int d2, const BwdParams& p, int tiles_q, int n_items, int n_combs,
                                    hipStream_t stream)
 {
-#define X(a, b_)                                                                                    \
-    if (d1 == a && d2 == b_) {                                                                      \
-        if (tiles_q > 0)                                                                            \
-            hipLaunchKernelGGL((k_cmp_attn_bwd_dq<E, a, b_>), dim3(tiles_q), dim3(256), 0, stream, p); \
-        if (tiles_k > 0)                                                                            \
-            hipLaunchKernelGGL((k_cmp_attn_bwd_dkv<E, a, b_>), dim3(tiles_k), dim3(256), 0, stream, p); \
-        return hipGetLastError();                                                                   \
+#define X(a, b_)                                                                                      \
+    if (d1 == a && d2 == b_) {                                                                        \
+        if (tiles_q > 0)                                                                              \
+            hipLaunchKernelGGL((k_cmp_attn_bwd_dq<E, a, b_>), dim3(tiles_q), dim3(256), 0, stream, p);   \
+        if (n_items > 0)                                                                              \
+            hipLaunchKernelGGL((k_cmp_attn_bwd_dkv<E, a, b_>), dim3(n_items), dim3(256), 0, stream, p);  \
+        if (n_combs > 0)                                                                              \
+            hipLaunchKernelGGL((k_cmp_attn_bwd_combine<a, b_>), dim3(n_combs), dim3(256), 0, stream, p); \
+        return hipGetLastError();                                                                     \
     }
     NSA_BWD_CONFIGS(X)
 #undef X
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_bwd(int dtype, int d1, int d2, const BwdParams& p, int tiles_q, int tiles_k,
+hipError_t launch_attn_bwd(int dtype, int d1, int d2, const BwdParams& p, int tiles_q, int n_items, int n_combs,
                            hipStream_t stream)
 {
     if (dtype == ElemBf16::code)
-        return launch_bwd_typed<ElemBf16>(d1, d2, p, tiles_q, tiles_k, stream);
+        return launch_bwd_typed<ElemBf16>(d1, d2, p, tiles_q, n_items, n_combs, stream);
     if (dtype == ElemF16::code)
-        return launch_bwd_typed<ElemF16>(d1, d2, p, tiles_q, tiles_k, stream);
+        return launch_bwd_typed<ElemF16>(d1, d2, p, tiles_q, n_items, n_combs, stream);
     return hipErrorInvalidValue;
 }
 

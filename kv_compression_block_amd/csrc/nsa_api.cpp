@@ -85,7 +85,9 @@ struct nsa_plan_s {
     int64_t vis_words, cand_words;    // packed mask row lengths (32-bit words)
     size_t ws_masked_bytes;           // workspace of the calls that take masks
     size_t ws_bwd_bytes;              // workspace of the backward call
-    int64_t tiles_k;                  // workgroups of the key-side backward kernel
+    int64_t tiles_k;                  // key blocks of the key-side backward (all KV heads)
+    int64_t bwd_qmax;                 // query tiles per key-side work item, at most
+    int64_t bwd_items, bwd_combs, bwd_slots;   // the key-side work list's counts
     int log2gp, topk_waves, topk_kbufs, sb;
     size_t topk_lds;
     int64_t tiles_a, tiles_c, tiles_s;
@@ -204,6 +206,71 @@ nsa_status nsa_compress(const void* input, const void* weight, const int64_t* ac
             return fail(NSA_ERR_HIP, "compress launch failed: %s", hipGetErrorString(e));
     }
     return ok();
+}
+
+// Query tiles (32 rows t*G + hh) that see key block kb of a sequence: from
+// the row of the block's first entry to the end of the sequence.
+static int64_t bwd_tiles_of(const nsa::BatchEnt& e, int64_t kb, int64_t G, int64_t l, int64_t d)
+{
+    const int64_t first = std::min<int64_t>(std::max<int64_t>(kb * nsa::kBwdKeyBlock * d + l - 1 - e.pos_off, 0), e.T) * G;
+    return ((int64_t)e.T * G - first + 31) / 32;
+}
+
+// Key-side backward work list: every key block (per KV head) is cut into
+// ceil(n / qmax) pieces of its n query tiles, qmax chosen so that the list
+// holds about 2048 items (eight per compute unit) however long the sequences
+// are, and no fewer than 16 tiles per item.  The list is built on the device
+// (launch_bwd_plan); these counts size the workspace and the launches.
+static void bwd_counts(nsa_plan_s* plan)
+{
+    const int64_t G = plan->N1 / plan->N2;
+    int64_t total = 0;
+    for (int64_t b = 0; b < plan->B; ++b) {
+        const nsa::BatchEnt& e = plan->table[(size_t)b];
+        const int64_t nkb = (e.n_cmp + nsa::kBwdKeyBlock - 1) / nsa::kBwdKeyBlock;
+        for (int64_t kb = 0; kb < nkb; ++kb)
+            total += bwd_tiles_of(e, kb, G, plan->l, plan->d);
+    }
+    total *= plan->N2;
+    const int64_t qmax = std::max<int64_t>(16, (total + 2047) / 2048);
+    int64_t items = 0, combs = 0, slots = 0;
+    for (int64_t b = 0; b < plan->B; ++b) {
+        const nsa::BatchEnt& e = plan->table[(size_t)b];
+        const int64_t nkb = (e.n_cmp + nsa::kBwdKeyBlock - 1) / nsa::kBwdKeyBlock;
+        for (int64_t kb = 0; kb < nkb; ++kb) {
+            const int64_t n = bwd_tiles_of(e, kb, G, plan->l, plan->d);
+            const int64_t pieces = n > qmax ? (n + qmax - 1) / qmax : 1;
+            items += pieces;
+            if (pieces > 1) {
+                combs += 1;
+                slots += pieces;
+            }
+        }
+    }
+    plan->bwd_qmax = qmax;
+    plan->bwd_items = items * plan->N2;
+    plan->bwd_combs = combs * plan->N2;
+    plan->bwd_slots = slots * plan->N2;
+}
+
+// Backward workspace after the table: each row's exponent bias and Delta,
+// the work-list build's chunk totals, the work list, its combine items, and
+// the partial dK, dV of the pieces.
+struct BwdLayout {
+    size_t rowstat_off, chunk_off, items_off, combs_off, part_off, bytes;
+};
+
+static BwdLayout bwd_layout(const nsa_plan_s* plan)
+{
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    BwdLayout k;
+    k.rowstat_off = plan->ws_bytes;
+    k.chunk_off = k.rowstat_off + up((size_t)plan->T1 * (size_t)plan->N1 * 8);
+    k.items_off = k.chunk_off + up((size_t)nsa::plan_chunks(plan->tiles_k) * sizeof(int4));
+    k.combs_off = k.items_off + up((size_t)plan->bwd_items * sizeof(nsa::BwdItem));
+    k.part_off = k.combs_off + up((size_t)plan->bwd_combs * sizeof(nsa::CombineItem));
+    k.bytes = k.part_off + (size_t)plan->bwd_slots * nsa::kBwdKeyBlock * (size_t)(plan->D1 + plan->D2) * 4;
+    return k;
 }
 
 static nsa_status make_plan(
@@ -351,7 +418,7 @@ static nsa_status make_plan(
         e.tile_off_s = (int32_t)ts;
         ts += (int64_t)e.n_rb_s * kv_head_num;
         e.tile_off_k = (int32_t)tk;
-        tk += (clen[(size_t)b] + 31) / 32 * kv_head_num;
+        tk += (clen[(size_t)b] + nsa::kBwdKeyBlock - 1) / nsa::kBwdKeyBlock * kv_head_num;
         ta += (int64_t)e.n_rb_a * kv_head_num;
         tc += (int64_t)e.n_rb_c * kv_head_num;
         q_off += T;
@@ -383,7 +450,12 @@ static nsa_status make_plan(
     const size_t cand_bytes = ((size_t)T_max * (size_t)plan->cand_words * 4 + 255) / 256 * 256;
     const size_t span_bytes = ((size_t)T_max * 16 + 255) / 256 * 256;
     plan->ws_masked_bytes = plan->ws_bytes + vis_bytes + cand_bytes + span_bytes;
-    plan->ws_bwd_bytes = plan->ws_bytes + ((size_t)q_off * (size_t)head_num * 8 + 255) / 256 * 256;
+    bwd_counts(plan);
+    if (plan->bwd_items > INT32_MAX || plan->bwd_slots > INT32_MAX) {
+        delete plan;
+        return fail(NSA_ERR_UNSUPPORTED, "problem too large for one launch");
+    }
+    plan->ws_bwd_bytes = bwd_layout(plan).bytes;
     *workspace_bytes = plan->ws_bytes;
     *plan_out = plan;
     return ok();
@@ -595,8 +667,8 @@ nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const v
 // the attention kernel's row blocks in its own order (per sequence and KV
 // head, costliest first); a row block with n > C key tiles becomes
 // ceil(n / C) pieces, each with a partial slot, plus one combine item.  The
-// list itself is built on the device from the table (k_split_count /
-// k_split_fill); these host counts size the workspace and the launches, and
+// list itself is built on the device from the table (launch_split_plan);
+// these host counts size the workspace and the launches, and
 // the device checks its list against them.
 struct SplitCounts {
     int64_t items = 0, combs = 0, slots = 0;
@@ -626,7 +698,7 @@ SplitCounts split_counts(const nsa_plan_s* plan, int64_t C)
     }
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     k.chunk_off = plan->ws_bytes;
-    k.items_off = k.chunk_off + up((size_t)nsa::split_plan_chunks((int)plan->tiles_a) * sizeof(int4));
+    k.items_off = k.chunk_off + up((size_t)nsa::plan_chunks(plan->tiles_a) * sizeof(int4));
     k.combs_off = k.items_off + up((size_t)k.items * sizeof(nsa::SplitItem));
     k.part_off = k.combs_off + up((size_t)k.combs * sizeof(nsa::CombineItem));
     k.bytes = k.part_off + (size_t)k.slots * (size_t)rows_a * (size_t)(plan->D2 + 4) * 4;
@@ -1155,7 +1227,11 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
     a.dq = d_query;
     a.dkc = d_key;
     a.dvc = d_value;
-    a.rowstat = (float*)((char*)workspace + plan->ws_bytes);
+    const BwdLayout lay = bwd_layout(plan);
+    a.rowstat = (float*)((char*)workspace + lay.rowstat_off);
+    a.items = (const nsa::BwdItem*)((char*)workspace + lay.items_off);
+    a.combs = (const nsa::CombineItem*)((char*)workspace + lay.combs_off);
+    a.part = (float*)((char*)workspace + lay.part_off);
     a.bt = (const nsa::BatchEnt*)workspace;
     a.status = status_word(plan, workspace);
     a.B = (int)plan->B;
@@ -1176,8 +1252,27 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
         a.gdiv_s = sh;
         a.gdiv_m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << sh) - (uint64_t)a.G)) / (uint64_t)a.G + 1);
     }
-    hipError_t e = nsa::launch_attn_bwd(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a,
-                                        (int)plan->tiles_k, s);
+    nsa::BwdPlanParams bp;
+    std::memset(&bp, 0, sizeof bp);
+    bp.table = a.bt;
+    bp.status = (int*)a.status;
+    bp.chunk_tot = (int4*)((char*)workspace + lay.chunk_off);
+    bp.items = (nsa::BwdItem*)a.items;
+    bp.combs = (nsa::CombineItem*)a.combs;
+    bp.B = a.B;
+    bp.N2 = a.N2;
+    bp.G = a.G;
+    bp.l = a.l;
+    bp.d = a.d;
+    bp.qmax = (int)plan->bwd_qmax;
+    bp.tiles_k = (int)plan->tiles_k;
+    bp.n_items = plan->bwd_items;
+    bp.n_combs = plan->bwd_combs;
+    bp.n_slots = plan->bwd_slots;
+    hipError_t e = nsa::launch_bwd_plan(bp, s);
+    if (e == hipSuccess)
+        e = nsa::launch_attn_bwd(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a,
+                                 (int)plan->bwd_items, (int)plan->bwd_combs, s);
     if (e != hipSuccess)
         return fail(NSA_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return ok();

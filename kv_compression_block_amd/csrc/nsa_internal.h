@@ -23,7 +23,7 @@ struct BatchEnt {
     int32_t S_sel;      // select blocks of the sequence, ceil(T / l')
     int32_t tile_off_s; // first workgroup of the selected-block attention kernel
     int32_t n_rb_s;     // row blocks of the selected-block attention kernel (per KV head)
-    int32_t tile_off_k; // first workgroup of the key-side backward kernel (32 entries each, per KV head)
+    int32_t tile_off_k; // first key block (kBwdKeyBlock entries, per KV head) of the key-side backward
     int32_t pos_off;    // KV tokens before the first query token (chunked prefill; 0 otherwise)
     int32_t kv_off;     // first raw key/value token of the sequence (global; == q_off unless chunked)
     int32_t pad1, pad2;
@@ -41,7 +41,7 @@ constexpr int kMetaErrCmpLen = 4;     // compressed length != floor((Tkv - l)/d)
 constexpr int kMetaErrSelLen = 8;     // select length != ceil(Tkv / l')
 constexpr int kMetaErrCapacity = 16;  // a sequence exceeds the plan's longest / largest counts
 constexpr int kMetaErrTotals = 32;    // totals or launch sizes differ from the plan's
-constexpr int kMetaErrSplit = 64;     // the split work list differs from the host's counts
+constexpr int kMetaErrSplit = 64;     // a work list (split attention, key-side backward) differs from the host's counts
 
 // ---- planning on the device ----------------------------------------------------
 struct MetaParams {
@@ -158,7 +158,7 @@ struct SplitPlanParams {
     int B, N2, G, l, d, rows_a, C, tiles_a;
     int64_t n_items, n_combs, n_slots;   // the host's counts for this plan and C
 };
-int split_plan_chunks(int tiles_a);
+int plan_chunks(int64_t units);   // chunk totals a work-list build needs (int4 each)
 hipError_t launch_split_plan(const SplitPlanParams& p, hipStream_t stream);
 hipError_t launch_attn_combine(int dtype, int d1, int d2, const AttnParams& p, const CombineItem* items,
                                int n_items, hipStream_t stream);
@@ -229,6 +229,16 @@ hipError_t launch_sel_attn(int dtype, int d1, int d2, const SelParams& p, int n_
                            hipStream_t stream);
 
 // ---- backward of the compressed attention -------------------------------------
+constexpr int kBwdKeyBlock = 128;     // compressed entries per key-side work item (4 waves x 32)
+
+// One key-side work item: key block kb (entries kBwdKeyBlock*kb ...) of KV
+// head g of sequence b, query tiles [qt0, qt0 + n_qt) of the 32-row tiles
+// that see the block; slot < 0: the block's only item (writes dK, dV),
+// else its partial slot.
+struct BwdItem {
+    int32_t b, g, kb, qt0, n_qt, slot, pad0, pad1;
+};
+
 struct BwdParams {
     const uint16_t* q;     // [T1, N1, D1]
     const uint16_t* kc;    // [T2, N2, D1]
@@ -249,11 +259,27 @@ struct BwdParams {
     float scale;           // signed scale
     uint32_t qsign;        // 0x80008000 when scale < 0 (q negated), else 0
     uint32_t gdiv_m, gdiv_s;   // n / G = (umulhi(n, m) + n) >> s for 0 <= n < 2^31
+    const BwdItem* items;  // key-side work items
+    const CombineItem* combs;   // key blocks cut into pieces (rb = key block), added in piece order
+    float* part;           // [slots][kBwdKeyBlock][D1 + D2]: unscaled partial dK, dV
 };
 
+// Key-side work list, built on the device from the table: every key block
+// becomes ceil(n_qt / qmax) items (at least one).
+struct BwdPlanParams {
+    const BatchEnt* table;   // [B]
+    int* status;             // the table's status word (set on a count mismatch)
+    int4* chunk_tot;         // [chunks]: items, combine items, slots of each 256 key blocks
+    BwdItem* items;          // [n_items]
+    CombineItem* combs;      // [n_combs]
+    int B, N2, G, l, d, qmax, tiles_k;
+    int64_t n_items, n_combs, n_slots;   // the host's counts
+};
+hipError_t launch_bwd_plan(const BwdPlanParams& p, hipStream_t stream);
+
 bool attn_bwd_supported(int d1, int d2);
-hipError_t launch_attn_bwd(int dtype, int d1, int d2, const BwdParams& p, int tiles_q, int tiles_k,
-                           hipStream_t stream);
+hipError_t launch_attn_bwd(int dtype, int d1, int d2, const BwdParams& p, int tiles_q, int n_items,
+                           int n_combs, hipStream_t stream);
 
 constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)
 constexpr int kTopkRingDup = 4;        // ring slots repeated past its end (stencils of <= 5 taps)

@@ -15,12 +15,14 @@
 //     planner checks, and writes a status word next to the table.  Every
 //     kernel that reads the table exits at once when the word is not zero.
 //
-//   * k_split_count / k_split_fill -- the work list of a split attention
-//     launch, built from the table: every row block of the attention kernel
-//     becomes one piece, or ceil(n / C) pieces when it walks n > C key tiles.
-//     The pieces are numbered in row-block order by an exclusive prefix sum
-//     over chunks of 256 row blocks (the count kernel writes chunk totals,
-//     the fill kernel adds the totals of the chunks before its own).
+//   * k_list_count / k_list_fill -- work lists built from the table: for a
+//     split attention launch every row block of the attention kernel becomes
+//     one piece, or ceil(n / C) pieces when it walks n > C key tiles; for the
+//     key-side backward every key block becomes ceil(n / qmax) pieces of the
+//     n query tiles that see it.  The pieces are numbered in unit order by an
+//     exclusive prefix sum over chunks of 256 units (the count kernel writes
+//     chunk totals, the fill kernel adds the totals of the chunks before its
+//     own).
 #include "nsa_device.h"
 
 namespace nsa {
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_meta_table(MetaParams p)
         int64_t na = in ? ceil_div(T * p.G, p.rows_a) : 0;
         int64_t nt = in ? ceil_div(T * p.GP, p.rows_c) : 0;
         int64_t nsr = in ? ceil_div(T * p.G, p.rows_s) : 0;
-        int64_t nk = in ? ceil_div(nc, 32) : 0;
+        int64_t nk = in ? ceil_div(nc, kBwdKeyBlock) : 0;
         int64_t sv = in ? ns : 0;
         int64_t ea = na * p.N2, ec = nt * p.N2, es = nsr * p.N2, ek = nk * p.N2;
         const int64_t sum_a = block_exclusive_scan(sh, ea);
@@ -141,47 +143,108 @@ __global__ __launch_bounds__(kPlanThreads) void k_meta_table(MetaParams p)
     }
 }
 
-// Pieces of attention row block wg (the unsplit launch's workgroup wg).
-struct RowBlockSplit {
-    int b, g, rb, n_kt, pieces;
+// ---- work lists cut into pieces ------------------------------------------------
+// A unit (a row block of the attention kernel, or a key block of the
+// key-side backward) becomes one work item, or several pieces whose partial
+// results a combine item adds.  The count kernel writes the totals of each
+// chunk of 256 units; the fill kernel adds the totals of the chunks before
+// its own, numbers its units' items by an exclusive prefix sum and writes
+// them, and checks that the list ends where the host's counts say.
+struct UnitSplit {
+    int b, g, r, n, pieces;   // sequence, KV head, row or key block, tiles it walks, pieces
     bool split;
 };
 
-__device__ __forceinline__ RowBlockSplit split_of(const SplitPlanParams& p, int wg)
+__device__ __forceinline__ int last_le(const BatchEnt* t, int B, int u, int BatchEnt::*off)
 {
-    RowBlockSplit r;
-    int lo = 0, hi = p.B - 1;
+    int lo = 0, hi = B - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (p.table[mid].tile_off_a <= wg)
+        if (t[mid].*off <= u)
             lo = mid;
         else
             hi = mid - 1;
     }
-    const BatchEnt be = p.table[lo];
-    const int idx = wg - be.tile_off_a;
-    r.b = lo;
-    r.g = idx % p.N2;
-    r.rb = be.n_rb_a - 1 - idx / p.N2;
-    const int64_t rows = (int64_t)be.T * p.G;
-    const int64_t last_row = min((int64_t)(r.rb + 1) * p.rows_a, rows) - 1;
-    const int t = (int)(last_row / p.G) + be.pos_off;
-    const int nv = n_visible(t, p.l, p.d, be.n_cmp);
-    r.n_kt = (nv + kKeyTileMin - 1) / kKeyTileMin;
-    r.split = r.n_kt > p.C;
-    r.pieces = r.split ? (r.n_kt + p.C - 1) / p.C : 1;
-    return r;
+    return lo;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void k_split_count(SplitPlanParams p)
+// Split attention: row block wg of the unsplit launch walks n key tiles of
+// kKeyTileMin entries; pieces of C tiles when n > C.
+__device__ __forceinline__ int64_t units_of(const SplitPlanParams& p) { return p.tiles_a; }
+__device__ __forceinline__ UnitSplit unit_of(const SplitPlanParams& p, int wg)
+{
+    UnitSplit r;
+    const int b = last_le(p.table, p.B, wg, &BatchEnt::tile_off_a);
+    const BatchEnt be = p.table[b];
+    const int idx = wg - be.tile_off_a;
+    r.b = b;
+    r.g = idx % p.N2;
+    r.r = be.n_rb_a - 1 - idx / p.N2;
+    const int64_t rows = (int64_t)be.T * p.G;
+    const int64_t last_row = min((int64_t)(r.r + 1) * p.rows_a, rows) - 1;
+    const int t = (int)(last_row / p.G) + be.pos_off;
+    const int nv = n_visible(t, p.l, p.d, be.n_cmp);
+    r.n = (nv + kKeyTileMin - 1) / kKeyTileMin;
+    r.split = r.n > p.C;
+    r.pieces = r.split ? (r.n + p.C - 1) / p.C : 1;
+    return r;
+}
+__device__ __forceinline__ void write_unit(const SplitPlanParams& p, const UnitSplit& r, int64_t i0, int64_t c0,
+                                           int64_t s0)
+{
+    if (!r.split) {
+        p.items[i0] = SplitItem{r.b, r.g, r.r, 0, r.n, -1, 0, 0};
+        return;
+    }
+    for (int q = 0; q < r.pieces; ++q)
+        p.items[i0 + q] = SplitItem{r.b, r.g, r.r, q * p.C, min(p.C, r.n - q * p.C), (int)(s0 + q), 0, 0};
+    p.combs[c0] = CombineItem{r.b, r.g, r.r, (int)s0, r.pieces, 0, 0, 0};
+}
+
+// Key-side backward: key block kb (kBwdKeyBlock entries) of KV head g is
+// seen by the 32-row query tiles from the row of the block's first entry to
+// the end of the sequence; ceil(n / qmax) pieces of nearly equal length.
+__device__ __forceinline__ int64_t units_of(const BwdPlanParams& p) { return p.tiles_k; }
+__device__ __forceinline__ UnitSplit unit_of(const BwdPlanParams& p, int u)
+{
+    UnitSplit r;
+    const int b = last_le(p.table, p.B, u, &BatchEnt::tile_off_k);
+    const BatchEnt be = p.table[b];
+    const int idx = u - be.tile_off_k;
+    r.b = b;
+    r.g = idx % p.N2;
+    r.r = idx / p.N2;
+    const int64_t first = min(max((int64_t)r.r * kBwdKeyBlock * p.d + p.l - 1 - be.pos_off, (int64_t)0),
+                              (int64_t)be.T) * p.G;
+    r.n = (int)(((int64_t)be.T * p.G - first + 31) / 32);
+    r.pieces = r.n > p.qmax ? (r.n + p.qmax - 1) / p.qmax : 1;
+    r.split = r.pieces > 1;
+    return r;
+}
+__device__ __forceinline__ void write_unit(const BwdPlanParams& p, const UnitSplit& r, int64_t i0, int64_t c0,
+                                           int64_t s0)
+{
+    if (!r.split) {
+        p.items[i0] = BwdItem{r.b, r.g, r.r, 0, r.n, -1, 0, 0};
+        return;
+    }
+    for (int q = 0; q < r.pieces; ++q) {
+        const int a = (int)((int64_t)q * r.n / r.pieces), e = (int)((int64_t)(q + 1) * r.n / r.pieces);
+        p.items[i0 + q] = BwdItem{r.b, r.g, r.r, a, e - a, (int)(s0 + q), 0, 0};
+    }
+    p.combs[c0] = CombineItem{r.b, r.g, r.r, (int)s0, r.pieces, 0, 0, 0};
+}
+
+template <class P>
+__global__ __launch_bounds__(kPlanThreads) void k_list_count(P p)
 {
     __shared__ int64_t sh[kPlanThreads];
     if (*p.status != 0)
         return;
-    const int wg = blockIdx.x * kPlanThreads + threadIdx.x;
+    const int u = blockIdx.x * kPlanThreads + threadIdx.x;
     int64_t items = 0, combs = 0, slots = 0;
-    if (wg < p.tiles_a) {
-        const RowBlockSplit r = split_of(p, wg);
+    if (u < units_of(p)) {
+        const UnitSplit r = unit_of(p, u);
         items = r.pieces;
         combs = r.split ? 1 : 0;
         slots = r.split ? r.pieces : 0;
@@ -193,7 +256,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_split_count(SplitPlanParams p)
         p.chunk_tot[blockIdx.x] = make_int4((int)ti, (int)tcb, (int)tsl, 0);
 }
 
-__global__ __launch_bounds__(kPlanThreads) void k_split_fill(SplitPlanParams p)
+template <class P>
+__global__ __launch_bounds__(kPlanThreads) void k_list_fill(P p)
 {
     __shared__ int64_t sh[kPlanThreads];
     __shared__ int bad;
@@ -212,16 +276,17 @@ __global__ __launch_bounds__(kPlanThreads) void k_split_fill(SplitPlanParams p)
         bs += t.z;
     }
     int64_t x = bi;
-    bi = block_exclusive_scan(sh, x) ;   // sum over threads
+    bi = block_exclusive_scan(sh, x);   // sum over threads
     x = bc;
     bc = block_exclusive_scan(sh, x);
     x = bs;
     bs = block_exclusive_scan(sh, x);
-    const int wg = chunk * kPlanThreads + tid;
-    RowBlockSplit r{};
+    const int u = chunk * kPlanThreads + tid;
+    UnitSplit r{};
     int64_t items = 0, combs = 0, slots = 0;
-    if (wg < p.tiles_a) {
-        r = split_of(p, wg);
+    const bool in = u < units_of(p);
+    if (in) {
+        r = unit_of(p, u);
         items = r.pieces;
         combs = r.split ? 1 : 0;
         slots = r.split ? r.pieces : 0;
@@ -229,17 +294,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_split_fill(SplitPlanParams p)
     const int64_t ti = block_exclusive_scan(sh, items);
     const int64_t tcb = block_exclusive_scan(sh, combs);
     const int64_t tsl = block_exclusive_scan(sh, slots);
-    if (wg < p.tiles_a) {
+    if (in) {
         const int64_t i0 = bi + items, c0 = bc + combs, s0 = bs + slots;
-        if (i0 + r.pieces > p.n_items || (r.split && (c0 >= p.n_combs || s0 + r.pieces > p.n_slots))) {
+        if (i0 + r.pieces > p.n_items || (r.split && (c0 >= p.n_combs || s0 + r.pieces > p.n_slots)))
             atomicOr(&bad, 1);
-        } else if (!r.split) {
-            p.items[i0] = SplitItem{r.b, r.g, r.rb, 0, r.n_kt, -1, 0, 0};
-        } else {
-            for (int q = 0; q < r.pieces; ++q)
-                p.items[i0 + q] = SplitItem{r.b, r.g, r.rb, q * p.C, min(p.C, r.n_kt - q * p.C), (int)(s0 + q), 0, 0};
-            p.combs[c0] = CombineItem{r.b, r.g, r.rb, (int)s0, r.pieces, 0, 0, 0};
-        }
+        else
+            write_unit(p, r, i0, c0, s0);
     }
     __syncthreads();
     // The last chunk ends the list: its end must be the host's count.
@@ -248,25 +308,30 @@ __global__ __launch_bounds__(kPlanThreads) void k_split_fill(SplitPlanParams p)
         atomicOr(p.status, kMetaErrSplit);
 }
 
+template <class P>
+static hipError_t launch_list(const P& p, int64_t units, hipStream_t stream)
+{
+    const int chunks = plan_chunks(units);
+    if (chunks <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_list_count<P>, dim3(chunks), dim3(kPlanThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_list_fill<P>, dim3(chunks), dim3(kPlanThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_meta_table(const MetaParams& p, hipStream_t stream)
 {
     hipLaunchKernelGGL(k_meta_table, dim3(1), dim3(kPlanThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-int split_plan_chunks(int tiles_a) { return (tiles_a + kPlanThreads - 1) / kPlanThreads; }
+int plan_chunks(int64_t units) { return (int)((units + kPlanThreads - 1) / kPlanThreads); }
 
-hipError_t launch_split_plan(const SplitPlanParams& p, hipStream_t stream)
-{
-    const int chunks = split_plan_chunks(p.tiles_a);
-    if (chunks <= 0)
-        return hipSuccess;
-    hipLaunchKernelGGL(k_split_count, dim3(chunks), dim3(kPlanThreads), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(k_split_fill, dim3(chunks), dim3(kPlanThreads), 0, stream, p);
-    return hipGetLastError();
-}
+hipError_t launch_split_plan(const SplitPlanParams& p, hipStream_t stream) { return launch_list(p, p.tiles_a, stream); }
+
+hipError_t launch_bwd_plan(const BwdPlanParams& p, hipStream_t stream) { return launch_list(p, p.tiles_k, stream); }
 
 }  // namespace nsa

@@ -18,7 +18,6 @@
 // through LDS by buffer-unit copies of whole rows (16 bytes of padding per
 // row) and transposed reads (ds_read_b64_tr_b16) where an operand needs
 // the other orientation.
-#include <climits>
 #include <type_traits>
 
 #include "nsa_device.h"
@@ -334,11 +333,9 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     }
     // query rows r = t*G + hh (local token t at position pos_off + t): the
     // first row that sees this lane's key, the first that sees the wave's
-    // first key, the first that sees all 32 of them, and the first that
-    // sees the block's first key
+    // first key, and the first that sees the block's first key
     const int key_first_row = (key * p.d + p.l - 1 - be.pos_off) * G;
     const int wave_first_row = (key0 * p.d + p.l - 1 - be.pos_off) * G;
-    const int wave_full_row = key0 + 32 <= be.n_cmp ? ((key0 + 31) * p.d + p.l - 1 - be.pos_off) * G : INT_MAX;
     const int rows_total = be.T * G;
     const int r_first = min(max(it.kb * C::KB * p.d + p.l - 1 - be.pos_off, 0), be.T) * G;
 
@@ -435,63 +432,83 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         const uint16_t* qs = (const uint16_t*)rd;
         const uint16_t* os = (const uint16_t*)rd + C::QSZ;
         const float* st = (const float*)(rd + (C::QSZ + C::OSZ) * 2);
-        // S = Q K^T, dP = dO V^T: rows = queries 8*(x/4) + 4*hf + x%4, lane = entry
-        f32x16 s, dp;
+        // Four phases, each a run of MFMAs with the vector work that does
+        // not depend on them beside it:
+        //   1. S = Q K^T (rows = queries 8*(x/4) + 4*hf + x%4, lane = entry);
+        //   2. dP = dO V^T, beside P = exp2(S c - bias);
+        //   3. dV^T += dO^T P, beside dS = P (dP - Delta);
+        //   4. dK^T += Q^T dS.
+        // Only the causal test is needed for P: rows past the sequence were
+        // copied as zeros (q, dout, bias and Delta), which makes their dS and
+        // their dout rows zero, and keys past the block's entries are never
+        // stored.  Element x is row r0 + 8*(x/4) + 4*hf + x%4, visible iff
+        // that row >= key_first_row.
+        f32x16 sc, dp;
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-            s[x] = 0.f;
+            sc[x] = 0.f;
             dp[x] = 0.f;
+        }
+        f32x4 stv[8];   // (bias, Delta) of rows 8*r4 + 4*hf + {0, 1}, then {2, 3}
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            stv[2 * r4] = *(const f32x4*)&st[2 * (8 * r4 + 4 * hf)];
+            stv[2 * r4 + 1] = *(const f32x4*)&st[2 * (8 * r4 + 4 * hf) + 4];
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            s = E::mfma(*(const u32x4*)&qs[l32 * QR::S + ks * 16 + hf * 8], kf[ks], s);
+            sc = E::mfma(*(const u32x4*)&qs[l32 * QR::S + ks * 16 + hf * 8], kf[ks], sc);
+        __builtin_amdgcn_sched_barrier(0);
+        const int d0 = r0 + 4 * hf - key_first_row;
+        float pv[16];
+        u32x4 pf[2], dsf[2];
 #pragma unroll
         for (int ks = 0; ks < NDS; ++ks)
             dp = E::mfma(*(const u32x4*)&os[l32 * OR::S + ks * 16 + hf * 8], vf[ks], dp);
-        // P and dS; the visibility test only where a row of the tile misses
-        // a key of the wave or lies past the sequence
-        u32x4 pf[2], dsf[2];
-        auto p_ds = [&](auto mask_tag) __attribute__((always_inline)) {
-            constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int qr0 = 8 * r4 + 4 * hf;             // first of 4 consecutive rows
-                const f32x4 sa = *(const f32x4*)&st[2 * qr0];        // bias, Delta of rows qr0, qr0 + 1
-                const f32x4 sb = *(const f32x4*)&st[2 * qr0 + 4];    // ... of rows qr0 + 2, qr0 + 3
-                const float bias4[4] = {sa[0], sa[2], sb[0], sb[2]};
-                const float del4[4] = {sa[1], sa[3], sb[1], sb[3]};
-                float pv[4], dv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int x = 4 * r4 + e;
-                    float pr = fast_exp2(fmaf(s[x], c, -bias4[e]));
-                    if constexpr (MASK) {
-                        const int row = r0 + qr0 + e;
-                        pr = (kvalid && key_first_row <= row && row < rows_total) ? pr : 0.f;
-                    }
-                    pv[e] = pr;
-                    dv[e] = pr * (dp[x] - del4[e]);
-                }
-                const int kk = r4 >> 1, q2 = (r4 & 1) * 2;
-                pf[kk][q2] = E::pack2(pv[0], pv[1]);
-                pf[kk][q2 + 1] = E::pack2(pv[2], pv[3]);
-                dsf[kk][q2] = E::pack2(dv[0], dv[1]);
-                dsf[kk][q2 + 1] = E::pack2(dv[2], dv[3]);
-            }
+        for (int x = 0; x < 16; ++x) {
+            const int r4 = x >> 2, e = x & 3;
+            const float bias = stv[2 * r4 + (e >> 1)][(e & 1) * 2];
+            const float pr = fast_exp2(fmaf(sc[x], c, -bias));
+            pv[x] = d0 >= -(8 * r4 + e) ? pr : 0.f;
+            if (x & 1)
+                pf[r4 >> 1][(r4 & 1) * 2 + (e >> 1)] = E::pack2(pv[x - 1], pv[x]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Phases 3 and 4 as one run of 2*(NDB2 + NDB1) products: dV blocks
+        // (kk-major) then dK blocks, each operand read three products ahead
+        // of its use; the dS work sits beside the dV products.
+        constexpr int NGV = 2 * NDB2, NG = NGV + 2 * NDB1, PF = 3;
+        auto g_operand = [&](int m) __attribute__((always_inline)) -> u32x4 {
+            if (m < NGV)
+                return tr_read(&os[otr[m % NDB2] + (m / NDB2) * 16 * OR::S], OR::S);
+            const int j = m - NGV;
+            return tr_read(&qs[qtr[j % NDB1] + (j / NDB1) * 16 * QR::S], QR::S);
         };
-        if (r0 >= wave_full_row && r0 + 32 <= rows_total)
-            p_ds(std::false_type{});
-        else
-            p_ds(std::true_type{});
-        // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the row tiles)
+        u32x4 ga[NG];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int m = 0; m < PF; ++m)
+            ga[m] = g_operand(m);
 #pragma unroll
-            for (int db = 0; db < NDB2; ++db)
-                dva[db] = E::mfma(tr_read(&os[otr[db] + kk * 16 * OR::S], OR::S), pf[kk], dva[db]);
+        for (int m = 0; m < NG; ++m) {
+            if (m + PF < NG)
+                ga[m + PF] = g_operand(m + PF);
+            if (m < NGV) {
+                dva[m % NDB2] = E::mfma(ga[m], pf[m / NDB2], dva[m % NDB2]);
 #pragma unroll
-            for (int db = 0; db < NDB1; ++db)   // the true q: dkc = scale * sum dS q
-                dka[db] = E::mfma(tr_read(&qs[qtr[db] + kk * 16 * QR::S], QR::S), dsf[kk], dka[db]);
+                for (int x = 1; x < 16; x += 2) {
+                    if (((x >> 1) * NGV) / 8 != m)
+                        continue;
+                    const int r4 = x >> 2, e = x & 3;
+                    const f32x4& v = stv[2 * r4 + (e >> 1)];
+                    dsf[r4 >> 1][(r4 & 1) * 2 + (e >> 1)] =
+                        E::pack2(pv[x - 1] * (dp[x - 1] - v[1]), pv[x] * (dp[x] - v[3]));
+                }
+            } else {   // the true q: dkc = scale * sum dS q
+                const int j = m - NGV;
+                dka[j % NDB1] = E::mfma(ga[m], dsf[j / NDB1], dka[j % NDB1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 

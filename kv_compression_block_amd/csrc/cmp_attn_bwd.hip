@@ -56,6 +56,18 @@ __device__ __forceinline__ u32x4 tr_read(const uint16_t* base, int S)
     return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Buffer-to-LDS copies with a per-lane offset and a wave-uniform one:
+// lane i's 16 (or 4) bytes land at lds + 16 i (4 i).
+__device__ __forceinline__ void copy16_to_lds_so(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void copy4_to_lds_so(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
+
 }  // namespace
 
 // ---- query side: dq -----------------------------------------------------------
@@ -355,15 +367,61 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     };
 
     // Copies of tile tt (of the item) into a slot: every wave issues the same
-    // number of copy instructions (slack ones point past the buffers and land
-    // zeros in the slot's slack), so one immediate wait count fits all; tiles
-    // past the item's end are copied as zeros for the same reason.
+    // number of copy instructions (slack ones land in the slot's slack), so
+    // one immediate wait count fits all.  Lane (ins, lane) of a copy
+    // instruction always fills row rr, chunk ch of the tile (or a pad or
+    // slack position, never read).
+    //
+    // When G divides 32 or 32 divides G (the common head ratios), the
+    // element row of tile row rr is u(r0) + L(rr) with
+    //   u(r0) = (r0 / G) * N1 + g*G + r0 % G,  L(rr) = (rr / G) * N1 + rr % G
+    // (r0, a multiple of 32 past the first row of a token, never splits a
+    // tile across a token boundary when 32 divides G), so each lane's byte
+    // offset is a constant and the tile a scalar offset: no vector work per
+    // copy.  Rows past the sequence fall past the buffer and land as zeros;
+    // tiles past the item load whatever they hold (they are never read).
+    // Other ratios take the per-lane division, and rows past the sequence or
+    // the item are pointed past the buffer.
+    const bool affine = (G % 32 == 0) || (32 % G == 0);
+    uint32_t qv[C::QIW], ov[C::OIW], sv;
+    auto lane_row = [&](int rr) -> uint32_t { return (uint32_t)((rr / G) * p.N1 + rr % G); };
+#pragma unroll
+    for (int q = 0; q < C::QIW; ++q) {
+        const int ins = q * W + wave, sl = ins * 64 + lane;
+        const int rr = sl / (QR::CH + 1), ch = sl % (QR::CH + 1);
+        const bool ok = ins < QR::INS && ch < QR::CH && rr < 32;
+        qv[q] = ok ? lane_row(rr) * (uint32_t)(D1 * 2) + (uint32_t)ch * 16u : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < C::OIW; ++q) {
+        const int ins = q * W + wave, sl = ins * 64 + lane;
+        const int rr = sl / (OR::CH + 1), ch = sl % (OR::CH + 1);
+        const bool ok = ins < OR::INS && ch < OR::CH && rr < 32;
+        ov[q] = ok ? lane_row(rr) * (uint32_t)(D2 * 2) + (uint32_t)ch * 16u : 0u;
+    }
+    sv = (lane_row(8 * wave + ((lane & 15) >> 1)) * 2u + (uint32_t)(lane & 1)) * 4u;
     auto issue = [&](int tt, unsigned char* slot) __attribute__((always_inline)) {
         const int r0 = r_first + 32 * (it.qt0 + tt);
-        const bool live = tt < it.n_qt;
         uint16_t* qd = (uint16_t*)slot;
         uint16_t* od = (uint16_t*)slot + C::QSZ;
         float* sd = (float*)(slot + (C::QSZ + C::OSZ) * 2);
+        if (affine) {
+            const uint32_t t0 = (uint32_t)(((uint64_t)__umulhi((uint32_t)r0, p.gdiv_m) + (uint32_t)r0) >> p.gdiv_s);
+            const uint32_t u = t0 * (uint32_t)p.N1 + gG + ((uint32_t)r0 - t0 * (uint32_t)G);
+#pragma unroll
+            for (int q = 0; q < C::QIW; ++q)
+                copy16_to_lds_so(qrs, qd + (q * W + wave) * 512, qv[q], u * (uint32_t)(D1 * 2));
+#pragma unroll
+            for (int q = 0; q < C::OIW; ++q)
+                copy16_to_lds_so(ors, od + (q * W + wave) * 512, ov[q], u * (uint32_t)(D2 * 2));
+            // rows 8*wave .. 8*wave+7: lane i < 16 copies float i%2 (bias,
+            // Delta) of row 8*wave + i/2 to sd[16*wave + i]; the other lanes
+            // stay inactive (they would land on the other waves' rows)
+            if (lane < 16)
+                copy4_to_lds_so(srs, sd + 16 * wave, sv, u * 8u);
+            return;
+        }
+        const bool live = tt < it.n_qt;
 #pragma unroll
         for (int q = 0; q < C::QIW; ++q) {
             const int ins = q * W + wave;
@@ -382,10 +440,6 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
             const uint32_t off = row_elem(r0 + min(rr, 31)) * (uint32_t)(D2 * 2) + (uint32_t)ch * 16u;
             copy16_to_lds(ors, od + ins * 512, ok ? off : 0xFFFFFFF0u);
         }
-        // rows 8*wave .. 8*wave+7: lane i < 16 copies float i%2 (bias, Delta)
-        // of row 8*wave + i/2 to sd[16*wave + i]; the other lanes stay
-        // inactive (a lane whose load falls outside the buffer still writes
-        // its zero, and lanes 16.. would land on the other waves' rows)
         if (lane < 16) {
             const int rr = 8 * wave + (lane >> 1);
             const bool ok = live && r0 + rr < rows_total;

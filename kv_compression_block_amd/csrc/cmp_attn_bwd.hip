@@ -15,9 +15,9 @@
 //     waves): blocks seen by more tiles than an item holds leave partial
 //     sums, added in piece order by a combine kernel.
 // Both use bf16 or f16 MFMA 32x32x16 with fp32 accumulation; tiles go
-// through LDS by buffer-unit copies of whole rows (16 bytes of padding per
-// row) and transposed reads (ds_read_b64_tr_b16) where an operand needs
-// the other orientation.
+// through LDS by buffer-unit copies (16-byte chunks permuted within each
+// row so that row reads and transposed reads, ds_read_b64_tr_b16, are both
+// free of bank conflicts).
 #include <type_traits>
 
 #include "nsa_device.h"
@@ -28,31 +28,70 @@ namespace {
 
 constexpr float kLog2eB = 1.4426950408889634f;
 
-// Rows of `R` elements (a multiple of 8) padded by 8: copy layout in LDS.
+// A 32-row tile of R elements (R a multiple of 64) in LDS, rows packed,
+// the 16-byte chunks of row r permuted by c -> c ^ s(r).  The tile is read
+// two ways: whole rows (ds_read_b128, 16 lanes a pass: rows r..r+15 at one
+// chunk) and transposed (ds_read_b64_tr_b16, 32 lanes a pass: four rows
+// 4m..4m+3 at four chunks 4n..4n+3).  With 64 four-byte banks a pass is
+// free of bank conflicts when its 16-byte units fall on distinct positions
+// modulo 16; s is chosen so that both passes do:
+//   * 16 chunks a row (rows a multiple of 256 bytes): s(r) = 4 (r & 3) +
+//     ((r >> 2) & 3), a bijection on r & 15 (row reads), and for the rows
+//     4m + i of a transposed read 4 i + (m & 3): bits 2-3 follow i, bits
+//     0-1 the chunk;
+//   * 8 or 24 chunks a row (rows at 128-byte steps, alternate rows half a
+//     bank cycle apart): s(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3) < 8, a
+//     bijection on the even and on the odd rows of 16, and for rows 4m + i
+//     bit 2 follows i >> 1, bits 0-1 the chunk, the row's parity the rest.
 template <int R>
-struct PadRows {
-    static constexpr int CH = R / 8;                       // 16-byte chunks per row
-    static constexpr int S = R + 8;                        // row stride (elements)
-    static constexpr int INS = (32 * (CH + 1) + 63) / 64;  // wave copy instructions per 32 rows
-    static constexpr int BUF = INS * 512;                  // elements per 32-row buffer
+struct SwzRows {
+    static_assert(R % 64 == 0, "rows of a multiple of 64 elements");
+    static constexpr int CH = R / 8;                  // 16-byte chunks per row
+    static constexpr int UNITS = 32 * CH;             // 16-byte units of the tile
+    static constexpr int INS = (UNITS + 63) / 64;     // wave copy instructions per tile
+    static constexpr int BUF = INS * 512;             // elements per tile buffer
+    static constexpr int KK = 16 * R;                 // elements of 16 rows
+    __device__ static __forceinline__ int s(int r)
+    {
+        if constexpr (CH % 16 == 0)
+            return ((r & 3) << 2) | ((r >> 2) & 3);
+        else
+            return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    }
+    // element offset of chunk c (8 elements) of row r
+    __device__ static __forceinline__ int at(int r, int c) { return (r * CH + (c ^ s(r))) * 8; }
+    // Row reads of the A operand of k-step ks (chunk 2 ks + hf of row l32):
+    // at(l32, 2 ks + hf) = (lb ^ 16 (ks & M)) + G (ks >> L) with lb =
+    // at(l32, hf), since the XOR only moves chunks inside a group of 16 (8)
+    // and the row starts on a group boundary of the element offset.
+    static constexpr int M = CH % 16 == 0 ? 7 : 3, L = CH % 16 == 0 ? 3 : 2, G = CH % 16 == 0 ? 128 : 64;
+    __device__ static __forceinline__ int row_base(int l32, int hf) { return at(l32, hf); }
+    __device__ static __forceinline__ int row_at(int lb, int ks) { return (lb ^ (16 * (ks & M))) + G * (ks >> L); }
+    // unit P of the buffer holds chunk chunk_of(P) of row P / CH
+    __device__ static __forceinline__ int chunk_of(int P) { return (P % CH) ^ s(P / CH); }
+    // Transposed read: lane receives column 32 db + l32 of rows {4hf + 0..3}
+    // (lo) and {8 + 4hf + 0..3} (hi), + 16 kk rows (added as kk * KK): the
+    // order a score accumulator leaves its rows in.  Lane (vi, vgrp, hf)
+    // supplies the 8 bytes of row 4hf + vi/4 at dims 32 db + 16 vgrp +
+    // 4 (vi%4).  From the block-0 offset tb: block db flips chunk bits 2-3
+    // (bit 2 and the group for 8-chunk swizzles), and the row 8 further on
+    // has s(r + 8) = s(r) ^ 2, one chunk bit.
+    static constexpr int MD = CH % 16 == 0 ? 3 : 1, LD = CH % 16 == 0 ? 2 : 1, GD = CH % 16 == 0 ? 128 : 64;
+    __device__ static __forceinline__ int tr_base(int lane)
+    {
+        const int vi = lane & 15, vgrp = (lane >> 4) & 1, hf = lane >> 5;
+        const int r = 4 * hf + (vi >> 2);
+        const int dim = 16 * vgrp + 4 * (vi & 3);
+        return at(r, dim >> 3) + (dim & 7);
+    }
+    __device__ static __forceinline__ int tr_lo(int tb, int db) { return (tb ^ (32 * (db & MD))) + GD * (db >> LD); }
+    __device__ static __forceinline__ int tr_hi(int tb, int db) { return (tr_lo(tb, db) ^ 16) + 64 * CH; }
 };
 
-// Transposed-read offset (elements) for a 32-row tile with row stride S:
-// lane receives column `dim0 + l32` of rows {16kk + 4hf + 0..3, 16kk + 8 + 4hf + 0..3}
-// (kk added by the caller as kk * 16 * S): the order a score accumulator
-// leaves its rows in.
-template <int S>
-__device__ __forceinline__ int tr_off(int lane, int dim0)
+__device__ __forceinline__ u32x4 tr_read2(const uint16_t* lo_p, const uint16_t* hi_p)
 {
-    const int vi = lane & 15, vgrp = (lane >> 4) & 1, hf = lane >> 5;
-    const int r0 = 4 * hf + (vi >> 2);
-    return r0 * S + dim0 + 16 * vgrp + 4 * (vi & 3);
-}
-
-__device__ __forceinline__ u32x4 tr_read(const uint16_t* base, int S)
-{
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)base);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + 8 * S));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo_p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi_p);
     return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -75,8 +114,8 @@ template <typename E, int D1, int D2>
 __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
 {
     constexpr int KT = 32, W = 4;
-    using KR = PadRows<D1>;
-    using VR = PadRows<D2>;
+    using KR = SwzRows<D1>;
+    using VR = SwzRows<D2>;
     constexpr int NKS = D1 / 16, NDS = D2 / 16, NDB1 = D1 / 32;
     constexpr int KIPW = (KR::INS + W - 1) / W, VIPW = (VR::INS + W - 1) / W;
     __shared__ __attribute__((aligned(16))) uint16_t K0[KR::BUF], K1[KR::BUF];
@@ -153,15 +192,15 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     uint32_t kdo[KIPW], vdo[VIPW];
 #pragma unroll
     for (int q = 0; q < KIPW; ++q) {
-        const int slot = (q * W + wave) * 64 + lane;
-        const int rr = slot / (KR::CH + 1), ch = slot % (KR::CH + 1);
-        kdo[q] = (ch < KR::CH && rr < KT) ? (uint32_t)rr * kst_b + (uint32_t)ch * 16u : 0x7FFFFFF0u;
+        const int unit = (q * W + wave) * 64 + lane;
+        kdo[q] = unit < KR::UNITS ? (uint32_t)(unit / KR::CH) * kst_b + (uint32_t)KR::chunk_of(unit) * 16u
+                                  : 0x7FFFFFF0u;
     }
 #pragma unroll
     for (int q = 0; q < VIPW; ++q) {
-        const int slot = (q * W + wave) * 64 + lane;
-        const int rr = slot / (VR::CH + 1), ch = slot % (VR::CH + 1);
-        vdo[q] = (ch < VR::CH && rr < KT) ? (uint32_t)rr * vst_b + (uint32_t)ch * 16u : 0x7FFFFFF0u;
+        const int unit = (q * W + wave) * 64 + lane;
+        vdo[q] = unit < VR::UNITS ? (uint32_t)(unit / VR::CH) * vst_b + (uint32_t)VR::chunk_of(unit) * 16u
+                                  : 0x7FFFFFF0u;
     }
     auto copy_tile = [&](int kt, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)kt * KT * kstride, tile_bytes(kt, kst_b, D1 * 2));
@@ -191,12 +230,15 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
         for (int x = 0; x < 16; ++x)
             dqa[db][x] = 0.f;
     const float c = p.c;
-    int ktr[NDB1];
-#pragma unroll
-    for (int db = 0; db < NDB1; ++db)
-        ktr[db] = tr_off<KR::S>(lane, db * 32);
+    const int ktb0 = KR::tr_base(lane);
 
     auto tile = [&](int kt, const uint16_t* ks_, const uint16_t* vs_) __attribute__((always_inline)) {
+        // read offsets; with D1 = 192 the bases are made opaque to the
+        // compiler so that the per-step offsets are formed here (a few XORs)
+        // instead of held in registers, which two workgroups per CU lack
+        int klb = KR::row_base(l32, hf), vlb = VR::row_base(l32, hf), ktb = ktb0;
+        if constexpr (D1 > 128)
+            __asm__ volatile("" : "+v"(klb), "+v"(vlb), "+v"(ktb));
         // S^T = K Q^T and dP^T = V dO^T (rows = keys, lane = query row)
         f32x16 s, dp;
 #pragma unroll
@@ -206,10 +248,10 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            s = E::mfma(*(const u32x4*)&ks_[l32 * KR::S + ks * 16 + hf * 8], qf[ks], s);
+            s = E::mfma(*(const u32x4*)&ks_[KR::row_at(klb, ks)], qf[ks], s);
 #pragma unroll
         for (int ks = 0; ks < NDS; ++ks)
-            dp = E::mfma(*(const u32x4*)&vs_[l32 * VR::S + ks * 16 + hf * 8], dof[ks], dp);
+            dp = E::mfma(*(const u32x4*)&vs_[VR::row_at(vlb, ks)], dof[ks], dp);
         // key kt*KT + 8*(x/4) + 4*hf + x%4 is visible iff it is below nvq
         const int lim = nvq - kt * KT - 4 * hf;
         u32x4 dsf[2];
@@ -233,7 +275,8 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int db = 0; db < NDB1; ++db)
-                dqa[db] = E::mfma(tr_read(&ks_[ktr[db] + kk * 16 * KR::S], KR::S), dsf[kk], dqa[db]);
+                dqa[db] = E::mfma(tr_read2(&ks_[KR::tr_lo(ktb, db) + kk * KR::KK], &ks_[KR::tr_hi(ktb, db) + kk * KR::KK]),
+                                  dsf[kk], dqa[db]);
     };
 
     if (n_kt > 0)
@@ -285,8 +328,8 @@ struct DkvCfg {
     static constexpr int W = 4;
     static constexpr int KB = 32 * W;
     static_assert(KB == kBwdKeyBlock, "key block");
-    using QR = PadRows<D1>;
-    using OR = PadRows<D2>;
+    using QR = SwzRows<D1>;
+    using OR = SwzRows<D2>;
     static constexpr int QIW = (QR::INS + W - 1) / W;       // Q copy instructions per wave and tile
     static constexpr int OIW = (OR::INS + W - 1) / W;       // dout copy instructions per wave and tile
     static constexpr int QSZ = QIW * W * 512;               // elements of a slot's Q tile (with slack)
@@ -387,17 +430,13 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
     auto lane_row = [&](int rr) -> uint32_t { return (uint32_t)((rr / G) * p.N1 + rr % G); };
 #pragma unroll
     for (int q = 0; q < C::QIW; ++q) {
-        const int ins = q * W + wave, sl = ins * 64 + lane;
-        const int rr = sl / (QR::CH + 1), ch = sl % (QR::CH + 1);
-        const bool ok = ins < QR::INS && ch < QR::CH && rr < 32;
-        qv[q] = ok ? lane_row(rr) * (uint32_t)(D1 * 2) + (uint32_t)ch * 16u : 0u;
+        const int unit = (q * W + wave) * 64 + lane;
+        qv[q] = unit < QR::UNITS ? lane_row(unit / QR::CH) * (uint32_t)(D1 * 2) + (uint32_t)QR::chunk_of(unit) * 16u : 0u;
     }
 #pragma unroll
     for (int q = 0; q < C::OIW; ++q) {
-        const int ins = q * W + wave, sl = ins * 64 + lane;
-        const int rr = sl / (OR::CH + 1), ch = sl % (OR::CH + 1);
-        const bool ok = ins < OR::INS && ch < OR::CH && rr < 32;
-        ov[q] = ok ? lane_row(rr) * (uint32_t)(D2 * 2) + (uint32_t)ch * 16u : 0u;
+        const int unit = (q * W + wave) * 64 + lane;
+        ov[q] = unit < OR::UNITS ? lane_row(unit / OR::CH) * (uint32_t)(D2 * 2) + (uint32_t)OR::chunk_of(unit) * 16u : 0u;
     }
     sv = (lane_row(8 * wave + ((lane & 15) >> 1)) * 2u + (uint32_t)(lane & 1)) * 4u;
     auto issue = [&](int tt, unsigned char* slot) __attribute__((always_inline)) {
@@ -425,19 +464,19 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
 #pragma unroll
         for (int q = 0; q < C::QIW; ++q) {
             const int ins = q * W + wave;
-            const int sl = ins * 64 + lane;
-            const int rr = sl / (QR::CH + 1), ch = sl % (QR::CH + 1);
-            const bool ok = live && ins < QR::INS && ch < QR::CH && rr < 32 && r0 + rr < rows_total;
-            const uint32_t off = row_elem(r0 + min(rr, 31)) * (uint32_t)(D1 * 2) + (uint32_t)ch * 16u;
+            const int unit = ins * 64 + lane;
+            const int rr = min(unit / QR::CH, 31);
+            const bool ok = live && unit < QR::UNITS && r0 + rr < rows_total;
+            const uint32_t off = row_elem(r0 + rr) * (uint32_t)(D1 * 2) + (uint32_t)QR::chunk_of(unit) * 16u;
             copy16_to_lds(qrs, qd + ins * 512, ok ? off : 0xFFFFFFF0u);
         }
 #pragma unroll
         for (int q = 0; q < C::OIW; ++q) {
             const int ins = q * W + wave;
-            const int sl = ins * 64 + lane;
-            const int rr = sl / (OR::CH + 1), ch = sl % (OR::CH + 1);
-            const bool ok = live && ins < OR::INS && ch < OR::CH && rr < 32 && r0 + rr < rows_total;
-            const uint32_t off = row_elem(r0 + min(rr, 31)) * (uint32_t)(D2 * 2) + (uint32_t)ch * 16u;
+            const int unit = ins * 64 + lane;
+            const int rr = min(unit / OR::CH, 31);
+            const bool ok = live && unit < OR::UNITS && r0 + rr < rows_total;
+            const uint32_t off = row_elem(r0 + rr) * (uint32_t)(D2 * 2) + (uint32_t)OR::chunk_of(unit) * 16u;
             copy16_to_lds(ors, od + ins * 512, ok ? off : 0xFFFFFFF0u);
         }
         if (lane < 16) {
@@ -460,13 +499,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
 #pragma unroll
         for (int x = 0; x < 16; ++x)
             dva[db][x] = 0.f;
-    int qtr[NDB1], otr[NDB2];
-#pragma unroll
-    for (int db = 0; db < NDB1; ++db)
-        qtr[db] = tr_off<QR::S>(lane, db * 32);
-#pragma unroll
-    for (int db = 0; db < NDB2; ++db)
-        otr[db] = tr_off<OR::S>(lane, db * 32);
+    const int qtb0 = QR::tr_base(lane), otb0 = OR::tr_base(lane);
     const float c = p.c;
 
     // Step tt: wait until tile tt's copies have landed (the NS - 2 later
@@ -503,6 +536,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
             sc[x] = 0.f;
             dp[x] = 0.f;
         }
+        const int qlb = QR::row_base(l32, hf), olb = OR::row_base(l32, hf), qtb = qtb0, otb = otb0;
         f32x4 stv[8];   // (bias, Delta) of rows 8*r4 + 4*hf + {0, 1}, then {2, 3}
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -511,14 +545,14 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         }
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-            sc = E::mfma(*(const u32x4*)&qs[l32 * QR::S + ks * 16 + hf * 8], kf[ks], sc);
+            sc = E::mfma(*(const u32x4*)&qs[QR::row_at(qlb, ks)], kf[ks], sc);
         __builtin_amdgcn_sched_barrier(0);
         const int d0 = r0 + 4 * hf - key_first_row;
         float pv[16];
         u32x4 pf[2], dsf[2];
 #pragma unroll
         for (int ks = 0; ks < NDS; ++ks)
-            dp = E::mfma(*(const u32x4*)&os[l32 * OR::S + ks * 16 + hf * 8], vf[ks], dp);
+            dp = E::mfma(*(const u32x4*)&os[OR::row_at(olb, ks)], vf[ks], dp);
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
             const int r4 = x >> 2, e = x & 3;
@@ -535,9 +569,11 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
         constexpr int NGV = 2 * NDB2, NG = NGV + 2 * NDB1, PF = 3;
         auto g_operand = [&](int m) __attribute__((always_inline)) -> u32x4 {
             if (m < NGV)
-                return tr_read(&os[otr[m % NDB2] + (m / NDB2) * 16 * OR::S], OR::S);
+                return tr_read2(&os[OR::tr_lo(otb, m % NDB2) + (m / NDB2) * OR::KK],
+                                &os[OR::tr_hi(otb, m % NDB2) + (m / NDB2) * OR::KK]);
             const int j = m - NGV;
-            return tr_read(&qs[qtr[j % NDB1] + (j / NDB1) * 16 * QR::S], QR::S);
+            return tr_read2(&qs[QR::tr_lo(qtb, j % NDB1) + (j / NDB1) * QR::KK],
+                            &qs[QR::tr_hi(qtb, j % NDB1) + (j / NDB1) * QR::KK]);
         };
         u32x4 ga[NG];
 #pragma unroll

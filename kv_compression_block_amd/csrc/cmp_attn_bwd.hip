@@ -95,16 +95,27 @@ __device__ __forceinline__ u32x4 tr_read2(const uint16_t* lo_p, const uint16_t* 
     return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Buffer-to-LDS copies with a per-lane offset and a wave-uniform one:
-// lane i's 16 (or 4) bytes land at lds + 16 i (4 i).
-__device__ __forceinline__ void copy16_to_lds_so(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff)
+// Buffer-to-LDS copies with the LDS address passed as a plain number: the
+// compiler then cannot tie a copy to an LDS object and adds no waits of its
+// own before reads of other objects (it would otherwise wait for copies it
+// cannot tell apart, several tiles ahead).  The kernels order every copy
+// against its reads with their own wait counts and barriers.  16 (or 4)
+// bytes per lane land at lds + 16 i (4 i); voff per lane, soff per wave.
+__device__ __forceinline__ lds_void* lds_untracked(void* lds)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+    return (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
 }
 
-__device__ __forceinline__ void copy4_to_lds_so(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff)
+__device__ __forceinline__ void copy16_to_lds_untracked(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                                        uint32_t soff = 0)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void copy4_to_lds_untracked(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                                       uint32_t soff = 0)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_untracked(lds), 4, voff, soff, 0, 0);
 }
 
 }  // namespace
@@ -118,8 +129,12 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     using VR = SwzRows<D2>;
     constexpr int NKS = D1 / 16, NDS = D2 / 16, NDB1 = D1 / 32;
     constexpr int KIPW = (KR::INS + W - 1) / W, VIPW = (VR::INS + W - 1) / W;
-    __shared__ __attribute__((aligned(16))) uint16_t K0[KR::BUF], K1[KR::BUF];
-    __shared__ __attribute__((aligned(16))) uint16_t V0[VR::BUF], V1[VR::BUF];
+    constexpr int KBUF = KIPW * W * 512, VBUF = VIPW * W * 512;   // with the slack of uneven copies
+    constexpr int CPW = KIPW + VIPW;                              // copy instructions per wave and tile
+    // Three K and three V slots, walked in a fixed order: a tile is copied
+    // two tiles ahead of its use.
+    __shared__ __attribute__((aligned(16))) uint16_t K0[KBUF], K1[KBUF], K2[KBUF];
+    __shared__ __attribute__((aligned(16))) uint16_t V0[VBUF], V1[VBUF], V2[VBUF];
     if (*p.status != 0)
         return;   // the table failed the planner's checks
 
@@ -205,19 +220,21 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
     auto copy_tile = [&](int kt, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + (int64_t)kt * KT * kstride, tile_bytes(kt, kst_b, D1 * 2));
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + (int64_t)kt * KT * vstride, tile_bytes(kt, vst_b, D2 * 2));
+        // every wave issues CPW copies per tile (slack ones land past the
+        // tile in the slot, tiles past the end copy nothing but zeros), so
+        // one immediate wait count fits every wave
 #pragma unroll
         for (int q = 0; q < KIPW; ++q)
-            if (q * W + wave < KR::INS)
-                copy16_to_lds(kr, kd + (q * W + wave) * 512, kdo[q]);
+            copy16_to_lds_untracked(kr, kd + (q * W + wave) * 512, kdo[q]);
 #pragma unroll
         for (int q = 0; q < VIPW; ++q)
-            if (q * W + wave < VR::INS)
-                copy16_to_lds(vr, vd + (q * W + wave) * 512, vdo[q]);
+            copy16_to_lds_untracked(vr, vd + (q * W + wave) * 512, vdo[q]);
     };
-    // This wave's copies have landed and (after the barrier) every wave's;
-    // every wave is done with the previous tile's LDS reads.
+    // This wave's copies of the tile about to be read have landed (the next
+    // tile's may still be in flight) and, after the barrier, every wave's;
+    // every wave is done with the slot the next copy overwrites.
     auto step_barrier = [&]() __attribute__((always_inline)) {
-        __builtin_amdgcn_s_waitcnt(0x0070);
+        __builtin_amdgcn_s_waitcnt((CPW & 15) | ((CPW >> 4) << 14) | 0x0070);
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
@@ -279,19 +296,26 @@ __global__ __launch_bounds__(256, 2) void k_cmp_attn_bwd_dq(BwdParams p)
                                   dsf[kk], dqa[db]);
     };
 
-    if (n_kt > 0)
+    if (n_kt > 0) {
         copy_tile(0, K0, V0);
-    for (int kt = 0; kt < n_kt; kt += 2) {
-        step_barrier();
-        if (kt + 1 < n_kt)
-            copy_tile(kt + 1, K1, V1);
-        tile(kt, K0, V0);
-        if (kt + 1 >= n_kt)
-            break;
-        step_barrier();
-        if (kt + 2 < n_kt)
-            copy_tile(kt + 2, K0, V0);
-        tile(kt + 1, K1, V1);
+        copy_tile(1, K1, V1);
+        for (int kt = 0; kt < n_kt; kt += 3) {
+            step_barrier();
+            copy_tile(kt + 2, K2, V2);
+            tile(kt, K0, V0);
+            if (kt + 1 >= n_kt)
+                break;
+            step_barrier();
+            copy_tile(kt + 3, K0, V0);
+            tile(kt + 1, K1, V1);
+            if (kt + 2 >= n_kt)
+                break;
+            step_barrier();
+            copy_tile(kt + 4, K1, V1);
+            tile(kt + 2, K2, V2);
+        }
+        // the copies past the end land before the workgroup's LDS is released
+        __builtin_amdgcn_s_waitcnt(0x0070);
     }
 
     // dq = scale * (K^T dS^T)^T: lane l32 holds dims 8*(x/4) + 4*hf + x%4 of
@@ -449,15 +473,15 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
             const uint32_t u = t0 * (uint32_t)p.N1 + gG + ((uint32_t)r0 - t0 * (uint32_t)G);
 #pragma unroll
             for (int q = 0; q < C::QIW; ++q)
-                copy16_to_lds_so(qrs, qd + (q * W + wave) * 512, qv[q], u * (uint32_t)(D1 * 2));
+                copy16_to_lds_untracked(qrs, qd + (q * W + wave) * 512, qv[q], u * (uint32_t)(D1 * 2));
 #pragma unroll
             for (int q = 0; q < C::OIW; ++q)
-                copy16_to_lds_so(ors, od + (q * W + wave) * 512, ov[q], u * (uint32_t)(D2 * 2));
+                copy16_to_lds_untracked(ors, od + (q * W + wave) * 512, ov[q], u * (uint32_t)(D2 * 2));
             // rows 8*wave .. 8*wave+7: lane i < 16 copies float i%2 (bias,
             // Delta) of row 8*wave + i/2 to sd[16*wave + i]; the other lanes
             // stay inactive (they would land on the other waves' rows)
             if (lane < 16)
-                copy4_to_lds_so(srs, sd + 16 * wave, sv, u * 8u);
+                copy4_to_lds_untracked(srs, sd + 16 * wave, sv, u * 8u);
             return;
         }
         const bool live = tt < it.n_qt;
@@ -468,7 +492,7 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
             const int rr = min(unit / QR::CH, 31);
             const bool ok = live && unit < QR::UNITS && r0 + rr < rows_total;
             const uint32_t off = row_elem(r0 + rr) * (uint32_t)(D1 * 2) + (uint32_t)QR::chunk_of(unit) * 16u;
-            copy16_to_lds(qrs, qd + ins * 512, ok ? off : 0xFFFFFFF0u);
+            copy16_to_lds_untracked(qrs, qd + ins * 512, ok ? off : 0xFFFFFFF0u);
         }
 #pragma unroll
         for (int q = 0; q < C::OIW; ++q) {
@@ -477,14 +501,13 @@ __global__ __launch_bounds__(256, 1) void k_cmp_attn_bwd_dkv(BwdParams p)
             const int rr = min(unit / OR::CH, 31);
             const bool ok = live && unit < OR::UNITS && r0 + rr < rows_total;
             const uint32_t off = row_elem(r0 + rr) * (uint32_t)(D2 * 2) + (uint32_t)OR::chunk_of(unit) * 16u;
-            copy16_to_lds(ors, od + ins * 512, ok ? off : 0xFFFFFFF0u);
+            copy16_to_lds_untracked(ors, od + ins * 512, ok ? off : 0xFFFFFFF0u);
         }
         if (lane < 16) {
             const int rr = 8 * wave + (lane >> 1);
             const bool ok = live && r0 + rr < rows_total;
             const uint32_t off = (row_elem(r0 + rr) * 2u + (uint32_t)(lane & 1)) * 4u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)(sd + 16 * wave), 4, ok ? off : 0xFFFFFFF0u,
-                                                     0, 0, 0);
+            copy4_to_lds_untracked(srs, sd + 16 * wave, ok ? off : 0xFFFFFFF0u);
         }
     };
 

@@ -355,6 +355,15 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
             any |= growq[qb];
         if (__builtin_expect(__ballot(any) != 0, 0)) {
             __asm__ volatile("" ::: "memory");
+            // A row whose reference max is still -inf has O = 0 and sum 0
+            // (every P so far was 0): nothing to rescale.  Only when some
+            // row of the wave moves a finite max is O multiplied (always
+            // at a wave's first tile, the one place most rows move).
+            bool live = false;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                live |= growq[qb] && mref[qb] != -INFINITY;
+            const bool scale_o = __ballot(live) != 0;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 float alpha = 1.f;
@@ -362,12 +371,14 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                     alpha = (mref[qb] == -INFINITY) ? 0.f : fast_exp2((mref[qb] - tmaxq[qb]) * c);
                     mref[qb] = tmaxq[qb];
                 }
-                lsum[qb] *= alpha;
+                if (scale_o) {
+                    lsum[qb] *= alpha;
 #pragma unroll
-                for (int db = 0; db < C::NDB; ++db)
+                    for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        o[qb][db][r] *= alpha;
+                        for (int r = 0; r < 16; ++r)
+                            o[qb][db][r] *= alpha;
+                }
             }
         }
 #pragma unroll
@@ -562,6 +573,16 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         const float lf = half_sum(lsum[qb]);
         const bool empty = (mtrue[qb] == -INFINITY);
         const float inv = empty ? 0.f : 1.f / lf;
+        // The rows this lane stores in both passes, and where they go (null
+        // past the sequence): computed once, the two passes share them.
+        uint16_t* odst[32 / RPI];
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int r = row_wg + (wave * QB + qb) * 32 + i * RPI + lane_e / CPR;
+            const uint32_t tok = (uint32_t)r / (uint32_t)G;
+            const int64_t orow = (int64_t)(be.q_off + (int)tok) * p.N1 + (int64_t)g * G + (r - (int)tok * G);
+            odst[i] = r < rows_total ? p.out + orow * D2 + (lane_e % CPR) * 8 : nullptr;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -579,18 +600,14 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                 const int rr = i * RPI + lane_e / CPR;          // staged row
                 const int ch = lane_e % CPR;
                 const u32x4 v = *(const u32x4*)&ostg[rr * OPITCH + ch * 8];
-                const int r = row_wg + (wave * QB + qb) * 32 + rr;
-                if (r < rows_total) {
-                    const int tok = r / G;
-                    const int64_t orow = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + (r - tok * G);
-                    __builtin_nontemporal_store(v, (u32x4*)(p.out + orow * D2 + h * HD + ch * 8));
-                }
+                if (odst[i] != nullptr)
+                    __builtin_nontemporal_store(v, (u32x4*)(odst[i] + h * HD));
             }
         }
         const int r = row_wg + (wave * QB + qb) * 32 + l32_e;
         if (r >= rows_total)
             continue;
-        const int tok = r / G;
+        const int tok = (int)((uint32_t)r / (uint32_t)G);
         const int64_t grow = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + (r - tok * G);
         const float smv = empty ? -INFINITY : mtrue[qb] * p.abs_scale;
         const float ssv = empty ? 0.f : lf * fast_exp2((mref[qb] - mtrue[qb]) * c);

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float pv = fast_exp2(fmaf(s[rr][kb][r], c, -bias[rr][r]));
-                    if constexpr (MASK && !XM) {
+                    if constexpr (MASK && !XM && GP < 8) {
                         const int pr = rr * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
                         const int tok = tok_w + (pr >> LOG2GP);
                         // visible iff key*d + l - 1 <= the token's position
@@ -377,6 +377,19 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
                     }
                     acc[(rr * 32 + 8 * (r >> 2) + (r & 3)) >> LOG2GP][kb] += pv;
                 }
+            }
+        }
+        if constexpr (MASK && !XM && GP >= 8) {
+            // Groups of 8 or more: the heads summed in acc[tw][kb] are rows
+            // of token tok_w + tw in both half-waves, so the visibility rule
+            // applies to the sum (invisible entries' exponentials, however
+            // large, are dropped by the select).
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int key = kt * KT + kb * 32 + l32;
+#pragma unroll
+                for (int tw = 0; tw < TOKW; ++tw)
+                    acc[tw][kb] = (key * p.d + p.l - 1 <= tok_w + tw + be.pos_off) ? acc[tw][kb] : 0.f;
             }
         }
         if constexpr (MASK && XM) {

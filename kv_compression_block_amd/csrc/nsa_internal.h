@@ -281,7 +281,11 @@ bool attn_bwd_supported(int d1, int d2);
 hipError_t launch_attn_bwd(int dtype, int d1, int d2, const BwdParams& p, int tiles_q, int n_items,
                            int n_combs, hipStream_t stream);
 
-constexpr int kTopkRing = 128;         // per-token ring of group-summed P (floats)
+constexpr int kTopkRing = 128;         // smallest per-token ring of group-summed P (floats)
+// Ring length for 64 / 2^log2gp tokens per wave: the stencil pass runs once
+// per batch of key tiles, sized so that the wave's lanes are about all busy,
+// and the ring keeps a batch plus the stencil's reach (at most 15 entries).
+constexpr int topk_ring(int log2gp) { return log2gp >= 6 ? 4 * kTopkRing : (log2gp == 5 ? 2 * kTopkRing : kTopkRing); }
 constexpr int kTopkRingDup = 4;        // ring slots repeated past its end (stencils of <= 5 taps)
 constexpr int kTopkMaxNpl = 16;        // at most 1024 select blocks per sequence
 

@@ -76,8 +76,8 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     constexpr int NKS = D1 / 16;
     constexpr int KCH = D1 / 8;
     constexpr int KLD = KT * KCH / 256;
-    constexpr int RING = kTopkRing;
-    constexpr int RINGP = kTopkRing + kTopkRingDup;   // ring row: the ring, then its first slots again
+    constexpr int RING = topk_ring(LOG2GP);
+    constexpr int RINGP = RING + kTopkRingDup;        // ring row: the ring, then its first slots again
     constexpr int HSH = 4 >> LOG2GP;        // token offset of the upper half-wave (GP <= 4)
 
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -188,11 +188,17 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     uint32_t* my_stg = stg + wave * 128;     // XM mask words in the key loop; top-k staging after it
     for (int x = lane; x < TOKW * RINGP; x += 64)
         my_ring[x] = 0.f;
-    // Stencil lanes: lane -> (token tw_l, block slot jj_l) with nj_slots =
-    // ceil(KT / R) slots per token, tpp tokens per pass over the wave.
-    const int tw_l = lane / p.nj_slots;
-    const int jj_l = lane - tw_l * p.nj_slots;
-    const int tpp = 64 / p.nj_slots;
+    // The stencil runs once per batch of nbt key tiles: enough tiles that the
+    // (token, block) pairs they finish fill most of the wave's lanes, few
+    // enough that the ring still holds the batch plus the stencil's reach.
+    // Stencil lanes: lane -> (token tw_l, block slot jj_l) with nbt * nj_slots
+    // (nj_slots = ceil(KT / R)) slots per token, tpp tokens per pass.
+    const int nbt = max(1, min(64 / (TOKW * p.nj_slots), (RING - 16) / KT));
+    const int nj_bat = nbt * p.nj_slots;
+    const int tw_l = lane / nj_bat;
+    const int jj_l = lane - tw_l * nj_bat;
+    const int tpp = max(1, 64 / nj_bat);
+    int bat_n = 0;   // tiles of the current batch so far
 
     // ---- K tile staging ------------------------------------------------------------
     const int64_t kstride = (int64_t)p.N2 * D1;
@@ -436,20 +442,25 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         }
         wave_lds_sync();
 
-        // Select blocks j whose stencil top R*j lies in this tile (at most
-        // nj_slots of them per token), one (token, block) pair per lane.
-        const int key0 = kt * KT;
-        const int jlo = (key0 + R - 1) / R;
-        const int nj = min((key0 + KT + R - 1) / R, be.S_sel) - jlo;
-        for (int tw0 = 0; tw0 < TOKW; tw0 += tpp) {
-            const int tw = tw0 + tw_l;
-            if (tw_l < tpp && tw < TOKW && jj_l < nj) {
-                const int j = jlo + jj_l;
-                const float* rg = my_ring + tw * RINGP;
-                my_bins[tw * p.sb + j] = __builtin_expect(short_stencil, 1) ? stencil5(rg, j) : stencil_long(rg, j);
+        // At the end of a batch of nbt tiles (and after the last tile): the
+        // select blocks j whose stencil top R*j lies in the batch's keys (at
+        // most nbt * nj_slots of them per token), one (token, block) pair
+        // per lane.
+        if (++bat_n == nbt || kt + 1 == kt_end) {
+            const int key0 = (kt + 1 - bat_n) * KT;   // the batch's first key
+            bat_n = 0;
+            const int jlo = (key0 + R - 1) / R;
+            const int nj = min(((kt + 1) * KT + R - 1) / R, be.S_sel) - jlo;
+            for (int tw0 = 0; tw0 < TOKW; tw0 += tpp) {
+                const int tw = tw0 + tw_l;
+                if (tw_l < tpp && tw < TOKW && jj_l < nj) {
+                    const int j = jlo + jj_l;
+                    const float* rg = my_ring + tw * RINGP;
+                    my_bins[tw * p.sb + j] = __builtin_expect(short_stencil, 1) ? stencil5(rg, j) : stencil_long(rg, j);
+                }
             }
+            wave_lds_sync();
         }
-        wave_lds_sync();
 
         if (kt + 1 < kt_end) {
             if (nbuf == 1)
@@ -713,7 +724,7 @@ int topk_log2_gp(int G)
 size_t topk_lds_bytes(int d1, int log2gp, int waves, int sb, int kbufs)
 {
     const size_t tokw = (size_t)(64 >> log2gp);
-    return (size_t)kbufs * topk_key_tile(d1) * (d1 + 8) * 2 + (size_t)waves * tokw * (kTopkRing + kTopkRingDup) * 4 +
+    return (size_t)kbufs * topk_key_tile(d1) * (d1 + 8) * 2 + (size_t)waves * tokw * (topk_ring(log2gp) + kTopkRingDup) * 4 +
            (size_t)waves * tokw * sb * 4 + (size_t)waves * 128 * 4;
 }
 

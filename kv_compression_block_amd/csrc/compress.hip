@@ -4,65 +4,96 @@
 // accumulated in float32 in ascending p, rounded once to the element type
 // of x and w (bfloat16 or float16, nearest even).
 //
-// HBM-bound: one thread owns 8 consecutive elements (16 bytes) of one output
-// row and walks the l input rows of its window with 16-byte loads, so a wave
-// reads whole 64-byte..256-byte row segments.  Overlapping windows (l > d)
-// re-read rows through L2, not HBM.  Weights are staged in LDS as float32.
-// Grid: x = row-chunk blocks, y = sequence (blocks past a sequence's rows
-// exit at once).
+// HBM-bound.  A workgroup owns a run of nw consecutive windows of one
+// sequence and one column slab of cs 16-byte chunks of the [N*D] row: it
+// copies the run's (nw-1)*d + l input rows of that slab into LDS once
+// (every load independent, 16 bytes per lane), then thread (window j,
+// chunk c) walks its l rows in LDS.  Each input row is read from global
+// memory once per run instead of once per window that contains it; the
+// l - d rows two runs share are fetched by both, and the runs of a
+// sequence are numbered so that consecutive runs go to the same XCD (the
+// dispatcher deals workgroups to the eight XCDs in turn), where the
+// second fetch finds them in that XCD's L2.  Weights are staged in LDS as
+// float32.  Grid: x = XCD-ordered (run, slab) blocks, y = sequence (blocks
+// past a sequence's runs exit at once).
 #include "nsa_device.h"
 
 namespace nsa {
 
 constexpr int kCompressThreads = 256;
 constexpr int kCompressMaxW = 128 * 64;   // l * N floats staged in LDS (32 KB)
+constexpr int kCompressLoads = kCompressStageBytes / 16 / kCompressThreads;   // row-chunk copies per thread
 
 template <typename E>
 __global__ __launch_bounds__(kCompressThreads) void k_compress(CompressParams p)
 {
-    __shared__ float wl[kCompressMaxW];
+    extern __shared__ __attribute__((aligned(16))) unsigned char cmp_smem[];
+    u32x4* stage = (u32x4*)cmp_smem;                                   // [rows][cs]
+    float* wl = (float*)(cmp_smem + kCompressStageBytes);              // [l][N]
     const int seg = blockIdx.y;
     const int n_out = p.n_out[seg];
-    const int nd8 = (p.N * p.D) >> 3;              // 16-byte chunks per row
-    const int64_t item0 = (int64_t)blockIdx.x * kCompressThreads;
-    if (item0 >= (int64_t)n_out * nd8)
+    // XCD-ordered numbering: block x runs on XCD x % 8; the blocks of one
+    // XCD take consecutive (run, slab) numbers.
+    const int xb = blockIdx.x;
+    const int u = (xb & 7) * (p.max_blocks_x >> 3) + (xb >> 3);
+    const int run = u / p.nslab;
+    const int slab = u - run * p.nslab;
+    const int w0 = run * p.nw;
+    if (w0 >= n_out)
         return;                                    // uniform per block
+    const int nwv = min(p.nw, n_out - w0);         // windows of this run
+    const int nrows = (nwv - 1) * p.d + p.l;       // input rows they cover
+    const int cs_log2 = p.cs_log2;
+    const int cs = 1 << cs_log2;
+    const int64_t row_stride = (int64_t)p.N * p.D;     // elements
+    const uint16_t* src = p.x + ((int64_t)p.in_off[seg] + (int64_t)w0 * p.d) * row_stride + slab * cs * 8;
 
+    // Every copy of the run's rows is issued before the first one is stored.
+    u32x4 v[kCompressLoads];
+#pragma unroll
+    for (int k = 0; k < kCompressLoads; ++k) {
+        const int x = threadIdx.x + k * kCompressThreads;
+        const int r = x >> cs_log2;
+        if (r < nrows)
+            v[k] = *(const u32x4*)(src + (int64_t)r * row_stride + (x & (cs - 1)) * 8);
+    }
     const int nw = p.l * p.N;
-    for (int k = threadIdx.x; k < nw; k += kCompressThreads) {
+    for (int k = threadIdx.x; k < nw; k += kCompressThreads)
         wl[k] = E::widen(p.w[k]);
+#pragma unroll
+    for (int k = 0; k < kCompressLoads; ++k) {
+        const int x = threadIdx.x + k * kCompressThreads;
+        if ((x >> cs_log2) < nrows)
+            stage[x] = v[k];
     }
     __syncthreads();
 
-    const int64_t item = item0 + threadIdx.x;
-    if (item >= (int64_t)n_out * nd8)
+    const int j = threadIdx.x >> cs_log2;          // window of the run
+    const int c = threadIdx.x & (cs - 1);          // chunk of the slab
+    if (j >= nwv)
         return;
-    const int i = (int)(item / nd8);
-    const int c = (int)(item - (int64_t)i * nd8);
-    const int n = (c * 8) / p.D;
-    const int64_t row_stride = (int64_t)p.N * p.D;
-    const uint16_t* src = p.x + ((int64_t)p.in_off[seg] + (int64_t)i * p.d) * row_stride + c * 8;
-
+    const int n = ((slab * cs + c) * 8) / p.D;     // the chunk's head
     float acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        acc[j] = 0.f;
+    for (int e = 0; e < 8; ++e)
+        acc[e] = 0.f;
+    const u32x4* srow = stage + ((j * p.d) << cs_log2) + c;
     const float* wcol = wl + n;
 #pragma unroll 4
     for (int pp = 0; pp < p.l; ++pp) {
-        const u32x4 v = *(const u32x4*)(src + (int64_t)pp * row_stride);
+        const u32x4 x = srow[pp << cs_log2];
         const float wv = wcol[pp * p.N];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[2 * j] = fmaf(wv, E::lo(v[j]), acc[2 * j]);
-            acc[2 * j + 1] = fmaf(wv, E::hi(v[j]), acc[2 * j + 1]);
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(wv, E::lo(x[e]), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(wv, E::hi(x[e]), acc[2 * e + 1]);
         }
     }
     u32x4 o;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        o[j] = E::pack2(acc[2 * j], acc[2 * j + 1]);
-    *(u32x4*)(p.y + ((int64_t)p.out_off[seg] + i) * row_stride + c * 8) = o;
+    for (int e = 0; e < 4; ++e)
+        o[e] = E::pack2(acc[2 * e], acc[2 * e + 1]);
+    *(u32x4*)(p.y + ((int64_t)p.out_off[seg] + w0 + j) * row_stride + (slab * cs + c) * 8) = o;
 }
 
 // Backward (for training; the derivative of the formula above):
@@ -188,13 +219,22 @@ hipError_t launch_compress_bwd_dx(int dtype, const CompressBwdParams& p, hipStre
 
 hipError_t launch_compress(int dtype, const CompressParams& p, hipStream_t stream)
 {
-    if (p.l * p.N > kCompressMaxW)
+    const int cs = 1 << p.cs_log2;
+    if (p.l * p.N > kCompressMaxW || p.max_blocks_x % 8 != 0 || cs > 16 || p.nw < 1 ||
+        p.nw * cs > kCompressThreads || ((p.nw - 1) * p.d + p.l) * cs * 16 > kCompressStageBytes)
         return hipErrorInvalidValue;
     dim3 grid(p.max_blocks_x, p.nseg, 1);
+    const size_t lds = kCompressStageBytes + (size_t)p.l * p.N * sizeof(float);
+    if (lds > 64 * 1024) {
+        auto kern = dtype == ElemBf16::code ? (const void*)k_compress<ElemBf16> : (const void*)k_compress<ElemF16>;
+        const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess)
+            return e;
+    }
     if (dtype == ElemBf16::code)
-        hipLaunchKernelGGL(k_compress<ElemBf16>, grid, dim3(kCompressThreads), 0, stream, p);
+        hipLaunchKernelGGL(k_compress<ElemBf16>, grid, dim3(kCompressThreads), lds, stream, p);
     else if (dtype == ElemF16::code)
-        hipLaunchKernelGGL(k_compress<ElemF16>, grid, dim3(kCompressThreads), 0, stream, p);
+        hipLaunchKernelGGL(k_compress<ElemF16>, grid, dim3(kCompressThreads), lds, stream, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

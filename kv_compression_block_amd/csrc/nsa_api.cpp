@@ -179,6 +179,16 @@ nsa_status nsa_compress(const void* input, const void* weight, const int64_t* ac
     p.D = (int)head_dim;
     p.l = (int)l;
     p.d = (int)d;
+    // Column slab: the largest power of two <= 16 chunks that divides the
+    // row's chunks; a run: as many windows as the staged rows and the
+    // workgroup's threads allow.
+    p.cs_log2 = 0;
+    while (p.cs_log2 < 4 && nd8 % (2 << p.cs_log2) == 0)
+        ++p.cs_log2;
+    const int64_t cs = 1 << p.cs_log2;
+    p.nslab = (int)(nd8 / cs);
+    const int64_t stage_rows = nsa::kCompressStageBytes / 16 / cs;
+    p.nw = (int)std::min<int64_t>((stage_rows - l) / d + 1, 256 / cs);
     int64_t in_off = 0, out_off = 0;
     size_t b = 0;
     while (b < lens.size()) {
@@ -190,8 +200,9 @@ nsa_status nsa_compress(const void* input, const void* weight, const int64_t* ac
                 p.in_off[p.nseg] = (int)in_off;
                 p.out_off[p.nseg] = (int)out_off;
                 p.n_out[p.nseg] = (int)n;
-                if (n * nd8 > max_items)
-                    max_items = n * nd8;
+                const int64_t blocks = (n + p.nw - 1) / p.nw * p.nslab;
+                if (blocks > max_items)
+                    max_items = blocks;
                 ++p.nseg;
             }
             in_off += lens[b];
@@ -200,7 +211,9 @@ nsa_status nsa_compress(const void* input, const void* weight, const int64_t* ac
         }
         if (p.nseg == 0)
             continue;
-        p.max_blocks_x = (int)((max_items + 255) / 256);
+        if (max_items > (int64_t)INT32_MAX - 8)
+            return fail(NSA_ERR_CONSTRAINT, "sequence too long for one compression launch");
+        p.max_blocks_x = (int)((max_items + 7) / 8 * 8);
         hipError_t e = nsa::launch_compress((int)dtype, p, (hipStream_t)stream);
         if (e != hipSuccess)
             return fail(NSA_ERR_HIP, "compress launch failed: %s", hipGetErrorString(e));
@@ -616,6 +629,18 @@ const int* status_word(nsa_plan plan, const void* workspace)
 }
 
 float exp2_scale(const nsa_plan_s* plan) { return std::fabs(plan->scale) * 1.4426950408889634f; }
+
+// Magic numbers for division by G (round-up method): s = ceil(log2 G),
+// m = floor(2^32 (2^s - G) / G) + 1; then n / G = (umulhi(n, m) + n) >> s
+// for 0 <= n < 2^31.
+void g_magic(int G, uint32_t* m, uint32_t* s)
+{
+    uint32_t sh = 0;
+    while (((uint64_t)1 << sh) < (uint64_t)G)
+        ++sh;
+    *s = sh;
+    *m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << sh) - (uint64_t)G)) / (uint64_t)G + 1);
+}
 uint32_t q_sign(const nsa_plan_s* plan) { return plan->scale < 0.f ? 0x80008000u : 0u; }
 
 nsa::AttnParams fwd_params(nsa_plan plan, const void* query, const void* key, const void* value,
@@ -1243,15 +1268,7 @@ nsa_status nsa_compress_attention_backward(nsa_plan plan, const void* query, con
     a.c = std::fmax(exp2_scale(plan), 1e-30f);
     a.scale = plan->scale;
     a.qsign = q_sign(plan);
-    {
-        // magic numbers for division by G (round-up method): s = ceil(log2 G),
-        // m = floor(2^32 (2^s - G) / G) + 1
-        uint32_t sh = 0;
-        while (((uint64_t)1 << sh) < (uint64_t)a.G)
-            ++sh;
-        a.gdiv_s = sh;
-        a.gdiv_m = (uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << sh) - (uint64_t)a.G)) / (uint64_t)a.G + 1);
-    }
+    g_magic(a.G, &a.gdiv_m, &a.gdiv_s);
     nsa::BwdPlanParams bp;
     std::memset(&bp, 0, sizeof bp);
     bp.table = a.bt;

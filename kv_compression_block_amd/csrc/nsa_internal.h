@@ -61,13 +61,21 @@ hipError_t launch_meta_table(const MetaParams& p, hipStream_t stream);
 // ---- compression kernel ---------------------------------------------------
 constexpr int kCompressMaxSeg = 128;   // sequences per launch (more -> several launches)
 
+// Compression: a workgroup owns a run of nw consecutive windows of one
+// sequence and one column slab (cs 16-byte chunks) of the [N*D] row, and
+// stages the run's input rows in LDS (at most kCompressStageBytes).
+constexpr int kCompressStageBytes = 64 * 1024;
+
 struct CompressParams {
     const uint16_t* x;   // [T, N, D]
     const uint16_t* w;   // [l, N]
     uint16_t* y;         // [T2, N, D]
     int N, D, l, d;
     int nseg;
-    int max_blocks_x;
+    int max_blocks_x;    // grid x: a multiple of 8 covering (runs x slabs) of the longest sequence
+    int cs_log2;         // log2 of the 16-byte chunks per column slab
+    int nslab;           // column slabs per row: N*D/8 / cs
+    int nw;              // windows per run
     int in_off[kCompressMaxSeg];   // first input token of each sequence
     int out_off[kCompressMaxSeg];  // first output entry of each sequence
     int n_out[kCompressMaxSeg];    // output entries of each sequence

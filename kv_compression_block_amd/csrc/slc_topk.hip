@@ -20,16 +20,18 @@
 //     workgroup barrier per tile.  Everything else a wave touches in LDS (its tokens' rings,
 //     importance scores and top-k staging) is private to the wave and needs
 //     only wave-level ordering.
-//   * The group-summed P of each token goes to a 128-entry LDS ring indexed
-//     by compressed-entry number; after every key tile the select blocks
-//     whose whole stencil is available are finished as a fixed-order weighted
-//     sum of at most H+1 ring entries (the remap written as a stencil over
-//     r = m + n with coefficient c(r) = number of (m, n) pairs).  The ring
-//     keeps the H entries a later block still needs.  Its first four slots
-//     are repeated past its end, so a stencil of up to five taps (every
-//     workload's: H = R + floor(l/d) - 2 = 4) reads five consecutive slots
-//     from one address with immediate offsets.  The (token, block) pairs of
-//     a tile are spread over the wave's lanes.
+//   * The group-summed P of each token goes to an LDS ring indexed by
+//     compressed-entry number; after every batch of key tiles (as many as
+//     keep the wave's lanes about busy in the stencil, one tile when a wave
+//     holds four tokens or more) the select blocks whose whole stencil is
+//     available are finished as a fixed-order weighted sum of at most H+1
+//     ring entries (the remap written as a stencil over r = m + n with
+//     coefficient c(r) = number of (m, n) pairs).  The ring (128-512
+//     entries) keeps a batch plus the H entries a later block still needs.
+//     Its first four slots are repeated past its end, so a stencil of up
+//     to five taps (every workload's: H = R + floor(l/d) - 2 = 4) reads
+//     five consecutive slots from one address with immediate offsets.  The
+//     (token, block) pairs of a batch are spread over the wave's lanes.
 //   * Top-k per (token, KV head) row, wave-local, on the float bits (scores
 //     are >= 0, so their bit patterns order like the values).  A radix
 //     select over the 64 per-lane maxima (one ballot per bit) gives a lower

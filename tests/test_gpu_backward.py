@@ -32,6 +32,11 @@ SMALL = {
 }
 NEG = dataclasses.replace(synth.WORKLOADS[0], name="negative-scale-bwd", N1=8, N2=2, scale=-0.09,
                           seqlens=(400, 77))
+# Sequences long enough (136-161 compressed entries, five or six key tiles)
+# that the query-side kernel runs its steady state: the key-tile slots wrap
+# around, and most waves take the loop without the visibility test.
+LONG = dataclasses.replace(synth.small_variant(4, [2600, 333]), name="long-seqs-bwd", N1=16)
+LONG192 = dataclasses.replace(synth.small_variant(1, [2200]), name="long-seq-d192-bwd")
 
 
 def assert_grad_close(got: np.ndarray, ref: np.ndarray, what: str):
@@ -73,7 +78,8 @@ def _run(wl, keys=("dq",)):
 
 
 @pytest.mark.parametrize("name,wl,dtype", [(f"w{i}", SMALL[i], "bf16") for i in SMALL] +
-                         [("neg", NEG, "bf16"), ("w2-f16", SMALL[2], "f16")])
+                         [("neg", NEG, "bf16"), ("w2-f16", SMALL[2], "f16"), ("long", LONG, "bf16"),
+                          ("long-f16", LONG, "f16"), ("long-d192", LONG192, "bf16")])
 def test_backward_against_oracle(name, wl, dtype):
     _run(wl.with_dtype(dtype), keys=("dq", "dkc", "dvc"))
 

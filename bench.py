@@ -4,7 +4,8 @@
 One step = the whole hot path over one batch of synthetic input resident in
 HBM: compress K, compress V (nsa_compress), compressed attention
 (nsa_compress_attention_fwd: scores, mask, softmax, P.V) and the importance
-scores + top-k (nsa_compress_attention_select).  W untimed warm-up steps,
+scores + top-k (nsa_compress_attention_select, reading the per-row softmax
+bias the forward left in the workspace, as nsa_compress_attention does).  W untimed warm-up steps,
 then K timed steps bracketed by synchronisations; HIP events recorded on the
 launch stream between the four calls give each kernel's duration inside the
 same timed region.
@@ -105,9 +106,12 @@ def workload_work(wl, T2: int) -> dict:
     comp_flops = 2.0 * wl.l * T2 * wl.N2 * (wl.D1 + wl.D2)
     bytes_ck = 2.0 * (wl.T + T2) * wl.N2 * wl.D1
     bytes_cv = 2.0 * (wl.T + T2) * wl.N2 * wl.D2
+    # attention: q, Kc, Vc, out, the two [T, N1, 8] statistics and the
+    # per-row bias (4 B) it leaves for the importance pass
     bytes_attn = (2.0 * wl.T * wl.N1 * (wl.D1 + wl.D2) + 2.0 * T2 * wl.N2 * (wl.D1 + wl.D2)
-                  + 2 * 32.0 * wl.T * wl.N1)
-    bytes_sel = (2.0 * wl.T * wl.N1 * wl.D1 + 2.0 * T2 * wl.N2 * wl.D1 + 8.0 * wl.T * wl.N1
+                  + 2 * 32.0 * wl.T * wl.N1 + 4.0 * wl.T * wl.N1)
+    # importance + top-k: q, Kc, the per-row bias, topk_indices
+    bytes_sel = (2.0 * wl.T * wl.N1 * wl.D1 + 2.0 * T2 * wl.N2 * wl.D1 + 4.0 * wl.T * wl.N1
                  + 4.0 * wl.T * wl.N2 * wl.count)
     return {"visible_pairs": vis, "attn_flops": attn_flops, "compress_flops": comp_flops,
             "bytes_compress_k": bytes_ck, "bytes_compress_v": bytes_cv,
@@ -401,7 +405,9 @@ class Path:
                                            stream=stream, atten_mask=self.masks.get("atten_mask"))
         if ev is not None:
             ev[3].record(stream)
-        nsa.nsa_compress_attention_select(self.plan, inp["q"], self.kc, outs["softmax_max"], outs["softmax_sum"],
+        # the row statistics from the per-row bias the forward left in the
+        # workspace (as nsa_compress_attention does)
+        nsa.nsa_compress_attention_select(self.plan, inp["q"], self.kc, None, None,
                                           workspace=self.ws, outputs=outs, stream=stream,
                                           atten_mask=self.masks.get("atten_mask"),
                                           topk_mask=self.masks.get("topk_mask"))

@@ -153,7 +153,12 @@ nsa_status nsa_compress_backward(const void* input, const void* weight, const fl
  *   select_block_count    k: in [1, 32]
  *   dtype                 element type of q/k/v/out; the second phase must
  *                         be given tensors of this type
- *   workspace_bytes       out: bytes of device workspace the second phase needs
+ *   workspace_bytes       out: bytes of device workspace the second phase needs:
+ *                         the per-sequence table (64 bytes per sequence plus
+ *                         one status entry, rounded up to 256), then one
+ *                         float32 per (query token, query head) that the
+ *                         forward calls fill with the row's base-2
+ *                         log-normaliser for the importance pass
  *   plan_out              out: the plan (caller frees it)
  *
  * Errors: NSA_ERR_NULLPTR, NSA_ERR_DTYPE (unknown dtype code), NSA_ERR_SHAPE,
@@ -236,13 +241,21 @@ nsa_status nsa_compress_attention_noalloc(nsa_plan plan, const void* query, cons
  * nsa_compress_attention_select on the same stream.
  *
  * nsa_compress_attention_fwd -- steps 1-3: attention_out, softmax_max and
- * softmax_sum (arguments as for nsa_compress_attention).
+ * softmax_sum (arguments as for nsa_compress_attention).  It also writes
+ * into the workspace, for every query row, max * log2(e) + log2(sum)
+ * (+inf where nothing is visible): the row's softmax in base 2, 4 bytes
+ * instead of the 64 of the two [.., 8] statistics.
  *
  * nsa_compress_attention_select -- steps 4-7: topk_indices (and p_slc_debug)
- * from query, key and the softmax_max / softmax_sum the first half wrote;
- * the recomputed P_cmp = exp(score - max) / sum is the normalised softmax.
- * It must run after nsa_compress_attention_fwd of the same inputs (same
- * stream, or an event in between).
+ * from query, key and the row statistics of the first half; the recomputed
+ * P_cmp = exp(score - max) / sum is the normalised softmax.  The statistics
+ * are read from softmax_max / softmax_sum when both are given, or from the
+ * per-row array the forward call wrote into this workspace when both are
+ * NULL (the same outputs bit for bit; one is NULL and the other not:
+ * NSA_ERR_NULLPTR).  nsa_compress_attention takes the second way.  It must
+ * run after nsa_compress_attention_fwd of the same inputs (same stream, or
+ * an event in between), with the forward's workspace when the statistics
+ * are NULL.
  *
  * Both take the plan and a workspace of the size phase one returned, and
  * return the same errors as nsa_compress_attention.
@@ -347,7 +360,10 @@ nsa_status nsa_compress_attention_fwd_split(nsa_plan plan, const void* query, co
  * mask in it may be NULL).  The masks are packed to bits inside the
  * workspace first, so the workspace must hold masked_workspace_bytes (plan
  * info) whenever a mask is given.  nsa_compress_attention_select_masked
- * needs the same atten_mask as the fwd call whose statistics it reads.
+ * needs the same atten_mask as the fwd call whose statistics it reads, and
+ * takes them from softmax_max / softmax_sum or, when both are NULL, from
+ * the workspace as nsa_compress_attention_select does (the fwd calls with
+ * and without masks both fill that array).
  * Errors: those of the unmasked calls, plus NSA_ERR_SHAPE (a mask smaller
  * than stated above) and NSA_ERR_WORKSPACE (workspace below
  * masked_workspace_bytes).

@@ -420,15 +420,25 @@ def nsa_compress_attention_fwd_split(plan: Plan, query: torch.Tensor, key: torch
 
 
 def nsa_compress_attention_select(plan: Plan, query: torch.Tensor, key: torch.Tensor,
-                                  softmax_max: torch.Tensor, softmax_sum: torch.Tensor,
+                                  softmax_max: Optional[torch.Tensor], softmax_sum: Optional[torch.Tensor],
                                   workspace: Optional[torch.Tensor] = None, return_p_slc: bool = False,
                                   outputs: Optional[dict] = None, stream=None, atten_mask=None,
                                   topk_mask=None):
     """Steps 4-7 from the first half's softmax statistics: returns
     topk_indices (and the importance scores with ``return_p_slc``).  The
-    atten_mask must be the one the first half was given."""
+    atten_mask must be the one the first half was given.  With
+    ``softmax_max`` and ``softmax_sum`` both None the statistics are the
+    per-row array the first half wrote into ``workspace`` (which must then
+    be that call's workspace)."""
     _check_qkv(plan, query, key)
+    if (softmax_max is None) != (softmax_sum is None):
+        raise ValueError("give softmax_max and softmax_sum together, or neither (then the forward's workspace)")
+    if softmax_max is None and workspace is None:
+        raise ValueError("without softmax_max / softmax_sum the statistics come from the forward call's "
+                         "workspace: pass it")
     for t, name in ((softmax_max, "softmax_max"), (softmax_sum, "softmax_sum")):
+        if t is None:
+            continue
         _need_tensor(t, name)
         if t.dtype != torch.float32 or tuple(t.shape) != (plan.info["total_q_tokens"], plan.info["head_num"], 8):
             raise ValueError(f"{name} must be float32 [T1, N1, 8]")

@@ -393,7 +393,9 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         auto& s = scur;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-            float ps = 0.f;
+            // the tile's sum starts at its first exponential (the same value
+            // as 0 + it: every P is >= +0), saving one add per tile
+            float ps;
 #pragma unroll
             for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
                     const float sv = s[qb][kb][r];
                     const float pv = fast_exp2(fmaf(sv, c, nbias[qb]));
                     s[qb][kb][r] = pv;
-                    ps += pv;
+                    ps = (kb == 0 && r == 0) ? pv : ps + pv;
                 }
             }
             lsum[qb] += ps;
@@ -616,6 +618,8 @@ __global__ __launch_bounds__(64 * W, (D1 == 128 && D2 == 128) ? 3 : 2) void k_cm
         f32x4 v4 = {val, val, val, val};
         __builtin_nontemporal_store(v4, (f32x4*)dst);
         __builtin_nontemporal_store(v4, (f32x4*)(dst + 4));
+        if (p.bias != nullptr && hf_e == 0)
+            p.bias[grow] = row_bias(smv, ssv);
     }
 }
 
@@ -676,6 +680,8 @@ __global__ __launch_bounds__(256) void k_cmp_attn_combine(AttnParams p, const Co
             *(f32x4*)(p.smax + orow * 8 + 4) = a;
             *(f32x4*)(p.ssum + orow * 8) = bb;
             *(f32x4*)(p.ssum + orow * 8 + 4) = bb;
+            if (p.bias != nullptr)
+                p.bias[orow] = row_bias(smv, ssv);
         }
     }
 }

@@ -91,7 +91,9 @@ struct nsa_plan_s {
     int log2gp, topk_waves, topk_kbufs, sb;
     size_t topk_lds;
     int64_t tiles_a, tiles_c, tiles_s;
-    size_t ws_bytes;
+    size_t ws_bytes;                  // the table, then the per-row bias array (the headline calls' workspace)
+    size_t table_bytes;               // the table and its status entry, rounded up to 256 bytes
+    size_t bias_off;                  // byte offset of the [T1, N1] float32 bias array the forward writes
     // B entries, then one zero entry whose first word is the status word
     // (kernels exit at once when it is not 0; the upload keeps it 0)
     std::vector<nsa::BatchEnt> table;
@@ -454,7 +456,9 @@ static nsa_status make_plan(
     plan->tiles_c = tc;
     plan->tiles_s = ts;
     plan->tiles_k = tk;
-    plan->ws_bytes = ((size_t)(batch + 1) * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
+    plan->table_bytes = ((size_t)(batch + 1) * sizeof(nsa::BatchEnt) + 255) / 256 * 256;
+    plan->bias_off = plan->table_bytes;
+    plan->ws_bytes = plan->bias_off + ((size_t)q_off * (size_t)head_num * 4 + 255) / 256 * 256;
     plan->T_max = T_max;
     plan->ncmp_max = ncmp_max;
     plan->vis_words = std::max<int64_t>(1, (ncmp_max + 31) / 32);
@@ -596,11 +600,16 @@ nsa_status nsa_compress_attention_metadata(nsa_plan device_plan, const int64_t* 
 
 namespace {
 
+// `need`: the workspace bytes the call reads and writes (default: the plan's
+// workspace size).
 nsa_status check_exec(nsa_plan plan, void* workspace, size_t workspace_bytes,
-                      std::initializer_list<const void*> a16, std::initializer_list<const void*> a4)
+                      std::initializer_list<const void*> a16, std::initializer_list<const void*> a4,
+                      size_t need = SIZE_MAX)
 {
-    if (workspace_bytes < plan->ws_bytes || (plan->ws_bytes > 0 && !workspace))
-        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, plan->ws_bytes);
+    if (need == SIZE_MAX)
+        need = plan->ws_bytes;
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(NSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
     for (const void* ptr : a16)
         if (ptr && !aligned(ptr, 16))
             return fail(NSA_ERR_CONSTRAINT, "tensors and workspace must be 16-byte aligned");
@@ -628,6 +637,26 @@ const int* status_word(nsa_plan plan, const void* workspace)
     return (const int*)((const char*)workspace + plan->B * (int64_t)sizeof(nsa::BatchEnt));
 }
 
+// The [T1, N1] array of per-row biases (base-2 log-normalisers) that every
+// forward call writes into its workspace and the importance pass may read
+// instead of the two [T1, N1, 8] statistics.
+float* ws_bias(nsa_plan plan, void* workspace) { return (float*)((char*)workspace + plan->bias_off); }
+
+// Where the importance pass takes its row statistics from: softmax_max and
+// softmax_sum when both are given, the bias array the forward call left in
+// the workspace when both are NULL.
+nsa_status select_stats(nsa_plan plan, const float* softmax_max, const float* softmax_sum, void* workspace,
+                        const float** bias)
+{
+    *bias = nullptr;
+    if ((softmax_max == nullptr) != (softmax_sum == nullptr))
+        return fail(NSA_ERR_NULLPTR, "softmax_max and softmax_sum must both be given, or both be NULL "
+                    "(then the forward call's statistics in the workspace are read)");
+    if (softmax_max == nullptr)
+        *bias = ws_bias(plan, workspace);
+    return NSA_OK;
+}
+
 float exp2_scale(const nsa_plan_s* plan) { return std::fabs(plan->scale) * 1.4426950408889634f; }
 
 // Magic numbers for division by G (round-up method): s = ceil(log2 G),
@@ -644,7 +673,8 @@ void g_magic(int G, uint32_t* m, uint32_t* s)
 uint32_t q_sign(const nsa_plan_s* plan) { return plan->scale < 0.f ? 0x80008000u : 0u; }
 
 nsa::AttnParams fwd_params(nsa_plan plan, const void* query, const void* key, const void* value,
-                           void* attention_out, float* softmax_max, float* softmax_sum, void* workspace)
+                           void* attention_out, float* softmax_max, float* softmax_sum, void* workspace,
+                           bool write_bias = true)
 {
     const float abs_scale = std::fabs(plan->scale);
     const float c = exp2_scale(plan);
@@ -656,6 +686,7 @@ nsa::AttnParams fwd_params(nsa_plan plan, const void* query, const void* key, co
     a.out = (uint16_t*)attention_out;
     a.smax = softmax_max;
     a.ssum = softmax_sum;
+    a.bias = write_bias ? ws_bias(plan, workspace) : nullptr;
     a.bt = (const nsa::BatchEnt*)workspace;
     a.status = status_word(plan, workspace);
     a.B = (int)plan->B;
@@ -677,9 +708,11 @@ nsa::AttnParams fwd_params(nsa_plan plan, const void* query, const void* key, co
 
 nsa_status launch_fwd(nsa_plan plan, const void* query, const void* key, const void* value,
                       void* attention_out, float* softmax_max, float* softmax_sum, void* workspace,
-                      hipStream_t s, const uint32_t* vis = nullptr, const int4* vis_span = nullptr)
+                      hipStream_t s, const uint32_t* vis = nullptr, const int4* vis_span = nullptr,
+                      bool write_bias = true)
 {
-    nsa::AttnParams a = fwd_params(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace);
+    nsa::AttnParams a = fwd_params(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace,
+                                   write_bias);
     a.vis = vis;
     a.vis_span = vis_span;
     hipError_t e = nsa::launch_cmp_attn(plan->dtype, (int)plan->D1, (int)plan->D2, a, (int)plan->tiles_a, s);
@@ -731,7 +764,7 @@ SplitCounts split_counts(const nsa_plan_s* plan, int64_t C)
 }
 
 nsa_status launch_select(nsa_plan plan, const void* query, const void* key, const float* softmax_max,
-                         const float* softmax_sum, int32_t* topk_indices, float* p_slc_debug,
+                         const float* softmax_sum, const float* bias, int32_t* topk_indices, float* p_slc_debug,
                          void* workspace, hipStream_t s, const uint32_t* vis = nullptr,
                          const int4* vis_span = nullptr, const uint32_t* cand = nullptr)
 {
@@ -741,6 +774,7 @@ nsa_status launch_select(nsa_plan plan, const void* query, const void* key, cons
     t.kc = (const uint16_t*)key;
     t.smax = softmax_max;
     t.ssum = softmax_sum;
+    t.bias = bias;
     t.topk = topk_indices;
     t.pslc = p_slc_debug;
     t.bt = (const nsa::BatchEnt*)workspace;
@@ -940,18 +974,22 @@ nsa_status nsa_compress_attention_select(nsa_plan plan, const void* query, const
 {
     if (!plan)
         return fail(NSA_ERR_NULLPTR, "plan is NULL");
-    if (plan->T1 > 0 && (!query || !topk_indices || !softmax_max || !softmax_sum))
-        return fail(NSA_ERR_NULLPTR, "query, softmax_max, softmax_sum and topk_indices must not be NULL");
+    if (plan->T1 > 0 && (!query || !topk_indices))
+        return fail(NSA_ERR_NULLPTR, "query and topk_indices must not be NULL");
     if (plan->T2 > 0 && !key)
         return fail(NSA_ERR_NULLPTR, "key must not be NULL");
     nsa_status st = check_exec(plan, workspace, workspace_bytes, {query, key, softmax_max, softmax_sum, workspace},
                                {topk_indices, p_slc_debug});
     if (st != NSA_OK || plan->T1 == 0)
         return st == NSA_OK ? ok() : st;
+    const float* bias = nullptr;
+    if ((st = select_stats(plan, softmax_max, softmax_sum, workspace, &bias)) != NSA_OK)
+        return st;
     hipStream_t s = (hipStream_t)stream;
     if ((st = upload_table(plan, workspace, s)) != NSA_OK)
         return st;
-    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s)) != NSA_OK)
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, bias, topk_indices, p_slc_debug, workspace,
+                            s)) != NSA_OK)
         return st;
     return ok();
 }
@@ -977,7 +1015,8 @@ nsa_status nsa_compress_attention(nsa_plan plan, const void* query, const void* 
         return st;
     if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s)) != NSA_OK)
         return st;
-    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s)) != NSA_OK)
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, ws_bias(plan, workspace), topk_indices,
+                            p_slc_debug, workspace, s)) != NSA_OK)
         return st;
     return ok();
 }
@@ -1052,16 +1091,20 @@ nsa_status nsa_compress_attention_noalloc(nsa_plan plan, const void* query, cons
         return st;
     const size_t ws_bytes = sizeof(nsa::BatchEnt) * (kNoAllocMaxBatch + 4);
     if ((st = check_exec(plan, ws, ws_bytes, {query, key, value, attention_out, softmax_max, softmax_sum},
-                         {topk_indices, p_slc_debug})) != NSA_OK)
+                         {topk_indices, p_slc_debug}, plan->table_bytes)) != NSA_OK)
         return st;
     if (plan->T1 == 0)
         return ok();
     hipStream_t s = (hipStream_t)stream;
     if ((st = upload_table(plan, ws, s)) != NSA_OK)
         return st;
-    if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, ws, s)) != NSA_OK)
+    // The scratch holds the table only: the importance pass reads the row
+    // statistics from softmax_max / softmax_sum.
+    if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, ws, s, nullptr, nullptr,
+                         false)) != NSA_OK)
         return st;
-    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, ws, s)) != NSA_OK)
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, nullptr, topk_indices, p_slc_debug, ws,
+                            s)) != NSA_OK)
         return st;
     return ok();
 }
@@ -1103,14 +1146,17 @@ nsa_status nsa_compress_attention_select_masked(nsa_plan plan, const void* query
 {
     if (!plan)
         return fail(NSA_ERR_NULLPTR, "plan is NULL");
-    if (plan->T1 > 0 && (!query || !topk_indices || !softmax_max || !softmax_sum))
-        return fail(NSA_ERR_NULLPTR, "query, softmax_max, softmax_sum and topk_indices must not be NULL");
+    if (plan->T1 > 0 && (!query || !topk_indices))
+        return fail(NSA_ERR_NULLPTR, "query and topk_indices must not be NULL");
     if (plan->T2 > 0 && !key)
         return fail(NSA_ERR_NULLPTR, "key must not be NULL");
     nsa_status st = check_exec(plan, workspace, workspace_bytes, {query, key, softmax_max, softmax_sum, workspace},
                                {topk_indices, p_slc_debug});
     if (st != NSA_OK || plan->T1 == 0)
         return st == NSA_OK ? ok() : st;
+    const float* bias = nullptr;
+    if ((st = select_stats(plan, softmax_max, softmax_sum, workspace, &bias)) != NSA_OK)
+        return st;
     hipStream_t s = (hipStream_t)stream;
     const uint32_t *vis = nullptr, *cand = nullptr;
     const int4* span = nullptr;
@@ -1118,8 +1164,8 @@ nsa_status nsa_compress_attention_select_masked(nsa_plan plan, const void* query
         return st;
     if ((st = upload_table(plan, workspace, s)) != NSA_OK)
         return st;
-    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s,
-                            vis, span, cand)) != NSA_OK)
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, bias, topk_indices, p_slc_debug, workspace,
+                            s, vis, span, cand)) != NSA_OK)
         return st;
     return ok();
 }
@@ -1151,8 +1197,8 @@ nsa_status nsa_compress_attention_masked(nsa_plan plan, const void* query, const
     if ((st = launch_fwd(plan, query, key, value, attention_out, softmax_max, softmax_sum, workspace, s,
                          vis, span)) != NSA_OK)
         return st;
-    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, topk_indices, p_slc_debug, workspace, s,
-                            vis, span, cand)) != NSA_OK)
+    if ((st = launch_select(plan, query, key, softmax_max, softmax_sum, ws_bias(plan, workspace), topk_indices,
+                            p_slc_debug, workspace, s, vis, span, cand)) != NSA_OK)
         return st;
     return ok();
 }

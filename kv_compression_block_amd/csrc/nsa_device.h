@@ -77,10 +77,14 @@ struct ElemF16 {
 };
 
 // Combine a value with the one held by the lane 32 positions away.
+// The max as a compare and a select: equal to fmaxf for any two values that
+// are not NaN, without the two quieting instructions fmaxf needs for
+// operands that come out of a lane exchange.
 __device__ __forceinline__ float half_max(float x)
 {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return a > b ? a : b;
 }
 
 __device__ __forceinline__ float half_sum(float x)
@@ -90,6 +94,16 @@ __device__ __forceinline__ float half_sum(float x)
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Base-2 log-normaliser of a softmax row from its natural-unit max m and its
+// sum L of exp(score - m): the row's probability is then
+// exp2(score * |scale| * log2(e) - bias).  +inf (probability 0) for a row
+// that sees nothing (L = 0).  The attention epilogue and the importance pass
+// both derive it here, so either may compute it for the other.
+__device__ __forceinline__ float row_bias(float m, float L)
+{
+    return L > 0.f ? fmaf(m, 1.4426950408889634f, __builtin_amdgcn_logf(L)) : __builtin_inff();
+}
 
 // Buffer resource over [base, base + bytes): raw (unstrided) loads at byte
 // offsets >= bytes return zero, so a tile that runs past the end of its rows

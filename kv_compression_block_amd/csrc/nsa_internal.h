@@ -134,6 +134,7 @@ struct AttnParams {
     uint16_t* out;        // [T1, N1, D2]
     float* smax;          // [T1, N1, 8]
     float* ssum;          // [T1, N1, 8]
+    float* bias;          // NULL or [T1, N1]: row_bias(max, sum) of every row, for the importance pass
     const BatchEnt* bt;   // [B], device
     const int* status;    // the table's status word (a kernel returns at once when it is not 0)
     int B, N1, N2, G;
@@ -187,6 +188,7 @@ struct TopkParams {
     const uint16_t* kc;   // [T2, N2, D1]
     const float* smax;    // [T1, N1, 8]
     const float* ssum;    // [T1, N1, 8]
+    const float* bias;    // NULL (derive from smax, ssum) or [T1, N1] as the attention pass wrote it
     int32_t* topk;        // [T1, N2, count]
     float* pslc;          // NULL or [T1, N2, s_stride]
     const BatchEnt* bt;   // [B], device

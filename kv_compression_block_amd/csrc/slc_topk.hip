@@ -54,8 +54,6 @@
 
 namespace nsa {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // Orders this wave's LDS accesses: a wave's LDS operations execute in order,
 // so it is enough to keep the compiler from moving them across this point.
 __device__ __forceinline__ void wave_lds_sync()
@@ -63,6 +61,18 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Whether accumulator register r of row half rr is the first, in the order
+// (rr, r), whose row (rr * 32 + 8 * (r / 4) + r % 4 in the lower half-wave)
+// belongs to its token (rows of one token: 2^log2gp consecutive rows).
+constexpr bool first_term(int rr, int r, int log2gp)
+{
+    const int tw = (rr * 32 + 8 * (r >> 2) + (r & 3)) >> log2gp;
+    for (int r2 = 0; r2 < rr * 16 + r; ++r2)
+        if (((r2 >> 4) * 32 + 8 * ((r2 & 15) >> 2) + (r2 & 3)) >> log2gp == tw)
+            return false;
+    return true;
 }
 
 // Three waves per SIMD where the registers allow it (D1 = 128 with groups
@@ -132,18 +142,16 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
     }
     // Per accumulator register: P = exp2(S*c - bias) is the normalised P_cmp.
     // Rows that are padding, past the sequence, or see no block get +inf.
-    // Each lane loads the statistics of row `lane` of its wave (two loads),
-    // then every register fetches its row's bias from that lane.
+    // Each lane loads the bias of row `lane` of its wave (one load from the
+    // attention pass's compact array, else the two statistics), then every
+    // register fetches its row's bias from that lane.
     float bias_lane = INFINITY;
     {
         const int tok = tok_w + (lane >> LOG2GP);
         const int hh = lane & (GP - 1);
         if (tok < be.T && hh < G) {
             const int64_t row = (int64_t)(be.q_off + tok) * p.N1 + (int64_t)g * G + hh;
-            const float m = p.smax[row * 8];
-            const float L = p.ssum[row * 8];
-            if (L > 0.f)
-                bias_lane = m * kLog2e + __builtin_amdgcn_logf(L);
+            bias_lane = p.bias != nullptr ? p.bias[row] : row_bias(p.smax[row * 8], p.ssum[row * 8]);
         }
     }
     float bias[2][16];
@@ -364,11 +372,9 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         }
 
         // P, masked on the last tiles, summed over the heads of each token.
+        // A token's sum starts at its first term (the same value as 0 + it:
+        // every P is >= +0); every token of the wave has at least one term.
         float acc[TOKW][NKB];
-#pragma unroll
-        for (int tw = 0; tw < TOKW; ++tw)
-            for (int kb = 0; kb < NKB; ++kb)
-                acc[tw][kb] = 0.f;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -383,7 +389,11 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
                         // visible iff key*d + l - 1 <= the token's position
                         pv = (key * p.d + p.l - 1 <= tok + be.pos_off) ? pv : 0.f;
                     }
-                    acc[(rr * 32 + 8 * (r >> 2) + (r & 3)) >> LOG2GP][kb] += pv;
+                    const int tw = (rr * 32 + 8 * (r >> 2) + (r & 3)) >> LOG2GP;
+                    if (first_term(rr, r, LOG2GP))
+                        acc[tw][kb] = pv;
+                    else
+                        acc[tw][kb] += pv;
                 }
             }
         }

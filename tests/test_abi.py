@@ -133,6 +133,34 @@ def test_compute_call_rejects_before_touching_the_device():
     lib.nsa_plan_destroy(None)
 
 
+def test_select_statistics_both_or_neither():
+    """The importance pass reads softmax_max and softmax_sum, or (both NULL)
+    the per-row array the forward left in the workspace; one without the
+    other is refused before any device work."""
+    st, ws, plan = _ws(**_good())
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    for smax, ssum in ((fake, None), (None, fake)):
+        assert lib.nsa_compress_attention_select(plan, fake, fake, smax, ssum, fake, None, fake, ws, None) \
+            == _lib.NSA_ERR_NULLPTR
+        assert "both" in lib.nsa_last_error().decode()
+        m = _lib.Masks()
+        assert lib.nsa_compress_attention_select_masked(plan, fake, fake, ctypes.byref(m), smax, ssum, fake, None,
+                                                        fake, ws, None) == _lib.NSA_ERR_NULLPTR
+    lib.nsa_plan_destroy(plan)
+
+
+def test_workspace_holds_table_and_row_biases():
+    """Phase one's workspace: the table (64 B per sequence plus a status
+    entry, rounded to 256 B), then one float32 per (query token, head)."""
+    for N1, B, qlen, clen, slen in ((16, 2, [100, 300], [5, 16], [2, 6]), (64, 1, [4097], [255], [65])):
+        st, ws, plan = _ws(**_good(N1=N1, B=B, qlen=qlen, clen=clen, slen=slen))
+        assert st == _lib.NSA_OK
+        table = ((B + 1) * 64 + 255) // 256 * 256
+        assert ws == table + (qlen[-1] * N1 * 4 + 255) // 256 * 256
+        _lib.load().nsa_plan_destroy(plan)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(l=24), _lib.NSA_ERR_CONSTRAINT), (dict(l=160), _lib.NSA_ERR_CONSTRAINT),
     (dict(d=48, l=32), _lib.NSA_ERR_CONSTRAINT), (dict(D=72), _lib.NSA_ERR_CONSTRAINT),

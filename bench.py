@@ -441,6 +441,13 @@ class Path:
         ai = work["attn_flops"] / work["bytes_attn"]
         attainable = min(peak, ai * PEAK_HBM_GBS / 1e3)
         recompute = 2.0 * wl.D1 * work["visible_pairs"] * wl.N1
+        # The importance pass is bound by arithmetic, not bytes: the recomputed
+        # Q.K^T on MFMA, and per score an FMA, an exp2 (half rate) and an add on
+        # the vector ALUs (four wave64 issue slots of 4 cycles per 64 scores,
+        # 1024 SIMDs at 2.4 GHz).  On this part the two pipes barely overlap,
+        # so the floor it can reach is their sum.
+        sel_mfma_ms = recompute / (peak * 1e12) * 1e3
+        sel_valu_ms = work["visible_pairs"] * wl.N1 * 0.25 / (1024 * 2.4e9) * 1e3
 
         def gbs(b, ms):
             return b / (ms / 1e3) / 1e9
@@ -455,7 +462,9 @@ class Path:
                           "frac_of_attainable": attn_tflops / attainable},
             "select_topk": {"ms": per["select_topk"], "GB/s": gbs(work["bytes_select"], per["select_topk"]),
                             "frac_of_hbm_peak": gbs(work["bytes_select"], per["select_topk"]) / PEAK_HBM_GBS,
-                            "recompute_TFLOP/s": recompute / (per["select_topk"] / 1e3) / 1e12},
+                            "recompute_TFLOP/s": recompute / (per["select_topk"] / 1e3) / 1e12,
+                            "alu_floor_ms": {"mfma": sel_mfma_ms, "valu": sel_valu_ms},
+                            "frac_of_serial_alu_floor": (sel_mfma_ms + sel_valu_ms) / per["select_topk"]},
         }
         total_flops = work["attn_flops"] + work["compress_flops"]
         return {"ms_per_step": ms_step, "query_tokens_per_s": wl.T / (ms_step / 1e3),

@@ -579,9 +579,12 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
             if (i < nch)
                 ncand += __popcll(__ballot(((cm >> i) & 1u) && key[i] >= tau0));
         if (ncand <= 64) {
-            // Stage the candidates (score bits at [0, 64), indices at [64, 128)),
-            // then each ranks itself against all of them by (score desc,
-            // index asc); the first kk ranks are the picks.
+            // Stage the candidates as 64-bit keys (score bits << 32 | ~index):
+            // they order like (score desc, index asc), all distinct, and the
+            // zeros that pad the staging to a multiple of 8 rank below every
+            // candidate.  Each candidate's rank is the number of larger keys;
+            // the first kk ranks are the picks.
+            uint64_t* stg64 = (uint64_t*)my_stg;
             int pos = 0;
 #pragma unroll
             for (int i = 0; i < kTopkMaxNpl; ++i) {
@@ -590,26 +593,29 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
                     const uint64_t bs = __ballot(sel);
                     if (sel) {
                         const int at = pos + __popcll(bs & lt_mask);
-                        my_stg[at] = key[i];
-                        my_stg[64 + at] = (uint32_t)(lane + 64 * i);
+                        stg64[at] = ((uint64_t)key[i] << 32) | (uint32_t)~(uint32_t)(lane + 64 * i);
                     }
                     pos += __popcll(bs);
                 }
             }
+            const int nc8 = (ncand + 7) & ~7;
+            if (lane >= ncand && lane < nc8)
+                stg64[lane] = 0;
             wave_lds_sync();
             if (lane < ncand) {
-                const uint32_t mk = my_stg[lane];
-                const uint32_t mi = my_stg[64 + lane];
+                const uint64_t mu = stg64[lane];
                 int rank = 0;
-                for (int q = 0; q < ncand; q += 4) {
-                    const u32x4 ok = *(const u32x4*)&my_stg[q];
-                    const u32x4 oi = *(const u32x4*)&my_stg[64 + q];
+                for (int q = 0; q < nc8; q += 8) {
+                    u64x2 o[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        rank += (q + e < ncand) && (ok[e] > mk || (ok[e] == mk && oi[e] < mi));
+                        o[e] = *(const u64x2*)&stg64[q + 2 * e];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        rank += (int)(o[e][0] > mu) + (int)(o[e][1] > mu);
                 }
                 if (rank < kk)
-                    trow[rank] = (int32_t)mi;
+                    trow[rank] = (int32_t)~(uint32_t)mu;
             }
             if (lane >= kk && lane < p.count)
                 trow[lane] = -1;

@@ -555,9 +555,10 @@ __global__ __launch_bounds__(256, (D1 == 128 && LOG2GP >= 4) ? 3 : 2) void k_slc
         // Lower bound first: the kk-th largest of the per-lane maxima.  The
         // kk lanes at or above it hold kk distinct scores >= it, so every
         // score of the top kk is >= it too; usually only a few dozen
-        // candidates reach it.
+        // candidates reach it.  With at most 64 candidates the bound stays 0
+        // and all of them are ranked.
         uint32_t tau0 = 0;
-        if (nvalid > kk) {
+        if (nvalid > 64) {
             uint32_t lmax = 0;
 #pragma unroll
             for (int i = 0; i < kTopkMaxNpl; ++i)
